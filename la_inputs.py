@@ -1,0 +1,106 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module only draws random numbers and names workloads; it holds none of the
+method's arithmetic, so the oracle and the HIP path can both take their inputs
+from it without sharing any computation.
+
+Recipe (the shapes are the workloads the library is measured on):
+  * every tensor is [B, H, N, d] row-major (decode vectors are [B, H, d]);
+  * Q, K, V ~ N(0, 1), scaled by 1/sqrt(d) when ``scale`` is set, drawn in
+    fp32 and rounded to the target dtype (round-to-nearest-even for bf16);
+  * the output gradient dO ~ N(0, 1) in the target dtype;
+  * draws come from one torch.Generator seeded with ``seed``, in the order
+    q, k, v, dout.  ``device="cuda"`` draws with the device generator (fast for
+    the multi-GiB workloads); tests copy the exact drawn values to the host.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: torch.dtype
+    scale: bool          # divide Q, K, V by sqrt(d)
+    chunk: int = 64
+    calls: tuple = ()
+
+
+# The five measured workloads.
+TINY = Workload("tiny", 1, 2, 256, 32, torch.float32, False,
+                calls=("fwd_noncausal", "fwd_causal", "bwd_causal"))
+MID = Workload("mid", 4, 16, 4096, 64, torch.bfloat16, True,
+               calls=("fwd_causal", "bwd_causal", "fwd_noncausal"))
+LONG = Workload("long", 8, 16, 16384, 128, torch.bfloat16, True, calls=("fwd_causal", "bwd_causal"))
+VERYLONG = Workload("verylong", 1, 32, 131072, 128, torch.bfloat16, True, calls=("fwd_causal",))
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    batch: int
+    H: int
+    d: int
+    prefix: int
+    steps: int
+    dtype: torch.dtype
+
+
+DECODE = DecodeWorkload("decode", 256, 32, 128, 2048, 512, torch.bfloat16)
+
+WORKLOADS = {w.name: w for w in (TINY, MID, LONG, VERYLONG)}
+
+
+def generator(seed: int, device: str = "cpu") -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def normal(shape, gen: torch.Generator, dtype: torch.dtype, scale: float = 1.0,
+           device: str = "cpu") -> torch.Tensor:
+    """N(0, 1) * scale drawn in fp32, then rounded to ``dtype``."""
+    x = torch.randn(tuple(shape), generator=gen, dtype=torch.float32, device=device)
+    if scale != 1.0:
+        x.mul_(scale)
+    return x.to(dtype)
+
+
+def qkv(B, H, N, d, dtype=torch.bfloat16, seed=0, scale=True, device="cpu", with_dout=False):
+    """Draw q, k, v (and dout) of shape [B, H, N, d] in that order from one generator."""
+    gen = generator(seed, device)
+    s = 1.0 / math.sqrt(d) if scale else 1.0
+    q = normal((B, H, N, d), gen, dtype, s, device)
+    k = normal((B, H, N, d), gen, dtype, s, device)
+    v = normal((B, H, N, d), gen, dtype, s, device)
+    if not with_dout:
+        return q, k, v
+    dout = normal((B, H, N, d), gen, dtype, 1.0, device)
+    return q, k, v, dout
+
+
+def workload_inputs(w: Workload, seed=0, device="cpu", with_dout=True):
+    return qkv(w.B, w.H, w.N, w.d, w.dtype, seed, w.scale, device, with_dout)
+
+
+def decode_tokens(batch, H, d, steps, dtype=torch.bfloat16, seed=1, device="cpu"):
+    """Per-step decode vectors q, k, v of shape [steps, batch, H, d] ~ N(0,1)/sqrt(d)."""
+    gen = generator(seed, device)
+    s = 1.0 / math.sqrt(d)
+    q = normal((steps, batch, H, d), gen, dtype, s, device)
+    k = normal((steps, batch, H, d), gen, dtype, s, device)
+    v = normal((steps, batch, H, d), gen, dtype, s, device)
+    return q, k, v
+
+
+def to_f64(x: torch.Tensor):
+    """Exact widening of a tensor's values to a float64 numpy array on the host."""
+    return x.detach().to("cpu", torch.float64).numpy()

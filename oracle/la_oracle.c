@@ -1,0 +1,376 @@
+/*
+ * la_oracle.c -- fp64 CPU oracle for kernelized linear attention.
+ *
+ * TEST INFRASTRUCTURE ONLY (see la_oracle.h): used by the tests, the smoke
+ * check and the CPU-baseline leg of the benchmark, never by the product path.
+ *
+ * Each function follows one passage of the page "Efficient Transformers Survey"
+ * (economicspath.com), section "Linear Attention", Proposition "Linear
+ * Attention via Kernel Decomposition", or the chain rule applied to it.  Loops
+ * are written out plainly, per head, in fp64, with no blocking or reordering
+ * beyond what the cited formula states.  Heads are independent and run in
+ * parallel (OpenMP); nothing inside a head is parallel.
+ */
+#include "la_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static int g_threads = 0;
+
+void la_oracle_set_threads(int n) { g_threads = n; }
+
+int la_oracle_get_threads(void) {
+#ifdef _OPENMP
+    return g_threads > 0 ? g_threads : omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* phi(x) = elu(x) + 1 (ELU with alpha = 1): x + 1 for x > 0, exp(x) otherwise.
+ * Positive everywhere, so every denominator below is positive. */
+double la_oracle_phi(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
+
+/* d phi / dx: 1 for x > 0, exp(x) otherwise (both branches agree at 0). */
+double la_oracle_dphi(double x) { return x > 0.0 ? 1.0 : exp(x); }
+
+static double* zalloc(int64_t n) { return (double*)calloc((size_t)(n > 0 ? n : 1), sizeof(double)); }
+
+/* ---- forward, non-causal --------------------------------------------------
+ * Statement of the proposition: S = sum_j phi(K_j) V_j^T, z = sum_j phi(K_j),
+ * Attn_i = phi(Q_i)^T S / phi(Q_i)^T z. */
+static void fwd_noncausal_head(int64_t N, int64_t d, const double* q, const double* k,
+                               const double* v, double* o, double* den_out, double* S_out,
+                               double* z_out) {
+    double* S = zalloc(d * d);
+    double* z = zalloc(d);
+    double* f = zalloc(d);
+    for (int64_t j = 0; j < N; ++j) {
+        for (int64_t a = 0; a < d; ++a) f[a] = la_oracle_phi(k[j * d + a]);
+        for (int64_t a = 0; a < d; ++a) {
+            z[a] += f[a];
+            for (int64_t b = 0; b < d; ++b) S[a * d + b] += f[a] * v[j * d + b];
+        }
+    }
+    for (int64_t i = 0; i < N; ++i) {
+        for (int64_t a = 0; a < d; ++a) f[a] = la_oracle_phi(q[i * d + a]);
+        double den = 0.0;
+        for (int64_t a = 0; a < d; ++a) den += f[a] * z[a];
+        for (int64_t b = 0; b < d; ++b) {
+            double num = 0.0;
+            for (int64_t a = 0; a < d; ++a) num += f[a] * S[a * d + b];
+            o[i * d + b] = num / den;
+        }
+        if (den_out) den_out[i] = den;
+    }
+    if (S_out) memcpy(S_out, S, (size_t)(d * d) * sizeof(double));
+    if (z_out) memcpy(z_out, z, (size_t)d * sizeof(double));
+    free(S);
+    free(z);
+    free(f);
+}
+
+void la_oracle_forward_noncausal(int64_t BH, int64_t N, int64_t d, const double* q,
+                                 const double* k, const double* v, double* o, double* den_out,
+                                 double* S_out, double* z_out) {
+    int nt = la_oracle_get_threads();
+    (void)nt;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t h = 0; h < BH; ++h) {
+        const int64_t off = h * N * d;
+        fwd_noncausal_head(N, d, q + off, k + off, v + off, o + off,
+                           den_out ? den_out + h * N : NULL, S_out ? S_out + h * d * d : NULL,
+                           z_out ? z_out + h * d : NULL);
+    }
+}
+
+/* ---- forward, causal (recurrent) ------------------------------------------
+ * "Why it matters": tokens are processed one by one, S and z are updated
+ * incrementally.  Row i reads the state after token i has been added. */
+static void fwd_causal_head(int64_t N, int64_t d, const double* q, const double* k,
+                            const double* v, double* o, double* den_out, double* S_out,
+                            double* z_out) {
+    double* S = zalloc(d * d);
+    double* z = zalloc(d);
+    double* f = zalloc(d);
+    for (int64_t i = 0; i < N; ++i) {
+        for (int64_t a = 0; a < d; ++a) f[a] = la_oracle_phi(k[i * d + a]);
+        for (int64_t a = 0; a < d; ++a) {
+            z[a] += f[a];
+            for (int64_t b = 0; b < d; ++b) S[a * d + b] += f[a] * v[i * d + b];
+        }
+        for (int64_t a = 0; a < d; ++a) f[a] = la_oracle_phi(q[i * d + a]);
+        double den = 0.0;
+        for (int64_t a = 0; a < d; ++a) den += f[a] * z[a];
+        for (int64_t b = 0; b < d; ++b) {
+            double num = 0.0;
+            for (int64_t a = 0; a < d; ++a) num += f[a] * S[a * d + b];
+            o[i * d + b] = num / den;
+        }
+        if (den_out) den_out[i] = den;
+    }
+    if (S_out) memcpy(S_out, S, (size_t)(d * d) * sizeof(double));
+    if (z_out) memcpy(z_out, z, (size_t)d * sizeof(double));
+    free(S);
+    free(z);
+    free(f);
+}
+
+void la_oracle_forward_causal(int64_t BH, int64_t N, int64_t d, const double* q,
+                              const double* k, const double* v, double* o, double* den_out,
+                              double* S_out, double* z_out) {
+    int nt = la_oracle_get_threads();
+    (void)nt;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t h = 0; h < BH; ++h) {
+        const int64_t off = h * N * d;
+        fwd_causal_head(N, d, q + off, k + off, v + off, o + off,
+                        den_out ? den_out + h * N : NULL, S_out ? S_out + h * d * d : NULL,
+                        z_out ? z_out + h * d : NULL);
+    }
+}
+
+/* ---- backward --------------------------------------------------------------
+ * Chain rule through Attn_i = num_i / den_i with num_i = sum_j A_ij V_j,
+ * den_i = sum_j A_ij, A_ij = phi(Q_i) . phi(K_j) (j <= i when causal):
+ *   G_i  = dL/dnum_i = dO_i / den_i
+ *   g_i  = dL/dden_i = -(dO_i . O_i) / den_i = -G_i . O_i
+ *   dA_ij = G_i . V_j + g_i
+ *   dphi(Q_i) = sum_j dA_ij phi(K_j)  = S_i G_i + g_i z_i       (prefix state)
+ *   dphi(K_j) = sum_i dA_ij phi(Q_i)  = R_j V_j + r_j           (suffix state)
+ *   dV_j      = sum_i A_ij G_i        = R_j^T phi(K_j)
+ * with R_j = sum_{i >= j} phi(Q_i) G_i^T and r_j = sum_{i >= j} g_i phi(Q_i)
+ * (all i for the non-causal form), then dQ = dphi(Q) * phi'(Q) and
+ * dK = dphi(K) * phi'(K) elementwise. */
+static void bwd_head(int64_t N, int64_t d, int causal, const double* q, const double* k,
+                     const double* v, const double* dout, double* dq, double* dk, double* dv) {
+    double* S = zalloc(d * d);
+    double* z = zalloc(d);
+    double* R = zalloc(d * d);
+    double* r = zalloc(d);
+    double* f = zalloc(d);
+    double* kf = zalloc(d);
+    double* O = zalloc(d);
+    double* G = zalloc(N * d);
+    double* g = zalloc(N);
+
+    if (!causal) { /* global state first */
+        for (int64_t j = 0; j < N; ++j) {
+            for (int64_t a = 0; a < d; ++a) kf[a] = la_oracle_phi(k[j * d + a]);
+            for (int64_t a = 0; a < d; ++a) {
+                z[a] += kf[a];
+                for (int64_t b = 0; b < d; ++b) S[a * d + b] += kf[a] * v[j * d + b];
+            }
+        }
+    }
+    /* prefix sweep: recompute O_i, den_i from the state, then G_i, g_i, dQ_i */
+    for (int64_t i = 0; i < N; ++i) {
+        if (causal) {
+            for (int64_t a = 0; a < d; ++a) kf[a] = la_oracle_phi(k[i * d + a]);
+            for (int64_t a = 0; a < d; ++a) {
+                z[a] += kf[a];
+                for (int64_t b = 0; b < d; ++b) S[a * d + b] += kf[a] * v[i * d + b];
+            }
+        }
+        for (int64_t a = 0; a < d; ++a) f[a] = la_oracle_phi(q[i * d + a]);
+        double den = 0.0;
+        for (int64_t a = 0; a < d; ++a) den += f[a] * z[a];
+        double dot = 0.0;
+        for (int64_t b = 0; b < d; ++b) {
+            double num = 0.0;
+            for (int64_t a = 0; a < d; ++a) num += f[a] * S[a * d + b];
+            O[b] = num / den;
+            G[i * d + b] = dout[i * d + b] / den;
+            dot += G[i * d + b] * O[b];
+        }
+        g[i] = -dot;
+        for (int64_t a = 0; a < d; ++a) {
+            double s = g[i] * z[a];
+            for (int64_t b = 0; b < d; ++b) s += S[a * d + b] * G[i * d + b];
+            dq[i * d + a] = s * la_oracle_dphi(q[i * d + a]);
+        }
+    }
+    if (!causal) { /* global suffix sums */
+        for (int64_t i = 0; i < N; ++i) {
+            for (int64_t a = 0; a < d; ++a) f[a] = la_oracle_phi(q[i * d + a]);
+            for (int64_t a = 0; a < d; ++a) {
+                r[a] += g[i] * f[a];
+                for (int64_t b = 0; b < d; ++b) R[a * d + b] += f[a] * G[i * d + b];
+            }
+        }
+    }
+    /* suffix sweep: R, r accumulate rows i >= j (causal), then dK_j, dV_j */
+    for (int64_t j = N - 1; j >= 0; --j) {
+        if (causal) {
+            for (int64_t a = 0; a < d; ++a) f[a] = la_oracle_phi(q[j * d + a]);
+            for (int64_t a = 0; a < d; ++a) {
+                r[a] += g[j] * f[a];
+                for (int64_t b = 0; b < d; ++b) R[a * d + b] += f[a] * G[j * d + b];
+            }
+        }
+        for (int64_t a = 0; a < d; ++a) kf[a] = la_oracle_phi(k[j * d + a]);
+        for (int64_t a = 0; a < d; ++a) {
+            double s = r[a];
+            for (int64_t b = 0; b < d; ++b) s += R[a * d + b] * v[j * d + b];
+            dk[j * d + a] = s * la_oracle_dphi(k[j * d + a]);
+        }
+        for (int64_t b = 0; b < d; ++b) {
+            double s = 0.0;
+            for (int64_t a = 0; a < d; ++a) s += R[a * d + b] * kf[a];
+            dv[j * d + b] = s;
+        }
+    }
+    free(S);
+    free(z);
+    free(R);
+    free(r);
+    free(f);
+    free(kf);
+    free(O);
+    free(G);
+    free(g);
+}
+
+void la_oracle_backward_causal(int64_t BH, int64_t N, int64_t d, const double* q,
+                               const double* k, const double* v, const double* dout, double* dq,
+                               double* dk, double* dv) {
+    int nt = la_oracle_get_threads();
+    (void)nt;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t h = 0; h < BH; ++h) {
+        const int64_t off = h * N * d;
+        bwd_head(N, d, 1, q + off, k + off, v + off, dout + off, dq + off, dk + off, dv + off);
+    }
+}
+
+void la_oracle_backward_noncausal(int64_t BH, int64_t N, int64_t d, const double* q,
+                                  const double* k, const double* v, const double* dout, double* dq,
+                                  double* dk, double* dv) {
+    int nt = la_oracle_get_threads();
+    (void)nt;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t h = 0; h < BH; ++h) {
+        const int64_t off = h * N * d;
+        bwd_head(N, d, 0, q + off, k + off, v + off, dout + off, dq + off, dk + off, dv + off);
+    }
+}
+
+/* ---- decode ----------------------------------------------------------------
+ * One step of the recurrence: add the new token to (S, z), then read. */
+void la_oracle_decode_step(int64_t BH, int64_t d, double* S, double* z, const double* q,
+                           const double* k, const double* v, double* o) {
+    int nt = la_oracle_get_threads();
+    (void)nt;
+#pragma omp parallel for schedule(static) num_threads(nt)
+    for (int64_t h = 0; h < BH; ++h) {
+        double* Sh = S + h * d * d;
+        double* zh = z + h * d;
+        const double* qh = q + h * d;
+        const double* kh = k + h * d;
+        const double* vh = v + h * d;
+        double* oh = o + h * d;
+        for (int64_t a = 0; a < d; ++a) {
+            double kf = la_oracle_phi(kh[a]);
+            zh[a] += kf;
+            for (int64_t b = 0; b < d; ++b) Sh[a * d + b] += kf * vh[b];
+        }
+        double den = 0.0;
+        for (int64_t a = 0; a < d; ++a) den += la_oracle_phi(qh[a]) * zh[a];
+        for (int64_t b = 0; b < d; ++b) {
+            double num = 0.0;
+            for (int64_t a = 0; a < d; ++a) num += la_oracle_phi(qh[a]) * Sh[a * d + b];
+            oh[b] = num / den;
+        }
+    }
+}
+
+/* ---- quadratic forms ---------------------------------------------------------
+ * Proof sketch: Attn_i = sum_j k(Q_i,K_j) V_j / sum_j k(Q_i,K_j) with
+ * k(q,k) = phi(q) . phi(k); the n x n weights are formed explicitly. */
+static double kern(int64_t d, const double* qi, const double* kj) {
+    double s = 0.0;
+    for (int64_t a = 0; a < d; ++a) s += la_oracle_phi(qi[a]) * la_oracle_phi(kj[a]);
+    return s;
+}
+
+void la_oracle_quadratic_forward(int64_t BH, int64_t N, int64_t d, int causal, const double* q,
+                                 const double* k, const double* v, double* o, double* den_out) {
+    for (int64_t h = 0; h < BH; ++h) {
+        const double* qh = q + h * N * d;
+        const double* kh = k + h * N * d;
+        const double* vh = v + h * N * d;
+        double* oh = o + h * N * d;
+        for (int64_t i = 0; i < N; ++i) {
+            const int64_t jend = causal ? i + 1 : N;
+            double den = 0.0;
+            for (int64_t b = 0; b < d; ++b) oh[i * d + b] = 0.0;
+            for (int64_t j = 0; j < jend; ++j) {
+                double w = kern(d, qh + i * d, kh + j * d);
+                den += w;
+                for (int64_t b = 0; b < d; ++b) oh[i * d + b] += w * vh[j * d + b];
+            }
+            for (int64_t b = 0; b < d; ++b) oh[i * d + b] /= den;
+            if (den_out) den_out[h * N + i] = den;
+        }
+    }
+}
+
+/* Quadratic backward: the n x n weights A_ij and their gradient
+ * dA_ij = G_i . (V_j - O_i) are formed explicitly, then
+ * dphi(Q_i) = sum_j dA_ij phi(K_j), dphi(K_j) = sum_i dA_ij phi(Q_i),
+ * dV_j = sum_i A_ij G_i. */
+void la_oracle_quadratic_backward(int64_t BH, int64_t N, int64_t d, int causal, const double* q,
+                                  const double* k, const double* v, const double* dout, double* dq,
+                                  double* dk, double* dv) {
+    double* O = zalloc(N * d);
+    double* den = zalloc(N);
+    double* A = zalloc(N * N);
+    double* dA = zalloc(N * N);
+    for (int64_t h = 0; h < BH; ++h) {
+        const double* qh = q + h * N * d;
+        const double* kh = k + h * N * d;
+        const double* vh = v + h * N * d;
+        const double* doh = dout + h * N * d;
+        double* dqh = dq + h * N * d;
+        double* dkh = dk + h * N * d;
+        double* dvh = dv + h * N * d;
+        la_oracle_quadratic_forward(1, N, d, causal, qh, kh, vh, O, den);
+        for (int64_t i = 0; i < N; ++i)
+            for (int64_t j = 0; j < N; ++j) {
+                const int live = !causal || j <= i;
+                A[i * N + j] = live ? kern(d, qh + i * d, kh + j * d) : 0.0;
+                double s = 0.0;
+                if (live)
+                    for (int64_t b = 0; b < d; ++b)
+                        s += doh[i * d + b] / den[i] * (vh[j * d + b] - O[i * d + b]);
+                dA[i * N + j] = s;
+            }
+        for (int64_t i = 0; i < N; ++i)
+            for (int64_t a = 0; a < d; ++a) {
+                double s = 0.0;
+                for (int64_t j = 0; j < N; ++j) s += dA[i * N + j] * la_oracle_phi(kh[j * d + a]);
+                dqh[i * d + a] = s * la_oracle_dphi(qh[i * d + a]);
+            }
+        for (int64_t j = 0; j < N; ++j) {
+            for (int64_t a = 0; a < d; ++a) {
+                double s = 0.0;
+                for (int64_t i = 0; i < N; ++i) s += dA[i * N + j] * la_oracle_phi(qh[i * d + a]);
+                dkh[j * d + a] = s * la_oracle_dphi(kh[j * d + a]);
+            }
+            for (int64_t b = 0; b < d; ++b) {
+                double s = 0.0;
+                for (int64_t i = 0; i < N; ++i) s += A[i * N + j] * doh[i * d + b] / den[i];
+                dvh[j * d + b] = s;
+            }
+        }
+    }
+    free(O);
+    free(den);
+    free(A);
+    free(dA);
+}

@@ -1,0 +1,88 @@
+/*
+ * la_oracle.h -- plain, slow, fp64 CPU oracle for kernelized linear attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link or
+ * call this library; only the test-suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header or constant with the
+ * HIP library.
+ *
+ * What it computes comes from the page "Efficient Transformers Survey"
+ * (economicspath.com), section "Linear Attention", Proposition "Linear
+ * Attention via Kernel Decomposition":
+ *   - Statement:      Attn_i = phi(Q_i)^T S / phi(Q_i)^T z,
+ *                     S = sum_j phi(K_j) V_j^T (m x d), z = sum_j phi(K_j) (m).
+ *   - Proof sketch:   Attn_i = sum_j k(Q_i,K_j) V_j / sum_j k(Q_i,K_j) with
+ *                     k(q,k) = phi(q)^T phi(k)   (the quadratic form).
+ *   - Why it matters: the causal / recurrent form processes tokens one at a
+ *                     time, updating S and z incrementally.
+ * The feature map is phi(x) = elu(x) + 1 applied elementwise (so m = d); the
+ * pages leave phi abstract and this is the reading taken.  The backward pass is
+ * not written out on the pages (the arXiv 2510.21956 abstract only says one
+ * exists); it is derived from the forward by the chain rule, see
+ * la_oracle_backward_causal below.
+ *
+ * Layout: every tensor is row-major [B][H][N][d] (tokens x features per head),
+ * den is [B][H][N], a state S is [B][H][d][d] with S[a][b] (a = feature of
+ * phi(K), b = value column) and z is [B][H][d].  All arrays are double; the
+ * caller widens bf16 / fp32 inputs exactly.  Heads run in parallel under
+ * OpenMP; each head is a plain sequential loop.
+ */
+#ifndef LA_ORACLE_H
+#define LA_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* phi(x) = elu(x) + 1 and its derivative. */
+double la_oracle_phi(double x);
+double la_oracle_dphi(double x);
+
+/* Non-causal forward: global S, z over all N keys, then every row reads them.
+ * o: [BH][N][d]; S_out [BH][d][d], z_out [BH][d], den_out [BH][N] may be NULL. */
+void la_oracle_forward_noncausal(int64_t BH, int64_t N, int64_t d,
+                                 const double* q, const double* k, const double* v,
+                                 double* o, double* den_out, double* S_out, double* z_out);
+
+/* Causal forward, recurrent form: for i = 0..N-1, first S += phi(k_i) v_i^T and
+ * z += phi(k_i), then o_i = phi(q_i)^T S / phi(q_i)^T z (inclusive: row i sees
+ * keys 0..i).  S_out / z_out receive the final state; any output may be NULL
+ * except o. */
+void la_oracle_forward_causal(int64_t BH, int64_t N, int64_t d,
+                              const double* q, const double* k, const double* v,
+                              double* o, double* den_out, double* S_out, double* z_out);
+
+/* Causal backward: gradients of L = sum(dout * o) w.r.t. q, k, v for the causal
+ * forward above.  Prefix sweep gives dq, suffix sweep gives dk, dv. */
+void la_oracle_backward_causal(int64_t BH, int64_t N, int64_t d,
+                               const double* q, const double* k, const double* v,
+                               const double* dout, double* dq, double* dk, double* dv);
+
+/* Non-causal backward (same algebra with global S, z and global suffix sums). */
+void la_oracle_backward_noncausal(int64_t BH, int64_t N, int64_t d,
+                                  const double* q, const double* k, const double* v,
+                                  const double* dout, double* dq, double* dk, double* dv);
+
+/* One decode step per head, in place: S += phi(k) v^T, z += phi(k), then
+ * o = phi(q)^T S / phi(q)^T z.  S: [BH][d][d], z: [BH][d], q/k/v/o: [BH][d]. */
+void la_oracle_decode_step(int64_t BH, int64_t d, double* S, double* z,
+                           const double* q, const double* k, const double* v, double* o);
+
+/* Quadratic (brute-force) forms, O(N^2 d): the proof-sketch definition.
+ * causal != 0 restricts row i to keys j <= i.  For small inputs only. */
+void la_oracle_quadratic_forward(int64_t BH, int64_t N, int64_t d, int causal,
+                                 const double* q, const double* k, const double* v,
+                                 double* o, double* den_out);
+void la_oracle_quadratic_backward(int64_t BH, int64_t N, int64_t d, int causal,
+                                  const double* q, const double* k, const double* v,
+                                  const double* dout, double* dq, double* dk, double* dv);
+
+/* Number of OpenMP threads the oracle's parallel loops use (0 = runtime default). */
+void la_oracle_set_threads(int n);
+int la_oracle_get_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,285 @@
+"""Pins for the fp64 CPU oracle (CPU only, no GPU).
+
+The oracle computes the recurrent / state form of kernelized linear attention
+(page "Efficient Transformers Survey", section "Linear Attention", Proposition
+"Linear Attention via Kernel Decomposition").  None of these checks re-types the
+oracle's own formula: each compares it with something the pages or plain
+mathematics fix independently --
+
+  * the quadratic form of the proof sketch, written here in numpy as explicit
+    n x n weights (a different algorithm from the oracle's S/z recurrence);
+  * a hand-worked example with exact rational answers (tests/golden);
+  * closed-form special cases (constant V, constant K, N = 1, first row);
+  * invariants (convex combination, causality, Euler homogeneity, sum of dV);
+  * central finite differences of the numpy quadratic form for the backward.
+
+A dropped term, a swapped operand, an off-by-one in the causal mask, a wrong
+sign in the backward or an exclusive instead of inclusive prefix each fails at
+least one of these.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---- independent reference: the proof-sketch quadratic form in numpy --------
+def np_phi(x):
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def np_quadratic(q, k, v, causal):
+    """Attn_i = sum_j k(q_i,k_j) v_j / sum_j k(q_i,k_j), k(q,k) = phi(q).phi(k)."""
+    A = np_phi(q) @ np.swapaxes(np_phi(k), -1, -2)
+    if causal:
+        n = q.shape[-2]
+        A = A * np.tril(np.ones((n, n)))
+    den = A.sum(-1)
+    return (A @ v) / den[..., None], den
+
+
+def rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def rel(x, y):
+    return float(np.linalg.norm(x - y) / max(np.linalg.norm(y), 1e-300))
+
+
+# ---- feature map ---------------------------------------------------------------
+def test_phi_values(oracle):
+    assert oracle.phi(0.0) == 1.0
+    assert oracle.phi(1.0) == 2.0
+    assert oracle.phi(2.5) == 3.5
+    assert oracle.phi(-1.0) == pytest.approx(math.exp(-1.0), rel=1e-15)
+    assert oracle.phi(-700.0) > 0.0
+    assert oracle.dphi(3.0) == 1.0
+    assert oracle.dphi(0.0) == 1.0
+    assert oracle.dphi(-2.0) == pytest.approx(math.exp(-2.0), rel=1e-15)
+    # continuity at 0 from both sides
+    assert oracle.phi(1e-12) == pytest.approx(oracle.phi(-1e-12), abs=1e-11)
+
+
+# ---- hand-worked example -----------------------------------------------------------
+def _val(x):
+    if isinstance(x, str):
+        if x.startswith("-ln"):
+            return -math.log(float(x[3:]))
+        return float(Fraction(x))
+    return float(x)
+
+
+def _arr(rows):
+    return np.array([[_val(e) for e in r] if isinstance(r, list) else _val(r) for r in rows], dtype=np.float64)
+
+
+def test_hand_example(oracle):
+    g = json.load(open(os.path.join(GOLDEN, "hand_example.json")))
+    q, k, v, do = (_arr(g[n]) for n in ("q", "k", "v", "dout"))
+    o, den, S, z = oracle.forward_causal(q, k, v, return_den=True, return_state=True)
+    np.testing.assert_allclose(o, _arr(g["causal_o"]), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(den, _arr(g["causal_den"]), rtol=1e-13)
+    np.testing.assert_allclose(S, _arr(g["final_S"]), rtol=1e-13)
+    np.testing.assert_allclose(z, _arr(g["final_z"]), rtol=1e-13)
+    o2, den2, S2, z2 = oracle.forward_noncausal(q, k, v, return_den=True, return_state=True)
+    np.testing.assert_allclose(o2, _arr(g["noncausal_o"]), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(den2, _arr(g["noncausal_den"]), rtol=1e-13)
+    np.testing.assert_allclose(S2, _arr(g["final_S"]), rtol=1e-13)
+    np.testing.assert_allclose(z2, _arr(g["final_z"]), rtol=1e-13)
+    dq, dk, dv = oracle.backward_causal(q, k, v, do)
+    np.testing.assert_allclose(dv, _arr(g["causal_dv"]), rtol=1e-13, atol=1e-14)
+
+
+# ---- forward vs the quadratic form -------------------------------------------------
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape,scale", [((2, 3, 17, 5), 1.0), ((1, 2, 40, 8), 0.35), ((1, 1, 1, 4), 1.0)])
+def test_forward_matches_quadratic(oracle, causal, shape, scale):
+    q, k, v = rand(shape, 1, scale), rand(shape, 2, scale), rand(shape, 3)
+    ref, ref_den = np_quadratic(q, k, v, causal)
+    fn = oracle.forward_causal if causal else oracle.forward_noncausal
+    o, den = fn(q, k, v, return_den=True)
+    assert rel(o, ref) < 1e-13
+    assert rel(den, ref_den) < 1e-13
+    # the oracle's own brute force agrees as well
+    o_q, den_q = oracle.quadratic_forward(q, k, v, causal=causal, return_den=True)
+    assert rel(o_q, ref) < 1e-13 and rel(den_q, ref_den) < 1e-13
+
+
+def test_reassociation_identity():
+    """(phi(Q) phi(K)^T) V == phi(Q) (phi(K)^T V): the associativity the method rests on."""
+    q, k, v = rand((30, 6), 4), rand((30, 6), 5), rand((30, 6), 6)
+    lhs = (np_phi(q) @ np_phi(k).T) @ v
+    rhs = np_phi(q) @ (np_phi(k).T @ v)
+    assert rel(lhs, rhs) < 1e-13
+
+
+def test_state_matches_definition(oracle):
+    q, k, v = rand((2, 9, 4), 7), rand((2, 9, 4), 8), rand((2, 9, 4), 9)
+    _, S, z = oracle.forward_causal(q, k, v, return_state=True)
+    S_ref = np.einsum("hja,hjb->hab", np_phi(k), v)
+    z_ref = np_phi(k).sum(1)
+    assert rel(S, S_ref) < 1e-14 and rel(z, z_ref) < 1e-14
+    _, S2, z2 = oracle.forward_noncausal(q, k, v, return_state=True)
+    assert rel(S2, S_ref) < 1e-14 and rel(z2, z_ref) < 1e-14
+
+
+# ---- closed-form special cases ----------------------------------------------------
+@pytest.mark.parametrize("causal", [True, False])
+def test_constant_v_returns_constant(oracle, causal):
+    n, d = 23, 6
+    q, k = rand((n, d), 10), rand((n, d), 11)
+    c = rand((d,), 12)
+    v = np.tile(c, (n, 1))
+    fn = oracle.forward_causal if causal else oracle.forward_noncausal
+    o = fn(q, k, v)
+    np.testing.assert_allclose(o, v, rtol=1e-13, atol=1e-14)
+
+
+def test_constant_k_gives_prefix_mean(oracle):
+    n, d = 19, 5
+    q, v = rand((n, d), 13), rand((n, d), 14)
+    k = np.tile(rand((d,), 15), (n, 1))
+    o = oracle.forward_causal(q, k, v)
+    pm = np.cumsum(v, 0) / np.arange(1, n + 1)[:, None]
+    np.testing.assert_allclose(o, pm, rtol=1e-12, atol=1e-13)
+    o2 = oracle.forward_noncausal(q, k, v)
+    np.testing.assert_allclose(o2, np.tile(v.mean(0), (n, 1)), rtol=1e-12, atol=1e-13)
+
+
+def test_first_row_last_row_and_n1(oracle):
+    q, k, v = rand((3, 31, 7), 16), rand((3, 31, 7), 17), rand((3, 31, 7), 18)
+    oc = oracle.forward_causal(q, k, v)
+    on = oracle.forward_noncausal(q, k, v)
+    np.testing.assert_allclose(oc[:, 0], v[:, 0], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(oc[:, -1], on[:, -1], rtol=1e-12, atol=1e-13)
+    o1 = oracle.forward_causal(q[:, :1], k[:, :1], v[:, :1])
+    np.testing.assert_allclose(o1, v[:, :1], rtol=1e-13, atol=1e-14)
+
+
+def test_convex_combination(oracle):
+    """phi > 0, so every output row is a convex combination of the value rows it sees."""
+    n, d = 40, 4
+    q, k, v = rand((n, d), 19, 2.0), rand((n, d), 20, 2.0), rand((n, d), 21)
+    o = oracle.forward_causal(q, k, v)
+    for i in range(n):
+        lo, hi = v[: i + 1].min(0), v[: i + 1].max(0)
+        assert np.all(o[i] >= lo - 1e-12) and np.all(o[i] <= hi + 1e-12)
+
+
+def test_causality_nan_in_future(oracle):
+    n, d, cut = 20, 4, 11
+    q, k, v = rand((n, d), 22), rand((n, d), 23), rand((n, d), 24)
+    o = oracle.forward_causal(q, k, v)
+    k2, v2 = k.copy(), v.copy()
+    k2[cut + 1:] = np.nan
+    v2[cut + 1:] = np.inf
+    o2 = oracle.forward_causal(q, k2, v2)
+    np.testing.assert_array_equal(o2[: cut + 1], o[: cut + 1])
+    assert not np.isfinite(o2[cut + 1:]).any()
+
+
+# ---- backward ----------------------------------------------------------------------------
+def _fd_grads(q, k, v, do, causal, h=1e-6):
+    def loss(q_, k_, v_):
+        return float((np_quadratic(q_, k_, v_, causal)[0] * do).sum())
+
+    grads = []
+    for which in range(3):
+        args = [q.copy(), k.copy(), v.copy()]
+        g = np.zeros_like(args[which])
+        it = np.nditer(g, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            plus = [a.copy() for a in args]
+            minus = [a.copy() for a in args]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            g[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_finite_differences(oracle, causal):
+    n, d = 12, 5
+    q, k, v, do = rand((n, d), 25), rand((n, d), 26), rand((n, d), 27), rand((n, d), 28)
+    fd = _fd_grads(q, k, v, do, causal)
+    fn = oracle.backward_causal if causal else oracle.backward_noncausal
+    got = fn(q, k, v, do)
+    for name, g, f in zip(("dq", "dk", "dv"), got, fd):
+        assert rel(g, f) < 1e-7, name
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_matches_quadratic_backward(oracle, causal):
+    shape = (2, 2, 21, 6)
+    q, k, v, do = rand(shape, 29, 0.5), rand(shape, 30, 0.5), rand(shape, 31), rand(shape, 32)
+    fn = oracle.backward_causal if causal else oracle.backward_noncausal
+    got = fn(q, k, v, do)
+    ref = oracle.quadratic_backward(q, k, v, do, causal=causal)
+    for g, r in zip(got, ref):
+        assert rel(g, r) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_invariants(oracle, causal):
+    n, d = 33, 6
+    q, k, v, do = rand((n, d), 33), rand((n, d), 34), rand((n, d), 35), rand((n, d), 36)
+    fn = oracle.backward_causal if causal else oracle.backward_noncausal
+    dq, dk, dv = fn(q, k, v, do)
+    # shifting every value row by c shifts every output row by c
+    np.testing.assert_allclose(dv.sum(0), do.sum(0), rtol=1e-11, atol=1e-12)
+    # each O_i is homogeneous of degree 0 in phi(Q_i): sum_a dphi(Q)_ia phi(Q_ia) = 0
+    dqf = dq / np.where(q > 0, 1.0, np.exp(np.minimum(q, 0)))
+    euler_q = (dqf * np_phi(q)).sum(1)
+    assert np.abs(euler_q).max() < 1e-11 * max(1.0, np.abs(dqf).max())
+    # ... and of degree 0 in all phi(K_j) jointly
+    dkf = dk / np.where(k > 0, 1.0, np.exp(np.minimum(k, 0)))
+    assert abs((dkf * np_phi(k)).sum()) < 1e-10 * max(1.0, np.abs(dkf).max())
+
+
+def test_constant_v_zero_grads(oracle):
+    n, d = 17, 4
+    q, k, do = rand((n, d), 37), rand((n, d), 38), rand((n, d), 39)
+    v = np.tile(rand((d,), 40), (n, 1))
+    dq, dk, dv = oracle.backward_causal(q, k, v, do)
+    assert np.abs(dq).max() < 1e-12 and np.abs(dk).max() < 1e-12
+
+
+# ---- decode --------------------------------------------------------------------------------
+def test_decode_reproduces_causal_rows(oracle):
+    bh, n, d = 3, 14, 5
+    q, k, v = rand((bh, n, d), 41), rand((bh, n, d), 42), rand((bh, n, d), 43)
+    o_ref, S_ref, z_ref = oracle.forward_causal(q, k, v, return_state=True)
+    S, z = np.zeros((bh, d, d)), np.zeros((bh, d))
+    for t in range(n):
+        o, S, z = oracle.decode_step(S, z, q[:, t], k[:, t], v[:, t])
+        np.testing.assert_allclose(o, o_ref[:, t], rtol=1e-12, atol=1e-13)
+    _, S_nc, z_nc = oracle.forward_noncausal(q, k, v, return_state=True)
+    assert rel(S, S_ref) < 1e-13 and rel(S, S_nc) < 1e-13 and rel(z, z_nc) < 1e-13
+
+
+def test_decode_from_prefix_state(oracle):
+    bh, n, d = 2, 10, 4
+    q, k, v = rand((bh, n + 1, d), 44), rand((bh, n + 1, d), 45), rand((bh, n + 1, d), 46)
+    _, S0, z0 = oracle.forward_causal(q[:, :n], k[:, :n], v[:, :n], return_state=True)
+    o, _, _ = oracle.decode_step(S0, z0, q[:, n], k[:, n], v[:, n])
+    full = oracle.forward_causal(q, k, v)
+    np.testing.assert_allclose(o, full[:, n], rtol=1e-12, atol=1e-13)
+
+
+def test_thread_count_does_not_change_results(oracle):
+    shape = (4, 3, 25, 6)
+    q, k, v, do = rand(shape, 47), rand(shape, 48), rand(shape, 49), rand(shape, 50)
+    oracle.set_threads(1)
+    a = oracle.backward_causal(q, k, v, do)
+    oracle.set_threads(4)
+    b = oracle.backward_causal(q, k, v, do)
+    oracle.set_threads(0)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
