@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Benchmark of the kernelized linear-attention hot path on one MI355X.
+
+A step is one causal forward plus one causal backward (la_forward_causal +
+la_backward_causal through the C ABI) over the workload B=4, H=16, N=4096,
+d=64, bf16 inputs ~ N(0,1)/sqrt(d), chunk 64.  W untimed warmup steps, then K
+steps timed back to back between two device synchronisations.  Inputs are
+resident in HBM before the timed region; the step rotates over several input
+sets whose total exceeds the 256 MB last-level cache, so each step starts with
+its inputs in HBM, not in cache.
+
+The JSON line also carries
+  * roofline    : the dominant kernel's algorithmic bytes per launch over its
+                  average duration (HIP events around every launch, recorded
+                  on the library's stream during the timed steps) against the
+                  8 TB/s HBM peak;
+  * step_roofline: the same for the whole step (22 d bytes per token-head);
+  * calls       : the other measured calls (non-causal forward at the same
+                  size, the long and very-long causal workloads, 512 decode
+                  steps), each with its throughput and roofline fraction;
+  * cpu_baseline: the fp64 CPU oracle timed on this host on repeated full
+                  steps of the same workload (bounded to about 10 s).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-calls] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+LLC_BYTES = 256 * 2**20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-calls", action="store_true", help="skip the other calls")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def kernel_stats(entries):
+    """{name: (launches, total ms)} from the library's per-launch events."""
+    out = {}
+    for name, ms in entries:
+        n, t = out.get(name, (0, 0.0))
+        out[name] = (n + 1, t + ms)
+    return out
+
+
+def unit_bytes(B, H, N, d, esize=2):
+    return B * H * N * d * esize
+
+
+# Algorithmic bytes per launch of each kernel, in [B,H,N,d] tensors read or
+# written through the ABI (workspace traffic is not algorithmic).
+KERNEL_UNITS = {"seg_state": 2, "causal_fwd": 4, "noncausal_fwd": 2, "bwd_prefix": 5, "bwd_suffix": 6}
+
+
+def sequence_roofline(stats, B, H, N, d, steps):
+    name = max(stats, key=lambda k: stats[k][1])
+    n, tot = stats[name]
+    avg_s = tot / n * 1e-3
+    units = KERNEL_UNITS.get(name)
+    if units is None:
+        return name, None
+    alg = units * unit_bytes(B, H, N, d)
+    ach = alg / avg_s / 1e9
+    return name, {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                  "kernel": name, "launches": n, "avg_us": round(avg_s * 1e6, 2),
+                  "alg_bytes_per_launch": alg}
+
+
+def time_steps(fn, nsets, warmup, steps, la, torch):
+    for i in range(warmup):
+        fn(i % nsets)
+    torch.cuda.synchronize()
+    la.profile_enable(True)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i % nsets)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    stats = kernel_stats(la.profile_entries())
+    la.profile_enable(False)
+    return dt, stats
+
+
+def bench_mid(args, la, inp, torch):
+    w = inp.MID
+    B, H, N, d = w.B, w.H, w.N, w.d
+    per_set = 4 * unit_bytes(B, H, N, d)
+    nsets = max(2, math.ceil(2 * LLC_BYTES / per_set))
+    sets = [inp.workload_inputs(w, seed=s, device="cuda", with_dout=True) for s in range(nsets)]
+    o = torch.empty_like(sets[0][0])
+    grads = tuple(torch.empty_like(sets[0][0]) for _ in range(3))
+    wsf = torch.empty(la.workspace_size(la.LA_OP_FWD_CAUSAL, B, H, N, d, w.dtype), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(la.workspace_size(la.LA_OP_BWD_CAUSAL, B, H, N, d, w.dtype), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        q, k, v, do = sets[i]
+        la.la_forward_causal(q, k, v, out=o, workspace=wsf)
+        la.la_backward_causal(q, k, v, do, out=grads, workspace=wsb)
+
+    dt, stats = time_steps(step, nsets, args.warmup, args.steps, la, torch)
+    T = B * H * N
+    step_s = dt / args.steps
+    step_bytes = 11 * unit_bytes(B, H, N, d)
+    flops = 14 * d * d * T
+    kname, roof = sequence_roofline(stats, B, H, N, d, args.steps)
+    return {
+        "value": B * N * args.steps / dt,
+        "ms_per_step": step_s * 1e3,
+        "roofline": roof,
+        "step_roofline": {"bound": "hbm", "alg_bytes": step_bytes,
+                          "achieved": round(step_bytes / step_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                          "frac": round(step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+                          "alg_tflops": round(flops / step_s / 1e12, 2),
+                          "mfma_frac": round(flops / step_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},
+        "kernels_us": {k: round(t / n * 1e3, 2) for k, (n, t) in sorted(stats.items())},
+        "input_sets": nsets,
+    }, sets[0]
+
+
+def bench_call(name, fn, warmup, steps, tokens, alg_bytes, la, torch, nsets=1):
+    dt, stats = time_steps(fn, nsets, warmup, steps, la, torch)
+    s = dt / steps
+    return {"tokens_per_s": round(tokens / s, 1), "ms": round(s * 1e3, 4),
+            "alg_bytes": alg_bytes, "achieved_GBs": round(alg_bytes / s / 1e9, 1),
+            "hbm_frac": round(alg_bytes / s / 1e9 / HBM_PEAK_GBS, 4),
+            "kernels_us": {k: round(t / n * 1e3, 2) for k, (n, t) in sorted(stats.items())}}
+
+
+def bench_calls(args, la, inp, torch, mid_set):
+    calls = {}
+    w = inp.MID
+    q, k, v, _ = mid_set
+    o = torch.empty_like(q)
+    ws = torch.empty(la.workspace_size(la.LA_OP_FWD_NONCAUSAL, w.B, w.H, w.N, w.d, w.dtype), dtype=torch.uint8,
+                     device="cuda")
+    calls["mid_noncausal_fwd"] = bench_call(
+        "noncausal", lambda i: la.la_forward_noncausal(q, k, v, out=o, workspace=ws), 5, 20, w.B * w.N,
+        4 * unit_bytes(w.B, w.H, w.N, w.d), la, torch)
+    del o, ws
+
+    w = inp.LONG
+    q, k, v, do = inp.workload_inputs(w, seed=0, device="cuda", with_dout=True)
+    o = torch.empty_like(q)
+    g = tuple(torch.empty_like(q) for _ in range(3))
+    wsf = torch.empty(la.workspace_size(la.LA_OP_FWD_CAUSAL, w.B, w.H, w.N, w.d, w.dtype), dtype=torch.uint8,
+                      device="cuda")
+    wsb = torch.empty(la.workspace_size(la.LA_OP_BWD_CAUSAL, w.B, w.H, w.N, w.d, w.dtype), dtype=torch.uint8,
+                      device="cuda")
+
+    def long_step(i):
+        la.la_forward_causal(q, k, v, out=o, workspace=wsf)
+        la.la_backward_causal(q, k, v, do, out=g, workspace=wsb)
+
+    calls["long_causal_fwd_bwd"] = bench_call("long", long_step, 2, 10, w.B * w.N,
+                                              11 * unit_bytes(w.B, w.H, w.N, w.d), la, torch)
+    del q, k, v, do, o, g, wsf, wsb
+
+    w = inp.VERYLONG
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    q, k, v = inp.workload_inputs(w, seed=0, device="cuda", with_dout=False)
+    o = torch.empty_like(q)
+    wsf = torch.empty(la.workspace_size(la.LA_OP_FWD_CAUSAL, w.B, w.H, w.N, w.d, w.dtype), dtype=torch.uint8,
+                      device="cuda")
+    r = bench_call("verylong", lambda i: la.la_forward_causal(q, k, v, out=o, workspace=wsf), 2, 10, w.B * w.N,
+                   4 * unit_bytes(w.B, w.H, w.N, w.d), la, torch)
+    r["peak_mem_bytes"] = int(torch.cuda.max_memory_allocated() - base)
+    r["workspace_bytes"] = int(wsf.numel())
+    r["state_bytes_per_head"] = (w.d * w.d + w.d) * 4
+    r["softmax_matrix_bytes_per_head_bf16"] = w.N * w.N * 2
+    calls["verylong_causal_fwd"] = r
+    del q, k, v, o, wsf
+
+    w = inp.DECODE
+    B, H, d = w.batch, w.H, w.d
+    S = torch.empty(B, H, d, d, device="cuda")
+    z = torch.empty(B, H, d, device="cuda")
+    nb = 32
+    for b0 in range(0, B, nb):
+        pq, pk, pv = inp.qkv(nb, H, w.prefix, d, w.dtype, seed=1000 + b0, device="cuda")
+        _, Sb, zb = la.la_forward_causal(pq, pk, pv, return_state=True)
+        S[b0:b0 + nb].copy_(Sb)
+        z[b0:b0 + nb].copy_(zb)
+        del pq, pk, pv
+    sq, sk, sv = inp.decode_tokens(B, H, d, w.steps, w.dtype, seed=2, device="cuda")
+    od = torch.empty(B, H, d, dtype=w.dtype, device="cuda")
+
+    def span(i):
+        for t in range(w.steps):
+            la.la_decode_step(S, z, sq[t], sk[t], sv[t], out=od)
+
+    step_bytes = B * H * (2 * 4 * d * d + 2 * 4 * d + 4 * 2 * d)
+    r = bench_call("decode", span, 1, 3, B * w.steps, step_bytes * w.steps, la, torch)
+    r["tokens_per_s"] = r.pop("tokens_per_s")
+    r["us_per_step"] = round(r["ms"] * 1e3 / w.steps, 2)
+    r["alg_bytes_per_step"] = step_bytes
+    calls["decode_512_steps"] = r
+    return calls
+
+
+def cpu_baseline(args, inp, torch, mid_set):
+    import oracle
+
+    w = inp.MID
+    q, k, v, do = (inp.to_f64(t) for t in mid_set)
+    cores = len(os.sched_getaffinity(0))
+    cores = min(cores, 16)
+    oracle.set_threads(cores)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.forward_causal(q, k, v)
+        oracle.backward_causal(q, k, v, do)
+        reps += 1
+        if time.perf_counter() - t0 >= args.cpu_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(reps * w.B * w.N / dt, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} full causal fwd+bwd steps of B4 H16 N4096 d64 (all 64 heads), fp64, "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import la_inputs as inp
+    import linear_attention_02_amd as la
+
+    la.load_library()
+    torch.cuda.set_device(0)
+    res, mid_set = bench_mid(args, la, inp, torch)
+    calls = None if args.no_calls else bench_calls(args, la, inp, torch, mid_set)
+    cpu = None if args.no_cpu else cpu_baseline(args, inp, torch, mid_set)
+    line = {
+        "metric": "causal LA fwd+bwd tokens/s, B4 H16 N4096 d64 bf16; % of HBM/MFMA roofline",
+        "value": round(res["value"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal linear attention fwd+bwd, B4 H16 N4096 d64, bf16 in / fp32 accumulate, "
+                               "phi = elu+1, chunk 64", "global_batch": 4, "seq_len": 4096, "heads": 16,
+                   "head_dim": 64, "parallelism": "single GPU"},
+        "roofline": res["roofline"],
+        "step_roofline": res["step_roofline"],
+        "kernels_us": res["kernels_us"],
+        "calls": calls,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,137 @@
+/*
+ * linattn.h -- C ABI of the MI355X (gfx950) kernelized linear-attention library.
+ *
+ * The operation is the one stated on the page "Efficient Transformers Survey"
+ * (economicspath.com), section "Linear Attention", Proposition "Linear
+ * Attention via Kernel Decomposition":
+ *
+ *     Attn_i = phi(Q_i)^T S / phi(Q_i)^T z,
+ *     S = sum_j phi(K_j) V_j^T  (m x d),   z = sum_j phi(K_j)  (m),
+ *
+ * evaluated in O(N m d) by reassociating (phi(Q) phi(K)^T) V as
+ * phi(Q) (phi(K)^T V) ("Intuition" of the same proposition; also the page on
+ * memory-efficient Transformers at blopig.com, "Softmax approximators").  The
+ * causal form updates S and z token by token ("Why It Matters"), so row i reads
+ * keys 0..i inclusive.  The feature map is phi(x) = elu(x) + 1 elementwise, so
+ * m = d.  No 1/sqrt(d) scale is applied inside: the formula has none, callers
+ * scale Q or K themselves.  No epsilon is added to the denominator: phi > 0.
+ *
+ * Conventions for every call
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays,
+ *     aligned to 16 bytes.  Q, K, V, O, dO, dQ, dK, dV are [B][H][N][d];
+ *     den is [B][H][N] fp32; a state S is [B][H][d][d] fp32 with S[a][b]
+ *     (a = feature of phi(K), b = value column); z is [B][H][d] fp32.
+ *   - dtype is LA_BF16 (bf16 inputs/outputs, fp32 accumulation and state) or
+ *     LA_F32 (fp32 everywhere).  Outputs take the input dtype, rounded to
+ *     nearest-even from fp32.
+ *   - d must be 32, 64 or 128; B, H, N >= 1 (N = 0 is accepted and does
+ *     nothing).  chunk is 0 (default) or 64.
+ *   - The caller owns every buffer, including the workspace, whose size comes
+ *     from la_workspace_size().  The library never allocates or frees device
+ *     memory and keeps no device state between calls.
+ *   - Outputs may not overlap inputs (decode's S and z are in/out by design).
+ *   - stream is a hipStream_t (NULL = the default stream).  Every call is
+ *     stream-ordered and returns without synchronising the host.
+ *   - Every call validates its arguments before launching anything and never
+ *     throws.  A non-OK status leaves outputs untouched;
+ *     la_last_error_message() gives a thread-local description.  Device-side
+ *     faults surface at the caller's next synchronisation.
+ *   - Results are deterministic: the same inputs give bitwise-identical
+ *     outputs (fixed-order reductions, no floating-point atomics).
+ *   - Non-finite inputs: rows never read keys from later chunks of 64 tokens,
+ *     but a NaN/Inf value row can reach earlier rows of its own chunk through
+ *     the masked in-chunk product.  Inputs are expected to be finite.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misalignment, overlap */
+    LA_ERR_UNSUPPORTED = 2,      /* d, chunk or dtype outside what is built */
+    LA_ERR_WORKSPACE = 3,        /* workspace missing or smaller than la_workspace_size() */
+    LA_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+} la_status;
+
+typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+typedef enum { LA_OP_FWD_NONCAUSAL = 0, LA_OP_FWD_CAUSAL = 1, LA_OP_BWD_CAUSAL = 2 } la_op;
+
+/* Bytes of device workspace that `op` needs for this shape (0 is possible).
+ * Pure host computation; no device is touched. */
+la_status la_workspace_size(la_op op, int64_t B, int64_t H, int64_t N, int64_t d, int chunk,
+                            la_dtype dt, size_t* bytes_out);
+
+/* Non-causal forward (Statement of the proposition): one reduction of
+ * S = sum_j phi(K_j) V_j^T and z = sum_j phi(K_j) over all N keys per head,
+ * then O_i = phi(Q_i)^T S / phi(Q_i)^T z for every row.
+ * In: q, k, v [B][H][N][d].  Out: o [B][H][N][d]. */
+la_status la_forward_noncausal(const void* q, const void* k, const void* v, void* o, int64_t B,
+                               int64_t H, int64_t N, int64_t d, la_dtype dt, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Causal forward (the recurrent form of "Why It Matters", evaluated chunk by
+ * chunk): O_i = phi(Q_i)^T S_i / phi(Q_i)^T z_i with S_i, z_i summed over keys
+ * j <= i.  Optional outputs (NULL to skip): den_out [B][H][N] fp32 holds
+ * phi(Q_i)^T z_i; S_out [B][H][d][d] and z_out [B][H][d] receive the state
+ * after the last token, ready for la_decode_step. */
+la_status la_forward_causal(const void* q, const void* k, const void* v, void* o, float* den_out,
+                            float* S_out, float* z_out, int64_t B, int64_t H, int64_t N, int64_t d,
+                            int chunk, la_dtype dt, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Causal backward: dQ, dK, dV of L = sum(dO * O) for the causal forward, by
+ * the chain rule (the arXiv 2510.21956 abstract on vix.ing states that a
+ * forward and backward pass exist; the formulas are derived, not printed):
+ *   G_i = dO_i / den_i, g_i = -G_i . O_i,
+ *   dphi(Q_i) = S_i G_i + g_i z_i,
+ *   dphi(K_j) = R_j V_j + r_j, dV_j = R_j^T phi(K_j),
+ *   R_j = sum_{i>=j} phi(Q_i) G_i^T, r_j = sum_{i>=j} g_i phi(Q_i),
+ * then dQ = dphi(Q) * phi'(Q), dK = dphi(K) * phi'(K).  O and den are
+ * recomputed in fp32 from q, k, v; the forward's outputs are not inputs here.
+ * In: q, k, v, dout [B][H][N][d].  Out: dq, dk, dv [B][H][N][d]. */
+la_status la_backward_causal(const void* q, const void* k, const void* v, const void* dout,
+                             void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
+                             int64_t d, int chunk, la_dtype dt, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* One recurrent decode step per (b, h), in place ("Why It Matters": constant
+ * memory per step): S += phi(k) v^T, z += phi(k), then
+ * o = phi(q)^T S / phi(q)^T z.  S [B][H][d][d] and z [B][H][d] are fp32 and
+ * updated in place; q, k, v, o are [B][H][d] in dtype dt.  Needs no workspace. */
+la_status la_decode_step(float* S, float* z, const void* q, const void* k, const void* v, void* o,
+                         int64_t B, int64_t H, int64_t d, la_dtype dt, void* stream);
+
+/* Static description of a status code. */
+const char* la_status_string(la_status s);
+
+/* Thread-local description of the last non-OK status returned on this thread. */
+const char* la_last_error_message(void);
+
+/* Library version string. */
+const char* la_version(void);
+
+/* Per-kernel timing for benchmarks and profiling.  While enabled (on != 0) on
+ * the calling thread, every kernel that a call on this thread launches is
+ * bracketed by two HIP events recorded on the call's stream; enabling or
+ * disabling clears the list.  Events come from a per-thread pool that the
+ * library creates once with hipEventCreate and reuses (no device memory).
+ * la_profile_count() is the number of launches recorded since; entry i
+ * synchronises on its stop event and returns the kernel's name ("seg_state",
+ * "scan", "causal_fwd", "noncausal_fwd", "final_state", "bwd_prefix", "rscan",
+ * "bwd_suffix", "decode", "fill_zero") and its duration in milliseconds. */
+la_status la_profile_enable(int on);
+int la_profile_count(void);
+la_status la_profile_entry(int i, const char** name, float* ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LINATTN_H */

@@ -1,0 +1,27 @@
+"""MI355X (gfx950) kernelized linear attention.
+
+The compute path is the HIP library ``liblinattn.so`` (C ABI in
+``include/linattn.h``); this package is its thin Python binding.  PyTorch is
+used only for device memory and the current stream.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    LA_BF16,
+    LA_F32,
+    LA_OP_BWD_CAUSAL,
+    LA_OP_FWD_CAUSAL,
+    LA_OP_FWD_NONCAUSAL,
+    LIB_PATH,
+    LinAttnError,
+    causal_linear_attention,
+    la_backward_causal,
+    la_decode_step,
+    la_forward_causal,
+    la_forward_noncausal,
+    load_library,
+    profile_enable,
+    profile_entries,
+    workspace_size,
+)
+
+__version__ = "0.1.0"

@@ -1,0 +1,225 @@
+"""ctypes binding of ``liblinattn.so`` (the C ABI in include/linattn.h).
+
+Argument marshalling only: tensors are checked, outputs and the workspace are
+allocated with ``torch.empty`` on the inputs' device, and the raw device
+pointers plus the current HIP stream are handed to the library.  Every step of
+the computation runs in the library's gfx950 kernels; there is no fallback,
+and a missing or unloadable library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblinattn.so")
+
+LA_OK, LA_ERR_INVALID_ARGUMENT, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = range(5)
+LA_F32, LA_BF16 = 0, 1
+LA_OP_FWD_NONCAUSAL, LA_OP_FWD_CAUSAL, LA_OP_BWD_CAUSAL = 0, 1, 2
+
+EXPORTS = ("la_workspace_size", "la_forward_noncausal", "la_forward_causal", "la_backward_causal",
+           "la_decode_step", "la_status_string", "la_last_error_message", "la_version",
+           "la_profile_enable", "la_profile_count", "la_profile_entry")
+
+_lib = None
+
+
+class LinAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(message)
+
+
+def load_library(path: str | None = None):
+    """Load liblinattn.so (raises if it is missing; the library is never replaced by Python code)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+                          "or `python -m linear_attention_02_amd._build`")
+    lib = ctypes.CDLL(p)
+    i64, sz, vp, i32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
+    lib.la_workspace_size.restype = i32
+    lib.la_workspace_size.argtypes = [i32, i64, i64, i64, i64, i32, i32, ctypes.POINTER(sz)]
+    lib.la_forward_noncausal.restype = i32
+    lib.la_forward_noncausal.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]
+    lib.la_forward_causal.restype = i32
+    lib.la_forward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.la_backward_causal.restype = i32
+    lib.la_backward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.la_decode_step.restype = i32
+    lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.la_status_string.restype = ctypes.c_char_p
+    lib.la_status_string.argtypes = [i32]
+    lib.la_last_error_message.restype = ctypes.c_char_p
+    lib.la_last_error_message.argtypes = []
+    lib.la_version.restype = ctypes.c_char_p
+    lib.la_version.argtypes = []
+    lib.la_profile_enable.restype = i32
+    lib.la_profile_enable.argtypes = [i32]
+    lib.la_profile_count.restype = i32
+    lib.la_profile_count.argtypes = []
+    lib.la_profile_entry.restype = i32
+    lib.la_profile_entry.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float)]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != LA_OK:
+        lib = load_library()
+        name = lib.la_status_string(status).decode()
+        msg = lib.la_last_error_message().decode()
+        raise LinAttnError(status, f"{name}: {msg}")
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return LA_BF16
+    if dt == torch.float32:
+        return LA_F32
+    raise ValueError(f"unsupported dtype {dt}; use torch.bfloat16 or torch.float32")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_seq(*ts):
+    ref = ts[0]
+    if ref.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    for t in ts:
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("q, k, v (and dout) must share shape, dtype and device")
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a HIP device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return ref.shape
+
+
+def workspace_size(op: int, B: int, H: int, N: int, d: int, dtype: torch.dtype, chunk: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().la_workspace_size(op, B, H, N, d, chunk, _dtype_code(dtype), ctypes.byref(out)))
+    return int(out.value)
+
+
+def _workspace(op, B, H, N, d, dtype, device, chunk, workspace):
+    need = workspace_size(op, B, H, N, d, dtype, chunk)
+    if workspace is not None:
+        return workspace
+    if need == 0:
+        return None
+    return torch.empty(need, dtype=torch.uint8, device=device)
+
+
+def la_forward_noncausal(q, k, v, *, out=None, workspace=None):
+    """O_i = phi(Q_i)^T S / phi(Q_i)^T z with S, z over all keys.  q, k, v: [B, H, N, d]."""
+    B, H, N, d = _check_seq(q, k, v)
+    o = torch.empty_like(q) if out is None else out
+    ws = _workspace(LA_OP_FWD_NONCAUSAL, B, H, N, d, q.dtype, q.device, 0, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().la_forward_noncausal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d,
+                                               _dtype_code(q.dtype), _ptr(ws), nbytes, _stream(q.device)))
+    return o
+
+
+def la_forward_causal(q, k, v, *, chunk=0, return_den=False, return_state=False, out=None, workspace=None):
+    """Causal forward; returns o, plus den [B,H,N] and/or the final (S [B,H,d,d], z [B,H,d]) if asked."""
+    B, H, N, d = _check_seq(q, k, v)
+    o = torch.empty_like(q) if out is None else out
+    den = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_den else None
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device) if return_state else None
+    z = torch.empty((B, H, d), dtype=torch.float32, device=q.device) if return_state else None
+    ws = _workspace(LA_OP_FWD_CAUSAL, B, H, N, d, q.dtype, q.device, chunk, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().la_forward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den), _ptr(S), _ptr(z),
+                                            B, H, N, d, chunk, _dtype_code(q.dtype), _ptr(ws), nbytes,
+                                            _stream(q.device)))
+    res = [o]
+    if return_den:
+        res.append(den)
+    if return_state:
+        res += [S, z]
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def la_backward_causal(q, k, v, dout, *, chunk=0, out=None, workspace=None):
+    """Gradients (dq, dk, dv) of sum(dout * la_forward_causal(q, k, v))."""
+    B, H, N, d = _check_seq(q, k, v, dout)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    else:
+        dq, dk, dv = out
+    ws = _workspace(LA_OP_BWD_CAUSAL, B, H, N, d, q.dtype, q.device, chunk, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().la_backward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                             B, H, N, d, chunk, _dtype_code(q.dtype), _ptr(ws), nbytes,
+                                             _stream(q.device)))
+    return dq, dk, dv
+
+
+def la_decode_step(S, z, q, k, v, *, out=None):
+    """One in-place recurrent step: S += phi(k) v^T, z += phi(k); returns o = phi(q)^T S / phi(q)^T z.
+
+    S: [B, H, d, d] fp32, z: [B, H, d] fp32, q/k/v: [B, H, d] bf16 or fp32 (contiguous, same device)."""
+    if q.dim() != 3:
+        raise ValueError("q, k, v must be [B, H, d]")
+    B, H, d = q.shape
+    for t in (k, v):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
+            raise ValueError("q, k, v must share shape, dtype and device and be contiguous")
+    if S.shape != (B, H, d, d) or z.shape != (B, H, d) or S.dtype != torch.float32 or z.dtype != torch.float32:
+        raise ValueError("S must be [B, H, d, d] fp32 and z [B, H, d] fp32")
+    if not (S.is_contiguous() and z.is_contiguous() and q.is_contiguous()):
+        raise ValueError("tensors must be contiguous")
+    if not q.is_cuda:
+        raise ValueError("tensors must be on a HIP device")
+    o = torch.empty_like(q) if out is None else out
+    _check(load_library().la_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, d,
+                                         _dtype_code(q.dtype), _stream(q.device)))
+    return o
+
+
+def profile_enable(on: bool = True) -> None:
+    """Start (or stop) recording HIP events around every kernel this thread's calls launch."""
+    _check(load_library().la_profile_enable(1 if on else 0))
+
+
+def profile_entries():
+    """[(kernel name, milliseconds)] for the launches recorded since profile_enable()."""
+    lib = load_library()
+    out = []
+    name, ms = ctypes.c_char_p(), ctypes.c_float()
+    for i in range(lib.la_profile_count()):
+        _check(lib.la_profile_entry(i, ctypes.byref(name), ctypes.byref(ms)))
+        out.append((name.value.decode(), float(ms.value)))
+    return out
+
+
+class _CausalLinearAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v):
+        ctx.save_for_backward(q, k, v)
+        return la_forward_causal(q, k, v)
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v = ctx.saved_tensors
+        return la_backward_causal(q, k, v, dout.contiguous())
+
+
+def causal_linear_attention(q, k, v):
+    """Autograd-aware causal linear attention (forward and backward both run the HIP kernels)."""
+    return _CausalLinearAttention.apply(q, k, v)

@@ -1,0 +1,367 @@
+// api.cpp -- the C ABI (include/linattn.h): argument validation, workspace
+// layout and kernel sequencing.  No device memory is allocated here; every
+// launch goes on the caller's stream.
+#include "linattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+la_status fail(la_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+la_status fail(la_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+la_status hip_fail(hipError_t e, const char* what) {
+    return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---- optional per-kernel timing (benchmarks) ---------------------------------------------
+// While enabled on a thread, every kernel launched by a call on that thread is
+// bracketed by two HIP events on its stream.  Events come from a per-thread
+// pool that is created once and reused; nothing is allocated on the device.
+struct KernelTiming {
+    bool on = false;
+    std::vector<hipEvent_t> pool;  // 2 events per record
+    std::vector<const char*> names;
+    size_t used = 0;               // records in use
+};
+thread_local KernelTiming g_timing;
+
+struct Timed {
+    hipStream_t s;
+    hipEvent_t stop = nullptr;
+    Timed(const char* name, hipStream_t stream) : s(stream) {
+        KernelTiming& T = g_timing;
+        if (!T.on) return;
+        if (2 * (T.used + 1) > T.pool.size()) {
+            hipEvent_t a = nullptr, b = nullptr;
+            if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return;
+            T.pool.push_back(a);
+            T.pool.push_back(b);
+        }
+        if (T.names.size() < T.used + 1) T.names.resize(T.used + 1);
+        T.names[T.used] = name;
+        hipEventRecord(T.pool[2 * T.used], s);
+        stop = T.pool[2 * T.used + 1];
+        ++T.used;
+    }
+    ~Timed() {
+        if (stop != nullptr) hipEventRecord(stop, s);
+    }
+};
+
+template <class F>
+hipError_t timed(const char* name, hipStream_t s, F&& f) {
+    Timed t(name, s);
+    return f();
+}
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    const char* name;
+    const void* p;
+    size_t bytes;
+};
+
+bool overlap(const Range& a, const Range& b) {
+    if (a.p == nullptr || b.p == nullptr || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+size_t elem_size(la_dtype dt) { return dt == LA_BF16 ? 2 : 4; }
+
+// Shape checks common to the sequence calls.  Sets *empty when there is no work.
+la_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt, bool* empty) {
+    if (dt != LA_F32 && dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "dtype %d is not LA_F32 or LA_BF16", (int)dt);
+    if (d != 32 && d != 64 && d != 128) return fail(LA_ERR_UNSUPPORTED, "d = %lld; built for 32, 64 and 128", (long long)d);
+    if (chunk != 0 && chunk != la::kChunk)
+        return fail(LA_ERR_UNSUPPORTED, "chunk = %d; only 0 (default) and %d are supported", chunk, la::kChunk);
+    if (B < 0 || H < 0 || N < 0) return fail(LA_ERR_INVALID_ARGUMENT, "negative size (B=%lld H=%lld N=%lld)",
+                                             (long long)B, (long long)H, (long long)N);
+    if (N > (int64_t)1 << 30) return fail(LA_ERR_UNSUPPORTED, "N = %lld exceeds 2^30 tokens per head", (long long)N);
+    if (B > 0 && H > ((int64_t)1 << 31) / B) return fail(LA_ERR_UNSUPPORTED, "B*H exceeds 2^31 heads");
+    *empty = (B == 0 || H == 0 || N == 0);
+    return LA_OK;
+}
+
+// Workspace layout of the sequence calls.
+struct Layout {
+    la::SegPlan plan;
+    int64_t heads = 0;
+    size_t rec = 0, total = 0, rrec = 0, rowstat = 0;  // byte offsets
+    size_t bytes = 0;
+};
+
+Layout layout(la_op op, int64_t B, int64_t H, int64_t N, int64_t d) {
+    Layout L;
+    const int64_t BH = B * H;
+    L.plan = la::plan_segments(BH, N);
+    L.heads = BH;
+    const size_t recb = (size_t)BH * L.plan.nseg * la::rec_floats(d) * sizeof(float);
+    size_t off = 0;
+    L.rec = off;
+    off += align_up(recb);
+    if (op == LA_OP_FWD_NONCAUSAL || op == LA_OP_FWD_CAUSAL) {
+        L.total = off;
+        off += align_up((size_t)BH * la::rec_floats(d) * sizeof(float));
+    } else {
+        L.rrec = off;
+        off += align_up(recb);
+        L.rowstat = off;
+        off += align_up((size_t)BH * N * 2 * sizeof(float));
+    }
+    L.bytes = off;
+    return L;
+}
+
+la_status check_workspace(const Layout& L, const void* ws, size_t ws_bytes) {
+    if (L.bytes == 0) return LA_OK;
+    if ((int64_t)L.plan.nseg * L.heads > ((int64_t)1 << 24))
+        return fail(LA_ERR_UNSUPPORTED, "%lld workgroups exceed the 2^24 grid limit",
+                    (long long)L.plan.nseg * L.heads);
+    if (ws == nullptr) return fail(LA_ERR_WORKSPACE, "workspace is NULL; %zu bytes are needed", L.bytes);
+    if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+        return fail(LA_ERR_INVALID_ARGUMENT, "workspace must be %zu-byte aligned", kAlign);
+    if (ws_bytes < L.bytes) return fail(LA_ERR_WORKSPACE, "workspace has %zu bytes; %zu are needed", ws_bytes, L.bytes);
+    return LA_OK;
+}
+
+la_status check_ptrs(const Range* in, int nin, const Range* out, int nout) {
+    for (int i = 0; i < nin + nout; ++i) {
+        const Range& r = i < nin ? in[i] : out[i - nin];
+        if (r.p != nullptr && !aligned16(r.p)) return fail(LA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", r.name);
+    }
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < nin; ++j)
+            if (overlap(out[i], in[j]))
+                return fail(LA_ERR_INVALID_ARGUMENT, "output %s overlaps input %s", out[i].name, in[j].name);
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(out[i], out[j]))
+                return fail(LA_ERR_INVALID_ARGUMENT, "outputs %s and %s overlap", out[i].name, out[j].name);
+    }
+    return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* la_status_string(la_status s) {
+    switch (s) {
+        case LA_OK: return "LA_OK";
+        case LA_ERR_INVALID_ARGUMENT: return "LA_ERR_INVALID_ARGUMENT";
+        case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
+        case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE";
+        case LA_ERR_HIP: return "LA_ERR_HIP";
+    }
+    return "LA_ERR_UNKNOWN";
+}
+
+const char* la_last_error_message(void) { return g_last_error.c_str(); }
+
+const char* la_version(void) { return "linattn 0.1.0 (gfx950)"; }
+
+la_status la_profile_enable(int on) {
+    g_timing.on = on != 0;
+    g_timing.used = 0;
+    return LA_OK;
+}
+
+int la_profile_count(void) { return (int)g_timing.used; }
+
+la_status la_profile_entry(int i, const char** name, float* ms) {
+    if (i < 0 || (size_t)i >= g_timing.used || name == nullptr || ms == nullptr)
+        return fail(LA_ERR_INVALID_ARGUMENT, "profile entry %d out of range (have %zu)", i, g_timing.used);
+    hipEvent_t a = g_timing.pool[2 * i], b = g_timing.pool[2 * i + 1];
+    hipError_t e = hipEventSynchronize(b);
+    if (e != hipSuccess) return hip_fail(e, "profile event sync");
+    if ((e = hipEventElapsedTime(ms, a, b)) != hipSuccess) return hip_fail(e, "profile elapsed time");
+    *name = g_timing.names[i];
+    return LA_OK;
+}
+
+la_status la_workspace_size(la_op op, int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt,
+                            size_t* bytes_out) {
+    if (bytes_out == nullptr) return fail(LA_ERR_INVALID_ARGUMENT, "bytes_out is NULL");
+    if (op != LA_OP_FWD_NONCAUSAL && op != LA_OP_FWD_CAUSAL && op != LA_OP_BWD_CAUSAL)
+        return fail(LA_ERR_INVALID_ARGUMENT, "unknown op %d", (int)op);
+    bool empty = false;
+    la_status st = check_shape(B, H, N, d, chunk, dt, &empty);
+    if (st != LA_OK) return st;
+    *bytes_out = empty ? 0 : layout(op, B, H, N, d).bytes;
+    return LA_OK;
+}
+
+la_status la_forward_noncausal(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
+                               int64_t N, int64_t d, la_dtype dt, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    bool empty = false;
+    la_status st = check_shape(B, H, N, d, 0, dt, &empty);
+    if (st != LA_OK) return st;
+    if (!q || !k || !v || !o) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-NULL");
+    const size_t tb = (size_t)B * H * N * d * elem_size(dt);
+    const Range in[] = {{"q", q, tb}, {"k", k, tb}, {"v", v, tb}};
+    const Range out[] = {{"o", o, tb}};
+    if ((st = check_ptrs(in, 3, out, 1)) != LA_OK) return st;
+    if (empty) return LA_OK;
+    const Layout L = layout(LA_OP_FWD_NONCAUSAL, B, H, N, d);
+    if ((st = check_workspace(L, workspace, workspace_bytes)) != LA_OK) return st;
+    const Range wsr[] = {{"workspace", workspace, L.bytes}};
+    if ((st = check_ptrs(in, 3, wsr, 1)) != LA_OK) return st;
+    if (overlap(wsr[0], out[0])) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps o");
+
+    char* ws = static_cast<char*>(workspace);
+    float* rec = reinterpret_cast<float*>(ws + L.rec);
+    float* total = reinterpret_cast<float*>(ws + L.total);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t BH = B * H;
+    const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
+    hipError_t e;
+    if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
+        return hip_fail(e, "seg_state launch");
+    if ((e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, total, BH, L.plan.nseg, false, s); })) != hipSuccess)
+        return hip_fail(e, "scan launch");
+    if ((e = timed("noncausal_fwd", s, [&] { return la::launch_noncausal_fwd(idt, (int)d, q, o, total, BH, N, L.plan, s); })) != hipSuccess)
+        return hip_fail(e, "noncausal_fwd launch");
+    return LA_OK;
+}
+
+la_status la_forward_causal(const void* q, const void* k, const void* v, void* o, float* den_out, float* S_out,
+                            float* z_out, int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    bool empty = false;
+    la_status st = check_shape(B, H, N, d, chunk, dt, &empty);
+    if (st != LA_OK) return st;
+    if (dt == LA_F32 && d == 128) return fail(LA_ERR_UNSUPPORTED, "fp32 causal forward is built for d = 32 and 64");
+    if (!q || !k || !v || !o) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-NULL");
+    const size_t tb = (size_t)B * H * N * d * elem_size(dt);
+    const Range in[] = {{"q", q, tb}, {"k", k, tb}, {"v", v, tb}};
+    const Range out[] = {{"o", o, tb},
+                         {"den_out", den_out, (size_t)B * H * N * sizeof(float)},
+                         {"S_out", S_out, (size_t)B * H * d * d * sizeof(float)},
+                         {"z_out", z_out, (size_t)B * H * d * sizeof(float)}};
+    if ((st = check_ptrs(in, 3, out, 4)) != LA_OK) return st;
+    if (B == 0 || H == 0) return LA_OK;
+    const int64_t BH = B * H;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (N == 0) {  // empty sequence: the state is zero
+        if (S_out && (e = timed("fill_zero", s, [&] { return la::launch_fill_zero(S_out, (size_t)BH * d * d, s); })) != hipSuccess)
+            return hip_fail(e, "S_out clear");
+        if (z_out && (e = timed("fill_zero", s, [&] { return la::launch_fill_zero(z_out, (size_t)BH * d, s); })) != hipSuccess)
+            return hip_fail(e, "z_out clear");
+        return LA_OK;
+    }
+    const Layout L = layout(LA_OP_FWD_CAUSAL, B, H, N, d);
+    if ((st = check_workspace(L, workspace, workspace_bytes)) != LA_OK) return st;
+    const Range wsr[] = {{"workspace", workspace, L.bytes}};
+    if ((st = check_ptrs(in, 3, wsr, 1)) != LA_OK) return st;
+    for (const Range& r : out)
+        if (overlap(wsr[0], r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+
+    char* ws = static_cast<char*>(workspace);
+    float* rec = reinterpret_cast<float*>(ws + L.rec);
+    float* total = reinterpret_cast<float*>(ws + L.total);
+    const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
+    const bool want_state = S_out != nullptr || z_out != nullptr;
+    if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
+        return hip_fail(e, "seg_state launch");
+    if ((e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, want_state ? total : nullptr, BH, L.plan.nseg, true, s); })) != hipSuccess)
+        return hip_fail(e, "scan launch");
+    if ((e = timed("causal_fwd", s, [&] { return la::launch_causal_fwd(idt, (int)d, q, k, v, o, den_out, rec, BH, N, L.plan, s); })) != hipSuccess)
+        return hip_fail(e, "causal_fwd launch");
+    if (want_state && (e = timed("final_state", s, [&] { return la::launch_final_state((int)d, total, S_out, z_out, BH, N, s); })) != hipSuccess)
+        return hip_fail(e, "final_state launch");
+    return LA_OK;
+}
+
+la_status la_backward_causal(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+                             void* dv, int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    bool empty = false;
+    la_status st = check_shape(B, H, N, d, chunk, dt, &empty);
+    if (st != LA_OK) return st;
+    if (dt == LA_F32 && d == 128) return fail(LA_ERR_UNSUPPORTED, "fp32 causal backward is built for d = 32 and 64");
+    if (!q || !k || !v || !dout || !dq || !dk || !dv)
+        return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v, dout, dq, dk and dv must be non-NULL");
+    const size_t tb = (size_t)B * H * N * d * elem_size(dt);
+    const Range in[] = {{"q", q, tb}, {"k", k, tb}, {"v", v, tb}, {"dout", dout, tb}};
+    const Range out[] = {{"dq", dq, tb}, {"dk", dk, tb}, {"dv", dv, tb}};
+    if ((st = check_ptrs(in, 4, out, 3)) != LA_OK) return st;
+    if (empty) return LA_OK;
+    const Layout L = layout(LA_OP_BWD_CAUSAL, B, H, N, d);
+    if ((st = check_workspace(L, workspace, workspace_bytes)) != LA_OK) return st;
+    const Range wsr[] = {{"workspace", workspace, L.bytes}};
+    if ((st = check_ptrs(in, 4, wsr, 1)) != LA_OK) return st;
+    for (const Range& r : out)
+        if (overlap(wsr[0], r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+
+    char* ws = static_cast<char*>(workspace);
+    float* rec = reinterpret_cast<float*>(ws + L.rec);
+    float* rrec = reinterpret_cast<float*>(ws + L.rrec);
+    float* rowstat = reinterpret_cast<float*>(ws + L.rowstat);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t BH = B * H;
+    const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
+    hipError_t e;
+    if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
+        return hip_fail(e, "seg_state launch");
+    if ((e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, nullptr, BH, L.plan.nseg, true, s); })) != hipSuccess)
+        return hip_fail(e, "scan launch");
+    if ((e = timed("bwd_prefix", s, [&] { return la::launch_bwd_prefix(idt, (int)d, q, k, v, dout, dq, rowstat, rrec, rec, BH, N, L.plan, s); })) !=
+        hipSuccess)
+        return hip_fail(e, "bwd_prefix launch");
+    if ((e = timed("rscan", s, [&] { return la::launch_rscan((int)d, rrec, BH, L.plan.nseg, s); })) != hipSuccess) return hip_fail(e, "rscan launch");
+    if ((e = timed("bwd_suffix", s, [&] { return la::launch_bwd_suffix(idt, (int)d, q, k, v, dout, dk, dv, rowstat, rrec, BH, N, L.plan, s); })) !=
+        hipSuccess)
+        return hip_fail(e, "bwd_suffix launch");
+    return LA_OK;
+}
+
+la_status la_decode_step(float* S, float* z, const void* q, const void* k, const void* v, void* o, int64_t B,
+                         int64_t H, int64_t d, la_dtype dt, void* stream) {
+    if (dt != LA_F32 && dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "dtype %d is not LA_F32 or LA_BF16", (int)dt);
+    if (d != 32 && d != 64 && d != 128) return fail(LA_ERR_UNSUPPORTED, "d = %lld; built for 32, 64 and 128", (long long)d);
+    if (B < 0 || H < 0) return fail(LA_ERR_INVALID_ARGUMENT, "negative size (B=%lld H=%lld)", (long long)B, (long long)H);
+    if (B > 0 && H > ((int64_t)1 << 24) / B) return fail(LA_ERR_UNSUPPORTED, "B*H exceeds 2^24 heads");
+    if (!S || !z || !q || !k || !v || !o) return fail(LA_ERR_INVALID_ARGUMENT, "S, z, q, k, v and o must be non-NULL");
+    const int64_t BH = B * H;
+    const size_t vb = (size_t)BH * d * elem_size(dt);
+    const Range in[] = {{"q", q, vb}, {"k", k, vb}, {"v", v, vb}};
+    const Range out[] = {{"S", S, (size_t)BH * d * d * sizeof(float)},
+                         {"z", z, (size_t)BH * d * sizeof(float)},
+                         {"o", o, vb}};
+    la_status st = check_ptrs(in, 3, out, 3);
+    if (st != LA_OK) return st;
+    if (BH == 0) return LA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed("decode", s, [&] {
+        return la::launch_decode(dt == LA_BF16 ? la::kBF16 : la::kF32, (int)d, S, z, q, k, v, o, BH, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return LA_OK;
+}
+
+}  // extern "C"

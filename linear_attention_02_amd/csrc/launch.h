@@ -1,0 +1,62 @@
+// launch.h -- host-side launchers of the gfx950 kernels (internal to the library).
+//
+// Every launcher enqueues on `stream` and returns the launch status; shapes and
+// pointers have been validated by the C-ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace la {
+
+constexpr int kChunk = 64;       // tokens per chunk (one MFMA-tiled block of the scan)
+constexpr int kBlock = 256;      // threads per workgroup (4 wavefronts)
+
+enum DType { kF32 = 0, kBF16 = 1 };
+
+// Sequence segmentation: each (head, segment) pair is one workgroup; a segment
+// is `cps` consecutive chunks.  Segments are joined by an exclusive scan of
+// their fp32 state aggregates.
+struct SegPlan {
+    int cps;   // chunks per segment
+    int nseg;  // segments per head
+};
+SegPlan plan_segments(int64_t BH, int64_t N);
+
+// Number of floats in one segment-state record for head dimension d:
+// S_E^T [d][d], z_E [d], P [d].
+inline int64_t rec_floats(int64_t d) { return d * d + 2 * d; }
+
+// Forward pieces.
+hipError_t launch_seg_state(int dt, int d, const void* k, const void* v, float* rec, int64_t BH,
+                            int64_t N, SegPlan p, hipStream_t s);
+// Exclusive prefix of the segment records in place (write_prefix) and/or the
+// per-head total (total != nullptr).
+hipError_t launch_scan(int d, float* rec, float* total, int64_t BH, int nseg, bool write_prefix,
+                       hipStream_t s);
+hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const void* v, void* o,
+                             float* den_out, const float* rec, int64_t BH, int64_t N, SegPlan p,
+                             hipStream_t s);
+hipError_t launch_noncausal_fwd(int dt, int d, const void* q, void* o, const float* total,
+                                int64_t BH, int64_t N, SegPlan p, hipStream_t s);
+hipError_t launch_final_state(int d, const float* total, float* S_out, float* z_out, int64_t BH,
+                              int64_t N, hipStream_t s);
+
+// Backward pieces.
+hipError_t launch_bwd_prefix(int dt, int d, const void* q, const void* k, const void* v,
+                             const void* dout, void* dq, float* rowstat, float* rrec,
+                             const float* rec, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
+hipError_t launch_rscan(int d, float* rrec, int64_t BH, int nseg, hipStream_t s);
+hipError_t launch_bwd_suffix(int dt, int d, const void* q, const void* k, const void* v,
+                             const void* dout, void* dk, void* dv, const float* rowstat,
+                             const float* rrec, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
+
+// Zero-fill n floats with a kernel (no memset node, so the call can sit in a captured graph).
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
+
+// Decode.
+hipError_t launch_decode(int dt, int d, float* S, float* z, const void* q, const void* k,
+                         const void* v, void* o, int64_t BH, hipStream_t s);
+
+}  // namespace la

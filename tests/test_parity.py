@@ -1,0 +1,230 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 CPU oracle.
+
+Metric: for every (b, h) slice, ||gpu - oracle||_F / ||oracle||_F, maximum
+over slices, and every output finite.  Tolerances: 1e-4 for fp32 inputs and
+2e-2 for bf16 inputs with fp32 accumulation.  Inputs are seeded synthetic
+tensors (la_inputs); the oracle sees the exact values the GPU saw, widened to
+fp64.  Sizes span several 64-token chunks, several segments and ragged tails.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import la_inputs as inp  # noqa: E402
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+
+
+@pytest.fixture(scope="module")
+def la():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_attention_02_amd as m
+    m.load_library()
+    return m
+
+
+def f64(x):
+    return inp.to_f64(x)
+
+
+def record(name, **errs):
+    """Append measured errors to $LA_PARITY_LOG (JSON lines) when it is set."""
+    path = os.environ.get("LA_PARITY_LOG")
+    if path:
+        with open(path, "a") as fh:
+            fh.write(json.dumps({"case": name, **errs}) + "\n")
+
+
+def slice_err(gpu, ref):
+    """max over leading slices of the Frobenius relative error (last two dims form a slice)."""
+    g = f64(gpu) if isinstance(gpu, torch.Tensor) else gpu
+    assert np.isfinite(g).all(), "non-finite GPU output"
+    g = g.reshape(-1, *g.shape[-2:]) if g.ndim >= 2 else g.reshape(1, 1, -1)
+    r = ref.reshape(g.shape)
+    num = np.linalg.norm((g - r).reshape(g.shape[0], -1), axis=1)
+    den = np.maximum(np.linalg.norm(r.reshape(g.shape[0], -1), axis=1), 1e-300)
+    return float((num / den).max())
+
+
+def draw(B, H, N, d, dtype, seed=0, scale=None):
+    sc = (dtype == torch.bfloat16) if scale is None else scale
+    q, k, v, do = inp.qkv(B, H, N, d, dtype, seed=seed, scale=sc, with_dout=True)
+    return [t.cuda() for t in (q, k, v, do)]
+
+
+def run_fwd_causal(la, oracle, B, H, N, d, dtype, seed=0, scale=None):
+    q, k, v, _ = draw(B, H, N, d, dtype, seed, scale)
+    o, den, S, z = la.la_forward_causal(q, k, v, return_den=True, return_state=True)
+    torch.cuda.synchronize()
+    ro, rden, rS, rz = oracle.forward_causal(f64(q), f64(k), f64(v), return_den=True, return_state=True)
+    tol = TOL[dtype]
+    errs = {"o": slice_err(o, ro), "den": slice_err(den, rden), "S": slice_err(S, rS),
+            "z": slice_err(z[..., None], rz[..., None])}
+    record(f"fwd_causal {B}x{H}x{N}x{d} {dtype}", **errs)
+    assert errs["o"] < tol, errs
+    assert max(errs["den"], errs["S"], errs["z"]) < min(tol, 1e-3), errs
+
+
+def run_fwd_noncausal(la, oracle, B, H, N, d, dtype, seed=0, scale=None):
+    q, k, v, _ = draw(B, H, N, d, dtype, seed, scale)
+    o = la.la_forward_noncausal(q, k, v)
+    torch.cuda.synchronize()
+    ro = oracle.forward_noncausal(f64(q), f64(k), f64(v))
+    err = slice_err(o, ro)
+    record(f"fwd_noncausal {B}x{H}x{N}x{d} {dtype}", o=err)
+    assert err < TOL[dtype]
+
+
+def run_bwd_causal(la, oracle, B, H, N, d, dtype, seed=0, scale=None):
+    q, k, v, do = draw(B, H, N, d, dtype, seed, scale)
+    dq, dk, dv = la.la_backward_causal(q, k, v, do)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = oracle.backward_causal(f64(q), f64(k), f64(v), f64(do))
+    tol = TOL[dtype]
+    if N == 1:
+        # A single token: O_0 = V_0 whatever q and k are, so dq and dk vanish exactly and
+        # no relative error exists; they must be negligible next to dv = dout.
+        scale = float(np.abs(f64(do)).max())
+        assert float(np.abs(f64(dq)).max()) < 1e-3 * tol * scale
+        assert float(np.abs(f64(dk)).max()) < 1e-3 * tol * scale
+        assert slice_err(dv, rdv) < tol
+        return
+    errs = {"dq": slice_err(dq, rdq), "dk": slice_err(dk, rdk), "dv": slice_err(dv, rdv)}
+    record(f"bwd_causal {B}x{H}x{N}x{d} {dtype}", **errs)
+    assert max(errs.values()) < tol, errs
+
+
+# ---- the small fp32 workload: B1 H2 N256 d32, N(0,1) unscaled ---------------------------
+def test_tiny_fp32_all_calls(la, oracle):
+    w = inp.TINY
+    run_fwd_noncausal(la, oracle, w.B, w.H, w.N, w.d, w.dtype, scale=False)
+    run_fwd_causal(la, oracle, w.B, w.H, w.N, w.d, w.dtype, scale=False)
+    run_bwd_causal(la, oracle, w.B, w.H, w.N, w.d, w.dtype, scale=False)
+
+
+# ---- shapes spanning chunks, segments and ragged tails ----------------------------------------
+SHAPES = [
+    (1, 1, 1, 32), (1, 2, 63, 64), (2, 1, 64, 64), (1, 1, 65, 128), (2, 3, 200, 64),
+    (1, 2, 257, 32), (1, 2, 300, 128), (2, 2, 1000, 64), (1, 1, 4096 + 17, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_forward_causal(la, oracle, shape, dtype):
+    B, H, N, d = shape
+    if dtype == torch.float32 and d == 128:
+        pytest.skip("fp32 causal path is built for d <= 64")
+    run_fwd_causal(la, oracle, B, H, N, d, dtype, seed=N)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_forward_noncausal(la, oracle, shape, dtype):
+    B, H, N, d = shape
+    run_fwd_noncausal(la, oracle, B, H, N, d, dtype, seed=N + 1)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_backward_causal(la, oracle, shape, dtype):
+    B, H, N, d = shape
+    if dtype == torch.float32 and d == 128:
+        pytest.skip("fp32 causal path is built for d <= 64")
+    run_bwd_causal(la, oracle, B, H, N, d, dtype, seed=N + 2)
+
+
+# ---- decode --------------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_decode_from_causal_prefix(la, oracle, d, dtype):
+    B, H, N0, steps = 2, 3, 130, 5
+    q, k, v, _ = draw(B, H, N0, d, dtype, seed=d)
+    if dtype == torch.float32 and d == 128:
+        # fp32 prefix state through the oracle-independent recurrence: start from zero
+        S = torch.zeros(B, H, d, d, device="cuda")
+        z = torch.zeros(B, H, d, device="cuda")
+        rS, rz = np.zeros((B, H, d, d)), np.zeros((B, H, d))
+    else:
+        _, S, z = la.la_forward_causal(q, k, v, return_state=True)
+        _, rS, rz = oracle.forward_causal(f64(q), f64(k), f64(v), return_state=True)
+    sq, sk, sv = inp.decode_tokens(B, H, d, steps, dtype, seed=d + 7)
+    for t in range(steps):
+        qt, kt, vt = sq[t].cuda(), sk[t].cuda(), sv[t].cuda()
+        o = la.la_decode_step(S, z, qt, kt, vt)
+        torch.cuda.synchronize()
+        ro, rS, rz = oracle.decode_step(rS, rz, f64(qt), f64(kt), f64(vt))
+        assert slice_err(o[..., None], ro[..., None]) < TOL[dtype]
+    assert slice_err(S, rS) < 1e-3
+    assert slice_err(z[..., None], rz[..., None]) < 1e-3
+
+
+def test_decode_random_state(la, oracle):
+    """State with both signs in S and a positive z, as any prefix would give."""
+    B, H, d = 3, 2, 64
+    gen = inp.generator(11)
+    S = torch.randn(B, H, d, d, generator=gen)
+    z = torch.rand(B, H, d, generator=gen) * 100 + 1
+    q, k, v = (t[0] for t in inp.decode_tokens(B, H, d, 1, torch.bfloat16, seed=12))
+    Sg, zg = S.clone().cuda(), z.clone().cuda()
+    o = la.la_decode_step(Sg, zg, q.cuda(), k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    ro, rS, rz = oracle.decode_step(f64(S), f64(z), f64(q), f64(k), f64(v))
+    assert slice_err(o[..., None], ro[..., None]) < 2e-2
+    assert slice_err(Sg, rS) < 1e-6
+    assert slice_err(zg[..., None], rz[..., None]) < 1e-6
+
+
+# ---- properties -------------------------------------------------------------------------------------
+def test_deterministic(la):
+    q, k, v, do = draw(2, 4, 1000, 64, torch.bfloat16, seed=5)
+    a = [la.la_forward_causal(q, k, v), la.la_forward_noncausal(q, k, v), *la.la_backward_causal(q, k, v, do)]
+    b = [la.la_forward_causal(q, k, v), la.la_forward_noncausal(q, k, v), *la.la_backward_causal(q, k, v, do)]
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_constant_v(la):
+    B, H, N, d = 1, 2, 333, 64
+    q, k, _, _ = draw(B, H, N, d, torch.float32, seed=9)
+    c = torch.randn(B, H, 1, d, device="cuda")
+    v = c.expand(B, H, N, d).contiguous()
+    o = la.la_forward_causal(q, k, v)
+    o2 = la.la_forward_noncausal(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.allclose(o, v, rtol=1e-5, atol=1e-6)
+    assert torch.allclose(o2, v, rtol=1e-5, atol=1e-6)
+
+
+def test_causality_across_chunks(la):
+    """Poisoning keys/values from token 128 on leaves rows 0..127 (two whole chunks) untouched."""
+    B, H, N, d = 1, 2, 256, 64
+    q, k, v, _ = draw(B, H, N, d, torch.bfloat16, seed=10)
+    o = la.la_forward_causal(q, k, v)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, 128:] = float("nan")
+    v2[:, :, 128:] = float("inf")
+    o2 = la.la_forward_causal(q, k2, v2)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :, :128], o2[:, :, :128])
+
+
+def test_autograd_function(la, oracle):
+    q, k, v, do = draw(1, 2, 150, 32, torch.float32, seed=13)
+    q.requires_grad_(True)
+    k.requires_grad_(True)
+    v.requires_grad_(True)
+    o = la.causal_linear_attention(q, k, v)
+    o.backward(do)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = oracle.backward_causal(f64(q), f64(k), f64(v), f64(do))
+    assert slice_err(q.grad, rdq) < 1e-4
+    assert slice_err(k.grad, rdk) < 1e-4
+    assert slice_err(v.grad, rdv) < 1e-4

@@ -1,0 +1,125 @@
+"""GPU parity at the full measured sizes, in the launch configuration the
+benchmark times (default chunk, library-chosen segments, one call per op).
+
+Inputs are drawn on the device with the seeded device generator (la_inputs);
+the exact values of the checked heads are copied to the host and the fp64
+oracle recomputes those heads from scratch.  Mid is checked on every head;
+the larger workloads on a seeded sample of heads (heads are independent).
+Metric and tolerances as in test_parity.py.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import la_inputs as inp  # noqa: E402
+from test_parity import TOL, f64, record, slice_err  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def la():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_attention_02_amd as m
+    m.load_library()
+    return m
+
+
+def heads(x, idx):
+    """[B, H, ...] -> selected flat heads [len(idx), ...] on the host in fp64."""
+    flat = x.reshape(-1, *x.shape[2:])
+    return f64(flat[idx])
+
+
+def pick(BH, n, seed):
+    if n >= BH:
+        return np.arange(BH)
+    return np.sort(np.random.default_rng(seed).choice(BH, size=n, replace=False))
+
+
+def check_workload(la, oracle, w, nheads, with_bwd, seed=0):
+    q, k, v, do = inp.workload_inputs(w, seed=seed, device="cuda", with_dout=True)
+    o, den = la.la_forward_causal(q, k, v, return_den=True)
+    dq = dk = dv = None
+    if with_bwd:
+        dq, dk, dv = la.la_backward_causal(q, k, v, do)
+    torch.cuda.synchronize()
+    idx = pick(w.B * w.H, nheads, seed + 1)
+    hq, hk, hv = heads(q, idx), heads(k, idx), heads(v, idx)
+    ro, rden = oracle.forward_causal(hq, hk, hv, return_den=True)
+    errs = {"o": slice_err(heads(o, idx), ro), "den": slice_err(heads(den, idx)[..., None], rden[..., None])}
+    if with_bwd:
+        rdq, rdk, rdv = oracle.backward_causal(hq, hk, hv, heads(do, idx))
+        errs.update(dq=slice_err(heads(dq, idx), rdq), dk=slice_err(heads(dk, idx), rdk),
+                    dv=slice_err(heads(dv, idx), rdv))
+    record(f"full {w.name} heads={len(idx)}", **errs)
+    print(w.name, errs, flush=True)
+    assert max(errs.values()) < TOL[w.dtype], errs
+
+
+def test_mid_all_heads(la, oracle):
+    check_workload(la, oracle, inp.MID, nheads=10**9, with_bwd=True)
+
+
+def test_mid_noncausal_all_heads(la, oracle):
+    w = inp.MID
+    q, k, v = inp.workload_inputs(w, seed=0, device="cuda", with_dout=False)
+    o = la.la_forward_noncausal(q, k, v)
+    torch.cuda.synchronize()
+    ro = oracle.forward_noncausal(f64(q), f64(k), f64(v))
+    err = slice_err(o, ro)
+    record("full mid noncausal", o=err)
+    assert err < TOL[w.dtype]
+
+
+def test_long_sampled_heads(la, oracle):
+    check_workload(la, oracle, inp.LONG, nheads=12, with_bwd=True)
+
+
+def test_verylong_sampled_heads_and_footprint(la, oracle):
+    w = inp.VERYLONG
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    check_workload(la, oracle, w, nheads=3, with_bwd=False)
+    peak = torch.cuda.max_memory_allocated() - base
+    unit = w.B * w.H * w.N * w.d * 2
+    # q, k, v, dout, o (bf16) + den (fp32) + workspace (segment states): O(N d) + O(d^2) per segment
+    assert peak < 5 * unit + w.B * w.H * w.N * 4 + 64 * 2**20 * w.H, peak
+
+
+def test_decode_sampled_sequences(la, oracle):
+    w = inp.DECODE
+    B, H, d, N0, steps = w.batch, w.H, w.d, w.prefix, w.steps
+    S = torch.empty(B, H, d, d, device="cuda")
+    z = torch.empty(B, H, d, device="cuda")
+    idx = pick(B * H, 24, 5)
+    pk, pv, pq = [], [], []
+    nb = 32  # prefix drawn and reduced 32 sequences at a time
+    for b0 in range(0, B, nb):
+        q, k, v = inp.qkv(nb, H, N0, d, w.dtype, seed=1000 + b0, device="cuda")
+        _, Sb, zb = la.la_forward_causal(q, k, v, return_state=True)
+        S[b0:b0 + nb].copy_(Sb)
+        z[b0:b0 + nb].copy_(zb)
+        sel = [i - b0 * H for i in idx if b0 * H <= i < (b0 + nb) * H]
+        if sel:
+            pk.append(heads(k, sel))
+            pv.append(heads(v, sel))
+            pq.append(heads(q, sel))
+        del q, k, v
+    _, rS, rz = oracle.forward_causal(np.concatenate(pq), np.concatenate(pk), np.concatenate(pv),
+                                      return_state=True)
+    sq, sk, sv = inp.decode_tokens(B, H, d, steps, w.dtype, seed=2, device="cuda")
+    outs = torch.empty(steps, B, H, d, dtype=w.dtype, device="cuda")
+    for t in range(steps):
+        outs[t] = la.la_decode_step(S, z, sq[t], sk[t], sv[t])
+    torch.cuda.synchronize()
+    worst = 0.0
+    for t in range(steps):
+        ro, rS, rz = oracle.decode_step(rS, rz, heads(sq[t], idx), heads(sk[t], idx), heads(sv[t], idx))
+        worst = max(worst, slice_err(heads(outs[t], idx)[:, None, :], ro[:, None, :]))
+    rS_gpu = heads(S, idx)
+    errs = {"o_worst_step": worst, "S_final": slice_err(rS_gpu, rS)}
+    record("full decode 512 steps sampled", **errs)
+    assert worst < TOL[w.dtype] and errs["S_final"] < 1e-3, errs
