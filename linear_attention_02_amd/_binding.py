@@ -34,11 +34,13 @@ class LinAttnError(RuntimeError):
 
 
 def load_library(path: str | None = None):
-    """Load liblinattn.so (raises if it is missing; the library is never replaced by Python code)."""
+    """Load liblinattn.so (raises if it is missing; the library is never replaced by Python code).
+
+    $LINATTN_LIBRARY, when set, names another build of the same library to load."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("LINATTN_LIBRARY") or LIB_PATH
     if not os.path.exists(p):
         raise ImportError(f"{p} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
                           "or `python -m linear_attention_02_amd._build`")

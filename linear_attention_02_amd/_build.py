@@ -30,7 +30,8 @@ def hipcc() -> str:
 
 
 def common_flags() -> list[str]:
-    return [
+    extra = os.environ.get("LINATTN_HIPCC_FLAGS", "").split()
+    return extra + [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # no packed-fp32 instructions in device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -48,22 +49,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link liblinattn.so; returns its path."""
+def build(jobs: int | None = None, verbose: bool = False, out: str | None = None) -> str:
+    """Compile every HIP source for gfx950 and link liblinattn.so (or `out`); returns its path."""
     os.makedirs(OBJDIR, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    lib = out or LIB
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
-    return LIB
+        print(f"built {lib}", file=sys.stderr)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, out=sys.argv[1] if len(sys.argv) > 1 else None)

@@ -1,20 +1,26 @@
-// chunk.h -- chunk staging and state helpers shared by the forward and backward kernels.
+// chunk.h -- chunk staging and carried-state helpers shared by the forward and
+// backward kernels.
 //
-// A chunk is C consecutive tokens of one head (C = 64, or 32 where LDS is
-// short).  Its [C][d] input tiles are read from HBM with coalesced 16-byte
-// loads into registers one chunk ahead, then staged into swizzled LDS tiles
-// (row-major and/or transposed) for the MFMA products.  The carried state is
-// split around the constant part of phi(K) = 1 + E(K) (E = elu):
-//   S = 1 P^T + S_E, z = n 1 + z_E with P = sum V, S_E = sum E(K) V^T, z_E = sum E(K).
+// A chunk is kChunk = 64 consecutive tokens of one head.  Its [64][d] input
+// tiles are read from HBM with coalesced 16-byte loads into registers one
+// chunk ahead, transformed (phi, elu, 1/den), and staged row-major into
+// swizzled LDS tiles; operands that contract over tokens are read back with
+// the transposing LDS load.  The carried state is split around the constant
+// part of phi(K) = 1 + E(K) (E = elu):
+//   S = 1 P^T + S_E, z = n 1 + z_E, with P = sum V, S_E = sum E(K) V^T, z_E = sum E(K).
 #pragma once
+
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
 
 namespace la {
 
-// Segment record (fp32): S_E^T[b][a] (d*d), then z_E[a] (d), then P[b] (d).
-// The backward's suffix records use the same layout for R^T, r and w.
+constexpr int kC = kChunk;
+
+// Segment record (fp32): X^T[b][a] (d*d), then two d-vectors.  Forward
+// records hold (S_E, z_E, P); the backward's suffix records (R, r, w).
 template <int D>
 struct Rec {
     static constexpr int kSt = 0;
@@ -23,18 +29,24 @@ struct Rec {
     static constexpr int kSize = D * D + 2 * D;
 };
 
-// Coalesced loader of one [C][D] chunk: each thread holds NV 16-byte vectors;
+// Coalesced loader of one [64][D] chunk: each thread holds NV 16-byte vectors;
 // vector i covers row row(i), granule gran(i).  Rows at or beyond N read as 0.
-template <typename T, int D, int C>
+// kWaveRows = false: the block's threads cover the rows in order;
+// kWaveRows = true : wavefront w covers rows 16w .. 16w+15 (its own token tile).
+template <typename T, int D, bool kWaveRows = false>
 struct ChunkRegs {
     static constexpr int EV = 16 / (int)sizeof(T);
     static constexpr int VPR = D / EV;  // vectors per row (held by consecutive lanes)
-    static constexpr int NV = C * VPR / kBlock;
-    static_assert(NV >= 1 && (C * VPR) % kBlock == 0, "chunk must split evenly over the block");
+    static constexpr int NV = kC * VPR / kBlock;
+    static_assert(NV >= 1 && (kC * VPR) % kBlock == 0, "chunk must split evenly over the block");
     static_assert(VPR <= kWave, "a row must sit inside one wavefront");
     uint4 r[NV];
-    __device__ __forceinline__ static int row(int i, int tid) { return (tid + kBlock * i) / VPR; }
-    __device__ __forceinline__ static int gran(int i, int tid) { return (tid + kBlock * i) % VPR; }
+    __device__ __forceinline__ static int row(int i, int tid) {
+        return kWaveRows ? 16 * (tid >> 6) + ((tid & 63) + kWave * i) / VPR : (tid + kBlock * i) / VPR;
+    }
+    __device__ __forceinline__ static int gran(int i, int tid) {
+        return kWaveRows ? ((tid & 63) + kWave * i) % VPR : (tid + kBlock * i) % VPR;
+    }
     __device__ __forceinline__ void load(const T* head, int tok0, int N, int tid) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
@@ -42,101 +54,60 @@ struct ChunkRegs {
             r[i] = tok < N ? load16(head + (int64_t)tok * D + gran(i, tid) * EV) : make_uint4(0, 0, 0, 0);
         }
     }
-    __device__ __forceinline__ float get(int i, int e) const {
-        return to_f32(reinterpret_cast<const T*>(&r[i])[e]);
-    }
-    __device__ __forceinline__ T raw(int i, int e) const { return reinterpret_cast<const T*>(&r[i])[e]; }
+    __device__ __forceinline__ float get(int i, int e) const { return to_f32(reinterpret_cast<const T*>(&r[i])[e]); }
 };
 
-// Stage phi(Q) row-major (and optionally transposed) and the row sums q_sum_t
-// of the values as rounded for the MFMA.
-template <typename T, int D, int C, bool kTransposed>
-__device__ __forceinline__ void stage_q(const ChunkRegs<T, D, C>& cq, const Tile<T, C, D>& tQf,
-                                        const Tile<T, D, C>& tQft, float* s_qsum, int tid) {
-    using CR = ChunkRegs<T, D, C>;
+// phi(Q) row-major into LDS.
+template <typename T, int D>
+__device__ __forceinline__ void stage_phi(const ChunkRegs<T, D>& cq, const Tile<T, kC, D>& tQ, int tid) {
+    using CR = ChunkRegs<T, D>;
 #pragma unroll
     for (int i = 0; i < CR::NV; ++i) {
-        const int t = CR::row(i, tid), gi = CR::gran(i, tid);
-        uint4 packed;
-        T* pk = reinterpret_cast<T*>(&packed);
-        float qs = 0.f;
-#pragma unroll
-        for (int e = 0; e < CR::EV; ++e) {
-            const T f = from_f32<T>(phi_f(cq.get(i, e)));
-            pk[e] = f;
-            qs += to_f32(f);
-            if (kTransposed) tQft.at(gi * CR::EV + e, t) = f;
-        }
-        *reinterpret_cast<uint4*>(tQf.granule(t, gi)) = packed;
-        qs = sum_lanes<CR::VPR>(qs);
-        if (gi == 0) s_qsum[t] = qs;
-    }
-}
-
-// Stage E(K) = elu(K) row-major and/or transposed.
-template <typename T, int D, int C, bool kRow, bool kTransposed>
-__device__ __forceinline__ void stage_e(const ChunkRegs<T, D, C>& ck, const Tile<T, C, D>& tEk,
-                                        const Tile<T, D, C>& tEkt, int tid) {
-    using CR = ChunkRegs<T, D, C>;
-#pragma unroll
-    for (int i = 0; i < CR::NV; ++i) {
-        const int t = CR::row(i, tid), gi = CR::gran(i, tid);
         uint4 packed;
         T* pk = reinterpret_cast<T*>(&packed);
 #pragma unroll
-        for (int e = 0; e < CR::EV; ++e) {
-            const T ev = from_f32<T>(elu_f(ck.get(i, e)));
-            pk[e] = ev;
-            if (kTransposed) tEkt.at(gi * CR::EV + e, t) = ev;
-        }
-        if (kRow) *reinterpret_cast<uint4*>(tEk.granule(t, gi)) = packed;
+        for (int e = 0; e < CR::EV; ++e) pk[e] = from_f32<T>(phi_f(cq.get(i, e)));
+        *reinterpret_cast<uint4*>(tQ.granule(CR::row(i, tid), CR::gran(i, tid))) = packed;
     }
 }
 
-// Stage a raw input chunk row-major and/or transposed.
-template <typename T, int D, int C, bool kRow, bool kTransposed>
-__device__ __forceinline__ void stage_raw(const ChunkRegs<T, D, C>& cx, const Tile<T, C, D>& tX,
-                                          const Tile<T, D, C>& tXt, int tid) {
-    using CR = ChunkRegs<T, D, C>;
+// E(K) = elu(K) row-major into LDS.
+template <typename T, int D>
+__device__ __forceinline__ void stage_elu(const ChunkRegs<T, D>& ck, const Tile<T, kC, D>& tE, int tid) {
+    using CR = ChunkRegs<T, D>;
 #pragma unroll
     for (int i = 0; i < CR::NV; ++i) {
-        const int t = CR::row(i, tid), gi = CR::gran(i, tid);
-        if (kTransposed) {
+        uint4 packed;
+        T* pk = reinterpret_cast<T*>(&packed);
 #pragma unroll
-            for (int e = 0; e < CR::EV; ++e) tXt.at(gi * CR::EV + e, t) = cx.raw(i, e);
-        }
-        if (kRow) *reinterpret_cast<uint4*>(tX.granule(t, gi)) = cx.r[i];
+        for (int e = 0; e < CR::EV; ++e) pk[e] = from_f32<T>(elu_f(ck.get(i, e)));
+        *reinterpret_cast<uint4*>(tE.granule(CR::row(i, tid), CR::gran(i, tid))) = packed;
     }
 }
 
-// Sum of one row of an LDS tile, in fixed order.
-template <typename T, int ROWS, int COLS>
-__device__ __forceinline__ float row_sum(const Tile<T, ROWS, COLS>& t, int r) {
-    constexpr int EV = Tile<T, ROWS, COLS>::EV;
-    float s = 0.f;
+// A raw chunk row-major into LDS.
+template <typename T, int D>
+__device__ __forceinline__ void stage_raw(const ChunkRegs<T, D>& cx, const Tile<T, kC, D>& tX, int tid) {
+    using CR = ChunkRegs<T, D>;
 #pragma unroll
-    for (int gi = 0; gi < COLS / EV; ++gi) {
-        const uint4 g = *reinterpret_cast<const uint4*>(t.granule(r, gi));
-        const T* p = reinterpret_cast<const T*>(&g);
-#pragma unroll
-        for (int e = 0; e < EV; ++e) s += to_f32(p[e]);
-    }
-    return s;
+    for (int i = 0; i < CR::NV; ++i) *reinterpret_cast<uint4*>(tX.granule(CR::row(i, tid), CR::gran(i, tid))) = cx.r[i];
 }
 
-// Weighted sum of one row of an LDS tile: sum_c t[r][c] * wgt[c], fixed order.
-template <typename T, int ROWS, int COLS>
-__device__ __forceinline__ float row_dot(const Tile<T, ROWS, COLS>& t, int r, const float* wgt) {
-    constexpr int EV = Tile<T, ROWS, COLS>::EV;
-    float s = 0.f;
+// G = round(dO / den) row-major into LDS; rows at or beyond N are 0.
+template <typename T, int D, bool kWaveRows>
+__device__ __forceinline__ void stage_grad(const ChunkRegs<T, D, kWaveRows>& cdo, const Tile<T, kC, D>& tG,
+                                           const float* s_den, int c0, int N, int tid) {
+    using CR = ChunkRegs<T, D, kWaveRows>;
 #pragma unroll
-    for (int gi = 0; gi < COLS / EV; ++gi) {
-        const uint4 g = *reinterpret_cast<const uint4*>(t.granule(r, gi));
-        const T* p = reinterpret_cast<const T*>(&g);
+    for (int i = 0; i < CR::NV; ++i) {
+        const int t = CR::row(i, tid);
+        const float inv = c0 + t < N ? rcp_f(s_den[t]) : 0.f;
+        uint4 packed;
+        T* pk = reinterpret_cast<T*>(&packed);
 #pragma unroll
-        for (int e = 0; e < EV; ++e) s += to_f32(p[e]) * wgt[gi * EV + e];
+        for (int e = 0; e < CR::EV; ++e) pk[e] = from_f32<T>(cdo.get(i, e) * inv);
+        *reinterpret_cast<uint4*>(tG.granule(t, CR::gran(i, tid))) = packed;
     }
-    return s;
 }
 
 // Tiles of a d x d state owned by one of the 4 wavefronts: NAT row tiles
@@ -149,13 +120,20 @@ struct StateTiles {
     static constexpr int NBT = TPW >= DT ? DT : TPW;
     __device__ __forceinline__ static int at0(int w) { return (w * TPW) / DT; }
     __device__ __forceinline__ static int bt0(int w) { return (w * TPW) % DT; }
+    // The d-vector tiles a wave owns (vector index = tile of 16): the wave whose
+    // tiles start a row block owns that block's vector tiles.
+    static constexpr int NVT = DT >= 4 ? DT / 4 : 1;
+    __device__ __forceinline__ static bool owns_vec(int w) { return DT >= 4 || (w % (4 / DT)) == 0; }
+    __device__ __forceinline__ static int vt0(int w) { return DT >= 4 ? w * (DT / 4) : w / (4 / DT); }
 };
 
 template <int D>
 using StateAcc = f32x4[StateTiles<D>::NAT][StateTiles<D>::NBT];
+template <int D>
+using VecAcc = f32x4[StateTiles<D>::NVT];
 
-// The lane's 4 values of state tile (a-tile at, b-tile bt) inside a record's
-// transposed d x d block X^T[b][a].
+// Offset of the lane's 4 values of state tile (a-tile at, b-tile bt) inside a
+// record's transposed d x d block X^T[b][a].
 template <int D>
 __device__ __forceinline__ int rec_st_off(int at, int bt, int lane) {
     return (bt * 16 + (lane & 15)) * D + at * 16 + 4 * (lane >> 4);
@@ -170,7 +148,13 @@ __device__ __forceinline__ void zero_state(StateAcc<D>& st) {
 }
 
 template <int D>
-__device__ __forceinline__ void load_state_acc(const float* r, StateAcc<D>& st, int lane, int w) {
+__device__ __forceinline__ void zero_vec(VecAcc<D>& v) {
+#pragma unroll
+    for (int x = 0; x < StateTiles<D>::NVT; ++x) v[x] = zero4();
+}
+
+template <int D>
+__device__ __forceinline__ void load_state(const float* r, StateAcc<D>& st, int lane, int w) {
     using ST = StateTiles<D>;
 #pragma unroll
     for (int ia = 0; ia < ST::NAT; ++ia)
@@ -180,7 +164,7 @@ __device__ __forceinline__ void load_state_acc(const float* r, StateAcc<D>& st, 
 }
 
 template <int D>
-__device__ __forceinline__ void store_state_acc(float* r, const StateAcc<D>& st, int lane, int w) {
+__device__ __forceinline__ void store_state(float* r, const StateAcc<D>& st, int lane, int w) {
     using ST = StateTiles<D>;
 #pragma unroll
     for (int ia = 0; ia < ST::NAT; ++ia)
@@ -189,47 +173,100 @@ __device__ __forceinline__ void store_state_acc(float* r, const StateAcc<D>& st,
             *reinterpret_cast<f32x4*>(r + rec_st_off<D>(ST::at0(w) + ia, ST::bt0(w) + ib, lane)) = st[ia][ib];
 }
 
-// Rounded copies of the state in LDS: X^T[b][a] (transposed) and/or X[a][b].
-template <typename T, int D, bool kT, bool kN>
-__device__ __forceinline__ void publish_state(const StateAcc<D>& st, const Tile<T, D, D>& tXt,
-                                              const Tile<T, D, D>& tX, int lane, int w) {
+// Vector accumulators hold v[tile*16 + 4 (l >> 4) + e] in every column; the
+// accumulator layout is the MFMA output of X (rows = vector index) times a
+// constant operand.
+template <int D>
+__device__ __forceinline__ void load_vec(const float* v, VecAcc<D>& acc, int lane, int w) {
+    using ST = StateTiles<D>;
+#pragma unroll
+    for (int x = 0; x < ST::NVT; ++x) acc[x] = *reinterpret_cast<const f32x4*>(v + (ST::vt0(w) + x) * 16 + 4 * (lane >> 4));
+}
+
+template <int D>
+__device__ __forceinline__ void store_vec(float* v, const VecAcc<D>& acc, int lane, int w) {
+    using ST = StateTiles<D>;
+    if (!ST::owns_vec(w) || (lane & 15) != 0) return;
+#pragma unroll
+    for (int x = 0; x < ST::NVT; ++x) *reinterpret_cast<f32x4*>(v + (ST::vt0(w) + x) * 16 + 4 * (lane >> 4)) = acc[x];
+}
+
+// Rounded copy of the state into LDS as X^T[b][a].
+template <typename T, int D>
+__device__ __forceinline__ void publish_state(const StateAcc<D>& st, const Tile<T, D, D>& tXt, int lane, int w) {
     using ST = StateTiles<D>;
 #pragma unroll
     for (int ia = 0; ia < ST::NAT; ++ia)
 #pragma unroll
-        for (int ib = 0; ib < ST::NBT; ++ib) {
-            const int a0 = (ST::at0(w) + ia) * 16, b0 = (ST::bt0(w) + ib) * 16;
-            if (kT) store_T(tXt, a0, b0, st[ia][ib], lane);
-            if (kN) store_N(tX, a0, b0, st[ia][ib], lane);
-        }
+        for (int ib = 0; ib < ST::NBT; ++ib)
+            store_T(tXt, (ST::at0(w) + ia) * 16, (ST::bt0(w) + ib) * 16, st[ia][ib], lane);
 }
 
-// acc += X^T Y over k in [k0, k1) for the wave's state tiles, X^T from tX
-// (rows a, k contiguous) and Y from tY (rows b, k contiguous).
-template <typename T, int D, int R, int K>
-__device__ __forceinline__ void state_mma(StateAcc<D>& st, const Tile<T, R, K>& tX, const Tile<T, R, K>& tY,
-                                          int lane, int w) {
+// st[a][b] += sum_t X[t][a] Y[t][b] over the chunk, X and Y row-major [64][D]
+// tiles read with the transposing load; optionally
+// va[a] += sum_t X[t][a] * u[t] and vb[b] += sum_t Y[t][b] * v[t] for the
+// wave's vector tiles, with u, v either all ones (null pointer) or fp32
+// vectors in LDS (split hi + lo in bf16).
+template <typename T, int D, bool kVecA, bool kVecB>
+__device__ __forceinline__ void state_update(StateAcc<D>& st, VecAcc<D>& va, VecAcc<D>& vb, const Tile<T, kC, D>& tX,
+                                             const Tile<T, kC, D>& tY, const float* u, const float* v, int lane,
+                                             int w) {
     using M = Mma<T>;
     using ST = StateTiles<D>;
+    const typename M::frag one = M::ones();
 #pragma unroll
-    for (int k0 = 0; k0 < K; k0 += M::KSTEP) {
+    for (int k0 = 0; k0 < kC; k0 += M::KSTEP) {
         typename M::frag xf[ST::NAT];
 #pragma unroll
-        for (int ia = 0; ia < ST::NAT; ++ia) xf[ia] = M::load(tX, (ST::at0(w) + ia) * 16, k0, lane);
+        for (int ia = 0; ia < ST::NAT; ++ia) xf[ia] = M::ld_tr(tX, k0, (ST::at0(w) + ia) * 16, lane);
 #pragma unroll
         for (int ib = 0; ib < ST::NBT; ++ib) {
-            const typename M::frag yf = M::load(tY, (ST::bt0(w) + ib) * 16, k0, lane);
+            const typename M::frag yf = M::ld_tr(tY, k0, (ST::bt0(w) + ib) * 16, lane);
 #pragma unroll
             for (int ia = 0; ia < ST::NAT; ++ia) st[ia][ib] = M::mma(xf[ia], yf, st[ia][ib]);
+        }
+        if (ST::owns_vec(w)) {
+            if (kVecA) {
+                typename M::frag hi = one, lo = one;
+                if (u != nullptr) M::splat(u, k0, lane, hi, lo);
+#pragma unroll
+                for (int x = 0; x < ST::NVT; ++x) {
+                    const typename M::frag xv = M::ld_tr(tX, k0, (ST::vt0(w) + x) * 16, lane);
+                    va[x] = M::mma(xv, hi, va[x]);
+                    if (M::kSplitSplat && u != nullptr) va[x] = M::mma(xv, lo, va[x]);
+                }
+            }
+            if (kVecB) {
+                typename M::frag hi = one, lo = one;
+                if (v != nullptr) M::splat(v, k0, lane, hi, lo);
+#pragma unroll
+                for (int x = 0; x < ST::NVT; ++x) {
+                    const typename M::frag yv = M::ld_tr(tY, k0, (ST::vt0(w) + x) * 16, lane);
+                    vb[x] = M::mma(yv, hi, vb[x]);
+                    if (M::kSplitSplat && v != nullptr) vb[x] = M::mma(yv, lo, vb[x]);
+                }
+            }
         }
     }
 }
 
-// phi(Q_t) . wgt over all d features for the lane's token row t (each 16-lane
-// group covers a quarter of the features; the result is summed over groups).
-template <typename T, int D, int C>
-__device__ __forceinline__ float row_dot_quarters(const Tile<T, C, D>& tQf, const float* wgt, int t, int lane) {
-    constexpr int EV = Tile<T, C, D>::EV;
+// q_sum_t = sum_a phi(Q)[t][a] for the token tile t0.. as an MFMA against a
+// ones operand: every element of the returned accumulator column t holds q_sum_t.
+template <typename T, int D>
+__device__ __forceinline__ f32x4 tile_row_sums(const Tile<T, kC, D>& tQ, int t0, int lane) {
+    using M = Mma<T>;
+    const typename M::frag one = M::ones();
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int k0 = 0; k0 < D; k0 += M::KSTEP) acc = M::mma(one, M::ld(tQ, t0, k0, lane), acc);
+    return acc;
+}
+
+// phi(Q_t) . wgt over all d features for token row t: each 16-lane group
+// covers a quarter of the features; the result is summed over the groups.
+template <typename T, int D>
+__device__ __forceinline__ float row_dot_quarters(const Tile<T, kC, D>& tQ, const float* wgt, int t, int lane) {
+    constexpr int EV = Tile<T, kC, D>::EV;
     constexpr int GPQ = D / 4 / EV;
     static_assert(GPQ >= 1, "a quarter of the features must be whole granules");
     const int g = lane >> 4;
@@ -237,7 +274,7 @@ __device__ __forceinline__ float row_dot_quarters(const Tile<T, C, D>& tQf, cons
 #pragma unroll
     for (int x = 0; x < GPQ; ++x) {
         const int gi = g * GPQ + x;
-        const uint4 raw = *reinterpret_cast<const uint4*>(tQf.granule(t, gi));
+        const uint4 raw = *reinterpret_cast<const uint4*>(tQ.granule(t, gi));
         const T* p = reinterpret_cast<const T*>(&raw);
 #pragma unroll
         for (int e = 0; e < EV; ++e) s += to_f32(p[e]) * wgt[gi * EV + e];
@@ -245,7 +282,18 @@ __device__ __forceinline__ float row_dot_quarters(const Tile<T, C, D>& tQf, cons
     return sum_over_groups(s);
 }
 
-// Store / load 4 consecutive elements of a global row.
+// 4 consecutive raw input elements kept packed in registers (8 bytes in bf16,
+// 16 in fp32) until they are needed.
+template <typename T>
+struct Raw4 {
+    typedef typename std::conditional<sizeof(T) == 2, uint2, uint4>::type type;
+    type u;
+    __device__ __forceinline__ void load(const T* p) { u = *reinterpret_cast<const type*>(p); }
+    __device__ __forceinline__ void clear() { u = type{}; }
+    __device__ __forceinline__ float get(int e) const { return to_f32(reinterpret_cast<const T*>(&u)[e]); }
+};
+
+// 4 consecutive elements of a global row.
 __device__ __forceinline__ void gstore4(float* p, f32x4 a) { *reinterpret_cast<f32x4*>(p) = a; }
 __device__ __forceinline__ void gstore4(bf16* p, f32x4 a) {
     bf16 h[4] = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
@@ -257,32 +305,5 @@ __device__ __forceinline__ f32x4 gload4(const bf16* p) {
     const bf16* h = reinterpret_cast<const bf16*>(&u);
     return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
 }
-// 4 consecutive elements of an LDS tile row as fp32.
-template <typename T, int R, int K>
-__device__ __forceinline__ f32x4 lds_load4(const Tile<T, R, K>& t, int r, int c) {
-    const T* p = &t.at(r, c);
-    return f32x4{to_f32(p[0]), to_f32(p[1]), to_f32(p[2]), to_f32(p[3])};
-}
-
-// Fragment of the lower-triangular ones matrix L[t][s] = (s <= t) for MFMA
-// operand row t (lane & 15 of the tile at row0) and k-step k0.
-template <typename T>
-struct OnesFrag;
-template <>
-struct OnesFrag<bf16> {
-    __device__ __forceinline__ static bf16x8 lower(int t, int k0, int lane) {
-        const int s0 = k0 + 8 * (lane >> 4);
-        bf16x8 f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = (bf16)(s0 + e <= t ? 1.f : 0.f);
-        return f;
-    }
-};
-template <>
-struct OnesFrag<float> {
-    __device__ __forceinline__ static float lower(int t, int k0, int lane) {
-        return (k0 + (lane >> 4)) <= t ? 1.f : 0.f;
-    }
-};
 
 }  // namespace la

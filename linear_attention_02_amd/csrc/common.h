@@ -1,8 +1,9 @@
 // common.h -- device helpers shared by the gfx950 linear-attention kernels.
 //
-// Everything here is written for CDNA4 (gfx950): 64-lane wavefronts, the
-// v_mfma_f32_16x16x32_bf16 / v_mfma_f32_16x16x4_f32 matrix instructions, and
-// LDS tiles with an XOR swizzle on 16-byte granules.
+// Written for CDNA4 (gfx950): 64-lane wavefronts, v_mfma_f32_16x16x32_bf16 and
+// v_mfma_f32_16x16x4_f32, LDS tiles with an XOR swizzle on 16-byte granules,
+// and the transposing LDS load ds_read_b64_tr_b16 for operands whose
+// contraction index runs along the tile's rows.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,9 +13,23 @@ namespace la {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+
+// Wave index as a wave-uniform (scalar) value, so branches on it are scalar.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// LDS writes of this wave become visible to this wave's later LDS reads
+// (LDS requests of one wave complete in order; this only stops the compiler
+// from reordering across the point and drains the queue).
+__device__ __forceinline__ void wave_lds_sync() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // ---- scalar conversions ------------------------------------------------------------
 __device__ __forceinline__ float to_f32(float x) { return x; }
@@ -25,33 +40,20 @@ __device__ __forceinline__ T from_f32(float x);
 template <>
 __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
-__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
-
-// Round a float through the operand type and back (the value the MFMA sees).
-template <typename OT>
-__device__ __forceinline__ float round_to(float x) { return to_f32(from_f32<OT>(x)); }
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // round to nearest even
 
 // ---- feature map phi(x) = elu(x) + 1 -------------------------------------------------
-// phi(x) = x + 1 (x > 0), exp(x) (x <= 0).  E(x) = phi(x) - 1 = elu(x).
-__device__ __forceinline__ float phi_f(float x) { return x > 0.f ? x + 1.f : __expf(x); }
-__device__ __forceinline__ float elu_f(float x) { return x > 0.f ? x : expm1f(x); }
+// phi(x) = x + 1 (x > 0), exp(x) (x <= 0);  E(x) = phi(x) - 1 = elu(x);
 // phi'(x) = 1 (x > 0), exp(x) (x <= 0).
+__device__ __forceinline__ float phi_f(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+__device__ __forceinline__ float elu_f(float x) { return x > 0.f ? x : __expf(x) - 1.f; }
 __device__ __forceinline__ float dphi_f(float x) { return x > 0.f ? 1.f : __expf(x); }
 
-// ---- 16-byte vectors of input elements -------------------------------------------------
-template <typename T>
-struct Vec16 {
-    static constexpr int EV = 16 / (int)sizeof(T);  // elements per 16 bytes
-    uint4 raw;
-    __device__ __forceinline__ float get(int e) const {
-        const T* p = reinterpret_cast<const T*>(&raw);
-        return to_f32(p[e]);
-    }
-    __device__ __forceinline__ void set(int e, float x) {
-        T* p = reinterpret_cast<T*>(&raw);
-        p[e] = from_f32<T>(x);
-    }
-};
+// 1/x to within an ulp: hardware reciprocal refined by one Newton step.
+__device__ __forceinline__ float rcp_f(float x) {
+    float r = __builtin_amdgcn_rcpf(x);
+    return r * (2.f - x * r);
+}
 
 template <typename T>
 __device__ __forceinline__ uint4 load16(const T* p) {
@@ -60,9 +62,8 @@ __device__ __forceinline__ uint4 load16(const T* p) {
 
 // ---- swizzled LDS tiles ----------------------------------------------------------------
 // ROWS x COLS elements of OT, row-major, with the 16-byte granule index of each
-// row XOR-ed by a row-dependent value.  MFMA operand reads (16 rows x one
-// granule) and transposed scalar writes (8 rows x one column) then spread over
-// the LDS banks.
+// row XOR-ed by a row-dependent value so that 16-row operand reads, 8-row
+// granule writes and 4-row transposing reads all spread over the banks.
 template <typename OT, int ROWS, int COLS>
 struct Tile {
     static constexpr int EV = 16 / (int)sizeof(OT);
@@ -71,21 +72,33 @@ struct Tile {
     static_assert(G >= 4 && (G & (G - 1)) == 0, "granules per row must be a power of two >= 4");
     static constexpr int kElems = ROWS * COLS;
     OT* p;
-    __device__ __forceinline__ static int swz(int r) { return (r + (r >> 3)) & (G - 1); }
+    // 16-byte granule permutation of row r.  With 32 four-byte banks (128 B):
+    //  - 16 lanes reading one granule of 16 consecutive rows hit 8 distinct bank
+    //    groups per 8 rows (operand loads);
+    //  - 16 lanes of a transposing load reading two adjacent granules of 4
+    //    consecutive rows hit 8 distinct bank groups;
+    //  - 8 (G >= 8) or 4 (G == 4) lanes writing the granules of a row never collide.
+    __device__ __forceinline__ static int swz(int r) {
+        return G >= 8 ? 2 * (r & 3) + ((r >> 2) & 1) : 2 * ((r >> 1) & 1) + ((r >> 2) & 1);
+    }
     __device__ __forceinline__ int off(int r, int c) const {
         return r * COLS + (((c / EV) ^ swz(r)) * EV) + (c % EV);
     }
-    __device__ __forceinline__ OT* granule(int r, int gi) const {
-        return p + r * COLS + ((gi ^ swz(r)) * EV);
-    }
+    __device__ __forceinline__ OT* granule(int r, int gi) const { return p + r * COLS + ((gi ^ swz(r)) * EV); }
     __device__ __forceinline__ OT& at(int r, int c) const { return p[off(r, c)]; }
 };
 
-// ---- MFMA ------------------------------------------------------------------------------
-// 16x16 output tile D[i][j] += sum_k X[i][k] * Y[j][k].  Lane l supplies row
-// (l & 15) of X and of Y; the k values it supplies are the same for X and Y,
-// so the result does not depend on how the hardware orders k within a step.
-// The accumulator holds D[4 * (l >> 4) + r][l & 15] in element r.
+// ---- MFMA operands ---------------------------------------------------------------------
+// A 16x16 output tile D[i][j] += sum_k X[i][k] Y[j][k].  Lane l supplies row
+// (l & 15) of X and of Y with the same k values, so the result does not depend
+// on how the instruction orders k inside a step.  The accumulator holds
+// D[4 (l >> 4) + r][l & 15] in element r.
+//
+//   ld    : operand rows are tile rows row0.., k runs along the tile's columns;
+//   ld_tr : operand rows are tile columns col0.., k runs along the tile's rows
+//           (for bf16 two ds_read_b64_tr_b16: within each 16-lane group, lane
+//           j of the result holds column col0 + j at 4 consecutive rows);
+//   splat : every operand row is the same vector v[k] (from fp32 in LDS).
 template <typename OT>
 struct Mma;
 
@@ -93,11 +106,39 @@ template <>
 struct Mma<bf16> {
     static constexpr int KSTEP = 32;
     typedef bf16x8 frag;
-    template <int ROWS, int COLS>
-    __device__ __forceinline__ static frag load(const Tile<bf16, ROWS, COLS>& t, int row0, int k0,
-                                                int lane) {
+    template <int R, int K>
+    __device__ __forceinline__ static frag ld(const Tile<bf16, R, K>& t, int row0, int k0, int lane) {
         return *reinterpret_cast<const frag*>(t.granule(row0 + (lane & 15), (k0 >> 3) + (lane >> 4)));
     }
+    template <int R, int K>
+    __device__ __forceinline__ static frag ld_tr(const Tile<bf16, R, K>& t, int k0, int col0, int lane) {
+        typedef __attribute__((address_space(3))) bf16x4 lds4;
+        const int j = lane & 15;
+        const int r = k0 + 8 * (lane >> 4) + (j >> 2);
+        const int c = col0 + 4 * (j & 3);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(&t.at(r, c)));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(&t.at(r + 4, c)));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    // v: fp32 vector in LDS indexed by k; hi/lo split keeps ~16 bits of each value.
+    __device__ __forceinline__ static void splat(const float* v, int k0, int lane, frag& hi, frag& lo) {
+        const f32x4* p = reinterpret_cast<const f32x4*>(v + k0 + 8 * (lane >> 4));
+        const f32x4 a = p[0], b = p[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            hi[e] = (bf16)a[e];
+            lo[e] = (bf16)(a[e] - (float)hi[e]);
+            hi[4 + e] = (bf16)b[e];
+            lo[4 + e] = (bf16)(b[e] - (float)hi[4 + e]);
+        }
+    }
+    __device__ __forceinline__ static frag ones() {
+        frag f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = (bf16)1.f;
+        return f;
+    }
+    static constexpr bool kSplitSplat = true;
     __device__ __forceinline__ static f32x4 mma(frag x, frag y, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
     }
@@ -107,11 +148,20 @@ template <>
 struct Mma<float> {
     static constexpr int KSTEP = 4;
     typedef float frag;
-    template <int ROWS, int COLS>
-    __device__ __forceinline__ static frag load(const Tile<float, ROWS, COLS>& t, int row0, int k0,
-                                                int lane) {
+    template <int R, int K>
+    __device__ __forceinline__ static frag ld(const Tile<float, R, K>& t, int row0, int k0, int lane) {
         return t.at(row0 + (lane & 15), k0 + (lane >> 4));
     }
+    template <int R, int K>
+    __device__ __forceinline__ static frag ld_tr(const Tile<float, R, K>& t, int k0, int col0, int lane) {
+        return t.at(k0 + (lane >> 4), col0 + (lane & 15));
+    }
+    __device__ __forceinline__ static void splat(const float* v, int k0, int lane, frag& hi, frag& lo) {
+        hi = v[k0 + (lane >> 4)];
+        lo = 0.f;
+    }
+    __device__ __forceinline__ static frag ones() { return 1.f; }
+    static constexpr bool kSplitSplat = false;
     __device__ __forceinline__ static f32x4 mma(frag x, frag y, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, c, 0, 0, 0);
     }
@@ -119,9 +169,8 @@ struct Mma<float> {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// Write an accumulator tile transposed: element (i, j) goes to dst[col0 + j][row0 + i].
-// Each lane writes 4 consecutive elements of one destination row (8 bytes for
-// bf16, 16 bytes for fp32; row0 is a multiple of 16, so they share a granule).
+// Write an accumulator tile transposed: element (i, j) goes to dst[col0 + j][row0 + i];
+// each lane writes 4 consecutive elements of one row (8 bytes in bf16, 16 in fp32).
 __device__ __forceinline__ void store4(bf16* p, f32x4 a) {
     bf16 h[4] = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
     *reinterpret_cast<uint2*>(p) = *reinterpret_cast<const uint2*>(h);
@@ -129,19 +178,16 @@ __device__ __forceinline__ void store4(bf16* p, f32x4 a) {
 __device__ __forceinline__ void store4(float* p, f32x4 a) { *reinterpret_cast<f32x4*>(p) = a; }
 
 template <typename OT, int ROWS, int COLS>
-__device__ __forceinline__ void store_T(const Tile<OT, ROWS, COLS>& dst, int row0, int col0, f32x4 acc,
-                                        int lane) {
+__device__ __forceinline__ void store_T(const Tile<OT, ROWS, COLS>& dst, int row0, int col0, f32x4 acc, int lane) {
     store4(&dst.at(col0 + (lane & 15), row0 + 4 * (lane >> 4)), acc);
 }
 
-// Write an accumulator tile in place: element (i, j) goes to dst[row0 + i][col0 + j].
-template <typename OT, int ROWS, int COLS>
-__device__ __forceinline__ void store_N(const Tile<OT, ROWS, COLS>& dst, int row0, int col0, f32x4 acc,
-                                        int lane) {
-    const int c = col0 + (lane & 15);
-    const int r = row0 + 4 * (lane >> 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dst.at(r + e, c) = from_f32<OT>(acc[e]);
+// 4 consecutive elements of an LDS tile row as fp32.
+__device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 lds4(const bf16* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    const bf16* h = reinterpret_cast<const bf16*>(&u);
+    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
 }
 
 // ---- wave reductions -------------------------------------------------------------------
@@ -152,7 +198,7 @@ __device__ __forceinline__ float sum_over_groups(float x) {
     return x;
 }
 
-// Sum over aligned groups of `width` consecutive lanes (width a power of two <= 64).
+// Sum over aligned groups of WIDTH consecutive lanes (WIDTH a power of two <= 64).
 template <int WIDTH>
 __device__ __forceinline__ float sum_lanes(float x) {
 #pragma unroll

@@ -13,6 +13,12 @@ namespace la {
 constexpr int kChunk = 64;       // tokens per chunk (one MFMA-tiled block of the scan)
 constexpr int kBlock = 256;      // threads per workgroup (4 wavefronts)
 
+// Minimum wavefronts per SIMD the register allocator must allow for the large
+// per-chunk kernels (2 = two resident workgroups per CU).
+#ifndef LA_HEAVY_WAVES_PER_SIMD
+#define LA_HEAVY_WAVES_PER_SIMD 2
+#endif
+
 enum DType { kF32 = 0, kBF16 = 1 };
 
 // Sequence segmentation: each (head, segment) pair is one workgroup; a segment
