@@ -2,17 +2,19 @@
 """Benchmark of the kernelized linear-attention hot path on one MI355X.
 
 A step is one causal forward plus one causal backward (la_forward_causal +
-la_backward_causal through the C ABI) over the workload B=4, H=16, N=4096,
+la_backward_causal through the C ABI, the backward reading the carried state
+the forward saved, as a training step would) over the workload B=4, H=16, N=4096,
 d=64, bf16 inputs ~ N(0,1)/sqrt(d), chunk 64.  W untimed warmup steps, then K
 steps timed back to back between two device synchronisations.  Inputs are
 resident in HBM before the timed region; the step rotates over several input
 sets whose total exceeds the 256 MB last-level cache, so each step starts with
-its inputs in HBM, not in cache.
+its inputs in HBM, not in cache.  The per-kernel event times come from a second
+run of the same K steps right after the timed one.
 
 The JSON line also carries
   * roofline    : the dominant kernel's algorithmic bytes per launch over its
                   average duration (HIP events around every launch, recorded
-                  on the library's stream during the timed steps) against the
+                  on the library's stream over a second run of the timed steps) against the
                   8 TB/s HBM peak;
   * step_roofline: the same for the whole step (22 d bytes per token-head);
   * calls       : the other measured calls (non-causal forward at the same
@@ -85,15 +87,19 @@ def sequence_roofline(stats, B, H, N, d, steps):
 
 
 def time_steps(fn, nsets, warmup, steps, la, torch):
+    """Wall time of `steps` back-to-back steps, then per-kernel event times over a second run of them."""
     for i in range(warmup):
         fn(i % nsets)
     torch.cuda.synchronize()
-    la.profile_enable(True)
     t0 = time.perf_counter()
     for i in range(steps):
         fn(i % nsets)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    la.profile_enable(True)
+    for i in range(steps):
+        fn(i % nsets)
+    torch.cuda.synchronize()
     stats = kernel_stats(la.profile_entries())
     la.profile_enable(False)
     return dt, stats
@@ -109,11 +115,12 @@ def bench_mid(args, la, inp, torch):
     grads = tuple(torch.empty_like(sets[0][0]) for _ in range(3))
     wsf = torch.empty(la.workspace_size(la.LA_OP_FWD_CAUSAL, B, H, N, d, w.dtype), dtype=torch.uint8, device="cuda")
     wsb = torch.empty(la.workspace_size(la.LA_OP_BWD_CAUSAL, B, H, N, d, w.dtype), dtype=torch.uint8, device="cuda")
+    saved = la.new_saved_state(sets[0][0])
 
     def step(i):
         q, k, v, do = sets[i]
-        la.la_forward_causal(q, k, v, out=o, workspace=wsf)
-        la.la_backward_causal(q, k, v, do, out=grads, workspace=wsb)
+        la.la_forward_causal(q, k, v, out=o, workspace=wsf, saved_state=saved)
+        la.la_backward_causal(q, k, v, do, out=grads, workspace=wsb, saved_state=saved)
 
     dt, stats = time_steps(step, nsets, args.warmup, args.steps, la, torch)
     T = B * H * N
@@ -164,14 +171,15 @@ def bench_calls(args, la, inp, torch, mid_set):
                       device="cuda")
     wsb = torch.empty(la.workspace_size(la.LA_OP_BWD_CAUSAL, w.B, w.H, w.N, w.d, w.dtype), dtype=torch.uint8,
                       device="cuda")
+    saved = la.new_saved_state(q)
 
     def long_step(i):
-        la.la_forward_causal(q, k, v, out=o, workspace=wsf)
-        la.la_backward_causal(q, k, v, do, out=g, workspace=wsb)
+        la.la_forward_causal(q, k, v, out=o, workspace=wsf, saved_state=saved)
+        la.la_backward_causal(q, k, v, do, out=g, workspace=wsb, saved_state=saved)
 
     calls["long_causal_fwd_bwd"] = bench_call("long", long_step, 2, 10, w.B * w.N,
                                               11 * unit_bytes(w.B, w.H, w.N, w.d), la, torch)
-    del q, k, v, do, o, g, wsf, wsb
+    del q, k, v, do, o, g, wsf, wsb, saved
 
     w = inp.VERYLONG
     torch.cuda.empty_cache()

@@ -77,15 +77,23 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
                                int64_t H, int64_t N, int64_t d, la_dtype dt, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* Bytes of the opaque forward state that la_forward_causal can save for
+ * la_backward_causal on the same inputs (the carried (S, z) at the start of
+ * every sequence segment).  Pure host computation. */
+la_status la_saved_state_size(int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt,
+                              size_t* bytes_out);
+
 /* Causal forward (the recurrent form of "Why It Matters", evaluated chunk by
  * chunk): O_i = phi(Q_i)^T S_i / phi(Q_i)^T z_i with S_i, z_i summed over keys
  * j <= i.  Optional outputs (NULL to skip): den_out [B][H][N] fp32 holds
  * phi(Q_i)^T z_i; S_out [B][H][d][d] and z_out [B][H][d] receive the state
- * after the last token, ready for la_decode_step. */
+ * after the last token, ready for la_decode_step; saved_state (device,
+ * saved_state_bytes >= la_saved_state_size()) receives the per-segment carried
+ * state so that la_backward_causal on the same q, k, v need not rebuild it. */
 la_status la_forward_causal(const void* q, const void* k, const void* v, void* o, float* den_out,
-                            float* S_out, float* z_out, int64_t B, int64_t H, int64_t N, int64_t d,
-                            int chunk, la_dtype dt, void* workspace, size_t workspace_bytes,
-                            void* stream);
+                            float* S_out, float* z_out, void* saved_state, size_t saved_state_bytes,
+                            int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Causal backward: dQ, dK, dV of L = sum(dO * O) for the causal forward, by
  * the chain rule (the arXiv 2510.21956 abstract on vix.ing states that a
@@ -96,11 +104,15 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* o
  *   R_j = sum_{i>=j} phi(Q_i) G_i^T, r_j = sum_{i>=j} g_i phi(Q_i),
  * then dQ = dphi(Q) * phi'(Q), dK = dphi(K) * phi'(K).  O and den are
  * recomputed in fp32 from q, k, v; the forward's outputs are not inputs here.
+ * saved_state (nullable) is the buffer a la_forward_causal call on the same
+ * q, k, v and shape filled; when NULL the carried state is rebuilt from k, v.
+ * Either way the results are bitwise the same.
  * In: q, k, v, dout [B][H][N][d].  Out: dq, dk, dv [B][H][N][d]. */
 la_status la_backward_causal(const void* q, const void* k, const void* v, const void* dout,
-                             void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
-                             int64_t d, int chunk, la_dtype dt, void* workspace,
-                             size_t workspace_bytes, void* stream);
+                             void* dq, void* dk, void* dv, const void* saved_state,
+                             size_t saved_state_bytes, int64_t B, int64_t H, int64_t N, int64_t d,
+                             int chunk, la_dtype dt, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* One recurrent decode step per (b, h), in place ("Why It Matters": constant
  * memory per step): S += phi(k) v^T, z += phi(k), then

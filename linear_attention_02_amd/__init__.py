@@ -19,8 +19,10 @@ from ._binding import (  # noqa: F401
     la_forward_causal,
     la_forward_noncausal,
     load_library,
+    new_saved_state,
     profile_enable,
     profile_entries,
+    saved_state_size,
     workspace_size,
 )
 

@@ -20,7 +20,7 @@ LA_OK, LA_ERR_INVALID_ARGUMENT, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP
 LA_F32, LA_BF16 = 0, 1
 LA_OP_FWD_NONCAUSAL, LA_OP_FWD_CAUSAL, LA_OP_BWD_CAUSAL = 0, 1, 2
 
-EXPORTS = ("la_workspace_size", "la_forward_noncausal", "la_forward_causal", "la_backward_causal",
+EXPORTS = ("la_workspace_size", "la_saved_state_size", "la_forward_noncausal", "la_forward_causal", "la_backward_causal",
            "la_decode_step", "la_status_string", "la_last_error_message", "la_version",
            "la_profile_enable", "la_profile_count", "la_profile_entry")
 
@@ -50,10 +50,12 @@ def load_library(path: str | None = None):
     lib.la_workspace_size.argtypes = [i32, i64, i64, i64, i64, i32, i32, ctypes.POINTER(sz)]
     lib.la_forward_noncausal.restype = i32
     lib.la_forward_noncausal.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]
+    lib.la_saved_state_size.restype = i32
+    lib.la_saved_state_size.argtypes = [i64, i64, i64, i64, i32, i32, ctypes.POINTER(sz)]
     lib.la_forward_causal.restype = i32
-    lib.la_forward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.la_forward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.la_backward_causal.restype = i32
-    lib.la_backward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.la_backward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.la_decode_step.restype = i32
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.la_status_string.restype = ctypes.c_char_p
@@ -117,6 +119,22 @@ def workspace_size(op: int, B: int, H: int, N: int, d: int, dtype: torch.dtype, 
     return int(out.value)
 
 
+def saved_state_size(B: int, H: int, N: int, d: int, dtype: torch.dtype, chunk: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().la_saved_state_size(B, H, N, d, chunk, _dtype_code(dtype), ctypes.byref(out)))
+    return int(out.value)
+
+
+def new_saved_state(q, chunk: int = 0):
+    """An uninitialised buffer for the forward state of causal calls on tensors shaped like q."""
+    B, H, N, d = q.shape
+    return torch.empty(max(1, saved_state_size(B, H, N, d, q.dtype, chunk)), dtype=torch.uint8, device=q.device)
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def _workspace(op, B, H, N, d, dtype, device, chunk, workspace):
     need = workspace_size(op, B, H, N, d, dtype, chunk)
     if workspace is not None:
@@ -137,8 +155,11 @@ def la_forward_noncausal(q, k, v, *, out=None, workspace=None):
     return o
 
 
-def la_forward_causal(q, k, v, *, chunk=0, return_den=False, return_state=False, out=None, workspace=None):
-    """Causal forward; returns o, plus den [B,H,N] and/or the final (S [B,H,d,d], z [B,H,d]) if asked."""
+def la_forward_causal(q, k, v, *, chunk=0, return_den=False, return_state=False, out=None, workspace=None,
+                      saved_state=None):
+    """Causal forward; returns o, plus den [B,H,N] and/or the final (S [B,H,d,d], z [B,H,d]) if asked.
+
+    saved_state (optional, from new_saved_state) receives the carried state for la_backward_causal."""
     B, H, N, d = _check_seq(q, k, v)
     o = torch.empty_like(q) if out is None else out
     den = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_den else None
@@ -147,8 +168,8 @@ def la_forward_causal(q, k, v, *, chunk=0, return_den=False, return_state=False,
     ws = _workspace(LA_OP_FWD_CAUSAL, B, H, N, d, q.dtype, q.device, chunk, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load_library().la_forward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den), _ptr(S), _ptr(z),
-                                            B, H, N, d, chunk, _dtype_code(q.dtype), _ptr(ws), nbytes,
-                                            _stream(q.device)))
+                                            _ptr(saved_state), _nbytes(saved_state), B, H, N, d, chunk,
+                                            _dtype_code(q.dtype), _ptr(ws), nbytes, _stream(q.device)))
     res = [o]
     if return_den:
         res.append(den)
@@ -157,8 +178,10 @@ def la_forward_causal(q, k, v, *, chunk=0, return_den=False, return_state=False,
     return res[0] if len(res) == 1 else tuple(res)
 
 
-def la_backward_causal(q, k, v, dout, *, chunk=0, out=None, workspace=None):
-    """Gradients (dq, dk, dv) of sum(dout * la_forward_causal(q, k, v))."""
+def la_backward_causal(q, k, v, dout, *, chunk=0, out=None, workspace=None, saved_state=None):
+    """Gradients (dq, dk, dv) of sum(dout * la_forward_causal(q, k, v)).
+
+    saved_state: the buffer a la_forward_causal call on the same q, k, v filled (optional)."""
     B, H, N, d = _check_seq(q, k, v, dout)
     if out is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
@@ -167,8 +190,8 @@ def la_backward_causal(q, k, v, dout, *, chunk=0, out=None, workspace=None):
     ws = _workspace(LA_OP_BWD_CAUSAL, B, H, N, d, q.dtype, q.device, chunk, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load_library().la_backward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-                                             B, H, N, d, chunk, _dtype_code(q.dtype), _ptr(ws), nbytes,
-                                             _stream(q.device)))
+                                             _ptr(saved_state), _nbytes(saved_state), B, H, N, d, chunk,
+                                             _dtype_code(q.dtype), _ptr(ws), nbytes, _stream(q.device)))
     return dq, dk, dv
 
 
@@ -213,13 +236,15 @@ def profile_entries():
 class _CausalLinearAttention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v):
-        ctx.save_for_backward(q, k, v)
-        return la_forward_causal(q, k, v)
+        st = new_saved_state(q)
+        o = la_forward_causal(q, k, v, saved_state=st)
+        ctx.save_for_backward(q, k, v, st)
+        return o
 
     @staticmethod
     def backward(ctx, dout):
-        q, k, v = ctx.saved_tensors
-        return la_backward_causal(q, k, v, dout.contiguous())
+        q, k, v, st = ctx.saved_tensors
+        return la_backward_causal(q, k, v, dout.contiguous(), saved_state=st)
 
 
 def causal_linear_attention(q, k, v):

@@ -136,6 +136,11 @@ Layout layout(la_op op, int64_t B, int64_t H, int64_t N, int64_t d) {
     return L;
 }
 
+size_t saved_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+    const la::SegPlan p = la::plan_segments(B * H, N);
+    return (size_t)(B * H) * p.nseg * la::rec_floats(d) * sizeof(float);
+}
+
 la_status check_workspace(const Layout& L, const void* ws, size_t ws_bytes) {
     if (L.bytes == 0) return LA_OK;
     if ((int64_t)L.plan.nseg * L.heads > ((int64_t)1 << 24))
@@ -214,6 +219,16 @@ la_status la_workspace_size(la_op op, int64_t B, int64_t H, int64_t N, int64_t d
     return LA_OK;
 }
 
+la_status la_saved_state_size(int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt,
+                              size_t* bytes_out) {
+    if (bytes_out == nullptr) return fail(LA_ERR_INVALID_ARGUMENT, "bytes_out is NULL");
+    bool empty = false;
+    la_status st = check_shape(B, H, N, d, chunk, dt, &empty);
+    if (st != LA_OK) return st;
+    *bytes_out = empty ? 0 : saved_bytes(B, H, N, d);
+    return LA_OK;
+}
+
 la_status la_forward_noncausal(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
                                int64_t N, int64_t d, la_dtype dt, void* workspace, size_t workspace_bytes,
                                void* stream) {
@@ -249,8 +264,9 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
 }
 
 la_status la_forward_causal(const void* q, const void* k, const void* v, void* o, float* den_out, float* S_out,
-                            float* z_out, int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            float* z_out, void* saved_state, size_t saved_state_bytes, int64_t B, int64_t H,
+                            int64_t N, int64_t d, int chunk, la_dtype dt, void* workspace, size_t workspace_bytes,
+                            void* stream) {
     bool empty = false;
     la_status st = check_shape(B, H, N, d, chunk, dt, &empty);
     if (st != LA_OK) return st;
@@ -258,11 +274,15 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* o
     if (!q || !k || !v || !o) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-NULL");
     const size_t tb = (size_t)B * H * N * d * elem_size(dt);
     const Range in[] = {{"q", q, tb}, {"k", k, tb}, {"v", v, tb}};
+    const size_t sb = saved_state ? saved_bytes(B, H, N, d) : 0;
+    if (saved_state && saved_state_bytes < sb)
+        return fail(LA_ERR_INVALID_ARGUMENT, "saved_state has %zu bytes; %zu are needed", saved_state_bytes, sb);
     const Range out[] = {{"o", o, tb},
                          {"den_out", den_out, (size_t)B * H * N * sizeof(float)},
                          {"S_out", S_out, (size_t)B * H * d * d * sizeof(float)},
-                         {"z_out", z_out, (size_t)B * H * d * sizeof(float)}};
-    if ((st = check_ptrs(in, 3, out, 4)) != LA_OK) return st;
+                         {"z_out", z_out, (size_t)B * H * d * sizeof(float)},
+                         {"saved_state", saved_state, sb}};
+    if ((st = check_ptrs(in, 3, out, 5)) != LA_OK) return st;
     if (B == 0 || H == 0) return LA_OK;
     const int64_t BH = B * H;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -282,7 +302,8 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* o
         if (overlap(wsr[0], r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
 
     char* ws = static_cast<char*>(workspace);
-    float* rec = reinterpret_cast<float*>(ws + L.rec);
+    // The segment records go straight into the saved state when one is asked for.
+    float* rec = saved_state ? static_cast<float*>(saved_state) : reinterpret_cast<float*>(ws + L.rec);
     float* total = reinterpret_cast<float*>(ws + L.total);
     const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
     const bool want_state = S_out != nullptr || z_out != nullptr;
@@ -298,8 +319,9 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* o
 }
 
 la_status la_backward_causal(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
-                             void* dv, int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+                             void* dv, const void* saved_state, size_t saved_state_bytes, int64_t B, int64_t H,
+                             int64_t N, int64_t d, int chunk, la_dtype dt, void* workspace, size_t workspace_bytes,
+                             void* stream) {
     bool empty = false;
     la_status st = check_shape(B, H, N, d, chunk, dt, &empty);
     if (st != LA_OK) return st;
@@ -307,29 +329,35 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
     if (!q || !k || !v || !dout || !dq || !dk || !dv)
         return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v, dout, dq, dk and dv must be non-NULL");
     const size_t tb = (size_t)B * H * N * d * elem_size(dt);
-    const Range in[] = {{"q", q, tb}, {"k", k, tb}, {"v", v, tb}, {"dout", dout, tb}};
+    const size_t sb = saved_state ? saved_bytes(B, H, N, d) : 0;
+    if (saved_state && saved_state_bytes < sb)
+        return fail(LA_ERR_INVALID_ARGUMENT, "saved_state has %zu bytes; %zu are needed", saved_state_bytes, sb);
+    const Range in[] = {{"q", q, tb}, {"k", k, tb}, {"v", v, tb}, {"dout", dout, tb}, {"saved_state", saved_state, sb}};
     const Range out[] = {{"dq", dq, tb}, {"dk", dk, tb}, {"dv", dv, tb}};
-    if ((st = check_ptrs(in, 4, out, 3)) != LA_OK) return st;
+    if ((st = check_ptrs(in, 5, out, 3)) != LA_OK) return st;
     if (empty) return LA_OK;
     const Layout L = layout(LA_OP_BWD_CAUSAL, B, H, N, d);
     if ((st = check_workspace(L, workspace, workspace_bytes)) != LA_OK) return st;
     const Range wsr[] = {{"workspace", workspace, L.bytes}};
-    if ((st = check_ptrs(in, 4, wsr, 1)) != LA_OK) return st;
+    if ((st = check_ptrs(in, 5, wsr, 1)) != LA_OK) return st;
     for (const Range& r : out)
         if (overlap(wsr[0], r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
 
     char* ws = static_cast<char*>(workspace);
-    float* rec = reinterpret_cast<float*>(ws + L.rec);
+    float* rec = saved_state ? const_cast<float*>(static_cast<const float*>(saved_state))
+                             : reinterpret_cast<float*>(ws + L.rec);
     float* rrec = reinterpret_cast<float*>(ws + L.rrec);
     float* rowstat = reinterpret_cast<float*>(ws + L.rowstat);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t BH = B * H;
     const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
     hipError_t e;
-    if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
-        return hip_fail(e, "seg_state launch");
-    if ((e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, nullptr, BH, L.plan.nseg, true, s); })) != hipSuccess)
-        return hip_fail(e, "scan launch");
+    if (saved_state == nullptr) {
+        if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
+            return hip_fail(e, "seg_state launch");
+        if ((e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, nullptr, BH, L.plan.nseg, true, s); })) != hipSuccess)
+            return hip_fail(e, "scan launch");
+    }
     if ((e = timed("bwd_prefix", s, [&] { return la::launch_bwd_prefix(idt, (int)d, q, k, v, dout, dq, rowstat, rrec, rec, BH, N, L.plan, s); })) !=
         hipSuccess)
         return hip_fail(e, "bwd_prefix launch");

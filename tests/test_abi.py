@@ -55,6 +55,17 @@ def ws(lib, op, B, H, N, d, chunk=0, dt=la.LA_BF16):
     return st, out.value
 
 
+def test_saved_state_size(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.la_saved_state_size(4, 16, 4096, 64, 0, la.LA_BF16, ctypes.byref(out)) == 0
+    n = out.value
+    assert n > 0 and n % 16 == 0
+    # one carried state (d*d + 2d floats) per head and segment, at least one segment per head
+    assert n >= 4 * 16 * (64 * 64 + 128) * 4
+    assert lib.la_saved_state_size(4, 16, 0, 64, 0, la.LA_BF16, ctypes.byref(out)) == 0 and out.value == 0
+    assert lib.la_saved_state_size(4, 16, 64, 40, 0, la.LA_BF16, ctypes.byref(out)) == 2
+
+
 def test_workspace_sizes(lib):
     for op in (la.LA_OP_FWD_NONCAUSAL, la.LA_OP_FWD_CAUSAL, la.LA_OP_BWD_CAUSAL):
         st, n = ws(lib, op, 4, 16, 4096, 64)
@@ -76,8 +87,8 @@ A = 0x10000000  # fake, 256-byte aligned device addresses; never dereferenced
 
 
 def fwd_causal(lib, q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000, den=None, S=None, z=None,
-               B=1, H=1, N=64, d=64, chunk=0, dt=la.LA_BF16, wsp=A + 0x4000000, wsb=0):
-    return lib.la_forward_causal(q, k, v, o, den, S, z, B, H, N, d, chunk, dt, wsp, wsb, None)
+               saved=None, saved_bytes=0, B=1, H=1, N=64, d=64, chunk=0, dt=la.LA_BF16, wsp=A + 0x4000000, wsb=0):
+    return lib.la_forward_causal(q, k, v, o, den, S, z, saved, saved_bytes, B, H, N, d, chunk, dt, wsp, wsb, None)
 
 
 def test_forward_causal_validation(lib):
@@ -92,6 +103,8 @@ def test_forward_causal_validation(lib):
     assert fwd_causal(lib, wsp=A + 0x4000010, wsb=1 << 30) == 1   # workspace misaligned
     assert fwd_causal(lib, wsp=A + 0x2000000, wsb=1 << 30) == 1  # workspace overlaps v
     assert fwd_causal(lib, B=0) == 0                         # nothing to do, no launch
+    assert fwd_causal(lib, saved=A + 0x5000000, saved_bytes=8, wsb=1 << 30) == 1       # saved state too small
+    assert fwd_causal(lib, saved=A + 0x3000000, saved_bytes=1 << 20, wsb=1 << 30) == 1  # saved state overlaps o
     msg = lib.la_last_error_message()
     assert isinstance(msg, bytes)
 
@@ -103,13 +116,15 @@ def test_forward_noncausal_and_backward_validation(lib):
     assert f(A, A + 0x1000000, A + 0x2000000, A + 0x3000000, 1, 1, 0, 64, 1, None, 0, None) == 0
     b = lib.la_backward_causal
     args = [A, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000, A + 0x5000000, A + 0x6000000]
-    assert b(*args, 1, 1, 64, 64, 0, 1, A + 0x7000000, 8, None) == 3
+    assert b(*args, None, 0, 1, 1, 64, 64, 0, 1, A + 0x7000000, 8, None) == 3
     bad = list(args)
     bad[5] = args[4]                                          # dk aliases dq
-    assert b(*bad, 1, 1, 64, 64, 0, 1, A + 0x7000000, 1 << 30, None) == 1
+    assert b(*bad, None, 0, 1, 1, 64, 64, 0, 1, A + 0x7000000, 1 << 30, None) == 1
     bad = list(args)
     bad[6] = args[3]                                          # dv aliases dout
-    assert b(*bad, 1, 1, 64, 64, 0, 1, A + 0x7000000, 1 << 30, None) == 1
+    assert b(*bad, None, 0, 1, 1, 64, 64, 0, 1, A + 0x7000000, 1 << 30, None) == 1
+    assert b(*args, A + 0x8000000, 4, 1, 1, 64, 64, 0, 1, A + 0x7000000, 1 << 30, None) == 1  # saved state short
+    assert b(*args, A + 0x4000000, 1 << 20, 1, 1, 64, 64, 0, 1, A + 0x7000000, 1 << 30, None) == 1  # overlaps dq
 
 
 def test_decode_validation(lib):
