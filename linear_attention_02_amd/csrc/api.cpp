@@ -123,10 +123,10 @@ Layout layout(la_op op, int64_t B, int64_t H, int64_t N, int64_t d) {
     size_t off = 0;
     L.rec = off;
     off += align_up(recb);
-    if (op == LA_OP_FWD_NONCAUSAL || op == LA_OP_FWD_CAUSAL) {
+    if (op == LA_OP_FWD_NONCAUSAL) {
         L.total = off;
         off += align_up((size_t)BH * la::rec_floats(d) * sizeof(float));
-    } else {
+    } else if (op == LA_OP_BWD_CAUSAL) {
         L.rrec = off;
         off += align_up(recb);
         L.rowstat = off;
@@ -256,8 +256,8 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
     hipError_t e;
     if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
         return hip_fail(e, "seg_state launch");
-    if ((e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, total, BH, L.plan.nseg, false, s); })) != hipSuccess)
-        return hip_fail(e, "scan launch");
+    if ((e = timed("total", s, [&] { return la::launch_total((int)d, rec, total, BH, L.plan.nseg, s); })) != hipSuccess)
+        return hip_fail(e, "total launch");
     if ((e = timed("noncausal_fwd", s, [&] { return la::launch_noncausal_fwd(idt, (int)d, q, o, total, BH, N, L.plan, s); })) != hipSuccess)
         return hip_fail(e, "noncausal_fwd launch");
     return LA_OK;
@@ -304,17 +304,13 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* o
     char* ws = static_cast<char*>(workspace);
     // The segment records go straight into the saved state when one is asked for.
     float* rec = saved_state ? static_cast<float*>(saved_state) : reinterpret_cast<float*>(ws + L.rec);
-    float* total = reinterpret_cast<float*>(ws + L.total);
     const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
-    const bool want_state = S_out != nullptr || z_out != nullptr;
     if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
         return hip_fail(e, "seg_state launch");
-    if ((e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, want_state ? total : nullptr, BH, L.plan.nseg, true, s); })) != hipSuccess)
-        return hip_fail(e, "scan launch");
-    if ((e = timed("causal_fwd", s, [&] { return la::launch_causal_fwd(idt, (int)d, q, k, v, o, den_out, rec, BH, N, L.plan, s); })) != hipSuccess)
+    if ((e = timed("causal_fwd", s, [&] {
+             return la::launch_causal_fwd(idt, (int)d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, L.plan, s);
+         })) != hipSuccess)
         return hip_fail(e, "causal_fwd launch");
-    if (want_state && (e = timed("final_state", s, [&] { return la::launch_final_state((int)d, total, S_out, z_out, BH, N, s); })) != hipSuccess)
-        return hip_fail(e, "final_state launch");
     return LA_OK;
 }
 
@@ -355,13 +351,10 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
     if (saved_state == nullptr) {
         if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
             return hip_fail(e, "seg_state launch");
-        if ((e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, nullptr, BH, L.plan.nseg, true, s); })) != hipSuccess)
-            return hip_fail(e, "scan launch");
     }
     if ((e = timed("bwd_prefix", s, [&] { return la::launch_bwd_prefix(idt, (int)d, q, k, v, dout, dq, rowstat, rrec, rec, BH, N, L.plan, s); })) !=
         hipSuccess)
         return hip_fail(e, "bwd_prefix launch");
-    if ((e = timed("rscan", s, [&] { return la::launch_rscan((int)d, rrec, BH, L.plan.nseg, s); })) != hipSuccess) return hip_fail(e, "rscan launch");
     if ((e = timed("bwd_suffix", s, [&] { return la::launch_bwd_suffix(idt, (int)d, q, k, v, dout, dk, dv, rowstat, rrec, BH, N, L.plan, s); })) !=
         hipSuccess)
         return hip_fail(e, "bwd_suffix launch");

@@ -57,10 +57,76 @@ struct ChunkRegs {
     __device__ __forceinline__ float get(int i, int e) const { return to_f32(reinterpret_cast<const T*>(&r[i])[e]); }
 };
 
-// phi(Q) row-major into LDS.
+// One 16-row token tile of a [N][D] input held in registers in MFMA operand
+// layout: lane l holds row (l & 15), 16-byte vector x at elements (4 x + g) EV
+// with g = l >> 4 -- for bf16 the k values of step 32 x, for fp32 those of the
+// steps 16 x + 4 e (element e), matching Mma's k order.  Rows at or beyond N read as 0.
 template <typename T, int D>
-__device__ __forceinline__ void stage_phi(const ChunkRegs<T, D>& cq, const Tile<T, kC, D>& tQ, int tid) {
-    using CR = ChunkRegs<T, D>;
+struct RowFrag {
+    using M = Mma<T>;
+    static constexpr int EV = 16 / (int)sizeof(T);
+    static constexpr int NR = D / (4 * EV);
+    static constexpr int NF = D / M::KSTEP;
+    static_assert(NR >= 1, "a row must cover the four lane groups");
+    uint4 r[NR];
+    __device__ __forceinline__ static int col(int x, int lane) { return (4 * x + (lane >> 4)) * EV; }
+    __device__ __forceinline__ void load(const T* head, int tok0, int N, int lane) {
+        const int tok = tok0 + (lane & 15);
+#pragma unroll
+        for (int x = 0; x < NR; ++x)
+            r[x] = tok < N ? load16(head + (int64_t)tok * D + col(x, lane)) : make_uint4(0, 0, 0, 0);
+    }
+    // f[k0 / KSTEP] = phi of the held elements as operands; returns the lane's
+    // part of sum_a phi(x_a) wgt[a] (fp32 weights in LDS).
+    __device__ __forceinline__ float phi_ops(typename M::frag* f, const float* wgt, int lane) const {
+        float dot = 0.f;
+#pragma unroll
+        for (int x = 0; x < NR; ++x) {
+            const T* h = reinterpret_cast<const T*>(&r[x]);
+            const int c = col(x, lane);
+            float y[EV];
+#pragma unroll
+            for (int e = 0; e < EV; e += 4) {
+                const f32x4 wv = *reinterpret_cast<const f32x4*>(wgt + c + e);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    y[e + u] = phi_f(to_f32(h[e + u]));
+                    dot += y[e + u] * wv[u];
+                }
+            }
+            if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                for (int e = 0; e < EV; ++e) f[x][e] = (T)y[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < EV; ++e) f[4 * x + e] = y[e];
+            }
+        }
+        return dot;
+    }
+};
+
+// One token row per lane in accumulator order: lane l holds row tok0 + (l & 15),
+// elements 16 m + 4 (l >> 4) + 0..3 in word m (the order of an accumulator
+// tile's rows).  Rows at or beyond N read as 0.
+template <typename T, int D>
+struct RowAcc {
+    typedef typename std::conditional<sizeof(T) == 2, uint2, uint4>::type word;
+    static constexpr int NW = D / 16;
+    word r[NW];
+    __device__ __forceinline__ void load(const T* head, int tok0, int N, int lane) {
+        const int tok = tok0 + (lane & 15);
+#pragma unroll
+        for (int m = 0; m < NW; ++m)
+            r[m] = tok < N ? *reinterpret_cast<const word*>(head + (int64_t)tok * D + 16 * m + 4 * (lane >> 4)) : word{};
+    }
+    __device__ __forceinline__ float get(int i) const { return to_f32(reinterpret_cast<const T*>(r)[i]); }
+};
+
+// phi(Q) row-major into LDS.
+template <typename T, int D, bool kWaveRows = false>
+__device__ __forceinline__ void stage_phi(const ChunkRegs<T, D, kWaveRows>& cq, const Tile<T, kC, D>& tQ, int tid) {
+    using CR = ChunkRegs<T, D, kWaveRows>;
 #pragma unroll
     for (int i = 0; i < CR::NV; ++i) {
         uint4 packed;
@@ -191,6 +257,41 @@ __device__ __forceinline__ void store_vec(float* v, const VecAcc<D>& acc, int la
     for (int x = 0; x < ST::NVT; ++x) *reinterpret_cast<f32x4*>(v + (ST::vt0(w) + x) * 16 + 4 * (lane >> 4)) = acc[x];
 }
 
+// Add the segment records rec[j * stride] for j = 0 .. count-1, in that order,
+// to the wave's state tiles and vector tiles (fixed order: bitwise reproducible).
+template <int D>
+__device__ __forceinline__ void add_records(const float* rec, int64_t stride, int count, StateAcc<D>& st,
+                                            VecAcc<D>& va, VecAcc<D>& vb, int lane, int w) {
+    using ST = StateTiles<D>;
+    constexpr int B = 4;
+    for (int j0 = 0; j0 < count; j0 += B) {
+        f32x4 xs[B][ST::NAT][ST::NBT], xa[B][ST::NVT], xb[B][ST::NVT];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (j0 + b < count) {
+                const float* r = rec + (int64_t)(j0 + b) * stride;
+                load_state<D>(r, xs[b], lane, w);
+                load_vec<D>(r + Rec<D>::kZ, xa[b], lane, w);
+                load_vec<D>(r + Rec<D>::kP, xb[b], lane, w);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (j0 + b < count) {
+#pragma unroll
+                for (int ia = 0; ia < ST::NAT; ++ia)
+#pragma unroll
+                    for (int ib = 0; ib < ST::NBT; ++ib) st[ia][ib] += xs[b][ia][ib];
+#pragma unroll
+                for (int x = 0; x < ST::NVT; ++x) {
+                    va[x] += xa[b][x];
+                    vb[x] += xb[b][x];
+                }
+            }
+        }
+    }
+}
+
 // Rounded copy of the state into LDS as X^T[b][a].
 template <typename T, int D>
 __device__ __forceinline__ void publish_state(const StateAcc<D>& st, const Tile<T, D, D>& tXt, int lane, int w) {
@@ -281,17 +382,6 @@ __device__ __forceinline__ float row_dot_quarters(const Tile<T, kC, D>& tQ, cons
     }
     return sum_over_groups(s);
 }
-
-// 4 consecutive raw input elements kept packed in registers (8 bytes in bf16,
-// 16 in fp32) until they are needed.
-template <typename T>
-struct Raw4 {
-    typedef typename std::conditional<sizeof(T) == 2, uint2, uint4>::type type;
-    type u;
-    __device__ __forceinline__ void load(const T* p) { u = *reinterpret_cast<const type*>(p); }
-    __device__ __forceinline__ void clear() { u = type{}; }
-    __device__ __forceinline__ float get(int e) const { return to_f32(reinterpret_cast<const T*>(&u)[e]); }
-};
 
 // 4 consecutive elements of a global row.
 __device__ __forceinline__ void gstore4(float* p, f32x4 a) { *reinterpret_cast<f32x4*>(p) = a; }

@@ -120,6 +120,55 @@ struct Mma<bf16> {
         const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(&t.at(r + 4, c)));
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
+    // As ld_tr, but lane l takes the k values k0 + 4 (l >> 4) + 0..3 and
+    // k0 + 16 + 4 (l >> 4) + 0..3: the rows that accumulator tiles k0/16 and
+    // k0/16 + 1 hold in lane l, so that such a pair can be the other operand (acc_op).
+    template <int R, int K>
+    __device__ __forceinline__ static frag ld_tr_acc(const Tile<bf16, R, K>& t, int k0, int col0, int lane) {
+        typedef __attribute__((address_space(3))) bf16x4 lds4;
+        const int j = lane & 15;
+        const int r = k0 + 4 * (lane >> 4) + (j >> 2);
+        const int c = col0 + 4 * (j & 3);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(&t.at(r, c)));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(&t.at(r + 16, c)));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    // As ld, in the k order of ld_tr_acc: lane l takes columns k0 + 4 (l >> 4) + 0..3
+    // and k0 + 16 + 4 (l >> 4) + 0..3 of its row.
+    template <int R, int K>
+    __device__ __forceinline__ static frag ld_acc(const Tile<bf16, R, K>& t, int row0, int k0, int lane) {
+        const int r = row0 + (lane & 15), c = k0 + 4 * (lane >> 4);
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&t.at(r, c));
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(&t.at(r, c + 16));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    // Operand for k-step k0 from per-lane values in accumulator order: y[4 m + e]
+    // is the value at k = 16 m + 4 (l >> 4) + e (the layout of an accumulator
+    // tile's rows, and of the k order of ld_acc / ld_tr_acc).
+    __device__ __forceinline__ static frag vals_op(const float* y, int k0) {
+        frag f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = (bf16)y[k0 / 4 + e];
+        return f;
+    }
+    // The same from raw inputs already in that order (4 elements per 8-byte word).
+    __device__ __forceinline__ static frag raw_op(const uint2* r, int k0) {
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&r[k0 / 16]);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(&r[k0 / 16 + 1]);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    // Operand for k-step k0 of a contraction over the row index of accumulator
+    // tiles acc[0..]: the column index of the tiles is the operand row.
+    __device__ __forceinline__ static frag acc_op(const f32x4* acc, int k0) {
+        const f32x4 a = acc[k0 / 16], b = acc[k0 / 16 + 1];
+        frag f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[e] = (bf16)a[e];
+            f[4 + e] = (bf16)b[e];
+        }
+        return f;
+    }
     // v: fp32 vector in LDS indexed by k; hi/lo split keeps ~16 bits of each value.
     __device__ __forceinline__ static void splat(const float* v, int k0, int lane, frag& hi, frag& lo) {
         const f32x4* p = reinterpret_cast<const f32x4*>(v + k0 + 8 * (lane >> 4));
@@ -148,16 +197,34 @@ template <>
 struct Mma<float> {
     static constexpr int KSTEP = 4;
     typedef float frag;
+    // k order inside each block of 16: step k0 = 16 x + 4 e gives lane group g
+    // the value 16 x + 4 g + e, which is also the row that accumulator tile x
+    // holds in element e of lane group g.  Every operand uses this order, so
+    // contraction lengths are multiples of 16.
+    __device__ __forceinline__ static int kap(int k0, int lane) { return (k0 & ~15) + 4 * (lane >> 4) + ((k0 & 15) >> 2); }
     template <int R, int K>
     __device__ __forceinline__ static frag ld(const Tile<float, R, K>& t, int row0, int k0, int lane) {
-        return t.at(row0 + (lane & 15), k0 + (lane >> 4));
+        return t.at(row0 + (lane & 15), kap(k0, lane));
     }
     template <int R, int K>
     __device__ __forceinline__ static frag ld_tr(const Tile<float, R, K>& t, int k0, int col0, int lane) {
-        return t.at(k0 + (lane >> 4), col0 + (lane & 15));
+        return t.at(kap(k0, lane), col0 + (lane & 15));
     }
+    template <int R, int K>
+    __device__ __forceinline__ static frag ld_tr_acc(const Tile<float, R, K>& t, int k0, int col0, int lane) {
+        return ld_tr(t, k0, col0, lane);
+    }
+    template <int R, int K>
+    __device__ __forceinline__ static frag ld_acc(const Tile<float, R, K>& t, int row0, int k0, int lane) {
+        return ld(t, row0, k0, lane);
+    }
+    __device__ __forceinline__ static frag vals_op(const float* y, int k0) { return y[k0 / 4]; }
+    __device__ __forceinline__ static frag raw_op(const uint4* r, int k0) {
+        return reinterpret_cast<const float*>(&r[k0 >> 4])[(k0 & 15) >> 2];
+    }
+    __device__ __forceinline__ static frag acc_op(const f32x4* acc, int k0) { return acc[k0 >> 4][(k0 & 15) >> 2]; }
     __device__ __forceinline__ static void splat(const float* v, int k0, int lane, frag& hi, frag& lo) {
-        hi = v[k0 + (lane >> 4)];
+        hi = v[kap(k0, lane)];
         lo = 0.f;
     }
     __device__ __forceinline__ static frag ones() { return 1.f; }

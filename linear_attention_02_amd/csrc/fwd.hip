@@ -14,19 +14,23 @@
 //   num_t = q_sum_t P + phi(Q_t) S_E + sum_{s<=t in chunk} A_ts V_s,
 //   den_t = q_sum_t n + phi(Q_t) . z_E + sum_{s<=t in chunk} A_ts.
 //
-// Work decomposition.  One workgroup (4 wavefronts) per (head, segment of
-// `cps` chunks).  seg_state reduces each segment's keys to (S_E, z_E, P);
-// scan turns those into exclusive prefixes in segment order (fixed order, so
-// results are bitwise reproducible) and per-head totals; causal_fwd walks a
-// segment's chunks from its prefix.  The non-causal forward is seg_state +
-// scan (totals) + noncausal_fwd.
+// Work decomposition.  One workgroup (4 wavefronts) per (segment of `cps`
+// chunks, head), numbered segment-major so that with the round-robin
+// placement of workgroups on the 8 XCDs all segments of a head share an XCD
+// (and its L2) whenever the head count is a multiple of 8.  seg_state reduces
+// each segment's keys to (S_E, z_E, P); causal_fwd starts a segment from the
+// sum of the records before it, added in segment order (fixed order, so the
+// results are bitwise reproducible), and walks its chunks.  The non-causal
+// forward is seg_state + per-head totals (scan) + noncausal_fwd.
 //
 // Data layout.  Inputs/outputs [BH][N][d] row-major in HBM.  Per chunk the
-// workgroup stages phi(Q), E(K) and V row-major in LDS (bf16 for bf16 inputs,
-// fp32 for fp32 inputs); products that contract over tokens read them with the
-// transposing LDS load.  The in-chunk weights A and the rounded S_E^T live in
-// LDS, S_E itself stays in fp32 MFMA accumulators across chunks; z_E and P are
-// accumulated by MFMA against a ones operand.  Segment records are fp32
+// workgroup stages E(K) and V row-major in LDS (bf16 for bf16 inputs, fp32 for
+// fp32 inputs, double-buffered so one barrier per chunk suffices); each
+// wavefront keeps phi(Q) of its own 16 tokens in registers in MFMA operand
+// layout, and the in-chunk weights A stay in the accumulators that produce them
+// and feed the A V product directly.  S_E stays in fp32 MFMA accumulators
+// across chunks and is published to LDS (rounded) once per chunk; z_E and P
+// are accumulated by MFMA against a ones operand.  Segment records are fp32
 // [S_E^T | z_E | P].
 #include "chunk.h"
 
@@ -34,14 +38,14 @@ namespace la {
 
 // ---------------------------------------------------------------------------------------
 // seg_state: per (segment, head) the aggregates (S_E, z_E, P) of the segment's keys.
+// Two chunks are in flight ahead of the one being reduced.
 template <typename T, int D>
-__global__ __launch_bounds__(kBlock) void seg_state_kernel(const T* __restrict__ k, const T* __restrict__ v,
-                                                           float* __restrict__ rec, int N, int cps, int nseg) {
-    __shared__ __attribute__((aligned(16))) T sm_e[kC * D];
-    __shared__ __attribute__((aligned(16))) T sm_v[kC * D];
-    const Tile<T, kC, D> tE{sm_e}, tV{sm_v};
+__global__ __launch_bounds__(kBlock, 4) void seg_state_kernel(const T* __restrict__ k, const T* __restrict__ v,
+                                                           float* __restrict__ rec, int N, int cps, int nseg, int BH) {
+    __shared__ __attribute__((aligned(16))) T sm_e[2][kC * D];
+    __shared__ __attribute__((aligned(16))) T sm_v[2][kC * D];
 
-    const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+    const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int64_t hoff = (int64_t)bh * N * D;
     const int tok_begin = seg * cps * kC;
@@ -53,19 +57,29 @@ __global__ __launch_bounds__(kBlock) void seg_state_kernel(const T* __restrict__
     zero_vec<D>(vz);
     zero_vec<D>(vp);
 
-    ChunkRegs<T, D> ck, cv;
-    ck.load(k + hoff, tok_begin, N, tid);
-    cv.load(v + hoff, tok_begin, N, tid);
-    for (int c0 = tok_begin; c0 < tok_end; c0 += kC) {
-        stage_elu<T, D>(ck, tE, tid);
-        stage_raw<T, D>(cv, tV, tid);
-        if (c0 + kC < tok_end) {
-            ck.load(k + hoff, c0 + kC, N, tid);
-            cv.load(v + hoff, c0 + kC, N, tid);
+    ChunkRegs<T, D> ck[2], cv[2];
+    ck[0].load(k + hoff, tok_begin, N, tid);
+    cv[0].load(v + hoff, tok_begin, N, tid);
+    ck[1].load(k + hoff, tok_begin + kC, N, tid);
+    cv[1].load(v + hoff, tok_begin + kC, N, tid);
+    int c0 = tok_begin;
+    auto step = [&](ChunkRegs<T, D>& rk, ChunkRegs<T, D>& rv, int buf) {
+        const Tile<T, kC, D> tE{sm_e[buf]}, tV{sm_v[buf]};
+        stage_elu<T, D>(rk, tE, tid);
+        stage_raw<T, D>(rv, tV, tid);
+        if (c0 + 2 * kC < tok_end) {
+            rk.load(k + hoff, c0 + 2 * kC, N, tid);
+            rv.load(v + hoff, c0 + 2 * kC, N, tid);
         }
         __syncthreads();
         state_update<T, D, true, true>(st, vz, vp, tE, tV, nullptr, nullptr, lane, w);
-        __syncthreads();
+        c0 += kC;
+    };
+    while (true) {
+        step(ck[0], cv[0], 0);
+        if (c0 >= tok_end) break;
+        step(ck[1], cv[1], 1);
+        if (c0 >= tok_end) break;
     }
     float* r = rec + ((int64_t)bh * nseg + seg) * Rec<D>::kSize;
     store_state<D>(r, st, lane, w);
@@ -74,109 +88,103 @@ __global__ __launch_bounds__(kBlock) void seg_state_kernel(const T* __restrict__
 }
 
 // ---------------------------------------------------------------------------------------
-// scan: per head, replace each segment record by the sum of the records before
-// it (in segment order), or after it (reverse order) for the backward's suffix
-// records, and/or write the head total.  Records are loaded in batches ahead
-// of the running sum.
+// total: per head, the sum of the segment records in segment order.  Records
+// are loaded in batches ahead of the running sum.
 template <int D>
-__global__ __launch_bounds__(kBlock) void scan_kernel(float* __restrict__ rec, float* __restrict__ total, int nseg,
-                                                      int write_prefix, int reverse) {
+__global__ __launch_bounds__(kBlock) void total_kernel(const float* __restrict__ rec, float* __restrict__ total,
+                                                       int nseg) {
     constexpr int R4 = Rec<D>::kSize / 4;
     constexpr int NBLK = (R4 + kBlock - 1) / kBlock;
     constexpr int BATCH = 16;
     const int e4 = (blockIdx.x % NBLK) * kBlock + threadIdx.x;
     const int bh = blockIdx.x / NBLK;
     if (e4 >= R4) return;
-    f32x4* r = reinterpret_cast<f32x4*>(rec) + (int64_t)bh * nseg * R4 + e4;
+    const f32x4* r = reinterpret_cast<const f32x4*>(rec) + (int64_t)bh * nseg * R4 + e4;
     f32x4 run = zero4();
     for (int i0 = 0; i0 < nseg; i0 += BATCH) {
         f32x4 x[BATCH];
 #pragma unroll
-        for (int b = 0; b < BATCH; ++b) {
-            const int i = i0 + b;
-            const int s = reverse ? nseg - 1 - i : i;
-            x[b] = i < nseg ? r[(int64_t)s * R4] : zero4();
-        }
+        for (int b = 0; b < BATCH; ++b) x[b] = i0 + b < nseg ? r[(int64_t)(i0 + b) * R4] : zero4();
 #pragma unroll
-        for (int b = 0; b < BATCH; ++b) {
-            const int i = i0 + b;
-            const int s = reverse ? nseg - 1 - i : i;
-            if (write_prefix && i < nseg) r[(int64_t)s * R4] = run;
-            run += x[b];
-        }
+        for (int b = 0; b < BATCH; ++b) run += x[b];
     }
-    if (total != nullptr) reinterpret_cast<f32x4*>(total)[(int64_t)bh * R4 + e4] = run;
+    reinterpret_cast<f32x4*>(total)[(int64_t)bh * R4 + e4] = run;
 }
 
 // ---------------------------------------------------------------------------------------
-// causal_fwd: per (segment, head), walk the segment's chunks from its prefix state.
+// causal_fwd: per (segment, head), walk the segment's chunks from the state
+// carried in by the segments before it.  The last segment of a head also
+// writes the final state S = 1 P^T + S_E, z = N 1 + z_E when asked to.
 template <typename T, int D>
-__global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void causal_fwd_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                                                            const T* __restrict__ v, T* __restrict__ o,
-                                                            float* __restrict__ den_out, const float* __restrict__ rec,
-                                                            int N, int cps, int nseg) {
+__global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void causal_fwd_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ o,
+    float* __restrict__ den_out, const float* __restrict__ rec, float* __restrict__ S_out, float* __restrict__ z_out,
+    int N, int cps, int nseg, int BH) {
     using M = Mma<T>;
     constexpr int KS = M::KSTEP;
     constexpr int DT = D / 16;
-    __shared__ __attribute__((aligned(16))) T sm_q[kC * D];
-    __shared__ __attribute__((aligned(16))) T sm_e[kC * D];
-    __shared__ __attribute__((aligned(16))) T sm_v[kC * D];
-    __shared__ __attribute__((aligned(16))) T sm_a[kC * kC];
-    __shared__ __attribute__((aligned(16))) T sm_st[D * D];
-    __shared__ __attribute__((aligned(16))) float s_z[D], s_p[D];
-    const Tile<T, kC, D> tQ{sm_q}, tE{sm_e}, tV{sm_v};
-    const Tile<T, kC, kC> tA{sm_a};
-    const Tile<T, D, D> tSt{sm_st};
+    __shared__ __attribute__((aligned(16))) T sm_e[2][kC * D];
+    __shared__ __attribute__((aligned(16))) T sm_v[2][kC * D];
+    __shared__ __attribute__((aligned(16))) T sm_st[2][D * D];
+    __shared__ __attribute__((aligned(16))) float s_z[2][D], s_p[2][D];
 
-    const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+    const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
     const int64_t hoff = (int64_t)bh * N * D;
     const int tok_begin = seg * cps * kC;
     const int tok_end = min(N, tok_begin + cps * kC);
 
-    // Starting state: the exclusive prefix of the segments before this one.
-    const float* r = rec + ((int64_t)bh * nseg + seg) * Rec<D>::kSize;
+    // Starting state: the records of the segments before this one, in order.
     StateAcc<D> st;
     VecAcc<D> vz, vp;
-    load_state<D>(r, st, lane, w);
-    load_vec<D>(r + Rec<D>::kZ, vz, lane, w);
-    load_vec<D>(r + Rec<D>::kP, vp, lane, w);
+    zero_state<D>(st);
+    zero_vec<D>(vz);
+    zero_vec<D>(vp);
+    add_records<D>(rec + (int64_t)bh * nseg * Rec<D>::kSize, Rec<D>::kSize, seg, st, vz, vp, lane, w);
     float n = (float)tok_begin;
-
-    ChunkRegs<T, D> cq, ck, cv;
-    cq.load(q + hoff, tok_begin, N, tid);
-    ck.load(k + hoff, tok_begin, N, tid);
-    cv.load(v + hoff, tok_begin, N, tid);
 
     const int t0 = 16 * w;            // this wave's token tile
     const int tl = t0 + (lane & 15);  // this lane's token (accumulator column)
+    ChunkRegs<T, D> ck, cv;
+    RowFrag<T, D> qr;
+    ck.load(k + hoff, tok_begin, N, tid);
+    cv.load(v + hoff, tok_begin, N, tid);
+    qr.load(q + hoff, tok_begin + t0, N, lane);
 
-    for (int c0 = tok_begin; c0 < tok_end; c0 += kC) {
-        // Publish the state reached so far and stage this chunk.
+    int buf = 0;
+    for (int c0 = tok_begin; c0 < tok_end; c0 += kC, buf ^= 1) {
+        const Tile<T, kC, D> tE{sm_e[buf]}, tV{sm_v[buf]};
+        const Tile<T, D, D> tSt{sm_st[buf]};
+        const float* sz = s_z[buf];
+        const float* sp = s_p[buf];
+        // Publish the state reached so far and stage this chunk's keys and values.
         publish_state<T, D>(st, tSt, lane, w);
-        store_vec<D>(s_z, vz, lane, w);
-        store_vec<D>(s_p, vp, lane, w);
-        stage_phi<T, D>(cq, tQ, tid);
+        store_vec<D>(s_z[buf], vz, lane, w);
+        store_vec<D>(s_p[buf], vp, lane, w);
         stage_elu<T, D>(ck, tE, tid);
         stage_raw<T, D>(cv, tV, tid);
         if (c0 + kC < tok_end) {
-            cq.load(q + hoff, c0 + kC, N, tid);
             ck.load(k + hoff, c0 + kC, N, tid);
             cv.load(v + hoff, c0 + kC, N, tid);
         }
         __syncthreads();
 
-        // In-chunk weights A_ts = q_sum_t + phi(Q_t).E(K_s) for s <= t (accumulator [s][t]);
-        // every wave forms all four key tiles so the code has no wave-dependent branches.
+        // phi(Q) of this wave's tokens as operands, and phi(Q_t) . z_E.
+        typename M::frag qf[D / KS];
+        const float zdot = sum_over_groups(qr.phi_ops(qf, sz, lane));
+        if (c0 + kC < tok_end) qr.load(q + hoff, c0 + kC + t0, N, lane);
+
+        // In-chunk weights A_ts = q_sum_t + phi(Q_t).E(K_s) for s <= t (accumulator [s][t]).
         float qs_t, den = 0.f;
+        f32x4 acc_a[4];
         {
             const typename M::frag one = M::ones();
-            f32x4 acc_a[4], acc_q = zero4();
+            f32x4 acc_q = zero4();
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc_a[j] = zero4();
 #pragma unroll
             for (int k0 = 0; k0 < D; k0 += KS) {
-                const typename M::frag yf = M::ld(tQ, t0, k0, lane);
+                const typename M::frag yf = qf[k0 / KS];
                 acc_q = M::mma(one, yf, acc_q);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc_a[j] = M::mma(M::ld(tE, 16 * j, k0, lane), yf, acc_a[j]);
@@ -190,12 +198,10 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void causal_fwd_ke
                     acc_a[j][e] = a;
                     den += a;
                 }
-                store_T(tA, 16 * j, t0, acc_a[j], lane);
             }
         }
-        den = sum_over_groups(den) + n * qs_t + row_dot_quarters<T, D>(tQ, s_z, tl, lane);
+        den = sum_over_groups(den) + n * qs_t + zdot;
         const float inv = rcp_f(den);
-        wave_lds_sync();  // this wave's rows of A
 
         // num^T[b][t] = sum_s V[s][b] A[t][s] + sum_a S_E^T[b][a] phi(Q)[t][a]
         f32x4 acc[DT];
@@ -203,13 +209,13 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void causal_fwd_ke
         for (int m = 0; m < DT; ++m) acc[m] = zero4();
 #pragma unroll
         for (int k0 = 0; k0 < kC; k0 += KS) {
-            const typename M::frag yf = M::ld(tA, t0, k0, lane);
+            const typename M::frag yf = M::acc_op(acc_a, k0);
 #pragma unroll
-            for (int m = 0; m < DT; ++m) acc[m] = M::mma(M::ld_tr(tV, k0, 16 * m, lane), yf, acc[m]);
+            for (int m = 0; m < DT; ++m) acc[m] = M::mma(M::ld_tr_acc(tV, k0, 16 * m, lane), yf, acc[m]);
         }
 #pragma unroll
         for (int k0 = 0; k0 < D; k0 += KS) {
-            const typename M::frag yf = M::ld(tQ, t0, k0, lane);
+            const typename M::frag yf = qf[k0 / KS];
 #pragma unroll
             for (int m = 0; m < DT; ++m) acc[m] = M::mma(M::ld(tSt, 16 * m, k0, lane), yf, acc[m]);
         }
@@ -219,7 +225,7 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void causal_fwd_ke
 #pragma unroll
             for (int m = 0; m < DT; ++m) {
                 const int b0 = 16 * m + 4 * g;
-                const f32x4 p4 = lds4(&s_p[b0]);
+                const f32x4 p4 = lds4(&sp[b0]);
                 f32x4 x;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] = (acc[m][e] + qs_t * p4[e]) * inv;
@@ -231,26 +237,45 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void causal_fwd_ke
         // State update: S_E += E(K)^T V, z_E += colsum E(K), P += colsum V.
         state_update<T, D, true, true>(st, vz, vp, tE, tV, nullptr, nullptr, lane, w);
         n += (float)min(kC, N - c0);
+    }
+
+    if (seg == nseg - 1 && (S_out != nullptr || z_out != nullptr)) {
+        // The buffer not read by the last chunk is free once every wave is past its barrier.
+        store_vec<D>(s_z[buf], vz, lane, w);
+        store_vec<D>(s_p[buf], vp, lane, w);
         __syncthreads();
+        using ST = StateTiles<D>;
+        if (S_out != nullptr) {
+            float* s = S_out + (int64_t)bh * D * D;
+#pragma unroll
+            for (int ia = 0; ia < ST::NAT; ++ia)
+#pragma unroll
+                for (int ib = 0; ib < ST::NBT; ++ib) {
+                    const int b = (ST::bt0(w) + ib) * 16 + (lane & 15);
+                    const float pb = s_p[buf][b];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s[(int64_t)((ST::at0(w) + ia) * 16 + 4 * g + e) * D + b] = pb + st[ia][ib][e];
+                }
+        }
+        if (z_out != nullptr && tid < D) z_out[(int64_t)bh * D + tid] = (float)N + s_z[buf][tid];
     }
 }
 
 // ---------------------------------------------------------------------------------------
-// noncausal_fwd: every row reads the head's total state.
+// noncausal_fwd: every row reads the head's total state; each wavefront works
+// on its own token tiles with phi(Q) in registers (no barrier in the loop).
 template <typename T, int D>
 __global__ __launch_bounds__(kBlock) void noncausal_fwd_kernel(const T* __restrict__ q, T* __restrict__ o,
                                                                const float* __restrict__ total, int N, int cps,
-                                                               int nseg) {
+                                                               int nseg, int BH) {
     using M = Mma<T>;
     constexpr int KS = M::KSTEP;
     constexpr int DT = D / 16;
-    __shared__ __attribute__((aligned(16))) T sm_q[kC * D];
     __shared__ __attribute__((aligned(16))) T sm_st[D * D];
     __shared__ __attribute__((aligned(16))) float s_z[D], s_p[D];
-    const Tile<T, kC, D> tQ{sm_q};
     const Tile<T, D, D> tSt{sm_st};
 
-    const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+    const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
     const int64_t hoff = (int64_t)bh * N * D;
     const int tok_begin = seg * cps * kC;
@@ -265,26 +290,30 @@ __global__ __launch_bounds__(kBlock) void noncausal_fwd_kernel(const T* __restri
     if (tid < D) s_z[tid] = r[Rec<D>::kZ + tid];
     else if (tid < 2 * D) s_p[tid - D] = r[Rec<D>::kP + tid - D];
     const float n = (float)N;
-
-    ChunkRegs<T, D> cq;
-    cq.load(q + hoff, tok_begin, N, tid);
     const int t0 = 16 * w;
     const int tl = t0 + (lane & 15);
+    RowFrag<T, D> qr;
+    qr.load(q + hoff, tok_begin + t0, N, lane);
+    __syncthreads();
+
     for (int c0 = tok_begin; c0 < tok_end; c0 += kC) {
-        stage_phi<T, D>(cq, tQ, tid);
-        if (c0 + kC < tok_end) cq.load(q + hoff, c0 + kC, N, tid);
-        __syncthreads();
-        const float qs_t = tile_row_sums<T, D>(tQ, t0, lane)[0];
-        const float inv = rcp_f(n * qs_t + row_dot_quarters<T, D>(tQ, s_z, tl, lane));
+        typename M::frag qf[D / KS];
+        const float zdot = sum_over_groups(qr.phi_ops(qf, s_z, lane));
+        if (c0 + kC < tok_end) qr.load(q + hoff, c0 + kC + t0, N, lane);
+        const typename M::frag one = M::ones();
+        f32x4 acc_q = zero4();
         f32x4 acc[DT];
 #pragma unroll
         for (int m = 0; m < DT; ++m) acc[m] = zero4();
 #pragma unroll
         for (int k0 = 0; k0 < D; k0 += KS) {
-            const typename M::frag yf = M::ld(tQ, t0, k0, lane);
+            const typename M::frag yf = qf[k0 / KS];
+            acc_q = M::mma(one, yf, acc_q);
 #pragma unroll
             for (int m = 0; m < DT; ++m) acc[m] = M::mma(M::ld(tSt, 16 * m, k0, lane), yf, acc[m]);
         }
+        const float qs_t = acc_q[0];
+        const float inv = rcp_f(n * qs_t + zdot);
         const int tok = c0 + tl;
         if (tok < N) {
             T* orow = o + hoff + (int64_t)tok * D;
@@ -298,27 +327,7 @@ __global__ __launch_bounds__(kBlock) void noncausal_fwd_kernel(const T* __restri
                 gstore4(orow + b0, x);
             }
         }
-        __syncthreads();
     }
-}
-
-// ---------------------------------------------------------------------------------------
-// final_state: S[a][b] = P[b] + S_E[a][b], z[a] = N + z_E[a] from the head totals.
-template <int D>
-__global__ __launch_bounds__(kBlock) void final_state_kernel(const float* __restrict__ total,
-                                                             float* __restrict__ S_out, float* __restrict__ z_out,
-                                                             int N) {
-    const int bh = blockIdx.x;
-    const float* r = total + (int64_t)bh * Rec<D>::kSize;
-    if (S_out != nullptr) {
-        float* s = S_out + (int64_t)bh * D * D;
-        for (int x = threadIdx.x; x < D * D; x += kBlock) {
-            const int a = x / D, b = x % D;
-            s[x] = r[Rec<D>::kP + b] + r[b * D + a];
-        }
-    }
-    if (z_out != nullptr && threadIdx.x < D)
-        z_out[(int64_t)bh * D + threadIdx.x] = (float)N + r[Rec<D>::kZ + threadIdx.x];
 }
 
 __global__ __launch_bounds__(kBlock) void fill_zero_kernel(float* __restrict__ p, size_t n) {
@@ -329,8 +338,10 @@ __global__ __launch_bounds__(kBlock) void fill_zero_kernel(float* __restrict__ p
 // Host launchers.
 SegPlan plan_segments(int64_t BH, int64_t N) {
     const int64_t nchunk = (N + kC - 1) / kC;
-    // Aim for about 1024 workgroups (4 per CU) while keeping >= 1 chunk per segment.
-    int64_t cps = (BH * nchunk + 1023) / 1024;
+    // Aim for about 512 workgroups (2 per CU): the heavy kernels keep 2-3
+    // workgroups resident per CU, and starting a segment costs one record read
+    // per segment before it, so fewer, longer segments are cheaper.
+    int64_t cps = (BH * nchunk + 511) / 512;
     if (cps < 1) cps = 1;
     if (cps > 16) cps = 16;
     SegPlan p;
@@ -370,51 +381,43 @@ hipError_t launch_seg_state(int dt, int d, const void* k, const void* v, float* 
     const dim3 grid((unsigned)(p.nseg * BH));
     if (dt == kBF16) {
         LA_DISPATCH_D(d, hipLaunchKernelGGL((seg_state_kernel<bf16, D>), grid, dim3(kBlock), 0, s, (const bf16*)k,
-                                            (const bf16*)v, rec, (int)N, p.cps, p.nseg));
+                                            (const bf16*)v, rec, (int)N, p.cps, p.nseg, (int)BH));
     } else {
         LA_DISPATCH_D(d, hipLaunchKernelGGL((seg_state_kernel<float, D>), grid, dim3(kBlock), 0, s, (const float*)k,
-                                            (const float*)v, rec, (int)N, p.cps, p.nseg));
+                                            (const float*)v, rec, (int)N, p.cps, p.nseg, (int)BH));
     }
     return hipGetLastError();
 }
 
-static hipError_t scan_launch(int d, float* rec, float* total, int64_t BH, int nseg, bool write_prefix, bool reverse,
-                              hipStream_t s) {
+hipError_t launch_total(int d, const float* rec, float* total, int64_t BH, int nseg, hipStream_t s) {
     const int r4 = (int)(rec_floats(d) / 4);
     const dim3 grid((unsigned)(((r4 + kBlock - 1) / kBlock) * BH));
-    LA_DISPATCH_D(d, hipLaunchKernelGGL((scan_kernel<D>), grid, dim3(kBlock), 0, s, rec, total, nseg,
-                                        write_prefix ? 1 : 0, reverse ? 1 : 0));
+    LA_DISPATCH_D(d, hipLaunchKernelGGL((total_kernel<D>), grid, dim3(kBlock), 0, s, rec, total, nseg));
     return hipGetLastError();
-}
-
-hipError_t launch_scan(int d, float* rec, float* total, int64_t BH, int nseg, bool write_prefix, hipStream_t s) {
-    return scan_launch(d, rec, total, BH, nseg, write_prefix, false, s);
-}
-
-hipError_t launch_rscan(int d, float* rrec, int64_t BH, int nseg, hipStream_t s) {
-    return scan_launch(d, rrec, nullptr, BH, nseg, true, true, s);
 }
 
 hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const void* v, void* o, float* den_out,
-                             const float* rec, int64_t BH, int64_t N, SegPlan p, hipStream_t s) {
+                             const float* rec, float* S_out, float* z_out, int64_t BH, int64_t N, SegPlan p,
+                             hipStream_t s) {
     const dim3 grid((unsigned)(p.nseg * BH));
+#define LA_CFWD(TT, DD)                                                                                          \
+    hipLaunchKernelGGL((causal_fwd_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k,       \
+                       (const TT*)v, (TT*)o, den_out, rec, S_out, z_out, (int)N, p.cps, p.nseg, (int)BH)
     if (dt == kBF16) {
-        LA_DISPATCH_D(d, hipLaunchKernelGGL((causal_fwd_kernel<bf16, D>), grid, dim3(kBlock), 0, s, (const bf16*)q,
-                                            (const bf16*)k, (const bf16*)v, (bf16*)o, den_out, rec, (int)N, p.cps,
-                                            p.nseg));
+        switch (d) {
+            case 32: LA_CFWD(bf16, 32); break;
+            case 64: LA_CFWD(bf16, 64); break;
+            case 128: LA_CFWD(bf16, 128); break;
+            default: return hipErrorInvalidValue;
+        }
     } else {
         switch (d) {
-            case 32:
-                hipLaunchKernelGGL((causal_fwd_kernel<float, 32>), grid, dim3(kBlock), 0, s, (const float*)q,
-                                   (const float*)k, (const float*)v, (float*)o, den_out, rec, (int)N, p.cps, p.nseg);
-                break;
-            case 64:
-                hipLaunchKernelGGL((causal_fwd_kernel<float, 64>), grid, dim3(kBlock), 0, s, (const float*)q,
-                                   (const float*)k, (const float*)v, (float*)o, den_out, rec, (int)N, p.cps, p.nseg);
-                break;
+            case 32: LA_CFWD(float, 32); break;
+            case 64: LA_CFWD(float, 64); break;
             default: return hipErrorInvalidValue;
         }
     }
+#undef LA_CFWD
     return hipGetLastError();
 }
 
@@ -423,18 +426,11 @@ hipError_t launch_noncausal_fwd(int dt, int d, const void* q, void* o, const flo
     const dim3 grid((unsigned)(p.nseg * BH));
     if (dt == kBF16) {
         LA_DISPATCH_D(d, hipLaunchKernelGGL((noncausal_fwd_kernel<bf16, D>), grid, dim3(kBlock), 0, s,
-                                            (const bf16*)q, (bf16*)o, total, (int)N, p.cps, p.nseg));
+                                            (const bf16*)q, (bf16*)o, total, (int)N, p.cps, p.nseg, (int)BH));
     } else {
         LA_DISPATCH_D(d, hipLaunchKernelGGL((noncausal_fwd_kernel<float, D>), grid, dim3(kBlock), 0, s,
-                                            (const float*)q, (float*)o, total, (int)N, p.cps, p.nseg));
+                                            (const float*)q, (float*)o, total, (int)N, p.cps, p.nseg, (int)BH));
     }
-    return hipGetLastError();
-}
-
-hipError_t launch_final_state(int d, const float* total, float* S_out, float* z_out, int64_t BH, int64_t N,
-                              hipStream_t s) {
-    LA_DISPATCH_D(d, hipLaunchKernelGGL((final_state_kernel<D>), dim3((unsigned)BH), dim3(kBlock), 0, s, total, S_out,
-                                        z_out, (int)N));
     return hipGetLastError();
 }
 

@@ -21,9 +21,9 @@ constexpr int kBlock = 256;      // threads per workgroup (4 wavefronts)
 
 enum DType { kF32 = 0, kBF16 = 1 };
 
-// Sequence segmentation: each (head, segment) pair is one workgroup; a segment
-// is `cps` consecutive chunks.  Segments are joined by an exclusive scan of
-// their fp32 state aggregates.
+// Sequence segmentation: each (segment, head) pair is one workgroup; a segment
+// is `cps` consecutive chunks.  A segment starts from the sum of the fp32 state
+// aggregates of the segments before it (after it, for the backward's suffix state).
 struct SegPlan {
     int cps;   // chunks per segment
     int nseg;  // segments per head
@@ -34,26 +34,25 @@ SegPlan plan_segments(int64_t BH, int64_t N);
 // S_E^T [d][d], z_E [d], P [d].
 inline int64_t rec_floats(int64_t d) { return d * d + 2 * d; }
 
-// Forward pieces.
+// Forward pieces.  Segment records are per-segment aggregates laid out
+// [BH][nseg][rec_floats(d)]; workgroups are numbered segment-major.
 hipError_t launch_seg_state(int dt, int d, const void* k, const void* v, float* rec, int64_t BH,
                             int64_t N, SegPlan p, hipStream_t s);
-// Exclusive prefix of the segment records in place (write_prefix) and/or the
-// per-head total (total != nullptr).
-hipError_t launch_scan(int d, float* rec, float* total, int64_t BH, int nseg, bool write_prefix,
-                       hipStream_t s);
+// Per-head sum of the segment records (segment order).
+hipError_t launch_total(int d, const float* rec, float* total, int64_t BH, int nseg, hipStream_t s);
+// Causal outputs; the last segment of each head writes S_out / z_out when non-null.
 hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const void* v, void* o,
-                             float* den_out, const float* rec, int64_t BH, int64_t N, SegPlan p,
-                             hipStream_t s);
+                             float* den_out, const float* rec, float* S_out, float* z_out, int64_t BH,
+                             int64_t N, SegPlan p, hipStream_t s);
 hipError_t launch_noncausal_fwd(int dt, int d, const void* q, void* o, const float* total,
                                 int64_t BH, int64_t N, SegPlan p, hipStream_t s);
-hipError_t launch_final_state(int d, const float* total, float* S_out, float* z_out, int64_t BH,
-                              int64_t N, hipStream_t s);
 
-// Backward pieces.
+// Backward pieces.  bwd_prefix starts each segment from the sum of the forward
+// records before it and writes the segment's suffix-state aggregate to rrec;
+// bwd_suffix starts each segment from the sum of the rrec records after it.
 hipError_t launch_bwd_prefix(int dt, int d, const void* q, const void* k, const void* v,
                              const void* dout, void* dq, float* rowstat, float* rrec,
                              const float* rec, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
-hipError_t launch_rscan(int d, float* rrec, int64_t BH, int nseg, hipStream_t s);
 hipError_t launch_bwd_suffix(int dt, int d, const void* q, const void* k, const void* v,
                              const void* dout, void* dk, void* dv, const float* rowstat,
                              const float* rrec, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
