@@ -78,7 +78,7 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
                                size_t workspace_bytes, void* stream);
 
 /* Bytes of the opaque forward state that la_forward_causal can save for
- * la_backward_causal on the same inputs (the carried (S, z) at the start of
+ * la_backward_causal on the same inputs (the keys' contribution to (S, z) of
  * every sequence segment).  Pure host computation. */
 la_status la_saved_state_size(int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt,
                               size_t* bytes_out);

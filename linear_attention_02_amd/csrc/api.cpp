@@ -101,6 +101,9 @@ la_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_
     if (B < 0 || H < 0 || N < 0) return fail(LA_ERR_INVALID_ARGUMENT, "negative size (B=%lld H=%lld N=%lld)",
                                              (long long)B, (long long)H, (long long)N);
     if (N > (int64_t)1 << 30) return fail(LA_ERR_UNSUPPORTED, "N = %lld exceeds 2^30 tokens per head", (long long)N);
+    // Kernels address one head through a buffer resource with a 31-bit byte range.
+    if (N * d * (int64_t)elem_size(dt) + 64 * d * (int64_t)elem_size(dt) > ((int64_t)1 << 31) - 1)
+        return fail(LA_ERR_UNSUPPORTED, "one head of N = %lld tokens at d = %lld exceeds 2^31 bytes", (long long)N, (long long)d);
     if (B > 0 && H > ((int64_t)1 << 31) / B) return fail(LA_ERR_UNSUPPORTED, "B*H exceeds 2^31 heads");
     *empty = (B == 0 || H == 0 || N == 0);
     return LA_OK;

@@ -68,6 +68,9 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
     const int t0 = 16 * w, tl = t0 + (lane & 15);
     const int64_t hoff = (int64_t)bh * N * D;
+    const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
+    const GBuf bq(q + hoff, hbytes), bk(k + hoff, hbytes), bv(v + hoff, hbytes), bdo(dout + hoff, hbytes);
+    const GBuf bdq(dq + hoff, hbytes), brs(rowstat + (int64_t)bh * N, (uint32_t)N * 8);
     const int tok_begin = seg * cps * kC;
     const int tok_end = min(N, tok_begin + cps * kC);
 
@@ -86,10 +89,10 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
     ChunkRegs<T, D> ck, cv;
     ChunkRegs<T, D, true> cq;
     RowAcc<T, D> cdo;
-    ck.load(k + hoff, tok_begin, N, tid);
-    cv.load(v + hoff, tok_begin, N, tid);
-    cq.load(q + hoff, tok_begin, N, tid);
-    cdo.load(dout + hoff, tok_begin + t0, N, lane);
+    ck.load(bk, tok_begin, tid);
+    cv.load(bv, tok_begin, tid);
+    cq.load(bq, tok_begin, tid);
+    cdo.load(bdo, tok_begin + t0, lane);
 
     int buf = 0;
     for (int c0 = tok_begin; c0 < tok_end; c0 += kC, buf ^= 1) {
@@ -99,10 +102,11 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
         store_vec<D>(s_p, vp, lane, w);
         stage_elu<T, D>(ck, tE, tid);
         stage_raw<T, D>(cv, tV, tid);
-        if (c0 + kC < tok_end) {
-            ck.load(k + hoff, c0 + kC, N, tid);
-            cv.load(v + hoff, c0 + kC, N, tid);
-        }
+        // Loads past the segment are aimed at row N: out of the buffer's range,
+        // they return zeros without touching memory, and the loop stays branch free.
+        const int nxt = c0 + kC < tok_end ? c0 + kC : N;
+        ck.load(bk, nxt, tid);
+        cv.load(bv, nxt, tid);
         const int tok = c0 + tl;
         const bool valid = tok < N;
         __syncthreads();
@@ -110,7 +114,7 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
         // phi(Q) of this wave's rows: staged (for the R update) and read back in
         // accumulator order where it is used (short register lifetimes).
         stage_phi<T, D, true>(cq, tQ, tid);
-        if (c0 + kC < tok_end) cq.load(q + hoff, c0 + kC, N, tid);
+        cq.load(bq, nxt, tid);
         wave_lds_sync();
         auto read_y = [&](float* y) {
 #pragma unroll
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
 #pragma unroll
                 for (int e = 0; e < 4; ++e) gp += gy[4 * m + e] * pv[e];
             }
-            if (c0 + kC < tok_end) cdo.load(dout + hoff, c0 + kC + t0, N, lane);
+            cdo.load(bdo, nxt < N ? nxt + t0 : N, lane);
 #pragma unroll
             for (int j = 0; j < 4; ++j) accGV[j] = zero4();
 #pragma unroll
@@ -204,7 +208,7 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
         const float gt = valid ? -(sum_over_groups(s1) + qs_t * gp + sum_over_groups(s3)) * inv_den : 0.f;
         if (g == 0) {
             s_g[tl] = gt;
-            if (valid) rowstat[(int64_t)bh * N + tok] = make_float2(den, gt);
+            brs.st8((uint32_t)tok * 8, make_uint2(__float_as_uint(den), __float_as_uint(gt)));
         }
 
         // (5) dA_ts = G_t.V_s + g_t for s <= t, in place; its row sums.
@@ -227,9 +231,8 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
 #pragma unroll
             for (int m = 0; m < DT; ++m) accQ[m] = M::mma(M::ld_tr_acc(tE, k0, 16 * m, lane), yd, accQ[m]);
         }
-        if (valid) {
+        {
             const float bracket = rowdA + gp + gt * n;
-            T* drow = dq + hoff + (int64_t)tok * D;
 #pragma unroll
             for (int m = 0; m < DT; ++m) {
                 const int f0 = 16 * m + 4 * g;
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
                 f32x4 x;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] = (accQ[m][e] + zv[e] * gt + bracket) * fminf(y[4 * m + e], 1.f);
-                gstore4(drow + f0, x);
+                gstore4<T>(bdq, (uint32_t)(tok * D + f0), x);
             }
         }
         __syncthreads();  // all rows of phi(Q), G and g are staged; S_E^T, z_E, P are no longer read
@@ -280,7 +283,9 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_ke
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
     const int s0 = 16 * w, sl = s0 + (lane & 15);  // this wave's key tile, this lane's key
     const int64_t hoff = (int64_t)bh * N * D;
-    const float2* rs = rowstat + (int64_t)bh * N;
+    const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
+    const GBuf bq(q + hoff, hbytes), bk(k + hoff, hbytes), bv(v + hoff, hbytes), bdo(dout + hoff, hbytes);
+    const GBuf bdk(dk + hoff, hbytes), bdv(dv + hoff, hbytes), brs(rowstat + (int64_t)bh * N, (uint32_t)N * 8);
     const int tok_begin = seg * cps * kC;
     const int tok_end = min(N, tok_begin + cps * kC);
     const int nch = (tok_end - tok_begin + kC - 1) / kC;
@@ -299,16 +304,14 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_ke
     float dn[CR::NV];
     float gv = 0.f;
     auto load_chunk = [&](int c) {
-        cq.load(q + hoff, c, N, tid);
-        cdo.load(dout + hoff, c, N, tid);
-        kr.load(k + hoff, c + s0, N, lane);
-        vrow.load(v + hoff, c + s0, N, lane);
+        cq.load(bq, c, tid);
+        cdo.load(bdo, c, tid);
+        kr.load(bk, c + s0, lane);
+        vrow.load(bv, c + s0, lane);
+        // den of the rows this thread stages, g of token tid (rows past the head read as 0)
 #pragma unroll
-        for (int i = 0; i < CR::NV; ++i) {
-            const int tok = c + CR::row(i, tid);
-            dn[i] = tok < N ? rs[tok].x : 1.f;
-        }
-        if (tid < kC) gv = c + tid < N ? rs[c + tid].y : 0.f;
+        for (int i = 0; i < CR::NV; ++i) dn[i] = brs.ld4f((uint32_t)(c + CR::row(i, tid)) * 8);
+        gv = brs.ld4f((uint32_t)(c + (tid & (kC - 1))) * 8 + 4);
     };
     load_chunk(tok_begin + (nch - 1) * kC);
 
@@ -342,9 +345,8 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_ke
             dphik[i] = x > 0.f ? 1.f : ex;
         }
         const RowAcc<T, D> vcur = vrow;
-        if (ci > 0) load_chunk(c0 - kC);
+        load_chunk(ci > 0 ? c0 - kC : N);  // past the head: zeros, no memory traffic
         const int tok = c0 + sl;
-        const bool valid = tok < N;
         __syncthreads();
 
         // (1) dA_ts = G_t.V_s + g_t and A_ts = q_sum_t + phi(Q_t).E(K_s) for s <= t
@@ -405,18 +407,15 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_ke
                 }
             }
         }
-        if (valid) {
-            const int64_t roff = hoff + (int64_t)tok * D;
 #pragma unroll
-            for (int m = 0; m < DT; ++m) {
-                const int f0 = 16 * m + 4 * g;
-                const f32x4 rv = lds4(&s_r[buf][f0]);
-                f32x4 xk;
+        for (int m = 0; m < DT; ++m) {
+            const int f0 = 16 * m + 4 * g;
+            const f32x4 rv = lds4(&s_r[buf][f0]);
+            f32x4 xk;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) xk[e] = (acck[m][e] + rv[e]) * dphik[4 * m + e];
-                gstore4(dk + roff + f0, xk);
-                gstore4(dv + roff + f0, accv[m]);
-            }
+            for (int e = 0; e < 4; ++e) xk[e] = (acck[m][e] + rv[e]) * dphik[4 * m + e];
+            gstore4<T>(bdk, (uint32_t)(tok * D + f0), xk);
+            gstore4<T>(bdv, (uint32_t)(tok * D + f0), accv[m]);
         }
 
         // (3) Suffix state: R += phi(Q)^T G, r += phi(Q)^T g.

@@ -30,7 +30,7 @@ struct Rec {
 };
 
 // Coalesced loader of one [64][D] chunk: each thread holds NV 16-byte vectors;
-// vector i covers row row(i), granule gran(i).  Rows at or beyond N read as 0.
+// vector i covers row row(i), granule gran(i).  Rows past the head's range read as 0.
 // kWaveRows = false: the block's threads cover the rows in order;
 // kWaveRows = true : wavefront w covers rows 16w .. 16w+15 (its own token tile).
 template <typename T, int D, bool kWaveRows = false>
@@ -47,12 +47,10 @@ struct ChunkRegs {
     __device__ __forceinline__ static int gran(int i, int tid) {
         return kWaveRows ? ((tid & 63) + kWave * i) % VPR : (tid + kBlock * i) % VPR;
     }
-    __device__ __forceinline__ void load(const T* head, int tok0, int N, int tid) {
+    __device__ __forceinline__ void load(const GBuf& b, int tok0, int tid) {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int tok = tok0 + row(i, tid);
-            r[i] = tok < N ? load16(head + (int64_t)tok * D + gran(i, tid) * EV) : make_uint4(0, 0, 0, 0);
-        }
+        for (int i = 0; i < NV; ++i)
+            r[i] = b.ld16((uint32_t)((tok0 + row(i, tid)) * D + gran(i, tid) * EV) * (uint32_t)sizeof(T));
     }
     __device__ __forceinline__ float get(int i, int e) const { return to_f32(reinterpret_cast<const T*>(&r[i])[e]); }
 };
@@ -60,7 +58,7 @@ struct ChunkRegs {
 // One 16-row token tile of a [N][D] input held in registers in MFMA operand
 // layout: lane l holds row (l & 15), 16-byte vector x at elements (4 x + g) EV
 // with g = l >> 4 -- for bf16 the k values of step 32 x, for fp32 those of the
-// steps 16 x + 4 e (element e), matching Mma's k order.  Rows at or beyond N read as 0.
+// steps 16 x + 4 e (element e), matching Mma's k order.  Rows past the head read as 0.
 template <typename T, int D>
 struct RowFrag {
     using M = Mma<T>;
@@ -70,11 +68,10 @@ struct RowFrag {
     static_assert(NR >= 1, "a row must cover the four lane groups");
     uint4 r[NR];
     __device__ __forceinline__ static int col(int x, int lane) { return (4 * x + (lane >> 4)) * EV; }
-    __device__ __forceinline__ void load(const T* head, int tok0, int N, int lane) {
+    __device__ __forceinline__ void load(const GBuf& b, int tok0, int lane) {
         const int tok = tok0 + (lane & 15);
 #pragma unroll
-        for (int x = 0; x < NR; ++x)
-            r[x] = tok < N ? load16(head + (int64_t)tok * D + col(x, lane)) : make_uint4(0, 0, 0, 0);
+        for (int x = 0; x < NR; ++x) r[x] = b.ld16((uint32_t)(tok * D + col(x, lane)) * (uint32_t)sizeof(T));
     }
     // f[k0 / KSTEP] = phi of the held elements as operands; returns the lane's
     // part of sum_a phi(x_a) wgt[a] (fp32 weights in LDS).
@@ -108,17 +105,19 @@ struct RowFrag {
 
 // One token row per lane in accumulator order: lane l holds row tok0 + (l & 15),
 // elements 16 m + 4 (l >> 4) + 0..3 in word m (the order of an accumulator
-// tile's rows).  Rows at or beyond N read as 0.
+// tile's rows).  Rows past the head read as 0.
 template <typename T, int D>
 struct RowAcc {
     typedef typename std::conditional<sizeof(T) == 2, uint2, uint4>::type word;
     static constexpr int NW = D / 16;
     word r[NW];
-    __device__ __forceinline__ void load(const T* head, int tok0, int N, int lane) {
-        const int tok = tok0 + (lane & 15);
+    __device__ __forceinline__ void load(const GBuf& b, int tok0, int lane) {
+        const uint32_t base = (uint32_t)((tok0 + (lane & 15)) * D + 4 * (lane >> 4)) * (uint32_t)sizeof(T);
 #pragma unroll
-        for (int m = 0; m < NW; ++m)
-            r[m] = tok < N ? *reinterpret_cast<const word*>(head + (int64_t)tok * D + 16 * m + 4 * (lane >> 4)) : word{};
+        for (int m = 0; m < NW; ++m) {
+            if constexpr (sizeof(T) == 2) r[m] = b.ld8(base + 32 * m);
+            else r[m] = b.ld16(base + 64 * m);
+        }
     }
     __device__ __forceinline__ float get(int i) const { return to_f32(reinterpret_cast<const T*>(r)[i]); }
 };
@@ -157,23 +156,6 @@ __device__ __forceinline__ void stage_raw(const ChunkRegs<T, D>& cx, const Tile<
     using CR = ChunkRegs<T, D>;
 #pragma unroll
     for (int i = 0; i < CR::NV; ++i) *reinterpret_cast<uint4*>(tX.granule(CR::row(i, tid), CR::gran(i, tid))) = cx.r[i];
-}
-
-// G = round(dO / den) row-major into LDS; rows at or beyond N are 0.
-template <typename T, int D, bool kWaveRows>
-__device__ __forceinline__ void stage_grad(const ChunkRegs<T, D, kWaveRows>& cdo, const Tile<T, kC, D>& tG,
-                                           const float* s_den, int c0, int N, int tid) {
-    using CR = ChunkRegs<T, D, kWaveRows>;
-#pragma unroll
-    for (int i = 0; i < CR::NV; ++i) {
-        const int t = CR::row(i, tid);
-        const float inv = c0 + t < N ? rcp_f(s_den[t]) : 0.f;
-        uint4 packed;
-        T* pk = reinterpret_cast<T*>(&packed);
-#pragma unroll
-        for (int e = 0; e < CR::EV; ++e) pk[e] = from_f32<T>(cdo.get(i, e) * inv);
-        *reinterpret_cast<uint4*>(tG.granule(t, CR::gran(i, tid))) = packed;
-    }
 }
 
 // Tiles of a d x d state owned by one of the 4 wavefronts: NAT row tiles
@@ -383,17 +365,15 @@ __device__ __forceinline__ float row_dot_quarters(const Tile<T, kC, D>& tQ, cons
     return sum_over_groups(s);
 }
 
-// 4 consecutive elements of a global row.
-__device__ __forceinline__ void gstore4(float* p, f32x4 a) { *reinterpret_cast<f32x4*>(p) = a; }
-__device__ __forceinline__ void gstore4(bf16* p, f32x4 a) {
-    bf16 h[4] = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
-    *reinterpret_cast<uint2*>(p) = *reinterpret_cast<const uint2*>(h);
-}
-__device__ __forceinline__ f32x4 gload4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-__device__ __forceinline__ f32x4 gload4(const bf16* p) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    const bf16* h = reinterpret_cast<const bf16*>(&u);
-    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+// 4 consecutive elements of a head's row at element offset `elem`, rounded to T.
+template <typename T>
+__device__ __forceinline__ void gstore4(const GBuf& b, uint32_t elem, f32x4 a) {
+    if constexpr (sizeof(T) == 2) {
+        bf16 h[4] = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+        b.st8(elem * 2, *reinterpret_cast<const uint2*>(h));
+    } else {
+        b.st16(elem * 4, make_uint4(__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]), __float_as_uint(a[3])));
+    }
 }
 
 }  // namespace la

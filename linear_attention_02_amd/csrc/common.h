@@ -55,10 +55,37 @@ __device__ __forceinline__ float rcp_f(float x) {
     return r * (2.f - x * r);
 }
 
-template <typename T>
-__device__ __forceinline__ uint4 load16(const T* p) {
-    return *reinterpret_cast<const uint4*>(p);
-}
+// ---- HBM access through buffer resources -----------------------------------------------
+// A buffer resource covers one head's range; reads beyond it return 0 and
+// writes beyond it are dropped, so sequence tails need no branches and the
+// compiler can count outstanding memory operations exactly.  Offsets are bytes.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+struct GBuf {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ GBuf(const void* base, uint32_t bytes)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000)) {}
+    __device__ __forceinline__ uint4 ld16(uint32_t off) const {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        return make_uint4(x.x, x.y, x.z, x.w);
+    }
+    __device__ __forceinline__ uint2 ld8(uint32_t off) const {
+        const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        return make_uint2(x.x, x.y);
+    }
+    __device__ __forceinline__ float ld4f(uint32_t off) const {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    }
+    __device__ __forceinline__ void st16(uint32_t off, uint4 v) const {
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, off, 0, 0);
+    }
+    __device__ __forceinline__ void st8(uint32_t off, uint2 v) const {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, off, 0, 0);
+    }
+    __device__ __forceinline__ void st4f(uint32_t off, float v) const {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+    }
+};
 
 // ---- swizzled LDS tiles ----------------------------------------------------------------
 // ROWS x COLS elements of OT, row-major, with the 16-byte granule index of each

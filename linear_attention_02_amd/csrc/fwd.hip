@@ -48,6 +48,8 @@ __global__ __launch_bounds__(kBlock, 4) void seg_state_kernel(const T* __restric
     const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
     const int64_t hoff = (int64_t)bh * N * D;
+    const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
+    const GBuf bk(k + hoff, hbytes), bv(v + hoff, hbytes);
     const int tok_begin = seg * cps * kC;
     const int tok_end = min(N, tok_begin + cps * kC);
 
@@ -58,19 +60,20 @@ __global__ __launch_bounds__(kBlock, 4) void seg_state_kernel(const T* __restric
     zero_vec<D>(vp);
 
     ChunkRegs<T, D> ck[2], cv[2];
-    ck[0].load(k + hoff, tok_begin, N, tid);
-    cv[0].load(v + hoff, tok_begin, N, tid);
-    ck[1].load(k + hoff, tok_begin + kC, N, tid);
-    cv[1].load(v + hoff, tok_begin + kC, N, tid);
+    ck[0].load(bk, tok_begin, tid);
+    cv[0].load(bv, tok_begin, tid);
+    ck[1].load(bk, tok_begin + kC < tok_end ? tok_begin + kC : N, tid);
+    cv[1].load(bv, tok_begin + kC < tok_end ? tok_begin + kC : N, tid);
     int c0 = tok_begin;
+    // Loads past the segment are aimed at row N: out of the buffer's range, they
+    // return zeros without touching memory, and the loop stays branch free.
     auto step = [&](ChunkRegs<T, D>& rk, ChunkRegs<T, D>& rv, int buf) {
         const Tile<T, kC, D> tE{sm_e[buf]}, tV{sm_v[buf]};
         stage_elu<T, D>(rk, tE, tid);
         stage_raw<T, D>(rv, tV, tid);
-        if (c0 + 2 * kC < tok_end) {
-            rk.load(k + hoff, c0 + 2 * kC, N, tid);
-            rv.load(v + hoff, c0 + 2 * kC, N, tid);
-        }
+        const int nxt = c0 + 2 * kC < tok_end ? c0 + 2 * kC : N;
+        rk.load(bk, nxt, tid);
+        rv.load(bv, nxt, tid);
         __syncthreads();
         state_update<T, D, true, true>(st, vz, vp, tE, tV, nullptr, nullptr, lane, w);
         c0 += kC;
@@ -131,6 +134,9 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void causal_fwd_ke
     const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
     const int64_t hoff = (int64_t)bh * N * D;
+    const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
+    const GBuf bq(q + hoff, hbytes), bk(k + hoff, hbytes), bv(v + hoff, hbytes), bo(o + hoff, hbytes);
+    const GBuf bden(den_out != nullptr ? den_out + (int64_t)bh * N : nullptr, den_out != nullptr ? (uint32_t)N * 4 : 0u);
     const int tok_begin = seg * cps * kC;
     const int tok_end = min(N, tok_begin + cps * kC);
 
@@ -143,36 +149,41 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void causal_fwd_ke
     add_records<D>(rec + (int64_t)bh * nseg * Rec<D>::kSize, Rec<D>::kSize, seg, st, vz, vp, lane, w);
     float n = (float)tok_begin;
 
-    const int t0 = 16 * w;            // this wave's token tile
-    const int tl = t0 + (lane & 15);  // this lane's token (accumulator column)
+    // Wavefront w takes token tile tt = (w + ci) mod 4 of chunk ci: the causal
+    // mask leaves tt + 1 key tiles, and the rotation spreads that work evenly
+    // over the SIMDs.
     ChunkRegs<T, D> ck, cv;
     RowFrag<T, D> qr;
-    ck.load(k + hoff, tok_begin, N, tid);
-    cv.load(v + hoff, tok_begin, N, tid);
-    qr.load(q + hoff, tok_begin + t0, N, lane);
+    ck.load(bk, tok_begin, tid);
+    cv.load(bv, tok_begin, tid);
+    qr.load(bq, tok_begin + 16 * w, lane);
+    // Stage the first chunk and publish the starting state; later chunks are
+    // staged into the other buffer while the current one finishes.
+    publish_state<T, D>(st, Tile<T, D, D>{sm_st[0]}, lane, w);
+    store_vec<D>(s_z[0], vz, lane, w);
+    store_vec<D>(s_p[0], vp, lane, w);
+    stage_elu<T, D>(ck, Tile<T, kC, D>{sm_e[0]}, tid);
+    stage_raw<T, D>(cv, Tile<T, kC, D>{sm_v[0]}, tid);
+    // Loads past the segment are aimed at row N: out of the buffer's range, they
+    // return zeros without touching memory, and the loop stays branch free.
+    ck.load(bk, tok_begin + kC < tok_end ? tok_begin + kC : N, tid);
+    cv.load(bv, tok_begin + kC < tok_end ? tok_begin + kC : N, tid);
+    __syncthreads();
 
-    int buf = 0;
-    for (int c0 = tok_begin; c0 < tok_end; c0 += kC, buf ^= 1) {
+    int buf = 0, ci = 0;
+    for (int c0 = tok_begin; c0 < tok_end; c0 += kC, buf ^= 1, ++ci) {
         const Tile<T, kC, D> tE{sm_e[buf]}, tV{sm_v[buf]};
         const Tile<T, D, D> tSt{sm_st[buf]};
         const float* sz = s_z[buf];
         const float* sp = s_p[buf];
-        // Publish the state reached so far and stage this chunk's keys and values.
-        publish_state<T, D>(st, tSt, lane, w);
-        store_vec<D>(s_z[buf], vz, lane, w);
-        store_vec<D>(s_p[buf], vp, lane, w);
-        stage_elu<T, D>(ck, tE, tid);
-        stage_raw<T, D>(cv, tV, tid);
-        if (c0 + kC < tok_end) {
-            ck.load(k + hoff, c0 + kC, N, tid);
-            cv.load(v + hoff, c0 + kC, N, tid);
-        }
-        __syncthreads();
+        const bool more = c0 + kC < tok_end;
+        const int tt = (w + ci) & 3;
+        const int tl = 16 * tt + (lane & 15);  // this lane's token (accumulator column)
 
         // phi(Q) of this wave's tokens as operands, and phi(Q_t) . z_E.
         typename M::frag qf[D / KS];
         const float zdot = sum_over_groups(qr.phi_ops(qf, sz, lane));
-        if (c0 + kC < tok_end) qr.load(q + hoff, c0 + kC + t0, N, lane);
+        qr.load(bq, more ? c0 + kC + 16 * ((w + ci + 1) & 3) : N, lane);
 
         // In-chunk weights A_ts = q_sum_t + phi(Q_t).E(K_s) for s <= t (accumulator [s][t]).
         float qs_t, den = 0.f;
@@ -181,22 +192,31 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void causal_fwd_ke
             const typename M::frag one = M::ones();
             f32x4 acc_q = zero4();
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc_a[j] = zero4();
+            for (int k0 = 0; k0 < D; k0 += KS) acc_q = M::mma(one, qf[k0 / KS], acc_q);
 #pragma unroll
-            for (int k0 = 0; k0 < D; k0 += KS) {
-                const typename M::frag yf = qf[k0 / KS];
-                acc_q = M::mma(one, yf, acc_q);
+            for (int j = 0; j < 4; ++j) {
+                acc_a[j] = zero4();
+                if (j <= tt) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc_a[j] = M::mma(M::ld(tE, 16 * j, k0, lane), yf, acc_a[j]);
+                    for (int k0 = 0; k0 < D; k0 += KS) acc_a[j] = M::mma(M::ld(tE, 16 * j, k0, lane), qf[k0 / KS], acc_a[j]);
+                }
             }
             qs_t = acc_q[0];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
+                if (j < tt) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float a = (16 * j + 4 * g + e) <= tl ? qs_t + acc_a[j][e] : 0.f;
-                    acc_a[j][e] = a;
-                    den += a;
+                    for (int e = 0; e < 4; ++e) {
+                        acc_a[j][e] += qs_t;
+                        den += acc_a[j][e];
+                    }
+                } else if (j == tt) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float a = (4 * g + e) <= (lane & 15) ? qs_t + acc_a[j][e] : 0.f;
+                        acc_a[j][e] = a;
+                        den += a;
+                    }
                 }
             }
         }
@@ -209,9 +229,11 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void causal_fwd_ke
         for (int m = 0; m < DT; ++m) acc[m] = zero4();
 #pragma unroll
         for (int k0 = 0; k0 < kC; k0 += KS) {
-            const typename M::frag yf = M::acc_op(acc_a, k0);
+            if (k0 / 16 <= tt) {
+                const typename M::frag yf = M::acc_op(acc_a, k0);
 #pragma unroll
-            for (int m = 0; m < DT; ++m) acc[m] = M::mma(M::ld_tr_acc(tV, k0, 16 * m, lane), yf, acc[m]);
+                for (int m = 0; m < DT; ++m) acc[m] = M::mma(M::ld_tr_acc(tV, k0, 16 * m, lane), yf, acc[m]);
+            }
         }
 #pragma unroll
         for (int k0 = 0; k0 < D; k0 += KS) {
@@ -219,28 +241,35 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void causal_fwd_ke
 #pragma unroll
             for (int m = 0; m < DT; ++m) acc[m] = M::mma(M::ld(tSt, 16 * m, k0, lane), yf, acc[m]);
         }
-        const int tok = c0 + tl;
-        if (tok < N) {
-            T* orow = o + hoff + (int64_t)tok * D;
+        const int tok = c0 + tl;  // rows past the head are dropped by the buffer range
 #pragma unroll
-            for (int m = 0; m < DT; ++m) {
-                const int b0 = 16 * m + 4 * g;
-                const f32x4 p4 = lds4(&sp[b0]);
-                f32x4 x;
+        for (int m = 0; m < DT; ++m) {
+            const int b0 = 16 * m + 4 * g;
+            const f32x4 p4 = lds4(&sp[b0]);
+            f32x4 x;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = (acc[m][e] + qs_t * p4[e]) * inv;
-                gstore4(orow + b0, x);
-            }
-            if (den_out != nullptr && g == 0) den_out[(int64_t)bh * N + tok] = den;
+            for (int e = 0; e < 4; ++e) x[e] = (acc[m][e] + qs_t * p4[e]) * inv;
+            gstore4<T>(bo, (uint32_t)(tok * D + b0), x);
         }
+        if (den_out != nullptr && g == 0) bden.st4f((uint32_t)tok * 4, den);
 
-        // State update: S_E += E(K)^T V, z_E += colsum E(K), P += colsum V.
+        // Stage the next chunk into the other buffer (idle after the last chunk),
+        // then the state update: S_E += E(K)^T V, z_E += colsum E(K), P += colsum V,
+        // published for the next chunk.
+        stage_elu<T, D>(ck, Tile<T, kC, D>{sm_e[buf ^ 1]}, tid);
+        stage_raw<T, D>(cv, Tile<T, kC, D>{sm_v[buf ^ 1]}, tid);
+        ck.load(bk, c0 + 2 * kC < tok_end ? c0 + 2 * kC : N, tid);
+        cv.load(bv, c0 + 2 * kC < tok_end ? c0 + 2 * kC : N, tid);
         state_update<T, D, true, true>(st, vz, vp, tE, tV, nullptr, nullptr, lane, w);
+        publish_state<T, D>(st, Tile<T, D, D>{sm_st[buf ^ 1]}, lane, w);
+        store_vec<D>(s_z[buf ^ 1], vz, lane, w);
+        store_vec<D>(s_p[buf ^ 1], vp, lane, w);
         n += (float)min(kC, N - c0);
+        __syncthreads();
     }
 
     if (seg == nseg - 1 && (S_out != nullptr || z_out != nullptr)) {
-        // The buffer not read by the last chunk is free once every wave is past its barrier.
+        // The buffer not read by the last chunk is free: every wave is past the last barrier.
         store_vec<D>(s_z[buf], vz, lane, w);
         store_vec<D>(s_p[buf], vp, lane, w);
         __syncthreads();
@@ -278,6 +307,8 @@ __global__ __launch_bounds__(kBlock) void noncausal_fwd_kernel(const T* __restri
     const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
     const int64_t hoff = (int64_t)bh * N * D;
+    const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
+    const GBuf bq(q + hoff, hbytes), bo(o + hoff, hbytes);
     const int tok_begin = seg * cps * kC;
     const int tok_end = min(N, tok_begin + cps * kC);
     const float* r = total + (int64_t)bh * Rec<D>::kSize;
@@ -293,13 +324,13 @@ __global__ __launch_bounds__(kBlock) void noncausal_fwd_kernel(const T* __restri
     const int t0 = 16 * w;
     const int tl = t0 + (lane & 15);
     RowFrag<T, D> qr;
-    qr.load(q + hoff, tok_begin + t0, N, lane);
+    qr.load(bq, tok_begin + t0, lane);
     __syncthreads();
 
     for (int c0 = tok_begin; c0 < tok_end; c0 += kC) {
         typename M::frag qf[D / KS];
         const float zdot = sum_over_groups(qr.phi_ops(qf, s_z, lane));
-        if (c0 + kC < tok_end) qr.load(q + hoff, c0 + kC + t0, N, lane);
+        qr.load(bq, c0 + kC < tok_end ? c0 + kC + t0 : N, lane);
         const typename M::frag one = M::ones();
         f32x4 acc_q = zero4();
         f32x4 acc[DT];
@@ -315,17 +346,14 @@ __global__ __launch_bounds__(kBlock) void noncausal_fwd_kernel(const T* __restri
         const float qs_t = acc_q[0];
         const float inv = rcp_f(n * qs_t + zdot);
         const int tok = c0 + tl;
-        if (tok < N) {
-            T* orow = o + hoff + (int64_t)tok * D;
 #pragma unroll
-            for (int m = 0; m < DT; ++m) {
-                const int b0 = 16 * m + 4 * g;
-                const f32x4 p4 = lds4(&s_p[b0]);
-                f32x4 x;
+        for (int m = 0; m < DT; ++m) {
+            const int b0 = 16 * m + 4 * g;
+            const f32x4 p4 = lds4(&s_p[b0]);
+            f32x4 x;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = (acc[m][e] + qs_t * p4[e]) * inv;
-                gstore4(orow + b0, x);
-            }
+            for (int e = 0; e < 4; ++e) x[e] = (acc[m][e] + qs_t * p4[e]) * inv;
+            gstore4<T>(bo, (uint32_t)(tok * D + b0), x);
         }
     }
 }
