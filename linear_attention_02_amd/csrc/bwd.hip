@@ -66,7 +66,6 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
 
     const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
-    const int t0 = 16 * w, tl = t0 + (lane & 15);
     const int64_t hoff = (int64_t)bh * N * D;
     const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
     const GBuf bq(q + hoff, hbytes), bk(k + hoff, hbytes), bv(v + hoff, hbytes), bdo(dout + hoff, hbytes);
@@ -89,14 +88,19 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
     ChunkRegs<T, D> ck, cv;
     ChunkRegs<T, D, true> cq;
     RowAcc<T, D> cdo;
+    // Wavefront w takes token tile tt = (w + ci) mod 4 of chunk ci: the causal
+    // mask leaves tt + 1 key tiles, and the rotation spreads that work evenly
+    // over the SIMDs.
     ck.load(bk, tok_begin, tid);
     cv.load(bv, tok_begin, tid);
-    cq.load(bq, tok_begin, tid);
-    cdo.load(bdo, tok_begin + t0, lane);
+    cq.load(bq, tok_begin + 16 * w, tid);
+    cdo.load(bdo, tok_begin + 16 * w, lane);
 
-    int buf = 0;
-    for (int c0 = tok_begin; c0 < tok_end; c0 += kC, buf ^= 1) {
+    int buf = 0, ci = 0;
+    for (int c0 = tok_begin; c0 < tok_end; c0 += kC, buf ^= 1, ++ci) {
         const Tile<T, kC, D> tE{sm_e[buf]}, tV{sm_v[buf]};
+        const int tt = (w + ci) & 3, tt_next = (w + ci + 1) & 3;
+        const int tl = 16 * tt + (lane & 15);
         publish_state<T, D>(stS, tSt, lane, w);
         store_vec<D>(s_z, vz, lane, w);
         store_vec<D>(s_p, vp, lane, w);
@@ -113,8 +117,8 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
 
         // phi(Q) of this wave's rows: staged (for the R update) and read back in
         // accumulator order where it is used (short register lifetimes).
-        stage_phi<T, D, true>(cq, tQ, tid);
-        cq.load(bq, nxt, tid);
+        stage_phi<T, D, true>(cq, tQ, tid, 16 * tt);
+        cq.load(bq, nxt < N ? nxt + 16 * tt_next : N, tid);
         wave_lds_sync();
         auto read_y = [&](float* y) {
 #pragma unroll
@@ -146,17 +150,24 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
                 const typename M::frag yq = M::vals_op(y, k0);
                 accq = M::mma(one, yq, accq);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) accB[j] = M::mma(M::ld_acc(tE, 16 * j, k0, lane), yq, accB[j]);
+                for (int j = 0; j < 4; ++j)
+                    if (j <= tt) accB[j] = M::mma(M::ld_acc(tE, 16 * j, k0, lane), yq, accB[j]);
             }
             qs_t = accq[0];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j) {
+                if (j < tt) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float b = (16 * j + 4 * g + e) <= tl ? accB[j][e] : 0.f;
-                    accB[j][e] = b;
-                    rowB += b;
+                    for (int e = 0; e < 4; ++e) rowB += accB[j][e];
+                } else if (j == tt) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float b = (4 * g + e) <= (lane & 15) ? accB[j][e] : 0.f;
+                        accB[j][e] = b;
+                        rowB += b;
+                    }
                 }
+            }
         }
         const float den = qs_t * (n + (float)(tl + 1)) + sum_over_groups(rowB) + sum_over_groups(zd);
         const float inv_den = rcp_f(den);
@@ -176,7 +187,7 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
 #pragma unroll
                 for (int e = 0; e < 4; ++e) gp += gy[4 * m + e] * pv[e];
             }
-            cdo.load(bdo, nxt < N ? nxt + t0 : N, lane);
+            cdo.load(bdo, nxt < N ? nxt + 16 * tt_next : N, lane);
 #pragma unroll
             for (int j = 0; j < 4; ++j) accGV[j] = zero4();
 #pragma unroll
@@ -185,9 +196,10 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
             for (int k0 = 0; k0 < D; k0 += KS) {
                 const typename M::frag yg = M::vals_op(gy, k0);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) accGV[j] = M::mma(M::ld_acc(tV, 16 * j, k0, lane), yg, accGV[j]);
-#pragma unroll
                 for (int m = 0; m < DT; ++m) accQ[m] = M::mma(M::ld_tr_acc(tSt, k0, 16 * m, lane), yg, accQ[m]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (j <= tt) accGV[j] = M::mma(M::ld_acc(tV, 16 * j, k0, lane), yg, accGV[j]);
             }
         }
         gp = sum_over_groups(gp);
@@ -196,9 +208,15 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
         //     G_t . num_t = sum_{s<=t} A_ts (G_t.V_s) + q_sum_t (G_t.P) + phi(Q_t).(S_E G_t).
         float s1 = 0.f, s3 = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
+            if (j < tt) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s1 += (16 * j + 4 * g + e) <= tl ? (qs_t + accB[j][e]) * accGV[j][e] : 0.f;
+                for (int e = 0; e < 4; ++e) s1 += (qs_t + accB[j][e]) * accGV[j][e];
+            } else if (j == tt) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s1 += (4 * g + e) <= (lane & 15) ? (qs_t + accB[j][e]) * accGV[j][e] : 0.f;
+            }
+        }
         float y[NY];
         read_y(y);
 #pragma unroll
@@ -214,22 +232,33 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
         // (5) dA_ts = G_t.V_s + g_t for s <= t, in place; its row sums.
         float rowdA = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
+            if (j < tt) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float a = (16 * j + 4 * g + e) <= tl ? accGV[j][e] + gt : 0.f;
-                accGV[j][e] = a;
-                rowdA += a;
+                for (int e = 0; e < 4; ++e) {
+                    accGV[j][e] += gt;
+                    rowdA += accGV[j][e];
+                }
+            } else if (j == tt) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float a = (4 * g + e) <= (lane & 15) ? accGV[j][e] + gt : 0.f;
+                    accGV[j][e] = a;
+                    rowdA += a;
+                }
             }
+        }
         rowdA = sum_over_groups(rowdA);
 
         // (6) dphi(Q)^T[a][t] = (S_E G_t)_a + sum_s E[s][a] dA[t][s] + z_E[a] g_t + bracket_t;
         //     dQ = dphi(Q) phi'(Q) with phi'(Q) = min(phi(Q), 1).
 #pragma unroll
         for (int k0 = 0; k0 < kC; k0 += KS) {
-            const typename M::frag yd = M::acc_op(accGV, k0);
+            if (k0 / 16 <= tt) {
+                const typename M::frag yd = M::acc_op(accGV, k0);
 #pragma unroll
-            for (int m = 0; m < DT; ++m) accQ[m] = M::mma(M::ld_tr_acc(tE, k0, 16 * m, lane), yd, accQ[m]);
+                for (int m = 0; m < DT; ++m) accQ[m] = M::mma(M::ld_tr_acc(tE, k0, 16 * m, lane), yd, accQ[m]);
+            }
         }
         {
             const float bracket = rowdA + gp + gt * n;
@@ -258,8 +287,9 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
 }
 
 // ---------------------------------------------------------------------------------------
-// bwd_suffix.  Wavefront w owns the key tile s = 16 w .. 16 w + 15 of every
-// chunk; its K and V rows stay in registers in accumulator order (E(K) and
+// bwd_suffix.  Wavefront w owns key tile st = (w + it) mod 4 of the it-th chunk
+// it visits (the causal mask leaves 4 - st token tiles; the rotation spreads
+// that work evenly over the SIMDs); its K and V rows stay in registers in accumulator order (E(K) and
 // phi'(K) share one exp), while phi(Q), G and the rounded R^T are staged in LDS
 // (double-buffered, one barrier per chunk).  A and dA for the wave's keys stay
 // in the accumulators that form them and feed the dV and dK products directly;
@@ -281,7 +311,6 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_ke
 
     const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
-    const int s0 = 16 * w, sl = s0 + (lane & 15);  // this wave's key tile, this lane's key
     const int64_t hoff = (int64_t)bh * N * D;
     const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
     const GBuf bq(q + hoff, hbytes), bk(k + hoff, hbytes), bv(v + hoff, hbytes), bdo(dout + hoff, hbytes);
@@ -303,21 +332,23 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_ke
     RowAcc<T, D> kr, vrow;
     float dn[CR::NV];
     float gv = 0.f;
-    auto load_chunk = [&](int c) {
+    auto load_chunk = [&](int c, int st) {
         cq.load(bq, c, tid);
         cdo.load(bdo, c, tid);
-        kr.load(bk, c + s0, lane);
-        vrow.load(bv, c + s0, lane);
+        kr.load(bk, c < N ? c + 16 * st : N, lane);
+        vrow.load(bv, c < N ? c + 16 * st : N, lane);
         // den of the rows this thread stages, g of token tid (rows past the head read as 0)
 #pragma unroll
         for (int i = 0; i < CR::NV; ++i) dn[i] = brs.ld4f((uint32_t)(c + CR::row(i, tid)) * 8);
         gv = brs.ld4f((uint32_t)(c + (tid & (kC - 1))) * 8 + 4);
     };
-    load_chunk(tok_begin + (nch - 1) * kC);
+    load_chunk(tok_begin + (nch - 1) * kC, w);
 
     int buf = 0;
-    for (int ci = nch - 1; ci >= 0; --ci, buf ^= 1) {
+    for (int ci = nch - 1, it = 0; ci >= 0; --ci, ++it, buf ^= 1) {
         const int c0 = tok_begin + ci * kC;
+        const int st = (w + it) & 3;
+        const int sl = 16 * st + (lane & 15);  // this lane's key
         const Tile<T, kC, D> tQ{sm_q[buf]}, tG{sm_g[buf]};
         const Tile<T, D, D> tRt{sm_rt[buf]};
         publish_state<T, D>(stR, tRt, lane, w);
@@ -345,7 +376,7 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_ke
             dphik[i] = x > 0.f ? 1.f : ex;
         }
         const RowAcc<T, D> vcur = vrow;
-        load_chunk(ci > 0 ? c0 - kC : N);  // past the head: zeros, no memory traffic
+        load_chunk(ci > 0 ? c0 - kC : N, (w + it + 1) & 3);  // past the head: zeros, no memory traffic
         const int tok = c0 + sl;
         __syncthreads();
 
@@ -354,22 +385,37 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_ke
         f32x4 dA[4], A[4];
         {
             const typename M::frag one = M::ones();
+            typename M::frag yv[D / KS], ye[D / KS];
+#pragma unroll
+            for (int k0 = 0; k0 < D; k0 += KS) {
+                yv[k0 / KS] = M::raw_op(vcur.r, k0);
+                ye[k0 / KS] = M::vals_op(ke, k0);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                f32x4 acc_d = zero4(), acc_b = zero4(), acc_q = zero4();
+                dA[i] = zero4();
+                A[i] = zero4();
+                if (i >= st) {
+                    f32x4 acc_d = zero4(), acc_b = zero4(), acc_q = zero4();
 #pragma unroll
-                for (int k0 = 0; k0 < D; k0 += KS) {
-                    const typename M::frag xq = M::ld_acc(tQ, 16 * i, k0, lane);
-                    acc_d = M::mma(M::ld_acc(tG, 16 * i, k0, lane), M::raw_op(vcur.r, k0), acc_d);
-                    acc_b = M::mma(xq, M::vals_op(ke, k0), acc_b);
-                    acc_q = M::mma(xq, one, acc_q);
-                }
-                const f32x4 gt4 = lds4(&s_g[buf][16 * i + 4 * g]);
+                    for (int k0 = 0; k0 < D; k0 += KS) {
+                        const typename M::frag xq = M::ld_acc(tQ, 16 * i, k0, lane);
+                        acc_d = M::mma(M::ld_acc(tG, 16 * i, k0, lane), yv[k0 / KS], acc_d);
+                        acc_b = M::mma(xq, ye[k0 / KS], acc_b);
+                        acc_q = M::mma(xq, one, acc_q);
+                    }
+                    const f32x4 gt4 = lds4(&s_g[buf][16 * i + 4 * g]);
+                    if (i > st) {
+                        dA[i] = acc_d + gt4;
+                        A[i] = acc_b + acc_q;
+                    } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool live = sl <= 16 * i + 4 * g + e;
-                    dA[i][e] = live ? acc_d[e] + gt4[e] : 0.f;
-                    A[i][e] = live ? acc_b[e] + acc_q[e] : 0.f;
+                        for (int e = 0; e < 4; ++e) {
+                            const bool live = (lane & 15) <= 4 * g + e;
+                            dA[i][e] = live ? acc_d[e] + gt4[e] : 0.f;
+                            A[i][e] = live ? acc_b[e] + acc_q[e] : 0.f;
+                        }
+                    }
                 }
             }
         }
@@ -384,12 +430,14 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_ke
         }
 #pragma unroll
         for (int k0 = 0; k0 < kC; k0 += KS) {
-            const typename M::frag yd = M::acc_op(dA, k0);
-            const typename M::frag ya = M::acc_op(A, k0);
+            if ((k0 + KS - 1) / 16 >= st) {
+                const typename M::frag yd = M::acc_op(dA, k0);
+                const typename M::frag ya = M::acc_op(A, k0);
 #pragma unroll
-            for (int m = 0; m < DT; ++m) {
-                acck[m] = M::mma(M::ld_tr_acc(tQ, k0, 16 * m, lane), yd, acck[m]);
-                accv[m] = M::mma(M::ld_tr_acc(tG, k0, 16 * m, lane), ya, accv[m]);
+                for (int m = 0; m < DT; ++m) {
+                    acck[m] = M::mma(M::ld_tr_acc(tQ, k0, 16 * m, lane), yd, acck[m]);
+                    accv[m] = M::mma(M::ld_tr_acc(tG, k0, 16 * m, lane), ya, accv[m]);
+                }
             }
         }
         {

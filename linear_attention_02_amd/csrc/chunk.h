@@ -31,22 +31,23 @@ struct Rec {
 
 // Coalesced loader of one [64][D] chunk: each thread holds NV 16-byte vectors;
 // vector i covers row row(i), granule gran(i).  Rows past the head's range read as 0.
-// kWaveRows = false: the block's threads cover the rows in order;
-// kWaveRows = true : wavefront w covers rows 16w .. 16w+15 (its own token tile).
+// kWaveRows = false: the block's threads cover the 64 rows in order;
+// kWaveRows = true : each wavefront covers 16 rows (a token tile) from tok0.
 template <typename T, int D, bool kWaveRows = false>
 struct ChunkRegs {
     static constexpr int EV = 16 / (int)sizeof(T);
     static constexpr int VPR = D / EV;  // vectors per row (held by consecutive lanes)
-    static constexpr int NV = kC * VPR / kBlock;
-    static_assert(NV >= 1 && (kC * VPR) % kBlock == 0, "chunk must split evenly over the block");
+    static_assert((kC * VPR) % kBlock == 0 && (16 * VPR) % kWave == 0, "rows must split evenly over the threads");
     static_assert(VPR <= kWave, "a row must sit inside one wavefront");
-    uint4 r[NV];
+    static constexpr int ROWS = kWaveRows ? 16 : kC;
+    static constexpr int NV = ROWS * VPR / (kWaveRows ? kWave : kBlock);
     __device__ __forceinline__ static int row(int i, int tid) {
-        return kWaveRows ? 16 * (tid >> 6) + ((tid & 63) + kWave * i) / VPR : (tid + kBlock * i) / VPR;
+        return kWaveRows ? ((tid & 63) + kWave * i) / VPR : (tid + kBlock * i) / VPR;
     }
     __device__ __forceinline__ static int gran(int i, int tid) {
         return kWaveRows ? ((tid & 63) + kWave * i) % VPR : (tid + kBlock * i) % VPR;
     }
+    uint4 r[NV];
     __device__ __forceinline__ void load(const GBuf& b, int tok0, int tid) {
 #pragma unroll
         for (int i = 0; i < NV; ++i)
@@ -123,8 +124,10 @@ struct RowAcc {
 };
 
 // phi(Q) row-major into LDS.
+// (kWaveRows: the wavefront's rows go to tile rows row0 ..)
 template <typename T, int D, bool kWaveRows = false>
-__device__ __forceinline__ void stage_phi(const ChunkRegs<T, D, kWaveRows>& cq, const Tile<T, kC, D>& tQ, int tid) {
+__device__ __forceinline__ void stage_phi(const ChunkRegs<T, D, kWaveRows>& cq, const Tile<T, kC, D>& tQ, int tid,
+                                          int row0 = 0) {
     using CR = ChunkRegs<T, D, kWaveRows>;
 #pragma unroll
     for (int i = 0; i < CR::NV; ++i) {
@@ -132,7 +135,7 @@ __device__ __forceinline__ void stage_phi(const ChunkRegs<T, D, kWaveRows>& cq, 
         T* pk = reinterpret_cast<T*>(&packed);
 #pragma unroll
         for (int e = 0; e < CR::EV; ++e) pk[e] = from_f32<T>(phi_f(cq.get(i, e)));
-        *reinterpret_cast<uint4*>(tQ.granule(CR::row(i, tid), CR::gran(i, tid))) = packed;
+        *reinterpret_cast<uint4*>(tQ.granule(row0 + CR::row(i, tid), CR::gran(i, tid))) = packed;
     }
 }
 
