@@ -23,7 +23,15 @@ The JSON line also carries
   * cpu_baseline: the fp64 CPU oracle timed on this host on repeated full
                   steps of the same workload (bounded to about 10 s).
 
+The roofline's "traffic" is the dominant kernel's measured HBM bytes per
+launch: FETCH_SIZE and WRITE_SIZE from two rocprofv3 counter passes over this
+script, each divided by the factor the same counter reads for a plain copy of
+known size (`--copy-probe`).  They are read from profiles/<kernel>_traffic.txt,
+which records a hash of the kernel sources; when the sources have changed since
+the counters were taken the field is null.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-calls] [--no-cpu]
+       python bench.py --copy-probe      (a 256 MiB device copy, for counter calibration)
 """
 from __future__ import annotations
 
@@ -50,7 +58,54 @@ def parse():
     ap.add_argument("--no-calls", action="store_true", help="skip the other calls")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe", action="store_true", help="only run 5 device copies of 256 MiB")
     return ap.parse_args()
+
+
+COPY_PROBE_BYTES = 256 * 2**20
+
+
+def copy_probe(torch):
+    """Five copies of COPY_PROBE_BYTES between two device buffers (counter calibration)."""
+    src = torch.ones(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "copies": 5}), flush=True)
+
+
+def kernel_source_hash():
+    """sha256 over the HIP sources and headers the library is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_02_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from profiles/<kernel>_traffic.txt, or None if
+    absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def kernel_stats(entries):
@@ -81,7 +136,7 @@ def sequence_roofline(stats, B, H, N, d, steps):
     alg = units * unit_bytes(B, H, N, d)
     ach = alg / avg_s / 1e9
     return name, {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                  "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name),
                   "kernel": name, "launches": n, "avg_us": round(avg_s * 1e6, 2),
                   "alg_bytes_per_launch": alg}
 
@@ -254,6 +309,10 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
+
+    if args.copy_probe:
+        copy_probe(torch)
+        return
 
     import la_inputs as inp
     import linear_attention_02_amd as la
