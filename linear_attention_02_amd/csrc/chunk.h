@@ -123,6 +123,32 @@ struct RowAcc {
     __device__ __forceinline__ float get(int i) const { return to_f32(reinterpret_cast<const T*>(r)[i]); }
 };
 
+// Direct-to-LDS fill of a swizzled [64][D] tile from rows tok0.. of a head: each
+// wavefront issues PER_WAVE buffer loads whose 64 lanes land 16 bytes apiece on
+// consecutive LDS granules; the global address of each lane is chosen so that
+// the granule lands at its swizzled place.  Rows past the head's range fill
+// with zeros and move no bytes.  Completion is tracked by the vector-memory
+// count (PER_WAVE per tile per wavefront).
+typedef __attribute__((address_space(3))) void lds_void;
+template <typename T, int D>
+struct TileDma {
+    static constexpr int EV = 16 / (int)sizeof(T);
+    static constexpr int G = D / EV;
+    static constexpr int PER_WAVE = kC * G / (kWave * (kBlock / kWave));
+    static_assert(PER_WAVE >= 1 && kC * G % kBlock == 0, "a tile must split evenly over the wavefronts");
+    __device__ __forceinline__ static void issue(const GBuf& b, int tok0, T* tile, int w, int lane) {
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int slot0 = (w * PER_WAVE + i) * kWave;
+            const int sl = slot0 + lane;
+            const int r = sl / G, p = sl % G;
+            const int gi = p ^ Tile<T, kC, D>::swz(r);
+            const uint32_t off = (uint32_t)((tok0 + r) * D + gi * EV) * (uint32_t)sizeof(T);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (lds_void*)(tile + slot0 * EV), 16, off, 0, 0, 0);
+        }
+    }
+};
+
 // phi(Q) row-major into LDS.
 // (kWaveRows: the wavefront's rows go to tile rows row0 ..)
 template <typename T, int D, bool kWaveRows = false>
@@ -292,44 +318,71 @@ __device__ __forceinline__ void publish_state(const StateAcc<D>& st, const Tile<
 // tiles read with the transposing load; optionally
 // va[a] += sum_t X[t][a] * u[t] and vb[b] += sum_t Y[t][b] * v[t] for the
 // wave's vector tiles, with u, v either all ones (null pointer) or fp32
-// vectors in LDS (split hi + lo in bf16).
-template <typename T, int D, bool kVecA, bool kVecB>
+// vectors in LDS (split hi + lo in bf16).  The vector tiles a wave owns are
+// its own row tiles, so va reuses the X operands.  kEluX: X holds raw keys and
+// the operands are E(X) = elu(X), applied after the load.
+template <typename T, int D, bool kVecA, bool kVecB, bool kEluX = false>
 __device__ __forceinline__ void state_update(StateAcc<D>& st, VecAcc<D>& va, VecAcc<D>& vb, const Tile<T, kC, D>& tX,
                                              const Tile<T, kC, D>& tY, const float* u, const float* v, int lane,
                                              int w) {
     using M = Mma<T>;
     using ST = StateTiles<D>;
-    const typename M::frag one = M::ones();
+    static_assert(ST::NVT == ST::NAT, "a wave's vector tiles are its row tiles");
+    typedef typename M::frag F;
+    // All LDS operands of a group of KG k-steps are requested before the first
+    // MFMA, so the LDS latency is paid once per group rather than once per product.
+    constexpr int FR = (int)(sizeof(F) / 4);
+    constexpr int PER_K = ST::NAT + ST::NBT + (kVecB ? ST::NVT : 0);
+    constexpr int KSTEPS = kC / M::KSTEP;
+    constexpr int KG0 = 48 / (PER_K * FR) > 0 ? 48 / (PER_K * FR) : 1;
+    constexpr int KG1 = KG0 < KSTEPS ? KG0 : KSTEPS;
+    constexpr int KG = KG1 >= 16 ? 16 : KG1 >= 8 ? 8 : KG1 >= 4 ? 4 : KG1 >= 2 ? 2 : 1;  // a power of two
+    static_assert(KSTEPS % KG == 0, "k-step groups must tile the chunk");
+    const F one = M::ones();
 #pragma unroll
-    for (int k0 = 0; k0 < kC; k0 += M::KSTEP) {
-        typename M::frag xf[ST::NAT];
+    for (int kg = 0; kg < KSTEPS; kg += KG) {
+        F xf[KG][ST::NAT], yf[KG][ST::NBT], yv[KG][kVecB ? ST::NVT : 1];
 #pragma unroll
-        for (int ia = 0; ia < ST::NAT; ++ia) xf[ia] = M::ld_tr(tX, k0, (ST::at0(w) + ia) * 16, lane);
+        for (int kk = 0; kk < KG; ++kk) {
+            const int k0 = (kg + kk) * M::KSTEP;
 #pragma unroll
-        for (int ib = 0; ib < ST::NBT; ++ib) {
-            const typename M::frag yf = M::ld_tr(tY, k0, (ST::bt0(w) + ib) * 16, lane);
+            for (int ia = 0; ia < ST::NAT; ++ia) xf[kk][ia] = M::ld_tr(tX, k0, (ST::at0(w) + ia) * 16, lane);
 #pragma unroll
-            for (int ia = 0; ia < ST::NAT; ++ia) st[ia][ib] = M::mma(xf[ia], yf, st[ia][ib]);
-        }
-        if (ST::owns_vec(w)) {
-            if (kVecA) {
-                typename M::frag hi = one, lo = one;
-                if (u != nullptr) M::splat(u, k0, lane, hi, lo);
+            for (int ib = 0; ib < ST::NBT; ++ib) yf[kk][ib] = M::ld_tr(tY, k0, (ST::bt0(w) + ib) * 16, lane);
+            if (kVecB && ST::owns_vec(w)) {
 #pragma unroll
-                for (int x = 0; x < ST::NVT; ++x) {
-                    const typename M::frag xv = M::ld_tr(tX, k0, (ST::vt0(w) + x) * 16, lane);
-                    va[x] = M::mma(xv, hi, va[x]);
-                    if (M::kSplitSplat && u != nullptr) va[x] = M::mma(xv, lo, va[x]);
-                }
+                for (int x = 0; x < ST::NVT; ++x) yv[kk][x] = M::ld_tr(tY, k0, (ST::vt0(w) + x) * 16, lane);
             }
-            if (kVecB) {
-                typename M::frag hi = one, lo = one;
-                if (v != nullptr) M::splat(v, k0, lane, hi, lo);
+        }
 #pragma unroll
-                for (int x = 0; x < ST::NVT; ++x) {
-                    const typename M::frag yv = M::ld_tr(tY, k0, (ST::vt0(w) + x) * 16, lane);
-                    vb[x] = M::mma(yv, hi, vb[x]);
-                    if (M::kSplitSplat && v != nullptr) vb[x] = M::mma(yv, lo, vb[x]);
+        for (int kk = 0; kk < KG; ++kk) {
+            const int k0 = (kg + kk) * M::KSTEP;
+            if (kEluX) {
+#pragma unroll
+                for (int ia = 0; ia < ST::NAT; ++ia) xf[kk][ia] = M::elu_op(xf[kk][ia]);
+            }
+#pragma unroll
+            for (int ib = 0; ib < ST::NBT; ++ib)
+#pragma unroll
+                for (int ia = 0; ia < ST::NAT; ++ia) st[ia][ib] = M::mma(xf[kk][ia], yf[kk][ib], st[ia][ib]);
+            if (ST::owns_vec(w)) {
+                if (kVecA) {
+                    F hi = one, lo = one;
+                    if (u != nullptr) M::splat(u, k0, lane, hi, lo);
+#pragma unroll
+                    for (int x = 0; x < ST::NVT; ++x) {
+                        va[x] = M::mma(xf[kk][x], hi, va[x]);
+                        if (M::kSplitSplat && u != nullptr) va[x] = M::mma(xf[kk][x], lo, va[x]);
+                    }
+                }
+                if (kVecB) {
+                    F hi = one, lo = one;
+                    if (v != nullptr) M::splat(v, k0, lane, hi, lo);
+#pragma unroll
+                    for (int x = 0; x < ST::NVT; ++x) {
+                        vb[x] = M::mma(yv[kk][x], hi, vb[x]);
+                        if (M::kSplitSplat && v != nullptr) vb[x] = M::mma(yv[kk][x], lo, vb[x]);
+                    }
                 }
             }
         }

@@ -87,6 +87,27 @@ struct GBuf {
     }
 };
 
+// ---- waits and barriers managed by hand ---------------------------------------------------
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding).
+// The signal fences keep the compiler from moving memory operations across
+// these points (they emit no instruction).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding direct-to-LDS load): the caller has made the LDS
+// data it needs complete with explicit waits.
+__device__ __forceinline__ void raw_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS operations are done
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---- swizzled LDS tiles ----------------------------------------------------------------
 // ROWS x COLS elements of OT, row-major, with the 16-byte granule index of each
 // row XOR-ed by a row-dependent value so that 16-row operand reads, 8-row
@@ -184,6 +205,13 @@ struct Mma<bf16> {
         const bf16x4 hi = *reinterpret_cast<const bf16x4*>(&r[k0 / 16 + 1]);
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
+    // elu of every element, rounded back to bf16.
+    __device__ __forceinline__ static frag elu_op(frag x) {
+        frag f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = (bf16)elu_f((float)x[e]);
+        return f;
+    }
     // Operand for k-step k0 of a contraction over the row index of accumulator
     // tiles acc[0..]: the column index of the tiles is the operand row.
     __device__ __forceinline__ static frag acc_op(const f32x4* acc, int k0) {
@@ -250,6 +278,7 @@ struct Mma<float> {
         return reinterpret_cast<const float*>(&r[k0 >> 4])[(k0 & 15) >> 2];
     }
     __device__ __forceinline__ static frag acc_op(const f32x4* acc, int k0) { return acc[k0 >> 4][(k0 & 15) >> 2]; }
+    __device__ __forceinline__ static frag elu_op(frag x) { return elu_f(x); }
     __device__ __forceinline__ static void splat(const float* v, int k0, int lane, frag& hi, frag& lo) {
         hi = v[kap(k0, lane)];
         lo = 0.f;

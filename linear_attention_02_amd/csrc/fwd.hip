@@ -38,12 +38,21 @@ namespace la {
 
 // ---------------------------------------------------------------------------------------
 // seg_state: per (segment, head) the aggregates (S_E, z_E, P) of the segment's keys.
-// Two chunks are in flight ahead of the one being reduced.
+// K and V chunks stream into an LDS ring of R slots with direct-to-LDS loads
+// (R - 1 chunks in flight while one is reduced); E = elu is applied to the
+// MFMA operands, since each wavefront reads its own key columns only.  Waits
+// and barriers are explicit: a step waits for its slot's loads, synchronises
+// the workgroup, then refills the slot the previous step has finished reading.
 template <typename T, int D>
-__global__ __launch_bounds__(kBlock, 4) void seg_state_kernel(const T* __restrict__ k, const T* __restrict__ v,
+__global__ __launch_bounds__(kBlock, 2) void seg_state_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                            float* __restrict__ rec, int N, int cps, int nseg, int BH) {
-    __shared__ __attribute__((aligned(16))) T sm_e[2][kC * D];
-    __shared__ __attribute__((aligned(16))) T sm_v[2][kC * D];
+    using DMA = TileDma<T, D>;
+    constexpr int R = kC * D * (int)sizeof(T) >= 16384 ? 2 : 4;
+    constexpr int RS = R > 2 ? kC * D : 16;  // slots 2 and 3 exist only for R = 4
+    __shared__ __attribute__((aligned(16))) T sk0[kC * D], sk1[kC * D], sk2[RS], sk3[RS];
+    __shared__ __attribute__((aligned(16))) T sv0[kC * D], sv1[kC * D], sv2[RS], sv3[RS];
+    T* const ks[4] = {sk0, sk1, sk2, sk3};
+    T* const vs[4] = {sv0, sv1, sv2, sv3};
 
     const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
@@ -52,6 +61,10 @@ __global__ __launch_bounds__(kBlock, 4) void seg_state_kernel(const T* __restric
     const GBuf bk(k + hoff, hbytes), bv(v + hoff, hbytes);
     const int tok_begin = seg * cps * kC;
     const int tok_end = min(N, tok_begin + cps * kC);
+    const int nch = (tok_end - tok_begin + kC - 1) / kC;
+    const int nsteps = (nch + R - 1) / R * R;
+    // Chunks past the segment are aimed at row N: zeros, no memory traffic.
+    auto chunk_tok = [&](int c) { return c < nch ? tok_begin + c * kC : N; };
 
     StateAcc<D> st;
     VecAcc<D> vz, vp;
@@ -59,31 +72,31 @@ __global__ __launch_bounds__(kBlock, 4) void seg_state_kernel(const T* __restric
     zero_vec<D>(vz);
     zero_vec<D>(vp);
 
-    ChunkRegs<T, D> ck[2], cv[2];
-    ck[0].load(bk, tok_begin, tid);
-    cv[0].load(bv, tok_begin, tid);
-    ck[1].load(bk, tok_begin + kC < tok_end ? tok_begin + kC : N, tid);
-    cv[1].load(bv, tok_begin + kC < tok_end ? tok_begin + kC : N, tid);
-    int c0 = tok_begin;
-    // Loads past the segment are aimed at row N: out of the buffer's range, they
-    // return zeros without touching memory, and the loop stays branch free.
-    auto step = [&](ChunkRegs<T, D>& rk, ChunkRegs<T, D>& rv, int buf) {
-        const Tile<T, kC, D> tE{sm_e[buf]}, tV{sm_v[buf]};
-        stage_elu<T, D>(rk, tE, tid);
-        stage_raw<T, D>(rv, tV, tid);
-        const int nxt = c0 + 2 * kC < tok_end ? c0 + 2 * kC : N;
-        rk.load(bk, nxt, tid);
-        rv.load(bv, nxt, tid);
-        __syncthreads();
-        state_update<T, D, true, true>(st, vz, vp, tE, tV, nullptr, nullptr, lane, w);
-        c0 += kC;
-    };
-    while (true) {
-        step(ck[0], cv[0], 0);
-        if (c0 >= tok_end) break;
-        step(ck[1], cv[1], 1);
-        if (c0 >= tok_end) break;
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+        DMA::issue(bk, chunk_tok(u), ks[u], w, lane);
+        DMA::issue(bv, chunk_tok(u), vs[u], w, lane);
     }
+    for (int c0 = 0; c0 < nsteps; c0 += R) {
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int c = c0 + u;
+            // Every step from the second on refills one slot (past the segment
+            // with zero chunks that move no bytes), so exactly the refills of
+            // steps c-R+2 .. c-1 -- (R - 2) x 2 x PER_WAVE loads -- are younger
+            // than chunk c's (more at step 0, where the wait is conservative).
+            wait_vmcnt<(R - 2) * 2 * DMA::PER_WAVE>();
+            raw_barrier();
+            const int ur = (u + R - 1) % R;  // the slot step c - 1 read
+            if (c >= 1) {
+                DMA::issue(bk, chunk_tok(c - 1 + R), ks[ur], w, lane);
+                DMA::issue(bv, chunk_tok(c - 1 + R), vs[ur], w, lane);
+            }
+            state_update<T, D, true, true, true>(st, vz, vp, Tile<T, kC, D>{ks[u]}, Tile<T, kC, D>{vs[u]}, nullptr,
+                                                 nullptr, lane, w);
+        }
+    }
+    wait_vmcnt<0>();  // no direct-to-LDS load may outlive the workgroup
     float* r = rec + ((int64_t)bh * nseg + seg) * Rec<D>::kSize;
     store_state<D>(r, st, lane, w);
     store_vec<D>(r + Rec<D>::kZ, vz, lane, w);

@@ -112,6 +112,9 @@ def test_tiny_fp32_all_calls(la, oracle):
 SHAPES = [
     (1, 1, 1, 32), (1, 2, 63, 64), (2, 1, 64, 64), (1, 1, 65, 128), (2, 3, 200, 64),
     (1, 2, 257, 32), (1, 2, 300, 128), (2, 2, 1000, 64), (1, 1, 4096 + 17, 64),
+    # enough chunks per head that segments hold several chunks (about 512
+    # workgroups per launch), with ragged last segments and token tails
+    (1, 8, 64 * 130 + 17, 64), (2, 4, 64 * 80, 32), (1, 4, 64 * 200 + 5, 128),
 ]
 
 
@@ -189,6 +192,22 @@ def test_deterministic(la):
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_deterministic_multichunk_segments(la):
+    """Repeated calls at a size with several chunks per segment are bitwise equal
+    (catches ordering races in the chunk pipelines, which vary run to run)."""
+    q, k, v, do = draw(2, 8, 64 * 96 + 9, 64, torch.bfloat16, seed=6)
+    ref_o = la.la_forward_causal(q, k, v)
+    ref_n = la.la_forward_noncausal(q, k, v)
+    ref_g = la.la_backward_causal(q, k, v, do)
+    for _ in range(4):
+        o = la.la_forward_causal(q, k, v)
+        n = la.la_forward_noncausal(q, k, v)
+        g = la.la_backward_causal(q, k, v, do)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(n, ref_n)
+        assert all(torch.equal(x, y) for x, y in zip(g, ref_g))
 
 
 def test_constant_v(la):
