@@ -259,9 +259,14 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
     hipError_t e;
     if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
         return hip_fail(e, "seg_state launch");
-    if ((e = timed("total", s, [&] { return la::launch_total((int)d, rec, total, BH, L.plan.nseg, s); })) != hipSuccess)
+    // Few segments: every readout workgroup sums its head's records; many: one total per head first.
+    const bool direct = L.plan.nseg <= la::kDirectTotalMaxSegments;
+    if (!direct && (e = timed("total", s, [&] { return la::launch_total((int)d, rec, total, BH, L.plan.nseg, s); })) != hipSuccess)
         return hip_fail(e, "total launch");
-    if ((e = timed("noncausal_fwd", s, [&] { return la::launch_noncausal_fwd(idt, (int)d, q, o, total, BH, N, L.plan, s); })) != hipSuccess)
+    if ((e = timed("noncausal_fwd", s, [&] {
+             return la::launch_noncausal_fwd(idt, (int)d, q, o, direct ? rec : total, direct ? L.plan.nseg : 1, BH, N,
+                                             L.plan, s);
+         })) != hipSuccess)
         return hip_fail(e, "noncausal_fwd launch");
     return LA_OK;
 }

@@ -64,7 +64,9 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
     const Tile<T, kC, D> tQ{sm_q}, tG{sm_g};
     const Tile<T, D, D> tSt{sm_st};
 
-    const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
+    // Later segments sum more records: they are dispatched first, since a CU's
+    // older workgroup issues ahead of its younger one.
+    const int seg = nseg - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
     const int64_t hoff = (int64_t)bh * N * D;
     const uint32_t hbytes = (uint32_t)N * D * sizeof(T);

@@ -274,7 +274,9 @@ template <int D>
 __device__ __forceinline__ void add_records(const float* rec, int64_t stride, int count, StateAcc<D>& st,
                                             VecAcc<D>& va, VecAcc<D>& vb, int lane, int w) {
     using ST = StateTiles<D>;
-    constexpr int B = 4;
+    // records in flight per batch: about 192 registers' worth
+    constexpr int PER_REC = 4 * (ST::NAT * ST::NBT + 2 * ST::NVT);
+    constexpr int B = 192 / PER_REC >= 8 ? 8 : 192 / PER_REC >= 1 ? 192 / PER_REC : 1;
     for (int j0 = 0; j0 < count; j0 += B) {
         f32x4 xs[B][ST::NAT][ST::NBT], xa[B][ST::NVT], xb[B][ST::NVT];
 #pragma unroll

@@ -144,7 +144,9 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void causal_fwd_ke
     __shared__ __attribute__((aligned(16))) T sm_st[2][D * D];
     __shared__ __attribute__((aligned(16))) float s_z[2][D], s_p[2][D];
 
-    const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
+    // Later segments sum more records: they are dispatched first, since a CU's
+    // older workgroup issues ahead of its younger one.
+    const int seg = nseg - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
     const int64_t hoff = (int64_t)bh * N * D;
     const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
@@ -308,8 +310,8 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void causal_fwd_ke
 // on its own token tiles with phi(Q) in registers (no barrier in the loop).
 template <typename T, int D>
 __global__ __launch_bounds__(kBlock) void noncausal_fwd_kernel(const T* __restrict__ q, T* __restrict__ o,
-                                                               const float* __restrict__ total, int N, int cps,
-                                                               int nseg, int BH) {
+                                                               const float* __restrict__ total, int ntotal, int N,
+                                                               int cps, int nseg, int BH) {
     using M = Mma<T>;
     constexpr int KS = M::KSTEP;
     constexpr int DT = D / 16;
@@ -324,15 +326,19 @@ __global__ __launch_bounds__(kBlock) void noncausal_fwd_kernel(const T* __restri
     const GBuf bq(q + hoff, hbytes), bo(o + hoff, hbytes);
     const int tok_begin = seg * cps * kC;
     const int tok_end = min(N, tok_begin + cps * kC);
-    const float* r = total + (int64_t)bh * Rec<D>::kSize;
-
+    // The head's state: the sum of its ntotal records in order (ntotal = nseg:
+    // the segment records themselves; ntotal = 1: a precomputed total).
     {
         StateAcc<D> st;
-        load_state<D>(r, st, lane, w);
+        VecAcc<D> vz, vp;
+        zero_state<D>(st);
+        zero_vec<D>(vz);
+        zero_vec<D>(vp);
+        add_records<D>(total + (int64_t)bh * ntotal * Rec<D>::kSize, Rec<D>::kSize, ntotal, st, vz, vp, lane, w);
         publish_state<T, D>(st, tSt, lane, w);
+        store_vec<D>(s_z, vz, lane, w);
+        store_vec<D>(s_p, vp, lane, w);
     }
-    if (tid < D) s_z[tid] = r[Rec<D>::kZ + tid];
-    else if (tid < 2 * D) s_p[tid - D] = r[Rec<D>::kP + tid - D];
     const float n = (float)N;
     const int t0 = 16 * w;
     const int tl = t0 + (lane & 15);
@@ -462,15 +468,16 @@ hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const 
     return hipGetLastError();
 }
 
-hipError_t launch_noncausal_fwd(int dt, int d, const void* q, void* o, const float* total, int64_t BH, int64_t N,
-                                SegPlan p, hipStream_t s) {
+hipError_t launch_noncausal_fwd(int dt, int d, const void* q, void* o, const float* total, int ntotal, int64_t BH,
+                                int64_t N, SegPlan p, hipStream_t s) {
     const dim3 grid((unsigned)(p.nseg * BH));
     if (dt == kBF16) {
         LA_DISPATCH_D(d, hipLaunchKernelGGL((noncausal_fwd_kernel<bf16, D>), grid, dim3(kBlock), 0, s,
-                                            (const bf16*)q, (bf16*)o, total, (int)N, p.cps, p.nseg, (int)BH));
+                                            (const bf16*)q, (bf16*)o, total, ntotal, (int)N, p.cps, p.nseg, (int)BH));
     } else {
         LA_DISPATCH_D(d, hipLaunchKernelGGL((noncausal_fwd_kernel<float, D>), grid, dim3(kBlock), 0, s,
-                                            (const float*)q, (float*)o, total, (int)N, p.cps, p.nseg, (int)BH));
+                                            (const float*)q, (float*)o, total, ntotal, (int)N, p.cps, p.nseg,
+                                            (int)BH));
     }
     return hipGetLastError();
 }
