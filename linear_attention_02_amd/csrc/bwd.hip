@@ -373,9 +373,9 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_ke
 #pragma unroll
         for (int i = 0; i < NY; ++i) {
             const float x = kr.get(i);
-            const float ex = __expf(x);
-            ke[i] = to_f32(from_f32<T>(x > 0.f ? x : ex - 1.f));
-            dphik[i] = x > 0.f ? 1.f : ex;
+            const float c = expc_f(x);
+            ke[i] = to_f32(from_f32<T>(fmaxf(x, c - 1.f)));
+            dphik[i] = c;
         }
         const RowAcc<T, D> vcur = vrow;
         load_chunk(ci > 0 ? c0 - kC : N, (w + it + 1) & 3);  // past the head: zeros, no memory traffic

@@ -45,9 +45,16 @@ __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // 
 // ---- feature map phi(x) = elu(x) + 1 -------------------------------------------------
 // phi(x) = x + 1 (x > 0), exp(x) (x <= 0);  E(x) = phi(x) - 1 = elu(x);
 // phi'(x) = 1 (x > 0), exp(x) (x <= 0).
-__device__ __forceinline__ float phi_f(float x) { return x > 0.f ? x + 1.f : __expf(x); }
-__device__ __forceinline__ float elu_f(float x) { return x > 0.f ? x : __expf(x) - 1.f; }
-__device__ __forceinline__ float dphi_f(float x) { return x > 0.f ? 1.f : __expf(x); }
+// With c(x) = min(exp(x), 1) = exp(min(x, 0)), one exp whose result the hardware
+// clamps to [0, 1]: phi'(x) = c(x), and since exp(x) >= 1 + x everywhere and
+// c(x) = 1 for x > 0, phi(x) = max(x + 1, c(x)) and E(x) = max(x, c(x) - 1).
+// Each costs four VALU operations (mul, exp, add, max) and no compare or select.
+__device__ __forceinline__ float expc_f(float x) {
+    return __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(x * 1.4426950408889634f), 0.f, 1.f);
+}
+__device__ __forceinline__ float phi_f(float x) { return fmaxf(x + 1.f, expc_f(x)); }
+__device__ __forceinline__ float elu_f(float x) { return fmaxf(x, expc_f(x) - 1.f); }
+__device__ __forceinline__ float dphi_f(float x) { return expc_f(x); }
 
 // 1/x to within an ulp: hardware reciprocal refined by one Newton step.
 __device__ __forceinline__ float rcp_f(float x) {
