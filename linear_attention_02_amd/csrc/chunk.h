@@ -102,6 +102,20 @@ struct RowFrag {
         }
         return dot;
     }
+    // f[k0 / KSTEP] = phi of the held elements as operands.
+    __device__ __forceinline__ void phi_ops(typename M::frag* f) const {
+#pragma unroll
+        for (int x = 0; x < NR; ++x) {
+            const T* h = reinterpret_cast<const T*>(&r[x]);
+            if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                for (int e = 0; e < EV; ++e) f[x][e] = (T)phi_f(to_f32(h[e]));
+            } else {
+#pragma unroll
+                for (int e = 0; e < EV; ++e) f[4 * x + e] = phi_f(h[e]);
+            }
+        }
+    }
 };
 
 // One token row per lane in accumulator order: lane l holds row tok0 + (l & 15),
@@ -268,15 +282,24 @@ __device__ __forceinline__ void store_vec(float* v, const VecAcc<D>& acc, int la
     for (int x = 0; x < ST::NVT; ++x) *reinterpret_cast<f32x4*>(v + (ST::vt0(w) + x) * 16 + 4 * (lane >> 4)) = acc[x];
 }
 
+// The same vector tiles rounded to T (operand copies of a vector).
+template <typename T, int D>
+__device__ __forceinline__ void store_vec_as(T* v, const VecAcc<D>& acc, int lane, int w) {
+    using ST = StateTiles<D>;
+    if (!ST::owns_vec(w) || (lane & 15) != 0) return;
+#pragma unroll
+    for (int x = 0; x < ST::NVT; ++x) store4(v + (ST::vt0(w) + x) * 16 + 4 * (lane >> 4), acc[x]);
+}
+
 // Add the segment records rec[j * stride] for j = 0 .. count-1, in that order,
 // to the wave's state tiles and vector tiles (fixed order: bitwise reproducible).
-template <int D>
+// kRegs: registers the records in flight may take (at most 8 records per batch).
+template <int D, int kRegs = 192>
 __device__ __forceinline__ void add_records(const float* rec, int64_t stride, int count, StateAcc<D>& st,
                                             VecAcc<D>& va, VecAcc<D>& vb, int lane, int w) {
     using ST = StateTiles<D>;
-    // records in flight per batch: about 192 registers' worth
     constexpr int PER_REC = 4 * (ST::NAT * ST::NBT + 2 * ST::NVT);
-    constexpr int B = 192 / PER_REC >= 8 ? 8 : 192 / PER_REC >= 1 ? 192 / PER_REC : 1;
+    constexpr int B = kRegs / PER_REC >= 8 ? 8 : kRegs / PER_REC >= 1 ? kRegs / PER_REC : 1;
     for (int j0 = 0; j0 < count; j0 += B) {
         f32x4 xs[B][ST::NAT][ST::NBT], xa[B][ST::NVT], xb[B][ST::NVT];
 #pragma unroll

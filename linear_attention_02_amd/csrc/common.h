@@ -249,6 +249,10 @@ struct Mma<bf16> {
         for (int e = 0; e < 8; ++e) f[e] = (bf16)1.f;
         return f;
     }
+    // Every operand row is the vector v[k] (bf16 in LDS, read as it is stored).
+    __device__ __forceinline__ static frag vec_op(const bf16* v, int k0, int lane) {
+        return *reinterpret_cast<const frag*>(v + k0 + 8 * (lane >> 4));
+    }
     static constexpr bool kSplitSplat = true;
     __device__ __forceinline__ static f32x4 mma(frag x, frag y, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
@@ -291,6 +295,7 @@ struct Mma<float> {
         lo = 0.f;
     }
     __device__ __forceinline__ static frag ones() { return 1.f; }
+    __device__ __forceinline__ static frag vec_op(const float* v, int k0, int lane) { return v[kap(k0, lane)]; }
     static constexpr bool kSplitSplat = false;
     __device__ __forceinline__ static f32x4 mma(frag x, frag y, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, c, 0, 0, 0);
@@ -298,6 +303,19 @@ struct Mma<float> {
 };
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ f32x4 splat4(float x) { return f32x4{x, x, x, x}; }
+
+// 0.f that the compiler cannot see through: selecting between a value and it
+// keeps the select on the fp32 value (a select against a literal 0 is moved
+// past the later bf16 rounding, which then costs a separate pack).
+__device__ __forceinline__ float opaque_zero() {
+    uint32_t z;
+    asm("s_mov_b32 %0, 0" : "=s"(z));
+    return __uint_as_float(z);
+}
+// Lane l of the wavefront reads bit l of the uniform mask m (a select on it
+// needs no compare).
+__device__ __forceinline__ bool lane_bit(uint64_t m) { return __builtin_amdgcn_inverse_ballot_w64(m); }
 
 // Write an accumulator tile transposed: element (i, j) goes to dst[col0 + j][row0 + i];
 // each lane writes 4 consecutive elements of one row (8 bytes in bf16, 16 in fp32).

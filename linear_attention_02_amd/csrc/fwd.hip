@@ -14,18 +14,18 @@
 //   num_t = q_sum_t P + phi(Q_t) S_E + sum_{s<=t in chunk} A_ts V_s,
 //   den_t = q_sum_t n + phi(Q_t) . z_E + sum_{s<=t in chunk} A_ts.
 //
-// Work decomposition.  One workgroup (4 wavefronts) per (segment of `cps`
-// chunks, head), numbered segment-major so that with the round-robin
+// Work decomposition.  One workgroup (4 wavefronts; 8 for causal_fwd, in two
+// roles) per (segment of `cps` chunks, head), numbered segment-major so that with the round-robin
 // placement of workgroups on the 8 XCDs all segments of a head share an XCD
 // (and its L2) whenever the head count is a multiple of 8.  seg_state reduces
 // each segment's keys to (S_E, z_E, P); causal_fwd starts a segment from the
 // sum of the records before it, added in segment order (fixed order, so the
 // results are bitwise reproducible), and walks its chunks.  The non-causal
-// forward is seg_state + per-head totals (scan) + noncausal_fwd.
+// forward is seg_state + per-head totals (total, beyond two segments) + noncausal_fwd.
 //
 // Data layout.  Inputs/outputs [BH][N][d] row-major in HBM.  Per chunk the
 // workgroup stages E(K) and V row-major in LDS (bf16 for bf16 inputs, fp32 for
-// fp32 inputs, double-buffered so one barrier per chunk suffices); each
+// fp32 inputs, double-buffered so one barrier per chunk suffices); each output
 // wavefront keeps phi(Q) of its own 16 tokens in registers in MFMA operand
 // layout, and the in-chunk weights A stay in the accumulators that produce them
 // and feed the A V product directly.  S_E stays in fp32 MFMA accumulators
@@ -131,177 +131,224 @@ __global__ __launch_bounds__(kBlock) void total_kernel(const float* __restrict__
 // causal_fwd: per (segment, head), walk the segment's chunks from the state
 // carried in by the segments before it.  The last segment of a head also
 // writes the final state S = 1 P^T + S_E, z = N 1 + z_E when asked to.
+//
+// Eight wavefronts in two roles meet at one barrier per chunk.  While the
+// output waves (0-3) compute chunk c's outputs from the state S(c) and the
+// chunk's staged E(K), V, the state waves (4-7) stage chunk c+1 into the other
+// buffers and form S(c+1) = S(c) + E(K_c)^T V_c, z_E and P from the same tiles.
+// The two halves of the per-chunk work run side by side, and each role keeps
+// only its own registers (more resident waves per SIMD).
+//
+// Per chunk and output wavefront (16 tokens t), all products on MFMA:
+//   q_sum_t                    = ones . phi(Q_t)
+//   A_ts = q_sum_t + phi(Q_t).E(K_s), s <= t, 32 keys per block, masked by lane bits
+//   num^T[b][t] = sum_s V[s][b] A_ts + sum_a S_E^T[b][a] phi(Q_t)[a]     (tiles 0 .. D/16-1)
+//   den_t - n q_sum_t = sum_s A_ts + sum_a z_E[a] phi(Q_t)[a]           (one more tile: an
+//                      all-ones value column in the first product, z_E rows in the second)
+// Chunk loops are unrolled by two so that each chunk's LDS buffer is a
+// compile-time choice (its offsets fold into the instructions).
 template <typename T, int D>
-__global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void causal_fwd_kernel(
+struct CausalFwdCfg {
+    // resident waves per SIMD the register allocation must allow (two workgroups per CU where d <= 64)
+    static constexpr int kWavesPerSimd = D <= 64 ? 4 : 2;
+    // registers the state waves give to segment records in flight
+    static constexpr int kRecordRegs = D <= 64 ? 48 : 128;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) void causal_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ o,
     float* __restrict__ den_out, const float* __restrict__ rec, float* __restrict__ S_out, float* __restrict__ z_out,
     int N, int cps, int nseg, int BH) {
     using M = Mma<T>;
+    using F = typename M::frag;
     constexpr int KS = M::KSTEP;
     constexpr int DT = D / 16;
     __shared__ __attribute__((aligned(16))) T sm_e[2][kC * D];
     __shared__ __attribute__((aligned(16))) T sm_v[2][kC * D];
     __shared__ __attribute__((aligned(16))) T sm_st[2][D * D];
-    __shared__ __attribute__((aligned(16))) float s_z[2][D], s_p[2][D];
+    __shared__ __attribute__((aligned(16))) T s_zb[2][D];
+    __shared__ __attribute__((aligned(16))) float s_p[2][D];
 
     // Later segments sum more records: they are dispatched first, since a CU's
     // older workgroup issues ahead of its younger one.
     const int seg = nseg - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
-    const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
+    const int wv = wave_id(), lane = threadIdx.x & 63, g = lane >> 4;
+    const int w = wv & 3;                     // wave index inside its role
+    const int rtid = (int)threadIdx.x & (kBlock - 1);  // thread index inside its role
     const int64_t hoff = (int64_t)bh * N * D;
     const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
-    const GBuf bq(q + hoff, hbytes), bk(k + hoff, hbytes), bv(v + hoff, hbytes), bo(o + hoff, hbytes);
-    const GBuf bden(den_out != nullptr ? den_out + (int64_t)bh * N : nullptr, den_out != nullptr ? (uint32_t)N * 4 : 0u);
     const int tok_begin = seg * cps * kC;
     const int tok_end = min(N, tok_begin + cps * kC);
 
-    // Starting state: the records of the segments before this one, in order.
-    StateAcc<D> st;
-    VecAcc<D> vz, vp;
-    zero_state<D>(st);
-    zero_vec<D>(vz);
-    zero_vec<D>(vp);
-    add_records<D>(rec + (int64_t)bh * nseg * Rec<D>::kSize, Rec<D>::kSize, seg, st, vz, vp, lane, w);
-    float n = (float)tok_begin;
+    if (wv >= 4) {
+        // ---- state waves -------------------------------------------------------------
+        const GBuf bk(k + hoff, hbytes), bv(v + hoff, hbytes);
+        // The first chunk's loads are in flight while the starting state is summed:
+        // the records of the segments before this one, in order.
+        ChunkRegs<T, D> ck, cv;
+        ck.load(bk, tok_begin, rtid);
+        cv.load(bv, tok_begin, rtid);
+        StateAcc<D> st;
+        VecAcc<D> vz, vp;
+        zero_state<D>(st);
+        zero_vec<D>(vz);
+        zero_vec<D>(vp);
+        add_records<D, CausalFwdCfg<T, D>::kRecordRegs>(rec + (int64_t)bh * nseg * Rec<D>::kSize, Rec<D>::kSize, seg,
+                                                       st, vz, vp, lane, w);
+        publish_state<T, D>(st, Tile<T, D, D>{sm_st[0]}, lane, w);
+        store_vec_as<T, D>(s_zb[0], vz, lane, w);
+        store_vec<D>(s_p[0], vp, lane, w);
+        stage_elu<T, D>(ck, Tile<T, kC, D>{sm_e[0]}, rtid);
+        stage_raw<T, D>(cv, Tile<T, kC, D>{sm_v[0]}, rtid);
+        // Loads past the segment are aimed at row N: out of the buffer's range, they
+        // return zeros without touching memory, and the loop stays branch free.
+        ck.load(bk, tok_begin + kC < tok_end ? tok_begin + kC : N, rtid);
+        cv.load(bv, tok_begin + kC < tok_end ? tok_begin + kC : N, rtid);
+        __syncthreads();
 
+        auto chunk = [&](auto bsel, int c0) {
+            constexpr int B = decltype(bsel)::value;
+            // Stage the next chunk into the other buffer (idle after the last chunk),
+            // then S_E += E(K)^T V, z_E += colsum E(K), P += colsum V, published
+            // for the next chunk.
+            stage_elu<T, D>(ck, Tile<T, kC, D>{sm_e[B ^ 1]}, rtid);
+            stage_raw<T, D>(cv, Tile<T, kC, D>{sm_v[B ^ 1]}, rtid);
+            ck.load(bk, c0 + 2 * kC < tok_end ? c0 + 2 * kC : N, rtid);
+            cv.load(bv, c0 + 2 * kC < tok_end ? c0 + 2 * kC : N, rtid);
+            state_update<T, D, true, true>(st, vz, vp, Tile<T, kC, D>{sm_e[B]}, Tile<T, kC, D>{sm_v[B]}, nullptr,
+                                           nullptr, lane, w);
+            publish_state<T, D>(st, Tile<T, D, D>{sm_st[B ^ 1]}, lane, w);
+            store_vec_as<T, D>(s_zb[B ^ 1], vz, lane, w);
+            store_vec<D>(s_p[B ^ 1], vp, lane, w);
+            __syncthreads();
+        };
+        for (int c0 = tok_begin; c0 < tok_end; c0 += 2 * kC) {
+            chunk(std::integral_constant<int, 0>{}, c0);
+            if (c0 + kC >= tok_end) break;
+            chunk(std::integral_constant<int, 1>{}, c0 + kC);
+        }
+
+        if (seg == nseg - 1) {
+            // P of the whole head was published into s_p[nch & 1] before the last barrier.
+            using ST = StateTiles<D>;
+            const int nch = (tok_end - tok_begin + kC - 1) / kC;
+            if (S_out != nullptr) {
+                const float* sp = s_p[nch & 1];
+                float* s = S_out + (int64_t)bh * D * D;
+#pragma unroll
+                for (int ia = 0; ia < ST::NAT; ++ia)
+#pragma unroll
+                    for (int ib = 0; ib < ST::NBT; ++ib) {
+                        const int b = (ST::bt0(w) + ib) * 16 + (lane & 15);
+                        const float pb = sp[b];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            s[(int64_t)((ST::at0(w) + ia) * 16 + 4 * g + e) * D + b] = pb + st[ia][ib][e];
+                    }
+            }
+            if (z_out != nullptr && ST::owns_vec(w) && (lane & 15) == 0) {
+#pragma unroll
+                for (int x = 0; x < ST::NVT; ++x)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        z_out[(int64_t)bh * D + (ST::vt0(w) + x) * 16 + 4 * g + e] = (float)N + vz[x][e];
+            }
+        }
+        return;
+    }
+
+    // ---- output waves ------------------------------------------------------------------
+    const GBuf bq(q + hoff, hbytes), bo(o + hoff, hbytes);
+    const GBuf bden(den_out != nullptr ? den_out + (int64_t)bh * N : nullptr, den_out != nullptr ? (uint32_t)N * 4 : 0u);
+    float n = (float)tok_begin;
     // Wavefront w takes token tile tt = (w + ci) mod 4 of chunk ci: the causal
     // mask leaves tt + 1 key tiles, and the rotation spreads that work evenly
     // over the SIMDs.
-    ChunkRegs<T, D> ck, cv;
     RowFrag<T, D> qr;
-    ck.load(bk, tok_begin, tid);
-    cv.load(bv, tok_begin, tid);
     qr.load(bq, tok_begin + 16 * w, lane);
-    // Stage the first chunk and publish the starting state; later chunks are
-    // staged into the other buffer while the current one finishes.
-    publish_state<T, D>(st, Tile<T, D, D>{sm_st[0]}, lane, w);
-    store_vec<D>(s_z[0], vz, lane, w);
-    store_vec<D>(s_p[0], vp, lane, w);
-    stage_elu<T, D>(ck, Tile<T, kC, D>{sm_e[0]}, tid);
-    stage_raw<T, D>(cv, Tile<T, kC, D>{sm_v[0]}, tid);
-    // Loads past the segment are aimed at row N: out of the buffer's range, they
-    // return zeros without touching memory, and the loop stays branch free.
-    ck.load(bk, tok_begin + kC < tok_end ? tok_begin + kC : N, tid);
-    cv.load(bv, tok_begin + kC < tok_end ? tok_begin + kC : N, tid);
+    // Key s = 16 j + 4 g + e of tile j is visible to token t = 16 tt + (lane & 15)
+    // iff j < tt, or j == tt and bit lane of diag[e] is set.
+    uint64_t diag[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) diag[e] = __ballot(4 * g + e <= (lane & 15));
+    const float zero = opaque_zero();
+    const F one = M::ones();
     __syncthreads();
 
-    int buf = 0, ci = 0;
-    for (int c0 = tok_begin; c0 < tok_end; c0 += kC, buf ^= 1, ++ci) {
-        const Tile<T, kC, D> tE{sm_e[buf]}, tV{sm_v[buf]};
-        const Tile<T, D, D> tSt{sm_st[buf]};
-        const float* sz = s_z[buf];
-        const float* sp = s_p[buf];
+    auto chunk = [&](auto bsel, int c0, int ci) {
+        constexpr int B = decltype(bsel)::value;
+        const Tile<T, kC, D> tE{sm_e[B]}, tV{sm_v[B]};
+        const Tile<T, D, D> tSt{sm_st[B]};
         const bool more = c0 + kC < tok_end;
         const int tt = (w + ci) & 3;
         const int tl = 16 * tt + (lane & 15);  // this lane's token (accumulator column)
 
-        // phi(Q) of this wave's tokens as operands, and phi(Q_t) . z_E.
-        typename M::frag qf[D / KS];
-        const float zdot = sum_over_groups(qr.phi_ops(qf, sz, lane));
+        F qf[D / KS];
+        qr.phi_ops(qf);
         qr.load(bq, more ? c0 + kC + 16 * ((w + ci + 1) & 3) : N, lane);
+        f32x4 acc_q = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < D; k0 += KS) acc_q = M::mma(one, qf[k0 / KS], acc_q);
+        const float qs_t = acc_q[0];
 
-        // In-chunk weights A_ts = q_sum_t + phi(Q_t).E(K_s) for s <= t (accumulator [s][t]).
-        float qs_t, den = 0.f;
-        f32x4 acc_a[4];
-        {
-            const typename M::frag one = M::ones();
-            f32x4 acc_q = zero4();
+        f32x4 acc[DT + 1];
 #pragma unroll
-            for (int k0 = 0; k0 < D; k0 += KS) acc_q = M::mma(one, qf[k0 / KS], acc_q);
+        for (int m = 0; m <= DT; ++m) acc[m] = zero4();
+        // In-chunk part, 32 keys (two tiles) per block; blocks past the diagonal are skipped.
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                acc_a[j] = zero4();
-                if (j <= tt) {
+        for (int kb = 0; kb < kC / 32; ++kb) {
+            if (2 * kb <= tt) {
+                f32x4 a[2];
 #pragma unroll
-                    for (int k0 = 0; k0 < D; k0 += KS) acc_a[j] = M::mma(M::ld(tE, 16 * j, k0, lane), qf[k0 / KS], acc_a[j]);
+                for (int h = 0; h < 2; ++h) {
+                    const int j = 2 * kb + h;
+                    a[h] = splat4(qs_t);
+#pragma unroll
+                    for (int k0 = 0; k0 < D; k0 += KS) a[h] = M::mma(M::ld(tE, 16 * j, k0, lane), qf[k0 / KS], a[h]);
+                    // all ones when j < tt (resp. j <= tt), from sign shifts: scalar only
+                    const uint64_t lt = ~(uint64_t)((int64_t)(tt - j - 1) >> 63);
+                    const uint64_t le = ~(uint64_t)((int64_t)(tt - j) >> 63);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a[h][e] = lane_bit(lt | (le & diag[e])) ? a[h][e] : zero;
                 }
-            }
-            qs_t = acc_q[0];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (j < tt) {
+                for (int kk = 0; kk < 32; kk += KS) {
+                    const F yf = M::acc_op(a, kk);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        acc_a[j][e] += qs_t;
-                        den += acc_a[j][e];
-                    }
-                } else if (j == tt) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float a = (4 * g + e) <= (lane & 15) ? qs_t + acc_a[j][e] : 0.f;
-                        acc_a[j][e] = a;
-                        den += a;
-                    }
+                    for (int m = 0; m < DT; ++m) acc[m] = M::mma(M::ld_tr_acc(tV, 32 * kb + kk, 16 * m, lane), yf, acc[m]);
+                    acc[DT] = M::mma(one, yf, acc[DT]);
                 }
             }
         }
-        den = sum_over_groups(den) + n * qs_t + zdot;
-        const float inv = rcp_f(den);
-
-        // num^T[b][t] = sum_s V[s][b] A[t][s] + sum_a S_E^T[b][a] phi(Q)[t][a]
-        f32x4 acc[DT];
-#pragma unroll
-        for (int m = 0; m < DT; ++m) acc[m] = zero4();
-#pragma unroll
-        for (int k0 = 0; k0 < kC; k0 += KS) {
-            if (k0 / 16 <= tt) {
-                const typename M::frag yf = M::acc_op(acc_a, k0);
-#pragma unroll
-                for (int m = 0; m < DT; ++m) acc[m] = M::mma(M::ld_tr_acc(tV, k0, 16 * m, lane), yf, acc[m]);
-            }
-        }
+        // State part: S_E^T phi(Q_t) and z_E . phi(Q_t).
 #pragma unroll
         for (int k0 = 0; k0 < D; k0 += KS) {
-            const typename M::frag yf = qf[k0 / KS];
+            const F yf = qf[k0 / KS];
 #pragma unroll
             for (int m = 0; m < DT; ++m) acc[m] = M::mma(M::ld(tSt, 16 * m, k0, lane), yf, acc[m]);
+            acc[DT] = M::mma(M::vec_op(s_zb[B], k0, lane), yf, acc[DT]);
         }
+        const float den = acc[DT][0] + n * qs_t;
+        const float inv = rcp_f(den);
         const int tok = c0 + tl;  // rows past the head are dropped by the buffer range
 #pragma unroll
         for (int m = 0; m < DT; ++m) {
             const int b0 = 16 * m + 4 * g;
-            const f32x4 p4 = lds4(&sp[b0]);
+            const f32x4 p4 = lds4(&s_p[B][b0]);
             f32x4 x;
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = (acc[m][e] + qs_t * p4[e]) * inv;
             gstore4<T>(bo, (uint32_t)(tok * D + b0), x);
         }
         if (den_out != nullptr && g == 0) bden.st4f((uint32_t)tok * 4, den);
-
-        // Stage the next chunk into the other buffer (idle after the last chunk),
-        // then the state update: S_E += E(K)^T V, z_E += colsum E(K), P += colsum V,
-        // published for the next chunk.
-        stage_elu<T, D>(ck, Tile<T, kC, D>{sm_e[buf ^ 1]}, tid);
-        stage_raw<T, D>(cv, Tile<T, kC, D>{sm_v[buf ^ 1]}, tid);
-        ck.load(bk, c0 + 2 * kC < tok_end ? c0 + 2 * kC : N, tid);
-        cv.load(bv, c0 + 2 * kC < tok_end ? c0 + 2 * kC : N, tid);
-        state_update<T, D, true, true>(st, vz, vp, tE, tV, nullptr, nullptr, lane, w);
-        publish_state<T, D>(st, Tile<T, D, D>{sm_st[buf ^ 1]}, lane, w);
-        store_vec<D>(s_z[buf ^ 1], vz, lane, w);
-        store_vec<D>(s_p[buf ^ 1], vp, lane, w);
         n += (float)min(kC, N - c0);
         __syncthreads();
-    }
-
-    if (seg == nseg - 1 && (S_out != nullptr || z_out != nullptr)) {
-        // The buffer not read by the last chunk is free: every wave is past the last barrier.
-        store_vec<D>(s_z[buf], vz, lane, w);
-        store_vec<D>(s_p[buf], vp, lane, w);
-        __syncthreads();
-        using ST = StateTiles<D>;
-        if (S_out != nullptr) {
-            float* s = S_out + (int64_t)bh * D * D;
-#pragma unroll
-            for (int ia = 0; ia < ST::NAT; ++ia)
-#pragma unroll
-                for (int ib = 0; ib < ST::NBT; ++ib) {
-                    const int b = (ST::bt0(w) + ib) * 16 + (lane & 15);
-                    const float pb = s_p[buf][b];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) s[(int64_t)((ST::at0(w) + ia) * 16 + 4 * g + e) * D + b] = pb + st[ia][ib][e];
-                }
-        }
-        if (z_out != nullptr && tid < D) z_out[(int64_t)bh * D + tid] = (float)N + s_z[buf][tid];
+    };
+    for (int c0 = tok_begin, ci = 0; c0 < tok_end; c0 += 2 * kC, ci += 2) {
+        chunk(std::integral_constant<int, 0>{}, c0, ci);
+        if (c0 + kC >= tok_end) break;
+        chunk(std::integral_constant<int, 1>{}, c0 + kC, ci + 1);
     }
 }
 
@@ -448,7 +495,7 @@ hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const 
                              hipStream_t s) {
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_CFWD(TT, DD)                                                                                          \
-    hipLaunchKernelGGL((causal_fwd_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k,       \
+    hipLaunchKernelGGL((causal_fwd_kernel<TT, DD>), grid, dim3(2 * kBlock), 0, s, (const TT*)q, (const TT*)k,       \
                        (const TT*)v, (TT*)o, den_out, rec, S_out, z_out, (int)N, p.cps, p.nseg, (int)BH)
     if (dt == kBF16) {
         switch (d) {
