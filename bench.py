@@ -8,8 +8,14 @@ d=64, bf16 inputs ~ N(0,1)/sqrt(d), chunk 64.  W untimed warmup steps, then K
 steps timed back to back between two device synchronisations.  Inputs are
 resident in HBM before the timed region; the step rotates over several input
 sets whose total exceeds the 256 MB last-level cache, so each step starts with
-its inputs in HBM, not in cache.  The per-kernel event times come from a second
-run of the same K steps right after the timed one.
+its inputs in HBM, not in cache.  The defaults (300 warmup steps, 1000 timed)
+measure the steady state: the first few milliseconds of work after start-up run
+while the GPU clock ramps up and read about 5% slow.  Launches are eager; with
+--graph each input set's step is captured once into a HIP graph and the timed
+region replays the graphs (every graph's replays are first checked bitwise
+against eager steps; on this stack replays measure a few microseconds slower
+per step).  The per-kernel event times come from a second, eager run of the
+same K steps right after the timed one.
 
 The JSON line also carries
   * roofline    : the dominant kernel's algorithmic bytes per launch over its
@@ -30,7 +36,7 @@ known size (`--copy-probe`).  They are read from profiles/<kernel>_traffic.txt,
 which records a hash of the kernel sources; when the sources have changed since
 the counters were taken the field is null.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-calls] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-calls] [--no-cpu] [--graph]
        python bench.py --copy-probe      (a 256 MiB device copy, for counter calibration)
 """
 from __future__ import annotations
@@ -53,10 +59,11 @@ LLC_BYTES = 256 * 2**20
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-calls", action="store_true", help="skip the other calls")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--graph", action="store_true", help="time HIP-graph replays of the steps instead of eager launches")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe", action="store_true", help="only run 5 device copies of 256 MiB")
     return ap.parse_args()
@@ -141,14 +148,18 @@ def sequence_roofline(stats, B, H, N, d, steps):
                   "alg_bytes_per_launch": alg}
 
 
-def time_steps(fn, nsets, warmup, steps, la, torch):
-    """Wall time of `steps` back-to-back steps, then per-kernel event times over a second run of them."""
+def time_steps(fn, nsets, warmup, steps, la, torch, timed_fn=None):
+    """Wall time of `steps` back-to-back steps, then per-kernel event times over a second run of them.
+
+    timed_fn (default fn) is what the timed region runs per step, e.g. the replay of
+    a captured graph of fn; the per-kernel event run always calls fn itself."""
+    run = timed_fn or fn
     for i in range(warmup):
-        fn(i % nsets)
+        run(i % nsets)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        fn(i % nsets)
+        run(i % nsets)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     la.profile_enable(True)
@@ -158,6 +169,40 @@ def time_steps(fn, nsets, warmup, steps, la, torch):
     stats = kernel_stats(la.profile_entries())
     la.profile_enable(False)
     return dt, stats
+
+
+def capture_graphs(step, nsets, outputs, torch):
+    """One HIP graph per input set of step(i) (all its kernel launches), or None.
+
+    Every graph is replayed twice, with the eager step of another set and a
+    synchronisation between the replays, and each replay's outputs must equal
+    the eager step's outputs bitwise (the kernels are deterministic); otherwise
+    the bench keeps eager launches."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(nsets):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(nsets):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(nsets):
+        step(i)
+        ref = [t.clone() for t in outputs]
+        for _ in range(2):
+            step((i + 1) % nsets)
+            torch.cuda.synchronize()
+            graphs[i].replay()
+            torch.cuda.synchronize()
+            if not all(torch.equal(a, b) for a, b in zip(outputs, ref)):
+                return None
+    return graphs
 
 
 def bench_mid(args, la, inp, torch):
@@ -177,7 +222,9 @@ def bench_mid(args, la, inp, torch):
         la.la_forward_causal(q, k, v, out=o, workspace=wsf, saved_state=saved)
         la.la_backward_causal(q, k, v, do, out=grads, workspace=wsb, saved_state=saved)
 
-    dt, stats = time_steps(step, nsets, args.warmup, args.steps, la, torch)
+    graphs = capture_graphs(step, nsets, (o,) + grads, torch) if args.graph else None
+    replay = None if graphs is None else (lambda i: graphs[i].replay())
+    dt, stats = time_steps(step, nsets, args.warmup, args.steps, la, torch, timed_fn=replay)
     T = B * H * N
     step_s = dt / args.steps
     step_bytes = 11 * unit_bytes(B, H, N, d)
@@ -194,6 +241,7 @@ def bench_mid(args, la, inp, torch):
                           "mfma_frac": round(flops / step_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},
         "kernels_us": {k: round(t / n * 1e3, 2) for k, (n, t) in sorted(stats.items())},
         "input_sets": nsets,
+        "launch": "hip_graph" if graphs is not None else "eager",
     }, sets[0]
 
 
@@ -214,7 +262,7 @@ def bench_calls(args, la, inp, torch, mid_set):
     ws = torch.empty(la.workspace_size(la.LA_OP_FWD_NONCAUSAL, w.B, w.H, w.N, w.d, w.dtype), dtype=torch.uint8,
                      device="cuda")
     calls["mid_noncausal_fwd"] = bench_call(
-        "noncausal", lambda i: la.la_forward_noncausal(q, k, v, out=o, workspace=ws), 5, 20, w.B * w.N,
+        "noncausal", lambda i: la.la_forward_noncausal(q, k, v, out=o, workspace=ws), 100, 400, w.B * w.N,
         4 * unit_bytes(w.B, w.H, w.N, w.d), la, torch)
     del o, ws
 
@@ -337,7 +385,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "causal linear attention fwd+bwd, B4 H16 N4096 d64, bf16 in / fp32 accumulate, "
                                "phi = elu+1, chunk 64", "global_batch": 4, "seq_len": 4096, "heads": 16,
-                   "head_dim": 64, "parallelism": "single GPU"},
+                   "head_dim": 64, "parallelism": "single GPU", "launch": res["launch"]},
         "roofline": res["roofline"],
         "step_roofline": res["step_roofline"],
         "kernels_us": res["kernels_us"],
