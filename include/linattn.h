@@ -137,8 +137,8 @@ const char* la_version(void);
  * library creates once with hipEventCreate and reuses (no device memory).
  * la_profile_count() is the number of launches recorded since; entry i
  * synchronises on its stop event and returns the kernel's name ("seg_state",
- * "total", "causal_fwd", "noncausal_fwd", "bwd_prefix", "bwd_suffix", "decode",
- * "fill_zero") and its duration in milliseconds. */
+ * "total", "scan", "causal_fwd", "noncausal_fwd", "bwd_prefix", "rscan",
+ * "bwd_suffix", "decode", "fill_zero") and its duration in milliseconds. */
 la_status la_profile_enable(int on);
 int la_profile_count(void);
 la_status la_profile_entry(int i, const char** name, float* ms);

@@ -315,6 +315,8 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* o
     const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
     if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
         return hip_fail(e, "seg_state launch");
+    if (L.plan.scan && (e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, BH, L.plan.nseg, 1, s); })) != hipSuccess)
+        return hip_fail(e, "scan launch");
     if ((e = timed("causal_fwd", s, [&] {
              return la::launch_causal_fwd(idt, (int)d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, L.plan, s);
          })) != hipSuccess)
@@ -359,10 +361,14 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
     if (saved_state == nullptr) {
         if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
             return hip_fail(e, "seg_state launch");
+        if (L.plan.scan && (e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, BH, L.plan.nseg, 1, s); })) != hipSuccess)
+            return hip_fail(e, "scan launch");
     }
     if ((e = timed("bwd_prefix", s, [&] { return la::launch_bwd_prefix(idt, (int)d, q, k, v, dout, dq, rowstat, rrec, rec, BH, N, L.plan, s); })) !=
         hipSuccess)
         return hip_fail(e, "bwd_prefix launch");
+    if (L.plan.scan && (e = timed("rscan", s, [&] { return la::launch_scan((int)d, rrec, BH, L.plan.nseg, -1, s); })) != hipSuccess)
+        return hip_fail(e, "rscan launch");
     if ((e = timed("bwd_suffix", s, [&] { return la::launch_bwd_suffix(idt, (int)d, q, k, v, dout, dk, dv, rowstat, rrec, BH, N, L.plan, s); })) !=
         hipSuccess)
         return hip_fail(e, "bwd_suffix launch");

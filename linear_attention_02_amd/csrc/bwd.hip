@@ -47,7 +47,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dq, float2* __restrict__ rowstat, float* __restrict__ rrec, const float* __restrict__ rec, int N,
-    int cps, int nseg, int BH) {
+    int cps, int nseg, int BH, int prefixed) {
     using M = Mma<T>;
     constexpr int KS = M::KSTEP;
     constexpr int DT = D / 16;
@@ -76,13 +76,11 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
     const int tok_end = min(N, tok_begin + cps * kC);
 
     // Prefix state (S_E, z_E, P) at the start of the segment: the records of the
-    // segments before it, in order; segment aggregates from zero.
+    // segments before it, summed in order; segment aggregates from zero.
     StateAcc<D> stS, stR;
     VecAcc<D> vz, vp, vr;
-    zero_state<D>(stS);
-    zero_vec<D>(vz);
-    zero_vec<D>(vp);
-    add_records<D>(rec + (int64_t)bh * nseg * Rec<D>::kSize, Rec<D>::kSize, seg, stS, vz, vp, lane, w);
+    carried_state<D>(rec + (int64_t)bh * nseg * Rec<D>::kSize, Rec<D>::kSize, seg, prefixed != 0, stS, vz, vp, lane,
+                     w);
     zero_state<D>(stR);
     zero_vec<D>(vr);
     float n = (float)tok_begin;
@@ -300,7 +298,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dk, T* __restrict__ dv, const float2* __restrict__ rowstat, const float* __restrict__ rrec, int N,
-    int cps, int nseg, int BH) {
+    int cps, int nseg, int BH, int prefixed) {
     using M = Mma<T>;
     using CR = ChunkRegs<T, D>;
     constexpr int KS = M::KSTEP;
@@ -324,11 +322,8 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_ke
     // Suffix state (R, r): the records of the segments after this one, last segment first.
     StateAcc<D> stR;
     VecAcc<D> vr, vunused;
-    zero_state<D>(stR);
-    zero_vec<D>(vr);
-    zero_vec<D>(vunused);
-    add_records<D>(rrec + ((int64_t)bh * nseg + nseg - 1) * Rec<D>::kSize, -(int64_t)Rec<D>::kSize, nseg - 1 - seg,
-                   stR, vr, vunused, lane, w);
+    carried_state<D>(rrec + ((int64_t)bh * nseg + nseg - 1) * Rec<D>::kSize, -(int64_t)Rec<D>::kSize, nseg - 1 - seg,
+                     prefixed != 0, stR, vr, vunused, lane, w);
 
     CR cq, cdo;
     RowAcc<T, D> kr, vrow;
@@ -480,7 +475,8 @@ hipError_t launch_bwd_prefix(int dt, int d, const void* q, const void* k, const 
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_BWDP(TT, DD)                                                                                           \
     hipLaunchKernelGGL((bwd_prefix_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k,        \
-                       (const TT*)v, (const TT*)dout, (TT*)dq, (float2*)rowstat, rrec, rec, (int)N, p.cps, p.nseg, (int)BH)
+                       (const TT*)v, (const TT*)dout, (TT*)dq, (float2*)rowstat, rrec, rec, (int)N, p.cps, p.nseg, (int)BH, \
+                       (int)p.scan)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_BWDP(bf16, 32); break;
@@ -506,7 +502,7 @@ hipError_t launch_bwd_suffix(int dt, int d, const void* q, const void* k, const 
 #define LA_BWDS(TT, DD)                                                                                           \
     hipLaunchKernelGGL((bwd_suffix_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k,        \
                        (const TT*)v, (const TT*)dout, (TT*)dk, (TT*)dv, (const float2*)rowstat, rrec, (int)N, p.cps, \
-                       p.nseg, (int)BH)
+                       p.nseg, (int)BH, (int)p.scan)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_BWDS(bf16, 32); break;

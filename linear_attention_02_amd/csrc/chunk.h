@@ -329,6 +329,27 @@ __device__ __forceinline__ void add_records(const float* rec, int64_t stride, in
 }
 
 // Rounded copy of the state into LDS as X^T[b][a].
+// The state carried into a segment from records[0 .. count-1] at first + j * stride.
+// prefixed: a scan has already replaced each record by the running sum of the
+// ones before it (same order), so the record at first + count * stride is that
+// sum; otherwise the records are added here.  Either way the result is bitwise
+// the same.
+template <int D, int kRegs = 192>
+__device__ __forceinline__ void carried_state(const float* first, int64_t stride, int count, bool prefixed,
+                                              StateAcc<D>& st, VecAcc<D>& va, VecAcc<D>& vb, int lane, int w) {
+    if (prefixed) {
+        const float* r = first + (int64_t)count * stride;
+        load_state<D>(r, st, lane, w);
+        load_vec<D>(r + Rec<D>::kZ, va, lane, w);
+        load_vec<D>(r + Rec<D>::kP, vb, lane, w);
+    } else {
+        zero_state<D>(st);
+        zero_vec<D>(va);
+        zero_vec<D>(vb);
+        add_records<D, kRegs>(first, stride, count, st, va, vb, lane, w);
+    }
+}
+
 template <typename T, int D>
 __device__ __forceinline__ void publish_state(const StateAcc<D>& st, const Tile<T, D, D>& tXt, int lane, int w) {
     using ST = StateTiles<D>;

@@ -128,6 +128,42 @@ __global__ __launch_bounds__(kBlock) void total_kernel(const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------------------
+// scan: per head, the segment records become, in place, exclusive running sums
+// in segment order (dir > 0: record s holds the sum of records 0 .. s-1, the
+// state before segment s) or from the last segment down (dir < 0: record s
+// holds the sum of records nseg-1 .. s+1, the state after it).  The additions
+// run in that order, one at a time, so each record is bitwise the sum a
+// consumer would form itself.  Each thread carries one 16-byte column of the
+// records through the head's segments.
+template <int D>
+__global__ __launch_bounds__(kBlock) void scan_kernel(float* __restrict__ rec, int nseg, int dir) {
+    constexpr int R4 = Rec<D>::kSize / 4;
+    constexpr int NBLK = (R4 + kBlock - 1) / kBlock;
+    constexpr int BATCH = 8;
+    const int e4 = (blockIdx.x % NBLK) * kBlock + threadIdx.x;
+    const int bh = blockIdx.x / NBLK;
+    if (e4 >= R4) return;
+    f32x4* r = reinterpret_cast<f32x4*>(rec) + (int64_t)bh * nseg * R4 + e4;
+    f32x4 run = zero4();
+    for (int i0 = 0; i0 < nseg; i0 += BATCH) {
+        f32x4 x[BATCH];
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+            const int sg = dir > 0 ? i0 + b : nseg - 1 - (i0 + b);
+            x[b] = i0 + b < nseg ? r[(int64_t)sg * R4] : zero4();
+        }
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+            if (i0 + b < nseg) {
+                const int sg = dir > 0 ? i0 + b : nseg - 1 - (i0 + b);
+                r[(int64_t)sg * R4] = run;
+                run += x[b];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // causal_fwd: per (segment, head), walk the segment's chunks from the state
 // carried in by the segments before it.  The last segment of a head also
 // writes the final state S = 1 P^T + S_E, z = N 1 + z_E when asked to.
@@ -159,7 +195,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) void causal_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ o,
     float* __restrict__ den_out, const float* __restrict__ rec, float* __restrict__ S_out, float* __restrict__ z_out,
-    int N, int cps, int nseg, int BH) {
+    int N, int cps, int nseg, int BH, int prefixed) {
     using M = Mma<T>;
     using F = typename M::frag;
     constexpr int KS = M::KSTEP;
@@ -184,18 +220,15 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
     if (wv >= 4) {
         // ---- state waves -------------------------------------------------------------
         const GBuf bk(k + hoff, hbytes), bv(v + hoff, hbytes);
-        // The first chunk's loads are in flight while the starting state is summed:
-        // the records of the segments before this one, in order.
+        // The first chunk's loads are in flight while the starting state arrives:
+        // the records of the segments before this one, summed in order.
         ChunkRegs<T, D> ck, cv;
         ck.load(bk, tok_begin, rtid);
         cv.load(bv, tok_begin, rtid);
         StateAcc<D> st;
         VecAcc<D> vz, vp;
-        zero_state<D>(st);
-        zero_vec<D>(vz);
-        zero_vec<D>(vp);
-        add_records<D, CausalFwdCfg<T, D>::kRecordRegs>(rec + (int64_t)bh * nseg * Rec<D>::kSize, Rec<D>::kSize, seg,
-                                                       st, vz, vp, lane, w);
+        carried_state<D, CausalFwdCfg<T, D>::kRecordRegs>(rec + (int64_t)bh * nseg * Rec<D>::kSize, Rec<D>::kSize,
+                                                         seg, prefixed != 0, st, vz, vp, lane, w);
         publish_state<T, D>(st, Tile<T, D, D>{sm_st[0]}, lane, w);
         store_vec_as<T, D>(s_zb[0], vz, lane, w);
         store_vec<D>(s_p[0], vp, lane, w);
@@ -442,6 +475,7 @@ SegPlan plan_segments(int64_t BH, int64_t N) {
     p.cps = (int)cps;
     p.nseg = (int)((nchunk + cps - 1) / cps);
     if (p.nseg < 1) p.nseg = 1;
+    p.scan = p.nseg > kDirectRecordMaxSegments;
     return p;
 }
 
@@ -490,13 +524,21 @@ hipError_t launch_total(int d, const float* rec, float* total, int64_t BH, int n
     return hipGetLastError();
 }
 
+hipError_t launch_scan(int d, float* rec, int64_t BH, int nseg, int dir, hipStream_t s) {
+    const int r4 = (int)(rec_floats(d) / 4);
+    const dim3 grid((unsigned)(((r4 + kBlock - 1) / kBlock) * BH));
+    LA_DISPATCH_D(d, hipLaunchKernelGGL((scan_kernel<D>), grid, dim3(kBlock), 0, s, rec, nseg, dir));
+    return hipGetLastError();
+}
+
 hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const void* v, void* o, float* den_out,
                              const float* rec, float* S_out, float* z_out, int64_t BH, int64_t N, SegPlan p,
                              hipStream_t s) {
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_CFWD(TT, DD)                                                                                          \
     hipLaunchKernelGGL((causal_fwd_kernel<TT, DD>), grid, dim3(2 * kBlock), 0, s, (const TT*)q, (const TT*)k,       \
-                       (const TT*)v, (TT*)o, den_out, rec, S_out, z_out, (int)N, p.cps, p.nseg, (int)BH)
+                       (const TT*)v, (TT*)o, den_out, rec, S_out, z_out, (int)N, p.cps, p.nseg, (int)BH,          \
+                       (int)p.scan)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_CFWD(bf16, 32); break;

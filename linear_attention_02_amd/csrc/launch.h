@@ -25,9 +25,15 @@ enum DType { kF32 = 0, kBF16 = 1 };
 // is `cps` consecutive chunks.  A segment starts from the sum of the fp32 state
 // aggregates of the segments before it (after it, for the backward's suffix state).
 struct SegPlan {
-    int cps;   // chunks per segment
-    int nseg;  // segments per head
+    int cps;    // chunks per segment
+    int nseg;   // segments per head
+    bool scan;  // records are turned into running sums by a scan pass (long heads);
+                // otherwise each consumer sums the records it needs itself
 };
+// Segments per head up to which consumers sum the segment records themselves
+// (each workgroup re-reads its predecessors' records: quadratic in the segment
+// count, cheaper than a scan pass only while that count is small).
+constexpr int kDirectRecordMaxSegments = 12;
 SegPlan plan_segments(int64_t BH, int64_t N);
 
 // Number of floats in one segment-state record for head dimension d:
@@ -40,6 +46,8 @@ hipError_t launch_seg_state(int dt, int d, const void* k, const void* v, float* 
                             int64_t N, SegPlan p, hipStream_t s);
 // Per-head sum of the segment records (segment order).
 hipError_t launch_total(int d, const float* rec, float* total, int64_t BH, int nseg, hipStream_t s);
+// In place: record s becomes the sum of the records before it (dir > 0) or after it (dir < 0).
+hipError_t launch_scan(int d, float* rec, int64_t BH, int nseg, int dir, hipStream_t s);
 // Causal outputs; the last segment of each head writes S_out / z_out when non-null.
 hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const void* v, void* o,
                              float* den_out, const float* rec, float* S_out, float* z_out, int64_t BH,
