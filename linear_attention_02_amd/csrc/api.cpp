@@ -5,6 +5,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <unistd.h>
+
+#include <atomic>
+#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -113,7 +117,7 @@ la_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_
 struct Layout {
     la::SegPlan plan;
     int64_t heads = 0;
-    size_t rec = 0, total = 0, rrec = 0, rowstat = 0;  // byte offsets
+    size_t rec = 0, total = 0, rrec = 0, rowstat = 0, flags = 0;  // byte offsets
     size_t bytes = 0;
 };
 
@@ -134,9 +138,29 @@ Layout layout(la_op op, int64_t B, int64_t H, int64_t N, int64_t d) {
         off += align_up(recb);
         L.rowstat = off;
         off += align_up((size_t)BH * N * 2 * sizeof(float));
+        if (!L.plan.scan) {  // the fused backward's per-segment flags
+            L.flags = off;
+            off += align_up((size_t)BH * L.plan.nseg * sizeof(unsigned long long));
+        }
     }
     L.bytes = off;
     return L;
+}
+
+// A value for the fused backward's flag words that no earlier launch of this
+// process used and, being seeded from the clock and the process id, that flag
+// words another process left in a reused buffer do not hold (never zero, so a
+// zero-filled buffer never matches either).
+unsigned long long next_epoch() {
+    static std::atomic<unsigned long long> counter{[] {
+        unsigned long long x = (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+        x ^= (unsigned long long)getpid() << 40;
+        x *= 0x9E3779B97F4A7C15ull;  // spread the bits (golden-ratio multiplier)
+        return x ^ (x >> 29);
+    }()};
+    unsigned long long e;
+    do e = counter.fetch_add(1, std::memory_order_relaxed); while (e == 0);
+    return e;
 }
 
 size_t saved_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
@@ -363,6 +387,16 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
             return hip_fail(e, "seg_state launch");
         if (L.plan.scan && (e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, BH, L.plan.nseg, 1, s); })) != hipSuccess)
             return hip_fail(e, "scan launch");
+    }
+    if (!L.plan.scan) {
+        unsigned long long* flags = reinterpret_cast<unsigned long long*>(ws + L.flags);
+        const unsigned long long epoch = next_epoch();
+        if ((e = timed("bwd_fused", s, [&] {
+                 return la::launch_bwd_fused(idt, (int)d, q, k, v, dout, dq, dk, dv, rowstat, rrec, rec, flags, epoch, BH,
+                                             N, L.plan, s);
+             })) != hipSuccess)
+            return hip_fail(e, "bwd_fused launch");
+        return LA_OK;
     }
     if ((e = timed("bwd_prefix", s, [&] { return la::launch_bwd_prefix(idt, (int)d, q, k, v, dout, dq, rowstat, rrec, rec, BH, N, L.plan, s); })) !=
         hipSuccess)

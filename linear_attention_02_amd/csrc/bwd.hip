@@ -36,6 +36,21 @@
 
 namespace la {
 
+// LDS of the two sweeps, carved from one byte buffer so that the fused kernel
+// can run both sweeps in the same workgroup over the same bytes.
+template <typename T, int D>
+struct BwdPrefixLds {
+    static constexpr size_t kTile = (size_t)kC * D * sizeof(T), kSt = (size_t)D * D * sizeof(T);
+    static constexpr size_t oE = 0, oV = 2 * kTile, oQ = 4 * kTile, oG = 5 * kTile, oSt = 6 * kTile;
+    static constexpr size_t oZ = oSt + kSt, oP = oZ + D * 4, oGv = oP + D * 4, kBytes = oGv + kC * 4;
+};
+template <typename T, int D>
+struct BwdSuffixLds {
+    static constexpr size_t kTile = (size_t)kC * D * sizeof(T), kSt = (size_t)D * D * sizeof(T);
+    static constexpr size_t oQ = 0, oG = 2 * kTile, oRt = 4 * kTile, oGv = oRt + 2 * kSt, oR = oGv + 2 * kC * 4;
+    static constexpr size_t kBytes = oR + 2 * D * 4;
+};
+
 // ---------------------------------------------------------------------------------------
 // bwd_prefix.  Wavefront w owns the token tile t = 16 w .. 16 w + 15 of every
 // chunk and keeps phi(Q_t) and G_t of its tokens in registers in accumulator
@@ -43,11 +58,13 @@ namespace la {
 // reductions and the dQ epilogue use; dA stays in the accumulators that form it
 // and feeds the dQ product directly.  phi(Q) and G are also written to LDS for
 // the R update, which contracts over all tokens of the chunk.
-template <typename T, int D>
-__global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_kernel(
+// kCoherentRecord: the segment's (R, r) record is written with agent-coherent
+// stores (read by other workgroups of the same launch).
+template <typename T, int D, bool kCoherentRecord>
+__device__ __forceinline__ void bwd_prefix_body(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dq, float2* __restrict__ rowstat, float* __restrict__ rrec, const float* __restrict__ rec, int N,
-    int cps, int nseg, int BH, int prefixed) {
+    int cps, int nseg, int prefixed, int seg, int bh, char* lds) {
     using M = Mma<T>;
     constexpr int KS = M::KSTEP;
     constexpr int DT = D / 16;
@@ -55,18 +72,18 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
     // E(K) and V are read after the mid-chunk barrier and are double-buffered;
     // phi(Q), G and g are written after the first barrier and read before the
     // next chunk's first barrier; S_E^T, z_E and P are read before the second.
-    __shared__ __attribute__((aligned(16))) T sm_e[2][kC * D];
-    __shared__ __attribute__((aligned(16))) T sm_v[2][kC * D];
-    __shared__ __attribute__((aligned(16))) T sm_q[kC * D];
-    __shared__ __attribute__((aligned(16))) T sm_g[kC * D];
-    __shared__ __attribute__((aligned(16))) T sm_st[D * D];
-    __shared__ __attribute__((aligned(16))) float s_z[D], s_p[D], s_g[kC];
+    using L = BwdPrefixLds<T, D>;
+    T(*const sm_e)[kC * D] = reinterpret_cast<T(*)[kC * D]>(lds + L::oE);
+    T(*const sm_v)[kC * D] = reinterpret_cast<T(*)[kC * D]>(lds + L::oV);
+    T* const sm_q = reinterpret_cast<T*>(lds + L::oQ);
+    T* const sm_g = reinterpret_cast<T*>(lds + L::oG);
+    T* const sm_st = reinterpret_cast<T*>(lds + L::oSt);
+    float* const s_z = reinterpret_cast<float*>(lds + L::oZ);
+    float* const s_p = reinterpret_cast<float*>(lds + L::oP);
+    float* const s_g = reinterpret_cast<float*>(lds + L::oGv);
     const Tile<T, kC, D> tQ{sm_q}, tG{sm_g};
     const Tile<T, D, D> tSt{sm_st};
 
-    // Later segments sum more records: they are dispatched first, since a CU's
-    // older workgroup issues ahead of its younger one.
-    const int seg = nseg - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
     const int64_t hoff = (int64_t)bh * N * D;
     const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
@@ -279,11 +296,28 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
         state_update<T, D, true, false>(stR, vr, vr, tQ, tG, s_g, nullptr, lane, w);
         n += (float)min(kC, N - c0);
     }
-    float* rr = rrec + ((int64_t)bh * nseg + seg) * Rec<D>::kSize;
-    store_state<D>(rr, stR, lane, w);
-    store_vec<D>(rr + Rec<D>::kZ, vr, lane, w);
     // The record's last vector is unused (w = sum over a of R is formed from R where it is used).
-    if (tid < D) rr[Rec<D>::kP + tid] = 0.f;
+    if constexpr (kCoherentRecord) {
+        const GBuf brr(rrec + (int64_t)bh * nseg * Rec<D>::kSize, (uint32_t)(nseg * Rec<D>::kSize * 4));
+        store_record_coherent<D>(brr, (int64_t)seg * Rec<D>::kSize, stR, vr, nullptr, lane, w);
+    } else {
+        float* rr = rrec + ((int64_t)bh * nseg + seg) * Rec<D>::kSize;
+        store_state<D>(rr, stR, lane, w);
+        store_vec<D>(rr + Rec<D>::kZ, vr, lane, w);
+        if (tid < D) rr[Rec<D>::kP + tid] = 0.f;
+    }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
+    T* __restrict__ dq, float2* __restrict__ rowstat, float* __restrict__ rrec, const float* __restrict__ rec, int N,
+    int cps, int nseg, int BH, int prefixed) {
+    __shared__ __attribute__((aligned(16))) char lds[BwdPrefixLds<T, D>::kBytes];
+    // Later segments sum more records: they are dispatched first, since a CU's
+    // older workgroup issues ahead of its younger one.
+    const int seg = nseg - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
+    bwd_prefix_body<T, D, false>(q, k, v, dout, dq, rowstat, rrec, rec, N, cps, nseg, prefixed, seg, bh, lds);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -294,22 +328,26 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
 // (double-buffered, one barrier per chunk).  A and dA for the wave's keys stay
 // in the accumulators that form them and feed the dV and dK products directly;
 // w = sum_a R[a][b] comes from the same R^T operands against a ones operand.
-template <typename T, int D>
-__global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_kernel(
+// kCoherentRecords: the (R, r) records of the later segments are read with
+// agent-coherent loads (written by other workgroups of the same launch).
+// poison: the records could not be confirmed; the results are made NaN.
+template <typename T, int D, bool kCoherentRecords>
+__device__ __forceinline__ void bwd_suffix_body(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dk, T* __restrict__ dv, const float2* __restrict__ rowstat, const float* __restrict__ rrec, int N,
-    int cps, int nseg, int BH, int prefixed) {
+    int cps, int nseg, int prefixed, int seg, int bh, bool poison, char* lds) {
     using M = Mma<T>;
     using CR = ChunkRegs<T, D>;
     constexpr int KS = M::KSTEP;
     constexpr int DT = D / 16;
     constexpr int NY = D / 4;
-    __shared__ __attribute__((aligned(16))) T sm_q[2][kC * D];
-    __shared__ __attribute__((aligned(16))) T sm_g[2][kC * D];
-    __shared__ __attribute__((aligned(16))) T sm_rt[2][D * D];
-    __shared__ __attribute__((aligned(16))) float s_g[2][kC], s_r[2][D];
+    using L = BwdSuffixLds<T, D>;
+    T(*const sm_q)[kC * D] = reinterpret_cast<T(*)[kC * D]>(lds + L::oQ);
+    T(*const sm_g)[kC * D] = reinterpret_cast<T(*)[kC * D]>(lds + L::oG);
+    T(*const sm_rt)[D * D] = reinterpret_cast<T(*)[D * D]>(lds + L::oRt);
+    float(*const s_g)[kC] = reinterpret_cast<float(*)[kC]>(lds + L::oGv);
+    float(*const s_r)[D] = reinterpret_cast<float(*)[D]>(lds + L::oR);
 
-    const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
     const int64_t hoff = (int64_t)bh * N * D;
     const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
@@ -322,8 +360,25 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_ke
     // Suffix state (R, r): the records of the segments after this one, last segment first.
     StateAcc<D> stR;
     VecAcc<D> vr, vunused;
-    carried_state<D>(rrec + ((int64_t)bh * nseg + nseg - 1) * Rec<D>::kSize, -(int64_t)Rec<D>::kSize, nseg - 1 - seg,
-                     prefixed != 0, stR, vr, vunused, lane, w);
+    if constexpr (kCoherentRecords) {
+        const GBuf brr(rrec + (int64_t)bh * nseg * Rec<D>::kSize, (uint32_t)(nseg * Rec<D>::kSize * 4));
+        zero_state<D>(stR);
+        zero_vec<D>(vr);
+        zero_vec<D>(vunused);
+        add_records_from<D, 192>(RecCoherent{brr}, (int64_t)(nseg - 1) * Rec<D>::kSize, -(int64_t)Rec<D>::kSize,
+                                 nseg - 1 - seg, stR, vr, vunused, lane, w);
+        if (poison) {
+            using ST = StateTiles<D>;
+            const float nan = __builtin_nanf("");
+#pragma unroll
+            for (int ia = 0; ia < ST::NAT; ++ia)
+#pragma unroll
+                for (int ib = 0; ib < ST::NBT; ++ib) stR[ia][ib] = splat4(nan);
+        }
+    } else {
+        carried_state<D>(rrec + ((int64_t)bh * nseg + nseg - 1) * Rec<D>::kSize, -(int64_t)Rec<D>::kSize,
+                         nseg - 1 - seg, prefixed != 0, stR, vr, vunused, lane, w);
+    }
 
     CR cq, cdo;
     RowAcc<T, D> kr, vrow;
@@ -468,6 +523,47 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_ke
     }
 }
 
+template <typename T, int D>
+__global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
+    T* __restrict__ dk, T* __restrict__ dv, const float2* __restrict__ rowstat, const float* __restrict__ rrec, int N,
+    int cps, int nseg, int BH, int prefixed) {
+    __shared__ __attribute__((aligned(16))) char lds[BwdSuffixLds<T, D>::kBytes];
+    const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
+    bwd_suffix_body<T, D, false>(q, k, v, dout, dk, dv, rowstat, rrec, N, cps, nseg, prefixed, seg, bh, false, lds);
+}
+
+// ---------------------------------------------------------------------------------------
+// bwd_fused: both sweeps of one (segment, head) in one workgroup, for plans whose
+// consumers sum the segment records themselves.  After the prefix sweep the
+// workgroup publishes its (R, r) record (agent-coherent stores, then its flag)
+// and waits for the flags of the later segments of its head, whose workgroups
+// were dispatched before it (segments run last to first); then the suffix sweep
+// starts from their records.  The suffix sweep's cold start (records, first
+// chunk) overlaps other workgroups' prefix sweeps instead of following a kernel
+// boundary.  den and g per row stay with the workgroup that wrote them.
+template <typename T, int D>
+__global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_fused_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
+    T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv, float2* __restrict__ rowstat,
+    float* __restrict__ rrec, const float* __restrict__ rec, unsigned long long* __restrict__ flags,
+    unsigned long long epoch, int N, int cps, int nseg, int BH) {
+    constexpr size_t kP = BwdPrefixLds<T, D>::kBytes, kS = BwdSuffixLds<T, D>::kBytes;
+    __shared__ __attribute__((aligned(16))) char lds[kP > kS ? kP : kS];
+    const int seg = nseg - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
+    bwd_prefix_body<T, D, true>(q, k, v, dout, dq, rowstat, rrec, rec, N, cps, nseg, 0, seg, bh, lds);
+    // Every wave's record stores (and den, g rows) are complete before the flag.
+    wait_all_memory();
+    __syncthreads();
+    unsigned long long* hf = flags + (int64_t)bh * nseg;
+    if (threadIdx.x == 0) post_flag(&hf[seg], epoch);
+    bool ok = true;
+    if ((threadIdx.x & 63) == 0)
+        for (int j = seg + 1; j < nseg; ++j) ok = ok && await_flag(&hf[j], epoch);
+    ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
+    bwd_suffix_body<T, D, true>(q, k, v, dout, dk, dv, rowstat, rrec, N, cps, nseg, 0, seg, bh, !ok, lds);
+}
+
 // ---------------------------------------------------------------------------------------
 hipError_t launch_bwd_prefix(int dt, int d, const void* q, const void* k, const void* v, const void* dout, void* dq,
                              float* rowstat, float* rrec, const float* rec, int64_t BH, int64_t N, SegPlan p,
@@ -492,6 +588,32 @@ hipError_t launch_bwd_prefix(int dt, int d, const void* q, const void* k, const 
         }
     }
 #undef LA_BWDP
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_fused(int dt, int d, const void* q, const void* k, const void* v, const void* dout, void* dq,
+                            void* dk, void* dv, float* rowstat, float* rrec, const float* rec, unsigned long long* flags,
+                            unsigned long long epoch, int64_t BH, int64_t N, SegPlan p, hipStream_t s) {
+    const dim3 grid((unsigned)(p.nseg * BH));
+#define LA_BWDF(TT, DD)                                                                                           \
+    hipLaunchKernelGGL((bwd_fused_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k,         \
+                       (const TT*)v, (const TT*)dout, (TT*)dq, (TT*)dk, (TT*)dv, (float2*)rowstat, rrec, rec, flags, \
+                       epoch, (int)N, p.cps, p.nseg, (int)BH)
+    if (dt == kBF16) {
+        switch (d) {
+            case 32: LA_BWDF(bf16, 32); break;
+            case 64: LA_BWDF(bf16, 64); break;
+            case 128: LA_BWDF(bf16, 128); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (d) {
+            case 32: LA_BWDF(float, 32); break;
+            case 64: LA_BWDF(float, 64); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+#undef LA_BWDF
     return hipGetLastError();
 }
 

@@ -291,12 +291,25 @@ __device__ __forceinline__ void store_vec_as(T* v, const VecAcc<D>& acc, int lan
     for (int x = 0; x < ST::NVT; ++x) store4(v + (ST::vt0(w) + x) * 16 + 4 * (lane >> 4), acc[x]);
 }
 
-// Add the segment records rec[j * stride] for j = 0 .. count-1, in that order,
-// to the wave's state tiles and vector tiles (fixed order: bitwise reproducible).
-// kRegs: registers the records in flight may take (at most 8 records per batch).
-template <int D, int kRegs = 192>
-__device__ __forceinline__ void add_records(const float* rec, int64_t stride, int count, StateAcc<D>& st,
-                                            VecAcc<D>& va, VecAcc<D>& vb, int lane, int w) {
+// Sources of segment records (indices in floats from the source's base): plain
+// loads through a pointer, or agent-coherent loads through a buffer resource
+// (records that other workgroups of the same launch are publishing).
+struct RecPtr {
+    const float* p;
+    __device__ __forceinline__ f32x4 ld4(int64_t i) const { return *reinterpret_cast<const f32x4*>(p + i); }
+};
+struct RecCoherent {
+    GBuf b;
+    __device__ __forceinline__ f32x4 ld4(int64_t i) const { return b.ld16c((uint32_t)(i * 4)); }
+};
+
+// Add the segment records at base + j * stride of src for j = 0 .. count-1, in
+// that order, to the wave's state tiles and vector tiles (fixed order: bitwise
+// reproducible).  kRegs: registers the records in flight may take (at most 8
+// records per batch).
+template <int D, int kRegs, typename Src>
+__device__ __forceinline__ void add_records_from(const Src& src, int64_t base, int64_t stride, int count,
+                                                 StateAcc<D>& st, VecAcc<D>& va, VecAcc<D>& vb, int lane, int w) {
     using ST = StateTiles<D>;
     constexpr int PER_REC = 4 * (ST::NAT * ST::NBT + 2 * ST::NVT);
     constexpr int B = kRegs / PER_REC >= 8 ? 8 : kRegs / PER_REC >= 1 ? kRegs / PER_REC : 1;
@@ -305,10 +318,18 @@ __device__ __forceinline__ void add_records(const float* rec, int64_t stride, in
 #pragma unroll
         for (int b = 0; b < B; ++b) {
             if (j0 + b < count) {
-                const float* r = rec + (int64_t)(j0 + b) * stride;
-                load_state<D>(r, xs[b], lane, w);
-                load_vec<D>(r + Rec<D>::kZ, xa[b], lane, w);
-                load_vec<D>(r + Rec<D>::kP, xb[b], lane, w);
+                const int64_t r = base + (int64_t)(j0 + b) * stride;
+#pragma unroll
+                for (int ia = 0; ia < ST::NAT; ++ia)
+#pragma unroll
+                    for (int ib = 0; ib < ST::NBT; ++ib)
+                        xs[b][ia][ib] = src.ld4(r + rec_st_off<D>(ST::at0(w) + ia, ST::bt0(w) + ib, lane));
+#pragma unroll
+                for (int x = 0; x < ST::NVT; ++x) {
+                    const int o = (ST::vt0(w) + x) * 16 + 4 * (lane >> 4);
+                    xa[b][x] = src.ld4(r + Rec<D>::kZ + o);
+                    xb[b][x] = src.ld4(r + Rec<D>::kP + o);
+                }
             }
         }
 #pragma unroll
@@ -325,6 +346,33 @@ __device__ __forceinline__ void add_records(const float* rec, int64_t stride, in
                 }
             }
         }
+    }
+}
+
+// The same for records read through a plain pointer: rec[j * stride], j = 0 .. count-1.
+template <int D, int kRegs = 192>
+__device__ __forceinline__ void add_records(const float* rec, int64_t stride, int count, StateAcc<D>& st,
+                                            VecAcc<D>& va, VecAcc<D>& vb, int lane, int w) {
+    add_records_from<D, kRegs>(RecPtr{rec}, 0, stride, count, st, va, vb, lane, w);
+}
+
+// One record [X^T | a | b] written with agent-coherent stores through b at float
+// index base (b = zeros when vb is null).
+template <int D>
+__device__ __forceinline__ void store_record_coherent(const GBuf& buf, int64_t base, const StateAcc<D>& st,
+                                                      const VecAcc<D>& va, const VecAcc<D>* vb, int lane, int w) {
+    using ST = StateTiles<D>;
+#pragma unroll
+    for (int ia = 0; ia < ST::NAT; ++ia)
+#pragma unroll
+        for (int ib = 0; ib < ST::NBT; ++ib)
+            buf.st16c((uint32_t)((base + rec_st_off<D>(ST::at0(w) + ia, ST::bt0(w) + ib, lane)) * 4), st[ia][ib]);
+    if (!ST::owns_vec(w) || (lane & 15) != 0) return;
+#pragma unroll
+    for (int x = 0; x < ST::NVT; ++x) {
+        const int o = (ST::vt0(w) + x) * 16 + 4 * (lane >> 4);
+        buf.st16c((uint32_t)((base + Rec<D>::kZ + o) * 4), va[x]);
+        buf.st16c((uint32_t)((base + Rec<D>::kP + o) * 4), vb != nullptr ? (*vb)[x] : zero4());
     }
 }
 

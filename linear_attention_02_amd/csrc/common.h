@@ -92,7 +92,46 @@ struct GBuf {
     __device__ __forceinline__ void st4f(uint32_t off, float v) const {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
     }
+    // Agent-coherent 16-byte load / store (cache policy sc1): served by or written
+    // through to the device-wide coherence point, so data that another workgroup
+    // of the same launch stores this way is seen without any cache flush.
+    __device__ __forceinline__ f32x4 ld16c(uint32_t off) const {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent);
+        return f32x4{__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w)};
+    }
+    __device__ __forceinline__ void st16c(uint32_t off, f32x4 v) const {
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)}, r, off, 0,
+            kCoherent);
+    }
+    static constexpr int kCoherent = 16;  // the sc1 bit of the buffer instructions' cache policy
 };
+
+// ---- signals between workgroups of one launch -------------------------------------------
+// A 64-bit flag word holds the epoch (a value unique to the launch) once its
+// producer's data is complete.  The producer writes that data with agent-coherent
+// stores and waits for them (s_waitcnt) before the flag store; the consumer polls
+// the flag with agent-coherent loads and then reads the data agent-coherently.
+// No L2 writeback or invalidation is involved (those would cost every waiting
+// workgroup a flush of its XCD's L2).  The wait is bounded: after kSpinLimit
+// polls it gives up and reports failure, so a missing producer cannot hang the GPU.
+constexpr int kSpinLimit = 1 << 16;
+__device__ __forceinline__ void post_flag(unsigned long long* f, unsigned long long epoch) {
+    __hip_atomic_store(f, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool await_flag(const unsigned long long* f, unsigned long long epoch) {
+    for (int i = 0; i < kSpinLimit; ++i) {
+        if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) return true;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return false;
+}
+// Wait for every outstanding memory operation of this wave (stores acknowledged).
+__device__ __forceinline__ void wait_all_memory() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // ---- waits and barriers managed by hand ---------------------------------------------------
 // s_waitcnt with only the vector-memory count constrained (gfx9 encoding).

@@ -66,6 +66,11 @@ constexpr int kDirectTotalMaxSegments = 2;
 hipError_t launch_bwd_prefix(int dt, int d, const void* q, const void* k, const void* v,
                              const void* dout, void* dq, float* rowstat, float* rrec,
                              const float* rec, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
+// Both backward sweeps in one launch (plans without the record scan); flags holds
+// BH * nseg words, epoch is a value no earlier launch on this workspace used.
+hipError_t launch_bwd_fused(int dt, int d, const void* q, const void* k, const void* v, const void* dout, void* dq,
+                            void* dk, void* dv, float* rowstat, float* rrec, const float* rec, unsigned long long* flags,
+                            unsigned long long epoch, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
 hipError_t launch_bwd_suffix(int dt, int d, const void* q, const void* k, const void* v,
                              const void* dout, void* dk, void* dv, const float* rowstat,
                              const float* rrec, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
