@@ -130,7 +130,9 @@ def unit_bytes(B, H, N, d, esize=2):
 
 # Algorithmic bytes per launch of each kernel, in [B,H,N,d] tensors read or
 # written through the ABI (workspace traffic is not algorithmic).
-KERNEL_UNITS = {"seg_state": 2, "causal_fwd": 4, "noncausal_fwd": 2, "bwd_prefix": 5, "bwd_suffix": 6}
+# The fused backward reads q, k, v, dO and writes dq, dk, dv: 7 units (its second
+# sweep's re-reads of the segment are not algorithmic traffic).
+KERNEL_UNITS = {"seg_state": 2, "causal_fwd": 4, "noncausal_fwd": 2, "bwd_prefix": 5, "bwd_suffix": 6, "bwd_fused": 7}
 
 
 def sequence_roofline(stats, B, H, N, d, steps):
