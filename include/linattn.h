@@ -130,6 +130,17 @@ const char* la_last_error_message(void);
 /* Library version string. */
 const char* la_version(void);
 
+/* Test hook for the fused causal backward (used where a head has at most 12
+ * segments and d <= 64).  There each workgroup publishes its segment's suffix
+ * aggregates and waits for those of the later segments of its head; a wait that
+ * sees no data after `polls` polls (default 65536, tens of milliseconds) gives
+ * up, and the dk and dv rows of that segment become NaN instead of using data
+ * that never arrived.  polls = 0 makes every such wait give up at once (the last
+ * segment of each head, which waits for nothing, is unaffected).  Process-wide;
+ * LA_ERR_INVALID_ARGUMENT for polls < 0.  la_debug_wait_limit() returns the bound. */
+la_status la_debug_set_wait_limit(int polls);
+int la_debug_wait_limit(void);
+
 /* Per-kernel timing for benchmarks and profiling.  While enabled (on != 0) on
  * the calling thread, every kernel that a call on this thread launches is
  * bracketed by two HIP events recorded on the call's stream; enabling or

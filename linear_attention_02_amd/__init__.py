@@ -23,6 +23,8 @@ from ._binding import (  # noqa: F401
     profile_enable,
     profile_entries,
     saved_state_size,
+    set_wait_limit,
+    wait_limit,
     workspace_size,
 )
 

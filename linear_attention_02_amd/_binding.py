@@ -22,7 +22,8 @@ LA_OP_FWD_NONCAUSAL, LA_OP_FWD_CAUSAL, LA_OP_BWD_CAUSAL = 0, 1, 2
 
 EXPORTS = ("la_workspace_size", "la_saved_state_size", "la_forward_noncausal", "la_forward_causal", "la_backward_causal",
            "la_decode_step", "la_status_string", "la_last_error_message", "la_version",
-           "la_profile_enable", "la_profile_count", "la_profile_entry")
+           "la_profile_enable", "la_profile_count", "la_profile_entry", "la_debug_set_wait_limit",
+           "la_debug_wait_limit")
 
 _lib = None
 
@@ -68,6 +69,10 @@ def load_library(path: str | None = None):
     lib.la_profile_enable.argtypes = [i32]
     lib.la_profile_count.restype = i32
     lib.la_profile_count.argtypes = []
+    lib.la_debug_set_wait_limit.restype = i32
+    lib.la_debug_set_wait_limit.argtypes = [i32]
+    lib.la_debug_wait_limit.restype = i32
+    lib.la_debug_wait_limit.argtypes = []
     lib.la_profile_entry.restype = i32
     lib.la_profile_entry.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float)]
     if path is None:
@@ -215,6 +220,15 @@ def la_decode_step(S, z, q, k, v, *, out=None):
     _check(load_library().la_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, d,
                                          _dtype_code(q.dtype), _stream(q.device)))
     return o
+
+
+def set_wait_limit(polls: int) -> None:
+    """Bound on the polls of the fused backward's waits between workgroups (test hook; 0 = give up at once)."""
+    _check(load_library().la_debug_set_wait_limit(int(polls)))
+
+
+def wait_limit() -> int:
+    return int(load_library().la_debug_wait_limit())
 
 
 def profile_enable(on: bool = True) -> None:

@@ -118,6 +118,7 @@ struct Layout {
     la::SegPlan plan;
     int64_t heads = 0;
     size_t rec = 0, total = 0, rrec = 0, rowstat = 0, flags = 0;  // byte offsets
+    bool fused = false;  // backward: both sweeps in one launch
     size_t bytes = 0;
 };
 
@@ -138,7 +139,8 @@ Layout layout(la_op op, int64_t B, int64_t H, int64_t N, int64_t d) {
         off += align_up(recb);
         L.rowstat = off;
         off += align_up((size_t)BH * N * 2 * sizeof(float));
-        if (!L.plan.scan) {  // the fused backward's per-segment flags
+        L.fused = !L.plan.scan && la::prefix_forms_records((int)d);
+        if (L.fused) {  // the fused backward's per-segment flags
             L.flags = off;
             off += align_up((size_t)BH * L.plan.nseg * sizeof(unsigned long long));
         }
@@ -151,6 +153,10 @@ Layout layout(la_op op, int64_t B, int64_t H, int64_t N, int64_t d) {
 // process used and, being seeded from the clock and the process id, that flag
 // words another process left in a reused buffer do not hold (never zero, so a
 // zero-filled buffer never matches either).
+// Polls a workgroup spends waiting for another's record before it gives up
+// (its outputs are then NaN); lowered only by tests of that path.
+std::atomic<int> g_wait_limit{la::kDefaultWaitLimit};
+
 unsigned long long next_epoch() {
     static std::atomic<unsigned long long> counter{[] {
         unsigned long long x = (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
@@ -220,6 +226,14 @@ la_status la_profile_enable(int on) {
     g_timing.used = 0;
     return LA_OK;
 }
+
+la_status la_debug_set_wait_limit(int polls) {
+    if (polls < 0) return fail(LA_ERR_INVALID_ARGUMENT, "polls must be >= 0 (got %d)", polls);
+    g_wait_limit.store(polls, std::memory_order_relaxed);
+    return LA_OK;
+}
+
+int la_debug_wait_limit(void) { return g_wait_limit.load(std::memory_order_relaxed); }
 
 int la_profile_count(void) { return (int)g_timing.used; }
 
@@ -388,12 +402,12 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
         if (L.plan.scan && (e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, BH, L.plan.nseg, 1, s); })) != hipSuccess)
             return hip_fail(e, "scan launch");
     }
-    if (!L.plan.scan) {
+    if (L.fused) {
         unsigned long long* flags = reinterpret_cast<unsigned long long*>(ws + L.flags);
         const unsigned long long epoch = next_epoch();
         if ((e = timed("bwd_fused", s, [&] {
-                 return la::launch_bwd_fused(idt, (int)d, q, k, v, dout, dq, dk, dv, rowstat, rrec, rec, flags, epoch, BH,
-                                             N, L.plan, s);
+                 return la::launch_bwd_fused(idt, (int)d, q, k, v, dout, dq, dk, dv, rowstat, rrec, rec, flags, epoch,
+                                             g_wait_limit.load(std::memory_order_relaxed), BH, N, L.plan, s);
              })) != hipSuccess)
             return hip_fail(e, "bwd_fused launch");
         return LA_OK;
@@ -401,6 +415,10 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
     if ((e = timed("bwd_prefix", s, [&] { return la::launch_bwd_prefix(idt, (int)d, q, k, v, dout, dq, rowstat, rrec, rec, BH, N, L.plan, s); })) !=
         hipSuccess)
         return hip_fail(e, "bwd_prefix launch");
+    if (!la::prefix_forms_records((int)d) &&
+        (e = timed("rseg", s, [&] { return la::launch_rseg(idt, (int)d, q, dout, rowstat, rrec, BH, N, L.plan, s); })) !=
+            hipSuccess)
+        return hip_fail(e, "rseg launch");
     if (L.plan.scan && (e = timed("rscan", s, [&] { return la::launch_scan((int)d, rrec, BH, L.plan.nseg, -1, s); })) != hipSuccess)
         return hip_fail(e, "rscan launch");
     if ((e = timed("bwd_suffix", s, [&] { return la::launch_bwd_suffix(idt, (int)d, q, k, v, dout, dk, dv, rowstat, rrec, BH, N, L.plan, s); })) !=

@@ -58,9 +58,18 @@ struct BwdSuffixLds {
 // reductions and the dQ epilogue use; dA stays in the accumulators that form it
 // and feeds the dQ product directly.  phi(Q) and G are also written to LDS for
 // the R update, which contracts over all tokens of the chunk.
+// Whether the prefix sweep forms the segment's (R, r) record itself: at d = 128
+// the registers of R would make the sweep spill, and the rseg pass forms it.
+template <int D>
+struct BwdPrefixForms {
+    static constexpr bool kRecord = D <= 64;
+};
+
 // kCoherentRecord: the segment's (R, r) record is written with agent-coherent
 // stores (read by other workgroups of the same launch).
-template <typename T, int D, bool kCoherentRecord>
+// kRecord: the sweep also forms that record (for d = 128 the registers of R are
+// left to the sweep, and rseg forms the record from the saved den and g).
+template <typename T, int D, bool kCoherentRecord, bool kRecord = true>
 __device__ __forceinline__ void bwd_prefix_body(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dq, float2* __restrict__ rowstat, float* __restrict__ rrec, const float* __restrict__ rec, int N,
@@ -293,11 +302,12 @@ __device__ __forceinline__ void bwd_prefix_body(
 
         // (7) State S_E += E^T V, z_E, P; segment aggregates R += phi(Q)^T G, r += phi(Q)^T g.
         state_update<T, D, true, true>(stS, vz, vp, tE, tV, nullptr, nullptr, lane, w);
-        state_update<T, D, true, false>(stR, vr, vr, tQ, tG, s_g, nullptr, lane, w);
+        if constexpr (kRecord) state_update<T, D, true, false>(stR, vr, vr, tQ, tG, s_g, nullptr, lane, w);
         n += (float)min(kC, N - c0);
     }
     // The record's last vector is unused (w = sum over a of R is formed from R where it is used).
-    if constexpr (kCoherentRecord) {
+    if constexpr (!kRecord) {
+    } else if constexpr (kCoherentRecord) {
         const GBuf brr(rrec + (int64_t)bh * nseg * Rec<D>::kSize, (uint32_t)(nseg * Rec<D>::kSize * 4));
         store_record_coherent<D>(brr, (int64_t)seg * Rec<D>::kSize, stR, vr, nullptr, lane, w);
     } else {
@@ -317,7 +327,70 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
     // Later segments sum more records: they are dispatched first, since a CU's
     // older workgroup issues ahead of its younger one.
     const int seg = nseg - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
-    bwd_prefix_body<T, D, false>(q, k, v, dout, dq, rowstat, rrec, rec, N, cps, nseg, prefixed, seg, bh, lds);
+    bwd_prefix_body<T, D, false, BwdPrefixForms<D>::kRecord>(q, k, v, dout, dq, rowstat, rrec, rec, N, cps, nseg,
+                                                             prefixed, seg, bh, lds);
+}
+
+// ---------------------------------------------------------------------------------------
+// rseg: per (segment, head) the suffix-state aggregates R = sum phi(Q) G^T and
+// r = sum g phi(Q) of the segment's tokens, with G = round(dO / den) and g from
+// the per-row statistics the prefix sweep saved: the same operands, chunk order
+// and products as the prefix sweep's own update, so the record is bitwise the
+// same.  Used where the prefix sweep does not form the record (d = 128).
+template <typename T, int D>
+__global__ __launch_bounds__(kBlock, 2) void rseg_kernel(const T* __restrict__ q, const T* __restrict__ dout,
+                                                      const float2* __restrict__ rowstat, float* __restrict__ rrec,
+                                                      int N, int cps, int nseg, int BH) {
+    using CR = ChunkRegs<T, D>;
+    __shared__ __attribute__((aligned(16))) T sm_q[2][kC * D];
+    __shared__ __attribute__((aligned(16))) T sm_g[2][kC * D];
+    __shared__ __attribute__((aligned(16))) float s_g[2][kC];
+    const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int64_t hoff = (int64_t)bh * N * D;
+    const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
+    const GBuf bq(q + hoff, hbytes), bdo(dout + hoff, hbytes), brs(rowstat + (int64_t)bh * N, (uint32_t)N * 8);
+    const int tok_begin = seg * cps * kC;
+    const int tok_end = min(N, tok_begin + cps * kC);
+
+    StateAcc<D> stR;
+    VecAcc<D> vr;
+    zero_state<D>(stR);
+    zero_vec<D>(vr);
+    CR cq, cdo;
+    float dn[CR::NV];
+    float gv = 0.f;
+    auto load_chunk = [&](int c) {
+        cq.load(bq, c, tid);
+        cdo.load(bdo, c, tid);
+#pragma unroll
+        for (int i = 0; i < CR::NV; ++i) dn[i] = brs.ld4f((uint32_t)(c + CR::row(i, tid)) * 8);
+        gv = brs.ld4f((uint32_t)(c + (tid & (kC - 1))) * 8 + 4);
+    };
+    load_chunk(tok_begin);
+    int buf = 0;
+    for (int c0 = tok_begin; c0 < tok_end; c0 += kC, buf ^= 1) {
+        const Tile<T, kC, D> tQ{sm_q[buf]}, tG{sm_g[buf]};
+        stage_phi<T, D>(cq, tQ, tid);
+#pragma unroll
+        for (int i = 0; i < CR::NV; ++i) {
+            const int t = CR::row(i, tid);
+            const float inv = c0 + t < N ? rcp_f(dn[i]) : 0.f;
+            uint4 packed;
+            T* pk = reinterpret_cast<T*>(&packed);
+#pragma unroll
+            for (int e = 0; e < CR::EV; ++e) pk[e] = from_f32<T>(cdo.get(i, e) * inv);
+            *reinterpret_cast<uint4*>(tG.granule(t, CR::gran(i, tid))) = packed;
+        }
+        if (tid < kC) s_g[buf][tid] = gv;
+        load_chunk(c0 + kC < tok_end ? c0 + kC : N);  // past the segment: zeros, no memory traffic
+        __syncthreads();
+        state_update<T, D, true, false>(stR, vr, vr, tQ, tG, s_g[buf], nullptr, lane, w);
+    }
+    float* rr = rrec + ((int64_t)bh * nseg + seg) * Rec<D>::kSize;
+    store_state<D>(rr, stR, lane, w);
+    store_vec<D>(rr + Rec<D>::kZ, vr, lane, w);
+    if (tid < D) rr[Rec<D>::kP + tid] = 0.f;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -547,7 +620,7 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_fused_ker
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv, float2* __restrict__ rowstat,
     float* __restrict__ rrec, const float* __restrict__ rec, unsigned long long* __restrict__ flags,
-    unsigned long long epoch, int N, int cps, int nseg, int BH) {
+    unsigned long long epoch, int wait_limit, int N, int cps, int nseg, int BH) {
     constexpr size_t kP = BwdPrefixLds<T, D>::kBytes, kS = BwdSuffixLds<T, D>::kBytes;
     __shared__ __attribute__((aligned(16))) char lds[kP > kS ? kP : kS];
     const int seg = nseg - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
@@ -559,7 +632,7 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_fused_ker
     if (threadIdx.x == 0) post_flag(&hf[seg], epoch);
     bool ok = true;
     if ((threadIdx.x & 63) == 0)
-        for (int j = seg + 1; j < nseg; ++j) ok = ok && await_flag(&hf[j], epoch);
+        for (int j = seg + 1; j < nseg; ++j) ok = ok && await_flag(&hf[j], epoch, wait_limit);
     ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
     bwd_suffix_body<T, D, true>(q, k, v, dout, dk, dv, rowstat, rrec, N, cps, nseg, 0, seg, bh, !ok, lds);
 }
@@ -591,14 +664,38 @@ hipError_t launch_bwd_prefix(int dt, int d, const void* q, const void* k, const 
     return hipGetLastError();
 }
 
+hipError_t launch_rseg(int dt, int d, const void* q, const void* dout, const float* rowstat, float* rrec, int64_t BH,
+                       int64_t N, SegPlan p, hipStream_t s) {
+    const dim3 grid((unsigned)(p.nseg * BH));
+#define LA_RSEG(TT, DD)                                                                                           \
+    hipLaunchKernelGGL((rseg_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)dout,           \
+                       (const float2*)rowstat, rrec, (int)N, p.cps, p.nseg, (int)BH)
+    if (dt == kBF16) {
+        switch (d) {
+            case 32: LA_RSEG(bf16, 32); break;
+            case 64: LA_RSEG(bf16, 64); break;
+            case 128: LA_RSEG(bf16, 128); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (d) {
+            case 32: LA_RSEG(float, 32); break;
+            case 64: LA_RSEG(float, 64); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+#undef LA_RSEG
+    return hipGetLastError();
+}
+
 hipError_t launch_bwd_fused(int dt, int d, const void* q, const void* k, const void* v, const void* dout, void* dq,
                             void* dk, void* dv, float* rowstat, float* rrec, const float* rec, unsigned long long* flags,
-                            unsigned long long epoch, int64_t BH, int64_t N, SegPlan p, hipStream_t s) {
+                            unsigned long long epoch, int wait_limit, int64_t BH, int64_t N, SegPlan p, hipStream_t s) {
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_BWDF(TT, DD)                                                                                           \
     hipLaunchKernelGGL((bwd_fused_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k,         \
                        (const TT*)v, (const TT*)dout, (TT*)dq, (TT*)dk, (TT*)dv, (float2*)rowstat, rrec, rec, flags, \
-                       epoch, (int)N, p.cps, p.nseg, (int)BH)
+                       epoch, wait_limit, (int)N, p.cps, p.nseg, (int)BH)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_BWDF(bf16, 32); break;

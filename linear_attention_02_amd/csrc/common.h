@@ -113,14 +113,14 @@ struct GBuf {
 // stores and waits for them (s_waitcnt) before the flag store; the consumer polls
 // the flag with agent-coherent loads and then reads the data agent-coherently.
 // No L2 writeback or invalidation is involved (those would cost every waiting
-// workgroup a flush of its XCD's L2).  The wait is bounded: after kSpinLimit
-// polls it gives up and reports failure, so a missing producer cannot hang the GPU.
-constexpr int kSpinLimit = 1 << 16;
+// workgroup a flush of its XCD's L2).  The wait is bounded: after `limit` polls
+// (65536 unless a test lowers it) it gives up and reports failure, so a missing
+// producer cannot hang the GPU.
 __device__ __forceinline__ void post_flag(unsigned long long* f, unsigned long long epoch) {
     __hip_atomic_store(f, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ bool await_flag(const unsigned long long* f, unsigned long long epoch) {
-    for (int i = 0; i < kSpinLimit; ++i) {
+__device__ __forceinline__ bool await_flag(const unsigned long long* f, unsigned long long epoch, int limit) {
+    for (int i = 0; i < limit; ++i) {
         if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) return true;
         __builtin_amdgcn_s_sleep(2);
     }

@@ -66,11 +66,20 @@ constexpr int kDirectTotalMaxSegments = 2;
 hipError_t launch_bwd_prefix(int dt, int d, const void* q, const void* k, const void* v,
                              const void* dout, void* dq, float* rowstat, float* rrec,
                              const float* rec, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
+// The backward's per-segment (R, r) records from q, dout and the saved per-row
+// statistics, for head dimensions whose prefix sweep does not form them (d > 64).
+hipError_t launch_rseg(int dt, int d, const void* q, const void* dout, const float* rowstat, float* rrec, int64_t BH,
+                       int64_t N, SegPlan p, hipStream_t s);
+constexpr bool prefix_forms_records(int d) { return d <= 64; }
+// Default bound on the polls of one wait between workgroups (each poll sleeps
+// about 128 cycles after a coherent load: tens of milliseconds at most).
+constexpr int kDefaultWaitLimit = 1 << 16;
 // Both backward sweeps in one launch (plans without the record scan); flags holds
-// BH * nseg words, epoch is a value no earlier launch on this workspace used.
+// BH * nseg words, epoch is a value no earlier launch on this workspace used,
+// wait_limit bounds the polls of each wait for a later segment's record.
 hipError_t launch_bwd_fused(int dt, int d, const void* q, const void* k, const void* v, const void* dout, void* dq,
                             void* dk, void* dv, float* rowstat, float* rrec, const float* rec, unsigned long long* flags,
-                            unsigned long long epoch, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
+                            unsigned long long epoch, int wait_limit, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
 hipError_t launch_bwd_suffix(int dt, int d, const void* q, const void* k, const void* v,
                              const void* dout, void* dk, void* dv, const float* rowstat,
                              const float* rrec, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
