@@ -23,9 +23,10 @@ The JSON line also carries
                   on the library's stream over a second run of the timed steps) against the
                   8 TB/s HBM peak;
   * step_roofline: the same for the whole step (22 d bytes per token-head);
-  * calls       : the other measured calls (non-causal forward at the same
-                  size, the long and very-long causal workloads, 512 decode
-                  steps), each with its throughput and roofline fraction;
+  * calls       : the other measured calls (non-causal forward, and non-causal
+                  forward + backward, at the same size; the long and very-long
+                  causal workloads; 512 decode steps), each with its throughput
+                  and roofline fraction;
   * cpu_baseline: the fp64 CPU oracle timed on this host on repeated full
                   steps of the same workload (bounded to about 10 s).
 
@@ -132,7 +133,8 @@ def unit_bytes(B, H, N, d, esize=2):
 # written through the ABI (workspace traffic is not algorithmic).
 # The fused backward reads q, k, v, dO and writes dq, dk, dv: 7 units (its second
 # sweep's re-reads of the segment are not algorithmic traffic).
-KERNEL_UNITS = {"seg_state": 2, "causal_fwd": 4, "noncausal_fwd": 2, "bwd_prefix": 5, "bwd_suffix": 6, "bwd_fused": 7}
+KERNEL_UNITS = {"seg_state": 2, "causal_fwd": 4, "noncausal_fwd": 2, "bwd_prefix": 5, "bwd_suffix": 6, "bwd_fused": 7,
+                "ncbwd_q": 3, "ncbwd_kv": 4}
 
 
 def sequence_roofline(stats, B, H, N, d, steps):
@@ -266,7 +268,21 @@ def bench_calls(args, la, inp, torch, mid_set):
     calls["mid_noncausal_fwd"] = bench_call(
         "noncausal", lambda i: la.la_forward_noncausal(q, k, v, out=o, workspace=ws), 100, 400, w.B * w.N,
         4 * unit_bytes(w.B, w.H, w.N, w.d), la, torch)
-    del o, ws
+    # Non-causal training step: forward saving the key aggregates, backward reading them
+    # (the forward reads q, k, v and writes o; the backward reads q, k, v, dout and writes dq, dk, dv: 11 units).
+    do = mid_set[3]
+    g = tuple(torch.empty_like(q) for _ in range(3))
+    wsb = torch.empty(la.workspace_size(la.LA_OP_BWD_NONCAUSAL, w.B, w.H, w.N, w.d, w.dtype), dtype=torch.uint8,
+                      device="cuda")
+    saved = la.new_saved_state(q)
+
+    def nc_step(i):
+        la.la_forward_noncausal(q, k, v, out=o, workspace=ws, saved_state=saved)
+        la.la_backward_noncausal(q, k, v, do, out=g, workspace=wsb, saved_state=saved)
+
+    calls["mid_noncausal_fwd_bwd"] = bench_call("noncausal_step", nc_step, 100, 400, w.B * w.N,
+                                                11 * unit_bytes(w.B, w.H, w.N, w.d), la, torch)
+    del o, ws, g, wsb, saved
 
     w = inp.LONG
     q, k, v, do = inp.workload_inputs(w, seed=0, device="cuda", with_dout=True)

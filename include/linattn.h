@@ -62,26 +62,36 @@ typedef enum {
 
 typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 
-typedef enum { LA_OP_FWD_NONCAUSAL = 0, LA_OP_FWD_CAUSAL = 1, LA_OP_BWD_CAUSAL = 2 } la_op;
+typedef enum {
+    LA_OP_FWD_NONCAUSAL = 0,
+    LA_OP_FWD_CAUSAL = 1,
+    LA_OP_BWD_CAUSAL = 2,
+    LA_OP_BWD_NONCAUSAL = 3
+} la_op;
 
 /* Bytes of device workspace that `op` needs for this shape (0 is possible).
  * Pure host computation; no device is touched. */
 la_status la_workspace_size(la_op op, int64_t B, int64_t H, int64_t N, int64_t d, int chunk,
                             la_dtype dt, size_t* bytes_out);
 
+/* Bytes of the opaque forward state that la_forward_causal (la_forward_noncausal)
+ * can save for la_backward_causal (la_backward_noncausal) on the same inputs:
+ * the keys' contribution to (S, z) of every sequence segment.  The size is the
+ * same for both forms but the contents are not (for long heads the causal form
+ * keeps running sums): a state feeds only the backward of the form that saved
+ * it.  Pure host computation. */
+la_status la_saved_state_size(int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt,
+                              size_t* bytes_out);
+
 /* Non-causal forward (Statement of the proposition): one reduction of
  * S = sum_j phi(K_j) V_j^T and z = sum_j phi(K_j) over all N keys per head,
  * then O_i = phi(Q_i)^T S / phi(Q_i)^T z for every row.
- * In: q, k, v [B][H][N][d].  Out: o [B][H][N][d]. */
-la_status la_forward_noncausal(const void* q, const void* k, const void* v, void* o, int64_t B,
-                               int64_t H, int64_t N, int64_t d, la_dtype dt, void* workspace,
-                               size_t workspace_bytes, void* stream);
-
-/* Bytes of the opaque forward state that la_forward_causal can save for
- * la_backward_causal on the same inputs (the keys' contribution to (S, z) of
- * every sequence segment).  Pure host computation. */
-la_status la_saved_state_size(int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt,
-                              size_t* bytes_out);
+ * In: q, k, v [B][H][N][d].  Out: o [B][H][N][d]; saved_state (nullable,
+ * saved_state_bytes >= la_saved_state_size()) receives the per-segment key
+ * aggregates so that la_backward_noncausal on the same k, v need not rebuild them. */
+la_status la_forward_noncausal(const void* q, const void* k, const void* v, void* o, void* saved_state,
+                               size_t saved_state_bytes, int64_t B, int64_t H, int64_t N, int64_t d,
+                               la_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Causal forward (the recurrent form of "Why It Matters", evaluated chunk by
  * chunk): O_i = phi(Q_i)^T S_i / phi(Q_i)^T z_i with S_i, z_i summed over keys
@@ -113,6 +123,22 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
                              size_t saved_state_bytes, int64_t B, int64_t H, int64_t N, int64_t d,
                              int chunk, la_dtype dt, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/* Non-causal backward: dQ, dK, dV of L = sum(dO * O) for the non-causal forward,
+ * by the chain rule on the Statement's formula (the pages print no backward):
+ *   G_i = dO_i / den_i, g_i = -G_i . O_i, den_i = phi(Q_i)^T z,
+ *   dphi(Q_i) = S G_i + g_i z,
+ *   dphi(K_j) = R V_j + r, dV_j = R^T phi(K_j),
+ *   R = sum_i phi(Q_i) G_i^T, r = sum_i g_i phi(Q_i)   (over every query row),
+ * then dQ = dphi(Q) * phi'(Q), dK = dphi(K) * phi'(K).  den and O are
+ * recomputed in fp32 from q, k, v.  saved_state (nullable) is the buffer a
+ * la_forward_noncausal call on the same k, v and shape filled; when NULL the
+ * key aggregates are rebuilt from k, v, with bitwise the same results.  d = 32, 64, 128 in bf16; 32, 64 in fp32.
+ * In: q, k, v, dout [B][H][N][d].  Out: dq, dk, dv [B][H][N][d]. */
+la_status la_backward_noncausal(const void* q, const void* k, const void* v, const void* dout,
+                                void* dq, void* dk, void* dv, const void* saved_state,
+                                size_t saved_state_bytes, int64_t B, int64_t H, int64_t N, int64_t d,
+                                la_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
 
 /* One recurrent decode step per (b, h), in place ("Why It Matters": constant
  * memory per step): S += phi(k) v^T, z += phi(k), then
@@ -148,8 +174,9 @@ int la_debug_wait_limit(void);
  * library creates once with hipEventCreate and reuses (no device memory).
  * la_profile_count() is the number of launches recorded since; entry i
  * synchronises on its stop event and returns the kernel's name ("seg_state",
- * "total", "scan", "causal_fwd", "noncausal_fwd", "bwd_prefix", "rscan",
- * "bwd_suffix", "decode", "fill_zero") and its duration in milliseconds. */
+ * "total", "scan", "causal_fwd", "noncausal_fwd", "bwd_prefix", "rseg", "rscan",
+ * "bwd_suffix", "bwd_fused", "ncbwd_q", "ncbwd_kv", "decode", "fill_zero") and
+ * its duration in milliseconds. */
 la_status la_profile_enable(int on);
 int la_profile_count(void);
 la_status la_profile_entry(int i, const char** name, float* ms);

@@ -9,15 +9,18 @@ from ._binding import (  # noqa: F401
     LA_BF16,
     LA_F32,
     LA_OP_BWD_CAUSAL,
+    LA_OP_BWD_NONCAUSAL,
     LA_OP_FWD_CAUSAL,
     LA_OP_FWD_NONCAUSAL,
     LIB_PATH,
     LinAttnError,
     causal_linear_attention,
     la_backward_causal,
+    la_backward_noncausal,
     la_decode_step,
     la_forward_causal,
     la_forward_noncausal,
+    linear_attention,
     load_library,
     new_saved_state,
     profile_enable,

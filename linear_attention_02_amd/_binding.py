@@ -18,10 +18,10 @@ LIB_PATH = os.path.join(_PKG, "liblinattn.so")
 
 LA_OK, LA_ERR_INVALID_ARGUMENT, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = range(5)
 LA_F32, LA_BF16 = 0, 1
-LA_OP_FWD_NONCAUSAL, LA_OP_FWD_CAUSAL, LA_OP_BWD_CAUSAL = 0, 1, 2
+LA_OP_FWD_NONCAUSAL, LA_OP_FWD_CAUSAL, LA_OP_BWD_CAUSAL, LA_OP_BWD_NONCAUSAL = 0, 1, 2, 3
 
 EXPORTS = ("la_workspace_size", "la_saved_state_size", "la_forward_noncausal", "la_forward_causal", "la_backward_causal",
-           "la_decode_step", "la_status_string", "la_last_error_message", "la_version",
+           "la_backward_noncausal", "la_decode_step", "la_status_string", "la_last_error_message", "la_version",
            "la_profile_enable", "la_profile_count", "la_profile_entry", "la_debug_set_wait_limit",
            "la_debug_wait_limit")
 
@@ -50,13 +50,15 @@ def load_library(path: str | None = None):
     lib.la_workspace_size.restype = i32
     lib.la_workspace_size.argtypes = [i32, i64, i64, i64, i64, i32, i32, ctypes.POINTER(sz)]
     lib.la_forward_noncausal.restype = i32
-    lib.la_forward_noncausal.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]
+    lib.la_forward_noncausal.argtypes = [vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_saved_state_size.restype = i32
     lib.la_saved_state_size.argtypes = [i64, i64, i64, i64, i32, i32, ctypes.POINTER(sz)]
     lib.la_forward_causal.restype = i32
     lib.la_forward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.la_backward_causal.restype = i32
     lib.la_backward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.la_backward_noncausal.restype = i32
+    lib.la_backward_noncausal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_decode_step.restype = i32
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.la_status_string.restype = ctypes.c_char_p
@@ -131,7 +133,8 @@ def saved_state_size(B: int, H: int, N: int, d: int, dtype: torch.dtype, chunk: 
 
 
 def new_saved_state(q, chunk: int = 0):
-    """An uninitialised buffer for the forward state of causal calls on tensors shaped like q."""
+    """An uninitialised buffer for the forward state that a forward call on tensors shaped
+    like q saves for the backward of the same form (causal or non-causal)."""
     B, H, N, d = q.shape
     return torch.empty(max(1, saved_state_size(B, H, N, d, q.dtype, chunk)), dtype=torch.uint8, device=q.device)
 
@@ -149,14 +152,17 @@ def _workspace(op, B, H, N, d, dtype, device, chunk, workspace):
     return torch.empty(need, dtype=torch.uint8, device=device)
 
 
-def la_forward_noncausal(q, k, v, *, out=None, workspace=None):
-    """O_i = phi(Q_i)^T S / phi(Q_i)^T z with S, z over all keys.  q, k, v: [B, H, N, d]."""
+def la_forward_noncausal(q, k, v, *, out=None, workspace=None, saved_state=None):
+    """O_i = phi(Q_i)^T S / phi(Q_i)^T z with S, z over all keys.  q, k, v: [B, H, N, d].
+
+    saved_state (optional, from new_saved_state) receives the key aggregates for la_backward_noncausal."""
     B, H, N, d = _check_seq(q, k, v)
     o = torch.empty_like(q) if out is None else out
     ws = _workspace(LA_OP_FWD_NONCAUSAL, B, H, N, d, q.dtype, q.device, 0, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(load_library().la_forward_noncausal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, N, d,
-                                               _dtype_code(q.dtype), _ptr(ws), nbytes, _stream(q.device)))
+    _check(load_library().la_forward_noncausal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(saved_state),
+                                               _nbytes(saved_state), B, H, N, d, _dtype_code(q.dtype), _ptr(ws),
+                                               nbytes, _stream(q.device)))
     return o
 
 
@@ -197,6 +203,23 @@ def la_backward_causal(q, k, v, dout, *, chunk=0, out=None, workspace=None, save
     _check(load_library().la_backward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                                              _ptr(saved_state), _nbytes(saved_state), B, H, N, d, chunk,
                                              _dtype_code(q.dtype), _ptr(ws), nbytes, _stream(q.device)))
+    return dq, dk, dv
+
+
+def la_backward_noncausal(q, k, v, dout, *, out=None, workspace=None, saved_state=None):
+    """Gradients (dq, dk, dv) of sum(dout * la_forward_noncausal(q, k, v)).
+
+    saved_state: the buffer a la_forward_noncausal call on the same q, k, v filled (optional)."""
+    B, H, N, d = _check_seq(q, k, v, dout)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    else:
+        dq, dk, dv = out
+    ws = _workspace(LA_OP_BWD_NONCAUSAL, B, H, N, d, q.dtype, q.device, 0, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().la_backward_noncausal(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
+                                                _ptr(dv), _ptr(saved_state), _nbytes(saved_state), B, H, N, d,
+                                                _dtype_code(q.dtype), _ptr(ws), nbytes, _stream(q.device)))
     return dq, dk, dv
 
 
@@ -264,3 +287,22 @@ class _CausalLinearAttention(torch.autograd.Function):
 def causal_linear_attention(q, k, v):
     """Autograd-aware causal linear attention (forward and backward both run the HIP kernels)."""
     return _CausalLinearAttention.apply(q, k, v)
+
+
+class _LinearAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v):
+        st = new_saved_state(q)
+        o = la_forward_noncausal(q, k, v, saved_state=st)
+        ctx.save_for_backward(q, k, v, st)
+        return o
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, st = ctx.saved_tensors
+        return la_backward_noncausal(q, k, v, dout.contiguous(), saved_state=st)
+
+
+def linear_attention(q, k, v):
+    """Autograd-aware non-causal linear attention (forward and backward both run the HIP kernels)."""
+    return _LinearAttention.apply(q, k, v)

@@ -117,7 +117,7 @@ la_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_
 struct Layout {
     la::SegPlan plan;
     int64_t heads = 0;
-    size_t rec = 0, total = 0, rrec = 0, rowstat = 0, flags = 0;  // byte offsets
+    size_t rec = 0, total = 0, rrec = 0, rtotal = 0, rowstat = 0, flags = 0;  // byte offsets
     bool fused = false;  // backward: both sweeps in one launch
     size_t bytes = 0;
 };
@@ -131,9 +131,17 @@ Layout layout(la_op op, int64_t B, int64_t H, int64_t N, int64_t d) {
     size_t off = 0;
     L.rec = off;
     off += align_up(recb);
+    const size_t totb = (size_t)BH * la::rec_floats(d) * sizeof(float);
     if (op == LA_OP_FWD_NONCAUSAL) {
         L.total = off;
-        off += align_up((size_t)BH * la::rec_floats(d) * sizeof(float));
+        off += align_up(totb);
+    } else if (op == LA_OP_BWD_NONCAUSAL) {
+        L.total = off;
+        off += align_up(totb);
+        L.rrec = off;
+        off += align_up(recb);
+        L.rtotal = off;
+        off += align_up(totb);
     } else if (op == LA_OP_BWD_CAUSAL) {
         L.rrec = off;
         off += align_up(recb);
@@ -251,7 +259,7 @@ la_status la_profile_entry(int i, const char** name, float* ms) {
 la_status la_workspace_size(la_op op, int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt,
                             size_t* bytes_out) {
     if (bytes_out == nullptr) return fail(LA_ERR_INVALID_ARGUMENT, "bytes_out is NULL");
-    if (op != LA_OP_FWD_NONCAUSAL && op != LA_OP_FWD_CAUSAL && op != LA_OP_BWD_CAUSAL)
+    if (op != LA_OP_FWD_NONCAUSAL && op != LA_OP_FWD_CAUSAL && op != LA_OP_BWD_CAUSAL && op != LA_OP_BWD_NONCAUSAL)
         return fail(LA_ERR_INVALID_ARGUMENT, "unknown op %d", (int)op);
     bool empty = false;
     la_status st = check_shape(B, H, N, d, chunk, dt, &empty);
@@ -270,26 +278,31 @@ la_status la_saved_state_size(int64_t B, int64_t H, int64_t N, int64_t d, int ch
     return LA_OK;
 }
 
-la_status la_forward_noncausal(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
-                               int64_t N, int64_t d, la_dtype dt, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+la_status la_forward_noncausal(const void* q, const void* k, const void* v, void* o, void* saved_state,
+                               size_t saved_state_bytes, int64_t B, int64_t H, int64_t N, int64_t d, la_dtype dt,
+                               void* workspace, size_t workspace_bytes, void* stream) {
     bool empty = false;
     la_status st = check_shape(B, H, N, d, 0, dt, &empty);
     if (st != LA_OK) return st;
     if (!q || !k || !v || !o) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-NULL");
     const size_t tb = (size_t)B * H * N * d * elem_size(dt);
+    const size_t sb = saved_state ? saved_bytes(B, H, N, d) : 0;
+    if (saved_state && saved_state_bytes < sb)
+        return fail(LA_ERR_INVALID_ARGUMENT, "saved_state has %zu bytes; %zu are needed", saved_state_bytes, sb);
     const Range in[] = {{"q", q, tb}, {"k", k, tb}, {"v", v, tb}};
-    const Range out[] = {{"o", o, tb}};
-    if ((st = check_ptrs(in, 3, out, 1)) != LA_OK) return st;
+    const Range out[] = {{"o", o, tb}, {"saved_state", saved_state, sb}};
+    if ((st = check_ptrs(in, 3, out, 2)) != LA_OK) return st;
     if (empty) return LA_OK;
     const Layout L = layout(LA_OP_FWD_NONCAUSAL, B, H, N, d);
     if ((st = check_workspace(L, workspace, workspace_bytes)) != LA_OK) return st;
     const Range wsr[] = {{"workspace", workspace, L.bytes}};
     if ((st = check_ptrs(in, 3, wsr, 1)) != LA_OK) return st;
-    if (overlap(wsr[0], out[0])) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps o");
+    for (const Range& r : out)
+        if (overlap(wsr[0], r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
 
     char* ws = static_cast<char*>(workspace);
-    float* rec = reinterpret_cast<float*>(ws + L.rec);
+    // The segment records go straight into the saved state when one is asked for.
+    float* rec = saved_state ? static_cast<float*>(saved_state) : reinterpret_cast<float*>(ws + L.rec);
     float* total = reinterpret_cast<float*>(ws + L.total);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t BH = B * H;
@@ -424,6 +437,63 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
     if ((e = timed("bwd_suffix", s, [&] { return la::launch_bwd_suffix(idt, (int)d, q, k, v, dout, dk, dv, rowstat, rrec, BH, N, L.plan, s); })) !=
         hipSuccess)
         return hip_fail(e, "bwd_suffix launch");
+    return LA_OK;
+}
+
+la_status la_backward_noncausal(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+                                void* dv, const void* saved_state, size_t saved_state_bytes, int64_t B, int64_t H,
+                                int64_t N, int64_t d, la_dtype dt, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    bool empty = false;
+    la_status st = check_shape(B, H, N, d, 0, dt, &empty);
+    if (st != LA_OK) return st;
+    if (dt == LA_F32 && d == 128) return fail(LA_ERR_UNSUPPORTED, "fp32 non-causal backward is built for d = 32 and 64");
+    if (!q || !k || !v || !dout || !dq || !dk || !dv)
+        return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v, dout, dq, dk and dv must be non-NULL");
+    const size_t tb = (size_t)B * H * N * d * elem_size(dt);
+    const size_t sb = saved_state ? saved_bytes(B, H, N, d) : 0;
+    if (saved_state && saved_state_bytes < sb)
+        return fail(LA_ERR_INVALID_ARGUMENT, "saved_state has %zu bytes; %zu are needed", saved_state_bytes, sb);
+    const Range in[] = {{"q", q, tb}, {"k", k, tb}, {"v", v, tb}, {"dout", dout, tb}, {"saved_state", saved_state, sb}};
+    const Range out[] = {{"dq", dq, tb}, {"dk", dk, tb}, {"dv", dv, tb}};
+    if ((st = check_ptrs(in, 5, out, 3)) != LA_OK) return st;
+    if (empty) return LA_OK;
+    const Layout L = layout(LA_OP_BWD_NONCAUSAL, B, H, N, d);
+    if ((st = check_workspace(L, workspace, workspace_bytes)) != LA_OK) return st;
+    const Range wsr[] = {{"workspace", workspace, L.bytes}};
+    if ((st = check_ptrs(in, 5, wsr, 1)) != LA_OK) return st;
+    for (const Range& r : out)
+        if (overlap(wsr[0], r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+
+    char* ws = static_cast<char*>(workspace);
+    const float* rec = saved_state ? static_cast<const float*>(saved_state) : reinterpret_cast<float*>(ws + L.rec);
+    float* total = reinterpret_cast<float*>(ws + L.total);
+    float* rrec = reinterpret_cast<float*>(ws + L.rrec);
+    float* rtotal = reinterpret_cast<float*>(ws + L.rtotal);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t BH = B * H;
+    const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
+    hipError_t e;
+    if (saved_state == nullptr &&
+        (e = timed("seg_state", s, [&] {
+             return la::launch_seg_state(idt, (int)d, k, v, reinterpret_cast<float*>(ws + L.rec), BH, N, L.plan, s);
+         })) != hipSuccess)
+        return hip_fail(e, "seg_state launch");
+    // As in the forward: few segments are summed by every consumer, more go through one total per head.
+    const bool direct = L.plan.nseg <= la::kDirectTotalMaxSegments;
+    const int ntot = direct ? L.plan.nseg : 1;
+    if (!direct && (e = timed("total", s, [&] { return la::launch_total((int)d, rec, total, BH, L.plan.nseg, s); })) != hipSuccess)
+        return hip_fail(e, "total launch");
+    if ((e = timed("ncbwd_q", s, [&] {
+             return la::launch_ncbwd_q(idt, (int)d, q, dout, dq, direct ? rec : total, ntot, rrec, BH, N, L.plan, s);
+         })) != hipSuccess)
+        return hip_fail(e, "ncbwd_q launch");
+    if (!direct && (e = timed("total", s, [&] { return la::launch_total((int)d, rrec, rtotal, BH, L.plan.nseg, s); })) != hipSuccess)
+        return hip_fail(e, "total launch");
+    if ((e = timed("ncbwd_kv", s, [&] {
+             return la::launch_ncbwd_kv(idt, (int)d, k, v, dk, dv, direct ? rrec : rtotal, ntot, BH, N, L.plan, s);
+         })) != hipSuccess)
+        return hip_fail(e, "ncbwd_kv launch");
     return LA_OK;
 }
 

@@ -84,6 +84,15 @@ hipError_t launch_bwd_suffix(int dt, int d, const void* q, const void* k, const 
                              const void* dout, void* dk, void* dv, const float* rowstat,
                              const float* rrec, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
 
+// Non-causal backward.  ncbwd_q: dQ of every row from the head's key state (the
+// in-order sum of `ntotal` records per head at `total`) and each segment's
+// (R, r) record; ncbwd_kv: dK, dV of every key row from the in-order sum of
+// `ntotal` (R, r) records per head at `rtotal`.
+hipError_t launch_ncbwd_q(int dt, int d, const void* q, const void* dout, void* dq, const float* total, int ntotal,
+                          float* rrec, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
+hipError_t launch_ncbwd_kv(int dt, int d, const void* k, const void* v, void* dk, void* dv, const float* rtotal,
+                           int ntotal, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
+
 // Zero-fill n floats with a kernel (no memset node, so the call can sit in a captured graph).
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
 

@@ -33,7 +33,8 @@ def declared_functions():
 
 def test_header_declares_the_four_calls():
     names = declared_functions()
-    for n in ("la_forward_noncausal", "la_forward_causal", "la_backward_causal", "la_decode_step"):
+    for n in ("la_forward_noncausal", "la_forward_causal", "la_backward_causal", "la_backward_noncausal",
+              "la_decode_step"):
         assert n in names
 
 
@@ -67,7 +68,7 @@ def test_saved_state_size(lib):
 
 
 def test_workspace_sizes(lib):
-    for op in (la.LA_OP_FWD_NONCAUSAL, la.LA_OP_FWD_CAUSAL, la.LA_OP_BWD_CAUSAL):
+    for op in (la.LA_OP_FWD_NONCAUSAL, la.LA_OP_FWD_CAUSAL, la.LA_OP_BWD_CAUSAL, la.LA_OP_BWD_NONCAUSAL):
         st, n = ws(lib, op, 4, 16, 4096, 64)
         assert st == 0 and n > 0 and n % 256 == 0
         st, n0 = ws(lib, op, 4, 16, 0, 64)
@@ -111,9 +112,13 @@ def test_forward_causal_validation(lib):
 
 def test_forward_noncausal_and_backward_validation(lib):
     f = lib.la_forward_noncausal
-    assert f(A, A + 0x1000000, A + 0x2000000, None, 1, 1, 64, 64, 1, A + 0x4000000, 1 << 30, None) == 1
-    assert f(A, A + 0x1000000, A + 0x2000000, A + 0x3000000, 1, 1, 64, 64, 1, A + 0x4000000, 8, None) == 3
-    assert f(A, A + 0x1000000, A + 0x2000000, A + 0x3000000, 1, 1, 0, 64, 1, None, 0, None) == 0
+    qkv = (A, A + 0x1000000, A + 0x2000000)
+    assert f(*qkv, None, None, 0, 1, 1, 64, 64, 1, A + 0x4000000, 1 << 30, None) == 1
+    assert f(*qkv, A + 0x3000000, None, 0, 1, 1, 64, 64, 1, A + 0x4000000, 8, None) == 3
+    assert f(*qkv, A + 0x3000000, None, 0, 1, 1, 0, 64, 1, None, 0, None) == 0
+    assert f(*qkv, A + 0x3000000, A + 0x5000000, 8, 1, 1, 64, 64, 1, A + 0x4000000, 1 << 30, None) == 1  # short
+    assert f(*qkv, A + 0x3000000, A + 0x1000000, 1 << 20, 1, 1, 64, 64, 1, A + 0x4000000, 1 << 30, None) == 1  # overlaps k
+    assert f(*qkv, A + 0x3000000, A + 0x4000000, 1 << 20, 1, 1, 64, 64, 1, A + 0x4000000, 1 << 30, None) == 1  # overlaps ws
     b = lib.la_backward_causal
     args = [A, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000, A + 0x5000000, A + 0x6000000]
     assert b(*args, None, 0, 1, 1, 64, 64, 0, 1, A + 0x7000000, 8, None) == 3
@@ -137,3 +142,30 @@ def test_decode_validation(lib):
     assert f(S, z, q, k, v, o, 1, 1, 64, 5, None) == 2
     assert f(S, z, q + 2, k, v, o, 1, 1, 64, 1, None) == 1   # misaligned
     assert f(S, z, q, k, v, o, 0, 7, 64, 1, None) == 0       # empty
+
+
+def test_backward_noncausal_validation(lib):
+    b = lib.la_backward_noncausal
+    args = [A, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000, A + 0x5000000, A + 0x6000000]
+    wsp = A + 0x7000000
+    assert b(*args, None, 0, 1, 1, 64, 64, 1, wsp, 8, None) == 3                   # workspace too small
+    assert b(*args, None, 0, 1, 1, 64, 96, 1, wsp, 1 << 30, None) == 2             # d unsupported
+    assert b(*args, None, 0, 1, 1, 64, 128, 0, wsp, 1 << 30, None) == 2            # fp32 d=128 not built
+    assert b(*args, None, 0, 1, 1, 0, 64, 1, None, 0, None) == 0                   # empty
+    bad = list(args)
+    bad[6] = args[0]                                                                # dv aliases q
+    assert b(*bad, None, 0, 1, 1, 64, 64, 1, wsp, 1 << 30, None) == 1
+    bad = list(args)
+    bad[0] = None
+    assert b(*bad, None, 0, 1, 1, 64, 64, 1, wsp, 1 << 30, None) == 1
+    assert b(*args, A + 0x8000000, 4, 1, 1, 64, 64, 1, wsp, 1 << 30, None) == 1     # saved state short
+    assert b(*args, A + 0x5000000, 1 << 20, 1, 1, 64, 64, 1, wsp, 1 << 30, None) == 1  # saved state overlaps dk
+    assert b(*args, None, 0, 1, 1, 64, 64, 1, A + 0x6000000, 1 << 30, None) == 1    # workspace overlaps dv
+
+
+def test_noncausal_backward_workspace_holds_both_record_sets(lib):
+    _, nf = ws(lib, la.LA_OP_FWD_NONCAUSAL, 4, 16, 4096, 64)
+    _, nb = ws(lib, la.LA_OP_BWD_NONCAUSAL, 4, 16, 4096, 64)
+    out = ctypes.c_size_t(0)
+    lib.la_saved_state_size(4, 16, 4096, 64, 0, la.LA_BF16, ctypes.byref(out))
+    assert nb >= nf + out.value

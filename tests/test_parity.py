@@ -40,6 +40,11 @@ def f64(x):
     return inp.to_f64(x)
 
 
+def np_phi(x):
+    """elu(x) + 1 in fp64 (for error bounds computed in the tests)."""
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
 def record(name, **errs):
     """Append measured errors to $LA_PARITY_LOG (JSON lines) when it is set."""
     path = os.environ.get("LA_PARITY_LOG")
@@ -89,23 +94,46 @@ def run_fwd_noncausal(la, oracle, B, H, N, d, dtype, seed=0, scale=None):
     assert err < TOL[dtype]
 
 
-def run_bwd_causal(la, oracle, B, H, N, d, dtype, seed=0, scale=None):
+def run_bwd_causal(la, oracle, B, H, N, d, dtype, seed=0, scale=None, causal=True):
     q, k, v, do = draw(B, H, N, d, dtype, seed, scale)
-    dq, dk, dv = la.la_backward_causal(q, k, v, do)
+    if causal:
+        dq, dk, dv = la.la_backward_causal(q, k, v, do)
+    else:
+        dq, dk, dv = la.la_backward_noncausal(q, k, v, do)
     torch.cuda.synchronize()
-    rdq, rdk, rdv = oracle.backward_causal(f64(q), f64(k), f64(v), f64(do))
+    ref = oracle.backward_causal if causal else oracle.backward_noncausal
+    rdq, rdk, rdv = ref(f64(q), f64(k), f64(v), f64(do))
     tol = TOL[dtype]
     if N == 1:
         # A single token: O_0 = V_0 whatever q and k are, so dq and dk vanish exactly and
         # no relative error exists; they must be negligible next to dv = dout.
         scale = float(np.abs(f64(do)).max())
-        assert float(np.abs(f64(dq)).max()) < 1e-3 * tol * scale
-        assert float(np.abs(f64(dk)).max()) < 1e-3 * tol * scale
+        if causal or dtype == torch.float32:
+            assert float(np.abs(f64(dq)).max()) < 1e-3 * tol * scale
+            assert float(np.abs(f64(dk)).max()) < 1e-3 * tol * scale
+        else:
+            # The non-causal path takes S_E = E(K_0) V_0^T and R = phi(Q_0) G_0^T into
+            # its MFMAs rounded to bf16 (relative error <= 2^-9 per element) against
+            # fp32 rank-1 terms that cancel them in exact arithmetic.  With
+            # G = dO / den, M = sum_b |G_b V_b| and w = sum_c phi(Q_c) |E(K_c)| / den,
+            # the residuals are at most 2^-9 M (|E(K_a)| + phi(K_a) w) in dphi(Q)_a
+            # and 2^-9 M phi(Q_a) (1 + w) in dphi(K)_a (phi' <= 1); the bar doubles them.
+            fq, fk = np_phi(f64(q)), np_phi(f64(k))
+            ek = np.abs(fk - 1.0)
+            den = (fq * fk).sum(-1, keepdims=True)
+            m = (np.abs(f64(do) / den) * np.abs(f64(v))).sum(-1, keepdims=True)
+            w = (fq * ek).sum(-1, keepdims=True) / den
+            assert (np.abs(f64(dk)) <= 2.0 ** -8 * m * fq * (1 + w) + 1e-7 * scale).all()
+            assert (np.abs(f64(dq)) <= 2.0 ** -8 * m * (ek + fk * w) + 1e-7 * scale).all()
         assert slice_err(dv, rdv) < tol
         return
     errs = {"dq": slice_err(dq, rdq), "dk": slice_err(dk, rdk), "dv": slice_err(dv, rdv)}
-    record(f"bwd_causal {B}x{H}x{N}x{d} {dtype}", **errs)
+    record(f"bwd_{'causal' if causal else 'noncausal'} {B}x{H}x{N}x{d} {dtype}", **errs)
     assert max(errs.values()) < tol, errs
+
+
+def run_bwd_noncausal(la, oracle, B, H, N, d, dtype, seed=0, scale=None):
+    run_bwd_causal(la, oracle, B, H, N, d, dtype, seed, scale, causal=False)
 
 
 # ---- the small fp32 workload: B1 H2 N256 d32, N(0,1) unscaled ---------------------------
@@ -114,6 +142,7 @@ def test_tiny_fp32_all_calls(la, oracle):
     run_fwd_noncausal(la, oracle, w.B, w.H, w.N, w.d, w.dtype, scale=False)
     run_fwd_causal(la, oracle, w.B, w.H, w.N, w.d, w.dtype, scale=False)
     run_bwd_causal(la, oracle, w.B, w.H, w.N, w.d, w.dtype, scale=False)
+    run_bwd_noncausal(la, oracle, w.B, w.H, w.N, w.d, w.dtype, scale=False)
 
 
 # ---- shapes spanning chunks, segments and ragged tails ----------------------------------------
@@ -149,6 +178,15 @@ def test_backward_causal(la, oracle, shape, dtype):
     if dtype == torch.float32 and d == 128:
         pytest.skip("fp32 causal path is built for d <= 64")
     run_bwd_causal(la, oracle, B, H, N, d, dtype, seed=N + 2)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_backward_noncausal(la, oracle, shape, dtype):
+    B, H, N, d = shape
+    if dtype == torch.float32 and d == 128:
+        pytest.skip("fp32 backward is built for d <= 64")
+    run_bwd_noncausal(la, oracle, B, H, N, d, dtype, seed=N + 4)
 
 
 # ---- decode --------------------------------------------------------------------------------------
@@ -195,8 +233,10 @@ def test_decode_random_state(la, oracle):
 # ---- properties -------------------------------------------------------------------------------------
 def test_deterministic(la):
     q, k, v, do = draw(2, 4, 1000, 64, torch.bfloat16, seed=5)
-    a = [la.la_forward_causal(q, k, v), la.la_forward_noncausal(q, k, v), *la.la_backward_causal(q, k, v, do)]
-    b = [la.la_forward_causal(q, k, v), la.la_forward_noncausal(q, k, v), *la.la_backward_causal(q, k, v, do)]
+    a = [la.la_forward_causal(q, k, v), la.la_forward_noncausal(q, k, v), *la.la_backward_causal(q, k, v, do),
+         *la.la_backward_noncausal(q, k, v, do)]
+    b = [la.la_forward_causal(q, k, v), la.la_forward_noncausal(q, k, v), *la.la_backward_causal(q, k, v, do),
+         *la.la_backward_noncausal(q, k, v, do)]
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
@@ -209,13 +249,16 @@ def test_deterministic_multichunk_segments(la):
     ref_o = la.la_forward_causal(q, k, v)
     ref_n = la.la_forward_noncausal(q, k, v)
     ref_g = la.la_backward_causal(q, k, v, do)
+    ref_gn = la.la_backward_noncausal(q, k, v, do)
     for _ in range(4):
         o = la.la_forward_causal(q, k, v)
         n = la.la_forward_noncausal(q, k, v)
         g = la.la_backward_causal(q, k, v, do)
+        gn = la.la_backward_noncausal(q, k, v, do)
         torch.cuda.synchronize()
         assert torch.equal(o, ref_o) and torch.equal(n, ref_n)
         assert all(torch.equal(x, y) for x, y in zip(g, ref_g))
+        assert all(torch.equal(x, y) for x, y in zip(gn, ref_gn))
 
 
 def test_constant_v(la):
@@ -228,6 +271,20 @@ def test_constant_v(la):
     torch.cuda.synchronize()
     assert torch.allclose(o, v, rtol=1e-5, atol=1e-6)
     assert torch.allclose(o2, v, rtol=1e-5, atol=1e-6)
+
+
+def test_constant_v_noncausal_backward(la):
+    """O = V whatever q and k are when every value row is the same: dq and dk vanish,
+    dv = dout spread by the attention weights (its column sums equal those of dout)."""
+    B, H, N, d = 1, 2, 333, 64
+    q, k, _, do = draw(B, H, N, d, torch.float32, seed=19)
+    c = torch.randn(B, H, 1, d, device="cuda")
+    v = c.expand(B, H, N, d).contiguous()
+    dq, dk, dv = la.la_backward_noncausal(q, k, v, do)
+    torch.cuda.synchronize()
+    scale = float(do.abs().max())
+    assert float(dq.abs().max()) < 1e-5 * scale and float(dk.abs().max()) < 1e-5 * scale
+    assert torch.allclose(dv.sum(2), do.sum(2), rtol=1e-4, atol=1e-4 * scale)
 
 
 def test_causality_across_chunks(la):
@@ -255,6 +312,43 @@ def test_autograd_function(la, oracle):
     assert slice_err(q.grad, rdq) < 1e-4
     assert slice_err(k.grad, rdk) < 1e-4
     assert slice_err(v.grad, rdv) < 1e-4
+
+
+def test_autograd_function_noncausal(la, oracle):
+    q, k, v, do = draw(1, 2, 150, 32, torch.float32, seed=14)
+    q.requires_grad_(True)
+    k.requires_grad_(True)
+    v.requires_grad_(True)
+    o = la.linear_attention(q, k, v)
+    o.backward(do)
+    torch.cuda.synchronize()
+    ro = oracle.forward_noncausal(f64(q), f64(k), f64(v))
+    rdq, rdk, rdv = oracle.backward_noncausal(f64(q), f64(k), f64(v), f64(do))
+    assert slice_err(o, ro) < 1e-4
+    assert slice_err(q.grad, rdq) < 1e-4
+    assert slice_err(k.grad, rdk) < 1e-4
+    assert slice_err(v.grad, rdv) < 1e-4
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(2, 3, 1000, 64), (1, 2, 4096 + 17, 32), (1, 1, 300, 128), (1, 8, 64 * 130 + 17, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_saved_state_roundtrip_noncausal(la, shape, dtype):
+    """The non-causal backward fed the non-causal forward's saved state gives bitwise
+    the results of the one that rebuilds the key aggregates."""
+    B, H, N, d = shape
+    if dtype == torch.float32 and d == 128:
+        pytest.skip("fp32 backward is built for d <= 64")
+    q, k, v, do = draw(B, H, N, d, dtype, seed=N + 5)
+    st = la.new_saved_state(q)
+    o1 = la.la_forward_noncausal(q, k, v, saved_state=st)
+    o2 = la.la_forward_noncausal(q, k, v)
+    g1 = la.la_backward_noncausal(q, k, v, do, saved_state=st)
+    g2 = la.la_backward_noncausal(q, k, v, do)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])

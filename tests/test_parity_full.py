@@ -63,14 +63,21 @@ def test_mid_all_heads(la, oracle):
 
 
 def test_mid_noncausal_all_heads(la, oracle):
+    """Non-causal forward and backward at the full Mid size, every head, in the
+    launch sequence a training step uses (the backward reads the forward's saved state)."""
     w = inp.MID
-    q, k, v = inp.workload_inputs(w, seed=0, device="cuda", with_dout=False)
-    o = la.la_forward_noncausal(q, k, v)
+    q, k, v, do = inp.workload_inputs(w, seed=0, device="cuda", with_dout=True)
+    st = la.new_saved_state(q)
+    o = la.la_forward_noncausal(q, k, v, saved_state=st)
+    dq, dk, dv = la.la_backward_noncausal(q, k, v, do, saved_state=st)
     torch.cuda.synchronize()
-    ro = oracle.forward_noncausal(f64(q), f64(k), f64(v))
-    err = slice_err(o, ro)
-    record("full mid noncausal", o=err)
-    assert err < TOL[w.dtype]
+    hq, hk, hv, hdo = f64(q), f64(k), f64(v), f64(do)
+    ro = oracle.forward_noncausal(hq, hk, hv)
+    rdq, rdk, rdv = oracle.backward_noncausal(hq, hk, hv, hdo)
+    errs = {"o": slice_err(o, ro), "dq": slice_err(dq, rdq), "dk": slice_err(dk, rdk), "dv": slice_err(dv, rdv)}
+    record("full mid noncausal", **errs)
+    print("mid noncausal", errs, flush=True)
+    assert max(errs.values()) < TOL[w.dtype], errs
 
 
 def test_long_sampled_heads(la, oracle):
