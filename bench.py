@@ -246,7 +246,7 @@ def bench_mid(args, la, inp, torch):
         "kernels_us": {k: round(t / n * 1e3, 2) for k, (n, t) in sorted(stats.items())},
         "input_sets": nsets,
         "launch": "hip_graph" if graphs is not None else "eager",
-    }, sets[0]
+    }, sets
 
 
 def bench_call(name, fn, warmup, steps, tokens, alg_bytes, la, torch, nsets=1):
@@ -258,30 +258,37 @@ def bench_call(name, fn, warmup, steps, tokens, alg_bytes, la, torch, nsets=1):
             "kernels_us": {k: round(t / n * 1e3, 2) for k, (n, t) in sorted(stats.items())}}
 
 
-def bench_calls(args, la, inp, torch, mid_set):
+def bench_calls(args, la, inp, torch, mid_sets):
     calls = {}
     w = inp.MID
-    q, k, v, _ = mid_set
-    o = torch.empty_like(q)
+    # The Mid calls rotate over the headline step's input sets (together larger than
+    # the last-level cache), so each call reads its inputs from HBM.
+    nsets = len(mid_sets)
+    q0 = mid_sets[0][0]
+    o = torch.empty_like(q0)
     ws = torch.empty(la.workspace_size(la.LA_OP_FWD_NONCAUSAL, w.B, w.H, w.N, w.d, w.dtype), dtype=torch.uint8,
                      device="cuda")
-    calls["mid_noncausal_fwd"] = bench_call(
-        "noncausal", lambda i: la.la_forward_noncausal(q, k, v, out=o, workspace=ws), 100, 400, w.B * w.N,
-        4 * unit_bytes(w.B, w.H, w.N, w.d), la, torch)
+
+    def nc_fwd(i):
+        q, k, v, _ = mid_sets[i]
+        la.la_forward_noncausal(q, k, v, out=o, workspace=ws)
+
+    calls["mid_noncausal_fwd"] = bench_call("noncausal", nc_fwd, 100, 400, w.B * w.N,
+                                            4 * unit_bytes(w.B, w.H, w.N, w.d), la, torch, nsets=nsets)
     # Non-causal training step: forward saving the key aggregates, backward reading them
     # (the forward reads q, k, v and writes o; the backward reads q, k, v, dout and writes dq, dk, dv: 11 units).
-    do = mid_set[3]
-    g = tuple(torch.empty_like(q) for _ in range(3))
+    g = tuple(torch.empty_like(q0) for _ in range(3))
     wsb = torch.empty(la.workspace_size(la.LA_OP_BWD_NONCAUSAL, w.B, w.H, w.N, w.d, w.dtype), dtype=torch.uint8,
                       device="cuda")
-    saved = la.new_saved_state(q)
+    saved = la.new_saved_state(q0)
 
     def nc_step(i):
+        q, k, v, do = mid_sets[i]
         la.la_forward_noncausal(q, k, v, out=o, workspace=ws, saved_state=saved)
         la.la_backward_noncausal(q, k, v, do, out=g, workspace=wsb, saved_state=saved)
 
     calls["mid_noncausal_fwd_bwd"] = bench_call("noncausal_step", nc_step, 100, 400, w.B * w.N,
-                                                11 * unit_bytes(w.B, w.H, w.N, w.d), la, torch)
+                                                11 * unit_bytes(w.B, w.H, w.N, w.d), la, torch, nsets=nsets)
     del o, ws, g, wsb, saved
 
     w = inp.LONG
@@ -385,9 +392,9 @@ def main():
 
     la.load_library()
     torch.cuda.set_device(0)
-    res, mid_set = bench_mid(args, la, inp, torch)
-    calls = None if args.no_calls else bench_calls(args, la, inp, torch, mid_set)
-    cpu = None if args.no_cpu else cpu_baseline(args, inp, torch, mid_set)
+    res, mid_sets = bench_mid(args, la, inp, torch)
+    calls = None if args.no_calls else bench_calls(args, la, inp, torch, mid_sets)
+    cpu = None if args.no_cpu else cpu_baseline(args, inp, torch, mid_sets[0])
     line = {
         "metric": "causal LA fwd+bwd tokens/s, B4 H16 N4096 d64 bf16; % of HBM/MFMA roofline",
         "value": round(res["value"], 1),

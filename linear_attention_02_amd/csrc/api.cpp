@@ -177,9 +177,15 @@ unsigned long long next_epoch() {
     return e;
 }
 
-size_t saved_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+// The saved forward state: every segment record, then (filled by the non-causal
+// forward only) one total per head.
+size_t saved_records_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
     const la::SegPlan p = la::plan_segments(B * H, N);
-    return (size_t)(B * H) * p.nseg * la::rec_floats(d) * sizeof(float);
+    return align_up((size_t)(B * H) * p.nseg * la::rec_floats(d) * sizeof(float));
+}
+
+size_t saved_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+    return saved_records_bytes(B, H, N, d) + (size_t)(B * H) * la::rec_floats(d) * sizeof(float);
 }
 
 la_status check_workspace(const Layout& L, const void* ws, size_t ws_bytes) {
@@ -301,22 +307,21 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
         if (overlap(wsr[0], r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
 
     char* ws = static_cast<char*>(workspace);
-    // The segment records go straight into the saved state when one is asked for.
+    // The segment records and the totals go straight into the saved state when one is asked for.
     float* rec = saved_state ? static_cast<float*>(saved_state) : reinterpret_cast<float*>(ws + L.rec);
-    float* total = reinterpret_cast<float*>(ws + L.total);
+    float* total = saved_state ? reinterpret_cast<float*>(static_cast<char*>(saved_state) + saved_records_bytes(B, H, N, d))
+                               : reinterpret_cast<float*>(ws + L.total);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t BH = B * H;
     const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
     hipError_t e;
     if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
         return hip_fail(e, "seg_state launch");
-    // Few segments: every readout workgroup sums its head's records; many: one total per head first.
-    const bool direct = L.plan.nseg <= la::kDirectTotalMaxSegments;
-    if (!direct && (e = timed("total", s, [&] { return la::launch_total((int)d, rec, total, BH, L.plan.nseg, s); })) != hipSuccess)
+    // One total per head, read by every readout workgroup (and by the backward, from the saved state).
+    if ((e = timed("total", s, [&] { return la::launch_total((int)d, rec, total, BH, L.plan.nseg, s); })) != hipSuccess)
         return hip_fail(e, "total launch");
     if ((e = timed("noncausal_fwd", s, [&] {
-             return la::launch_noncausal_fwd(idt, (int)d, q, o, direct ? rec : total, direct ? L.plan.nseg : 1, BH, N,
-                                             L.plan, s);
+             return la::launch_noncausal_fwd(idt, (int)d, q, o, total, 1, BH, N, L.plan, s);
          })) != hipSuccess)
         return hip_fail(e, "noncausal_fwd launch");
     return LA_OK;
@@ -466,32 +471,31 @@ la_status la_backward_noncausal(const void* q, const void* k, const void* v, con
         if (overlap(wsr[0], r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
 
     char* ws = static_cast<char*>(workspace);
-    const float* rec = saved_state ? static_cast<const float*>(saved_state) : reinterpret_cast<float*>(ws + L.rec);
-    float* total = reinterpret_cast<float*>(ws + L.total);
+    // With a saved state the forward's totals are read from it; otherwise they are rebuilt here.
+    float* total = saved_state ? reinterpret_cast<float*>(const_cast<char*>(static_cast<const char*>(saved_state)) +
+                                                          saved_records_bytes(B, H, N, d))
+                               : reinterpret_cast<float*>(ws + L.total);
+    float* rec = reinterpret_cast<float*>(ws + L.rec);
     float* rrec = reinterpret_cast<float*>(ws + L.rrec);
     float* rtotal = reinterpret_cast<float*>(ws + L.rtotal);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t BH = B * H;
     const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
     hipError_t e;
-    if (saved_state == nullptr &&
-        (e = timed("seg_state", s, [&] {
-             return la::launch_seg_state(idt, (int)d, k, v, reinterpret_cast<float*>(ws + L.rec), BH, N, L.plan, s);
-         })) != hipSuccess)
-        return hip_fail(e, "seg_state launch");
-    // As in the forward: few segments are summed by every consumer, more go through one total per head.
-    const bool direct = L.plan.nseg <= la::kDirectTotalMaxSegments;
-    const int ntot = direct ? L.plan.nseg : 1;
-    if (!direct && (e = timed("total", s, [&] { return la::launch_total((int)d, rec, total, BH, L.plan.nseg, s); })) != hipSuccess)
-        return hip_fail(e, "total launch");
+    if (saved_state == nullptr) {
+        if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
+            return hip_fail(e, "seg_state launch");
+        if ((e = timed("total", s, [&] { return la::launch_total((int)d, rec, total, BH, L.plan.nseg, s); })) != hipSuccess)
+            return hip_fail(e, "total launch");
+    }
     if ((e = timed("ncbwd_q", s, [&] {
-             return la::launch_ncbwd_q(idt, (int)d, q, dout, dq, direct ? rec : total, ntot, rrec, BH, N, L.plan, s);
+             return la::launch_ncbwd_q(idt, (int)d, q, dout, dq, total, 1, rrec, BH, N, L.plan, s);
          })) != hipSuccess)
         return hip_fail(e, "ncbwd_q launch");
-    if (!direct && (e = timed("total", s, [&] { return la::launch_total((int)d, rrec, rtotal, BH, L.plan.nseg, s); })) != hipSuccess)
+    if ((e = timed("total", s, [&] { return la::launch_total((int)d, rrec, rtotal, BH, L.plan.nseg, s); })) != hipSuccess)
         return hip_fail(e, "total launch");
     if ((e = timed("ncbwd_kv", s, [&] {
-             return la::launch_ncbwd_kv(idt, (int)d, k, v, dk, dv, direct ? rrec : rtotal, ntot, BH, N, L.plan, s);
+             return la::launch_ncbwd_kv(idt, (int)d, k, v, dk, dv, rtotal, 1, BH, N, L.plan, s);
          })) != hipSuccess)
         return hip_fail(e, "ncbwd_kv launch");
     return LA_OK;

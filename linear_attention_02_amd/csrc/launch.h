@@ -56,9 +56,6 @@ hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const 
 // records per head at `total` (the segment records, or one precomputed total).
 hipError_t launch_noncausal_fwd(int dt, int d, const void* q, void* o, const float* total, int ntotal,
                                 int64_t BH, int64_t N, SegPlan p, hipStream_t s);
-// Segments per head up to which the non-causal readout sums the segment records
-// itself (beyond that every workgroup re-reading them costs more than a total pass).
-constexpr int kDirectTotalMaxSegments = 2;
 
 // Backward pieces.  bwd_prefix starts each segment from the sum of the forward
 // records before it and writes the segment's suffix-state aggregate to rrec;

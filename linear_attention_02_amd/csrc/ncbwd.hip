@@ -80,13 +80,18 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_q_kernel(const T* __restrict_
     const float n = (float)N;
     const int tl = 16 * w + (lane & 15);
 
-    RowAcc<T, D> qrow, cdo;
-    qrow.load(bq, tok_begin + 16 * w, lane);
-    cdo.load(bdo, tok_begin + 16 * w, lane);
+    // Rows of kAhead chunks are in flight per wave (one: a second measured no faster here).
+    constexpr int kAhead = 1;
+    RowAcc<T, D> qb[kAhead], db[kAhead];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+        const int c = tok_begin + u * kC;
+        qb[u].load(bq, c < tok_end ? c + 16 * w : N, lane);  // past the segment: row N, zeros, no traffic
+        db[u].load(bdo, c < tok_end ? c + 16 * w : N, lane);
+    }
     __syncthreads();
 
-    int buf = 0;
-    for (int c0 = tok_begin; c0 < tok_end; c0 += kC, buf ^= 1) {
+    auto chunk = [&](RowAcc<T, D>& qrow, RowAcc<T, D>& cdo, int c0, int buf) {
         const Tile<T, kC, D> tQ{sm_q[buf]}, tG{sm_g[buf]};
         const int tok = c0 + tl;
         const bool valid = tok < N;
@@ -124,8 +129,8 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_q_kernel(const T* __restrict_
             store4(&tG.at(tl, 16 * m + 4 * g), f32x4{gy[4 * m], gy[4 * m + 1], gy[4 * m + 2], gy[4 * m + 3]});
         }
         gp = sum_over_groups(gp);
-        // Next chunk's rows (past the segment: row N, zeros without memory traffic).
-        const int nxt = c0 + kC < tok_end ? c0 + kC + 16 * w : N;
+        // The rows kAhead chunks on (past the segment: row N, zeros without memory traffic).
+        const int nxt = c0 + kAhead * kC < tok_end ? c0 + kAhead * kC + 16 * w : N;
         qrow.load(bq, nxt, lane);
         cdo.load(bdo, nxt, lane);
 
@@ -163,6 +168,15 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_q_kernel(const T* __restrict_
 
         // R += phi(Q)^T G, r += phi(Q)^T g.
         state_update<T, D, true, false>(stR, vr, vr, tQ, tG, s_g[buf], nullptr, lane, w);
+    };
+    // LDS buffers alternate by chunk.
+    for (int c00 = tok_begin, ci = 0; c00 < tok_end; c00 += kAhead * kC) {
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u, ++ci) {
+            const int c0 = c00 + u * kC;
+            if (c0 >= tok_end) break;
+            chunk(qb[u], db[u], c0, ci & 1);
+        }
     }
     // Record [R^T | r | 0].
     float* rr = rrec + ((int64_t)bh * nseg + seg) * Rec<D>::kSize;
@@ -207,12 +221,18 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_kv_kernel(const T* __restrict
         publish_state<T, D>(stR, tRt, lane, w);
         store_vec<D>(s_r, vr, lane, w);
     }
-    RowAcc<T, D> kr, vrow;
-    kr.load(bk, tok_begin + 16 * w, lane);
-    vrow.load(bv, tok_begin + 16 * w, lane);
+    // Rows of kAhead chunks are in flight per wave (registers allowing).
+    constexpr int kAhead = D * sizeof(T) <= 128 ? 2 : 1;
+    RowAcc<T, D> kb[kAhead], vb[kAhead];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+        const int c = tok_begin + u * kC;
+        kb[u].load(bk, c < tok_end ? c + 16 * w : N, lane);  // past the segment: row N, zeros, no traffic
+        vb[u].load(bv, c < tok_end ? c + 16 * w : N, lane);
+    }
     __syncthreads();
 
-    for (int c0 = tok_begin; c0 < tok_end; c0 += kC) {
+    auto chunk = [&](RowAcc<T, D>& kr, RowAcc<T, D>& vrow, int c0) {
         // For d <= 64 the compiler keeps the R operands in registers across the
         // loop; at d = 128 they would take 256 registers, so they are re-read
         // from LDS every chunk (the fence stops the loads from being hoisted).
@@ -221,7 +241,7 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_kv_kernel(const T* __restrict
         // Raw K and V of this lane's row; E(K) is formed where the MFMAs take it
         // and phi'(K) in the epilogue (short register lifetimes at d = 128).
         const RowAcc<T, D> kcur = kr, vcur = vrow;
-        const int nxt = c0 + kC < tok_end ? c0 + kC + 16 * w : N;  // past the segment: zeros, no memory traffic
+        const int nxt = c0 + kAhead * kC < tok_end ? c0 + kAhead * kC + 16 * w : N;
         kr.load(bk, nxt, lane);
         vrow.load(bv, nxt, lane);
 
@@ -259,6 +279,14 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_kv_kernel(const T* __restrict
             for (int e = 0; e < 4; ++e) xk[e] = (acck[m][e] + rv[e]) * dphi_f(kcur.get(4 * m + e));
             gstore4<T>(bdk, (uint32_t)(tok * D + f0), xk);
             gstore4<T>(bdv, (uint32_t)(tok * D + f0), accv[m]);
+        }
+    };
+    for (int c00 = tok_begin; c00 < tok_end; c00 += kAhead * kC) {
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u) {
+            const int c0 = c00 + u * kC;
+            if (c0 >= tok_end) break;
+            chunk(kb[u], vb[u], c0);
         }
     }
 }
