@@ -58,6 +58,8 @@ def _load():
         f = getattr(lib, name)
         f.restype = None
         f.argtypes = [i64, i64, i64, dp, dp, dp, dp, dp, dp, dp]
+    lib.la_oracle_forward_causal_from.restype = None
+    lib.la_oracle_forward_causal_from.argtypes = [i64, i64, i64, dp, dp, dp, dp, dp, dp, dp, dp, dp]
     lib.la_oracle_decode_step.restype = None
     lib.la_oracle_decode_step.argtypes = [i64, i64, dp, dp, dp, dp, dp, dp]
     lib.la_oracle_quadratic_forward.restype = None
@@ -122,9 +124,34 @@ def _fwd(name, q, k, v, return_den, return_state):
     return out[0] if len(out) == 1 else tuple(out)
 
 
-def forward_causal(q, k, v, return_den=False, return_state=False):
-    """Causal forward, recurrent form (returns o, [den], [S, z])."""
-    return _fwd("la_oracle_forward_causal", q, k, v, return_den, return_state)
+def forward_causal(q, k, v, return_den=False, return_state=False, S0=None, z0=None):
+    """Causal forward, recurrent form (returns o, [den], [S, z]).
+
+    S0 [..., d, d] and z0 [..., d] (optional): the state the recurrence starts from."""
+    if S0 is None and z0 is None:
+        return _fwd("la_oracle_forward_causal", q, k, v, return_den, return_state)
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v must have the same shape")
+    bh, n, d = _heads(q)
+    S0 = None if S0 is None else _f64(S0)
+    z0 = None if z0 is None else _f64(z0)
+    if S0 is not None and S0.shape != q.shape[:-2] + (d, d):
+        raise ValueError("S0 must be [..., d, d] matching q")
+    if z0 is not None and z0.shape != q.shape[:-2] + (d,):
+        raise ValueError("z0 must be [..., d] matching q")
+    o = np.empty_like(q)
+    den = np.empty(q.shape[:-1], dtype=np.float64) if return_den else None
+    S = np.empty(q.shape[:-2] + (d, d), dtype=np.float64) if return_state else None
+    z = np.empty(q.shape[:-2] + (d,), dtype=np.float64) if return_state else None
+    _load().la_oracle_forward_causal_from(bh, n, d, _ptr(S0), _ptr(z0), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                          _ptr(den), _ptr(S), _ptr(z))
+    out = [o]
+    if return_den:
+        out.append(den)
+    if return_state:
+        out += [S, z]
+    return out[0] if len(out) == 1 else tuple(out)
 
 
 def forward_noncausal(q, k, v, return_den=False, return_state=False):

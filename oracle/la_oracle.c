@@ -91,13 +91,17 @@ void la_oracle_forward_noncausal(int64_t BH, int64_t N, int64_t d, const double*
 
 /* ---- forward, causal (recurrent) ------------------------------------------
  * "Why it matters": tokens are processed one by one, S and z are updated
- * incrementally.  Row i reads the state after token i has been added. */
-static void fwd_causal_head(int64_t N, int64_t d, const double* q, const double* k,
-                            const double* v, double* o, double* den_out, double* S_out,
-                            double* z_out) {
+ * incrementally.  Row i reads the state after token i has been added.  The
+ * recurrence starts from (S0, z0) when given (the state a previous call left,
+ * as when a long sequence is processed piece by piece), else from zero. */
+static void fwd_causal_head(int64_t N, int64_t d, const double* S0, const double* z0,
+                            const double* q, const double* k, const double* v, double* o,
+                            double* den_out, double* S_out, double* z_out) {
     double* S = zalloc(d * d);
     double* z = zalloc(d);
     double* f = zalloc(d);
+    if (S0) memcpy(S, S0, (size_t)(d * d) * sizeof(double));
+    if (z0) memcpy(z, z0, (size_t)d * sizeof(double));
     for (int64_t i = 0; i < N; ++i) {
         for (int64_t a = 0; a < d; ++a) f[a] = la_oracle_phi(k[i * d + a]);
         for (int64_t a = 0; a < d; ++a) {
@@ -121,18 +125,25 @@ static void fwd_causal_head(int64_t N, int64_t d, const double* q, const double*
     free(f);
 }
 
-void la_oracle_forward_causal(int64_t BH, int64_t N, int64_t d, const double* q,
-                              const double* k, const double* v, double* o, double* den_out,
-                              double* S_out, double* z_out) {
+void la_oracle_forward_causal_from(int64_t BH, int64_t N, int64_t d, const double* S0,
+                                   const double* z0, const double* q, const double* k,
+                                   const double* v, double* o, double* den_out, double* S_out,
+                                   double* z_out) {
     int nt = la_oracle_get_threads();
     (void)nt;
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
     for (int64_t h = 0; h < BH; ++h) {
         const int64_t off = h * N * d;
-        fwd_causal_head(N, d, q + off, k + off, v + off, o + off,
-                        den_out ? den_out + h * N : NULL, S_out ? S_out + h * d * d : NULL,
-                        z_out ? z_out + h * d : NULL);
+        fwd_causal_head(N, d, S0 ? S0 + h * d * d : NULL, z0 ? z0 + h * d : NULL, q + off, k + off,
+                        v + off, o + off, den_out ? den_out + h * N : NULL,
+                        S_out ? S_out + h * d * d : NULL, z_out ? z_out + h * d : NULL);
     }
+}
+
+void la_oracle_forward_causal(int64_t BH, int64_t N, int64_t d, const double* q,
+                              const double* k, const double* v, double* o, double* den_out,
+                              double* S_out, double* z_out) {
+    la_oracle_forward_causal_from(BH, N, d, NULL, NULL, q, k, v, o, den_out, S_out, z_out);
 }
 
 /* ---- backward --------------------------------------------------------------

@@ -53,6 +53,14 @@ void la_oracle_forward_causal(int64_t BH, int64_t N, int64_t d,
                               const double* q, const double* k, const double* v,
                               double* o, double* den_out, double* S_out, double* z_out);
 
+/* The same recurrence started from the state (S0 [BH][d][d], z0 [BH][d]) instead
+ * of zero (either may be NULL for zero): the continuation of a sequence whose
+ * earlier tokens left that state.  S_out / z_out then hold S0 + the new tokens. */
+void la_oracle_forward_causal_from(int64_t BH, int64_t N, int64_t d,
+                                   const double* S0, const double* z0,
+                                   const double* q, const double* k, const double* v,
+                                   double* o, double* den_out, double* S_out, double* z_out);
+
 /* Causal backward: gradients of L = sum(dout * o) w.r.t. q, k, v for the causal
  * forward above.  Prefix sweep gives dq, suffix sweep gives dk, dv. */
 void la_oracle_backward_causal(int64_t BH, int64_t N, int64_t d,

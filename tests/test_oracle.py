@@ -273,6 +273,54 @@ def test_decode_from_prefix_state(oracle):
     np.testing.assert_allclose(o, full[:, n], rtol=1e-12, atol=1e-13)
 
 
+# ---- a recurrence started from a given state ---------------------------------------------
+def test_start_state_equals_prepended_tokens(oracle):
+    """(S0, z0) left by virtual tokens (k*, v*) act exactly as those tokens placed before the
+    sequence: checked against the numpy quadratic form over the longer sequence."""
+    bh, m, n, d = 3, 4, 9, 5
+    kx, vx = rand((bh, m, d), 60), rand((bh, m, d), 61)
+    q, k, v = rand((bh, n, d), 62), rand((bh, n, d), 63), rand((bh, n, d), 64)
+    S0 = np.einsum("hja,hjb->hab", np_phi(kx), vx)
+    z0 = np_phi(kx).sum(1)
+    o, den, S, z = oracle.forward_causal(q, k, v, return_den=True, return_state=True, S0=S0, z0=z0)
+    qx = rand((bh, m, d), 65)
+    full_q, full_k, full_v = (np.concatenate(t, axis=1) for t in ((qx, q), (kx, k), (vx, v)))
+    ref, ref_den = np_quadratic(full_q, full_k, full_v, causal=True)
+    assert rel(o, ref[:, m:]) < 1e-12
+    assert rel(den, ref_den[:, m:]) < 1e-12
+    assert rel(S, np.einsum("hja,hjb->hab", np_phi(full_k), full_v)) < 1e-12
+    assert rel(z, np_phi(full_k).sum(1)) < 1e-12
+
+
+def test_start_state_continues_a_sequence(oracle):
+    """Processing [0, p) and then [p, n) from the state the first part left equals one pass."""
+    shape, p = (2, 2, 23, 6), 10
+    q, k, v = rand(shape, 66), rand(shape, 67), rand(shape, 68)
+    full, S_f, z_f = oracle.forward_causal(q, k, v, return_state=True)
+    _, S_p, z_p = oracle.forward_causal(q[..., :p, :], k[..., :p, :], v[..., :p, :], return_state=True)
+    rest, S_r, z_r = oracle.forward_causal(q[..., p:, :], k[..., p:, :], v[..., p:, :], return_state=True,
+                                           S0=S_p, z0=z_p)
+    assert rel(rest, full[..., p:, :]) < 1e-12
+    assert rel(S_r, S_f) < 1e-12 and rel(z_r, z_f) < 1e-12
+    # a zero start state is the plain forward
+    zero = oracle.forward_causal(q, k, v, S0=np.zeros(shape[:2] + (6, 6)), z0=np.zeros(shape[:2] + (6,)))
+    np.testing.assert_array_equal(zero, full)
+
+
+def test_start_state_matches_decode_steps(oracle):
+    """T decode steps from a state give the rows of the recurrence started from that state."""
+    bh, t, d = 3, 6, 4
+    S0 = np.abs(rand((bh, d, d), 69)) + 0.5
+    z0 = np.abs(rand((bh, d), 70)) + 2.0
+    q, k, v = rand((bh, t, d), 71), rand((bh, t, d), 72), rand((bh, t, d), 73)
+    o, S, z = oracle.forward_causal(q, k, v, return_state=True, S0=S0, z0=z0)
+    Sd, zd = S0.copy(), z0.copy()
+    for i in range(t):
+        od, Sd, zd = oracle.decode_step(Sd, zd, q[:, i], k[:, i], v[:, i])
+        np.testing.assert_allclose(od, o[:, i], rtol=1e-12, atol=1e-13)
+    assert rel(Sd, S) < 1e-13 and rel(zd, z) < 1e-13
+
+
 def test_thread_count_does_not_change_results(oracle):
     shape = (4, 3, 25, 6)
     q, k, v, do = rand(shape, 47), rand(shape, 48), rand(shape, 49), rand(shape, 50)
