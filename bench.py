@@ -25,8 +25,8 @@ The JSON line also carries
   * step_roofline: the same for the whole step (22 d bytes per token-head);
   * calls       : the other measured calls (non-causal forward, and non-causal
                   forward + backward, at the same size; the long and very-long
-                  causal workloads; 512 decode steps), each with its throughput
-                  and roofline fraction;
+                  causal workloads; 512 decode steps one per call, and 16 per
+                  call), each with its throughput and roofline fraction;
   * cpu_baseline: the fp64 CPU oracle timed on this host on repeated full
                   steps of the same workload (bounded to about 10 s).
 
@@ -350,6 +350,28 @@ def bench_calls(args, la, inp, torch, mid_sets):
     r["us_per_step"] = round(r["ms"] * 1e3 / w.steps, 2)
     r["alg_bytes_per_step"] = step_bytes
     calls["decode_512_steps"] = r
+
+    # The same 512 tokens per sequence through la_decode_steps, TPC tokens per call:
+    # the state moves once per call (2 * 4 d^2 + 2 * 4 d bytes per head) plus TPC
+    # tokens of q, k, v, o (4 * 2 d bytes each).
+    TPC = 16
+    calls_n = w.steps // TPC
+    blocks = [tuple(t[c * TPC:(c + 1) * TPC].permute(1, 2, 0, 3).contiguous() for t in (sq, sk, sv))
+              for c in range(calls_n)]
+    ob = torch.empty(B, H, TPC, d, dtype=w.dtype, device="cuda")
+
+    def span_multi(i):
+        for c in range(calls_n):
+            bq, bk, bv = blocks[c]
+            la.la_decode_steps(S, z, bq, bk, bv, out=ob)
+
+    call_bytes = B * H * (2 * 4 * d * d + 2 * 4 * d + TPC * 4 * 2 * d)
+    r = bench_call("decode_steps", span_multi, 1, 3, B * calls_n * TPC, call_bytes * calls_n, la, torch)
+    r["tokens_per_call"] = TPC
+    r["us_per_call"] = round(r["ms"] * 1e3 / calls_n, 2)
+    r["us_per_token_step"] = round(r["ms"] * 1e3 / (calls_n * TPC), 2)
+    r["alg_bytes_per_call"] = call_bytes
+    calls[f"decode_512_steps_{TPC}_per_call"] = r
     return calls
 
 

@@ -95,15 +95,23 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
 
 /* Causal forward (the recurrent form of "Why It Matters", evaluated chunk by
  * chunk): O_i = phi(Q_i)^T S_i / phi(Q_i)^T z_i with S_i, z_i summed over keys
- * j <= i.  Optional outputs (NULL to skip): den_out [B][H][N] fp32 holds
- * phi(Q_i)^T z_i; S_out [B][H][d][d] and z_out [B][H][d] receive the state
- * after the last token, ready for la_decode_step; saved_state (device,
- * saved_state_bytes >= la_saved_state_size()) receives the per-segment carried
- * state so that la_backward_causal on the same q, k, v need not rebuild it. */
-la_status la_forward_causal(const void* q, const void* k, const void* v, void* o, float* den_out,
-                            float* S_out, float* z_out, void* saved_state, size_t saved_state_bytes,
-                            int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt,
-                            void* workspace, size_t workspace_bytes, void* stream);
+ * j <= i.  Optional inputs (NULL for a zero state): S0 [B][H][d][d] and z0
+ * [B][H][d] fp32, a state the recurrence starts from (the state earlier tokens
+ * of the same sequences left, e.g. from a previous call's S_out, z_out: a long
+ * prefill in pieces); S0 may be the same buffer as S_out and z0 as z_out
+ * (continuing in place), and may overlap no other output.  Optional outputs
+ * (NULL to skip): den_out [B][H][N] fp32 holds phi(Q_i)^T z_i; S_out
+ * [B][H][d][d] and z_out [B][H][d] receive the state after the last token,
+ * ready for la_decode_step / la_decode_steps (with N = 0 they receive the start
+ * state); saved_state (device, saved_state_bytes >= la_saved_state_size())
+ * receives the per-segment carried state so that la_backward_causal on the same
+ * q, k, v need not rebuild it.  The backward starts from a zero state, so a
+ * saved_state together with S0 / z0 is LA_ERR_INVALID_ARGUMENT. */
+la_status la_forward_causal(const void* q, const void* k, const void* v, void* o, const float* S0,
+                            const float* z0, float* den_out, float* S_out, float* z_out,
+                            void* saved_state, size_t saved_state_bytes, int64_t B, int64_t H,
+                            int64_t N, int64_t d, int chunk, la_dtype dt, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* Causal backward: dQ, dK, dV of L = sum(dO * O) for the causal forward, by
  * the chain rule (the arXiv 2510.21956 abstract on vix.ing states that a
@@ -147,6 +155,16 @@ la_status la_backward_noncausal(const void* q, const void* k, const void* v, con
 la_status la_decode_step(float* S, float* z, const void* q, const void* k, const void* v, void* o,
                          int64_t B, int64_t H, int64_t d, la_dtype dt, void* stream);
 
+/* T recurrent decode steps per (b, h) in one call, in place ("Why It Matters":
+ * tokens one by one): for t = 0 .. T-1, S += phi(k_t) v_t^T, z += phi(k_t), then
+ * o_t = phi(q_t)^T S / phi(q_t)^T z.  The same results as T calls of
+ * la_decode_step up to fp32 rounding, with the state read and written once per
+ * call instead of once per token.  S [B][H][d][d] and z [B][H][d] are fp32 and
+ * updated in place; q, k, v, o are [B][H][T][d] in dtype dt (token t of head
+ * (b, h) at row t).  T = 0 does nothing.  Needs no workspace. */
+la_status la_decode_steps(float* S, float* z, const void* q, const void* k, const void* v, void* o,
+                          int64_t B, int64_t H, int64_t T, int64_t d, la_dtype dt, void* stream);
+
 /* Static description of a status code. */
 const char* la_status_string(la_status s);
 
@@ -175,7 +193,8 @@ int la_debug_wait_limit(void);
  * la_profile_count() is the number of launches recorded since; entry i
  * synchronises on its stop event and returns the kernel's name ("seg_state",
  * "total", "scan", "causal_fwd", "noncausal_fwd", "bwd_prefix", "rseg", "rscan",
- * "bwd_suffix", "bwd_fused", "ncbwd_q", "ncbwd_kv", "decode", "fill_zero") and
+ * "bwd_suffix", "bwd_fused", "ncbwd_q", "ncbwd_kv", "decode", "decode_steps",
+ * "state_split", "fill_zero") and
  * its duration in milliseconds. */
 la_status la_profile_enable(int on);
 int la_profile_count(void);

@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     la_backward_causal,
     la_backward_noncausal,
     la_decode_step,
+    la_decode_steps,
     la_forward_causal,
     la_forward_noncausal,
     linear_attention,

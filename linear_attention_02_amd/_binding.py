@@ -21,7 +21,7 @@ LA_F32, LA_BF16 = 0, 1
 LA_OP_FWD_NONCAUSAL, LA_OP_FWD_CAUSAL, LA_OP_BWD_CAUSAL, LA_OP_BWD_NONCAUSAL = 0, 1, 2, 3
 
 EXPORTS = ("la_workspace_size", "la_saved_state_size", "la_forward_noncausal", "la_forward_causal", "la_backward_causal",
-           "la_backward_noncausal", "la_decode_step", "la_status_string", "la_last_error_message", "la_version",
+           "la_backward_noncausal", "la_decode_step", "la_decode_steps", "la_status_string", "la_last_error_message", "la_version",
            "la_profile_enable", "la_profile_count", "la_profile_entry", "la_debug_set_wait_limit",
            "la_debug_wait_limit")
 
@@ -54,13 +54,15 @@ def load_library(path: str | None = None):
     lib.la_saved_state_size.restype = i32
     lib.la_saved_state_size.argtypes = [i64, i64, i64, i64, i32, i32, ctypes.POINTER(sz)]
     lib.la_forward_causal.restype = i32
-    lib.la_forward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.la_forward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.la_backward_causal.restype = i32
     lib.la_backward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.la_backward_noncausal.restype = i32
     lib.la_backward_noncausal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_decode_step.restype = i32
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.la_decode_steps.restype = i32
+    lib.la_decode_steps.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
     lib.la_status_string.restype = ctypes.c_char_p
     lib.la_status_string.argtypes = [i32]
     lib.la_last_error_message.restype = ctypes.c_char_p
@@ -166,21 +168,37 @@ def la_forward_noncausal(q, k, v, *, out=None, workspace=None, saved_state=None)
     return o
 
 
+def _check_state(S, z, B, H, d, device):
+    if S is not None and (S.shape != (B, H, d, d) or S.dtype != torch.float32 or not S.is_contiguous()
+                          or S.device != device):
+        raise ValueError("S0 must be a contiguous [B, H, d, d] fp32 tensor on the inputs' device")
+    if z is not None and (z.shape != (B, H, d) or z.dtype != torch.float32 or not z.is_contiguous()
+                          or z.device != device):
+        raise ValueError("z0 must be a contiguous [B, H, d] fp32 tensor on the inputs' device")
+
+
 def la_forward_causal(q, k, v, *, chunk=0, return_den=False, return_state=False, out=None, workspace=None,
-                      saved_state=None):
+                      saved_state=None, S0=None, z0=None, S_out=None, z_out=None):
     """Causal forward; returns o, plus den [B,H,N] and/or the final (S [B,H,d,d], z [B,H,d]) if asked.
 
+    S0, z0 (optional fp32 [B,H,d,d], [B,H,d]): the state the recurrence starts from (a
+    previous piece of the same sequences).  S_out, z_out (optional): where the final state
+    goes when return_state is set (they may be S0, z0 themselves: continuing in place).
     saved_state (optional, from new_saved_state) receives the carried state for la_backward_causal."""
     B, H, N, d = _check_seq(q, k, v)
+    _check_state(S0, z0, B, H, d, q.device)
+    _check_state(S_out, z_out, B, H, d, q.device)
     o = torch.empty_like(q) if out is None else out
     den = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_den else None
-    S = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device) if return_state else None
-    z = torch.empty((B, H, d), dtype=torch.float32, device=q.device) if return_state else None
+    S = z = None
+    if return_state:
+        S = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device) if S_out is None else S_out
+        z = torch.empty((B, H, d), dtype=torch.float32, device=q.device) if z_out is None else z_out
     ws = _workspace(LA_OP_FWD_CAUSAL, B, H, N, d, q.dtype, q.device, chunk, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(load_library().la_forward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(den), _ptr(S), _ptr(z),
-                                            _ptr(saved_state), _nbytes(saved_state), B, H, N, d, chunk,
-                                            _dtype_code(q.dtype), _ptr(ws), nbytes, _stream(q.device)))
+    _check(load_library().la_forward_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(S0), _ptr(z0), _ptr(den),
+                                            _ptr(S), _ptr(z), _ptr(saved_state), _nbytes(saved_state), B, H, N, d,
+                                            chunk, _dtype_code(q.dtype), _ptr(ws), nbytes, _stream(q.device)))
     res = [o]
     if return_den:
         res.append(den)
@@ -242,6 +260,28 @@ def la_decode_step(S, z, q, k, v, *, out=None):
     o = torch.empty_like(q) if out is None else out
     _check(load_library().la_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, d,
                                          _dtype_code(q.dtype), _stream(q.device)))
+    return o
+
+
+def la_decode_steps(S, z, q, k, v, *, out=None):
+    """T in-place recurrent steps per head in one call; returns o [B, H, T, d].
+
+    S: [B, H, d, d] fp32, z: [B, H, d] fp32, q/k/v: [B, H, T, d] bf16 or fp32 (token t at row t)."""
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    for t in (k, v):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
+            raise ValueError("q, k, v must share shape, dtype and device and be contiguous")
+    if not q.is_contiguous() or not q.is_cuda:
+        raise ValueError("q, k, v must be contiguous tensors on a HIP device")
+    if S.shape != (B, H, d, d) or z.shape != (B, H, d) or S.dtype != torch.float32 or z.dtype != torch.float32:
+        raise ValueError("S must be [B, H, d, d] fp32 and z [B, H, d] fp32")
+    if not (S.is_contiguous() and z.is_contiguous()):
+        raise ValueError("S and z must be contiguous")
+    o = torch.empty_like(q) if out is None else out
+    _check(load_library().la_decode_steps(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, T, d,
+                                          _dtype_code(q.dtype), _stream(q.device)))
     return o
 
 

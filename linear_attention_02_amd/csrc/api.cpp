@@ -117,7 +117,7 @@ la_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_
 struct Layout {
     la::SegPlan plan;
     int64_t heads = 0;
-    size_t rec = 0, total = 0, rrec = 0, rtotal = 0, rowstat = 0, flags = 0;  // byte offsets
+    size_t rec = 0, total = 0, rrec = 0, rtotal = 0, rowstat = 0, flags = 0, init = 0, init_n = 0;  // byte offsets
     bool fused = false;  // backward: both sweeps in one launch
     size_t bytes = 0;
 };
@@ -142,6 +142,11 @@ Layout layout(la_op op, int64_t B, int64_t H, int64_t N, int64_t d) {
         off += align_up(recb);
         L.rtotal = off;
         off += align_up(totb);
+    } else if (op == LA_OP_FWD_CAUSAL) {
+        L.init = off;  // a start state in split form, when one is given
+        off += align_up(totb);
+        L.init_n = off;
+        off += align_up((size_t)BH * sizeof(float));
     } else if (op == LA_OP_BWD_CAUSAL) {
         L.rrec = off;
         off += align_up(recb);
@@ -290,7 +295,8 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
     bool empty = false;
     la_status st = check_shape(B, H, N, d, 0, dt, &empty);
     if (st != LA_OK) return st;
-    if (!q || !k || !v || !o) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-NULL");
+    // Empty tensors (no tokens) may come as NULL pointers.
+    if (N > 0 && (!q || !k || !v || !o)) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-NULL");
     const size_t tb = (size_t)B * H * N * d * elem_size(dt);
     const size_t sb = saved_state ? saved_bytes(B, H, N, d) : 0;
     if (saved_state && saved_state_bytes < sb)
@@ -327,35 +333,55 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
     return LA_OK;
 }
 
-la_status la_forward_causal(const void* q, const void* k, const void* v, void* o, float* den_out, float* S_out,
-                            float* z_out, void* saved_state, size_t saved_state_bytes, int64_t B, int64_t H,
-                            int64_t N, int64_t d, int chunk, la_dtype dt, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+la_status la_forward_causal(const void* q, const void* k, const void* v, void* o, const float* S0, const float* z0,
+                            float* den_out, float* S_out, float* z_out, void* saved_state, size_t saved_state_bytes,
+                            int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt, void* workspace,
+                            size_t workspace_bytes, void* stream) {
     bool empty = false;
     la_status st = check_shape(B, H, N, d, chunk, dt, &empty);
     if (st != LA_OK) return st;
     if (dt == LA_F32 && d == 128) return fail(LA_ERR_UNSUPPORTED, "fp32 causal forward is built for d = 32 and 64");
-    if (!q || !k || !v || !o) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-NULL");
+    // Empty tensors (no tokens) may come as NULL pointers.
+    if (N > 0 && (!q || !k || !v || !o)) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-NULL");
+    const bool from_state = S0 != nullptr || z0 != nullptr;
+    if (from_state && saved_state)
+        return fail(LA_ERR_INVALID_ARGUMENT,
+                    "saved_state is for la_backward_causal, which starts from a zero state: not with S0 / z0");
     const size_t tb = (size_t)B * H * N * d * elem_size(dt);
+    const size_t Sb = (size_t)B * H * d * d * sizeof(float), zb = (size_t)B * H * d * sizeof(float);
     const Range in[] = {{"q", q, tb}, {"k", k, tb}, {"v", v, tb}};
     const size_t sb = saved_state ? saved_bytes(B, H, N, d) : 0;
     if (saved_state && saved_state_bytes < sb)
         return fail(LA_ERR_INVALID_ARGUMENT, "saved_state has %zu bytes; %zu are needed", saved_state_bytes, sb);
     const Range out[] = {{"o", o, tb},
                          {"den_out", den_out, (size_t)B * H * N * sizeof(float)},
-                         {"S_out", S_out, (size_t)B * H * d * d * sizeof(float)},
-                         {"z_out", z_out, (size_t)B * H * d * sizeof(float)},
+                         {"S_out", S_out, Sb},
+                         {"z_out", z_out, zb},
                          {"saved_state", saved_state, sb}};
     if ((st = check_ptrs(in, 3, out, 5)) != LA_OK) return st;
+    // The start state may be the very buffer the final state goes to (continuing in
+    // place: it is read before anything is written), but no other output.
+    const Range init_in[] = {{"S0", S0, Sb}, {"z0", z0, zb}};
+    for (const Range& r : init_in) {
+        if (r.p != nullptr && !aligned16(r.p)) return fail(LA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", r.name);
+        for (const Range& x : out)
+            if (overlap(r, x) && !(r.p == x.p && r.bytes == x.bytes && (x.p == S_out || x.p == z_out)))
+                return fail(LA_ERR_INVALID_ARGUMENT, "%s overlaps output %s", r.name, x.name);
+    }
+    if (overlap(init_in[0], init_in[1])) return fail(LA_ERR_INVALID_ARGUMENT, "S0 and z0 overlap");
     if (B == 0 || H == 0) return LA_OK;
     const int64_t BH = B * H;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (N == 0) {  // empty sequence: the state is zero
-        if (S_out && (e = timed("fill_zero", s, [&] { return la::launch_fill_zero(S_out, (size_t)BH * d * d, s); })) != hipSuccess)
-            return hip_fail(e, "S_out clear");
-        if (z_out && (e = timed("fill_zero", s, [&] { return la::launch_fill_zero(z_out, (size_t)BH * d, s); })) != hipSuccess)
-            return hip_fail(e, "z_out clear");
+    if (N == 0) {  // empty sequence: the final state is the start state
+        if (S_out && S_out != S0) {
+            e = timed("fill_zero", s, [&] { return la::launch_copy_or_zero(S_out, S0, (size_t)BH * d * d, s); });
+            if (e != hipSuccess) return hip_fail(e, "S_out");
+        }
+        if (z_out && z_out != z0) {
+            e = timed("fill_zero", s, [&] { return la::launch_copy_or_zero(z_out, z0, (size_t)BH * d, s); });
+            if (e != hipSuccess) return hip_fail(e, "z_out");
+        }
         return LA_OK;
     }
     const Layout L = layout(LA_OP_FWD_CAUSAL, B, H, N, d);
@@ -368,13 +394,21 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* o
     char* ws = static_cast<char*>(workspace);
     // The segment records go straight into the saved state when one is asked for.
     float* rec = saved_state ? static_cast<float*>(saved_state) : reinterpret_cast<float*>(ws + L.rec);
+    float* init = from_state ? reinterpret_cast<float*>(ws + L.init) : nullptr;
+    float* init_n = from_state ? reinterpret_cast<float*>(ws + L.init_n) : nullptr;
     const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
+    if (from_state &&
+        (e = timed("state_split", s, [&] { return la::launch_state_split((int)d, S0, z0, init, init_n, BH, s); })) !=
+            hipSuccess)
+        return hip_fail(e, "state_split launch");
     if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
         return hip_fail(e, "seg_state launch");
-    if (L.plan.scan && (e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, BH, L.plan.nseg, 1, s); })) != hipSuccess)
+    if (L.plan.scan &&
+        (e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, BH, L.plan.nseg, 1, s, init); })) != hipSuccess)
         return hip_fail(e, "scan launch");
     if ((e = timed("causal_fwd", s, [&] {
-             return la::launch_causal_fwd(idt, (int)d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, L.plan, s);
+             return la::launch_causal_fwd(idt, (int)d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, L.plan, s, init,
+                                          init_n);
          })) != hipSuccess)
         return hip_fail(e, "causal_fwd launch");
     return LA_OK;
@@ -388,7 +422,7 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
     la_status st = check_shape(B, H, N, d, chunk, dt, &empty);
     if (st != LA_OK) return st;
     if (dt == LA_F32 && d == 128) return fail(LA_ERR_UNSUPPORTED, "fp32 causal backward is built for d = 32 and 64");
-    if (!q || !k || !v || !dout || !dq || !dk || !dv)
+    if (N > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv))
         return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v, dout, dq, dk and dv must be non-NULL");
     const size_t tb = (size_t)B * H * N * d * elem_size(dt);
     const size_t sb = saved_state ? saved_bytes(B, H, N, d) : 0;
@@ -453,7 +487,7 @@ la_status la_backward_noncausal(const void* q, const void* k, const void* v, con
     la_status st = check_shape(B, H, N, d, 0, dt, &empty);
     if (st != LA_OK) return st;
     if (dt == LA_F32 && d == 128) return fail(LA_ERR_UNSUPPORTED, "fp32 non-causal backward is built for d = 32 and 64");
-    if (!q || !k || !v || !dout || !dq || !dk || !dv)
+    if (N > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv))
         return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v, dout, dq, dk and dv must be non-NULL");
     const size_t tb = (size_t)B * H * N * d * elem_size(dt);
     const size_t sb = saved_state ? saved_bytes(B, H, N, d) : 0;
@@ -522,6 +556,35 @@ la_status la_decode_step(float* S, float* z, const void* q, const void* k, const
         return la::launch_decode(dt == LA_BF16 ? la::kBF16 : la::kF32, (int)d, S, z, q, k, v, o, BH, s);
     });
     if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return LA_OK;
+}
+
+la_status la_decode_steps(float* S, float* z, const void* q, const void* k, const void* v, void* o, int64_t B,
+                          int64_t H, int64_t T, int64_t d, la_dtype dt, void* stream) {
+    if (dt != LA_F32 && dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "dtype %d is not LA_F32 or LA_BF16", (int)dt);
+    if (d != 32 && d != 64 && d != 128) return fail(LA_ERR_UNSUPPORTED, "d = %lld; built for 32, 64 and 128", (long long)d);
+    if (B < 0 || H < 0 || T < 0)
+        return fail(LA_ERR_INVALID_ARGUMENT, "negative size (B=%lld H=%lld T=%lld)", (long long)B, (long long)H,
+                    (long long)T);
+    if (B > 0 && H > ((int64_t)1 << 24) / B) return fail(LA_ERR_UNSUPPORTED, "B*H exceeds 2^24 heads");
+    if (T > ((int64_t)1 << 24)) return fail(LA_ERR_UNSUPPORTED, "T = %lld exceeds 2^24 tokens per call", (long long)T);
+    if (!S || !z) return fail(LA_ERR_INVALID_ARGUMENT, "S and z must be non-NULL");
+    // Empty token tensors (T = 0) may come as NULL pointers.
+    if (T > 0 && (!q || !k || !v || !o)) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-NULL");
+    const int64_t BH = B * H;
+    const size_t tb = (size_t)BH * T * d * elem_size(dt);
+    const Range in[] = {{"q", q, tb}, {"k", k, tb}, {"v", v, tb}};
+    const Range out[] = {{"S", S, (size_t)BH * d * d * sizeof(float)},
+                         {"z", z, (size_t)BH * d * sizeof(float)},
+                         {"o", o, tb}};
+    la_status st = check_ptrs(in, 3, out, 3);
+    if (st != LA_OK) return st;
+    if (BH == 0 || T == 0) return LA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed("decode_steps", s, [&] {
+        return la::launch_decode_steps(dt == LA_BF16 ? la::kBF16 : la::kF32, (int)d, S, z, q, k, v, o, BH, T, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "decode_steps launch");
     return LA_OK;
 }
 

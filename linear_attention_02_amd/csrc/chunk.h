@@ -381,19 +381,27 @@ __device__ __forceinline__ void store_record_coherent(const GBuf& buf, int64_t b
 // prefixed: a scan has already replaced each record by the running sum of the
 // ones before it (same order), so the record at first + count * stride is that
 // sum; otherwise the records are added here.  Either way the result is bitwise
-// the same.
+// the same.  init (nullable): a record the sum starts from (a scan starts from
+// it too, so a prefixed record already holds it).
 template <int D, int kRegs = 192>
 __device__ __forceinline__ void carried_state(const float* first, int64_t stride, int count, bool prefixed,
-                                              StateAcc<D>& st, VecAcc<D>& va, VecAcc<D>& vb, int lane, int w) {
+                                              StateAcc<D>& st, VecAcc<D>& va, VecAcc<D>& vb, int lane, int w,
+                                              const float* init = nullptr) {
     if (prefixed) {
         const float* r = first + (int64_t)count * stride;
         load_state<D>(r, st, lane, w);
         load_vec<D>(r + Rec<D>::kZ, va, lane, w);
         load_vec<D>(r + Rec<D>::kP, vb, lane, w);
     } else {
-        zero_state<D>(st);
-        zero_vec<D>(va);
-        zero_vec<D>(vb);
+        if (init != nullptr) {
+            load_state<D>(init, st, lane, w);
+            load_vec<D>(init + Rec<D>::kZ, va, lane, w);
+            load_vec<D>(init + Rec<D>::kP, vb, lane, w);
+        } else {
+            zero_state<D>(st);
+            zero_vec<D>(va);
+            zero_vec<D>(vb);
+        }
         add_records<D, kRegs>(first, stride, count, st, va, vb, lane, w);
     }
 }

@@ -136,7 +136,8 @@ __global__ __launch_bounds__(kBlock) void total_kernel(const float* __restrict__
 // consumer would form itself.  Each thread carries one 16-byte column of the
 // records through the head's segments.
 template <int D>
-__global__ __launch_bounds__(kBlock) void scan_kernel(float* __restrict__ rec, int nseg, int dir) {
+__global__ __launch_bounds__(kBlock) void scan_kernel(float* __restrict__ rec, int nseg, int dir,
+                                                      const float* __restrict__ init) {
     constexpr int R4 = Rec<D>::kSize / 4;
     constexpr int NBLK = (R4 + kBlock - 1) / kBlock;
     constexpr int BATCH = 8;
@@ -144,7 +145,8 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(float* __restrict__ rec, i
     const int bh = blockIdx.x / NBLK;
     if (e4 >= R4) return;
     f32x4* r = reinterpret_cast<f32x4*>(rec) + (int64_t)bh * nseg * R4 + e4;
-    f32x4 run = zero4();
+    // init (nullable): one record per head the running sum starts from.
+    f32x4 run = init != nullptr ? reinterpret_cast<const f32x4*>(init)[(int64_t)bh * R4 + e4] : zero4();
     for (int i0 = 0; i0 < nseg; i0 += BATCH) {
         f32x4 x[BATCH];
 #pragma unroll
@@ -195,7 +197,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) void causal_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ o,
     float* __restrict__ den_out, const float* __restrict__ rec, float* __restrict__ S_out, float* __restrict__ z_out,
-    int N, int cps, int nseg, int BH, int prefixed) {
+    const float* __restrict__ init, const float* __restrict__ init_n, int N, int cps, int nseg, int BH,
+    int prefixed) {
     using M = Mma<T>;
     using F = typename M::frag;
     constexpr int KS = M::KSTEP;
@@ -228,7 +231,8 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
         StateAcc<D> st;
         VecAcc<D> vz, vp;
         carried_state<D, CausalFwdCfg<T, D>::kRecordRegs>(rec + (int64_t)bh * nseg * Rec<D>::kSize, Rec<D>::kSize,
-                                                         seg, prefixed != 0, st, vz, vp, lane, w);
+                                                         seg, prefixed != 0, st, vz, vp, lane, w,
+                                                         init != nullptr ? init + (int64_t)bh * Rec<D>::kSize : nullptr);
         publish_state<T, D>(st, Tile<T, D, D>{sm_st[0]}, lane, w);
         store_vec_as<T, D>(s_zb[0], vz, lane, w);
         store_vec<D>(s_p[0], vp, lane, w);
@@ -285,7 +289,8 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
                 for (int x = 0; x < ST::NVT; ++x)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        z_out[(int64_t)bh * D + (ST::vt0(w) + x) * 16 + 4 * g + e] = (float)N + vz[x][e];
+                        z_out[(int64_t)bh * D + (ST::vt0(w) + x) * 16 + 4 * g + e] =
+                            (init_n != nullptr ? init_n[bh] + (float)N : (float)N) + vz[x][e];
             }
         }
         return;
@@ -294,7 +299,8 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
     // ---- output waves ------------------------------------------------------------------
     const GBuf bq(q + hoff, hbytes), bo(o + hoff, hbytes);
     const GBuf bden(den_out != nullptr ? den_out + (int64_t)bh * N : nullptr, den_out != nullptr ? (uint32_t)N * 4 : 0u);
-    float n = (float)tok_begin;
+    // Tokens before the chunk (the count of the rank-1 part of z), from the start state's count.
+    float n = init_n != nullptr ? init_n[bh] + (float)tok_begin : (float)tok_begin;
     // Wavefront w takes token tile tt = (w + ci) mod 4 of chunk ci: the causal
     // mask leaves tt + 1 key tiles, and the rotation spreads that work evenly
     // over the SIMDs.
@@ -457,8 +463,42 @@ __global__ __launch_bounds__(kBlock) void noncausal_fwd_kernel(const T* __restri
     }
 }
 
-__global__ __launch_bounds__(kBlock) void fill_zero_kernel(float* __restrict__ p, size_t n) {
-    for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (size_t)gridDim.x * kBlock) p[i] = 0.f;
+// ---------------------------------------------------------------------------------------
+// state_split: a start state (S0, z0) given as plain sums, rewritten in the split
+// form the kernels carry: S0 = 1 P0^T + S0_E, z0 = n0 1 + z0_E with P0 and n0 the
+// means over the feature index a, so that S0_E and z0_E hold only the deviations
+// (as small as a prefix's own S_E, z_E; the rank-1 parts stay in fp32).  Out: the
+// record [S0_E^T | z0_E | P0] and n0 per head.  Either input may be null (zero).
+// Thread b handles value column b (fixed-order sums: bitwise reproducible).
+template <int D>
+__global__ __launch_bounds__(kBlock) void state_split_kernel(const float* __restrict__ S0, const float* __restrict__ z0,
+                                                             float* __restrict__ init, float* __restrict__ init_n) {
+    const int bh = blockIdx.x, b = threadIdx.x;
+    float* r = init + (int64_t)bh * Rec<D>::kSize;
+    const float* Sh = S0 != nullptr ? S0 + (int64_t)bh * D * D : nullptr;
+    const float* zh = z0 != nullptr ? z0 + (int64_t)bh * D : nullptr;
+    float n0 = 0.f;
+    if (zh != nullptr) {
+        for (int a = 0; a < D; ++a) n0 += zh[a];
+        n0 *= 1.f / (float)D;
+    }
+    if (b >= D) return;
+    float p = 0.f;
+    if (Sh != nullptr) {
+        for (int a = 0; a < D; ++a) p += Sh[a * D + b];
+        p *= 1.f / (float)D;
+    }
+    for (int a = 0; a < D; ++a) r[Rec<D>::kSt + b * D + a] = Sh != nullptr ? Sh[a * D + b] - p : 0.f;
+    r[Rec<D>::kZ + b] = zh != nullptr ? zh[b] - n0 : 0.f;  // feature b of z0_E
+    r[Rec<D>::kP + b] = p;
+    if (b == 0) init_n[bh] = n0;
+}
+
+// dst[i] = src[i], or 0 when src is null.
+__global__ __launch_bounds__(kBlock) void fill_zero_kernel(float* __restrict__ p, const float* __restrict__ src,
+                                                           size_t n) {
+    for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (size_t)gridDim.x * kBlock)
+        p[i] = src != nullptr ? src[i] : 0.f;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -496,13 +536,22 @@ SegPlan plan_segments(int64_t BH, int64_t N) {
         default: return hipErrorInvalidValue; \
     }
 
-hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s) {
+hipError_t launch_state_split(int d, const float* S0, const float* z0, float* init, float* init_n, int64_t BH,
+                              hipStream_t s) {
+    LA_DISPATCH_D(d, hipLaunchKernelGGL((state_split_kernel<D>), dim3((unsigned)BH), dim3(kBlock), 0, s, S0, z0, init,
+                                        init_n));
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_or_zero(float* p, const float* src, size_t n, hipStream_t s) {
     if (n == 0) return hipSuccess;
     size_t blocks = (n + kBlock - 1) / kBlock;
     if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, s, p, n);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, s, p, src, n);
     return hipGetLastError();
 }
+
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s) { return launch_copy_or_zero(p, nullptr, n, s); }
 
 hipError_t launch_seg_state(int dt, int d, const void* k, const void* v, float* rec, int64_t BH, int64_t N,
                             SegPlan p, hipStream_t s) {
@@ -524,21 +573,21 @@ hipError_t launch_total(int d, const float* rec, float* total, int64_t BH, int n
     return hipGetLastError();
 }
 
-hipError_t launch_scan(int d, float* rec, int64_t BH, int nseg, int dir, hipStream_t s) {
+hipError_t launch_scan(int d, float* rec, int64_t BH, int nseg, int dir, hipStream_t s, const float* init) {
     const int r4 = (int)(rec_floats(d) / 4);
     const dim3 grid((unsigned)(((r4 + kBlock - 1) / kBlock) * BH));
-    LA_DISPATCH_D(d, hipLaunchKernelGGL((scan_kernel<D>), grid, dim3(kBlock), 0, s, rec, nseg, dir));
+    LA_DISPATCH_D(d, hipLaunchKernelGGL((scan_kernel<D>), grid, dim3(kBlock), 0, s, rec, nseg, dir, init));
     return hipGetLastError();
 }
 
 hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const void* v, void* o, float* den_out,
                              const float* rec, float* S_out, float* z_out, int64_t BH, int64_t N, SegPlan p,
-                             hipStream_t s) {
+                             hipStream_t s, const float* init, const float* init_n) {
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_CFWD(TT, DD)                                                                                          \
     hipLaunchKernelGGL((causal_fwd_kernel<TT, DD>), grid, dim3(2 * kBlock), 0, s, (const TT*)q, (const TT*)k,       \
-                       (const TT*)v, (TT*)o, den_out, rec, S_out, z_out, (int)N, p.cps, p.nseg, (int)BH,          \
-                       (int)p.scan)
+                       (const TT*)v, (TT*)o, den_out, rec, S_out, z_out, init, init_n, (int)N, p.cps, p.nseg,     \
+                       (int)BH, (int)p.scan)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_CFWD(bf16, 32); break;

@@ -46,12 +46,21 @@ hipError_t launch_seg_state(int dt, int d, const void* k, const void* v, float* 
                             int64_t N, SegPlan p, hipStream_t s);
 // Per-head sum of the segment records (segment order).
 hipError_t launch_total(int d, const float* rec, float* total, int64_t BH, int nseg, hipStream_t s);
-// In place: record s becomes the sum of the records before it (dir > 0) or after it (dir < 0).
-hipError_t launch_scan(int d, float* rec, int64_t BH, int nseg, int dir, hipStream_t s);
+// In place: record s becomes the sum of the records before it (dir > 0) or after it (dir < 0),
+// starting from init[bh] (one record per head) when init is non-null.
+hipError_t launch_scan(int d, float* rec, int64_t BH, int nseg, int dir, hipStream_t s,
+                       const float* init = nullptr);
 // Causal outputs; the last segment of each head writes S_out / z_out when non-null.
+// init / init_n (nullable): per head, a start-state record and its token count n0
+// (from launch_state_split); the carried state of every segment starts from them.
 hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const void* v, void* o,
                              float* den_out, const float* rec, float* S_out, float* z_out, int64_t BH,
-                             int64_t N, SegPlan p, hipStream_t s);
+                             int64_t N, SegPlan p, hipStream_t s, const float* init = nullptr,
+                             const float* init_n = nullptr);
+// A start state (S0 [BH][d][d], z0 [BH][d], either nullable = zero) in the carried split
+// form: one record [S0_E^T | z0_E | P0] per head in init, and n0 per head in init_n.
+hipError_t launch_state_split(int d, const float* S0, const float* z0, float* init, float* init_n, int64_t BH,
+                              hipStream_t s);
 // Non-causal outputs from each head's state: the in-order sum of `ntotal`
 // records per head at `total` (the segment records, or one precomputed total).
 hipError_t launch_noncausal_fwd(int dt, int d, const void* q, void* o, const float* total, int ntotal,
@@ -92,9 +101,14 @@ hipError_t launch_ncbwd_kv(int dt, int d, const void* k, const void* v, void* dk
 
 // Zero-fill n floats with a kernel (no memset node, so the call can sit in a captured graph).
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
+// Copy n floats from src (zero-fill when src is null) with the same kernel.
+hipError_t launch_copy_or_zero(float* p, const float* src, size_t n, hipStream_t s);
 
 // Decode.
 hipError_t launch_decode(int dt, int d, float* S, float* z, const void* q, const void* k,
                          const void* v, void* o, int64_t BH, hipStream_t s);
+// T decode steps per head in one pass over the state; q, k, v, o are [BH][T][d].
+hipError_t launch_decode_steps(int dt, int d, float* S, float* z, const void* q, const void* k,
+                               const void* v, void* o, int64_t BH, int64_t T, hipStream_t s);
 
 }  // namespace la

@@ -88,12 +88,15 @@ A = 0x10000000  # fake, 256-byte aligned device addresses; never dereferenced
 
 
 def fwd_causal(lib, q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000, den=None, S=None, z=None,
-               saved=None, saved_bytes=0, B=1, H=1, N=64, d=64, chunk=0, dt=la.LA_BF16, wsp=A + 0x4000000, wsb=0):
-    return lib.la_forward_causal(q, k, v, o, den, S, z, saved, saved_bytes, B, H, N, d, chunk, dt, wsp, wsb, None)
+               saved=None, saved_bytes=0, B=1, H=1, N=64, d=64, chunk=0, dt=la.LA_BF16, wsp=A + 0x4000000, wsb=0,
+               S0=None, z0=None):
+    return lib.la_forward_causal(q, k, v, o, S0, z0, den, S, z, saved, saved_bytes, B, H, N, d, chunk, dt, wsp, wsb,
+                                 None)
 
 
 def test_forward_causal_validation(lib):
     assert fwd_causal(lib, q=None) == 1
+    assert fwd_causal(lib, q=None, k=None, v=None, o=None, N=0) == 0  # no tokens: empty tensors may be NULL
     assert fwd_causal(lib, o=A + 1) == 1                     # misaligned
     assert fwd_causal(lib, o=A) == 1                         # o overlaps q
     assert fwd_causal(lib, d=96) == 2
@@ -106,6 +109,15 @@ def test_forward_causal_validation(lib):
     assert fwd_causal(lib, B=0) == 0                         # nothing to do, no launch
     assert fwd_causal(lib, saved=A + 0x5000000, saved_bytes=8, wsb=1 << 30) == 1       # saved state too small
     assert fwd_causal(lib, saved=A + 0x3000000, saved_bytes=1 << 20, wsb=1 << 30) == 1  # saved state overlaps o
+    # start state: may be the final-state buffer itself, nothing else; not with a saved state
+    S, z = A + 0x6000000, A + 0x6100000
+    assert fwd_causal(lib, S0=S, z0=z, saved=A + 0x5000000, saved_bytes=1 << 30, wsb=1 << 30) == 1
+    assert fwd_causal(lib, S0=A + 0x3000000, wsb=1 << 30) == 1                  # S0 overlaps o
+    assert fwd_causal(lib, S0=S, S=S + 64, z=z, wsb=1 << 30) == 1               # S0 overlaps S_out partially
+    assert fwd_causal(lib, S0=S + 4, wsb=1 << 30) == 1                          # S0 misaligned
+    assert fwd_causal(lib, S0=S, z0=S + 256, wsb=1 << 30) == 1                  # S0 and z0 overlap
+    # in place passes the pointer checks (and then stops at the too-small workspace, before any launch)
+    assert fwd_causal(lib, S0=S, z0=z, S=S, z=z, wsb=16) == 3
     msg = lib.la_last_error_message()
     assert isinstance(msg, bytes)
 
@@ -130,6 +142,19 @@ def test_forward_noncausal_and_backward_validation(lib):
     assert b(*bad, None, 0, 1, 1, 64, 64, 0, 1, A + 0x7000000, 1 << 30, None) == 1
     assert b(*args, A + 0x8000000, 4, 1, 1, 64, 64, 0, 1, A + 0x7000000, 1 << 30, None) == 1  # saved state short
     assert b(*args, A + 0x4000000, 1 << 20, 1, 1, 64, 64, 0, 1, A + 0x7000000, 1 << 30, None) == 1  # overlaps dq
+
+
+def test_decode_steps_validation(lib):
+    f = lib.la_decode_steps
+    S, z, q, k, v, o = A, A + 0x1000000, A + 0x2000000, A + 0x2100000, A + 0x2200000, A + 0x2300000
+    assert f(None, z, q, k, v, o, 1, 1, 8, 64, 1, None) == 1
+    assert f(S, z, q, k, v, q, 1, 1, 8, 64, 1, None) == 1     # o aliases q
+    assert f(S, z, q, k, v, o, 1, 1, 8, 96, 1, None) == 2     # d unsupported
+    assert f(S, z, q, k, v, o, 1, 1, -1, 64, 1, None) == 1    # negative T
+    assert f(S, z, q, k, v, o, 1, 1, 0, 64, 1, None) == 0     # no tokens: nothing to do
+    assert f(S, z, None, None, None, None, 1, 1, 0, 64, 1, None) == 0  # ... and the empty tensors may be NULL
+    assert f(S, None, None, None, None, None, 1, 1, 0, 64, 1, None) == 1  # the state may not
+    assert f(S, z, q, k, v, o, 0, 3, 8, 64, 1, None) == 0     # no heads
 
 
 def test_decode_validation(lib):

@@ -1,0 +1,138 @@
+"""GPU parity of the stateful calls against the fp64 oracle: the causal forward
+started from a given state (a long prefill in pieces) and multi-token decode.
+
+Start states are what real prefixes leave behind: the oracle's state after a
+seeded prefix of tokens (la_inputs), rounded to fp32 and handed to both sides.
+Metric and tolerances as in test_parity.py.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import la_inputs as inp  # noqa: E402
+from test_parity import DEN_TOL, STATE_TOL, TOL, draw, f64, record, slice_err  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def la():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_attention_02_amd as m
+    m.load_library()
+    return m
+
+
+def start_state(oracle, B, H, d, dtype, seed, npre=130):
+    """The oracle's state after npre seeded prefix tokens, as fp32 host tensors."""
+    pq, pk, pv = inp.qkv(B, H, npre, d, dtype, seed=seed, scale=dtype == torch.bfloat16)
+    _, S, z = oracle.forward_causal(f64(pq), f64(pk), f64(pv), return_state=True)
+    return torch.from_numpy(S).float(), torch.from_numpy(z).float()
+
+
+SHAPES = [(1, 1, 1, 32), (1, 2, 63, 64), (2, 3, 200, 64), (1, 2, 300, 128), (2, 2, 1000, 64),
+          (1, 2, 257, 32), (1, 8, 64 * 130 + 17, 64)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_forward_causal_from_state(la, oracle, shape, dtype):
+    B, H, N, d = shape
+    if dtype == torch.float32 and d == 128:
+        pytest.skip("fp32 causal path is built for d <= 64")
+    S0, z0 = start_state(oracle, B, H, d, dtype, seed=N + 11)
+    q, k, v, _ = draw(B, H, N, d, dtype, seed=N + 12)
+    o, den, S, z = la.la_forward_causal(q, k, v, return_den=True, return_state=True, S0=S0.cuda(), z0=z0.cuda())
+    torch.cuda.synchronize()
+    ro, rden, rS, rz = oracle.forward_causal(f64(q), f64(k), f64(v), return_den=True, return_state=True,
+                                             S0=f64(S0), z0=f64(z0))
+    errs = {"o": slice_err(o, ro), "den": slice_err(den, rden), "S": slice_err(S, rS),
+            "z": slice_err(z[..., None], rz[..., None])}
+    record(f"fwd_causal_from_state {B}x{H}x{N}x{d} {dtype}", **errs)
+    assert errs["o"] < TOL[dtype], errs
+    assert errs["den"] < DEN_TOL[dtype], errs
+    assert max(errs["S"], errs["z"]) < min(TOL[dtype], STATE_TOL), errs
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_prefill_in_pieces_in_place(la, oracle, dtype):
+    """A sequence fed in three pieces, each continuing in place from the state the last
+    one left (S_out = S0), matches the oracle's single pass over the whole sequence."""
+    B, H, N, d = 2, 2, 900, 64
+    q, k, v, _ = draw(B, H, N, d, dtype, seed=21)
+    cuts = [0, 130, 513, N]
+    S = torch.empty(B, H, d, d, device="cuda")
+    z = torch.empty(B, H, d, device="cuda")
+    outs = []
+    for i in range(3):
+        a, b = cuts[i], cuts[i + 1]
+        qs, ks, vs = (t[:, :, a:b].contiguous() for t in (q, k, v))
+        if i == 0:
+            outs.append(la.la_forward_causal(qs, ks, vs, return_state=True, S_out=S, z_out=z)[0])
+        else:
+            outs.append(la.la_forward_causal(qs, ks, vs, return_state=True, S0=S, z0=z, S_out=S, z_out=z)[0])
+    torch.cuda.synchronize()
+    ro, rS, rz = oracle.forward_causal(f64(q), f64(k), f64(v), return_state=True)
+    errs = {"o": slice_err(torch.cat(outs, dim=2), ro), "S": slice_err(S, rS), "z": slice_err(z[..., None], rz[..., None])}
+    record(f"prefill in pieces {dtype}", **errs)
+    assert errs["o"] < TOL[dtype] and max(errs["S"], errs["z"]) < min(TOL[dtype], STATE_TOL), errs
+
+
+def test_forward_from_state_without_tokens(la, oracle):
+    """N = 0: the final state is the start state; z0 alone (S0 = NULL) leaves S = 0."""
+    B, H, d = 2, 3, 64
+    S0, z0 = start_state(oracle, B, H, d, torch.bfloat16, seed=5)
+    S0, z0 = S0.cuda(), z0.cuda()
+    q = torch.empty(B, H, 0, d, dtype=torch.bfloat16, device="cuda")
+    _, S, z = la.la_forward_causal(q, q, q, return_state=True, S0=S0, z0=z0)
+    _, S2, z2 = la.la_forward_causal(q, q, q, return_state=True, z0=z0)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S0) and torch.equal(z, z0)
+    assert torch.equal(S2, torch.zeros_like(S0)) and torch.equal(z2, z0)
+
+
+def test_start_state_rejected_with_saved_state(la):
+    q, k, v, _ = draw(1, 1, 64, 64, torch.bfloat16, seed=3)
+    S0 = torch.zeros(1, 1, 64, 64, device="cuda")
+    with pytest.raises(la.LinAttnError):
+        la.la_forward_causal(q, k, v, S0=S0, saved_state=la.new_saved_state(q))
+
+
+# ---- multi-token decode ----------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("T", [1, 7, 16, 37])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_decode_steps(la, oracle, d, T, dtype):
+    B, H = 2, 3
+    S0, z0 = start_state(oracle, B, H, d, dtype, seed=d + T)
+    q, k, v = inp.qkv(B, H, T, d, dtype, seed=d * T + 1, scale=True)
+    S, z = S0.cuda(), z0.cuda()
+    o = la.la_decode_steps(S, z, q.cuda(), k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    rS, rz = f64(S0), f64(z0)
+    worst = 0.0
+    for t in range(T):
+        ro, rS, rz = oracle.decode_step(rS, rz, f64(q[:, :, t]), f64(k[:, :, t]), f64(v[:, :, t]))
+        worst = max(worst, slice_err(o[:, :, t][..., None], ro[..., None]))
+    errs = {"o": worst, "S": slice_err(S, rS), "z": slice_err(z[..., None], rz[..., None])}
+    record(f"decode_steps d={d} T={T} {dtype}", **errs)
+    assert errs["o"] < TOL[dtype], errs
+    assert max(errs["S"], errs["z"]) < 1e-5, errs
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_steps_match_single_steps(la, oracle, d):
+    """One call of T steps and T calls of one step update the fp32 state identically up
+    to rounding, and give the same outputs to within the reduction order."""
+    B, H, T = 3, 4, 19
+    S0, z0 = start_state(oracle, B, H, d, torch.bfloat16, seed=d)
+    q, k, v = (t.cuda() for t in inp.qkv(B, H, T, d, torch.bfloat16, seed=d + 2, scale=True))
+    S1, z1 = S0.cuda(), z0.cuda()
+    S2, z2 = S0.cuda(), z0.cuda()
+    o1 = la.la_decode_steps(S1, z1, q, k, v)
+    o2 = torch.stack([la.la_decode_step(S2, z2, q[:, :, t].contiguous(), k[:, :, t].contiguous(),
+                                        v[:, :, t].contiguous()) for t in range(T)], dim=2)
+    torch.cuda.synchronize()
+    assert torch.allclose(S1, S2, rtol=1e-6, atol=1e-6) and torch.allclose(z1, z2, rtol=1e-6, atol=1e-6)
+    assert slice_err(o1.float(), f64(o2.float())) < 2.0 ** -8
