@@ -25,8 +25,10 @@ The JSON line also carries
   * step_roofline: the same for the whole step (22 d bytes per token-head);
   * calls       : the other measured calls (non-causal forward, and non-causal
                   forward + backward, at the same size; the long and very-long
-                  causal workloads; 512 decode steps one per call, and 16 per
-                  call), each with its throughput and roofline fraction;
+                  causal workloads; 512 decode steps one per call, 16 per
+                  call, and 16 per call with 32 query heads on 4 shared
+                  key/value states), each with its throughput and roofline
+                  fraction;
   * cpu_baseline: the fp64 CPU oracle timed on this host on repeated full
                   steps of the same workload (bounded to about 10 s).
 
@@ -372,6 +374,27 @@ def bench_calls(args, la, inp, torch, mid_sets):
     r["us_per_token_step"] = round(r["ms"] * 1e3 / (calls_n * TPC), 2)
     r["alg_bytes_per_call"] = call_bytes
     calls[f"decode_512_steps_{TPC}_per_call"] = r
+
+    # Grouped heads: the same 32 query heads per sequence read 4 shared key/value states
+    # (8 query heads per state), so a call moves a quarter of the state bytes.
+    HKV = 4
+    Sg = S[:, :HKV].contiguous()
+    zg = z[:, :HKV].contiguous()
+    gblocks = [(bq, bk[:, :HKV].contiguous(), bv[:, :HKV].contiguous()) for bq, bk, bv in blocks]
+
+    def span_grouped(i):
+        for c in range(calls_n):
+            bq, bk, bv = gblocks[c]
+            la.la_decode_steps(Sg, zg, bq, bk, bv, out=ob)
+
+    gcall_bytes = B * (HKV * (2 * 4 * d * d + 2 * 4 * d + TPC * 2 * 2 * d) + H * TPC * 2 * 2 * d)
+    r = bench_call("decode_steps_gqa", span_grouped, 1, 3, B * calls_n * TPC, gcall_bytes * calls_n, la, torch)
+    r["tokens_per_call"] = TPC
+    r["kv_heads"] = HKV
+    r["us_per_call"] = round(r["ms"] * 1e3 / calls_n, 2)
+    r["us_per_token_step"] = round(r["ms"] * 1e3 / (calls_n * TPC), 2)
+    r["alg_bytes_per_call"] = gcall_bytes
+    calls[f"decode_512_steps_{TPC}_per_call_{H}q_{HKV}kv"] = r
     return calls
 
 

@@ -155,15 +155,20 @@ la_status la_backward_noncausal(const void* q, const void* k, const void* v, con
 la_status la_decode_step(float* S, float* z, const void* q, const void* k, const void* v, void* o,
                          int64_t B, int64_t H, int64_t d, la_dtype dt, void* stream);
 
-/* T recurrent decode steps per (b, h) in one call, in place ("Why It Matters":
- * tokens one by one): for t = 0 .. T-1, S += phi(k_t) v_t^T, z += phi(k_t), then
- * o_t = phi(q_t)^T S / phi(q_t)^T z.  The same results as T calls of
- * la_decode_step up to fp32 rounding, with the state read and written once per
- * call instead of once per token.  S [B][H][d][d] and z [B][H][d] are fp32 and
- * updated in place; q, k, v, o are [B][H][T][d] in dtype dt (token t of head
- * (b, h) at row t).  T = 0 does nothing.  Needs no workspace. */
+/* T recurrent decode steps in one call, in place ("Why It Matters": tokens one
+ * by one), with H query heads sharing Hkv key/value heads (H a multiple of Hkv;
+ * Hkv = H: one state per head; Hkv = 1: one state for all query heads).  Query
+ * head h reads the state of key/value head h / (H / Hkv).  Per key/value head
+ * (b, j) and token t = 0 .. T-1: S += phi(k_t) v_t^T, z += phi(k_t), then for
+ * each query head h of the group o_{h,t} = phi(q_{h,t})^T S / phi(q_{h,t})^T z.
+ * With Hkv = H this is T calls of la_decode_step up to fp32 rounding.  The state
+ * is read and written once per call (not once per token) and once per group
+ * (not once per query head).  S [B][Hkv][d][d] and z [B][Hkv][d] are fp32 and
+ * updated in place; q, o are [B][H][T][d] and k, v [B][Hkv][T][d] in dtype dt
+ * (token t at row t).  T = 0 does nothing.  Needs no workspace. */
 la_status la_decode_steps(float* S, float* z, const void* q, const void* k, const void* v, void* o,
-                          int64_t B, int64_t H, int64_t T, int64_t d, la_dtype dt, void* stream);
+                          int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t d, la_dtype dt,
+                          void* stream);
 
 /* Static description of a status code. */
 const char* la_status_string(la_status s);

@@ -62,7 +62,7 @@ def load_library(path: str | None = None):
     lib.la_decode_step.restype = i32
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.la_decode_steps.restype = i32
-    lib.la_decode_steps.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
+    lib.la_decode_steps.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
     lib.la_status_string.restype = ctypes.c_char_p
     lib.la_status_string.argtypes = [i32]
     lib.la_last_error_message.restype = ctypes.c_char_p
@@ -264,23 +264,28 @@ def la_decode_step(S, z, q, k, v, *, out=None):
 
 
 def la_decode_steps(S, z, q, k, v, *, out=None):
-    """T in-place recurrent steps per head in one call; returns o [B, H, T, d].
+    """T in-place recurrent steps per key/value head in one call; returns o [B, H, T, d].
 
-    S: [B, H, d, d] fp32, z: [B, H, d] fp32, q/k/v: [B, H, T, d] bf16 or fp32 (token t at row t)."""
-    if q.dim() != 4:
-        raise ValueError("q, k, v must be [B, H, T, d]")
+    q: [B, H, T, d]; k, v: [B, Hkv, T, d] with H a multiple of Hkv (query head h reads the
+    state of key/value head h // (H // Hkv)); S: [B, Hkv, d, d] fp32, z: [B, Hkv, d] fp32;
+    bf16 or fp32 tokens (token t at row t)."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, T, d] and k, v [B, Hkv, T, d]")
     B, H, T, d = q.shape
-    for t in (k, v):
-        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
-            raise ValueError("q, k, v must share shape, dtype and device and be contiguous")
-    if not q.is_contiguous() or not q.is_cuda:
-        raise ValueError("q, k, v must be contiguous tensors on a HIP device")
-    if S.shape != (B, H, d, d) or z.shape != (B, H, d) or S.dtype != torch.float32 or z.dtype != torch.float32:
-        raise ValueError("S must be [B, H, d, d] fp32 and z [B, H, d] fp32")
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, T, d) or v.shape != k.shape or Hkv == 0 or H % Hkv:
+        raise ValueError("k, v must be [B, Hkv, T, d] with H a multiple of Hkv")
+    for t in (q, k, v):
+        if t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
+            raise ValueError("q, k, v must share dtype and device and be contiguous")
+    if not q.is_cuda:
+        raise ValueError("tensors must be on a HIP device")
+    if S.shape != (B, Hkv, d, d) or z.shape != (B, Hkv, d) or S.dtype != torch.float32 or z.dtype != torch.float32:
+        raise ValueError("S must be [B, Hkv, d, d] fp32 and z [B, Hkv, d] fp32")
     if not (S.is_contiguous() and z.is_contiguous()):
         raise ValueError("S and z must be contiguous")
     o = torch.empty_like(q) if out is None else out
-    _check(load_library().la_decode_steps(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, T, d,
+    _check(load_library().la_decode_steps(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Hkv, T, d,
                                           _dtype_code(q.dtype), _stream(q.device)))
     return o
 

@@ -560,29 +560,33 @@ la_status la_decode_step(float* S, float* z, const void* q, const void* k, const
 }
 
 la_status la_decode_steps(float* S, float* z, const void* q, const void* k, const void* v, void* o, int64_t B,
-                          int64_t H, int64_t T, int64_t d, la_dtype dt, void* stream) {
+                          int64_t H, int64_t Hkv, int64_t T, int64_t d, la_dtype dt, void* stream) {
     if (dt != LA_F32 && dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "dtype %d is not LA_F32 or LA_BF16", (int)dt);
     if (d != 32 && d != 64 && d != 128) return fail(LA_ERR_UNSUPPORTED, "d = %lld; built for 32, 64 and 128", (long long)d);
-    if (B < 0 || H < 0 || T < 0)
-        return fail(LA_ERR_INVALID_ARGUMENT, "negative size (B=%lld H=%lld T=%lld)", (long long)B, (long long)H,
-                    (long long)T);
+    if (B < 0 || H < 0 || Hkv < 0 || T < 0)
+        return fail(LA_ERR_INVALID_ARGUMENT, "negative size (B=%lld H=%lld Hkv=%lld T=%lld)", (long long)B, (long long)H,
+                    (long long)Hkv, (long long)T);
+    if ((Hkv == 0) != (H == 0) || (Hkv > 0 && H % Hkv != 0))
+        return fail(LA_ERR_INVALID_ARGUMENT, "H = %lld query heads must be a multiple of Hkv = %lld", (long long)H,
+                    (long long)Hkv);
     if (B > 0 && H > ((int64_t)1 << 24) / B) return fail(LA_ERR_UNSUPPORTED, "B*H exceeds 2^24 heads");
     if (T > ((int64_t)1 << 24)) return fail(LA_ERR_UNSUPPORTED, "T = %lld exceeds 2^24 tokens per call", (long long)T);
     if (!S || !z) return fail(LA_ERR_INVALID_ARGUMENT, "S and z must be non-NULL");
     // Empty token tensors (T = 0) may come as NULL pointers.
     if (T > 0 && (!q || !k || !v || !o)) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-NULL");
-    const int64_t BH = B * H;
-    const size_t tb = (size_t)BH * T * d * elem_size(dt);
-    const Range in[] = {{"q", q, tb}, {"k", k, tb}, {"v", v, tb}};
-    const Range out[] = {{"S", S, (size_t)BH * d * d * sizeof(float)},
-                         {"z", z, (size_t)BH * d * sizeof(float)},
-                         {"o", o, tb}};
+    const int64_t BHkv = B * Hkv;
+    const size_t qb = (size_t)B * H * T * d * elem_size(dt), kb = (size_t)BHkv * T * d * elem_size(dt);
+    const Range in[] = {{"q", q, qb}, {"k", k, kb}, {"v", v, kb}};
+    const Range out[] = {{"S", S, (size_t)BHkv * d * d * sizeof(float)},
+                         {"z", z, (size_t)BHkv * d * sizeof(float)},
+                         {"o", o, qb}};
     la_status st = check_ptrs(in, 3, out, 3);
     if (st != LA_OK) return st;
-    if (BH == 0 || T == 0) return LA_OK;
+    if (BHkv == 0 || T == 0) return LA_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = timed("decode_steps", s, [&] {
-        return la::launch_decode_steps(dt == LA_BF16 ? la::kBF16 : la::kF32, (int)d, S, z, q, k, v, o, BH, T, s);
+        return la::launch_decode_steps(dt == LA_BF16 ? la::kBF16 : la::kF32, (int)d, S, z, q, k, v, o, BHkv, T, H / Hkv,
+                                       s);
     });
     if (e != hipSuccess) return hip_fail(e, "decode_steps launch");
     return LA_OK;

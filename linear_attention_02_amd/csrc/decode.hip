@@ -78,109 +78,124 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(float* __restrict__ S, f
 }
 
 // ---------------------------------------------------------------------------------------
-// decode_steps: T recurrent steps per (b, h) in one pass over the state.  The
-// same per-token update and read as decode_kernel, with the d x d state held in
-// registers across the tokens (thread (rg, cq) owns columns 4 cq .. 4 cq + 3 of
-// rows rg + RPP p), so the state moves through HBM once per call instead of once
-// per token.  Tokens go in blocks of TB: phi(q), phi(k) and v of a block are
-// staged in LDS; per token each thread updates its state entries and forms its
-// part of phi(q)^T S, reduced over the row groups with shuffles inside a
-// wavefront and through LDS across the four.
+// decode_steps: T recurrent steps per (b, key/value head) in one pass over the
+// state, for G = H / Hkv query heads sharing that head's state (G = 1: one state
+// per query head).  Per token t: S += phi(k_t) v_t^T, z += phi(k_t) once, then
+// each of the G query heads reads o = phi(q)^T S / phi(q)^T z.  The d x d state is
+// held in registers across the call (thread (rg, cq) owns columns 4 cq .. 4 cq + 3
+// of rows rg + RPP p), so it moves through HBM once per call instead of once per
+// token, and once per group instead of once per query head.
+// Work goes in rows (t, h), token-major: a block of RB rows stages phi(q) of each
+// row and, on the row that opens a token (h = 0), phi(k) and v of that token
+// (zeros elsewhere, so z sums each token once); per row each thread applies the
+// token's rank-1 update where the row opens one, then forms its part of
+// phi(q)^T S, reduced over the row groups with shuffles inside a wavefront and
+// through LDS across the four.
 template <typename T, int D>
 __global__ __launch_bounds__(kBlock) void decode_steps_kernel(float* __restrict__ S, float* __restrict__ z,
                                                               const T* __restrict__ q, const T* __restrict__ k,
-                                                              const T* __restrict__ v, T* __restrict__ o, int ntok) {
+                                                              const T* __restrict__ v, T* __restrict__ o, int ntok,
+                                                              int G) {
     constexpr int F4 = D / 4;         // float4 per state row
     constexpr int RPP = kBlock / F4;  // rows per pass
     constexpr int NP = D / RPP;       // passes
     constexpr int NW = kBlock / kWave;
-    constexpr int TB = D <= 64 ? 16 : 8;  // tokens per block
+    constexpr int RB = D <= 64 ? 16 : 8;  // (token, query head) rows per block
     static_assert(kBlock % F4 == 0 && D % RPP == 0 && F4 <= kWave, "state rows must tile the workgroup");
-    __shared__ __attribute__((aligned(16))) float s_qf[TB][D], s_kf[TB][D], s_v[TB][D];
-    __shared__ __attribute__((aligned(16))) float s_red[TB][NW][D];
-    __shared__ float s_den[TB][NW];
+    __shared__ __attribute__((aligned(16))) float s_qf[RB][D], s_kf[RB][D], s_v[RB][D];
+    __shared__ __attribute__((aligned(16))) float s_red[RB][NW][D];
+    __shared__ float s_den[RB][NW];
 
-    const int bh = blockIdx.x;
+    const int kvh = blockIdx.x;  // flat (b, key/value head)
     const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
     const int rg = tid / F4, cq = tid % F4;
-    f32x4* Sh = reinterpret_cast<f32x4*>(S + (int64_t)bh * D * D);
-    const int64_t tok0 = (int64_t)bh * ntok;  // first token row of this head in q, k, v, o
+    f32x4* Sh = reinterpret_cast<f32x4*>(S + (int64_t)kvh * D * D);
+    const int64_t krow0 = (int64_t)kvh * ntok;        // first token row of this head in k, v
+    const int64_t qrow0 = (int64_t)kvh * G * ntok;    // first row of the group's first query head in q, o
+    const int64_t nrows = (int64_t)G * ntok;
 
     f32x4 x[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) x[p] = Sh[(rg + RPP * p) * F4 + cq];
-    float zn = tid < D ? z[(int64_t)bh * D + tid] : 0.f;
+    float zn = tid < D ? z[(int64_t)kvh * D + tid] : 0.f;
 
-    for (int t0 = 0; t0 < ntok; t0 += TB) {
-        const int nb = min(TB, ntok - t0);
-        // Stage the block (tokens past the end: phi(k) = 0, v = 0, so they change nothing).
-        for (int i = tid; i < TB * D; i += kBlock) {
-            const int t = i / D, a = i % D;
+    for (int64_t r0 = 0; r0 < nrows; r0 += RB) {
+        const int nb = (int)min((int64_t)RB, nrows - r0);
+        // Stage the block: row i is token t = (r0 + i) / G of query head h = (r0 + i) % G.
+        // Rows past the end and rows that do not open a token carry phi(k) = 0, v = 0.
+        for (int i = tid; i < RB * D; i += kBlock) {
+            const int ri = i / D, a = i % D;
             float qf = 1.f, kf = 0.f, vv = 0.f;
-            if (t < nb) {
-                const int64_t off = (tok0 + t0 + t) * D + a;
-                qf = phi_f(to_f32(q[off]));
-                kf = phi_f(to_f32(k[off]));
-                vv = to_f32(v[off]);
+            if (ri < nb) {
+                const int64_t r = r0 + ri;
+                const int64_t t = r / G, h = r % G;
+                qf = phi_f(to_f32(q[(qrow0 + h * ntok + t) * D + a]));
+                if (h == 0) {
+                    kf = phi_f(to_f32(k[(krow0 + t) * D + a]));
+                    vv = to_f32(v[(krow0 + t) * D + a]);
+                }
             }
-            s_qf[t][a] = qf;
-            s_kf[t][a] = kf;
-            s_v[t][a] = vv;
+            s_qf[ri][a] = qf;
+            s_kf[ri][a] = kf;
+            s_v[ri][a] = vv;
         }
         __syncthreads();
-        // z and each token's denominator phi(q_t)^T z_t (feature a = tid).
+        // z and each row's denominator phi(q)^T z (feature a = tid).
 #pragma unroll
-        for (int t = 0; t < TB; ++t) {
+        for (int i = 0; i < RB; ++i) {
             float dp = 0.f;
             if (tid < D) {
-                zn += s_kf[t][tid];
-                dp = s_qf[t][tid] * zn;
+                zn += s_kf[i][tid];
+                dp = s_qf[i][tid] * zn;
             }
             dp = sum_lanes<kWave>(dp);
-            if (lane == 0) s_den[t][w] = dp;
+            if (lane == 0) s_den[i][w] = dp;
         }
-        // State update and phi(q_t)^T S_t, token by token.
+        // Rank-1 update where a row opens a token, then phi(q)^T S, row by row.
 #pragma unroll
-        for (int t = 0; t < TB; ++t) {
-            const f32x4 v4 = *reinterpret_cast<const f32x4*>(&s_v[t][4 * cq]);
+        for (int i = 0; i < RB; ++i) {
+            const bool opens = i < nb && (r0 + i) % G == 0;  // uniform over the workgroup
+            if (opens) {
+                const f32x4 v4 = *reinterpret_cast<const f32x4*>(&s_v[i][4 * cq]);
+#pragma unroll
+                for (int p = 0; p < NP; ++p) x[p] += s_kf[i][rg + RPP * p] * v4;
+            }
             f32x4 acc = zero4();
 #pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                const int a = rg + RPP * p;
-                x[p] += s_kf[t][a] * v4;
-                acc += s_qf[t][a] * x[p];
-            }
+            for (int p = 0; p < NP; ++p) acc += s_qf[i][rg + RPP * p] * x[p];
 #pragma unroll
             for (int off = F4; off < kWave; off <<= 1) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off, kWave);
             }
-            if (lane < F4) *reinterpret_cast<f32x4*>(&s_red[t][w][4 * cq]) = acc;
+            if (lane < F4) *reinterpret_cast<f32x4*>(&s_red[i][w][4 * cq]) = acc;
         }
         __syncthreads();
         for (int i = tid; i < nb * D; i += kBlock) {
-            const int t = i / D, b = i % D;
+            const int ri = i / D, b = i % D;
+            const int64_t r = r0 + ri;
+            const int64_t t = r / G, h = r % G;
             float num = 0.f, den = 0.f;
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) {
-                num += s_red[t][ww][b];
-                den += s_den[t][ww];
+                num += s_red[ri][ww][b];
+                den += s_den[ri][ww];
             }
-            o[(tok0 + t0 + t) * D + b] = from_f32<T>(num / den);
+            o[(qrow0 + h * ntok + t) * D + b] = from_f32<T>(num / den);
         }
         __syncthreads();  // the block's LDS is free for the next one
     }
 #pragma unroll
     for (int p = 0; p < NP; ++p) Sh[(rg + RPP * p) * F4 + cq] = x[p];
-    if (tid < D) z[(int64_t)bh * D + tid] = zn;
+    if (tid < D) z[(int64_t)kvh * D + tid] = zn;
 }
 
 hipError_t launch_decode_steps(int dt, int d, float* S, float* z, const void* q, const void* k, const void* v,
-                               void* o, int64_t BH, int64_t T, hipStream_t s) {
-    const dim3 grid((unsigned)BH);
+                               void* o, int64_t BHkv, int64_t T, int64_t G, hipStream_t s) {
+    const dim3 grid((unsigned)BHkv);
 #define LA_DECS(TT, DD)                                                                                     \
     hipLaunchKernelGGL((decode_steps_kernel<TT, DD>), grid, dim3(kBlock), 0, s, S, z, (const TT*)q,         \
-                       (const TT*)k, (const TT*)v, (TT*)o, (int)T)
+                       (const TT*)k, (const TT*)v, (TT*)o, (int)T, (int)G)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_DECS(bf16, 32); break;

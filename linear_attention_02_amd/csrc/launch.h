@@ -107,8 +107,9 @@ hipError_t launch_copy_or_zero(float* p, const float* src, size_t n, hipStream_t
 // Decode.
 hipError_t launch_decode(int dt, int d, float* S, float* z, const void* q, const void* k,
                          const void* v, void* o, int64_t BH, hipStream_t s);
-// T decode steps per head in one pass over the state; q, k, v, o are [BH][T][d].
+// T decode steps per key/value head in one pass over its state, read by G query heads;
+// k, v are [BHkv][T][d], q, o are [BHkv][G][T][d].
 hipError_t launch_decode_steps(int dt, int d, float* S, float* z, const void* q, const void* k,
-                               const void* v, void* o, int64_t BH, int64_t T, hipStream_t s);
+                               const void* v, void* o, int64_t BHkv, int64_t T, int64_t G, hipStream_t s);
 
 }  // namespace la

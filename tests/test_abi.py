@@ -147,14 +147,19 @@ def test_forward_noncausal_and_backward_validation(lib):
 def test_decode_steps_validation(lib):
     f = lib.la_decode_steps
     S, z, q, k, v, o = A, A + 0x1000000, A + 0x2000000, A + 0x2100000, A + 0x2200000, A + 0x2300000
-    assert f(None, z, q, k, v, o, 1, 1, 8, 64, 1, None) == 1
-    assert f(S, z, q, k, v, q, 1, 1, 8, 64, 1, None) == 1     # o aliases q
-    assert f(S, z, q, k, v, o, 1, 1, 8, 96, 1, None) == 2     # d unsupported
-    assert f(S, z, q, k, v, o, 1, 1, -1, 64, 1, None) == 1    # negative T
-    assert f(S, z, q, k, v, o, 1, 1, 0, 64, 1, None) == 0     # no tokens: nothing to do
-    assert f(S, z, None, None, None, None, 1, 1, 0, 64, 1, None) == 0  # ... and the empty tensors may be NULL
-    assert f(S, None, None, None, None, None, 1, 1, 0, 64, 1, None) == 1  # the state may not
-    assert f(S, z, q, k, v, o, 0, 3, 8, 64, 1, None) == 0     # no heads
+    assert f(None, z, q, k, v, o, 1, 1, 1, 8, 64, 1, None) == 1
+    assert f(S, z, q, k, v, q, 1, 1, 1, 8, 64, 1, None) == 1     # o aliases q
+    assert f(S, z, q, k, v, o, 1, 1, 1, 8, 96, 1, None) == 2     # d unsupported
+    assert f(S, z, q, k, v, o, 1, 1, 1, -1, 64, 1, None) == 1    # negative T
+    assert f(S, z, q, k, v, o, 1, 6, 4, 8, 64, 1, None) == 1     # H not a multiple of Hkv
+    assert f(S, z, q, k, v, o, 1, 6, 0, 8, 64, 1, None) == 1     # no key/value heads for 6 query heads
+    assert f(S, z, q, k, v, o, 1, 1, 1, 0, 64, 1, None) == 0     # no tokens: nothing to do
+    assert f(S, z, None, None, None, None, 1, 1, 1, 0, 64, 1, None) == 0  # ... and the empty tensors may be NULL
+    assert f(S, None, None, None, None, None, 1, 1, 1, 0, 64, 1, None) == 1  # the state may not
+    assert f(S, z, q, k, v, o, 0, 3, 3, 8, 64, 1, None) == 0     # no heads
+    # the state is sized by the key/value heads: 8 query heads on 2 states of 64 x 64 fp32
+    assert f(S, S + 2 * 64 * 64 * 4 - 16, q, k, v, o, 1, 8, 2, 8, 64, 1, None) == 1  # z overlaps S
+    assert f(S, S + 2 * 64 * 64 * 4, q, k, v, o, 1, 8, 2, 0, 64, 1, None) == 0
 
 
 def test_decode_validation(lib):

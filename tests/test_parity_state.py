@@ -136,3 +136,32 @@ def test_decode_steps_match_single_steps(la, oracle, d):
     torch.cuda.synchronize()
     assert torch.allclose(S1, S2, rtol=1e-6, atol=1e-6) and torch.allclose(z1, z2, rtol=1e-6, atol=1e-6)
     assert slice_err(o1.float(), f64(o2.float())) < 2.0 ** -8
+
+
+# ---- shared key/value heads (GQA / MQA) ------------------------------------------------------
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("heads", [(8, 2), (6, 1), (3, 3), (32, 1)], ids=lambda h: f"H{h[0]}kv{h[1]}")
+@pytest.mark.parametrize("T", [1, 5, 19])
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_steps_shared_state(la, oracle, d, T, heads, dtype):
+    """Each query head continues the causal recurrence of its key/value head from the
+    shared start state: the oracle runs that recurrence per query head."""
+    H, Hkv = heads
+    B, G = 2, H // Hkv
+    S0, z0 = start_state(oracle, B, Hkv, d, dtype, seed=7 * d + T)
+    q = inp.qkv(B, H, T, d, dtype, seed=d + 31 * T, scale=True)[0]
+    _, k, v = inp.qkv(B, Hkv, T, d, dtype, seed=d + 37 * T, scale=True)
+    S, z = S0.cuda(), z0.cuda()
+    o = la.la_decode_steps(S, z, q.cuda(), k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    worst, rS, rz = 0.0, [None] * Hkv, [None] * Hkv
+    for h in range(H):
+        j = h // G
+        ro, rS[j], rz[j] = oracle.forward_causal(f64(q[:, h]), f64(k[:, j]), f64(v[:, j]), return_state=True,
+                                                 S0=f64(S0[:, j]), z0=f64(z0[:, j]))
+        worst = max(worst, slice_err(o[:, h], ro))
+    rS, rz = np.stack(rS, axis=1), np.stack(rz, axis=1)
+    errs = {"o": worst, "S": slice_err(S, rS), "z": slice_err(z[..., None], rz[..., None])}
+    record(f"decode_steps H={H} Hkv={Hkv} d={d} T={T} {dtype}", **errs)
+    assert errs["o"] < TOL[dtype], errs
+    assert max(errs["S"], errs["z"]) < 1e-5, errs
