@@ -60,6 +60,10 @@ def _load():
         f.argtypes = [i64, i64, i64, dp, dp, dp, dp, dp, dp, dp]
     lib.la_oracle_forward_causal_from.restype = None
     lib.la_oracle_forward_causal_from.argtypes = [i64, i64, i64, dp, dp, dp, dp, dp, dp, dp, dp, dp]
+    lib.la_oracle_favor_features.restype = None
+    lib.la_oracle_favor_features.argtypes = [i64, i64, i64, dp, dp, dp]
+    lib.la_oracle_forward_features.restype = None
+    lib.la_oracle_forward_features.argtypes = [i64, i64, i64, i64, i32, dp, dp, dp, dp, dp, dp, dp]
     lib.la_oracle_decode_step.restype = None
     lib.la_oracle_decode_step.argtypes = [i64, i64, dp, dp, dp, dp, dp, dp]
     lib.la_oracle_quadratic_forward.restype = None
@@ -210,3 +214,37 @@ def quadratic_backward(q, k, v, dout, causal=True):
     _load().la_oracle_quadratic_backward(bh, n, d, int(bool(causal)), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                                          _ptr(dq), _ptr(dk), _ptr(dv))
     return dq, dk, dv
+
+
+def favor_features(x, omega):
+    """FAVOR+ features m^{-1/2} exp(omega x - |x|^2/2) of the rows of x [..., d]; omega [m, d]."""
+    x, omega = _f64(x), _f64(omega)
+    d = x.shape[-1]
+    if omega.ndim != 2 or omega.shape[1] != d:
+        raise ValueError("omega must be [m, d]")
+    m = omega.shape[0]
+    rows = int(np.prod(x.shape[:-1])) if x.ndim > 1 else 1
+    out = np.empty(x.shape[:-1] + (m,), dtype=np.float64)
+    _load().la_oracle_favor_features(rows, d, m, _ptr(x), _ptr(omega), _ptr(out))
+    return out
+
+
+def forward_features(fq, fk, v, causal, return_den=False, return_state=False):
+    """Linear attention on given features fq, fk [..., N, m] with values v [..., N, dv]."""
+    fq, fk, v = _f64(fq), _f64(fk), _f64(v)
+    if fq.shape != fk.shape or fq.shape[:-1] != v.shape[:-1]:
+        raise ValueError("fq, fk must match, and share [..., N] with v")
+    bh, n, m = _heads(fq)
+    dv = v.shape[-1]
+    o = np.empty(v.shape, dtype=np.float64)
+    den = np.empty(fq.shape[:-1], dtype=np.float64) if return_den else None
+    S = np.empty(fq.shape[:-2] + (m, dv), dtype=np.float64) if return_state else None
+    z = np.empty(fq.shape[:-2] + (m,), dtype=np.float64) if return_state else None
+    _load().la_oracle_forward_features(bh, n, m, dv, int(bool(causal)), _ptr(fq), _ptr(fk), _ptr(v), _ptr(o),
+                                       _ptr(den), _ptr(S), _ptr(z))
+    out = [o]
+    if return_den:
+        out.append(den)
+    if return_state:
+        out += [S, z]
+    return out[0] if len(out) == 1 else tuple(out)

@@ -385,3 +385,67 @@ void la_oracle_quadratic_backward(int64_t BH, int64_t N, int64_t d, int causal, 
     free(A);
     free(dA);
 }
+
+/* ---- FAVOR+ positive random features ------------------------------------------
+ * Page "Efficient Transformers Survey", section on Performer (FAVOR+):
+ *   phi(x) = m^{-1/2} exp(-|x|^2 / 2) [exp(w_1 . x), ..., exp(w_m . x)],
+ * w_i ~ N(0, I_d) given as the rows of omega [m][d]; x is taken as given (any
+ * 1/sqrt(d) scaling is the caller's pre-normalization). */
+void la_oracle_favor_features(int64_t rows, int64_t d, int64_t m, const double* x, const double* omega,
+                              double* out) {
+    const double c = 1.0 / sqrt((double)m);
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* xr = x + r * d;
+        double nrm = 0.0;
+        for (int64_t a = 0; a < d; ++a) nrm += xr[a] * xr[a];
+        for (int64_t i = 0; i < m; ++i) {
+            double u = 0.0;
+            for (int64_t a = 0; a < d; ++a) u += omega[i * d + a] * xr[a];
+            out[r * m + i] = c * exp(u - 0.5 * nrm);
+        }
+    }
+}
+
+/* ---- linear attention on given features ----------------------------------------
+ * The Statement of the linear-attention proposition with the feature map
+ * applied beforehand: fq = phi(Q) [N][m], fk = phi(K) [N][m], V [N][dv],
+ *   S = sum_j fk_j V_j^T (m x dv), z = sum_j fk_j, O_i = fq_i^T S / fq_i^T z,
+ * the sums over all j (causal == 0) or j <= i with the state updated before the
+ * read (causal != 0, the recurrent form of "Why It Matters"). */
+void la_oracle_forward_features(int64_t BH, int64_t N, int64_t m, int64_t dv, int causal,
+                                const double* fq, const double* fk, const double* v, double* o,
+                                double* den_out, double* S_out, double* z_out) {
+    int nt = la_oracle_get_threads();
+    (void)nt;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t h = 0; h < BH; ++h) {
+        const double* qh = fq + h * N * m;
+        const double* kh = fk + h * N * m;
+        const double* vh = v + h * N * dv;
+        double* oh = o + h * N * dv;
+        double* S = zalloc(m * dv);
+        double* z = zalloc(m);
+        int64_t added = 0; /* keys folded into (S, z) so far */
+        for (int64_t i = 0; i < N; ++i) {
+            const int64_t upto = causal ? i + 1 : N;
+            for (; added < upto; ++added) {
+                for (int64_t a = 0; a < m; ++a) {
+                    z[a] += kh[added * m + a];
+                    for (int64_t b = 0; b < dv; ++b) S[a * dv + b] += kh[added * m + a] * vh[added * dv + b];
+                }
+            }
+            double den = 0.0;
+            for (int64_t a = 0; a < m; ++a) den += qh[i * m + a] * z[a];
+            for (int64_t b = 0; b < dv; ++b) {
+                double num = 0.0;
+                for (int64_t a = 0; a < m; ++a) num += qh[i * m + a] * S[a * dv + b];
+                oh[i * dv + b] = num / den;
+            }
+            if (den_out) den_out[h * N + i] = den;
+        }
+        if (S_out) memcpy(S_out + h * m * dv, S, (size_t)(m * dv) * sizeof(double));
+        if (z_out) memcpy(z_out + h * m, z, (size_t)m * sizeof(double));
+        free(S);
+        free(z);
+    }
+}

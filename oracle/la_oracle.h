@@ -86,6 +86,19 @@ void la_oracle_quadratic_backward(int64_t BH, int64_t N, int64_t d, int causal,
                                   const double* q, const double* k, const double* v,
                                   const double* dout, double* dq, double* dk, double* dv);
 
+/* FAVOR+ positive random features (Performer section of the same page):
+ * out[r][i] = m^{-1/2} exp(omega_i . x_r - |x_r|^2 / 2) for rows x [rows][d] and
+ * omega [m][d] (one random direction per row). */
+void la_oracle_favor_features(int64_t rows, int64_t d, int64_t m, const double* x,
+                              const double* omega, double* out);
+
+/* Linear attention on given features fq, fk [BH][N][m] with values v [BH][N][dv]:
+ * global (causal == 0) or recurrent inclusive (causal != 0) sums; den_out
+ * [BH][N], S_out [BH][m][dv], z_out [BH][m] may be NULL. */
+void la_oracle_forward_features(int64_t BH, int64_t N, int64_t m, int64_t dv, int causal,
+                                const double* fq, const double* fk, const double* v, double* o,
+                                double* den_out, double* S_out, double* z_out);
+
 /* Number of OpenMP threads the oracle's parallel loops use (0 = runtime default). */
 void la_oracle_set_threads(int n);
 int la_oracle_get_threads(void);

@@ -321,6 +321,89 @@ def test_start_state_matches_decode_steps(oracle):
     assert rel(Sd, S) < 1e-13 and rel(zd, z) < 1e-13
 
 
+# ---- FAVOR+ features and attention on given features ------------------------------------------
+def test_favor_features_special_directions(oracle):
+    """omega = 0 leaves only the norm factor; omega = a unit vector picks one coordinate."""
+    x = np.array([[0.3, -1.2, 0.5], [2.0, 0.1, -0.4]])
+    omega = np.array([[0.0, 0.0, 0.0], [1.0, 0.0, 0.0], [0.0, 0.0, 1.0], [0.0, -1.0, 0.0]])
+    f = oracle.favor_features(x, omega)
+    nrm = (x * x).sum(1)
+    for r in range(2):
+        base = math.exp(-nrm[r] / 2) / 2.0  # m = 4
+        assert f[r, 0] == pytest.approx(base, rel=1e-14)
+        assert f[r, 1] == pytest.approx(base * math.exp(x[r, 0]), rel=1e-14)
+        assert f[r, 2] == pytest.approx(base * math.exp(x[r, 2]), rel=1e-14)
+        assert f[r, 3] == pytest.approx(base * math.exp(-x[r, 1]), rel=1e-14)
+
+
+def test_favor_estimator_is_unbiased(oracle):
+    """E_omega[phi(q).phi(k)] = exp(q.k) (Performer Approximation Quality): the Monte Carlo
+    mean over many directions lands within 5 standard errors of the exact kernel."""
+    rng = np.random.default_rng(80)
+    d, m = 6, 200_000
+    omega = rng.standard_normal((m, d))
+    for _ in range(4):
+        q, k = rng.standard_normal(d) * 0.4, rng.standard_normal(d) * 0.4
+        fq, fk = oracle.favor_features(q[None], omega)[0], oracle.favor_features(k[None], omega)[0]
+        terms = m * fq * fk                      # one unbiased sample per direction
+        est, se = terms.mean(), terms.std() / math.sqrt(m)
+        assert abs(est - fq @ fk) < 1e-12 * abs(est)
+        assert abs(est - math.exp(q @ k)) < 5 * se, (est, math.exp(q @ k), se)
+
+
+def test_favor_variance_falls_like_one_over_m(oracle):
+    """Var[phi(q).phi(k)] over independent draws of omega scales as 1/m: quadrupling m
+    divides it by about four."""
+    rng = np.random.default_rng(81)
+    d, reps = 5, 600
+    q, k = rng.standard_normal(d) * 0.3, rng.standard_normal(d) * 0.3
+    var = {}
+    for m in (16, 64):
+        est = []
+        for _ in range(reps):
+            omega = rng.standard_normal((m, d))
+            est.append(oracle.favor_features(q[None], omega)[0] @ oracle.favor_features(k[None], omega)[0])
+        var[m] = np.var(est)
+    assert 2.8 < var[16] / var[64] < 5.7, var
+
+
+def test_features_form_matches_quadratic_and_elu_path(oracle):
+    """Given features: the explicit n x n weights (numpy), and with elu+1 features the
+    oracle's own elementwise-map recurrence."""
+    rng = np.random.default_rng(82)
+    bh, n, m, dv = 2, 13, 7, 5
+    fq, fk = rng.uniform(0.1, 2.0, (bh, n, m)), rng.uniform(0.1, 2.0, (bh, n, m))
+    v = rng.standard_normal((bh, n, dv))
+    for causal in (True, False):
+        A = fq @ np.swapaxes(fk, -1, -2)
+        if causal:
+            A = A * np.tril(np.ones((n, n)))
+        ref = (A @ v) / A.sum(-1, keepdims=True)
+        o, den, S, z = oracle.forward_features(fq, fk, v, causal, return_den=True, return_state=True)
+        assert rel(o, ref) < 1e-13 and rel(den, A.sum(-1)) < 1e-13
+        assert rel(S, np.einsum("hja,hjb->hab", fk, v)) < 1e-13 and rel(z, fk.sum(1)) < 1e-13
+    q, k, v = rand((2, 11, 4), 83), rand((2, 11, 4), 84), rand((2, 11, 4), 85)
+    for causal in (True, False):
+        ref = (oracle.forward_causal if causal else oracle.forward_noncausal)(q, k, v)
+        assert rel(oracle.forward_features(np_phi(q), np_phi(k), v, causal), ref) < 1e-13
+
+
+def test_favor_attention_approximates_softmax(oracle):
+    """With many features, linear attention on FAVOR+ features approaches softmax attention
+    (the kernel the estimator targets), causal and not."""
+    rng = np.random.default_rng(86)
+    n, d, m = 12, 4, 100_000
+    q, k, v = rng.standard_normal((n, d)) * 0.5, rng.standard_normal((n, d)) * 0.5, rng.standard_normal((n, d))
+    omega = rng.standard_normal((m, d))
+    fq, fk = oracle.favor_features(q, omega), oracle.favor_features(k, omega)
+    for causal in (True, False):
+        w = np.exp(q @ k.T)
+        if causal:
+            w = w * np.tril(np.ones((n, n)))
+        ref = (w @ v) / w.sum(1, keepdims=True)
+        assert rel(oracle.forward_features(fq, fk, v, causal), ref) < 0.02
+
+
 def test_thread_count_does_not_change_results(oracle):
     shape = (4, 3, 25, 6)
     q, k, v, do = rand(shape, 47), rand(shape, 48), rand(shape, 49), rand(shape, 50)
