@@ -23,8 +23,9 @@ The JSON line also carries
                   on the library's stream over a second run of the timed steps) against the
                   8 TB/s HBM peak;
   * step_roofline: the same for the whole step (22 d bytes per token-head);
-  * calls       : the other measured calls (non-causal forward, and non-causal
-                  forward + backward, at the same size; the long and very-long
+  * calls       : the other measured calls (non-causal forward, non-causal
+                  forward + backward, and the causal forward on FAVOR+ random
+                  features, at the same size; the long and very-long
                   causal workloads; 512 decode steps one per call, 16 per
                   call, and 16 per call with 32 query heads on 4 shared
                   key/value states), each with its throughput and roofline
@@ -292,6 +293,26 @@ def bench_calls(args, la, inp, torch, mid_sets):
     calls["mid_noncausal_fwd_bwd"] = bench_call("noncausal_step", nc_step, 100, 400, w.B * w.N,
                                                 11 * unit_bytes(w.B, w.H, w.N, w.d), la, torch, nsets=nsets)
     del o, ws, g, wsb, saved
+
+    # Causal forward on FAVOR+ random features (m = d) at the Mid shape: the feature
+    # kernel on q and k, then the causal forward on the features.  Algorithmic bytes:
+    # q, k, v read and o written (4 units); the two feature passes add 4 more.
+    fsets = [inp.favor_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=s, device="cuda") for s in range(nsets)]
+    om = inp.favor_omega(w.d, seed=0, device="cuda")
+    fq, fk = torch.empty_like(q0), torch.empty_like(q0)
+    o = torch.empty_like(q0)
+    wsf = torch.empty(la.workspace_size(la.LA_OP_FWD_CAUSAL, w.B, w.H, w.N, w.d, w.dtype), dtype=torch.uint8,
+                      device="cuda")
+
+    def favor_fwd(i):
+        q, k, v = fsets[i]
+        la.favor_features(q, om, out=fq)
+        la.favor_features(k, om, out=fk)
+        la.la_forward_causal_features(fq, fk, v, out=o, workspace=wsf)
+
+    calls["mid_favor_causal_fwd"] = bench_call("favor", favor_fwd, 100, 400, w.B * w.N,
+                                               4 * unit_bytes(w.B, w.H, w.N, w.d), la, torch, nsets=nsets)
+    del fsets, fq, fk, o, wsf
 
     w = inp.LONG
     q, k, v, do = inp.workload_inputs(w, seed=0, device="cuda", with_dout=True)

@@ -170,6 +170,39 @@ la_status la_decode_steps(float* S, float* z, const void* q, const void* k, cons
                           int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t d, la_dtype dt,
                           void* stream);
 
+/* ---- Given feature maps: FAVOR+ (Performer section of the same page) ------------------
+ * FAVOR+ positive random features: out[r][i] = exp(omega_i . x_r - |x_r|^2 / 2) for
+ * every row x_r of x [rows][d] and every row omega_i of omega [d][d] fp32 (m = d
+ * random directions, e.g. drawn from N(0, I_d)).  The page's constant 1/sqrt(m)
+ * is left out: it scales all weights of a row alike and cancels in every output
+ * O (states and denominators computed from these features carry the factor m).
+ * Any 1/sqrt(d) scaling of queries and keys is the caller's pre-normalization
+ * (x = q d^(-1/4) puts it into q.k); features are computed in fp32, so rows with
+ * |x|^2 far beyond 100 underflow (every feature of such a row may round to 0).
+ * x and out in dtype dt (out rounded from fp32); omega is not overwritten. */
+la_status la_favor_features(const void* x, const float* omega, void* out, int64_t rows, int64_t d,
+                            la_dtype dt, void* stream);
+
+/* The forward calls and multi-token decode on features the caller has already
+ * applied (phi(Q), phi(K): FAVOR+ features from la_favor_features, or any other
+ * positive map with m = d features): O_i = fq_i^T S / fq_i^T z with S and z summed
+ * from fk and v exactly as in la_forward_causal / la_forward_noncausal /
+ * la_decode_steps, which apply phi = elu + 1 themselves.  Features must be
+ * positive (denominators must not vanish; an exact 0 is read as the padding
+ * past a sequence's end and adds nothing to the state).  Same layouts, workspaces
+ * (la_workspace_size of the matching op), start states and errors as those
+ * calls; no saved state (no backward on given features). */
+la_status la_forward_causal_features(const void* fq, const void* fk, const void* v, void* o,
+                                     const float* S0, const float* z0, float* den_out, float* S_out,
+                                     float* z_out, int64_t B, int64_t H, int64_t N, int64_t d,
+                                     la_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
+la_status la_forward_noncausal_features(const void* fq, const void* fk, const void* v, void* o,
+                                        int64_t B, int64_t H, int64_t N, int64_t d, la_dtype dt,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+la_status la_decode_steps_features(float* S, float* z, const void* fq, const void* fk, const void* v,
+                                   void* o, int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t d,
+                                   la_dtype dt, void* stream);
+
 /* Static description of a status code. */
 const char* la_status_string(la_status s);
 
@@ -199,7 +232,7 @@ int la_debug_wait_limit(void);
  * synchronises on its stop event and returns the kernel's name ("seg_state",
  * "total", "scan", "causal_fwd", "noncausal_fwd", "bwd_prefix", "rseg", "rscan",
  * "bwd_suffix", "bwd_fused", "ncbwd_q", "ncbwd_kv", "decode", "decode_steps",
- * "state_split", "fill_zero") and
+ * "state_split", "favor_features", "fill_zero") and
  * its duration in milliseconds. */
 la_status la_profile_enable(int on);
 int la_profile_count(void);

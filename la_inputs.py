@@ -9,6 +9,9 @@ Recipe (the shapes are the workloads the library is measured on):
   * Q, K, V ~ N(0, 1), scaled by 1/sqrt(d) when ``scale`` is set, drawn in
     fp32 and rounded to the target dtype (round-to-nearest-even for bf16);
   * the output gradient dO ~ N(0, 1) in the target dtype;
+  * FAVOR+ random directions (``favor_omega``): a [d, d] fp32 matrix with rows
+    ~ N(0, I_d), from its own seeded generator; FAVOR+ queries and keys
+    (``favor_qkv``) ~ N(0, 1) d^(-1/4), the page's pre-normalization;
   * draws come from one torch.Generator seeded with ``seed``, in the order
     q, k, v, dout.  ``device="cuda"`` draws with the device generator (fast for
     the multi-GiB workloads); tests copy the exact drawn values to the host.
@@ -99,6 +102,24 @@ def decode_tokens(batch, H, d, steps, dtype=torch.bfloat16, seed=1, device="cpu"
     k = normal((steps, batch, H, d), gen, dtype, s, device)
     v = normal((steps, batch, H, d), gen, dtype, s, device)
     return q, k, v
+
+
+def favor_qkv(B, H, N, d, dtype=torch.bfloat16, seed=0, device="cpu", with_dout=False):
+    """Inputs of the FAVOR+ path: q, k ~ N(0, 1) d^(-1/4) (the pre-normalization that puts
+    the softmax's 1/sqrt(d) into q.k), v ~ N(0, 1)/sqrt(d), dout ~ N(0, 1); same draw order."""
+    gen = generator(seed, device)
+    sqk = d ** -0.25
+    q = normal((B, H, N, d), gen, dtype, sqk, device)
+    k = normal((B, H, N, d), gen, dtype, sqk, device)
+    v = normal((B, H, N, d), gen, dtype, 1.0 / math.sqrt(d), device)
+    if not with_dout:
+        return q, k, v
+    return q, k, v, normal((B, H, N, d), gen, dtype, 1.0, device)
+
+
+def favor_omega(d, seed=0, device="cpu"):
+    """FAVOR+ random directions: a [d, d] fp32 matrix whose rows are drawn from N(0, I_d)."""
+    return torch.randn((d, d), generator=generator(seed, device), dtype=torch.float32, device=device)
 
 
 def to_f64(x: torch.Tensor):

@@ -19,6 +19,10 @@ from ._binding import (  # noqa: F401
     la_backward_noncausal,
     la_decode_step,
     la_decode_steps,
+    la_decode_steps_features,
+    la_forward_causal_features,
+    la_forward_noncausal_features,
+    favor_features,
     la_forward_causal,
     la_forward_noncausal,
     linear_attention,

@@ -21,7 +21,8 @@ LA_F32, LA_BF16 = 0, 1
 LA_OP_FWD_NONCAUSAL, LA_OP_FWD_CAUSAL, LA_OP_BWD_CAUSAL, LA_OP_BWD_NONCAUSAL = 0, 1, 2, 3
 
 EXPORTS = ("la_workspace_size", "la_saved_state_size", "la_forward_noncausal", "la_forward_causal", "la_backward_causal",
-           "la_backward_noncausal", "la_decode_step", "la_decode_steps", "la_status_string", "la_last_error_message", "la_version",
+           "la_backward_noncausal", "la_decode_step", "la_decode_steps", "la_favor_features",
+           "la_forward_causal_features", "la_forward_noncausal_features", "la_decode_steps_features", "la_status_string", "la_last_error_message", "la_version",
            "la_profile_enable", "la_profile_count", "la_profile_entry", "la_debug_set_wait_limit",
            "la_debug_wait_limit")
 
@@ -63,6 +64,14 @@ def load_library(path: str | None = None):
     lib.la_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.la_decode_steps.restype = i32
     lib.la_decode_steps.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+    lib.la_decode_steps_features.restype = i32
+    lib.la_decode_steps_features.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
+    lib.la_favor_features.restype = i32
+    lib.la_favor_features.argtypes = [vp, vp, vp, i64, i64, i32, vp]
+    lib.la_forward_causal_features.restype = i32
+    lib.la_forward_causal_features.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]
+    lib.la_forward_noncausal_features.restype = i32
+    lib.la_forward_noncausal_features.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_status_string.restype = ctypes.c_char_p
     lib.la_status_string.argtypes = [i32]
     lib.la_last_error_message.restype = ctypes.c_char_p
@@ -263,7 +272,7 @@ def la_decode_step(S, z, q, k, v, *, out=None):
     return o
 
 
-def la_decode_steps(S, z, q, k, v, *, out=None):
+def la_decode_steps(S, z, q, k, v, *, out=None, _features=False):
     """T in-place recurrent steps per key/value head in one call; returns o [B, H, T, d].
 
     q: [B, H, T, d]; k, v: [B, Hkv, T, d] with H a multiple of Hkv (query head h reads the
@@ -285,8 +294,67 @@ def la_decode_steps(S, z, q, k, v, *, out=None):
     if not (S.is_contiguous() and z.is_contiguous()):
         raise ValueError("S and z must be contiguous")
     o = torch.empty_like(q) if out is None else out
-    _check(load_library().la_decode_steps(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Hkv, T, d,
-                                          _dtype_code(q.dtype), _stream(q.device)))
+    fn = load_library().la_decode_steps_features if _features else load_library().la_decode_steps
+    _check(fn(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(o), B, H, Hkv, T, d, _dtype_code(q.dtype),
+              _stream(q.device)))
+    return o
+
+
+def la_decode_steps_features(S, z, fq, fk, v, *, out=None):
+    """la_decode_steps on features applied beforehand (fq, fk: positive, e.g. from favor_features)."""
+    return la_decode_steps(S, z, fq, fk, v, out=out, _features=True)
+
+
+def favor_features(x, omega, *, out=None):
+    """FAVOR+ features exp(omega x - |x|^2/2) of the rows of x [..., d] (bf16 or fp32); omega: [d, d] fp32.
+
+    The page's constant 1/sqrt(m) (m = d) is left out: it cancels in every attention output."""
+    d = x.shape[-1]
+    if omega.shape != (d, d) or omega.dtype != torch.float32 or not omega.is_contiguous():
+        raise ValueError("omega must be a contiguous [d, d] fp32 tensor")
+    if not x.is_contiguous() or not x.is_cuda or omega.device != x.device:
+        raise ValueError("x must be a contiguous tensor on the same HIP device as omega")
+    o = torch.empty_like(x) if out is None else out
+    rows = x.numel() // d if d else 0
+    _check(load_library().la_favor_features(_ptr(x), _ptr(omega), _ptr(o), rows, d, _dtype_code(x.dtype),
+                                            _stream(x.device)))
+    return o
+
+
+def la_forward_causal_features(fq, fk, v, *, return_den=False, return_state=False, out=None, workspace=None,
+                               S0=None, z0=None, S_out=None, z_out=None):
+    """Causal forward on given positive features fq = phi(Q), fk = phi(K) [B, H, N, d]."""
+    B, H, N, d = _check_seq(fq, fk, v)
+    _check_state(S0, z0, B, H, d, fq.device)
+    _check_state(S_out, z_out, B, H, d, fq.device)
+    o = torch.empty_like(v) if out is None else out
+    den = torch.empty((B, H, N), dtype=torch.float32, device=fq.device) if return_den else None
+    S = z = None
+    if return_state:
+        S = torch.empty((B, H, d, d), dtype=torch.float32, device=fq.device) if S_out is None else S_out
+        z = torch.empty((B, H, d), dtype=torch.float32, device=fq.device) if z_out is None else z_out
+    ws = _workspace(LA_OP_FWD_CAUSAL, B, H, N, d, fq.dtype, fq.device, 0, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().la_forward_causal_features(_ptr(fq), _ptr(fk), _ptr(v), _ptr(o), _ptr(S0), _ptr(z0),
+                                                     _ptr(den), _ptr(S), _ptr(z), B, H, N, d,
+                                                     _dtype_code(fq.dtype), _ptr(ws), nbytes, _stream(fq.device)))
+    res = [o]
+    if return_den:
+        res.append(den)
+    if return_state:
+        res += [S, z]
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def la_forward_noncausal_features(fq, fk, v, *, out=None, workspace=None):
+    """Non-causal forward on given positive features fq = phi(Q), fk = phi(K) [B, H, N, d]."""
+    B, H, N, d = _check_seq(fq, fk, v)
+    o = torch.empty_like(v) if out is None else out
+    ws = _workspace(LA_OP_FWD_NONCAUSAL, B, H, N, d, fq.dtype, fq.device, 0, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().la_forward_noncausal_features(_ptr(fq), _ptr(fk), _ptr(v), _ptr(o), B, H, N, d,
+                                                        _dtype_code(fq.dtype), _ptr(ws), nbytes,
+                                                        _stream(fq.device)))
     return o
 
 

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblinattn.so")
-SOURCES = ("fwd.hip", "bwd.hip", "ncbwd.hip", "decode.hip", "api.cpp")
+SOURCES = ("fwd.hip", "bwd.hip", "ncbwd.hip", "decode.hip", "favor.hip", "api.cpp")
 ARCH = "gfx950"
 
 

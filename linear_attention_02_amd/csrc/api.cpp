@@ -289,9 +289,13 @@ la_status la_saved_state_size(int64_t B, int64_t H, int64_t N, int64_t d, int ch
     return LA_OK;
 }
 
-la_status la_forward_noncausal(const void* q, const void* k, const void* v, void* o, void* saved_state,
-                               size_t saved_state_bytes, int64_t B, int64_t H, int64_t N, int64_t d, la_dtype dt,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+la_status forward_noncausal(const void* q, const void* k, const void* v, void* o, void* saved_state,
+                            size_t saved_state_bytes, int64_t B, int64_t H, int64_t N, int64_t d, la_dtype dt,
+                            void* workspace, size_t workspace_bytes, void* stream, int feat) {
     bool empty = false;
     la_status st = check_shape(B, H, N, d, 0, dt, &empty);
     if (st != LA_OK) return st;
@@ -321,22 +325,22 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
     const int64_t BH = B * H;
     const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
     hipError_t e;
-    if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
+    if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s, feat); })) != hipSuccess)
         return hip_fail(e, "seg_state launch");
     // One total per head, read by every readout workgroup (and by the backward, from the saved state).
     if ((e = timed("total", s, [&] { return la::launch_total((int)d, rec, total, BH, L.plan.nseg, s); })) != hipSuccess)
         return hip_fail(e, "total launch");
     if ((e = timed("noncausal_fwd", s, [&] {
-             return la::launch_noncausal_fwd(idt, (int)d, q, o, total, 1, BH, N, L.plan, s);
+             return la::launch_noncausal_fwd(idt, (int)d, q, o, total, 1, BH, N, L.plan, s, feat);
          })) != hipSuccess)
         return hip_fail(e, "noncausal_fwd launch");
     return LA_OK;
 }
 
-la_status la_forward_causal(const void* q, const void* k, const void* v, void* o, const float* S0, const float* z0,
-                            float* den_out, float* S_out, float* z_out, void* saved_state, size_t saved_state_bytes,
-                            int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+la_status forward_causal(const void* q, const void* k, const void* v, void* o, const float* S0, const float* z0,
+                         float* den_out, float* S_out, float* z_out, void* saved_state, size_t saved_state_bytes,
+                         int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt, void* workspace,
+                         size_t workspace_bytes, void* stream, int feat) {
     bool empty = false;
     la_status st = check_shape(B, H, N, d, chunk, dt, &empty);
     if (st != LA_OK) return st;
@@ -398,19 +402,75 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* o
     float* init_n = from_state ? reinterpret_cast<float*>(ws + L.init_n) : nullptr;
     const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
     if (from_state &&
-        (e = timed("state_split", s, [&] { return la::launch_state_split((int)d, S0, z0, init, init_n, BH, s); })) !=
+        (e = timed("state_split", s, [&] { return la::launch_state_split((int)d, S0, z0, init, init_n, BH, s, feat); })) !=
             hipSuccess)
         return hip_fail(e, "state_split launch");
-    if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
+    if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s, feat); })) != hipSuccess)
         return hip_fail(e, "seg_state launch");
     if (L.plan.scan &&
         (e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, BH, L.plan.nseg, 1, s, init); })) != hipSuccess)
         return hip_fail(e, "scan launch");
     if ((e = timed("causal_fwd", s, [&] {
              return la::launch_causal_fwd(idt, (int)d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, L.plan, s, init,
-                                          init_n);
+                                          init_n, feat);
          })) != hipSuccess)
         return hip_fail(e, "causal_fwd launch");
+    return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status la_forward_noncausal(const void* q, const void* k, const void* v, void* o, void* saved_state,
+                               size_t saved_state_bytes, int64_t B, int64_t H, int64_t N, int64_t d, la_dtype dt,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    return forward_noncausal(q, k, v, o, saved_state, saved_state_bytes, B, H, N, d, dt, workspace, workspace_bytes,
+                             stream, la::kFeatElu);
+}
+
+la_status la_forward_noncausal_features(const void* fq, const void* fk, const void* v, void* o, int64_t B, int64_t H,
+                                        int64_t N, int64_t d, la_dtype dt, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+    return forward_noncausal(fq, fk, v, o, nullptr, 0, B, H, N, d, dt, workspace, workspace_bytes, stream,
+                             la::kFeatGiven);
+}
+
+la_status la_forward_causal(const void* q, const void* k, const void* v, void* o, const float* S0, const float* z0,
+                            float* den_out, float* S_out, float* z_out, void* saved_state, size_t saved_state_bytes,
+                            int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    return forward_causal(q, k, v, o, S0, z0, den_out, S_out, z_out, saved_state, saved_state_bytes, B, H, N, d, chunk,
+                          dt, workspace, workspace_bytes, stream, la::kFeatElu);
+}
+
+la_status la_forward_causal_features(const void* fq, const void* fk, const void* v, void* o, const float* S0,
+                                     const float* z0, float* den_out, float* S_out, float* z_out, int64_t B, int64_t H,
+                                     int64_t N, int64_t d, la_dtype dt, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+    return forward_causal(fq, fk, v, o, S0, z0, den_out, S_out, z_out, nullptr, 0, B, H, N, d, 0, dt, workspace,
+                          workspace_bytes, stream, la::kFeatGiven);
+}
+
+la_status la_favor_features(const void* x, const float* omega, void* out, int64_t rows, int64_t d, la_dtype dt,
+                            void* stream) {
+    if (dt != LA_F32 && dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "dtype %d is not LA_F32 or LA_BF16", (int)dt);
+    if (d != 32 && d != 64 && d != 128) return fail(LA_ERR_UNSUPPORTED, "d = %lld; built for 32, 64 and 128", (long long)d);
+    if (rows < 0) return fail(LA_ERR_INVALID_ARGUMENT, "negative row count %lld", (long long)rows);
+    if (rows > ((int64_t)1 << 40)) return fail(LA_ERR_UNSUPPORTED, "rows = %lld exceeds 2^40", (long long)rows);
+    if (!omega) return fail(LA_ERR_INVALID_ARGUMENT, "omega must be non-NULL");
+    if (rows > 0 && (!x || !out)) return fail(LA_ERR_INVALID_ARGUMENT, "x and out must be non-NULL");
+    const size_t xb = (size_t)rows * d * elem_size(dt);
+    const Range in[] = {{"x", x, xb}, {"omega", omega, (size_t)d * d * sizeof(float)}};
+    const Range out_r[] = {{"out", out, xb}};
+    la_status st = check_ptrs(in, 2, out_r, 1);
+    if (st != LA_OK) return st;
+    if (rows == 0) return LA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed("favor_features", s, [&] {
+        return la::launch_favor_features(dt == LA_BF16 ? la::kBF16 : la::kF32, (int)d, x, omega, out, rows, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "favor_features launch");
     return LA_OK;
 }
 
@@ -559,8 +619,8 @@ la_status la_decode_step(float* S, float* z, const void* q, const void* k, const
     return LA_OK;
 }
 
-la_status la_decode_steps(float* S, float* z, const void* q, const void* k, const void* v, void* o, int64_t B,
-                          int64_t H, int64_t Hkv, int64_t T, int64_t d, la_dtype dt, void* stream) {
+static la_status decode_steps(float* S, float* z, const void* q, const void* k, const void* v, void* o, int64_t B,
+                              int64_t H, int64_t Hkv, int64_t T, int64_t d, la_dtype dt, void* stream, int feat) {
     if (dt != LA_F32 && dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "dtype %d is not LA_F32 or LA_BF16", (int)dt);
     if (d != 32 && d != 64 && d != 128) return fail(LA_ERR_UNSUPPORTED, "d = %lld; built for 32, 64 and 128", (long long)d);
     if (B < 0 || H < 0 || Hkv < 0 || T < 0)
@@ -586,10 +646,21 @@ la_status la_decode_steps(float* S, float* z, const void* q, const void* k, cons
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = timed("decode_steps", s, [&] {
         return la::launch_decode_steps(dt == LA_BF16 ? la::kBF16 : la::kF32, (int)d, S, z, q, k, v, o, BHkv, T, H / Hkv,
-                                       s);
+                                       s, feat);
     });
     if (e != hipSuccess) return hip_fail(e, "decode_steps launch");
     return LA_OK;
+}
+
+la_status la_decode_steps(float* S, float* z, const void* q, const void* k, const void* v, void* o, int64_t B,
+                          int64_t H, int64_t Hkv, int64_t T, int64_t d, la_dtype dt, void* stream) {
+    return decode_steps(S, z, q, k, v, o, B, H, Hkv, T, d, dt, stream, la::kFeatElu);
+}
+
+la_status la_decode_steps_features(float* S, float* z, const void* fq, const void* fk, const void* v, void* o,
+                                   int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t d, la_dtype dt,
+                                   void* stream) {
+    return decode_steps(S, z, fq, fk, v, o, B, H, Hkv, T, d, dt, stream, la::kFeatGiven);
 }
 
 }  // extern "C"

@@ -76,6 +76,7 @@ struct RowFrag {
     }
     // f[k0 / KSTEP] = phi of the held elements as operands; returns the lane's
     // part of sum_a phi(x_a) wgt[a] (fp32 weights in LDS).
+    template <class FM = FeatElu>
     __device__ __forceinline__ float phi_ops(typename M::frag* f, const float* wgt, int lane) const {
         float dot = 0.f;
 #pragma unroll
@@ -88,7 +89,7 @@ struct RowFrag {
                 const f32x4 wv = *reinterpret_cast<const f32x4*>(wgt + c + e);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    y[e + u] = phi_f(to_f32(h[e + u]));
+                    y[e + u] = FM::phi(to_f32(h[e + u]));
                     dot += y[e + u] * wv[u];
                 }
             }
@@ -103,16 +104,17 @@ struct RowFrag {
         return dot;
     }
     // f[k0 / KSTEP] = phi of the held elements as operands.
+    template <class FM = FeatElu>
     __device__ __forceinline__ void phi_ops(typename M::frag* f) const {
 #pragma unroll
         for (int x = 0; x < NR; ++x) {
             const T* h = reinterpret_cast<const T*>(&r[x]);
             if constexpr (sizeof(T) == 2) {
 #pragma unroll
-                for (int e = 0; e < EV; ++e) f[x][e] = (T)phi_f(to_f32(h[e]));
+                for (int e = 0; e < EV; ++e) f[x][e] = (T)FM::phi(to_f32(h[e]));
             } else {
 #pragma unroll
-                for (int e = 0; e < EV; ++e) f[4 * x + e] = phi_f(h[e]);
+                for (int e = 0; e < EV; ++e) f[4 * x + e] = FM::phi(h[e]);
             }
         }
     }
@@ -179,8 +181,8 @@ __device__ __forceinline__ void stage_phi(const ChunkRegs<T, D, kWaveRows>& cq, 
     }
 }
 
-// E(K) = elu(K) row-major into LDS.
-template <typename T, int D>
+// E(K) = phi(K) - 1 (elu(K) for the default map) row-major into LDS.
+template <typename T, int D, class FM = FeatElu>
 __device__ __forceinline__ void stage_elu(const ChunkRegs<T, D>& ck, const Tile<T, kC, D>& tE, int tid) {
     using CR = ChunkRegs<T, D>;
 #pragma unroll
@@ -188,7 +190,7 @@ __device__ __forceinline__ void stage_elu(const ChunkRegs<T, D>& ck, const Tile<
         uint4 packed;
         T* pk = reinterpret_cast<T*>(&packed);
 #pragma unroll
-        for (int e = 0; e < CR::EV; ++e) pk[e] = from_f32<T>(elu_f(ck.get(i, e)));
+        for (int e = 0; e < CR::EV; ++e) pk[e] = from_f32<T>(FM::e(ck.get(i, e)));
         *reinterpret_cast<uint4*>(tE.granule(CR::row(i, tid), CR::gran(i, tid))) = packed;
     }
 }
@@ -422,8 +424,8 @@ __device__ __forceinline__ void publish_state(const StateAcc<D>& st, const Tile<
 // wave's vector tiles, with u, v either all ones (null pointer) or fp32
 // vectors in LDS (split hi + lo in bf16).  The vector tiles a wave owns are
 // its own row tiles, so va reuses the X operands.  kEluX: X holds raw keys and
-// the operands are E(X) = elu(X), applied after the load.
-template <typename T, int D, bool kVecA, bool kVecB, bool kEluX = false>
+// the operands are E(X) = phi(X) - 1 of the feature map FM, applied after the load.
+template <typename T, int D, bool kVecA, bool kVecB, bool kEluX = false, class FM = FeatElu>
 __device__ __forceinline__ void state_update(StateAcc<D>& st, VecAcc<D>& va, VecAcc<D>& vb, const Tile<T, kC, D>& tX,
                                              const Tile<T, kC, D>& tY, const float* u, const float* v, int lane,
                                              int w) {
@@ -461,7 +463,7 @@ __device__ __forceinline__ void state_update(StateAcc<D>& st, VecAcc<D>& va, Vec
             const int k0 = (kg + kk) * M::KSTEP;
             if (kEluX) {
 #pragma unroll
-                for (int ia = 0; ia < ST::NAT; ++ia) xf[kk][ia] = M::elu_op(xf[kk][ia]);
+                for (int ia = 0; ia < ST::NAT; ++ia) xf[kk][ia] = M::template elu_op<FM>(xf[kk][ia]);
             }
 #pragma unroll
             for (int ib = 0; ib < ST::NBT; ++ib)

@@ -56,6 +56,28 @@ __device__ __forceinline__ float phi_f(float x) { return fmaxf(x + 1.f, expc_f(x
 __device__ __forceinline__ float elu_f(float x) { return fmaxf(x, expc_f(x) - 1.f); }
 __device__ __forceinline__ float dphi_f(float x) { return expc_f(x); }
 
+// The feature maps kernels are instantiated for.
+//   FeatElu: phi = elu + 1 elementwise (the default everywhere).  The kernels
+//     carry its sums split around the constant 1 (kSplit): S = 1 P^T + S_E,
+//     z = n 1 + z_E, with E(x) = phi(x) - 1 = elu(x) small at the usual input
+//     scales, and the rank-1 parts in exact fp32 terms.
+//   FeatGiven: the inputs already are positive features computed beforehand
+//     (FAVOR+ random features, say): phi(x) = x.  Such features need not sit near
+//     1 (FAVOR+ features of unscaled inputs are orders of magnitude below it,
+//     where a split around 1 would cancel catastrophically), so they are carried
+//     unsplit: E(x) = x and every rank-1 term is dropped.
+// Either way E(0) = 0: the zero rows read past a sequence's end add nothing.
+struct FeatElu {
+    static constexpr bool kSplit = true;
+    __device__ __forceinline__ static float phi(float x) { return phi_f(x); }
+    __device__ __forceinline__ static float e(float x) { return elu_f(x); }
+};
+struct FeatGiven {
+    static constexpr bool kSplit = false;
+    __device__ __forceinline__ static float phi(float x) { return x; }
+    __device__ __forceinline__ static float e(float x) { return x; }
+};
+
 // 1/x to within an ulp: hardware reciprocal refined by one Newton step.
 __device__ __forceinline__ float rcp_f(float x) {
     float r = __builtin_amdgcn_rcpf(x);
@@ -251,11 +273,12 @@ struct Mma<bf16> {
         const bf16x4 hi = *reinterpret_cast<const bf16x4*>(&r[k0 / 16 + 1]);
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    // elu of every element, rounded back to bf16.
+    // E = phi - 1 of every element (elu for the default map), rounded back to bf16.
+    template <class FM = FeatElu>
     __device__ __forceinline__ static frag elu_op(frag x) {
         frag f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = (bf16)elu_f((float)x[e]);
+        for (int e = 0; e < 8; ++e) f[e] = (bf16)FM::e((float)x[e]);
         return f;
     }
     // Operand for k-step k0 of a contraction over the row index of accumulator
@@ -328,7 +351,8 @@ struct Mma<float> {
         return reinterpret_cast<const float*>(&r[k0 >> 4])[(k0 & 15) >> 2];
     }
     __device__ __forceinline__ static frag acc_op(const f32x4* acc, int k0) { return acc[k0 >> 4][(k0 & 15) >> 2]; }
-    __device__ __forceinline__ static frag elu_op(frag x) { return elu_f(x); }
+    template <class FM = FeatElu>
+    __device__ __forceinline__ static frag elu_op(frag x) { return FM::e(x); }
     __device__ __forceinline__ static void splat(const float* v, int k0, int lane, frag& hi, frag& lo) {
         hi = v[kap(k0, lane)];
         lo = 0.f;

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(float* __restrict__ S, f
 // token's rank-1 update where the row opens one, then forms its part of
 // phi(q)^T S, reduced over the row groups with shuffles inside a wavefront and
 // through LDS across the four.
-template <typename T, int D>
+template <typename T, int D, class FM = FeatElu>
 __global__ __launch_bounds__(kBlock) void decode_steps_kernel(float* __restrict__ S, float* __restrict__ z,
                                                               const T* __restrict__ q, const T* __restrict__ k,
                                                               const T* __restrict__ v, T* __restrict__ o, int ntok,
@@ -129,9 +129,9 @@ __global__ __launch_bounds__(kBlock) void decode_steps_kernel(float* __restrict_
             if (ri < nb) {
                 const int64_t r = r0 + ri;
                 const int64_t t = r / G, h = r % G;
-                qf = phi_f(to_f32(q[(qrow0 + h * ntok + t) * D + a]));
+                qf = FM::phi(to_f32(q[(qrow0 + h * ntok + t) * D + a]));
                 if (h == 0) {
-                    kf = phi_f(to_f32(k[(krow0 + t) * D + a]));
+                    kf = FM::phi(to_f32(k[(krow0 + t) * D + a]));
                     vv = to_f32(v[(krow0 + t) * D + a]);
                 }
             }
@@ -190,11 +190,12 @@ __global__ __launch_bounds__(kBlock) void decode_steps_kernel(float* __restrict_
     if (tid < D) z[(int64_t)kvh * D + tid] = zn;
 }
 
-hipError_t launch_decode_steps(int dt, int d, float* S, float* z, const void* q, const void* k, const void* v,
-                               void* o, int64_t BHkv, int64_t T, int64_t G, hipStream_t s) {
+template <class FM>
+static hipError_t launch_decode_steps_fm(int dt, int d, float* S, float* z, const void* q, const void* k,
+                                         const void* v, void* o, int64_t BHkv, int64_t T, int64_t G, hipStream_t s) {
     const dim3 grid((unsigned)BHkv);
 #define LA_DECS(TT, DD)                                                                                     \
-    hipLaunchKernelGGL((decode_steps_kernel<TT, DD>), grid, dim3(kBlock), 0, s, S, z, (const TT*)q,         \
+    hipLaunchKernelGGL((decode_steps_kernel<TT, DD, FM>), grid, dim3(kBlock), 0, s, S, z, (const TT*)q,     \
                        (const TT*)k, (const TT*)v, (TT*)o, (int)T, (int)G)
     if (dt == kBF16) {
         switch (d) {
@@ -213,6 +214,12 @@ hipError_t launch_decode_steps(int dt, int d, float* S, float* z, const void* q,
     }
 #undef LA_DECS
     return hipGetLastError();
+}
+
+hipError_t launch_decode_steps(int dt, int d, float* S, float* z, const void* q, const void* k, const void* v,
+                               void* o, int64_t BHkv, int64_t T, int64_t G, hipStream_t s, int feat) {
+    return feat == kFeatGiven ? launch_decode_steps_fm<FeatGiven>(dt, d, S, z, q, k, v, o, BHkv, T, G, s)
+                              : launch_decode_steps_fm<FeatElu>(dt, d, S, z, q, k, v, o, BHkv, T, G, s);
 }
 
 hipError_t launch_decode(int dt, int d, float* S, float* z, const void* q, const void* k,

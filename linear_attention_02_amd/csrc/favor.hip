@@ -1,0 +1,142 @@
+// favor.hip -- FAVOR+ positive random features for gfx950.
+//
+// Performer section of the page "Efficient Transformers Survey": the softmax
+// kernel exp(q.k) is the expectation over w ~ N(0, I_d) of
+// exp(w.q - |q|^2/2) exp(w.k - |k|^2/2), so the features
+// phi(x)_i = m^{-1/2} exp(w_i.x - |x|^2/2), i < m, estimate it without bias and
+// stay positive.  Here m = d, and the constant m^{-1/2} is left out: it scales
+// every weight of a row equally, so num / den does not see it (states and
+// denominators carry the factor m).  Left out, the features average 1 over the
+// draw of w, which suits the split phi = 1 + E the linear-attention kernels carry.
+// The exponent needs fp32 accuracy (exp turns an absolute error in w.x into a
+// relative one), so X Omega^T runs on the fp32 MFMA (v_mfma_f32_16x16x4_f32)
+// with x widened exactly; one exp per feature finishes it.
+#include "chunk.h"
+
+namespace la {
+
+// One workgroup takes CPB chunks of 64 rows.  Omega is staged in LDS once; each
+// chunk's rows are prefetched into registers one chunk ahead, staged into LDS
+// with their squared norms reduced by shuffles on the way (the D/4 threads of a
+// row are adjacent lanes), and every wavefront forms the [D features x 16 rows]
+// tile of Omega X^T for its 16 rows on MFMA.  bf16 rows are exact in bf16, so
+// Omega is split into bf16 hi + lo parts and two bf16 MFMAs with fp32
+// accumulation give the exponent to about 2^-17 of sum |w_i x_i| (a sixteenth
+// of the fp32 MFMA's cost per product); fp32 rows use the fp32 MFMA.
+template <typename T, int D>
+__global__ __launch_bounds__(kBlock) void favor_features_kernel(const T* __restrict__ x,
+                                                                const float* __restrict__ omega, T* __restrict__ out,
+                                                                int64_t rows) {
+    constexpr bool kBF = sizeof(T) == 2;
+    using M = Mma<T>;
+    constexpr int DT = D / 16;
+    constexpr int CPB = 4;                 // chunks of 64 rows per workgroup
+    constexpr int TPR = D / 4;             // threads per row (4 elements each)
+    constexpr int NI = kC * TPR / kBlock;  // 4-element groups per thread per chunk
+    static_assert(NI >= 1 && kC * TPR % kBlock == 0 && TPR <= kWave, "rows must tile the workgroup");
+    typedef typename std::conditional<kBF, uint2, uint4>::type word;
+    __shared__ __attribute__((aligned(16))) T s_om[kBF ? 2 : 1][D * D];  // bf16: hi, lo; fp32: omega
+    __shared__ __attribute__((aligned(16))) T s_x[2][kC * D];
+    __shared__ float s_n[2][kC];
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
+
+    for (int i = tid; i < D * D / 4; i += kBlock) {
+        const int r = (4 * i) / D, c = (4 * i) % D;
+        const f32x4 om = reinterpret_cast<const f32x4*>(omega)[i];
+        if constexpr (kBF) {
+            f32x4 hi;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hi[e] = (float)(bf16)om[e];
+            store4(&Tile<T, D, D>{s_om[0]}.at(r, c), hi);
+            store4(&Tile<T, D, D>{s_om[kBF ? 1 : 0]}.at(r, c), om - hi);
+        } else {
+            store4(&Tile<T, D, D>{s_om[0]}.at(r, c), om);
+        }
+    }
+    // Group j of this thread: row (4 (tid + kBlock j)) / D of the chunk, columns 4 (tid mod TPR) ..
+    auto load = [&](word* xr, int64_t r0) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int i = tid + kBlock * j;
+            const int64_t row = r0 + (4 * i) / D;
+            xr[j] = row < rows ? *reinterpret_cast<const word*>(x + row * D + (4 * i) % D) : word{};
+        }
+    };
+    const int64_t base = (int64_t)blockIdx.x * CPB * kC;
+    word xr[NI];
+    load(xr, base);
+    for (int cb = 0; cb < CPB; ++cb) {
+        const int64_t r0 = base + (int64_t)cb * kC;
+        if (r0 >= rows) break;
+        const Tile<T, kC, D> tX{s_x[cb & 1]};
+        float* sn = s_n[cb & 1];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int i = tid + kBlock * j;
+            *reinterpret_cast<word*>(&tX.at((4 * i) / D, (4 * i) % D)) = xr[j];  // as loaded
+            const T* h = reinterpret_cast<const T*>(&xr[j]);
+            float nrm = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) nrm += to_f32(h[e]) * to_f32(h[e]);
+            nrm = sum_lanes<TPR>(nrm);
+            if ((4 * i) % D == 0) sn[(4 * i) / D] = nrm;
+        }
+        load(xr, r0 + kC);  // the next chunk (past the rows: nothing is read)
+        __syncthreads();    // rows and norms staged (and omega, for the first chunk)
+        // acc[m]: the accumulator tile [feature 16 m + 4 g + e][row 16 w + (lane & 15)] of Omega X^T.
+        f32x4 acc[DT];
+#pragma unroll
+        for (int m = 0; m < DT; ++m) acc[m] = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < D; k0 += M::KSTEP) {
+            const typename M::frag xf = M::ld(tX, 16 * w, k0, lane);
+#pragma unroll
+            for (int m = 0; m < DT; ++m) {
+                acc[m] = M::mma(M::ld(Tile<T, D, D>{s_om[0]}, 16 * m, k0, lane), xf, acc[m]);
+                if constexpr (kBF) acc[m] = M::mma(M::ld(Tile<T, D, D>{s_om[kBF ? 1 : 0]}, 16 * m, k0, lane), xf, acc[m]);
+            }
+        }
+        const int t = 16 * w + (lane & 15);
+        const int64_t row = r0 + t;
+        if (row < rows) {
+            const float half_n = 0.5f * sn[t];
+#pragma unroll
+            for (int m = 0; m < DT; ++m) {
+                f32x4 y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = __builtin_amdgcn_exp2f((acc[m][e] - half_n) * 1.4426950408889634f);
+                store4(out + row * D + 16 * m + 4 * g, y);
+            }
+        }
+        // The next chunk stages into the other LDS buffer; the barrier after that
+        // staging keeps this chunk's buffer intact until every wave has read it.
+    }
+}
+
+hipError_t launch_favor_features(int dt, int d, const void* x, const float* omega, void* out, int64_t rows,
+                                 hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    const dim3 grid((unsigned)((rows + 4 * kC - 1) / (4 * kC)));
+#define LA_FAV(TT, DD)                                                                                        \
+    hipLaunchKernelGGL((favor_features_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)x, omega, (TT*)out, \
+                       rows)
+    if (dt == kBF16) {
+        switch (d) {
+            case 32: LA_FAV(bf16, 32); break;
+            case 64: LA_FAV(bf16, 64); break;
+            case 128: LA_FAV(bf16, 128); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (d) {
+            case 32: LA_FAV(float, 32); break;
+            case 64: LA_FAV(float, 64); break;
+            case 128: LA_FAV(float, 128); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+#undef LA_FAV
+    return hipGetLastError();
+}
+
+}  // namespace la

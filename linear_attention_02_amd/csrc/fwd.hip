@@ -43,7 +43,7 @@ namespace la {
 // MFMA operands, since each wavefront reads its own key columns only.  Waits
 // and barriers are explicit: a step waits for its slot's loads, synchronises
 // the workgroup, then refills the slot the previous step has finished reading.
-template <typename T, int D>
+template <typename T, int D, class FM = FeatElu>
 __global__ __launch_bounds__(kBlock, 2) void seg_state_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                            float* __restrict__ rec, int N, int cps, int nseg, int BH) {
     using DMA = TileDma<T, D>;
@@ -92,8 +92,8 @@ __global__ __launch_bounds__(kBlock, 2) void seg_state_kernel(const T* __restric
                 DMA::issue(bk, chunk_tok(c - 1 + R), ks[ur], w, lane);
                 DMA::issue(bv, chunk_tok(c - 1 + R), vs[ur], w, lane);
             }
-            state_update<T, D, true, true, true>(st, vz, vp, Tile<T, kC, D>{ks[u]}, Tile<T, kC, D>{vs[u]}, nullptr,
-                                                 nullptr, lane, w);
+            state_update<T, D, true, true, true, FM>(st, vz, vp, Tile<T, kC, D>{ks[u]}, Tile<T, kC, D>{vs[u]},
+                                                     nullptr, nullptr, lane, w);
         }
     }
     wait_vmcnt<0>();  // no direct-to-LDS load may outlive the workgroup
@@ -193,7 +193,7 @@ struct CausalFwdCfg {
     static constexpr int kRecordRegs = D <= 64 ? 48 : 128;
 };
 
-template <typename T, int D>
+template <typename T, int D, class FM = FeatElu>
 __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) void causal_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ o,
     float* __restrict__ den_out, const float* __restrict__ rec, float* __restrict__ S_out, float* __restrict__ z_out,
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
         publish_state<T, D>(st, Tile<T, D, D>{sm_st[0]}, lane, w);
         store_vec_as<T, D>(s_zb[0], vz, lane, w);
         store_vec<D>(s_p[0], vp, lane, w);
-        stage_elu<T, D>(ck, Tile<T, kC, D>{sm_e[0]}, rtid);
+        stage_elu<T, D, FM>(ck, Tile<T, kC, D>{sm_e[0]}, rtid);
         stage_raw<T, D>(cv, Tile<T, kC, D>{sm_v[0]}, rtid);
         // Loads past the segment are aimed at row N: out of the buffer's range, they
         // return zeros without touching memory, and the loop stays branch free.
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
             // Stage the next chunk into the other buffer (idle after the last chunk),
             // then S_E += E(K)^T V, z_E += colsum E(K), P += colsum V, published
             // for the next chunk.
-            stage_elu<T, D>(ck, Tile<T, kC, D>{sm_e[B ^ 1]}, rtid);
+            stage_elu<T, D, FM>(ck, Tile<T, kC, D>{sm_e[B ^ 1]}, rtid);
             stage_raw<T, D>(cv, Tile<T, kC, D>{sm_v[B ^ 1]}, rtid);
             ck.load(bk, c0 + 2 * kC < tok_end ? c0 + 2 * kC : N, rtid);
             cv.load(bv, c0 + 2 * kC < tok_end ? c0 + 2 * kC : N, rtid);
@@ -281,7 +281,8 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
                         const float pb = sp[b];
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            s[(int64_t)((ST::at0(w) + ia) * 16 + 4 * g + e) * D + b] = pb + st[ia][ib][e];
+                            s[(int64_t)((ST::at0(w) + ia) * 16 + 4 * g + e) * D + b] =
+                                FM::kSplit ? pb + st[ia][ib][e] : st[ia][ib][e];
                     }
             }
             if (z_out != nullptr && ST::owns_vec(w) && (lane & 15) == 0) {
@@ -290,7 +291,8 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         z_out[(int64_t)bh * D + (ST::vt0(w) + x) * 16 + 4 * g + e] =
-                            (init_n != nullptr ? init_n[bh] + (float)N : (float)N) + vz[x][e];
+                            FM::kSplit ? (init_n != nullptr ? init_n[bh] + (float)N : (float)N) + vz[x][e]
+                                       : vz[x][e];
             }
         }
         return;
@@ -324,12 +326,16 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
         const int tl = 16 * tt + (lane & 15);  // this lane's token (accumulator column)
 
         F qf[D / KS];
-        qr.phi_ops(qf);
+        qr.template phi_ops<FM>(qf);
         qr.load(bq, more ? c0 + kC + 16 * ((w + ci + 1) & 3) : N, lane);
-        f32x4 acc_q = zero4();
+        // q_sum_t, the weight of the rank-1 parts (unsplit features have none).
+        float qs_t = 0.f;
+        if constexpr (FM::kSplit) {
+            f32x4 acc_q = zero4();
 #pragma unroll
-        for (int k0 = 0; k0 < D; k0 += KS) acc_q = M::mma(one, qf[k0 / KS], acc_q);
-        const float qs_t = acc_q[0];
+            for (int k0 = 0; k0 < D; k0 += KS) acc_q = M::mma(one, qf[k0 / KS], acc_q);
+            qs_t = acc_q[0];
+        }
 
         f32x4 acc[DT + 1];
 #pragma unroll
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
 // ---------------------------------------------------------------------------------------
 // noncausal_fwd: every row reads the head's total state; each wavefront works
 // on its own token tiles with phi(Q) in registers (no barrier in the loop).
-template <typename T, int D>
+template <typename T, int D, class FM = FeatElu>
 __global__ __launch_bounds__(kBlock) void noncausal_fwd_kernel(const T* __restrict__ q, T* __restrict__ o,
                                                                const float* __restrict__ total, int ntotal, int N,
                                                                int cps, int nseg, int BH) {
@@ -434,7 +440,7 @@ __global__ __launch_bounds__(kBlock) void noncausal_fwd_kernel(const T* __restri
 
     for (int c0 = tok_begin; c0 < tok_end; c0 += kC) {
         typename M::frag qf[D / KS];
-        const float zdot = sum_over_groups(qr.phi_ops(qf, s_z, lane));
+        const float zdot = sum_over_groups(qr.template phi_ops<FM>(qf, s_z, lane));
         qr.load(bq, c0 + kC < tok_end ? c0 + kC + t0 : N, lane);
         const typename M::frag one = M::ones();
         f32x4 acc_q = zero4();
@@ -444,11 +450,11 @@ __global__ __launch_bounds__(kBlock) void noncausal_fwd_kernel(const T* __restri
 #pragma unroll
         for (int k0 = 0; k0 < D; k0 += KS) {
             const typename M::frag yf = qf[k0 / KS];
-            acc_q = M::mma(one, yf, acc_q);
+            if constexpr (FM::kSplit) acc_q = M::mma(one, yf, acc_q);
 #pragma unroll
             for (int m = 0; m < DT; ++m) acc[m] = M::mma(M::ld(tSt, 16 * m, k0, lane), yf, acc[m]);
         }
-        const float qs_t = acc_q[0];
+        const float qs_t = FM::kSplit ? acc_q[0] : 0.f;  // weight of the rank-1 parts (none when unsplit)
         const float inv = rcp_f(n * qs_t + zdot);
         const int tok = c0 + tl;
 #pragma unroll
@@ -469,22 +475,24 @@ __global__ __launch_bounds__(kBlock) void noncausal_fwd_kernel(const T* __restri
 // means over the feature index a, so that S0_E and z0_E hold only the deviations
 // (as small as a prefix's own S_E, z_E; the rank-1 parts stay in fp32).  Out: the
 // record [S0_E^T | z0_E | P0] and n0 per head.  Either input may be null (zero).
+// split = 0 (features carried unsplit): P0 = 0, n0 = 0, the record is S0, z0 itself.
 // Thread b handles value column b (fixed-order sums: bitwise reproducible).
 template <int D>
 __global__ __launch_bounds__(kBlock) void state_split_kernel(const float* __restrict__ S0, const float* __restrict__ z0,
-                                                             float* __restrict__ init, float* __restrict__ init_n) {
+                                                             float* __restrict__ init, float* __restrict__ init_n,
+                                                             int split) {
     const int bh = blockIdx.x, b = threadIdx.x;
     float* r = init + (int64_t)bh * Rec<D>::kSize;
     const float* Sh = S0 != nullptr ? S0 + (int64_t)bh * D * D : nullptr;
     const float* zh = z0 != nullptr ? z0 + (int64_t)bh * D : nullptr;
     float n0 = 0.f;
-    if (zh != nullptr) {
+    if (zh != nullptr && split) {
         for (int a = 0; a < D; ++a) n0 += zh[a];
         n0 *= 1.f / (float)D;
     }
     if (b >= D) return;
     float p = 0.f;
-    if (Sh != nullptr) {
+    if (Sh != nullptr && split) {
         for (int a = 0; a < D; ++a) p += Sh[a * D + b];
         p *= 1.f / (float)D;
     }
@@ -537,9 +545,9 @@ SegPlan plan_segments(int64_t BH, int64_t N) {
     }
 
 hipError_t launch_state_split(int d, const float* S0, const float* z0, float* init, float* init_n, int64_t BH,
-                              hipStream_t s) {
+                              hipStream_t s, int feat) {
     LA_DISPATCH_D(d, hipLaunchKernelGGL((state_split_kernel<D>), dim3((unsigned)BH), dim3(kBlock), 0, s, S0, z0, init,
-                                        init_n));
+                                        init_n, feat == kFeatGiven ? 0 : 1));
     return hipGetLastError();
 }
 
@@ -553,17 +561,24 @@ hipError_t launch_copy_or_zero(float* p, const float* src, size_t n, hipStream_t
 
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s) { return launch_copy_or_zero(p, nullptr, n, s); }
 
-hipError_t launch_seg_state(int dt, int d, const void* k, const void* v, float* rec, int64_t BH, int64_t N,
-                            SegPlan p, hipStream_t s) {
+template <class FM>
+static hipError_t launch_seg_state_fm(int dt, int d, const void* k, const void* v, float* rec, int64_t BH, int64_t N,
+                                      SegPlan p, hipStream_t s) {
     const dim3 grid((unsigned)(p.nseg * BH));
     if (dt == kBF16) {
-        LA_DISPATCH_D(d, hipLaunchKernelGGL((seg_state_kernel<bf16, D>), grid, dim3(kBlock), 0, s, (const bf16*)k,
+        LA_DISPATCH_D(d, hipLaunchKernelGGL((seg_state_kernel<bf16, D, FM>), grid, dim3(kBlock), 0, s, (const bf16*)k,
                                             (const bf16*)v, rec, (int)N, p.cps, p.nseg, (int)BH));
     } else {
-        LA_DISPATCH_D(d, hipLaunchKernelGGL((seg_state_kernel<float, D>), grid, dim3(kBlock), 0, s, (const float*)k,
+        LA_DISPATCH_D(d, hipLaunchKernelGGL((seg_state_kernel<float, D, FM>), grid, dim3(kBlock), 0, s, (const float*)k,
                                             (const float*)v, rec, (int)N, p.cps, p.nseg, (int)BH));
     }
     return hipGetLastError();
+}
+
+hipError_t launch_seg_state(int dt, int d, const void* k, const void* v, float* rec, int64_t BH, int64_t N,
+                            SegPlan p, hipStream_t s, int feat) {
+    return feat == kFeatGiven ? launch_seg_state_fm<FeatGiven>(dt, d, k, v, rec, BH, N, p, s)
+                              : launch_seg_state_fm<FeatElu>(dt, d, k, v, rec, BH, N, p, s);
 }
 
 hipError_t launch_total(int d, const float* rec, float* total, int64_t BH, int nseg, hipStream_t s) {
@@ -580,12 +595,13 @@ hipError_t launch_scan(int d, float* rec, int64_t BH, int nseg, int dir, hipStre
     return hipGetLastError();
 }
 
-hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const void* v, void* o, float* den_out,
-                             const float* rec, float* S_out, float* z_out, int64_t BH, int64_t N, SegPlan p,
-                             hipStream_t s, const float* init, const float* init_n) {
+template <class FM>
+static hipError_t launch_causal_fwd_fm(int dt, int d, const void* q, const void* k, const void* v, void* o,
+                                       float* den_out, const float* rec, float* S_out, float* z_out, int64_t BH,
+                                       int64_t N, SegPlan p, hipStream_t s, const float* init, const float* init_n) {
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_CFWD(TT, DD)                                                                                          \
-    hipLaunchKernelGGL((causal_fwd_kernel<TT, DD>), grid, dim3(2 * kBlock), 0, s, (const TT*)q, (const TT*)k,       \
+    hipLaunchKernelGGL((causal_fwd_kernel<TT, DD, FM>), grid, dim3(2 * kBlock), 0, s, (const TT*)q, (const TT*)k,   \
                        (const TT*)v, (TT*)o, den_out, rec, S_out, z_out, init, init_n, (int)N, p.cps, p.nseg,     \
                        (int)BH, (int)p.scan)
     if (dt == kBF16) {
@@ -606,18 +622,33 @@ hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const 
     return hipGetLastError();
 }
 
-hipError_t launch_noncausal_fwd(int dt, int d, const void* q, void* o, const float* total, int ntotal, int64_t BH,
-                                int64_t N, SegPlan p, hipStream_t s) {
+hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const void* v, void* o, float* den_out,
+                             const float* rec, float* S_out, float* z_out, int64_t BH, int64_t N, SegPlan p,
+                             hipStream_t s, const float* init, const float* init_n, int feat) {
+    return feat == kFeatGiven
+               ? launch_causal_fwd_fm<FeatGiven>(dt, d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, p, s, init, init_n)
+               : launch_causal_fwd_fm<FeatElu>(dt, d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, p, s, init, init_n);
+}
+
+template <class FM>
+static hipError_t launch_noncausal_fwd_fm(int dt, int d, const void* q, void* o, const float* total, int ntotal,
+                                          int64_t BH, int64_t N, SegPlan p, hipStream_t s) {
     const dim3 grid((unsigned)(p.nseg * BH));
     if (dt == kBF16) {
-        LA_DISPATCH_D(d, hipLaunchKernelGGL((noncausal_fwd_kernel<bf16, D>), grid, dim3(kBlock), 0, s,
+        LA_DISPATCH_D(d, hipLaunchKernelGGL((noncausal_fwd_kernel<bf16, D, FM>), grid, dim3(kBlock), 0, s,
                                             (const bf16*)q, (bf16*)o, total, ntotal, (int)N, p.cps, p.nseg, (int)BH));
     } else {
-        LA_DISPATCH_D(d, hipLaunchKernelGGL((noncausal_fwd_kernel<float, D>), grid, dim3(kBlock), 0, s,
+        LA_DISPATCH_D(d, hipLaunchKernelGGL((noncausal_fwd_kernel<float, D, FM>), grid, dim3(kBlock), 0, s,
                                             (const float*)q, (float*)o, total, ntotal, (int)N, p.cps, p.nseg,
                                             (int)BH));
     }
     return hipGetLastError();
+}
+
+hipError_t launch_noncausal_fwd(int dt, int d, const void* q, void* o, const float* total, int ntotal, int64_t BH,
+                                int64_t N, SegPlan p, hipStream_t s, int feat) {
+    return feat == kFeatGiven ? launch_noncausal_fwd_fm<FeatGiven>(dt, d, q, o, total, ntotal, BH, N, p, s)
+                              : launch_noncausal_fwd_fm<FeatElu>(dt, d, q, o, total, ntotal, BH, N, p, s);
 }
 
 }  // namespace la

@@ -20,6 +20,9 @@ constexpr int kBlock = 256;      // threads per workgroup (4 wavefronts)
 #endif
 
 enum DType { kF32 = 0, kBF16 = 1 };
+// Feature map of the sequence kernels: elu + 1 applied to the inputs, or inputs that
+// already are the features.
+enum FeatureMap { kFeatElu = 0, kFeatGiven = 1 };
 
 // Sequence segmentation: each (segment, head) pair is one workgroup; a segment
 // is `cps` consecutive chunks.  A segment starts from the sum of the fp32 state
@@ -43,7 +46,7 @@ inline int64_t rec_floats(int64_t d) { return d * d + 2 * d; }
 // Forward pieces.  Segment records are per-segment aggregates laid out
 // [BH][nseg][rec_floats(d)]; workgroups are numbered segment-major.
 hipError_t launch_seg_state(int dt, int d, const void* k, const void* v, float* rec, int64_t BH,
-                            int64_t N, SegPlan p, hipStream_t s);
+                            int64_t N, SegPlan p, hipStream_t s, int feat = kFeatElu);
 // Per-head sum of the segment records (segment order).
 hipError_t launch_total(int d, const float* rec, float* total, int64_t BH, int nseg, hipStream_t s);
 // In place: record s becomes the sum of the records before it (dir > 0) or after it (dir < 0),
@@ -56,15 +59,15 @@ hipError_t launch_scan(int d, float* rec, int64_t BH, int nseg, int dir, hipStre
 hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const void* v, void* o,
                              float* den_out, const float* rec, float* S_out, float* z_out, int64_t BH,
                              int64_t N, SegPlan p, hipStream_t s, const float* init = nullptr,
-                             const float* init_n = nullptr);
+                             const float* init_n = nullptr, int feat = kFeatElu);
 // A start state (S0 [BH][d][d], z0 [BH][d], either nullable = zero) in the carried split
 // form: one record [S0_E^T | z0_E | P0] per head in init, and n0 per head in init_n.
 hipError_t launch_state_split(int d, const float* S0, const float* z0, float* init, float* init_n, int64_t BH,
-                              hipStream_t s);
+                              hipStream_t s, int feat = kFeatElu);
 // Non-causal outputs from each head's state: the in-order sum of `ntotal`
 // records per head at `total` (the segment records, or one precomputed total).
 hipError_t launch_noncausal_fwd(int dt, int d, const void* q, void* o, const float* total, int ntotal,
-                                int64_t BH, int64_t N, SegPlan p, hipStream_t s);
+                                int64_t BH, int64_t N, SegPlan p, hipStream_t s, int feat = kFeatElu);
 
 // Backward pieces.  bwd_prefix starts each segment from the sum of the forward
 // records before it and writes the segment's suffix-state aggregate to rrec;
@@ -110,6 +113,11 @@ hipError_t launch_decode(int dt, int d, float* S, float* z, const void* q, const
 // T decode steps per key/value head in one pass over its state, read by G query heads;
 // k, v are [BHkv][T][d], q, o are [BHkv][G][T][d].
 hipError_t launch_decode_steps(int dt, int d, float* S, float* z, const void* q, const void* k,
-                               const void* v, void* o, int64_t BHkv, int64_t T, int64_t G, hipStream_t s);
+                               const void* v, void* o, int64_t BHkv, int64_t T, int64_t G, hipStream_t s,
+                               int feat = kFeatElu);
+// FAVOR+ random features of `rows` rows of x [rows][d]: out[r][i] = exp(omega_i . x_r - |x_r|^2 / 2)
+// for the d rows of omega [d][d] fp32 (m = d features; the constant 1/sqrt(m) is left out).
+hipError_t launch_favor_features(int dt, int d, const void* x, const float* omega, void* out, int64_t rows,
+                                 hipStream_t s);
 
 }  // namespace la

@@ -1,0 +1,126 @@
+"""GPU parity of the FAVOR+ path (Performer section of the page "Efficient
+Transformers Survey") against the fp64 oracle: the random-feature kernel, the
+forward calls and multi-token decode on given features.  Queries and keys are
+pre-normalized by d^(-1/4) as the page prescribes (la_inputs.favor_qkv); without
+it the features of d = 128 rows fall below fp32's range.
+
+The library's features leave out the page's constant 1/sqrt(m) (m = d): it
+cancels in every output O, so outputs compare directly, while features, states
+and denominators compare after scaling the oracle's by sqrt(m) (states, z) or m
+(den).  Directions omega come from la_inputs.favor_omega (rows ~ N(0, I_d)).
+"""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import la_inputs as inp  # noqa: E402
+from test_parity import TOL, draw, f64, record, slice_err  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def la():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_attention_02_amd as m
+    m.load_library()
+    return m
+
+
+# Features of bf16 inputs are rounded to bf16 (relative 2^-9 per element); fp32 keeps
+# the exponent to fp32 rounding of a d-term dot product.
+FEAT_TOL = {torch.float32: 1e-5, torch.bfloat16: 2.0 ** -8}
+# States and denominators on bf16 features: sums of features each rounded once by up to
+# 2^-9; FAVOR+ features are heavy-tailed (lognormal), so a few large terms carry the
+# sums and the rounding does not average out: the bar is 2.5 * 2^-9 (fp32: 1e-4).
+SUM_TOL = {torch.float32: 1e-4, torch.bfloat16: 2.5 * 2.0 ** -9}
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_favor_features(la, oracle, d, dtype):
+    rows = 777  # several workgroups of 256 rows and a ragged tail
+    x = inp.normal((rows, d), inp.generator(d), dtype, d ** -0.25).cuda()
+    om = inp.favor_omega(d, seed=d + 1).cuda()
+    f = la.favor_features(x, om)
+    torch.cuda.synchronize()
+    ref = oracle.favor_features(f64(x), f64(om)) * math.sqrt(d)
+    err = slice_err(f[None], ref[None])
+    assert (f64(f) > 0).all()
+    record(f"favor_features d={d} {dtype}", f=err)
+    assert err < FEAT_TOL[dtype], err
+
+
+SHAPES = [(1, 1, 1, 32), (1, 2, 63, 64), (2, 3, 200, 64), (1, 2, 300, 128), (2, 2, 1000, 64), (1, 8, 64 * 130 + 17, 64)]
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_favor_forward(la, oracle, shape, dtype, causal):
+    B, H, N, d = shape
+    if dtype == torch.float32 and d == 128 and causal:
+        pytest.skip("fp32 causal path is built for d <= 64")
+    q, k, v = (t.cuda() for t in inp.favor_qkv(B, H, N, d, dtype, seed=N + 40))
+    om = inp.favor_omega(d, seed=N + 41).cuda()
+    fq, fk = la.favor_features(q, om), la.favor_features(k, om)
+    if causal:
+        o, den, S, z = la.la_forward_causal_features(fq, fk, v, return_den=True, return_state=True)
+    else:
+        o = la.la_forward_noncausal_features(fq, fk, v)
+    torch.cuda.synchronize()
+    rfq, rfk = oracle.favor_features(f64(q), f64(om)), oracle.favor_features(f64(k), f64(om))
+    errs = {}
+    if causal:
+        ro, rden, rS, rz = oracle.forward_features(rfq, rfk, f64(v), True, return_den=True, return_state=True)
+        m = float(d)
+        errs.update(den=slice_err(den, rden * m), S=slice_err(S, rS * math.sqrt(m)),
+                    z=slice_err(z[..., None], rz[..., None] * math.sqrt(m)))
+    else:
+        ro = oracle.forward_features(rfq, rfk, f64(v), False)
+    errs["o"] = slice_err(o, ro)
+    record(f"favor_fwd {'causal' if causal else 'noncausal'} {B}x{H}x{N}x{d} {dtype}", **errs)
+    assert errs["o"] < TOL[dtype], errs
+    if causal:
+        assert max(errs["den"], errs["S"], errs["z"]) < SUM_TOL[dtype], errs
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_favor_prefill_then_decode(la, oracle, dtype):
+    """Prefill on FAVOR+ features, then multi-token decode with grouped heads from the
+    state it left: the oracle runs each query head over its key/value head's whole
+    sequence of features."""
+    B, Hkv, G, N0, T, d = 2, 2, 3, 150, 9, 64
+    H = Hkv * G
+    om = inp.favor_omega(d, seed=5).cuda()
+    pq, pk, pv = (t.cuda() for t in inp.favor_qkv(B, Hkv, N0, d, dtype, seed=6))
+    _, S, z = la.la_forward_causal_features(la.favor_features(pq, om), la.favor_features(pk, om), pv,
+                                            return_state=True)
+    q = inp.favor_qkv(B, H, T, d, dtype, seed=7)[0].cuda()
+    _, k, v = (t.cuda() for t in inp.favor_qkv(B, Hkv, T, d, dtype, seed=8))
+    o = la.la_decode_steps_features(S, z, la.favor_features(q, om), la.favor_features(k, om), v)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for h in range(H):
+        j = h // G
+        kk, vv = np.concatenate([f64(pk[:, j]), f64(k[:, j])], 1), np.concatenate([f64(pv[:, j]), f64(v[:, j])], 1)
+        qq = np.concatenate([f64(pq[:, j]), f64(q[:, h])], 1)  # prefix rows are not compared
+        ro = oracle.forward_features(oracle.favor_features(qq, f64(om)), oracle.favor_features(kk, f64(om)), vv, True)
+        worst = max(worst, slice_err(o[:, h], ro[:, N0:]))
+    record(f"favor prefill+decode {dtype}", o=worst)
+    assert worst < TOL[dtype], worst
+
+
+def test_given_elu_features_match_builtin_map(la):
+    """Features elu(x) + 1 applied by the caller give the built-in map's outputs (fp32)."""
+    q, k, v, _ = draw(2, 3, 333, 64, torch.float32, seed=50)
+    phi = lambda x: torch.nn.functional.elu(x) + 1.0
+    a = la.la_forward_causal_features(phi(q), phi(k), v)
+    b = la.la_forward_causal(q, k, v)
+    c = la.la_forward_noncausal_features(phi(q), phi(k), v)
+    e = la.la_forward_noncausal(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.allclose(a, b, rtol=1e-4, atol=1e-5) and torch.allclose(c, e, rtol=1e-4, atol=1e-5)
