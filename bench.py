@@ -31,7 +31,9 @@ The JSON line also carries
                   key/value states), each with its throughput and roofline
                   fraction;
   * cpu_baseline: the fp64 CPU oracle timed on this host on repeated full
-                  steps of the same workload (bounded to about 10 s).
+                  steps of the same workload (bounded to about 10 s); each
+                  entry of calls carries the same for its own workload
+                  (cpu_oracle: about 1.5 s on a sample of heads or steps).
 
 The roofline's "traffic" is the dominant kernel's measured HBM bytes per
 launch: FETCH_SIZE and WRITE_SIZE from two rocprofv3 counter passes over this
@@ -51,6 +53,8 @@ import math
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -441,6 +445,69 @@ def cpu_baseline(args, inp, torch, mid_set):
                       f"{dt:.1f} s wall"}
 
 
+def call_oracles(args, inp, torch):
+    """The fp64 oracle timed on a bounded sample of each call's workload (a few heads, or
+    a few decode steps), as tokens/s of the whole workload: sample token-heads per
+    second divided by the workload's heads per token."""
+    import oracle
+
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    oracle.set_threads(cores)
+    f64 = inp.to_f64
+
+    def rate(fn, token_heads, heads_per_token, budget=1.5):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            if time.perf_counter() - t0 >= budget:
+                break
+        dt = time.perf_counter() - t0
+        return round(reps * token_heads / heads_per_token / dt, 1), reps, dt
+
+    out = {}
+
+    def record(name, fn, token_heads, heads_per_token, threads, what):
+        v, reps, dt = rate(fn, token_heads, heads_per_token)
+        out[name] = {"value": v, "unit": "tokens/s", "cores": min(cores, threads), "kind": "oracle",
+                     "sample": f"{reps} x {what}, fp64, {dt:.1f} s wall"}
+
+    w = inp.MID
+    hs = 8
+    q, k, v, do = (f64(t) for t in inp.qkv(1, hs, w.N, w.d, torch.float32, seed=90, with_dout=True))
+    record("mid_noncausal_fwd", lambda: oracle.forward_noncausal(q, k, v), hs * w.N, w.H,
+           hs, f"non-causal forward of {hs} of the 64 Mid heads")
+    record("mid_noncausal_fwd_bwd", lambda: (oracle.forward_noncausal(q, k, v), oracle.backward_noncausal(q, k, v, do)),
+           hs * w.N, w.H, hs, f"non-causal forward + backward of {hs} Mid heads")
+    fq, fk, fv = (f64(t) for t in inp.favor_qkv(1, hs, w.N, w.d, torch.float32, seed=91))
+    om = f64(inp.favor_omega(w.d, seed=0))
+    record("mid_favor_causal_fwd",
+           lambda: oracle.forward_features(oracle.favor_features(fq, om), oracle.favor_features(fk, om), fv, True),
+           hs * w.N, w.H, hs, f"FAVOR+ features + causal forward of {hs} Mid heads")
+    L = inp.LONG
+    hl = 4
+    q, k, v, do = (f64(t) for t in inp.qkv(1, hl, L.N, L.d, torch.float32, seed=92, with_dout=True))
+    record("long_causal_fwd_bwd", lambda: (oracle.forward_causal(q, k, v), oracle.backward_causal(q, k, v, do)),
+           hl * L.N, L.H, hl, f"causal forward + backward of {hl} of the 128 Long heads")
+    V = inp.VERYLONG
+    q, k, v = (f64(t) for t in inp.qkv(1, 2, V.N // 8, V.d, torch.float32, seed=93))
+    record("verylong_causal_fwd", lambda: oracle.forward_causal(q, k, v), 2 * (V.N // 8), V.H,
+           2, f"causal forward of 2 heads over the first {V.N // 8} tokens of a Very long head")
+    D = inp.DECODE
+    hd, steps = 64, 32
+    S0 = np.abs(np.random.default_rng(94).standard_normal((hd, D.d, D.d))) + 1.0
+    z0 = np.abs(np.random.default_rng(95).standard_normal((hd, D.d))) * 100 + 100.0
+    sq, sk, sv = (f64(t) for t in inp.decode_tokens(1, hd, D.d, steps, torch.float32, seed=96))
+
+    def dec():
+        S, z = S0, z0
+        for t in range(steps):
+            _, S, z = oracle.decode_step(S, z, sq[t, 0], sk[t, 0], sv[t, 0])
+
+    record("decode", dec, hd * steps, D.H, hd, f"{steps} decode steps of {hd} head-states")
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -461,6 +528,12 @@ def main():
     res, mid_sets = bench_mid(args, la, inp, torch)
     calls = None if args.no_calls else bench_calls(args, la, inp, torch, mid_sets)
     cpu = None if args.no_cpu else cpu_baseline(args, inp, torch, mid_sets[0])
+    if calls is not None and not args.no_cpu:
+        orc = call_oracles(args, inp, torch)
+        for name, r in calls.items():
+            key = "decode" if name.startswith("decode") else name
+            if key in orc:
+                r["cpu_oracle"] = orc[key]
     line = {
         "metric": "causal LA fwd+bwd tokens/s, B4 H16 N4096 d64 bf16; % of HBM/MFMA roofline",
         "value": round(res["value"], 1),
