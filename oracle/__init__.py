@@ -60,6 +60,8 @@ def _load():
         f.argtypes = [i64, i64, i64, dp, dp, dp, dp, dp, dp, dp]
     lib.la_oracle_forward_causal_from.restype = None
     lib.la_oracle_forward_causal_from.argtypes = [i64, i64, i64, dp, dp, dp, dp, dp, dp, dp, dp, dp]
+    lib.la_oracle_backward_causal_state.restype = None
+    lib.la_oracle_backward_causal_state.argtypes = [i64, i64, i64] + [dp] * 13
     lib.la_oracle_favor_features.restype = None
     lib.la_oracle_favor_features.argtypes = [i64, i64, i64, dp, dp, dp]
     lib.la_oracle_forward_features.restype = None
@@ -176,6 +178,31 @@ def _bwd(name, q, k, v, dout):
 def backward_causal(q, k, v, dout):
     """Gradients (dq, dk, dv) of sum(dout * forward_causal(q, k, v))."""
     return _bwd("la_oracle_backward_causal", q, k, v, dout)
+
+
+def backward_causal_state(q, k, v, dout, S0=None, z0=None, dSN=None, dzN=None):
+    """Gradients (dq, dk, dv, dS0, dz0) of sum(dout * o) + sum(dSN * S_N) + sum(dzN * z_N) for
+    forward_causal(q, k, v, S0=S0, z0=z0) with final state (S_N, z_N)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    if not (q.shape == k.shape == v.shape == dout.shape):
+        raise ValueError("q, k, v, dout must have the same shape")
+    bh, n, d = _heads(q)
+    st = q.shape[:-2]
+    def opt(x, shape):
+        if x is None:
+            return None
+        x = _f64(x)
+        if x.shape != shape:
+            raise ValueError(f"expected shape {shape}")
+        return x
+    S0, dSN = opt(S0, st + (d, d)), opt(dSN, st + (d, d))
+    z0, dzN = opt(z0, st + (d,)), opt(dzN, st + (d,))
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    dS0, dz0 = np.empty(st + (d, d)), np.empty(st + (d,))
+    _load().la_oracle_backward_causal_state(bh, n, d, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(S0), _ptr(z0),
+                                            _ptr(dSN), _ptr(dzN), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dS0),
+                                            _ptr(dz0))
+    return dq, dk, dv, dS0, dz0
 
 
 def backward_noncausal(q, k, v, dout):

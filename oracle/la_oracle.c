@@ -158,12 +158,25 @@ void la_oracle_forward_causal(int64_t BH, int64_t N, int64_t d, const double* q,
  * with R_j = sum_{i >= j} phi(Q_i) G_i^T and r_j = sum_{i >= j} g_i phi(Q_i)
  * (all i for the non-causal form), then dQ = dphi(Q) * phi'(Q) and
  * dK = dphi(K) * phi'(K) elementwise. */
-static void bwd_head(int64_t N, int64_t d, int causal, const double* q, const double* k,
-                     const double* v, const double* dout, double* dq, double* dk, double* dv) {
+/* With a start state (causal only): the forward's recurrence starts from
+ * (S0, z0), and the loss may also depend on the final state (S_N, z_N) with
+ * upstream gradients (dSN, dzN).  S_N = S0 + sum_j phi(K_j) V_j^T, so dSN adds
+ * to every suffix sum R_j and dzN to every r_j, i.e. the suffix sums start from
+ * (dSN, dzN); and S_i = S0 + ..., so the gradient reaching S0 (and z0) is the
+ * suffix sum at the first token, R_0 (r_0).  Any of these may be NULL (zero; no
+ * output). */
+static void bwd_head_state(int64_t N, int64_t d, int causal, const double* q, const double* k,
+                           const double* v, const double* dout, const double* S0, const double* z0,
+                           const double* dSN, const double* dzN, double* dq, double* dk, double* dv,
+                           double* dS0, double* dz0) {
     double* S = zalloc(d * d);
     double* z = zalloc(d);
     double* R = zalloc(d * d);
     double* r = zalloc(d);
+    if (S0) memcpy(S, S0, (size_t)(d * d) * sizeof(double));
+    if (z0) memcpy(z, z0, (size_t)d * sizeof(double));
+    if (dSN) memcpy(R, dSN, (size_t)(d * d) * sizeof(double));
+    if (dzN) memcpy(r, dzN, (size_t)d * sizeof(double));
     double* f = zalloc(d);
     double* kf = zalloc(d);
     double* O = zalloc(d);
@@ -236,6 +249,8 @@ static void bwd_head(int64_t N, int64_t d, int causal, const double* q, const do
             dv[j * d + b] = s;
         }
     }
+    if (dS0) memcpy(dS0, R, (size_t)(d * d) * sizeof(double));
+    if (dz0) memcpy(dz0, r, (size_t)d * sizeof(double));
     free(S);
     free(z);
     free(R);
@@ -245,6 +260,27 @@ static void bwd_head(int64_t N, int64_t d, int causal, const double* q, const do
     free(O);
     free(G);
     free(g);
+}
+
+static void bwd_head(int64_t N, int64_t d, int causal, const double* q, const double* k,
+                     const double* v, const double* dout, double* dq, double* dk, double* dv) {
+    bwd_head_state(N, d, causal, q, k, v, dout, NULL, NULL, NULL, NULL, dq, dk, dv, NULL, NULL);
+}
+
+void la_oracle_backward_causal_state(int64_t BH, int64_t N, int64_t d, const double* q,
+                                     const double* k, const double* v, const double* dout,
+                                     const double* S0, const double* z0, const double* dSN,
+                                     const double* dzN, double* dq, double* dk, double* dv,
+                                     double* dS0, double* dz0) {
+    int nt = la_oracle_get_threads();
+    (void)nt;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t h = 0; h < BH; ++h) {
+        const int64_t off = h * N * d, so = h * d * d, zo = h * d;
+        bwd_head_state(N, d, 1, q + off, k + off, v + off, dout + off, S0 ? S0 + so : NULL,
+                       z0 ? z0 + zo : NULL, dSN ? dSN + so : NULL, dzN ? dzN + zo : NULL, dq + off,
+                       dk + off, dv + off, dS0 ? dS0 + so : NULL, dz0 ? dz0 + zo : NULL);
+    }
 }
 
 void la_oracle_backward_causal(int64_t BH, int64_t N, int64_t d, const double* q,

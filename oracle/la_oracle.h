@@ -67,6 +67,17 @@ void la_oracle_backward_causal(int64_t BH, int64_t N, int64_t d,
                                const double* q, const double* k, const double* v,
                                const double* dout, double* dq, double* dk, double* dv);
 
+/* Causal backward of the recurrence started from (S0, z0) (la_oracle_forward_causal_from),
+ * for L = sum(dout * o) + sum(dSN * S_N) + sum(dzN * z_N), i.e. with upstream gradients
+ * dSN [BH][d][d], dzN [BH][d] of the final state: the suffix sums start from them, and
+ * dS0, dz0 receive the gradient of L with respect to the start state (the suffix sums
+ * at the first token).  S0, z0, dSN, dzN, dS0, dz0 may be NULL (zero / not wanted). */
+void la_oracle_backward_causal_state(int64_t BH, int64_t N, int64_t d, const double* q,
+                                     const double* k, const double* v, const double* dout,
+                                     const double* S0, const double* z0, const double* dSN,
+                                     const double* dzN, double* dq, double* dk, double* dv,
+                                     double* dS0, double* dz0);
+
 /* Non-causal backward (same algebra with global S, z and global suffix sums). */
 void la_oracle_backward_noncausal(int64_t BH, int64_t N, int64_t d,
                                   const double* q, const double* k, const double* v,

@@ -321,6 +321,63 @@ def test_start_state_matches_decode_steps(oracle):
     assert rel(Sd, S) < 1e-13 and rel(zd, z) < 1e-13
 
 
+# ---- backward of the recurrence from a start state ------------------------------------------------
+def _np_forward_from(q, k, v, S0, z0):
+    """Recurrence from (S0, z0) by cumulative sums (numpy): outputs and final state."""
+    kf, qf = np_phi(k), np_phi(q)
+    S = S0[None] + np.cumsum(kf[:, :, None] * v[:, None, :], axis=0)
+    z = z0[None] + np.cumsum(kf, axis=0)
+    o = np.einsum("ia,iab->ib", qf, S) / np.einsum("ia,ia->i", qf, z)[:, None]
+    return o, S[-1], z[-1]
+
+
+def test_backward_from_state_finite_differences(oracle):
+    """Gradients of sum(dO O) + sum(dSN S_N) + sum(dzN z_N) for the recurrence from (S0, z0),
+    against central differences of a numpy cumulative-sum forward (q, k, v, S0 and z0)."""
+    rng = np.random.default_rng(100)
+    n, d, h = 9, 4, 1e-6
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    S0, z0 = rng.uniform(0.5, 2.0, (d, d)), rng.uniform(2.0, 4.0, d)
+    dSN, dzN = rng.standard_normal((d, d)), rng.standard_normal(d)
+
+    def loss(q, k, v, S0, z0):
+        o, S, z = _np_forward_from(q, k, v, S0, z0)
+        return (do * o).sum() + (dSN * S).sum() + (dzN * z).sum()
+
+    args = [q, k, v, S0, z0]
+    got = oracle.backward_causal_state(q, k, v, do, S0=S0, z0=z0, dSN=dSN, dzN=dzN)
+    for which, g in enumerate(got):
+        fd = np.zeros_like(args[which])
+        for idx in np.ndindex(*fd.shape):
+            plus = [a.copy() for a in args]
+            minus = [a.copy() for a in args]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            fd[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        assert rel(g, fd) < 1e-7, which
+
+
+def test_backward_from_state_chains_pieces(oracle):
+    """A sequence's backward in two pieces: the second piece from the state the first left,
+    then the first with the second's start-state gradient as its final-state gradient,
+    equals the backward of the whole sequence."""
+    shape, p = (2, 2, 19, 5), 8
+    q, k, v, do = rand(shape, 101), rand(shape, 102), rand(shape, 103), rand(shape, 104)
+    full = oracle.backward_causal(q, k, v, do)
+    cut = lambda x, a, b: x[..., a:b, :]
+    _, S_p, z_p = oracle.forward_causal(cut(q, 0, p), cut(k, 0, p), cut(v, 0, p), return_state=True)
+    dq2, dk2, dv2, dS0, dz0 = oracle.backward_causal_state(cut(q, p, None), cut(k, p, None), cut(v, p, None),
+                                                           cut(do, p, None), S0=S_p, z0=z_p)
+    dq1, dk1, dv1, _, _ = oracle.backward_causal_state(cut(q, 0, p), cut(k, 0, p), cut(v, 0, p), cut(do, 0, p),
+                                                       dSN=dS0, dzN=dz0)
+    for f, a, b in zip(full, (dq1, dk1, dv1), (dq2, dk2, dv2)):
+        assert rel(np.concatenate([a, b], axis=-2), f) < 1e-12
+    # no state and no upstream gradient: the plain backward, bit for bit
+    plain = oracle.backward_causal_state(q, k, v, do)
+    for a, b in zip(plain[:3], full):
+        np.testing.assert_array_equal(a, b)
+
+
 # ---- FAVOR+ features and attention on given features ------------------------------------------
 def test_favor_features_special_directions(oracle):
     """omega = 0 leaves only the norm factor; omega = a unit vector picks one coordinate."""
