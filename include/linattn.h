@@ -148,6 +148,22 @@ la_status la_backward_noncausal(const void* q, const void* k, const void* v, con
                                 size_t saved_state_bytes, int64_t B, int64_t H, int64_t N, int64_t d,
                                 la_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Causal backward of la_forward_causal started from (S0, z0), for a sequence fed in
+ * pieces (truncated back-propagation): the loss may also depend on the final state
+ * (S_N, z_N), whose gradients dS_out [B][H][d][d], dz_out [B][H][d] fp32 (the start
+ * state's gradients the next piece's backward returned) join every suffix sum
+ * R_j, r_j; dS0, dz0 [B][H][d][d], [B][H][d] fp32 receive the gradients of the
+ * start state, R_0 and r_0, to pass to the previous piece as its dS_out, dz_out.
+ * Every state pointer is nullable (NULL input: zero; NULL output: not written);
+ * with all NULL this is la_backward_causal.  q, k, v, dout, dq, dk, dv, chunk,
+ * dtype, workspace (la_workspace_size(LA_OP_BWD_CAUSAL, ...)) and errors as there;
+ * the carried state is always rebuilt from k, v (no saved state). */
+la_status la_backward_causal_state(const void* q, const void* k, const void* v, const void* dout,
+                                   const float* S0, const float* z0, const float* dS_out,
+                                   const float* dz_out, void* dq, void* dk, void* dv, float* dS0,
+                                   float* dz0, int64_t B, int64_t H, int64_t N, int64_t d, int chunk,
+                                   la_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
+
 /* One recurrent decode step per (b, h), in place ("Why It Matters": constant
  * memory per step): S += phi(k) v^T, z += phi(k), then
  * o = phi(q)^T S / phi(q)^T z.  S [B][H][d][d] and z [B][H][d] are fp32 and

@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     LinAttnError,
     causal_linear_attention,
     la_backward_causal,
+    la_backward_causal_state,
     la_backward_noncausal,
     la_decode_step,
     la_decode_steps,

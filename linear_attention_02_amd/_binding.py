@@ -22,7 +22,8 @@ LA_OP_FWD_NONCAUSAL, LA_OP_FWD_CAUSAL, LA_OP_BWD_CAUSAL, LA_OP_BWD_NONCAUSAL = 0
 
 EXPORTS = ("la_workspace_size", "la_saved_state_size", "la_forward_noncausal", "la_forward_causal", "la_backward_causal",
            "la_backward_noncausal", "la_decode_step", "la_decode_steps", "la_favor_features",
-           "la_forward_causal_features", "la_forward_noncausal_features", "la_decode_steps_features", "la_status_string", "la_last_error_message", "la_version",
+           "la_forward_causal_features", "la_forward_noncausal_features", "la_decode_steps_features",
+           "la_backward_causal_state", "la_status_string", "la_last_error_message", "la_version",
            "la_profile_enable", "la_profile_count", "la_profile_entry", "la_debug_set_wait_limit",
            "la_debug_wait_limit")
 
@@ -58,6 +59,8 @@ def load_library(path: str | None = None):
     lib.la_forward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.la_backward_causal.restype = i32
     lib.la_backward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.la_backward_causal_state.restype = i32
+    lib.la_backward_causal_state.argtypes = [vp] * 13 + [i64, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.la_backward_noncausal.restype = i32
     lib.la_backward_noncausal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_decode_step.restype = i32
@@ -248,6 +251,31 @@ def la_backward_noncausal(q, k, v, dout, *, out=None, workspace=None, saved_stat
                                                 _ptr(dv), _ptr(saved_state), _nbytes(saved_state), B, H, N, d,
                                                 _dtype_code(q.dtype), _ptr(ws), nbytes, _stream(q.device)))
     return dq, dk, dv
+
+
+def la_backward_causal_state(q, k, v, dout, *, S0=None, z0=None, dS_out=None, dz_out=None, chunk=0, out=None,
+                             workspace=None, want_state_grad=True):
+    """Gradients of sum(dout * o) + sum(dS_out * S_N) + sum(dz_out * z_N) for
+    la_forward_causal(q, k, v, S0=S0, z0=z0) with final state (S_N, z_N).
+
+    Returns (dq, dk, dv, dS0, dz0); dS0 [B,H,d,d] and dz0 [B,H,d] (fp32) are the start state's
+    gradients (None unless want_state_grad)."""
+    B, H, N, d = _check_seq(q, k, v, dout)
+    for a, b in ((S0, z0), (dS_out, dz_out)):
+        _check_state(a, b, B, H, d, q.device)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    else:
+        dq, dk, dv = out
+    dS0 = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device) if want_state_grad else None
+    dz0 = torch.empty((B, H, d), dtype=torch.float32, device=q.device) if want_state_grad else None
+    ws = _workspace(LA_OP_BWD_CAUSAL, B, H, N, d, q.dtype, q.device, chunk, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().la_backward_causal_state(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(S0), _ptr(z0),
+                                                   _ptr(dS_out), _ptr(dz_out), _ptr(dq), _ptr(dk), _ptr(dv),
+                                                   _ptr(dS0), _ptr(dz0), B, H, N, d, chunk, _dtype_code(q.dtype),
+                                                   _ptr(ws), nbytes, _stream(q.device)))
+    return dq, dk, dv, dS0, dz0
 
 
 def la_decode_step(S, z, q, k, v, *, out=None):

@@ -117,7 +117,7 @@ la_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_
 struct Layout {
     la::SegPlan plan;
     int64_t heads = 0;
-    size_t rec = 0, total = 0, rrec = 0, rtotal = 0, rowstat = 0, flags = 0, init = 0, init_n = 0;  // byte offsets
+    size_t rec = 0, total = 0, rrec = 0, rtotal = 0, rowstat = 0, flags = 0, init = 0, init_n = 0, rinit = 0;  // byte offsets
     bool fused = false;  // backward: both sweeps in one launch
     size_t bytes = 0;
 };
@@ -157,6 +157,13 @@ Layout layout(la_op op, int64_t B, int64_t H, int64_t N, int64_t d) {
             L.flags = off;
             off += align_up((size_t)BH * L.plan.nseg * sizeof(unsigned long long));
         }
+        // a start state in split form, its counts, and the record of final-state gradients
+        L.init = off;
+        off += align_up(totb);
+        L.init_n = off;
+        off += align_up((size_t)BH * sizeof(float));
+        L.rinit = off;
+        off += align_up(totb);
     }
     L.bytes = off;
     return L;
@@ -474,10 +481,11 @@ la_status la_favor_features(const void* x, const float* omega, void* out, int64_
     return LA_OK;
 }
 
-la_status la_backward_causal(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
-                             void* dv, const void* saved_state, size_t saved_state_bytes, int64_t B, int64_t H,
-                             int64_t N, int64_t d, int chunk, la_dtype dt, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+static la_status backward_causal(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+                                 void* dv, const void* saved_state, size_t saved_state_bytes, const float* S0,
+                                 const float* z0, const float* dSN, const float* dzN, float* dS0, float* dz0,
+                                 int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
     bool empty = false;
     la_status st = check_shape(B, H, N, d, chunk, dt, &empty);
     if (st != LA_OK) return st;
@@ -488,14 +496,27 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
     const size_t sb = saved_state ? saved_bytes(B, H, N, d) : 0;
     if (saved_state && saved_state_bytes < sb)
         return fail(LA_ERR_INVALID_ARGUMENT, "saved_state has %zu bytes; %zu are needed", saved_state_bytes, sb);
-    const Range in[] = {{"q", q, tb}, {"k", k, tb}, {"v", v, tb}, {"dout", dout, tb}, {"saved_state", saved_state, sb}};
-    const Range out[] = {{"dq", dq, tb}, {"dk", dk, tb}, {"dv", dv, tb}};
-    if ((st = check_ptrs(in, 5, out, 3)) != LA_OK) return st;
-    if (empty) return LA_OK;
+    const size_t Sb = (size_t)B * H * d * d * sizeof(float), zb = (size_t)B * H * d * sizeof(float);
+    const Range in[] = {{"q", q, tb},           {"k", k, tb},     {"v", v, tb},     {"dout", dout, tb},
+                        {"saved_state", saved_state, sb}, {"S0", S0, Sb}, {"z0", z0, zb}, {"dS_out", dSN, Sb},
+                        {"dz_out", dzN, zb}};
+    const Range out[] = {{"dq", dq, tb}, {"dk", dk, tb}, {"dv", dv, tb}, {"dS0", dS0, Sb}, {"dz0", dz0, zb}};
+    if ((st = check_ptrs(in, 9, out, 5)) != LA_OK) return st;
+    if (B == 0 || H == 0) return LA_OK;
+    const int64_t BH = B * H;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (N == 0) {  // no tokens: the start state's gradient is the final state's
+        if (dS0 && (e = timed("fill_zero", s, [&] { return la::launch_copy_or_zero(dS0, dSN, (size_t)BH * d * d, s); })) != hipSuccess)
+            return hip_fail(e, "dS0");
+        if (dz0 && (e = timed("fill_zero", s, [&] { return la::launch_copy_or_zero(dz0, dzN, (size_t)BH * d, s); })) != hipSuccess)
+            return hip_fail(e, "dz0");
+        return LA_OK;
+    }
     const Layout L = layout(LA_OP_BWD_CAUSAL, B, H, N, d);
     if ((st = check_workspace(L, workspace, workspace_bytes)) != LA_OK) return st;
     const Range wsr[] = {{"workspace", workspace, L.bytes}};
-    if ((st = check_ptrs(in, 5, wsr, 1)) != LA_OK) return st;
+    if ((st = check_ptrs(in, 9, wsr, 1)) != LA_OK) return st;
     for (const Range& r : out)
         if (overlap(wsr[0], r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
 
@@ -504,14 +525,26 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
                              : reinterpret_cast<float*>(ws + L.rec);
     float* rrec = reinterpret_cast<float*>(ws + L.rrec);
     float* rowstat = reinterpret_cast<float*>(ws + L.rowstat);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int64_t BH = B * H;
+    const bool from_state = S0 != nullptr || z0 != nullptr;
+    const bool state_grad = dSN != nullptr || dzN != nullptr;
+    float* init = from_state ? reinterpret_cast<float*>(ws + L.init) : nullptr;
+    float* init_n = from_state ? reinterpret_cast<float*>(ws + L.init_n) : nullptr;
+    float* rinit = state_grad ? reinterpret_cast<float*>(ws + L.rinit) : nullptr;
     const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
-    hipError_t e;
+    if (from_state &&
+        (e = timed("state_split", s, [&] { return la::launch_state_split((int)d, S0, z0, init, init_n, BH, s); })) !=
+            hipSuccess)
+        return hip_fail(e, "state_split launch");
+    // The final-state gradients as an unsplit record: the suffix sums carry no split.
+    if (state_grad && (e = timed("state_split", s, [&] {
+                           return la::launch_state_split((int)d, dSN, dzN, rinit, nullptr, BH, s, la::kFeatGiven);
+                       })) != hipSuccess)
+        return hip_fail(e, "state_split launch");
     if (saved_state == nullptr) {
         if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
             return hip_fail(e, "seg_state launch");
-        if (L.plan.scan && (e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, BH, L.plan.nseg, 1, s); })) != hipSuccess)
+        if (L.plan.scan &&
+            (e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, BH, L.plan.nseg, 1, s, init); })) != hipSuccess)
             return hip_fail(e, "scan launch");
     }
     if (L.fused) {
@@ -519,24 +552,41 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
         const unsigned long long epoch = next_epoch();
         if ((e = timed("bwd_fused", s, [&] {
                  return la::launch_bwd_fused(idt, (int)d, q, k, v, dout, dq, dk, dv, rowstat, rrec, rec, flags, epoch,
-                                             g_wait_limit.load(std::memory_order_relaxed), BH, N, L.plan, s);
+                                             g_wait_limit.load(std::memory_order_relaxed), BH, N, L.plan, s, init,
+                                             init_n, rinit, dS0, dz0);
              })) != hipSuccess)
             return hip_fail(e, "bwd_fused launch");
         return LA_OK;
     }
-    if ((e = timed("bwd_prefix", s, [&] { return la::launch_bwd_prefix(idt, (int)d, q, k, v, dout, dq, rowstat, rrec, rec, BH, N, L.plan, s); })) !=
+    if ((e = timed("bwd_prefix", s, [&] { return la::launch_bwd_prefix(idt, (int)d, q, k, v, dout, dq, rowstat, rrec, rec, BH, N, L.plan, s, init, init_n); })) !=
         hipSuccess)
         return hip_fail(e, "bwd_prefix launch");
     if (!la::prefix_forms_records((int)d) &&
         (e = timed("rseg", s, [&] { return la::launch_rseg(idt, (int)d, q, dout, rowstat, rrec, BH, N, L.plan, s); })) !=
             hipSuccess)
         return hip_fail(e, "rseg launch");
-    if (L.plan.scan && (e = timed("rscan", s, [&] { return la::launch_scan((int)d, rrec, BH, L.plan.nseg, -1, s); })) != hipSuccess)
+    if (L.plan.scan && (e = timed("rscan", s, [&] { return la::launch_scan((int)d, rrec, BH, L.plan.nseg, -1, s, rinit); })) != hipSuccess)
         return hip_fail(e, "rscan launch");
-    if ((e = timed("bwd_suffix", s, [&] { return la::launch_bwd_suffix(idt, (int)d, q, k, v, dout, dk, dv, rowstat, rrec, BH, N, L.plan, s); })) !=
+    if ((e = timed("bwd_suffix", s, [&] { return la::launch_bwd_suffix(idt, (int)d, q, k, v, dout, dk, dv, rowstat, rrec, BH, N, L.plan, s, rinit, dS0, dz0); })) !=
         hipSuccess)
         return hip_fail(e, "bwd_suffix launch");
     return LA_OK;
+}
+
+la_status la_backward_causal(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+                             void* dv, const void* saved_state, size_t saved_state_bytes, int64_t B, int64_t H,
+                             int64_t N, int64_t d, int chunk, la_dtype dt, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    return backward_causal(q, k, v, dout, dq, dk, dv, saved_state, saved_state_bytes, nullptr, nullptr, nullptr,
+                           nullptr, nullptr, nullptr, B, H, N, d, chunk, dt, workspace, workspace_bytes, stream);
+}
+
+la_status la_backward_causal_state(const void* q, const void* k, const void* v, const void* dout, const float* S0,
+                                   const float* z0, const float* dS_out, const float* dz_out, void* dq, void* dk,
+                                   void* dv, float* dS0, float* dz0, int64_t B, int64_t H, int64_t N, int64_t d,
+                                   int chunk, la_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+    return backward_causal(q, k, v, dout, dq, dk, dv, nullptr, 0, S0, z0, dS_out, dz_out, dS0, dz0, B, H, N, d, chunk,
+                           dt, workspace, workspace_bytes, stream);
 }
 
 la_status la_backward_noncausal(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,

@@ -69,11 +69,14 @@ struct BwdPrefixForms {
 // stores (read by other workgroups of the same launch).
 // kRecord: the sweep also forms that record (for d = 128 the registers of R are
 // left to the sweep, and rseg forms the record from the saved den and g).
-template <typename T, int D, bool kCoherentRecord, bool kRecord = true>
+// init / init_n (nullable): the forward's start state in split form and its token
+// count, one record and one count per head (the carried state starts from them).
+template <typename T, int D, bool kCoherentRecord, bool kRecord = true, bool kState = false>
 __device__ __forceinline__ void bwd_prefix_body(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dq, float2* __restrict__ rowstat, float* __restrict__ rrec, const float* __restrict__ rec, int N,
-    int cps, int nseg, int prefixed, int seg, int bh, char* lds) {
+    int cps, int nseg, int prefixed, int seg, int bh, char* lds, const float* __restrict__ init,
+    const float* __restrict__ init_n) {
     using M = Mma<T>;
     constexpr int KS = M::KSTEP;
     constexpr int DT = D / 16;
@@ -105,11 +108,17 @@ __device__ __forceinline__ void bwd_prefix_body(
     // segments before it, summed in order; segment aggregates from zero.
     StateAcc<D> stS, stR;
     VecAcc<D> vz, vp, vr;
-    carried_state<D>(rec + (int64_t)bh * nseg * Rec<D>::kSize, Rec<D>::kSize, seg, prefixed != 0, stS, vz, vp, lane,
-                     w);
+    float n = (float)tok_begin;
+    if constexpr (kState) {
+        carried_state<D>(rec + (int64_t)bh * nseg * Rec<D>::kSize, Rec<D>::kSize, seg, prefixed != 0, stS, vz, vp,
+                         lane, w, init != nullptr ? init + (int64_t)bh * Rec<D>::kSize : nullptr);
+        if (init_n != nullptr) n += init_n[bh];
+    } else {
+        carried_state<D>(rec + (int64_t)bh * nseg * Rec<D>::kSize, Rec<D>::kSize, seg, prefixed != 0, stS, vz, vp,
+                         lane, w);
+    }
     zero_state<D>(stR);
     zero_vec<D>(vr);
-    float n = (float)tok_begin;
 
     ChunkRegs<T, D> ck, cv;
     ChunkRegs<T, D, true> cq;
@@ -318,17 +327,17 @@ __device__ __forceinline__ void bwd_prefix_body(
     }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool kState = false>
 __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dq, float2* __restrict__ rowstat, float* __restrict__ rrec, const float* __restrict__ rec, int N,
-    int cps, int nseg, int BH, int prefixed) {
+    int cps, int nseg, int BH, int prefixed, const float* __restrict__ init, const float* __restrict__ init_n) {
     __shared__ __attribute__((aligned(16))) char lds[BwdPrefixLds<T, D>::kBytes];
     // Later segments sum more records: they are dispatched first, since a CU's
     // older workgroup issues ahead of its younger one.
     const int seg = nseg - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
-    bwd_prefix_body<T, D, false, BwdPrefixForms<D>::kRecord>(q, k, v, dout, dq, rowstat, rrec, rec, N, cps, nseg,
-                                                             prefixed, seg, bh, lds);
+    bwd_prefix_body<T, D, false, BwdPrefixForms<D>::kRecord, kState>(q, k, v, dout, dq, rowstat, rrec, rec, N, cps,
+                                                                     nseg, prefixed, seg, bh, lds, init, init_n);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -404,11 +413,16 @@ __global__ __launch_bounds__(kBlock, 2) void rseg_kernel(const T* __restrict__ q
 // kCoherentRecords: the (R, r) records of the later segments are read with
 // agent-coherent loads (written by other workgroups of the same launch).
 // poison: the records could not be confirmed; the results are made NaN.
-template <typename T, int D, bool kCoherentRecords>
+// rinit (nullable): per head, a record [dS_N^T | dz_N | 0] of upstream gradients of
+// the final state, which every suffix sum starts from.  dS0, dz0 (nullable): the
+// first segment writes the suffix state at the first token there, the gradient of
+// the start state (S [a][b], z [a] layouts).
+template <typename T, int D, bool kCoherentRecords, bool kState = false>
 __device__ __forceinline__ void bwd_suffix_body(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dk, T* __restrict__ dv, const float2* __restrict__ rowstat, const float* __restrict__ rrec, int N,
-    int cps, int nseg, int prefixed, int seg, int bh, bool poison, char* lds) {
+    int cps, int nseg, int prefixed, int seg, int bh, bool poison, char* lds, const float* __restrict__ rinit,
+    float* __restrict__ dS0, float* __restrict__ dz0) {
     using M = Mma<T>;
     using CR = ChunkRegs<T, D>;
     constexpr int KS = M::KSTEP;
@@ -433,10 +447,16 @@ __device__ __forceinline__ void bwd_suffix_body(
     // Suffix state (R, r): the records of the segments after this one, last segment first.
     StateAcc<D> stR;
     VecAcc<D> vr, vunused;
+    const float* ri = kState && rinit != nullptr ? rinit + (int64_t)bh * Rec<D>::kSize : nullptr;
     if constexpr (kCoherentRecords) {
         const GBuf brr(rrec + (int64_t)bh * nseg * Rec<D>::kSize, (uint32_t)(nseg * Rec<D>::kSize * 4));
-        zero_state<D>(stR);
-        zero_vec<D>(vr);
+        if (ri != nullptr) {
+            load_state<D>(ri, stR, lane, w);
+            load_vec<D>(ri + Rec<D>::kZ, vr, lane, w);
+        } else {
+            zero_state<D>(stR);
+            zero_vec<D>(vr);
+        }
         zero_vec<D>(vunused);
         add_records_from<D, 192>(RecCoherent{brr}, (int64_t)(nseg - 1) * Rec<D>::kSize, -(int64_t)Rec<D>::kSize,
                                  nseg - 1 - seg, stR, vr, vunused, lane, w);
@@ -450,7 +470,7 @@ __device__ __forceinline__ void bwd_suffix_body(
         }
     } else {
         carried_state<D>(rrec + ((int64_t)bh * nseg + nseg - 1) * Rec<D>::kSize, -(int64_t)Rec<D>::kSize,
-                         nseg - 1 - seg, prefixed != 0, stR, vr, vunused, lane, w);
+                         nseg - 1 - seg, prefixed != 0, stR, vr, vunused, lane, w, ri);
     }
 
     CR cq, cdo;
@@ -594,16 +614,36 @@ __device__ __forceinline__ void bwd_suffix_body(
         // (3) Suffix state: R += phi(Q)^T G, r += phi(Q)^T g.
         state_update<T, D, true, false>(stR, vr, vr, tQ, tG, s_g[buf], nullptr, lane, w);
     }
+    if (kState && seg == 0 && dS0 != nullptr) {  // R at the first token: the start state's gradient
+        using ST = StateTiles<D>;
+        float* o = dS0 + (int64_t)bh * D * D;
+#pragma unroll
+        for (int ia = 0; ia < ST::NAT; ++ia)
+#pragma unroll
+            for (int ib = 0; ib < ST::NBT; ++ib)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[(int64_t)((ST::at0(w) + ia) * 16 + 4 * g + e) * D + (ST::bt0(w) + ib) * 16 + (lane & 15)] =
+                        stR[ia][ib][e];
+    }
+    if (kState && seg == 0 && dz0 != nullptr && StateTiles<D>::owns_vec(w) && (lane & 15) == 0) {
+#pragma unroll
+        for (int x = 0; x < StateTiles<D>::NVT; ++x)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dz0[(int64_t)bh * D + (StateTiles<D>::vt0(w) + x) * 16 + 4 * g + e] = vr[x][e];
+    }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool kState = false>
 __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dk, T* __restrict__ dv, const float2* __restrict__ rowstat, const float* __restrict__ rrec, int N,
-    int cps, int nseg, int BH, int prefixed) {
+    int cps, int nseg, int BH, int prefixed, const float* __restrict__ rinit, float* __restrict__ dS0,
+    float* __restrict__ dz0) {
     __shared__ __attribute__((aligned(16))) char lds[BwdSuffixLds<T, D>::kBytes];
     const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
-    bwd_suffix_body<T, D, false>(q, k, v, dout, dk, dv, rowstat, rrec, N, cps, nseg, prefixed, seg, bh, false, lds);
+    bwd_suffix_body<T, D, false, kState>(q, k, v, dout, dk, dv, rowstat, rrec, N, cps, nseg, prefixed, seg, bh, false,
+                                         lds, rinit, dS0, dz0);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -615,16 +655,19 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_ke
 // starts from their records.  The suffix sweep's cold start (records, first
 // chunk) overlaps other workgroups' prefix sweeps instead of following a kernel
 // boundary.  den and g per row stay with the workgroup that wrote them.
-template <typename T, int D>
+template <typename T, int D, bool kState = false>
 __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_fused_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv, float2* __restrict__ rowstat,
     float* __restrict__ rrec, const float* __restrict__ rec, unsigned long long* __restrict__ flags,
-    unsigned long long epoch, int wait_limit, int N, int cps, int nseg, int BH) {
+    unsigned long long epoch, int wait_limit, int N, int cps, int nseg, int BH, const float* __restrict__ init,
+    const float* __restrict__ init_n, const float* __restrict__ rinit, float* __restrict__ dS0,
+    float* __restrict__ dz0) {
     constexpr size_t kP = BwdPrefixLds<T, D>::kBytes, kS = BwdSuffixLds<T, D>::kBytes;
     __shared__ __attribute__((aligned(16))) char lds[kP > kS ? kP : kS];
     const int seg = nseg - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
-    bwd_prefix_body<T, D, true>(q, k, v, dout, dq, rowstat, rrec, rec, N, cps, nseg, 0, seg, bh, lds);
+    bwd_prefix_body<T, D, true, true, kState>(q, k, v, dout, dq, rowstat, rrec, rec, N, cps, nseg, 0, seg, bh, lds,
+                                              init, init_n);
     // Every wave's record stores (and den, g rows) are complete before the flag.
     wait_all_memory();
     __syncthreads();
@@ -634,18 +677,24 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_fused_ker
     if ((threadIdx.x & 63) == 0)
         for (int j = seg + 1; j < nseg; ++j) ok = ok && await_flag(&hf[j], epoch, wait_limit);
     ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
-    bwd_suffix_body<T, D, true>(q, k, v, dout, dk, dv, rowstat, rrec, N, cps, nseg, 0, seg, bh, !ok, lds);
+    bwd_suffix_body<T, D, true, kState>(q, k, v, dout, dk, dv, rowstat, rrec, N, cps, nseg, 0, seg, bh, !ok, lds,
+                                        rinit, dS0, dz0);
 }
 
 // ---------------------------------------------------------------------------------------
 hipError_t launch_bwd_prefix(int dt, int d, const void* q, const void* k, const void* v, const void* dout, void* dq,
                              float* rowstat, float* rrec, const float* rec, int64_t BH, int64_t N, SegPlan p,
-                             hipStream_t s) {
+                             hipStream_t s, const float* init, const float* init_n) {
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_BWDP(TT, DD)                                                                                           \
-    hipLaunchKernelGGL((bwd_prefix_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k,        \
-                       (const TT*)v, (const TT*)dout, (TT*)dq, (float2*)rowstat, rrec, rec, (int)N, p.cps, p.nseg, (int)BH, \
-                       (int)p.scan)
+    if (init != nullptr || init_n != nullptr)                                                                     \
+        hipLaunchKernelGGL((bwd_prefix_kernel<TT, DD, true>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k, \
+                           (const TT*)v, (const TT*)dout, (TT*)dq, (float2*)rowstat, rrec, rec, (int)N, p.cps, p.nseg, \
+                           (int)BH, (int)p.scan, init, init_n);                                                      \
+    else                                                                                                         \
+        hipLaunchKernelGGL((bwd_prefix_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k,    \
+                           (const TT*)v, (const TT*)dout, (TT*)dq, (float2*)rowstat, rrec, rec, (int)N, p.cps, p.nseg, \
+                           (int)BH, (int)p.scan, nullptr, nullptr)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_BWDP(bf16, 32); break;
@@ -690,12 +739,20 @@ hipError_t launch_rseg(int dt, int d, const void* q, const void* dout, const flo
 
 hipError_t launch_bwd_fused(int dt, int d, const void* q, const void* k, const void* v, const void* dout, void* dq,
                             void* dk, void* dv, float* rowstat, float* rrec, const float* rec, unsigned long long* flags,
-                            unsigned long long epoch, int wait_limit, int64_t BH, int64_t N, SegPlan p, hipStream_t s) {
+                            unsigned long long epoch, int wait_limit, int64_t BH, int64_t N, SegPlan p, hipStream_t s,
+                            const float* init, const float* init_n, const float* rinit, float* dS0, float* dz0) {
     const dim3 grid((unsigned)(p.nseg * BH));
+    const bool state = init != nullptr || init_n != nullptr || rinit != nullptr || dS0 != nullptr || dz0 != nullptr;
 #define LA_BWDF(TT, DD)                                                                                           \
-    hipLaunchKernelGGL((bwd_fused_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k,         \
-                       (const TT*)v, (const TT*)dout, (TT*)dq, (TT*)dk, (TT*)dv, (float2*)rowstat, rrec, rec, flags, \
-                       epoch, wait_limit, (int)N, p.cps, p.nseg, (int)BH)
+    if (state)                                                                                                   \
+        hipLaunchKernelGGL((bwd_fused_kernel<TT, DD, true>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k, \
+                           (const TT*)v, (const TT*)dout, (TT*)dq, (TT*)dk, (TT*)dv, (float2*)rowstat, rrec, rec,  \
+                           flags, epoch, wait_limit, (int)N, p.cps, p.nseg, (int)BH, init, init_n, rinit, dS0, dz0); \
+    else                                                                                                         \
+        hipLaunchKernelGGL((bwd_fused_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k,     \
+                           (const TT*)v, (const TT*)dout, (TT*)dq, (TT*)dk, (TT*)dv, (float2*)rowstat, rrec, rec,  \
+                           flags, epoch, wait_limit, (int)N, p.cps, p.nseg, (int)BH, nullptr, nullptr, nullptr,    \
+                           nullptr, nullptr)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_BWDF(bf16, 32); break;
@@ -716,12 +773,17 @@ hipError_t launch_bwd_fused(int dt, int d, const void* q, const void* k, const v
 
 hipError_t launch_bwd_suffix(int dt, int d, const void* q, const void* k, const void* v, const void* dout, void* dk,
                              void* dv, const float* rowstat, const float* rrec, int64_t BH, int64_t N, SegPlan p,
-                             hipStream_t s) {
+                             hipStream_t s, const float* rinit, float* dS0, float* dz0) {
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_BWDS(TT, DD)                                                                                           \
-    hipLaunchKernelGGL((bwd_suffix_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k,        \
-                       (const TT*)v, (const TT*)dout, (TT*)dk, (TT*)dv, (const float2*)rowstat, rrec, (int)N, p.cps, \
-                       p.nseg, (int)BH, (int)p.scan)
+    if (rinit != nullptr || dS0 != nullptr || dz0 != nullptr)                                                     \
+        hipLaunchKernelGGL((bwd_suffix_kernel<TT, DD, true>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k, \
+                           (const TT*)v, (const TT*)dout, (TT*)dk, (TT*)dv, (const float2*)rowstat, rrec, (int)N,  \
+                           p.cps, p.nseg, (int)BH, (int)p.scan, rinit, dS0, dz0);                                    \
+    else                                                                                                         \
+        hipLaunchKernelGGL((bwd_suffix_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k,    \
+                           (const TT*)v, (const TT*)dout, (TT*)dk, (TT*)dv, (const float2*)rowstat, rrec, (int)N,  \
+                           p.cps, p.nseg, (int)BH, (int)p.scan, nullptr, nullptr, nullptr)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_BWDS(bf16, 32); break;

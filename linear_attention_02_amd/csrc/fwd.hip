@@ -476,6 +476,7 @@ __global__ __launch_bounds__(kBlock) void noncausal_fwd_kernel(const T* __restri
 // (as small as a prefix's own S_E, z_E; the rank-1 parts stay in fp32).  Out: the
 // record [S0_E^T | z0_E | P0] and n0 per head.  Either input may be null (zero).
 // split = 0 (features carried unsplit): P0 = 0, n0 = 0, the record is S0, z0 itself.
+// init_n may be null (no count wanted).
 // Thread b handles value column b (fixed-order sums: bitwise reproducible).
 template <int D>
 __global__ __launch_bounds__(kBlock) void state_split_kernel(const float* __restrict__ S0, const float* __restrict__ z0,
@@ -499,7 +500,7 @@ __global__ __launch_bounds__(kBlock) void state_split_kernel(const float* __rest
     for (int a = 0; a < D; ++a) r[Rec<D>::kSt + b * D + a] = Sh != nullptr ? Sh[a * D + b] - p : 0.f;
     r[Rec<D>::kZ + b] = zh != nullptr ? zh[b] - n0 : 0.f;  // feature b of z0_E
     r[Rec<D>::kP + b] = p;
-    if (b == 0) init_n[bh] = n0;
+    if (b == 0 && init_n != nullptr) init_n[bh] = n0;
 }
 
 // dst[i] = src[i], or 0 when src is null.

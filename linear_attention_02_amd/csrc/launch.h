@@ -72,9 +72,13 @@ hipError_t launch_noncausal_fwd(int dt, int d, const void* q, void* o, const flo
 // Backward pieces.  bwd_prefix starts each segment from the sum of the forward
 // records before it and writes the segment's suffix-state aggregate to rrec;
 // bwd_suffix starts each segment from the sum of the rrec records after it.
+// init / init_n, rinit (nullable): the forward's start state (split record and count per
+// head) and a record of upstream final-state gradients; dS0, dz0 (nullable) receive the
+// start state's gradient.
 hipError_t launch_bwd_prefix(int dt, int d, const void* q, const void* k, const void* v,
                              const void* dout, void* dq, float* rowstat, float* rrec,
-                             const float* rec, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
+                             const float* rec, int64_t BH, int64_t N, SegPlan p, hipStream_t s,
+                             const float* init = nullptr, const float* init_n = nullptr);
 // The backward's per-segment (R, r) records from q, dout and the saved per-row
 // statistics, for head dimensions whose prefix sweep does not form them (d > 64).
 hipError_t launch_rseg(int dt, int d, const void* q, const void* dout, const float* rowstat, float* rrec, int64_t BH,
@@ -88,10 +92,13 @@ constexpr int kDefaultWaitLimit = 1 << 16;
 // wait_limit bounds the polls of each wait for a later segment's record.
 hipError_t launch_bwd_fused(int dt, int d, const void* q, const void* k, const void* v, const void* dout, void* dq,
                             void* dk, void* dv, float* rowstat, float* rrec, const float* rec, unsigned long long* flags,
-                            unsigned long long epoch, int wait_limit, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
+                            unsigned long long epoch, int wait_limit, int64_t BH, int64_t N, SegPlan p, hipStream_t s,
+                            const float* init = nullptr, const float* init_n = nullptr, const float* rinit = nullptr,
+                            float* dS0 = nullptr, float* dz0 = nullptr);
 hipError_t launch_bwd_suffix(int dt, int d, const void* q, const void* k, const void* v,
                              const void* dout, void* dk, void* dv, const float* rowstat,
-                             const float* rrec, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
+                             const float* rrec, int64_t BH, int64_t N, SegPlan p, hipStream_t s,
+                             const float* rinit = nullptr, float* dS0 = nullptr, float* dz0 = nullptr);
 
 // Non-causal backward.  ncbwd_q: dQ of every row from the head's key state (the
 // in-order sum of `ntotal` records per head at `total`) and each segment's

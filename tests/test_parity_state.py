@@ -165,3 +165,60 @@ def test_decode_steps_shared_state(la, oracle, d, T, heads, dtype):
     record(f"decode_steps H={H} Hkv={Hkv} d={d} T={T} {dtype}", **errs)
     assert errs["o"] < TOL[dtype], errs
     assert max(errs["S"], errs["z"]) < 1e-5, errs
+
+
+# ---- backward from a start state (a sequence trained in pieces) ------------------------------------
+BWD_SHAPES = [(1, 1, 1, 32), (2, 3, 200, 64), (1, 2, 300, 128), (2, 2, 1000, 64), (1, 8, 64 * 130 + 17, 64)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("shape", BWD_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_backward_causal_from_state(la, oracle, shape, dtype):
+    B, H, N, d = shape
+    if dtype == torch.float32 and d == 128:
+        pytest.skip("fp32 causal path is built for d <= 64")
+    S0, z0 = start_state(oracle, B, H, d, dtype, seed=N + 61)
+    q, k, v, do = draw(B, H, N, d, dtype, seed=N + 62)
+    rng = np.random.default_rng(N + 63)
+    dSN = torch.from_numpy(rng.standard_normal((B, H, d, d)) * 0.01).float()
+    dzN = torch.from_numpy(rng.standard_normal((B, H, d)) * 0.01).float()
+    dq, dk, dv, dS0, dz0 = la.la_backward_causal_state(q, k, v, do, S0=S0.cuda(), z0=z0.cuda(), dS_out=dSN.cuda(),
+                                                       dz_out=dzN.cuda())
+    torch.cuda.synchronize()
+    r = oracle.backward_causal_state(f64(q), f64(k), f64(v), f64(do), S0=f64(S0), z0=f64(z0), dSN=f64(dSN),
+                                     dzN=f64(dzN))
+    errs = {n: slice_err(g, ref) for n, g, ref in zip(("dq", "dk", "dv", "dS0"), (dq, dk, dv, dS0), r[:4])}
+    errs["dz0"] = slice_err(dz0[..., None], r[4][..., None])
+    record(f"bwd_causal_from_state {B}x{H}x{N}x{d} {dtype}", **errs)
+    assert max(errs.values()) < TOL[dtype], errs
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_training_in_pieces(la, oracle, dtype):
+    """Forward in two pieces (the second from the first's final state), backward of the
+    second piece from that state, then of the first with the second's start-state
+    gradients: together the oracle's one-pass backward of the whole sequence."""
+    B, H, N, d, p = 2, 2, 700, 64, 300
+    q, k, v, do = draw(B, H, N, d, dtype, seed=71)
+    cut = lambda t, a, b: t[:, :, a:b].contiguous()
+    _, S1, z1 = la.la_forward_causal(cut(q, 0, p), cut(k, 0, p), cut(v, 0, p), return_state=True)
+    dq2, dk2, dv2, dS1, dz1 = la.la_backward_causal_state(cut(q, p, N), cut(k, p, N), cut(v, p, N), cut(do, p, N),
+                                                          S0=S1, z0=z1)
+    dq1, dk1, dv1, _, _ = la.la_backward_causal_state(cut(q, 0, p), cut(k, 0, p), cut(v, 0, p), cut(do, 0, p),
+                                                      dS_out=dS1, dz_out=dz1, want_state_grad=False)
+    torch.cuda.synchronize()
+    ref = oracle.backward_causal(f64(q), f64(k), f64(v), f64(do))
+    got = [torch.cat([a, b], dim=2) for a, b in ((dq1, dq2), (dk1, dk2), (dv1, dv2))]
+    errs = {n: slice_err(g, rr) for n, g, rr in zip(("dq", "dk", "dv"), got, ref)}
+    record(f"training in pieces {dtype}", **errs)
+    assert max(errs.values()) < TOL[dtype], errs
+
+
+def test_backward_from_state_without_tokens(la):
+    B, H, d = 2, 3, 64
+    dSN = torch.randn(B, H, d, d, device="cuda")
+    dzN = torch.randn(B, H, d, device="cuda")
+    q = torch.empty(B, H, 0, d, dtype=torch.bfloat16, device="cuda")
+    _, _, _, dS0, dz0 = la.la_backward_causal_state(q, q, q, q, dS_out=dSN, dz_out=dzN)
+    torch.cuda.synchronize()
+    assert torch.equal(dS0, dSN) and torch.equal(dz0, dzN)
