@@ -113,6 +113,20 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* o
                             int64_t N, int64_t d, int chunk, la_dtype dt, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* The causal forward with H query heads sharing Hkv key/value heads (grouped or
+ * multi-query heads; H a multiple of Hkv): query head h reads the keys and values
+ * of key/value head h / (H / Hkv), whose state (S, z) is formed once for the group.
+ * q, o [B][H][N][d] and den_out [B][H][N]; k, v [B][Hkv][N][d]; S0, z0, S_out,
+ * z_out [B][Hkv][d][d], [B][Hkv][d] (the states la_decode_steps takes with the same
+ * H, Hkv).  Workspace: la_workspace_size(LA_OP_FWD_CAUSAL, B, H, N, d, ...).  No
+ * saved state (the backward has no grouped heads).  Otherwise as la_forward_causal;
+ * Hkv = H is la_forward_causal. */
+la_status la_forward_causal_grouped(const void* q, const void* k, const void* v, void* o,
+                                    const float* S0, const float* z0, float* den_out, float* S_out,
+                                    float* z_out, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                                    int chunk, la_dtype dt, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 /* Causal backward: dQ, dK, dV of L = sum(dO * O) for the causal forward, by
  * the chain rule (the arXiv 2510.21956 abstract on vix.ing states that a
  * forward and backward pass exist; the formulas are derived, not printed):

@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     la_forward_noncausal_features,
     favor_features,
     la_forward_causal,
+    la_forward_causal_grouped,
     la_forward_noncausal,
     linear_attention,
     load_library,

@@ -23,7 +23,7 @@ LA_OP_FWD_NONCAUSAL, LA_OP_FWD_CAUSAL, LA_OP_BWD_CAUSAL, LA_OP_BWD_NONCAUSAL = 0
 EXPORTS = ("la_workspace_size", "la_saved_state_size", "la_forward_noncausal", "la_forward_causal", "la_backward_causal",
            "la_backward_noncausal", "la_decode_step", "la_decode_steps", "la_favor_features",
            "la_forward_causal_features", "la_forward_noncausal_features", "la_decode_steps_features",
-           "la_backward_causal_state", "la_status_string", "la_last_error_message", "la_version",
+           "la_backward_causal_state", "la_forward_causal_grouped", "la_status_string", "la_last_error_message", "la_version",
            "la_profile_enable", "la_profile_count", "la_profile_entry", "la_debug_set_wait_limit",
            "la_debug_wait_limit")
 
@@ -59,6 +59,8 @@ def load_library(path: str | None = None):
     lib.la_forward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.la_backward_causal.restype = i32
     lib.la_backward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.la_forward_causal_grouped.restype = i32
+    lib.la_forward_causal_grouped.argtypes = [vp] * 9 + [i64, i64, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.la_backward_causal_state.restype = i32
     lib.la_backward_causal_state.argtypes = [vp] * 13 + [i64, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.la_backward_noncausal.restype = i32
@@ -251,6 +253,40 @@ def la_backward_noncausal(q, k, v, dout, *, out=None, workspace=None, saved_stat
                                                 _ptr(dv), _ptr(saved_state), _nbytes(saved_state), B, H, N, d,
                                                 _dtype_code(q.dtype), _ptr(ws), nbytes, _stream(q.device)))
     return dq, dk, dv
+
+
+def la_forward_causal_grouped(q, k, v, *, chunk=0, return_den=False, return_state=False, out=None, workspace=None,
+                              S0=None, z0=None, S_out=None, z_out=None):
+    """Causal forward with grouped key/value heads: q [B, H, N, d]; k, v [B, Hkv, N, d] with H a
+    multiple of Hkv; start / final states [B, Hkv, d, d], [B, Hkv, d]."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, N, d] and k, v [B, Hkv, N, d]")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, d) or v.shape != k.shape or Hkv == 0 or H % Hkv:
+        raise ValueError("k, v must be [B, Hkv, N, d] with H a multiple of Hkv")
+    for t in (q, k, v):
+        if t.dtype != q.dtype or t.device != q.device or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("q, k, v must be contiguous HIP tensors of one dtype")
+    _check_state(S0, z0, B, Hkv, d, q.device)
+    _check_state(S_out, z_out, B, Hkv, d, q.device)
+    o = torch.empty_like(q) if out is None else out
+    den = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_den else None
+    S = z = None
+    if return_state:
+        S = torch.empty((B, Hkv, d, d), dtype=torch.float32, device=q.device) if S_out is None else S_out
+        z = torch.empty((B, Hkv, d), dtype=torch.float32, device=q.device) if z_out is None else z_out
+    ws = _workspace(LA_OP_FWD_CAUSAL, B, H, N, d, q.dtype, q.device, chunk, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().la_forward_causal_grouped(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(S0), _ptr(z0), _ptr(den),
+                                                    _ptr(S), _ptr(z), B, H, Hkv, N, d, chunk, _dtype_code(q.dtype),
+                                                    _ptr(ws), nbytes, _stream(q.device)))
+    res = [o]
+    if return_den:
+        res.append(den)
+    if return_state:
+        res += [S, z]
+    return res[0] if len(res) == 1 else tuple(res)
 
 
 def la_backward_causal_state(q, k, v, dout, *, S0=None, z0=None, dS_out=None, dz_out=None, chunk=0, out=None,

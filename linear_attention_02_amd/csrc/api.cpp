@@ -344,13 +344,20 @@ la_status forward_noncausal(const void* q, const void* k, const void* v, void* o
     return LA_OK;
 }
 
+// Hkv: key/value heads (H a multiple of it); k, v, the start state and the final state
+// are per key/value head, q, o and den per query head.
 la_status forward_causal(const void* q, const void* k, const void* v, void* o, const float* S0, const float* z0,
                          float* den_out, float* S_out, float* z_out, void* saved_state, size_t saved_state_bytes,
                          int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt, void* workspace,
-                         size_t workspace_bytes, void* stream, int feat) {
+                         size_t workspace_bytes, void* stream, int feat, int64_t Hkv) {
     bool empty = false;
     la_status st = check_shape(B, H, N, d, chunk, dt, &empty);
     if (st != LA_OK) return st;
+    if (Hkv < 0 || (Hkv == 0) != (H == 0) || (Hkv > 0 && H % Hkv != 0))
+        return fail(LA_ERR_INVALID_ARGUMENT, "H = %lld query heads must be a multiple of Hkv = %lld", (long long)H,
+                    (long long)Hkv);
+    if (Hkv != H && saved_state)
+        return fail(LA_ERR_INVALID_ARGUMENT, "saved_state is for la_backward_causal, which has no grouped heads");
     if (dt == LA_F32 && d == 128) return fail(LA_ERR_UNSUPPORTED, "fp32 causal forward is built for d = 32 and 64");
     // Empty tensors (no tokens) may come as NULL pointers.
     if (N > 0 && (!q || !k || !v || !o)) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-NULL");
@@ -358,9 +365,9 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* o, c
     if (from_state && saved_state)
         return fail(LA_ERR_INVALID_ARGUMENT,
                     "saved_state is for la_backward_causal, which starts from a zero state: not with S0 / z0");
-    const size_t tb = (size_t)B * H * N * d * elem_size(dt);
-    const size_t Sb = (size_t)B * H * d * d * sizeof(float), zb = (size_t)B * H * d * sizeof(float);
-    const Range in[] = {{"q", q, tb}, {"k", k, tb}, {"v", v, tb}};
+    const size_t tb = (size_t)B * H * N * d * elem_size(dt), kb = (size_t)B * Hkv * N * d * elem_size(dt);
+    const size_t Sb = (size_t)B * Hkv * d * d * sizeof(float), zb = (size_t)B * Hkv * d * sizeof(float);
+    const Range in[] = {{"q", q, tb}, {"k", k, kb}, {"v", v, kb}};
     const size_t sb = saved_state ? saved_bytes(B, H, N, d) : 0;
     if (saved_state && saved_state_bytes < sb)
         return fail(LA_ERR_INVALID_ARGUMENT, "saved_state has %zu bytes; %zu are needed", saved_state_bytes, sb);
@@ -381,16 +388,16 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* o, c
     }
     if (overlap(init_in[0], init_in[1])) return fail(LA_ERR_INVALID_ARGUMENT, "S0 and z0 overlap");
     if (B == 0 || H == 0) return LA_OK;
-    const int64_t BH = B * H;
+    const int64_t BH = B * H, BHkv = B * Hkv;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (N == 0) {  // empty sequence: the final state is the start state
         if (S_out && S_out != S0) {
-            e = timed("fill_zero", s, [&] { return la::launch_copy_or_zero(S_out, S0, (size_t)BH * d * d, s); });
+            e = timed("fill_zero", s, [&] { return la::launch_copy_or_zero(S_out, S0, (size_t)BHkv * d * d, s); });
             if (e != hipSuccess) return hip_fail(e, "S_out");
         }
         if (z_out && z_out != z0) {
-            e = timed("fill_zero", s, [&] { return la::launch_copy_or_zero(z_out, z0, (size_t)BH * d, s); });
+            e = timed("fill_zero", s, [&] { return la::launch_copy_or_zero(z_out, z0, (size_t)BHkv * d, s); });
             if (e != hipSuccess) return hip_fail(e, "z_out");
         }
         return LA_OK;
@@ -408,18 +415,19 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* o, c
     float* init = from_state ? reinterpret_cast<float*>(ws + L.init) : nullptr;
     float* init_n = from_state ? reinterpret_cast<float*>(ws + L.init_n) : nullptr;
     const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
+    // The key state once per key/value head (the plan is the query heads'; its records fit).
     if (from_state &&
-        (e = timed("state_split", s, [&] { return la::launch_state_split((int)d, S0, z0, init, init_n, BH, s, feat); })) !=
+        (e = timed("state_split", s, [&] { return la::launch_state_split((int)d, S0, z0, init, init_n, BHkv, s, feat); })) !=
             hipSuccess)
         return hip_fail(e, "state_split launch");
-    if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s, feat); })) != hipSuccess)
+    if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BHkv, N, L.plan, s, feat); })) != hipSuccess)
         return hip_fail(e, "seg_state launch");
     if (L.plan.scan &&
-        (e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, BH, L.plan.nseg, 1, s, init); })) != hipSuccess)
+        (e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, BHkv, L.plan.nseg, 1, s, init); })) != hipSuccess)
         return hip_fail(e, "scan launch");
     if ((e = timed("causal_fwd", s, [&] {
              return la::launch_causal_fwd(idt, (int)d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, L.plan, s, init,
-                                          init_n, feat);
+                                          init_n, feat, (int)(H / Hkv));
          })) != hipSuccess)
         return hip_fail(e, "causal_fwd launch");
     return LA_OK;
@@ -448,7 +456,15 @@ la_status la_forward_causal(const void* q, const void* k, const void* v, void* o
                             int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt, void* workspace,
                             size_t workspace_bytes, void* stream) {
     return forward_causal(q, k, v, o, S0, z0, den_out, S_out, z_out, saved_state, saved_state_bytes, B, H, N, d, chunk,
-                          dt, workspace, workspace_bytes, stream, la::kFeatElu);
+                          dt, workspace, workspace_bytes, stream, la::kFeatElu, H);
+}
+
+la_status la_forward_causal_grouped(const void* q, const void* k, const void* v, void* o, const float* S0,
+                                    const float* z0, float* den_out, float* S_out, float* z_out, int64_t B, int64_t H,
+                                    int64_t Hkv, int64_t N, int64_t d, int chunk, la_dtype dt, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    return forward_causal(q, k, v, o, S0, z0, den_out, S_out, z_out, nullptr, 0, B, H, N, d, chunk, dt, workspace,
+                          workspace_bytes, stream, la::kFeatElu, Hkv);
 }
 
 la_status la_forward_causal_features(const void* fq, const void* fk, const void* v, void* o, const float* S0,
@@ -456,7 +472,7 @@ la_status la_forward_causal_features(const void* fq, const void* fk, const void*
                                      int64_t N, int64_t d, la_dtype dt, void* workspace, size_t workspace_bytes,
                                      void* stream) {
     return forward_causal(fq, fk, v, o, S0, z0, den_out, S_out, z_out, nullptr, 0, B, H, N, d, 0, dt, workspace,
-                          workspace_bytes, stream, la::kFeatGiven);
+                          workspace_bytes, stream, la::kFeatGiven, H);
 }
 
 la_status la_favor_features(const void* x, const float* omega, void* out, int64_t rows, int64_t d, la_dtype dt,

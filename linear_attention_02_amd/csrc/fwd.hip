@@ -198,7 +198,7 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ o,
     float* __restrict__ den_out, const float* __restrict__ rec, float* __restrict__ S_out, float* __restrict__ z_out,
     const float* __restrict__ init, const float* __restrict__ init_n, int N, int cps, int nseg, int BH,
-    int prefixed) {
+    int prefixed, int G) {
     using M = Mma<T>;
     using F = typename M::frag;
     constexpr int KS = M::KSTEP;
@@ -212,17 +212,20 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
     // Later segments sum more records: they are dispatched first, since a CU's
     // older workgroup issues ahead of its younger one.
     const int seg = nseg - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
+    // Query head bh reads the keys, values, records and start state of key/value
+    // head kv (G query heads share one: grouped heads; G = 1: one each).
+    const int kv = bh / G;
     const int wv = wave_id(), lane = threadIdx.x & 63, g = lane >> 4;
     const int w = wv & 3;                     // wave index inside its role
     const int rtid = (int)threadIdx.x & (kBlock - 1);  // thread index inside its role
-    const int64_t hoff = (int64_t)bh * N * D;
+    const int64_t hoff = (int64_t)bh * N * D, kvoff = (int64_t)kv * N * D;
     const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
     const int tok_begin = seg * cps * kC;
     const int tok_end = min(N, tok_begin + cps * kC);
 
     if (wv >= 4) {
         // ---- state waves -------------------------------------------------------------
-        const GBuf bk(k + hoff, hbytes), bv(v + hoff, hbytes);
+        const GBuf bk(k + kvoff, hbytes), bv(v + kvoff, hbytes);
         // The first chunk's loads are in flight while the starting state arrives:
         // the records of the segments before this one, summed in order.
         ChunkRegs<T, D> ck, cv;
@@ -230,9 +233,9 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
         cv.load(bv, tok_begin, rtid);
         StateAcc<D> st;
         VecAcc<D> vz, vp;
-        carried_state<D, CausalFwdCfg<T, D>::kRecordRegs>(rec + (int64_t)bh * nseg * Rec<D>::kSize, Rec<D>::kSize,
+        carried_state<D, CausalFwdCfg<T, D>::kRecordRegs>(rec + (int64_t)kv * nseg * Rec<D>::kSize, Rec<D>::kSize,
                                                          seg, prefixed != 0, st, vz, vp, lane, w,
-                                                         init != nullptr ? init + (int64_t)bh * Rec<D>::kSize : nullptr);
+                                                         init != nullptr ? init + (int64_t)kv * Rec<D>::kSize : nullptr);
         publish_state<T, D>(st, Tile<T, D, D>{sm_st[0]}, lane, w);
         store_vec_as<T, D>(s_zb[0], vz, lane, w);
         store_vec<D>(s_p[0], vp, lane, w);
@@ -266,13 +269,13 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
             chunk(std::integral_constant<int, 1>{}, c0 + kC);
         }
 
-        if (seg == nseg - 1) {
+        if (seg == nseg - 1 && bh % G == 0) {  // one query head of the group writes its state
             // P of the whole head was published into s_p[nch & 1] before the last barrier.
             using ST = StateTiles<D>;
             const int nch = (tok_end - tok_begin + kC - 1) / kC;
             if (S_out != nullptr) {
                 const float* sp = s_p[nch & 1];
-                float* s = S_out + (int64_t)bh * D * D;
+                float* s = S_out + (int64_t)kv * D * D;
 #pragma unroll
                 for (int ia = 0; ia < ST::NAT; ++ia)
 #pragma unroll
@@ -290,8 +293,8 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
                 for (int x = 0; x < ST::NVT; ++x)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        z_out[(int64_t)bh * D + (ST::vt0(w) + x) * 16 + 4 * g + e] =
-                            FM::kSplit ? (init_n != nullptr ? init_n[bh] + (float)N : (float)N) + vz[x][e]
+                        z_out[(int64_t)kv * D + (ST::vt0(w) + x) * 16 + 4 * g + e] =
+                            FM::kSplit ? (init_n != nullptr ? init_n[kv] + (float)N : (float)N) + vz[x][e]
                                        : vz[x][e];
             }
         }
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
     const GBuf bq(q + hoff, hbytes), bo(o + hoff, hbytes);
     const GBuf bden(den_out != nullptr ? den_out + (int64_t)bh * N : nullptr, den_out != nullptr ? (uint32_t)N * 4 : 0u);
     // Tokens before the chunk (the count of the rank-1 part of z), from the start state's count.
-    float n = init_n != nullptr ? init_n[bh] + (float)tok_begin : (float)tok_begin;
+    float n = init_n != nullptr ? init_n[kv] + (float)tok_begin : (float)tok_begin;
     // Wavefront w takes token tile tt = (w + ci) mod 4 of chunk ci: the causal
     // mask leaves tt + 1 key tiles, and the rotation spreads that work evenly
     // over the SIMDs.
@@ -599,12 +602,13 @@ hipError_t launch_scan(int d, float* rec, int64_t BH, int nseg, int dir, hipStre
 template <class FM>
 static hipError_t launch_causal_fwd_fm(int dt, int d, const void* q, const void* k, const void* v, void* o,
                                        float* den_out, const float* rec, float* S_out, float* z_out, int64_t BH,
-                                       int64_t N, SegPlan p, hipStream_t s, const float* init, const float* init_n) {
+                                       int64_t N, SegPlan p, hipStream_t s, const float* init, const float* init_n,
+                                       int G) {
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_CFWD(TT, DD)                                                                                          \
     hipLaunchKernelGGL((causal_fwd_kernel<TT, DD, FM>), grid, dim3(2 * kBlock), 0, s, (const TT*)q, (const TT*)k,   \
                        (const TT*)v, (TT*)o, den_out, rec, S_out, z_out, init, init_n, (int)N, p.cps, p.nseg,     \
-                       (int)BH, (int)p.scan)
+                       (int)BH, (int)p.scan, G)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_CFWD(bf16, 32); break;
@@ -625,10 +629,12 @@ static hipError_t launch_causal_fwd_fm(int dt, int d, const void* q, const void*
 
 hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const void* v, void* o, float* den_out,
                              const float* rec, float* S_out, float* z_out, int64_t BH, int64_t N, SegPlan p,
-                             hipStream_t s, const float* init, const float* init_n, int feat) {
+                             hipStream_t s, const float* init, const float* init_n, int feat, int G) {
     return feat == kFeatGiven
-               ? launch_causal_fwd_fm<FeatGiven>(dt, d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, p, s, init, init_n)
-               : launch_causal_fwd_fm<FeatElu>(dt, d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, p, s, init, init_n);
+               ? launch_causal_fwd_fm<FeatGiven>(dt, d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, p, s, init, init_n,
+                                                 G)
+               : launch_causal_fwd_fm<FeatElu>(dt, d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, p, s, init, init_n,
+                                               G);
 }
 
 template <class FM>

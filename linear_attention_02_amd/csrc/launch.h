@@ -56,10 +56,12 @@ hipError_t launch_scan(int d, float* rec, int64_t BH, int nseg, int dir, hipStre
 // Causal outputs; the last segment of each head writes S_out / z_out when non-null.
 // init / init_n (nullable): per head, a start-state record and its token count n0
 // (from launch_state_split); the carried state of every segment starts from them.
+// G: query heads per key/value head (BH counts query heads; k, v, rec, init, S_out
+// and z_out are indexed by key/value head bh / G).
 hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const void* v, void* o,
                              float* den_out, const float* rec, float* S_out, float* z_out, int64_t BH,
                              int64_t N, SegPlan p, hipStream_t s, const float* init = nullptr,
-                             const float* init_n = nullptr, int feat = kFeatElu);
+                             const float* init_n = nullptr, int feat = kFeatElu, int G = 1);
 // A start state (S0 [BH][d][d], z0 [BH][d], either nullable = zero) in the carried split
 // form: one record [S0_E^T | z0_E | P0] per head in init, and n0 per head in init_n.
 hipError_t launch_state_split(int d, const float* S0, const float* z0, float* init, float* init_n, int64_t BH,

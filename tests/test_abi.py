@@ -199,3 +199,22 @@ def test_noncausal_backward_workspace_holds_both_record_sets(lib):
     out = ctypes.c_size_t(0)
     lib.la_saved_state_size(4, 16, 4096, 64, 0, la.LA_BF16, ctypes.byref(out))
     assert nb >= nf + out.value
+
+
+def test_forward_causal_grouped_validation(lib):
+    f = lib.la_forward_causal_grouped
+    q, k, v, o, wsp = A, A + 0x1000000, A + 0x1100000, A + 0x2000000, A + 0x4000000
+    none4 = (None, None, None, None, None)
+    assert f(q, k, v, o, *none4, 1, 6, 4, 64, 64, 0, 1, wsp, 1 << 30, None) == 1   # H not a multiple of Hkv
+    assert f(q, k, v, o, *none4, 1, 6, 0, 64, 64, 0, 1, wsp, 1 << 30, None) == 1   # no key/value heads
+    assert f(q, k, v, o, *none4, 1, 8, 2, 64, 96, 0, 1, wsp, 1 << 30, None) == 2   # d unsupported
+    assert f(q, k, v, o, *none4, 1, 8, 2, 64, 64, 0, 1, wsp, 16, None) == 3        # workspace too small
+    # k and v are sized by the key/value heads: 8 query heads on 2 heads of 64 x 64 bf16 rows
+    kb = 2 * 64 * 64 * 2
+    assert f(q, k, v, k + kb - 16, *none4, 1, 8, 2, 64, 64, 0, 1, wsp, 1 << 30, None) == 1  # o overlaps k
+    assert f(q, k, v + 0x1000000, k + kb, *none4, 1, 8, 2, 64, 64, 0, 1, wsp, 16, None) == 3  # passes, then workspace
+    # the states are per key/value head too: S_out of 2 x 64 x 64 fp32, z_out right after it
+    S = A + 0x6000000
+    assert f(q, k, v, o, None, None, None, S, S + 2 * 64 * 64 * 4 - 16, 1, 8, 2, 64, 64, 0, 1, wsp, 1 << 30,
+             None) == 1                                                                   # z_out overlaps S_out
+    assert f(q, k, v, o, None, None, None, S, S + 2 * 64 * 64 * 4, 1, 8, 2, 64, 64, 0, 1, wsp, 16, None) == 3
