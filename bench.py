@@ -316,6 +316,25 @@ def bench_calls(args, la, inp, torch, mid_sets):
 
     calls["mid_favor_causal_fwd"] = bench_call("favor", favor_fwd, 100, 400, w.B * w.N,
                                                4 * unit_bytes(w.B, w.H, w.N, w.d), la, torch, nsets=nsets)
+    del fq, fk, wsf
+
+    # The same with m = 2d random features (two feature blocks per head): algorithmic
+    # bytes q, k, v read and o written (4 units); the features add 2 x (1 + 2) units.
+    m = 2 * w.d
+    om2 = inp.favor_omega(w.d, seed=0, device="cuda", m=m)
+    fq = torch.empty((w.B, w.H, 2, w.N, w.d), dtype=w.dtype, device="cuda")
+    fk = torch.empty_like(fq)
+    wsf = torch.empty(la.features_workspace_size(True, w.B, w.H, w.N, w.d, m, w.dtype), dtype=torch.uint8,
+                      device="cuda")
+
+    def favor_fwd_m2(i):
+        q, k, v = fsets[i]
+        la.favor_features_blocks(q, om2, out=fq)
+        la.favor_features_blocks(k, om2, out=fk)
+        la.la_forward_causal_features_blocks(fq, fk, v, out=o, workspace=wsf)
+
+    calls["mid_favor_m128_causal_fwd"] = bench_call("favor_m2", favor_fwd_m2, 100, 400, w.B * w.N,
+                                                    4 * unit_bytes(w.B, w.H, w.N, w.d), la, torch, nsets=nsets)
     del fsets, fq, fk, o, wsf
 
     w = inp.LONG
@@ -484,6 +503,10 @@ def call_oracles(args, inp, torch):
     record("mid_favor_causal_fwd",
            lambda: oracle.forward_features(oracle.favor_features(fq, om), oracle.favor_features(fk, om), fv, True),
            hs * w.N, w.H, hs, f"FAVOR+ features + causal forward of {hs} Mid heads")
+    om2 = f64(inp.favor_omega(w.d, seed=0, m=2 * w.d))
+    record("mid_favor_m128_causal_fwd",
+           lambda: oracle.forward_features(oracle.favor_features(fq, om2), oracle.favor_features(fk, om2), fv, True),
+           hs * w.N, w.H, hs, f"FAVOR+ features (m = 2d) + causal forward of {hs} Mid heads")
     L = inp.LONG
     hl = 4
     q, k, v, do = (f64(t) for t in inp.qkv(1, hl, L.N, L.d, torch.float32, seed=92, with_dout=True))

@@ -233,6 +233,40 @@ la_status la_decode_steps_features(float* S, float* z, const void* fq, const voi
                                    void* o, int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t d,
                                    la_dtype dt, void* stream);
 
+/* ---- More random features than d: m = KF d, KF = m / d feature blocks --------------------
+ * The Performer section of the same page draws m random directions, and m may exceed d
+ * (the estimate's variance falls as 1/m).  Features come in blocks of d: block j holds
+ * features j d .. j d + d - 1, and each head's features are stored block by block,
+ * [B][H][KF][N][d] (the "block layout"; KF = 1 is the plain [B][H][N][d]).  States keep
+ * the natural layout S [B][H][m][d] (row a = feature a) and z [B][H][m], which read block
+ * by block is one [d][d] state per block.  m must be a positive multiple of d with
+ * m / d <= 64 (LA_ERR_INVALID_ARGUMENT / LA_ERR_UNSUPPORTED otherwise); m = d is the
+ * plain call.
+ *
+ * la_favor_features_blocks: the features of x [heads][N][d] (heads = B H) for omega
+ * [m][d] fp32 into out [heads][KF][N][d]; otherwise as la_favor_features.
+ *
+ * la_forward_causal_features_blocks / la_forward_noncausal_features_blocks: attention on
+ * such features: fq, fk in block layout; v, o [B][H][N][d]; den_out [B][H][N] fp32
+ * (nullable) receives phi(Q_i)^T z over all m features.  Each block runs as a head of its
+ * own over its head's values (num_j, den_j), and O = sum_j num_j / sum_j den_j is formed
+ * as sum_j den_j O_j / sum_j den_j (O_j kept in dt in the workspace).  Start and final
+ * states (causal only, nullable, natural layout above) as la_forward_causal_features.
+ * Workspace: la_features_workspace_size(causal != 0, B, H, N, d, m, dt, &bytes), which
+ * for KF > 1 holds the blocks' outputs besides the plain call's workspace. */
+la_status la_features_workspace_size(int causal, int64_t B, int64_t H, int64_t N, int64_t d, int64_t m,
+                                     la_dtype dt, size_t* bytes_out);
+la_status la_favor_features_blocks(const void* x, const float* omega, void* out, int64_t heads, int64_t N,
+                                   int64_t d, int64_t m, la_dtype dt, void* stream);
+la_status la_forward_causal_features_blocks(const void* fq, const void* fk, const void* v, void* o,
+                                            const float* S0, const float* z0, float* den_out, float* S_out,
+                                            float* z_out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t m,
+                                            la_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
+la_status la_forward_noncausal_features_blocks(const void* fq, const void* fk, const void* v, void* o,
+                                               float* den_out, int64_t B, int64_t H, int64_t N, int64_t d,
+                                               int64_t m, la_dtype dt, void* workspace, size_t workspace_bytes,
+                                               void* stream);
+
 /* Static description of a status code. */
 const char* la_status_string(la_status s);
 

@@ -117,9 +117,10 @@ def favor_qkv(B, H, N, d, dtype=torch.bfloat16, seed=0, device="cpu", with_dout=
     return q, k, v, normal((B, H, N, d), gen, dtype, 1.0, device)
 
 
-def favor_omega(d, seed=0, device="cpu"):
-    """FAVOR+ random directions: a [d, d] fp32 matrix whose rows are drawn from N(0, I_d)."""
-    return torch.randn((d, d), generator=generator(seed, device), dtype=torch.float32, device=device)
+def favor_omega(d, seed=0, device="cpu", m=None):
+    """FAVOR+ random directions: an [m, d] fp32 matrix (m = d by default) whose rows are drawn from N(0, I_d)."""
+    return torch.randn((d if m is None else m, d), generator=generator(seed, device), dtype=torch.float32,
+                       device=device)
 
 
 def to_f64(x: torch.Tensor):

@@ -24,6 +24,10 @@ from ._binding import (  # noqa: F401
     la_forward_causal_features,
     la_forward_noncausal_features,
     favor_features,
+    favor_features_blocks,
+    features_workspace_size,
+    la_forward_causal_features_blocks,
+    la_forward_noncausal_features_blocks,
     la_forward_causal,
     la_forward_causal_grouped,
     la_forward_noncausal,

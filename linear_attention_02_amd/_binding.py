@@ -23,7 +23,8 @@ LA_OP_FWD_NONCAUSAL, LA_OP_FWD_CAUSAL, LA_OP_BWD_CAUSAL, LA_OP_BWD_NONCAUSAL = 0
 EXPORTS = ("la_workspace_size", "la_saved_state_size", "la_forward_noncausal", "la_forward_causal", "la_backward_causal",
            "la_backward_noncausal", "la_decode_step", "la_decode_steps", "la_favor_features",
            "la_forward_causal_features", "la_forward_noncausal_features", "la_decode_steps_features",
-           "la_backward_causal_state", "la_forward_causal_grouped", "la_status_string", "la_last_error_message", "la_version",
+           "la_backward_causal_state", "la_forward_causal_grouped", "la_features_workspace_size",
+           "la_favor_features_blocks", "la_forward_causal_features_blocks", "la_forward_noncausal_features_blocks", "la_status_string", "la_last_error_message", "la_version",
            "la_profile_enable", "la_profile_count", "la_profile_entry", "la_debug_set_wait_limit",
            "la_debug_wait_limit")
 
@@ -59,6 +60,14 @@ def load_library(path: str | None = None):
     lib.la_forward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.la_backward_causal.restype = i32
     lib.la_backward_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i32, i32, vp, sz, vp]
+    lib.la_features_workspace_size.restype = i32
+    lib.la_features_workspace_size.argtypes = [i32, i64, i64, i64, i64, i64, i32, ctypes.POINTER(sz)]
+    lib.la_favor_features_blocks.restype = i32
+    lib.la_favor_features_blocks.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, vp]
+    lib.la_forward_causal_features_blocks.restype = i32
+    lib.la_forward_causal_features_blocks.argtypes = [vp] * 9 + [i64, i64, i64, i64, i64, i32, vp, sz, vp]
+    lib.la_forward_noncausal_features_blocks.restype = i32
+    lib.la_forward_noncausal_features_blocks.argtypes = [vp] * 5 + [i64, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_forward_causal_grouped.restype = i32
     lib.la_forward_causal_grouped.argtypes = [vp] * 9 + [i64, i64, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.la_backward_causal_state.restype = i32
@@ -204,7 +213,7 @@ def la_forward_causal(q, k, v, *, chunk=0, return_den=False, return_state=False,
     _check_state(S_out, z_out, B, H, d, q.device)
     o = torch.empty_like(q) if out is None else out
     den = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_den else None
-    S = z = None
+    S, z = S_out, z_out  # a state buffer the caller passes is always written
     if return_state:
         S = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device) if S_out is None else S_out
         z = torch.empty((B, H, d), dtype=torch.float32, device=q.device) if z_out is None else z_out
@@ -272,7 +281,7 @@ def la_forward_causal_grouped(q, k, v, *, chunk=0, return_den=False, return_stat
     _check_state(S_out, z_out, B, Hkv, d, q.device)
     o = torch.empty_like(q) if out is None else out
     den = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_den else None
-    S = z = None
+    S, z = S_out, z_out  # a state buffer the caller passes is always written
     if return_state:
         S = torch.empty((B, Hkv, d, d), dtype=torch.float32, device=q.device) if S_out is None else S_out
         z = torch.empty((B, Hkv, d), dtype=torch.float32, device=q.device) if z_out is None else z_out
@@ -385,6 +394,90 @@ def favor_features(x, omega, *, out=None):
     return o
 
 
+def favor_features_blocks(x, omega, *, out=None):
+    """FAVOR+ features of x [B, H, N, d] for omega [m, d] fp32 (m a multiple of d), in block
+    layout [B, H, m // d, N, d]: block j holds features j d .. j d + d - 1."""
+    if x.dim() != 4:
+        raise ValueError("x must be [B, H, N, d]")
+    B, H, N, d = x.shape
+    m = omega.shape[0]
+    if omega.dim() != 2 or omega.shape[1] != d or omega.dtype != torch.float32 or not omega.is_contiguous():
+        raise ValueError("omega must be a contiguous [m, d] fp32 tensor")
+    if not x.is_contiguous() or not x.is_cuda or omega.device != x.device:
+        raise ValueError("x must be a contiguous tensor on the same HIP device as omega")
+    if m < d or m % d:
+        raise ValueError("m must be a positive multiple of d")
+    o = torch.empty((B, H, m // d, N, d), dtype=x.dtype, device=x.device) if out is None else out
+    _check(load_library().la_favor_features_blocks(_ptr(x), _ptr(omega), _ptr(o), B * H, N, d, m,
+                                                   _dtype_code(x.dtype), _stream(x.device)))
+    return o
+
+
+def features_workspace_size(causal, B, H, N, d, m, dtype):
+    out = ctypes.c_size_t(0)
+    _check(load_library().la_features_workspace_size(1 if causal else 0, B, H, N, d, m, _dtype_code(dtype),
+                                                     ctypes.byref(out)))
+    return out.value
+
+
+def _check_blocks(fq, fk, v):
+    if fq.dim() != 5 or fk.shape != fq.shape or v.dim() != 4:
+        raise ValueError("fq, fk must be [B, H, m // d, N, d] and v [B, H, N, d]")
+    B, H, KF, N, d = fq.shape
+    if v.shape != (B, H, N, d):
+        raise ValueError("v must be [B, H, N, d] for features [B, H, m // d, N, d]")
+    for t in (fq, fk, v):
+        if t.dtype != fq.dtype or t.device != fq.device or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("fq, fk, v must be contiguous HIP tensors of one dtype")
+    return B, H, N, d, KF * d
+
+
+def la_forward_causal_features_blocks(fq, fk, v, *, return_den=False, return_state=False, out=None,
+                                      workspace=None, S0=None, z0=None, S_out=None, z_out=None):
+    """Causal forward on m = KF d features in block layout fq, fk [B, H, KF, N, d]; states [B, H, m, d], [B, H, m]."""
+    B, H, N, d, m = _check_blocks(fq, fk, v)
+    for S, z in ((S0, z0), (S_out, z_out)):
+        if S is not None and (S.shape != (B, H, m, d) or S.dtype != torch.float32 or not S.is_contiguous()):
+            raise ValueError("states must be contiguous [B, H, m, d] fp32")
+        if z is not None and (z.shape != (B, H, m) or z.dtype != torch.float32 or not z.is_contiguous()):
+            raise ValueError("states must be contiguous [B, H, m] fp32")
+    o = torch.empty_like(v) if out is None else out
+    den = torch.empty((B, H, N), dtype=torch.float32, device=fq.device) if return_den else None
+    S, z = S_out, z_out  # a state buffer the caller passes is always written
+    if return_state:
+        S = torch.empty((B, H, m, d), dtype=torch.float32, device=fq.device) if S_out is None else S_out
+        z = torch.empty((B, H, m), dtype=torch.float32, device=fq.device) if z_out is None else z_out
+    need = features_workspace_size(True, B, H, N, d, m, fq.dtype)
+    ws = workspace if workspace is not None else (torch.empty(need, dtype=torch.uint8, device=fq.device)
+                                                  if need else None)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().la_forward_causal_features_blocks(_ptr(fq), _ptr(fk), _ptr(v), _ptr(o), _ptr(S0), _ptr(z0),
+                                                            _ptr(den), _ptr(S), _ptr(z), B, H, N, d, m,
+                                                            _dtype_code(fq.dtype), _ptr(ws), nbytes,
+                                                            _stream(fq.device)))
+    res = [o]
+    if return_den:
+        res.append(den)
+    if return_state:
+        res += [S, z]
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def la_forward_noncausal_features_blocks(fq, fk, v, *, return_den=False, out=None, workspace=None):
+    """Non-causal forward on m = KF d features in block layout fq, fk [B, H, KF, N, d]."""
+    B, H, N, d, m = _check_blocks(fq, fk, v)
+    o = torch.empty_like(v) if out is None else out
+    den = torch.empty((B, H, N), dtype=torch.float32, device=fq.device) if return_den else None
+    need = features_workspace_size(False, B, H, N, d, m, fq.dtype)
+    ws = workspace if workspace is not None else (torch.empty(need, dtype=torch.uint8, device=fq.device)
+                                                  if need else None)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().la_forward_noncausal_features_blocks(_ptr(fq), _ptr(fk), _ptr(v), _ptr(o), _ptr(den), B, H,
+                                                               N, d, m, _dtype_code(fq.dtype), _ptr(ws), nbytes,
+                                                               _stream(fq.device)))
+    return (o, den) if return_den else o
+
+
 def la_forward_causal_features(fq, fk, v, *, return_den=False, return_state=False, out=None, workspace=None,
                                S0=None, z0=None, S_out=None, z_out=None):
     """Causal forward on given positive features fq = phi(Q), fk = phi(K) [B, H, N, d]."""
@@ -393,7 +486,7 @@ def la_forward_causal_features(fq, fk, v, *, return_den=False, return_state=Fals
     _check_state(S_out, z_out, B, H, d, fq.device)
     o = torch.empty_like(v) if out is None else out
     den = torch.empty((B, H, N), dtype=torch.float32, device=fq.device) if return_den else None
-    S = z = None
+    S, z = S_out, z_out  # a state buffer the caller passes is always written
     if return_state:
         S = torch.empty((B, H, d, d), dtype=torch.float32, device=fq.device) if S_out is None else S_out
         z = torch.empty((B, H, d), dtype=torch.float32, device=fq.device) if z_out is None else z_out

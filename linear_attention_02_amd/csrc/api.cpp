@@ -300,9 +300,12 @@ la_status la_saved_state_size(int64_t B, int64_t H, int64_t N, int64_t d, int ch
 
 namespace {
 
+// Gv: heads per value head (v has B H / Gv heads; head h reads value head h / Gv).
+// den_out (nullable): [B][H][N] fp32 denominators.
 la_status forward_noncausal(const void* q, const void* k, const void* v, void* o, void* saved_state,
                             size_t saved_state_bytes, int64_t B, int64_t H, int64_t N, int64_t d, la_dtype dt,
-                            void* workspace, size_t workspace_bytes, void* stream, int feat) {
+                            void* workspace, size_t workspace_bytes, void* stream, int feat, int64_t Gv = 1,
+                            float* den_out = nullptr) {
     bool empty = false;
     la_status st = check_shape(B, H, N, d, 0, dt, &empty);
     if (st != LA_OK) return st;
@@ -312,9 +315,10 @@ la_status forward_noncausal(const void* q, const void* k, const void* v, void* o
     const size_t sb = saved_state ? saved_bytes(B, H, N, d) : 0;
     if (saved_state && saved_state_bytes < sb)
         return fail(LA_ERR_INVALID_ARGUMENT, "saved_state has %zu bytes; %zu are needed", saved_state_bytes, sb);
-    const Range in[] = {{"q", q, tb}, {"k", k, tb}, {"v", v, tb}};
-    const Range out[] = {{"o", o, tb}, {"saved_state", saved_state, sb}};
-    if ((st = check_ptrs(in, 3, out, 2)) != LA_OK) return st;
+    const Range in[] = {{"q", q, tb}, {"k", k, tb}, {"v", v, tb / Gv}};
+    const Range out[] = {{"o", o, tb}, {"saved_state", saved_state, sb},
+                         {"den_out", den_out, (size_t)B * H * N * sizeof(float)}};
+    if ((st = check_ptrs(in, 3, out, 3)) != LA_OK) return st;
     if (empty) return LA_OK;
     const Layout L = layout(LA_OP_FWD_NONCAUSAL, B, H, N, d);
     if ((st = check_workspace(L, workspace, workspace_bytes)) != LA_OK) return st;
@@ -332,24 +336,27 @@ la_status forward_noncausal(const void* q, const void* k, const void* v, void* o
     const int64_t BH = B * H;
     const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
     hipError_t e;
-    if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s, feat); })) != hipSuccess)
+    if ((e = timed("seg_state", s, [&] {
+             return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s, feat, (int)Gv);
+         })) != hipSuccess)
         return hip_fail(e, "seg_state launch");
     // One total per head, read by every readout workgroup (and by the backward, from the saved state).
     if ((e = timed("total", s, [&] { return la::launch_total((int)d, rec, total, BH, L.plan.nseg, s); })) != hipSuccess)
         return hip_fail(e, "total launch");
     if ((e = timed("noncausal_fwd", s, [&] {
-             return la::launch_noncausal_fwd(idt, (int)d, q, o, total, 1, BH, N, L.plan, s, feat);
+             return la::launch_noncausal_fwd(idt, (int)d, q, o, total, 1, BH, N, L.plan, s, feat, den_out);
          })) != hipSuccess)
         return hip_fail(e, "noncausal_fwd launch");
     return LA_OK;
 }
 
 // Hkv: key/value heads (H a multiple of it); k, v, the start state and the final state
-// are per key/value head, q, o and den per query head.
+// are per key/value head, q, o and den per query head.  Gv: key/value heads per value
+// head (v has B Hkv / Gv heads).
 la_status forward_causal(const void* q, const void* k, const void* v, void* o, const float* S0, const float* z0,
                          float* den_out, float* S_out, float* z_out, void* saved_state, size_t saved_state_bytes,
                          int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt, void* workspace,
-                         size_t workspace_bytes, void* stream, int feat, int64_t Hkv) {
+                         size_t workspace_bytes, void* stream, int feat, int64_t Hkv, int64_t Gv = 1) {
     bool empty = false;
     la_status st = check_shape(B, H, N, d, chunk, dt, &empty);
     if (st != LA_OK) return st;
@@ -367,7 +374,7 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* o, c
                     "saved_state is for la_backward_causal, which starts from a zero state: not with S0 / z0");
     const size_t tb = (size_t)B * H * N * d * elem_size(dt), kb = (size_t)B * Hkv * N * d * elem_size(dt);
     const size_t Sb = (size_t)B * Hkv * d * d * sizeof(float), zb = (size_t)B * Hkv * d * sizeof(float);
-    const Range in[] = {{"q", q, tb}, {"k", k, kb}, {"v", v, kb}};
+    const Range in[] = {{"q", q, tb}, {"k", k, kb}, {"v", v, kb / Gv}};
     const size_t sb = saved_state ? saved_bytes(B, H, N, d) : 0;
     if (saved_state && saved_state_bytes < sb)
         return fail(LA_ERR_INVALID_ARGUMENT, "saved_state has %zu bytes; %zu are needed", saved_state_bytes, sb);
@@ -420,14 +427,16 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* o, c
         (e = timed("state_split", s, [&] { return la::launch_state_split((int)d, S0, z0, init, init_n, BHkv, s, feat); })) !=
             hipSuccess)
         return hip_fail(e, "state_split launch");
-    if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BHkv, N, L.plan, s, feat); })) != hipSuccess)
+    if ((e = timed("seg_state", s, [&] {
+             return la::launch_seg_state(idt, (int)d, k, v, rec, BHkv, N, L.plan, s, feat, (int)Gv);
+         })) != hipSuccess)
         return hip_fail(e, "seg_state launch");
     if (L.plan.scan &&
         (e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, BHkv, L.plan.nseg, 1, s, init); })) != hipSuccess)
         return hip_fail(e, "scan launch");
     if ((e = timed("causal_fwd", s, [&] {
              return la::launch_causal_fwd(idt, (int)d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, L.plan, s, init,
-                                          init_n, feat, (int)(H / Hkv));
+                                          init_n, feat, (int)(H / Hkv), (int)Gv);
          })) != hipSuccess)
         return hip_fail(e, "causal_fwd launch");
     return LA_OK;
@@ -496,6 +505,155 @@ la_status la_favor_features(const void* x, const float* omega, void* out, int64_
     if (e != hipSuccess) return hip_fail(e, "favor_features launch");
     return LA_OK;
 }
+
+// ---- more random features than d: KF = m / d feature blocks -----------------------------
+namespace {
+
+la_status check_blocks(int64_t d, int64_t m) {
+    if (m < d || d <= 0 || m % d != 0)
+        return fail(LA_ERR_INVALID_ARGUMENT, "m = %lld features must be a positive multiple of d = %lld", (long long)m,
+                    (long long)d);
+    if (m / d > 64) return fail(LA_ERR_UNSUPPORTED, "m / d = %lld feature blocks; at most 64", (long long)(m / d));
+    return LA_OK;
+}
+
+// Workspace of a call on KF feature blocks: the m = d call's workspace for B x (H KF)
+// heads, then every block's outputs o_j [B][H][KF][N][d] and den_j [B][H][KF][N].
+struct BlockLayout {
+    size_t inner = 0, ob = 0, db = 0, bytes = 0;
+};
+BlockLayout block_layout(bool causal, int64_t B, int64_t H, int64_t N, int64_t d, int64_t KF, la_dtype dt) {
+    BlockLayout L;
+    if (B == 0 || H == 0 || N == 0) return L;
+    L.inner = layout(causal ? LA_OP_FWD_CAUSAL : LA_OP_FWD_NONCAUSAL, B, H * KF, N, d).bytes;
+    if (KF == 1) {
+        L.bytes = L.inner;
+        return L;
+    }
+    L.ob = align_up(L.inner);
+    L.db = L.ob + align_up((size_t)B * H * KF * N * d * elem_size(dt));
+    L.bytes = L.db + align_up((size_t)B * H * KF * N * sizeof(float));
+    return L;
+}
+
+la_status forward_blocks(bool causal, const void* fq, const void* fk, const void* v, void* o, const float* S0,
+                         const float* z0, float* den_out, float* S_out, float* z_out, int64_t B, int64_t H, int64_t N,
+                         int64_t d, int64_t m, la_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+    la_status st = check_blocks(d, m);
+    if (st != LA_OK) return st;
+    bool empty = false;
+    if ((st = check_shape(B, H, N, d, 0, dt, &empty)) != LA_OK) return st;
+    const int64_t KF = m / d;
+    if (KF == 1) {
+        return causal ? forward_causal(fq, fk, v, o, S0, z0, den_out, S_out, z_out, nullptr, 0, B, H, N, d, 0, dt,
+                                       workspace, workspace_bytes, stream, la::kFeatGiven, H)
+                      : forward_noncausal(fq, fk, v, o, nullptr, 0, B, H, N, d, dt, workspace, workspace_bytes, stream,
+                                          la::kFeatGiven, 1, den_out);
+    }
+    if (causal && dt == LA_F32 && d == 128)
+        return fail(LA_ERR_UNSUPPORTED, "fp32 causal forward is built for d = 32 and 64");
+    if (N > 0 && (!fq || !fk || !v || !o)) return fail(LA_ERR_INVALID_ARGUMENT, "fq, fk, v and o must be non-NULL");
+    const size_t tb = (size_t)B * H * N * d * elem_size(dt), fb = tb * KF;
+    const size_t Sb = (size_t)B * H * m * d * sizeof(float), zb = (size_t)B * H * m * sizeof(float);
+    const Range in[] = {{"fq", fq, fb}, {"fk", fk, fb}, {"v", v, tb}};
+    const Range out[] = {{"o", o, tb}, {"den_out", den_out, (size_t)B * H * N * sizeof(float)}};
+    if ((st = check_ptrs(in, 3, out, 2)) != LA_OK) return st;
+    const Range states[] = {{"S0", S0, Sb}, {"z0", z0, zb}, {"S_out", S_out, Sb}, {"z_out", z_out, zb}};
+    for (const Range& r : states)
+        for (const Range& x : out)
+            if (overlap(r, x)) return fail(LA_ERR_INVALID_ARGUMENT, "%s overlaps output %s", r.name, x.name);
+    if (B == 0 || H == 0) return LA_OK;
+    const BlockLayout BL = block_layout(causal, B, H, N, d, KF, dt);
+    char* ws = static_cast<char*>(workspace);
+    if (BL.bytes > 0) {
+        if (ws == nullptr) return fail(LA_ERR_WORKSPACE, "workspace is NULL; %zu bytes are needed", BL.bytes);
+        if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+            return fail(LA_ERR_INVALID_ARGUMENT, "workspace must be %zu-byte aligned", kAlign);
+        if (workspace_bytes < BL.bytes)
+            return fail(LA_ERR_WORKSPACE, "workspace has %zu bytes; %zu are needed", workspace_bytes, BL.bytes);
+        const Range wsr = {"workspace", ws, BL.bytes};
+        for (const Range& r : in)
+            if (overlap(wsr, r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+        for (const Range& r : out)
+            if (overlap(wsr, r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+        for (const Range& r : states)
+            if (overlap(wsr, r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+    }
+    // Every block as a head of its own, reading its head's values (Gv = KF) ...
+    void* ob = BL.bytes > 0 ? ws + BL.ob : nullptr;
+    float* db = BL.bytes > 0 ? reinterpret_cast<float*>(ws + BL.db) : nullptr;
+    st = causal ? forward_causal(fq, fk, v, ob, S0, z0, db, S_out, z_out, nullptr, 0, B, H * KF, N, d, 0, dt, ws,
+                                 BL.inner, stream, la::kFeatGiven, H * KF, KF)
+                : forward_noncausal(fq, fk, v, ob, nullptr, 0, B, H * KF, N, d, dt, ws, BL.inner, stream,
+                                    la::kFeatGiven, KF, db);
+    if (st != LA_OK || N == 0) return st;
+    // ... then num = sum_j num_j and den = sum_j den_j.
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed("combine_blocks", s, [&] {
+        return la::launch_combine_blocks(dt == LA_BF16 ? la::kBF16 : la::kF32, (int)d, ob, db, o, den_out, B * H * N,
+                                         N, (int)KF, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "combine_blocks launch");
+    return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status la_features_workspace_size(int causal, int64_t B, int64_t H, int64_t N, int64_t d, int64_t m, la_dtype dt,
+                                     size_t* bytes_out) {
+    if (bytes_out == nullptr) return fail(LA_ERR_INVALID_ARGUMENT, "bytes_out is NULL");
+    la_status st = check_blocks(d, m);
+    if (st != LA_OK) return st;
+    bool empty = false;
+    if ((st = check_shape(B, H, N, d, 0, dt, &empty)) != LA_OK) return st;
+    *bytes_out = empty ? 0 : block_layout(causal != 0, B, H, N, d, m / d, dt).bytes;
+    return LA_OK;
+}
+
+la_status la_favor_features_blocks(const void* x, const float* omega, void* out, int64_t heads, int64_t N, int64_t d,
+                                   int64_t m, la_dtype dt, void* stream) {
+    la_status st = check_blocks(d, m);
+    if (st != LA_OK) return st;
+    if (dt != LA_F32 && dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "dtype %d is not LA_F32 or LA_BF16", (int)dt);
+    if (d != 32 && d != 64 && d != 128) return fail(LA_ERR_UNSUPPORTED, "d = %lld; built for 32, 64 and 128", (long long)d);
+    if (heads < 0 || N < 0) return fail(LA_ERR_INVALID_ARGUMENT, "negative heads %lld or N %lld", (long long)heads,
+                                        (long long)N);
+    const int64_t rows = heads * N;
+    if (rows > ((int64_t)1 << 40)) return fail(LA_ERR_UNSUPPORTED, "rows = %lld exceeds 2^40", (long long)rows);
+    if (!omega) return fail(LA_ERR_INVALID_ARGUMENT, "omega must be non-NULL");
+    if (rows > 0 && (!x || !out)) return fail(LA_ERR_INVALID_ARGUMENT, "x and out must be non-NULL");
+    const size_t xb = (size_t)rows * d * elem_size(dt);
+    const Range in[] = {{"x", x, xb}, {"omega", omega, (size_t)m * d * sizeof(float)}};
+    const Range out_r[] = {{"out", out, xb * (size_t)(m / d)}};
+    if ((st = check_ptrs(in, 2, out_r, 1)) != LA_OK) return st;
+    if (rows == 0) return LA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed("favor_features", s, [&] {
+        return la::launch_favor_features(dt == LA_BF16 ? la::kBF16 : la::kF32, (int)d, x, omega, out, rows, s, N,
+                                         (int)(m / d));
+    });
+    if (e != hipSuccess) return hip_fail(e, "favor_features launch");
+    return LA_OK;
+}
+
+la_status la_forward_causal_features_blocks(const void* fq, const void* fk, const void* v, void* o, const float* S0,
+                                            const float* z0, float* den_out, float* S_out, float* z_out, int64_t B,
+                                            int64_t H, int64_t N, int64_t d, int64_t m, la_dtype dt, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+    return forward_blocks(true, fq, fk, v, o, S0, z0, den_out, S_out, z_out, B, H, N, d, m, dt, workspace,
+                          workspace_bytes, stream);
+}
+
+la_status la_forward_noncausal_features_blocks(const void* fq, const void* fk, const void* v, void* o, float* den_out,
+                                               int64_t B, int64_t H, int64_t N, int64_t d, int64_t m, la_dtype dt,
+                                               void* workspace, size_t workspace_bytes, void* stream) {
+    return forward_blocks(false, fq, fk, v, o, nullptr, nullptr, den_out, nullptr, nullptr, B, H, N, d, m, dt,
+                          workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
 
 static la_status backward_causal(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
                                  void* dv, const void* saved_state, size_t saved_state_bytes, const float* S0,

@@ -4,7 +4,7 @@
 // kernel exp(q.k) is the expectation over w ~ N(0, I_d) of
 // exp(w.q - |q|^2/2) exp(w.k - |k|^2/2), so the features
 // phi(x)_i = m^{-1/2} exp(w_i.x - |x|^2/2), i < m, estimate it without bias and
-// stay positive.  Here m = d, and the constant m^{-1/2} is left out: it scales
+// stay positive.  Here m is a multiple of d, and the constant m^{-1/2} is left out: it scales
 // every weight of a row equally, so num / den does not see it (states and
 // denominators carry the factor m).  Left out, the features average 1 over the
 // draw of w, which suits the split phi = 1 + E the linear-attention kernels carry.
@@ -23,10 +23,13 @@ namespace la {
 // Omega is split into bf16 hi + lo parts and two bf16 MFMAs with fp32
 // accumulation give the exponent to about 2^-17 of sum |w_i x_i| (a sixteenth
 // of the fp32 MFMA's cost per product); fp32 rows use the fp32 MFMA.
+// Feature block j = blockIdx.y (directions omega[j D .. j D + D - 1]) of row r = h N + t
+// goes to row (h KF + j) N + t of out: with KF = m / D blocks, each head's features
+// are KF contiguous [N][D] matrices (KF = 1: out is [rows][D] like x).
 template <typename T, int D>
 __global__ __launch_bounds__(kBlock) void favor_features_kernel(const T* __restrict__ x,
                                                                 const float* __restrict__ omega, T* __restrict__ out,
-                                                                int64_t rows) {
+                                                                int64_t rows, int64_t N, int KF) {
     constexpr bool kBF = sizeof(T) == 2;
     using M = Mma<T>;
     constexpr int DT = D / 16;
@@ -39,6 +42,8 @@ __global__ __launch_bounds__(kBlock) void favor_features_kernel(const T* __restr
     __shared__ __attribute__((aligned(16))) T s_x[2][kC * D];
     __shared__ float s_n[2][kC];
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
+    const int jb = blockIdx.y;
+    omega += (int64_t)jb * D * D;
 
     for (int i = tid; i < D * D / 4; i += kBlock) {
         const int r = (4 * i) / D, c = (4 * i) % D;
@@ -99,13 +104,15 @@ __global__ __launch_bounds__(kBlock) void favor_features_kernel(const T* __restr
         const int t = 16 * w + (lane & 15);
         const int64_t row = r0 + t;
         if (row < rows) {
+            const int64_t hh = row / N;
+            const int64_t orow = (hh * KF + jb) * N + (row - hh * N);
             const float half_n = 0.5f * sn[t];
 #pragma unroll
             for (int m = 0; m < DT; ++m) {
                 f32x4 y;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) y[e] = __builtin_amdgcn_exp2f((acc[m][e] - half_n) * 1.4426950408889634f);
-                store4(out + row * D + 16 * m + 4 * g, y);
+                store4(out + orow * D + 16 * m + 4 * g, y);
             }
         }
         // The next chunk stages into the other LDS buffer; the barrier after that
@@ -114,12 +121,13 @@ __global__ __launch_bounds__(kBlock) void favor_features_kernel(const T* __restr
 }
 
 hipError_t launch_favor_features(int dt, int d, const void* x, const float* omega, void* out, int64_t rows,
-                                 hipStream_t s) {
+                                 hipStream_t s, int64_t N, int KF) {
     if (rows == 0) return hipSuccess;
-    const dim3 grid((unsigned)((rows + 4 * kC - 1) / (4 * kC)));
+    if (N <= 0) N = rows;
+    const dim3 grid((unsigned)((rows + 4 * kC - 1) / (4 * kC)), (unsigned)KF);
 #define LA_FAV(TT, DD)                                                                                        \
     hipLaunchKernelGGL((favor_features_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)x, omega, (TT*)out, \
-                       rows)
+                       rows, N, KF)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_FAV(bf16, 32); break;
@@ -136,6 +144,62 @@ hipError_t launch_favor_features(int dt, int d, const void* x, const float* omeg
         }
     }
 #undef LA_FAV
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// combine_blocks: attention over KF feature blocks of one head, each computed as its own
+// head (o_j = num_j / den_j, den_j), put together: num = sum_j num_j and den = sum_j den_j,
+// so o = sum_j den_j o_j / sum_j den_j.  ob [BH][KF][N][D] in T, db [BH][KF][N] fp32;
+// o [BH][N][D], den_out (nullable) [BH][N].  One thread per 4 elements of a row.
+template <typename T, int D>
+__global__ __launch_bounds__(kBlock) void combine_blocks_kernel(const T* __restrict__ ob, const float* __restrict__ db,
+                                                                T* __restrict__ o, float* __restrict__ den_out,
+                                                                int64_t rows, int64_t N, int KF) {
+    constexpr int TPR = D / 4;
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int64_t row = i / TPR;
+    if (row >= rows) return;
+    const int c = 4 * (int)(i % TPR);
+    const int64_t hh = row / N, t = row - hh * N;
+    f32x4 acc = zero4();
+    float den = 0.f;
+    for (int j = 0; j < KF; ++j) {
+        const int64_t br = (hh * KF + j) * N + t;
+        const float dj = db[br];
+        const T* p = ob + br * D + c;
+        den += dj;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += dj * to_f32(p[e]);
+    }
+    const float inv = rcp_f(den);
+    store4(o + row * D + c, acc * inv);
+    if (den_out != nullptr && c == 0) den_out[row] = den;
+}
+
+hipError_t launch_combine_blocks(int dt, int d, const void* ob, const float* db, void* o, float* den_out,
+                                 int64_t rows, int64_t N, int KF, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    const dim3 grid((unsigned)((rows * (d / 4) + kBlock - 1) / kBlock));
+#define LA_CMB(TT, DD)                                                                                         \
+    hipLaunchKernelGGL((combine_blocks_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)ob, db, (TT*)o,    \
+                       den_out, rows, N, KF)
+    if (dt == kBF16) {
+        switch (d) {
+            case 32: LA_CMB(bf16, 32); break;
+            case 64: LA_CMB(bf16, 64); break;
+            case 128: LA_CMB(bf16, 128); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (d) {
+            case 32: LA_CMB(float, 32); break;
+            case 64: LA_CMB(float, 64); break;
+            case 128: LA_CMB(float, 128); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+#undef LA_CMB
     return hipGetLastError();
 }
 

@@ -43,9 +43,12 @@ namespace la {
 // MFMA operands, since each wavefront reads its own key columns only.  Waits
 // and barriers are explicit: a step waits for its slot's loads, synchronises
 // the workgroup, then refills the slot the previous step has finished reading.
+// Gv: heads per value head (head bh reads the values of head bh / Gv: the feature
+// blocks of one head share its values; Gv = 1: one each).
 template <typename T, int D, class FM = FeatElu>
 __global__ __launch_bounds__(kBlock, 2) void seg_state_kernel(const T* __restrict__ k, const T* __restrict__ v,
-                                                           float* __restrict__ rec, int N, int cps, int nseg, int BH) {
+                                                           float* __restrict__ rec, int N, int cps, int nseg, int BH,
+                                                           int Gv) {
     using DMA = TileDma<T, D>;
     constexpr int R = kC * D * (int)sizeof(T) >= 16384 ? 2 : 4;
     constexpr int RS = R > 2 ? kC * D : 16;  // slots 2 and 3 exist only for R = 4
@@ -56,9 +59,9 @@ __global__ __launch_bounds__(kBlock, 2) void seg_state_kernel(const T* __restric
 
     const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
-    const int64_t hoff = (int64_t)bh * N * D;
+    const int64_t hoff = (int64_t)bh * N * D, voff = (int64_t)(bh / Gv) * N * D;
     const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
-    const GBuf bk(k + hoff, hbytes), bv(v + hoff, hbytes);
+    const GBuf bk(k + hoff, hbytes), bv(v + voff, hbytes);
     const int tok_begin = seg * cps * kC;
     const int tok_end = min(N, tok_begin + cps * kC);
     const int nch = (tok_end - tok_begin + kC - 1) / kC;
@@ -198,7 +201,7 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ o,
     float* __restrict__ den_out, const float* __restrict__ rec, float* __restrict__ S_out, float* __restrict__ z_out,
     const float* __restrict__ init, const float* __restrict__ init_n, int N, int cps, int nseg, int BH,
-    int prefixed, int G) {
+    int prefixed, int G, int Gv) {
     using M = Mma<T>;
     using F = typename M::frag;
     constexpr int KS = M::KSTEP;
@@ -213,19 +216,20 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
     // older workgroup issues ahead of its younger one.
     const int seg = nseg - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
     // Query head bh reads the keys, values, records and start state of key/value
-    // head kv (G query heads share one: grouped heads; G = 1: one each).
+    // head kv (G query heads share one: grouped heads; G = 1: one each), and the
+    // values of head kv / Gv (feature blocks of one head share its values).
     const int kv = bh / G;
     const int wv = wave_id(), lane = threadIdx.x & 63, g = lane >> 4;
     const int w = wv & 3;                     // wave index inside its role
     const int rtid = (int)threadIdx.x & (kBlock - 1);  // thread index inside its role
-    const int64_t hoff = (int64_t)bh * N * D, kvoff = (int64_t)kv * N * D;
+    const int64_t hoff = (int64_t)bh * N * D, kvoff = (int64_t)kv * N * D, voff = (int64_t)(kv / Gv) * N * D;
     const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
     const int tok_begin = seg * cps * kC;
     const int tok_end = min(N, tok_begin + cps * kC);
 
     if (wv >= 4) {
         // ---- state waves -------------------------------------------------------------
-        const GBuf bk(k + kvoff, hbytes), bv(v + kvoff, hbytes);
+        const GBuf bk(k + kvoff, hbytes), bv(v + voff, hbytes);
         // The first chunk's loads are in flight while the starting state arrives:
         // the records of the segments before this one, summed in order.
         ChunkRegs<T, D> ck, cv;
@@ -405,6 +409,7 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
 // on its own token tiles with phi(Q) in registers (no barrier in the loop).
 template <typename T, int D, class FM = FeatElu>
 __global__ __launch_bounds__(kBlock) void noncausal_fwd_kernel(const T* __restrict__ q, T* __restrict__ o,
+                                                               float* __restrict__ den_out,
                                                                const float* __restrict__ total, int ntotal, int N,
                                                                int cps, int nseg, int BH) {
     using M = Mma<T>;
@@ -458,8 +463,10 @@ __global__ __launch_bounds__(kBlock) void noncausal_fwd_kernel(const T* __restri
             for (int m = 0; m < DT; ++m) acc[m] = M::mma(M::ld(tSt, 16 * m, k0, lane), yf, acc[m]);
         }
         const float qs_t = FM::kSplit ? acc_q[0] : 0.f;  // weight of the rank-1 parts (none when unsplit)
-        const float inv = rcp_f(n * qs_t + zdot);
+        const float den = n * qs_t + zdot;
+        const float inv = rcp_f(den);
         const int tok = c0 + tl;
+        if (den_out != nullptr && g == 0 && tok < tok_end) den_out[(int64_t)bh * N + tok] = den;
 #pragma unroll
         for (int m = 0; m < DT; ++m) {
             const int b0 = 16 * m + 4 * g;
@@ -567,22 +574,22 @@ hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s) { return launch_c
 
 template <class FM>
 static hipError_t launch_seg_state_fm(int dt, int d, const void* k, const void* v, float* rec, int64_t BH, int64_t N,
-                                      SegPlan p, hipStream_t s) {
+                                      SegPlan p, hipStream_t s, int Gv) {
     const dim3 grid((unsigned)(p.nseg * BH));
     if (dt == kBF16) {
         LA_DISPATCH_D(d, hipLaunchKernelGGL((seg_state_kernel<bf16, D, FM>), grid, dim3(kBlock), 0, s, (const bf16*)k,
-                                            (const bf16*)v, rec, (int)N, p.cps, p.nseg, (int)BH));
+                                            (const bf16*)v, rec, (int)N, p.cps, p.nseg, (int)BH, Gv));
     } else {
         LA_DISPATCH_D(d, hipLaunchKernelGGL((seg_state_kernel<float, D, FM>), grid, dim3(kBlock), 0, s, (const float*)k,
-                                            (const float*)v, rec, (int)N, p.cps, p.nseg, (int)BH));
+                                            (const float*)v, rec, (int)N, p.cps, p.nseg, (int)BH, Gv));
     }
     return hipGetLastError();
 }
 
 hipError_t launch_seg_state(int dt, int d, const void* k, const void* v, float* rec, int64_t BH, int64_t N,
-                            SegPlan p, hipStream_t s, int feat) {
-    return feat == kFeatGiven ? launch_seg_state_fm<FeatGiven>(dt, d, k, v, rec, BH, N, p, s)
-                              : launch_seg_state_fm<FeatElu>(dt, d, k, v, rec, BH, N, p, s);
+                            SegPlan p, hipStream_t s, int feat, int Gv) {
+    return feat == kFeatGiven ? launch_seg_state_fm<FeatGiven>(dt, d, k, v, rec, BH, N, p, s, Gv)
+                              : launch_seg_state_fm<FeatElu>(dt, d, k, v, rec, BH, N, p, s, Gv);
 }
 
 hipError_t launch_total(int d, const float* rec, float* total, int64_t BH, int nseg, hipStream_t s) {
@@ -603,12 +610,12 @@ template <class FM>
 static hipError_t launch_causal_fwd_fm(int dt, int d, const void* q, const void* k, const void* v, void* o,
                                        float* den_out, const float* rec, float* S_out, float* z_out, int64_t BH,
                                        int64_t N, SegPlan p, hipStream_t s, const float* init, const float* init_n,
-                                       int G) {
+                                       int G, int Gv) {
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_CFWD(TT, DD)                                                                                          \
     hipLaunchKernelGGL((causal_fwd_kernel<TT, DD, FM>), grid, dim3(2 * kBlock), 0, s, (const TT*)q, (const TT*)k,   \
                        (const TT*)v, (TT*)o, den_out, rec, S_out, z_out, init, init_n, (int)N, p.cps, p.nseg,     \
-                       (int)BH, (int)p.scan, G)
+                       (int)BH, (int)p.scan, G, Gv)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_CFWD(bf16, 32); break;
@@ -629,33 +636,34 @@ static hipError_t launch_causal_fwd_fm(int dt, int d, const void* q, const void*
 
 hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const void* v, void* o, float* den_out,
                              const float* rec, float* S_out, float* z_out, int64_t BH, int64_t N, SegPlan p,
-                             hipStream_t s, const float* init, const float* init_n, int feat, int G) {
+                             hipStream_t s, const float* init, const float* init_n, int feat, int G, int Gv) {
     return feat == kFeatGiven
                ? launch_causal_fwd_fm<FeatGiven>(dt, d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, p, s, init, init_n,
-                                                 G)
+                                                 G, Gv)
                : launch_causal_fwd_fm<FeatElu>(dt, d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, p, s, init, init_n,
-                                               G);
+                                               G, Gv);
 }
 
 template <class FM>
-static hipError_t launch_noncausal_fwd_fm(int dt, int d, const void* q, void* o, const float* total, int ntotal,
-                                          int64_t BH, int64_t N, SegPlan p, hipStream_t s) {
+static hipError_t launch_noncausal_fwd_fm(int dt, int d, const void* q, void* o, float* den_out, const float* total,
+                                          int ntotal, int64_t BH, int64_t N, SegPlan p, hipStream_t s) {
     const dim3 grid((unsigned)(p.nseg * BH));
     if (dt == kBF16) {
         LA_DISPATCH_D(d, hipLaunchKernelGGL((noncausal_fwd_kernel<bf16, D, FM>), grid, dim3(kBlock), 0, s,
-                                            (const bf16*)q, (bf16*)o, total, ntotal, (int)N, p.cps, p.nseg, (int)BH));
+                                            (const bf16*)q, (bf16*)o, den_out, total, ntotal, (int)N, p.cps, p.nseg,
+                                            (int)BH));
     } else {
         LA_DISPATCH_D(d, hipLaunchKernelGGL((noncausal_fwd_kernel<float, D, FM>), grid, dim3(kBlock), 0, s,
-                                            (const float*)q, (float*)o, total, ntotal, (int)N, p.cps, p.nseg,
+                                            (const float*)q, (float*)o, den_out, total, ntotal, (int)N, p.cps, p.nseg,
                                             (int)BH));
     }
     return hipGetLastError();
 }
 
 hipError_t launch_noncausal_fwd(int dt, int d, const void* q, void* o, const float* total, int ntotal, int64_t BH,
-                                int64_t N, SegPlan p, hipStream_t s, int feat) {
-    return feat == kFeatGiven ? launch_noncausal_fwd_fm<FeatGiven>(dt, d, q, o, total, ntotal, BH, N, p, s)
-                              : launch_noncausal_fwd_fm<FeatElu>(dt, d, q, o, total, ntotal, BH, N, p, s);
+                                int64_t N, SegPlan p, hipStream_t s, int feat, float* den_out) {
+    return feat == kFeatGiven ? launch_noncausal_fwd_fm<FeatGiven>(dt, d, q, o, den_out, total, ntotal, BH, N, p, s)
+                              : launch_noncausal_fwd_fm<FeatElu>(dt, d, q, o, den_out, total, ntotal, BH, N, p, s);
 }
 
 }  // namespace la

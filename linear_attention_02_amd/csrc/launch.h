@@ -45,8 +45,9 @@ inline int64_t rec_floats(int64_t d) { return d * d + 2 * d; }
 
 // Forward pieces.  Segment records are per-segment aggregates laid out
 // [BH][nseg][rec_floats(d)]; workgroups are numbered segment-major.
+// Gv: heads per value head (head bh reads the values of head bh / Gv).
 hipError_t launch_seg_state(int dt, int d, const void* k, const void* v, float* rec, int64_t BH,
-                            int64_t N, SegPlan p, hipStream_t s, int feat = kFeatElu);
+                            int64_t N, SegPlan p, hipStream_t s, int feat = kFeatElu, int Gv = 1);
 // Per-head sum of the segment records (segment order).
 hipError_t launch_total(int d, const float* rec, float* total, int64_t BH, int nseg, hipStream_t s);
 // In place: record s becomes the sum of the records before it (dir > 0) or after it (dir < 0),
@@ -57,19 +58,22 @@ hipError_t launch_scan(int d, float* rec, int64_t BH, int nseg, int dir, hipStre
 // init / init_n (nullable): per head, a start-state record and its token count n0
 // (from launch_state_split); the carried state of every segment starts from them.
 // G: query heads per key/value head (BH counts query heads; k, v, rec, init, S_out
-// and z_out are indexed by key/value head bh / G).
+// and z_out are indexed by key/value head bh / G).  Gv: key/value heads per value head
+// (v is indexed by (bh / G) / Gv).
 hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const void* v, void* o,
                              float* den_out, const float* rec, float* S_out, float* z_out, int64_t BH,
                              int64_t N, SegPlan p, hipStream_t s, const float* init = nullptr,
-                             const float* init_n = nullptr, int feat = kFeatElu, int G = 1);
+                             const float* init_n = nullptr, int feat = kFeatElu, int G = 1, int Gv = 1);
 // A start state (S0 [BH][d][d], z0 [BH][d], either nullable = zero) in the carried split
 // form: one record [S0_E^T | z0_E | P0] per head in init, and n0 per head in init_n.
 hipError_t launch_state_split(int d, const float* S0, const float* z0, float* init, float* init_n, int64_t BH,
                               hipStream_t s, int feat = kFeatElu);
 // Non-causal outputs from each head's state: the in-order sum of `ntotal`
 // records per head at `total` (the segment records, or one precomputed total).
+// den_out (nullable): phi(Q_i)^T z per row, [BH][N].
 hipError_t launch_noncausal_fwd(int dt, int d, const void* q, void* o, const float* total, int ntotal,
-                                int64_t BH, int64_t N, SegPlan p, hipStream_t s, int feat = kFeatElu);
+                                int64_t BH, int64_t N, SegPlan p, hipStream_t s, int feat = kFeatElu,
+                                float* den_out = nullptr);
 
 // Backward pieces.  bwd_prefix starts each segment from the sum of the forward
 // records before it and writes the segment's suffix-state aggregate to rrec;
@@ -127,6 +131,12 @@ hipError_t launch_decode_steps(int dt, int d, float* S, float* z, const void* q,
 // FAVOR+ random features of `rows` rows of x [rows][d]: out[r][i] = exp(omega_i . x_r - |x_r|^2 / 2)
 // for the d rows of omega [d][d] fp32 (m = d features; the constant 1/sqrt(m) is left out).
 hipError_t launch_favor_features(int dt, int d, const void* x, const float* omega, void* out, int64_t rows,
-                                 hipStream_t s);
+                                 hipStream_t s, int64_t N = 0, int KF = 1);
+// KF feature blocks of rows x [rows][d] (rows = heads x N; omega [KF d][d]) into
+// out [heads][KF][N][d]; N = 0: one head of all rows.
+// o = sum_j den_j o_j / sum_j den_j over the KF feature blocks of each head (ob
+// [heads][KF][N][d], db [heads][KF][N]); den_out (nullable) gets sum_j den_j.
+hipError_t launch_combine_blocks(int dt, int d, const void* ob, const float* db, void* o, float* den_out,
+                                 int64_t rows, int64_t N, int KF, hipStream_t s);
 
 }  // namespace la

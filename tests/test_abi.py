@@ -218,3 +218,39 @@ def test_forward_causal_grouped_validation(lib):
     assert f(q, k, v, o, None, None, None, S, S + 2 * 64 * 64 * 4 - 16, 1, 8, 2, 64, 64, 0, 1, wsp, 1 << 30,
              None) == 1                                                                   # z_out overlaps S_out
     assert f(q, k, v, o, None, None, None, S, S + 2 * 64 * 64 * 4, 1, 8, 2, 64, 64, 0, 1, wsp, 16, None) == 3
+
+
+def test_feature_blocks_validation(lib):
+    out = ctypes.c_size_t(0)
+    wsz = lambda causal, m: lib.la_features_workspace_size(causal, 1, 2, 64, 64, m, 1, ctypes.byref(out))
+    assert wsz(1, 96) == 1                                    # m not a multiple of d
+    assert wsz(1, 32) == 1                                    # fewer features than d
+    assert wsz(1, 64 * 65) == 2                               # more than 64 blocks
+    assert wsz(1, 64) == 0
+    assert out.value == ws(lib, la.LA_OP_FWD_CAUSAL, 1, 2, 64, 64)[1]  # m = d: the plain call's workspace
+    assert wsz(1, 128) == 0
+    # two blocks: the plain workspace of 4 heads plus the blocks' outputs (bf16 rows) and denominators
+    assert out.value >= ws(lib, la.LA_OP_FWD_CAUSAL, 1, 4, 64, 64)[1] + 4 * 64 * 64 * 2 + 4 * 64 * 4
+    assert wsz(0, 128) == 0 and out.value >= ws(lib, la.LA_OP_FWD_NONCAUSAL, 1, 4, 64, 64)[1] + 4 * 64 * 64 * 2
+    f = lib.la_forward_causal_features_blocks
+    fq, fk, v, o, wsp = A, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000
+    fb = 2 * 64 * 64 * 2 * 2                                  # B H N d bf16 x 2 blocks
+    n5 = (None,) * 5
+    assert f(fq, fk, v, o, *n5, 1, 2, 64, 64, 96, 1, wsp, 1 << 30, None) == 1
+    assert f(fq, fk, v, o, *n5, 1, 2, 64, 64, 128, 1, wsp, 16, None) == 3          # workspace too small
+    assert f(fq, fk, v, fk + fb - 16, *n5, 1, 2, 64, 64, 128, 1, wsp, 1 << 30, None) == 1  # o overlaps fk's blocks
+    assert f(fq, fk, v, fk + fb, *n5, 1, 2, 64, 64, 128, 1, wsp, 16, None) == 3            # ... and past them
+    assert f(fq, fk, v, o, *n5, 1, 2, 64, 64, 128, 1, o, 1 << 30, None) == 1       # workspace overlaps o
+    S, z = A + 0x6000000, A + 0x6100000
+    assert f(fq, fk, v, o, None, None, None, S, o + 64, 1, 2, 64, 64, 128, 1, wsp, 1 << 30, None) == 1  # z_out on o
+    assert f(fq, fk, v, o, *n5, 1, 2, 0, 64, 128, 1, None, 0, None) == 0            # no tokens
+    assert f(fq, fk, v, o, *n5, 1, 2, 64, 128, 256, 0, wsp, 1 << 30, None) == 2     # fp32 causal d = 128
+    g = lib.la_forward_noncausal_features_blocks
+    assert g(fq, fk, v, o, None, 1, 2, 64, 64, 128, 1, wsp, 16, None) == 3
+    assert g(fq, fk, v, o, o + 64, 1, 2, 64, 64, 128, 1, wsp, 1 << 30, None) == 1  # den_out overlaps o
+    h = lib.la_favor_features_blocks
+    om = A + 0x5000000
+    assert h(A, om, A + 0x1000000, 2, 64, 64, 96, 1, None) == 1                    # m not a multiple of d
+    assert h(A, om, A + 2 * 64 * 64 * 2 - 16, 2, 64, 64, 128, 1, None) == 1        # out overlaps x
+    assert h(A, None, A + 0x1000000, 2, 64, 64, 128, 1, None) == 1                 # no directions
+    assert h(A, om, A + 0x1000000, 0, 64, 64, 128, 1, None) == 0                   # no rows
