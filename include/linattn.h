@@ -253,7 +253,8 @@ la_status la_decode_steps_features(float* S, float* z, const void* fq, const voi
  * as sum_j den_j O_j / sum_j den_j (O_j kept in dt in the workspace).  Start and final
  * states (causal only, nullable, natural layout above) as la_forward_causal_features.
  * Workspace: la_features_workspace_size(causal != 0, B, H, N, d, m, dt, &bytes), which
- * for KF > 1 holds the blocks' outputs besides the plain call's workspace. */
+ * for KF > 1 holds the blocks' outputs besides the plain call's workspace (causal = 2:
+ * the workspace of la_decode_steps_features_blocks with N = T). */
 la_status la_features_workspace_size(int causal, int64_t B, int64_t H, int64_t N, int64_t d, int64_t m,
                                      la_dtype dt, size_t* bytes_out);
 la_status la_favor_features_blocks(const void* x, const float* omega, void* out, int64_t heads, int64_t N,
@@ -266,6 +267,15 @@ la_status la_forward_noncausal_features_blocks(const void* fq, const void* fk, c
                                                float* den_out, int64_t B, int64_t H, int64_t N, int64_t d,
                                                int64_t m, la_dtype dt, void* workspace, size_t workspace_bytes,
                                                void* stream);
+/* Multi-token decode (la_decode_steps_features) on m = KF d features: fq [B][H][KF][T][d]
+ * and fk [B][Hkv][KF][T][d] in block layout, v, o as la_decode_steps; the state of key/value
+ * head j is S [B][Hkv][m][d], z [B][Hkv][m] (what la_forward_causal_features_blocks leaves
+ * with H = Hkv).  Workspace (KF > 1): la_features_workspace_size(2, B, H, T, d, m, dt, &bytes);
+ * m = d needs none and is la_decode_steps_features. */
+la_status la_decode_steps_features_blocks(float* S, float* z, const void* fq, const void* fk, const void* v,
+                                          void* o, int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t d,
+                                          int64_t m, la_dtype dt, void* workspace, size_t workspace_bytes,
+                                          void* stream);
 
 /* Static description of a status code. */
 const char* la_status_string(la_status s);

@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     features_workspace_size,
     la_forward_causal_features_blocks,
     la_forward_noncausal_features_blocks,
+    la_decode_steps_features_blocks,
     la_forward_causal,
     la_forward_causal_grouped,
     la_forward_noncausal,

@@ -24,7 +24,8 @@ EXPORTS = ("la_workspace_size", "la_saved_state_size", "la_forward_noncausal", "
            "la_backward_noncausal", "la_decode_step", "la_decode_steps", "la_favor_features",
            "la_forward_causal_features", "la_forward_noncausal_features", "la_decode_steps_features",
            "la_backward_causal_state", "la_forward_causal_grouped", "la_features_workspace_size",
-           "la_favor_features_blocks", "la_forward_causal_features_blocks", "la_forward_noncausal_features_blocks", "la_status_string", "la_last_error_message", "la_version",
+           "la_favor_features_blocks", "la_forward_causal_features_blocks", "la_forward_noncausal_features_blocks",
+           "la_decode_steps_features_blocks", "la_status_string", "la_last_error_message", "la_version",
            "la_profile_enable", "la_profile_count", "la_profile_entry", "la_debug_set_wait_limit",
            "la_debug_wait_limit")
 
@@ -68,6 +69,8 @@ def load_library(path: str | None = None):
     lib.la_forward_causal_features_blocks.argtypes = [vp] * 9 + [i64, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_forward_noncausal_features_blocks.restype = i32
     lib.la_forward_noncausal_features_blocks.argtypes = [vp] * 5 + [i64, i64, i64, i64, i64, i32, vp, sz, vp]
+    lib.la_decode_steps_features_blocks.restype = i32
+    lib.la_decode_steps_features_blocks.argtypes = [vp] * 6 + [i64, i64, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_forward_causal_grouped.restype = i32
     lib.la_forward_causal_grouped.argtypes = [vp] * 9 + [i64, i64, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.la_backward_causal_state.restype = i32
@@ -415,7 +418,8 @@ def favor_features_blocks(x, omega, *, out=None):
 
 def features_workspace_size(causal, B, H, N, d, m, dtype):
     out = ctypes.c_size_t(0)
-    _check(load_library().la_features_workspace_size(1 if causal else 0, B, H, N, d, m, _dtype_code(dtype),
+    kind = 2 if causal == 2 else (1 if causal else 0)
+    _check(load_library().la_features_workspace_size(kind, B, H, N, d, m, _dtype_code(dtype),
                                                      ctypes.byref(out)))
     return out.value
 
@@ -476,6 +480,32 @@ def la_forward_noncausal_features_blocks(fq, fk, v, *, return_den=False, out=Non
                                                                N, d, m, _dtype_code(fq.dtype), _ptr(ws), nbytes,
                                                                _stream(fq.device)))
     return (o, den) if return_den else o
+
+
+def la_decode_steps_features_blocks(S, z, fq, fk, v, *, out=None, workspace=None):
+    """Multi-token decode on m = KF d features in block layout: fq [B, H, KF, T, d], fk [B, Hkv, KF, T, d],
+    v [B, Hkv, T, d]; S [B, Hkv, m, d] and z [B, Hkv, m] fp32, updated in place.  Returns o [B, H, T, d]."""
+    if fq.dim() != 5 or fk.dim() != 5 or v.dim() != 4:
+        raise ValueError("fq, fk must be [B, H(kv), KF, T, d] and v [B, Hkv, T, d]")
+    B, H, KF, T, d = fq.shape
+    Hkv = fk.shape[1]
+    m = KF * d
+    if fk.shape != (B, Hkv, KF, T, d) or v.shape != (B, Hkv, T, d) or Hkv == 0 or H % Hkv:
+        raise ValueError("fk must be [B, Hkv, KF, T, d], v [B, Hkv, T, d], with H a multiple of Hkv")
+    if S.shape != (B, Hkv, m, d) or z.shape != (B, Hkv, m) or S.dtype != torch.float32 or z.dtype != torch.float32:
+        raise ValueError("S must be [B, Hkv, m, d] and z [B, Hkv, m] fp32")
+    for t in (fq, fk, v, S, z):
+        if t.device != fq.device or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("all tensors must be contiguous on one HIP device")
+    o = torch.empty((B, H, T, d), dtype=fq.dtype, device=fq.device) if out is None else out
+    need = features_workspace_size(2, B, H, T, d, m, fq.dtype)
+    ws = workspace if workspace is not None else (torch.empty(need, dtype=torch.uint8, device=fq.device)
+                                                  if need else None)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().la_decode_steps_features_blocks(_ptr(S), _ptr(z), _ptr(fq), _ptr(fk), _ptr(v), _ptr(o), B, H,
+                                                          Hkv, T, d, m, _dtype_code(fq.dtype), _ptr(ws), nbytes,
+                                                          _stream(fq.device)))
+    return o
 
 
 def la_forward_causal_features(fq, fk, v, *, return_den=False, return_state=False, out=None, workspace=None,

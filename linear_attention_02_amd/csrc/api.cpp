@@ -608,6 +608,13 @@ la_status la_features_workspace_size(int causal, int64_t B, int64_t H, int64_t N
     if (st != LA_OK) return st;
     bool empty = false;
     if ((st = check_shape(B, H, N, d, 0, dt, &empty)) != LA_OK) return st;
+    if (causal == 2) {  // multi-token decode: N = T tokens per call, H query heads
+        const int64_t KF = m / d;
+        *bytes_out = (empty || KF == 1) ? 0
+                                        : align_up((size_t)B * H * KF * N * d * elem_size(dt)) +
+                                              align_up((size_t)B * H * KF * N * sizeof(float));
+        return LA_OK;
+    }
     *bytes_out = empty ? 0 : block_layout(causal != 0, B, H, N, d, m / d, dt).bytes;
     return LA_OK;
 }
@@ -843,8 +850,12 @@ la_status la_decode_step(float* S, float* z, const void* q, const void* k, const
     return LA_OK;
 }
 
+// KF > 1: features in KF blocks (q [B][H][KF][T][d], k [B][Hkv][KF][T][d], states
+// [B][Hkv][KF d][d]); the blocks' outputs and denominators go to the workspace and are
+// combined into o.
 static la_status decode_steps(float* S, float* z, const void* q, const void* k, const void* v, void* o, int64_t B,
-                              int64_t H, int64_t Hkv, int64_t T, int64_t d, la_dtype dt, void* stream, int feat) {
+                              int64_t H, int64_t Hkv, int64_t T, int64_t d, la_dtype dt, void* stream, int feat,
+                              int64_t KF = 1, void* workspace = nullptr, size_t workspace_bytes = 0) {
     if (dt != LA_F32 && dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "dtype %d is not LA_F32 or LA_BF16", (int)dt);
     if (d != 32 && d != 64 && d != 128) return fail(LA_ERR_UNSUPPORTED, "d = %lld; built for 32, 64 and 128", (long long)d);
     if (B < 0 || H < 0 || Hkv < 0 || T < 0)
@@ -860,19 +871,42 @@ static la_status decode_steps(float* S, float* z, const void* q, const void* k, 
     if (T > 0 && (!q || !k || !v || !o)) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-NULL");
     const int64_t BHkv = B * Hkv;
     const size_t qb = (size_t)B * H * T * d * elem_size(dt), kb = (size_t)BHkv * T * d * elem_size(dt);
-    const Range in[] = {{"q", q, qb}, {"k", k, kb}, {"v", v, kb}};
-    const Range out[] = {{"S", S, (size_t)BHkv * d * d * sizeof(float)},
-                         {"z", z, (size_t)BHkv * d * sizeof(float)},
+    const Range in[] = {{"q", q, qb * KF}, {"k", k, kb * KF}, {"v", v, kb}};
+    const Range out[] = {{"S", S, (size_t)BHkv * KF * d * d * sizeof(float)},
+                         {"z", z, (size_t)BHkv * KF * d * sizeof(float)},
                          {"o", o, qb}};
     la_status st = check_ptrs(in, 3, out, 3);
     if (st != LA_OK) return st;
     if (BHkv == 0 || T == 0) return LA_OK;
+    const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ob = o;
+    float* db = nullptr;
+    if (KF > 1) {  // the blocks' outputs and denominators, then their combination
+        const size_t obb = align_up(qb * KF), need = obb + align_up((size_t)B * H * KF * T * sizeof(float));
+        if (workspace == nullptr) return fail(LA_ERR_WORKSPACE, "workspace is NULL; %zu bytes are needed", need);
+        if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+            return fail(LA_ERR_INVALID_ARGUMENT, "workspace must be %zu-byte aligned", kAlign);
+        if (workspace_bytes < need)
+            return fail(LA_ERR_WORKSPACE, "workspace has %zu bytes; %zu are needed", workspace_bytes, need);
+        const Range wsr = {"workspace", workspace, need};
+        for (const Range& r : in)
+            if (overlap(wsr, r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+        for (const Range& r : out)
+            if (overlap(wsr, r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+        ob = workspace;
+        db = reinterpret_cast<float*>(static_cast<char*>(workspace) + obb);
+    }
     hipError_t e = timed("decode_steps", s, [&] {
-        return la::launch_decode_steps(dt == LA_BF16 ? la::kBF16 : la::kF32, (int)d, S, z, q, k, v, o, BHkv, T, H / Hkv,
-                                       s, feat);
+        return la::launch_decode_steps(idt, (int)d, S, z, q, k, v, ob, BHkv, T, H / Hkv, s, feat, (int)KF, db);
     });
     if (e != hipSuccess) return hip_fail(e, "decode_steps launch");
+    if (KF > 1) {
+        e = timed("combine_blocks", s, [&] {
+            return la::launch_combine_blocks(idt, (int)d, ob, db, o, nullptr, B * H * T, T, (int)KF, s);
+        });
+        if (e != hipSuccess) return hip_fail(e, "combine_blocks launch");
+    }
     return LA_OK;
 }
 
@@ -885,6 +919,15 @@ la_status la_decode_steps_features(float* S, float* z, const void* fq, const voi
                                    int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t d, la_dtype dt,
                                    void* stream) {
     return decode_steps(S, z, fq, fk, v, o, B, H, Hkv, T, d, dt, stream, la::kFeatGiven);
+}
+
+la_status la_decode_steps_features_blocks(float* S, float* z, const void* fq, const void* fk, const void* v, void* o,
+                                          int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t d, int64_t m,
+                                          la_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+    la_status st = check_blocks(d, m);
+    if (st != LA_OK) return st;
+    return decode_steps(S, z, fq, fk, v, o, B, H, Hkv, T, d, dt, stream, la::kFeatGiven, m / d, workspace,
+                        workspace_bytes);
 }
 
 }  // extern "C"

@@ -85,17 +85,22 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(float* __restrict__ S, f
 // held in registers across the call (thread (rg, cq) owns columns 4 cq .. 4 cq + 3
 // of rows rg + RPP p), so it moves through HBM once per call instead of once per
 // token, and once per group instead of once per query head.
+// With KF feature blocks (features m = KF d, block layout), the state of block j of
+// key/value head kv is a state of its own (flat index kv KF + j) that reads the
+// head's values; q, o are the block layout's [B][H][KF][T][d] and den_out (nullable)
+// gets each row's denominator, for the combine over blocks.
 // Work goes in rows (t, h), token-major: a block of RB rows stages phi(q) of each
 // row and, on the row that opens a token (h = 0), phi(k) and v of that token
 // (zeros elsewhere, so z sums each token once); per row each thread applies the
 // token's rank-1 update where the row opens one, then forms its part of
 // phi(q)^T S, reduced over the row groups with shuffles inside a wavefront and
 // through LDS across the four.
-template <typename T, int D, class FM = FeatElu>
+template <typename T, int D, class FM = FeatElu, bool kBlocks = false>
 __global__ __launch_bounds__(kBlock) void decode_steps_kernel(float* __restrict__ S, float* __restrict__ z,
                                                               const T* __restrict__ q, const T* __restrict__ k,
                                                               const T* __restrict__ v, T* __restrict__ o, int ntok,
-                                                              int G) {
+                                                              int G, int KFb, float* __restrict__ den_out) {
+    const int KF = kBlocks ? KFb : 1;  // feature blocks (compiled out for one)
     constexpr int F4 = D / 4;         // float4 per state row
     constexpr int RPP = kBlock / F4;  // rows per pass
     constexpr int NP = D / RPP;       // passes
@@ -106,12 +111,15 @@ __global__ __launch_bounds__(kBlock) void decode_steps_kernel(float* __restrict_
     __shared__ __attribute__((aligned(16))) float s_red[RB][NW][D];
     __shared__ float s_den[RB][NW];
 
-    const int kvh = blockIdx.x;  // flat (b, key/value head)
+    const int kvh = blockIdx.x;  // flat (b, key/value head, feature block)
+    const int64_t bkv = kvh / KF, jb = kvh - bkv * KF;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
     const int rg = tid / F4, cq = tid % F4;
     f32x4* Sh = reinterpret_cast<f32x4*>(S + (int64_t)kvh * D * D);
-    const int64_t krow0 = (int64_t)kvh * ntok;        // first token row of this head in k, v
-    const int64_t qrow0 = (int64_t)kvh * G * ntok;    // first row of the group's first query head in q, o
+    const int64_t krow0 = (int64_t)kvh * ntok;        // first token row of this state's keys
+    const int64_t vrow0 = bkv * ntok;                 // ... and of its head's values
+    // Row t of query head h of the group: ((bkv G + h) KF + jb) ntok + t in q, o.
+    auto qrow = [&](int64_t t, int64_t h) { return ((bkv * G + h) * KF + jb) * ntok + t; };
     const int64_t nrows = (int64_t)G * ntok;
 
     f32x4 x[NP];
@@ -129,10 +137,10 @@ __global__ __launch_bounds__(kBlock) void decode_steps_kernel(float* __restrict_
             if (ri < nb) {
                 const int64_t r = r0 + ri;
                 const int64_t t = r / G, h = r % G;
-                qf = FM::phi(to_f32(q[(qrow0 + h * ntok + t) * D + a]));
+                qf = FM::phi(to_f32(q[qrow(t, h) * D + a]));
                 if (h == 0) {
                     kf = FM::phi(to_f32(k[(krow0 + t) * D + a]));
-                    vv = to_f32(v[(krow0 + t) * D + a]);
+                    vv = to_f32(v[(vrow0 + t) * D + a]);
                 }
             }
             s_qf[ri][a] = qf;
@@ -181,7 +189,8 @@ __global__ __launch_bounds__(kBlock) void decode_steps_kernel(float* __restrict_
                 num += s_red[ri][ww][b];
                 den += s_den[ri][ww];
             }
-            o[(qrow0 + h * ntok + t) * D + b] = from_f32<T>(num / den);
+            o[qrow(t, h) * D + b] = from_f32<T>(num / den);
+            if (kBlocks && den_out != nullptr && b == 0) den_out[qrow(t, h)] = den;
         }
         __syncthreads();  // the block's LDS is free for the next one
     }
@@ -192,11 +201,18 @@ __global__ __launch_bounds__(kBlock) void decode_steps_kernel(float* __restrict_
 
 template <class FM>
 static hipError_t launch_decode_steps_fm(int dt, int d, float* S, float* z, const void* q, const void* k,
-                                         const void* v, void* o, int64_t BHkv, int64_t T, int64_t G, hipStream_t s) {
-    const dim3 grid((unsigned)BHkv);
-#define LA_DECS(TT, DD)                                                                                     \
-    hipLaunchKernelGGL((decode_steps_kernel<TT, DD, FM>), grid, dim3(kBlock), 0, s, S, z, (const TT*)q,     \
-                       (const TT*)k, (const TT*)v, (TT*)o, (int)T, (int)G)
+                                         const void* v, void* o, int64_t BHkv, int64_t T, int64_t G, hipStream_t s,
+                                         int KF, float* den_out) {
+    const dim3 grid((unsigned)(BHkv * KF));
+#define LA_DECS(TT, DD)                                                                                    \
+    do {                                                                                                   \
+        if (KF > 1)                                                                                        \
+            hipLaunchKernelGGL((decode_steps_kernel<TT, DD, FM, true>), grid, dim3(kBlock), 0, s, S, z,    \
+                               (const TT*)q, (const TT*)k, (const TT*)v, (TT*)o, (int)T, (int)G, KF, den_out); \
+        else                                                                                               \
+            hipLaunchKernelGGL((decode_steps_kernel<TT, DD, FM, false>), grid, dim3(kBlock), 0, s, S, z,   \
+                               (const TT*)q, (const TT*)k, (const TT*)v, (TT*)o, (int)T, (int)G, 1, nullptr); \
+    } while (0)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_DECS(bf16, 32); break;
@@ -217,9 +233,10 @@ static hipError_t launch_decode_steps_fm(int dt, int d, float* S, float* z, cons
 }
 
 hipError_t launch_decode_steps(int dt, int d, float* S, float* z, const void* q, const void* k, const void* v,
-                               void* o, int64_t BHkv, int64_t T, int64_t G, hipStream_t s, int feat) {
-    return feat == kFeatGiven ? launch_decode_steps_fm<FeatGiven>(dt, d, S, z, q, k, v, o, BHkv, T, G, s)
-                              : launch_decode_steps_fm<FeatElu>(dt, d, S, z, q, k, v, o, BHkv, T, G, s);
+                               void* o, int64_t BHkv, int64_t T, int64_t G, hipStream_t s, int feat, int KF,
+                               float* den_out) {
+    return feat == kFeatGiven ? launch_decode_steps_fm<FeatGiven>(dt, d, S, z, q, k, v, o, BHkv, T, G, s, KF, den_out)
+                              : launch_decode_steps_fm<FeatElu>(dt, d, S, z, q, k, v, o, BHkv, T, G, s, KF, den_out);
 }
 
 hipError_t launch_decode(int dt, int d, float* S, float* z, const void* q, const void* k,

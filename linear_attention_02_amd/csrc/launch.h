@@ -124,10 +124,12 @@ hipError_t launch_copy_or_zero(float* p, const float* src, size_t n, hipStream_t
 hipError_t launch_decode(int dt, int d, float* S, float* z, const void* q, const void* k,
                          const void* v, void* o, int64_t BH, hipStream_t s);
 // T decode steps per key/value head in one pass over its state, read by G query heads;
-// k, v are [BHkv][T][d], q, o are [BHkv][G][T][d].
+// k, v are [BHkv][T][d], q, o are [BHkv][G][T][d].  KF feature blocks: KF states per
+// key/value head ([BHkv][KF][d][d]), k [BHkv][KF][T][d], q, o [BHkv][G][KF][T][d], v as
+// before; den_out (nullable) takes the denominators in the layout of q's rows.
 hipError_t launch_decode_steps(int dt, int d, float* S, float* z, const void* q, const void* k,
                                const void* v, void* o, int64_t BHkv, int64_t T, int64_t G, hipStream_t s,
-                               int feat = kFeatElu);
+                               int feat = kFeatElu, int KF = 1, float* den_out = nullptr);
 // FAVOR+ random features of `rows` rows of x [rows][d]: out[r][i] = exp(omega_i . x_r - |x_r|^2 / 2)
 // for the d rows of omega [d][d] fp32 (m = d features; the constant 1/sqrt(m) is left out).
 hipError_t launch_favor_features(int dt, int d, const void* x, const float* omega, void* out, int64_t rows,

@@ -254,3 +254,20 @@ def test_feature_blocks_validation(lib):
     assert h(A, om, A + 2 * 64 * 64 * 2 - 16, 2, 64, 64, 128, 1, None) == 1        # out overlaps x
     assert h(A, None, A + 0x1000000, 2, 64, 64, 128, 1, None) == 1                 # no directions
     assert h(A, om, A + 0x1000000, 0, 64, 64, 128, 1, None) == 0                   # no rows
+
+
+def test_decode_blocks_validation(lib):
+    f = lib.la_decode_steps_features_blocks
+    S, z, q, k, v, o = A, A + 0x1000000, A + 0x2000000, A + 0x2100000, A + 0x2200000, A + 0x2300000
+    wsp = A + 0x4000000
+    out = ctypes.c_size_t(0)
+    assert lib.la_features_workspace_size(2, 1, 8, 16, 64, 64, 1, ctypes.byref(out)) == 0 and out.value == 0
+    assert lib.la_features_workspace_size(2, 1, 8, 16, 64, 128, 1, ctypes.byref(out)) == 0
+    assert out.value >= 8 * 2 * 16 * 64 * 2 + 8 * 2 * 16 * 4
+    assert f(S, z, q, k, v, o, 1, 8, 2, 16, 64, 96, 1, wsp, 1 << 30, None) == 1    # m not a multiple of d
+    assert f(S, z, q, k, v, o, 1, 8, 2, 16, 64, 128, 1, None, 0, None) == 3        # KF = 2 needs a workspace
+    assert f(S, z, q, k, v, o, 1, 8, 2, 16, 64, 128, 1, wsp, 16, None) == 3
+    assert f(S, z, q, k, v, o, 1, 8, 2, 16, 64, 128, 1, o, 1 << 30, None) == 1     # workspace overlaps o
+    # the states are m x d per key/value head: z right after S of 2 x 128 x 64 fp32
+    assert f(S, S + 2 * 128 * 64 * 4 - 16, q, k, v, o, 1, 8, 2, 16, 64, 128, 1, wsp, 1 << 30, None) == 1
+    assert f(S, z, q, k, v, o, 1, 8, 2, 0, 64, 128, 1, None, 0, None) == 0         # no tokens

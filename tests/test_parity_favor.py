@@ -232,3 +232,37 @@ def test_favor_blocks_of_one_match_plain_calls(la):
     e = la.la_forward_noncausal_features_blocks(bq, bk, v)
     torch.cuda.synchronize()
     assert torch.equal(fq, bq[:, :, 0]) and torch.equal(a, b) and torch.equal(c, e)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("KF", [2, 3])
+@pytest.mark.parametrize("d", [64, 128])
+def test_favor_blocks_prefill_then_decode(la, oracle, d, KF, dtype):
+    """m = KF d features: prefill per key/value head, then multi-token decode with 3 query
+    heads per key/value head from the [B, Hkv, m, d] state it left, against the oracle's
+    m-feature recurrence over each query head's whole sequence."""
+    if dtype == torch.float32 and d == 128:
+        pytest.skip("fp32 causal path is built for d <= 64")
+    B, Hkv, G, N0, T = 2, 2, 3, 150, 11
+    H, m = Hkv * G, KF * d
+    om = inp.favor_omega(d, seed=15 + KF, m=m).cuda()
+    pq, pk, pv = (t.cuda() for t in inp.favor_qkv(B, Hkv, N0, d, dtype, seed=16))
+    _, S, z = la.la_forward_causal_features_blocks(la.favor_features_blocks(pq, om), la.favor_features_blocks(pk, om),
+                                                   pv, return_state=True)
+    q = inp.favor_qkv(B, H, T, d, dtype, seed=17)[0].cuda()
+    _, k, v = (t.cuda() for t in inp.favor_qkv(B, Hkv, T, d, dtype, seed=18))
+    o = la.la_decode_steps_features_blocks(S, z, la.favor_features_blocks(q, om), la.favor_features_blocks(k, om), v)
+    torch.cuda.synchronize()
+    worst, rS, rz = 0.0, [None] * Hkv, [None] * Hkv
+    for h in range(H):
+        j = h // G
+        kk, vv = np.concatenate([f64(pk[:, j]), f64(k[:, j])], 1), np.concatenate([f64(pv[:, j]), f64(v[:, j])], 1)
+        qq = np.concatenate([f64(pq[:, j]), f64(q[:, h])], 1)  # prefix rows are not compared
+        ro, rS[j], rz[j] = oracle.forward_features(oracle.favor_features(qq, f64(om)),
+                                                   oracle.favor_features(kk, f64(om)), vv, True, return_state=True)
+        worst = max(worst, slice_err(o[:, h], ro[:, N0:]))
+    rS, rz = np.stack(rS, 1), np.stack(rz, 1)
+    errs = {"o": worst, "S": slice_err(S, rS * math.sqrt(m)), "z": slice_err(z[..., None], rz[..., None] * math.sqrt(m))}
+    record(f"favor blocks prefill+decode d={d} m={m} {dtype}", **errs)
+    assert errs["o"] < TOL[dtype], errs
+    assert max(errs["S"], errs["z"]) < SUM_TOL[dtype], errs
