@@ -66,6 +66,8 @@ def _load():
     lib.la_oracle_favor_features.argtypes = [i64, i64, i64, dp, dp, dp]
     lib.la_oracle_forward_features.restype = None
     lib.la_oracle_forward_features.argtypes = [i64, i64, i64, i64, i32, dp, dp, dp, dp, dp, dp, dp]
+    lib.la_oracle_backward_features.argtypes = [i64, i64, i64, i64, i32] + [dp] * 7
+    lib.la_oracle_favor_features_backward.argtypes = [i64, i64, i64, dp, dp, dp, dp]
     lib.la_oracle_decode_step.restype = None
     lib.la_oracle_decode_step.argtypes = [i64, i64, dp, dp, dp, dp, dp, dp]
     lib.la_oracle_quadratic_forward.restype = None
@@ -275,3 +277,29 @@ def forward_features(fq, fk, v, causal, return_den=False, return_state=False):
     if return_state:
         out += [S, z]
     return out[0] if len(out) == 1 else tuple(out)
+
+
+def backward_features(fq, fk, v, dout, causal):
+    """Gradients (dfq, dfk, dv) of sum(dout * O) for forward_features(fq, fk, v, causal)."""
+    fq, fk, v, dout = _f64(fq), _f64(fk), _f64(v), _f64(dout)
+    if fq.shape != fk.shape or fq.shape[:-1] != v.shape[:-1] or dout.shape != v.shape:
+        raise ValueError("fq, fk must match, and share [..., N] with v and dout")
+    bh, n, m = _heads(fq)
+    dv = v.shape[-1]
+    dfq, dfk, dvo = np.empty(fq.shape), np.empty(fk.shape), np.empty(v.shape)
+    _load().la_oracle_backward_features(bh, n, m, dv, int(bool(causal)), _ptr(fq), _ptr(fk), _ptr(v), _ptr(dout),
+                                        _ptr(dfq), _ptr(dfk), _ptr(dvo))
+    return dfq, dfk, dvo
+
+
+def favor_features_backward(x, omega, dout):
+    """Gradient with respect to x of sum(dout * favor_features(x, omega)); dout [..., m]."""
+    x, omega, dout = _f64(x), _f64(omega), _f64(dout)
+    d = x.shape[-1]
+    m = omega.shape[0]
+    if omega.shape != (m, d) or dout.shape != x.shape[:-1] + (m,):
+        raise ValueError("omega must be [m, d] and dout [..., m]")
+    rows = int(np.prod(x.shape[:-1])) if x.ndim > 1 else 1
+    dx = np.empty(x.shape, dtype=np.float64)
+    _load().la_oracle_favor_features_backward(rows, d, m, _ptr(x), _ptr(omega), _ptr(dout), _ptr(dx))
+    return dx

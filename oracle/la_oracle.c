@@ -485,3 +485,99 @@ void la_oracle_forward_features(int64_t BH, int64_t N, int64_t m, int64_t dv, in
         free(z);
     }
 }
+
+/* ---- backward on given features ------------------------------------------------
+ * Gradients of L = sum(dout * O) for la_oracle_forward_features, by the chain rule
+ * (the pages print no backward).  With den_i, O_i of the forward, G_i = dout_i / den_i
+ * and g_i = -G_i . O_i (the derivative of O_i = num_i / den_i):
+ *   dfq_i = S_i G_i + g_i z_i           (S_i, z_i: the state row i reads),
+ *   dfk_j = R_j V_j + r_j,  dV_j = R_j^T fk_j,
+ * where R_j = sum fq_i G_i^T and r_j = sum g_i fq_i run over the rows i that read key j
+ * (i >= j in the recurrent form, every row otherwise). */
+void la_oracle_backward_features(int64_t BH, int64_t N, int64_t m, int64_t dv, int causal,
+                                 const double* fq, const double* fk, const double* v,
+                                 const double* dout, double* dfq, double* dfk, double* dvo) {
+    int nt = la_oracle_get_threads();
+    (void)nt;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t h = 0; h < BH; ++h) {
+        const double* qh = fq + h * N * m;
+        const double* kh = fk + h * N * m;
+        const double* vh = v + h * N * dv;
+        const double* doh = dout + h * N * dv;
+        double* S = zalloc(m * dv);
+        double* z = zalloc(m);
+        double* G = zalloc(N * dv);
+        double* g = zalloc(N);
+        /* forward sweep: the state each row reads, den, O, G, g and dfq */
+        int64_t added = 0;
+        for (int64_t i = 0; i < N; ++i) {
+            const int64_t upto = causal ? i + 1 : N;
+            for (; added < upto; ++added)
+                for (int64_t a = 0; a < m; ++a) {
+                    z[a] += kh[added * m + a];
+                    for (int64_t b = 0; b < dv; ++b) S[a * dv + b] += kh[added * m + a] * vh[added * dv + b];
+                }
+            double den = 0.0;
+            for (int64_t a = 0; a < m; ++a) den += qh[i * m + a] * z[a];
+            double go = 0.0;
+            for (int64_t b = 0; b < dv; ++b) {
+                double num = 0.0;
+                for (int64_t a = 0; a < m; ++a) num += qh[i * m + a] * S[a * dv + b];
+                G[i * dv + b] = doh[i * dv + b] / den;
+                go += G[i * dv + b] * (num / den);
+            }
+            g[i] = -go;
+            for (int64_t a = 0; a < m; ++a) {
+                double x = g[i] * z[a];
+                for (int64_t b = 0; b < dv; ++b) x += S[a * dv + b] * G[i * dv + b];
+                dfq[(h * N + i) * m + a] = x;
+            }
+        }
+        /* backward sweep over the keys: R, r over the rows that read key j */
+        double* R = zalloc(m * dv);
+        double* r = zalloc(m);
+        int64_t taken = N; /* rows folded into (R, r): i >= taken */
+        for (int64_t j = N - 1; j >= 0; --j) {
+            const int64_t from = causal ? j : 0;
+            for (; taken > from; ) {
+                --taken;
+                for (int64_t a = 0; a < m; ++a) {
+                    r[a] += g[taken] * qh[taken * m + a];
+                    for (int64_t b = 0; b < dv; ++b) R[a * dv + b] += qh[taken * m + a] * G[taken * dv + b];
+                }
+            }
+            for (int64_t a = 0; a < m; ++a) {
+                double x = r[a];
+                for (int64_t b = 0; b < dv; ++b) x += R[a * dv + b] * vh[j * dv + b];
+                dfk[(h * N + j) * m + a] = x;
+            }
+            for (int64_t b = 0; b < dv; ++b) {
+                double x = 0.0;
+                for (int64_t a = 0; a < m; ++a) x += R[a * dv + b] * kh[j * m + a];
+                dvo[(h * N + j) * dv + b] = x;
+            }
+        }
+        free(S); free(z); free(G); free(g); free(R); free(r);
+    }
+}
+
+/* Gradient through the FAVOR+ features: out_ri = m^{-1/2} exp(omega_i . x_r - |x_r|^2 / 2)
+ * has d out_ri / d x_r = out_ri (omega_i - x_r), so for an upstream gradient dout [rows][m]
+ * dx_r = sum_i dout_ri out_ri (omega_i - x_r). */
+void la_oracle_favor_features_backward(int64_t rows, int64_t d, int64_t m, const double* x,
+                                       const double* omega, const double* dout, double* dx) {
+    const double c = 1.0 / sqrt((double)m);
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* xr = x + r * d;
+        double nrm = 0.0;
+        for (int64_t a = 0; a < d; ++a) nrm += xr[a] * xr[a];
+        for (int64_t a = 0; a < d; ++a) dx[r * d + a] = 0.0;
+        for (int64_t i = 0; i < m; ++i) {
+            double u = 0.0;
+            for (int64_t a = 0; a < d; ++a) u += omega[i * d + a] * xr[a];
+            const double w = dout[r * m + i] * c * exp(u - 0.5 * nrm);
+            for (int64_t a = 0; a < d; ++a) dx[r * d + a] += w * (omega[i * d + a] - xr[a]);
+        }
+    }
+}

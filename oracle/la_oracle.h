@@ -110,6 +110,17 @@ void la_oracle_forward_features(int64_t BH, int64_t N, int64_t m, int64_t dv, in
                                 const double* fq, const double* fk, const double* v, double* o,
                                 double* den_out, double* S_out, double* z_out);
 
+/* Gradients of L = sum(dout * o) for la_oracle_forward_features: dfq, dfk [BH][N][m],
+ * dv [BH][N][dv] (chain rule: G = dout / den, g = -G . o, dfq_i = S_i G_i + g_i z_i,
+ * dfk_j = R_j v_j + r_j, dv_j = R_j^T fk_j with R, r summed over the rows reading key j). */
+void la_oracle_backward_features(int64_t BH, int64_t N, int64_t m, int64_t dv, int causal,
+                                 const double* fq, const double* fk, const double* v,
+                                 const double* dout, double* dfq, double* dfk, double* dvo);
+
+/* Gradient through la_oracle_favor_features: dx_r = sum_i dout_ri out_ri (omega_i - x_r). */
+void la_oracle_favor_features_backward(int64_t rows, int64_t d, int64_t m, const double* x,
+                                       const double* omega, const double* dout, double* dx);
+
 /* Number of OpenMP threads the oracle's parallel loops use (0 = runtime default). */
 void la_oracle_set_threads(int n);
 int la_oracle_get_threads(void);

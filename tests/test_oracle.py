@@ -471,3 +471,60 @@ def test_thread_count_does_not_change_results(oracle):
     oracle.set_threads(0)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+
+
+# ---- backward on given features, and through the FAVOR+ feature map --------------------
+def _np_features_forward(fq, fk, v, causal):
+    """The explicit n x n weights form on given features (numpy)."""
+    A = fq @ fk.T
+    if causal:
+        A = A * np.tril(np.ones(A.shape))
+    return (A @ v) / A.sum(-1, keepdims=True)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_features_finite_differences(oracle, causal):
+    """m != dv: central differences of sum(dout * O) of the explicit-weights form."""
+    rng = np.random.default_rng(120 + causal)
+    n, m, dv, h = 9, 6, 4, 1e-6
+    fq, fk = rng.uniform(0.2, 2.0, (n, m)), rng.uniform(0.2, 2.0, (n, m))
+    v, do = rng.standard_normal((n, dv)), rng.standard_normal((n, dv))
+    args = [fq, fk, v]
+    got = oracle.backward_features(fq, fk, v, do, causal)
+    for which, g in enumerate(got):
+        fd = np.zeros_like(args[which])
+        for idx in np.ndindex(*fd.shape):
+            plus = [a.copy() for a in args]
+            minus = [a.copy() for a in args]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            fd[idx] = ((_np_features_forward(*plus, causal) - _np_features_forward(*minus, causal)) * do).sum() / (2 * h)
+        assert rel(g, fd) < 1e-7, which
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_features_chain_to_elu_backward(oracle, causal):
+    """With elu+1 features, dfq phi'(q), dfk phi'(k) and dv are the oracle's elementwise-map
+    backward (itself pinned by finite differences above)."""
+    q, k, v, do = rand((2, 15, 5), 130), rand((2, 15, 5), 131), rand((2, 15, 5), 132), rand((2, 15, 5), 133)
+    dfq, dfk, dv = oracle.backward_features(np_phi(q), np_phi(k), v, do, causal)
+    dphi = lambda x: np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
+    ref = (oracle.backward_causal if causal else oracle.backward_noncausal)(q, k, v, do)
+    for got, r in zip((dfq * dphi(q), dfk * dphi(k), dv), ref):
+        assert rel(got, r) < 1e-12
+
+
+def test_favor_features_backward_finite_differences(oracle):
+    rng = np.random.default_rng(140)
+    rows, d, m, h = 5, 4, 7, 1e-6
+    x = rng.standard_normal((rows, d)) * 0.7
+    om = rng.standard_normal((m, d))
+    dF = rng.standard_normal((rows, m))
+    got = oracle.favor_features_backward(x, om, dF)
+    fd = np.zeros_like(x)
+    for idx in np.ndindex(*x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += h
+        xm[idx] -= h
+        fd[idx] = ((oracle.favor_features(xp, om) - oracle.favor_features(xm, om)) * dF).sum() / (2 * h)
+    assert rel(got, fd) < 1e-7
