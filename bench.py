@@ -335,7 +335,32 @@ def bench_calls(args, la, inp, torch, mid_sets):
 
     calls["mid_favor_m128_causal_fwd"] = bench_call("favor_m2", favor_fwd_m2, 100, 400, w.B * w.N,
                                                     4 * unit_bytes(w.B, w.H, w.N, w.d), la, torch, nsets=nsets)
-    del fsets, fq, fk, o, wsf
+    del fq, fk, wsf
+
+    # A FAVOR+ training step (m = d): features of q and k, the causal forward on them, its
+    # backward on the features, and the gradient through the feature map for q and k.
+    # Algorithmic bytes: q, k, v, dout read and o, dq, dk, dv written (8 units).
+    fq, fk = torch.empty_like(q0), torch.empty_like(q0)
+    gfe = tuple(torch.empty_like(q0) for _ in range(3))
+    dq, dk = torch.empty_like(q0), torch.empty_like(q0)
+    dos = [inp.normal((w.B, w.H, w.N, w.d), inp.generator(50 + s, "cuda"), w.dtype, 1.0, "cuda") for s in range(nsets)]
+    wsf = torch.empty(la.workspace_size(la.LA_OP_FWD_CAUSAL, w.B, w.H, w.N, w.d, w.dtype), dtype=torch.uint8,
+                      device="cuda")
+    wsb = torch.empty(la.workspace_size(la.LA_OP_BWD_CAUSAL, w.B, w.H, w.N, w.d, w.dtype), dtype=torch.uint8,
+                      device="cuda")
+
+    def favor_step(i):
+        q, k, v = fsets[i]
+        la.favor_features(q, om, out=fq)
+        la.favor_features(k, om, out=fk)
+        la.la_forward_causal_features(fq, fk, v, out=o, workspace=wsf)
+        la.la_backward_causal_features(fq, fk, v, dos[i], out=gfe, workspace=wsb)
+        la.favor_features_backward(q, om, fq, gfe[0], out=dq)
+        la.favor_features_backward(k, om, fk, gfe[1], out=dk)
+
+    calls["mid_favor_causal_fwd_bwd"] = bench_call("favor_step", favor_step, 100, 400, w.B * w.N,
+                                                   8 * unit_bytes(w.B, w.H, w.N, w.d), la, torch, nsets=nsets)
+    del fsets, fq, fk, o, wsf, wsb, gfe, dq, dk, dos
 
     w = inp.LONG
     q, k, v, do = inp.workload_inputs(w, seed=0, device="cuda", with_dout=True)
@@ -503,6 +528,17 @@ def call_oracles(args, inp, torch):
     record("mid_favor_causal_fwd",
            lambda: oracle.forward_features(oracle.favor_features(fq, om), oracle.favor_features(fk, om), fv, True),
            hs * w.N, w.H, hs, f"FAVOR+ features + causal forward of {hs} Mid heads")
+    fdo = f64(inp.normal((1, hs, w.N, w.d), inp.generator(94), torch.float32, 1.0))
+
+    def favor_train():
+        rfq, rfk = oracle.favor_features(fq, om), oracle.favor_features(fk, om)
+        oracle.forward_features(rfq, rfk, fv, True)
+        gq, gk, _ = oracle.backward_features(rfq, rfk, fv, fdo, True)
+        oracle.favor_features_backward(fq, om, gq)
+        oracle.favor_features_backward(fk, om, gk)
+
+    record("mid_favor_causal_fwd_bwd", favor_train, hs * w.N, w.H, hs,
+           f"FAVOR+ features, causal forward and backward, feature-map backward of {hs} Mid heads")
     om2 = f64(inp.favor_omega(w.d, seed=0, m=2 * w.d))
     record("mid_favor_m128_causal_fwd",
            lambda: oracle.forward_features(oracle.favor_features(fq, om2), oracle.favor_features(fk, om2), fv, True),

@@ -233,6 +233,29 @@ la_status la_decode_steps_features(float* S, float* z, const void* fq, const voi
                                    void* o, int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t d,
                                    la_dtype dt, void* stream);
 
+/* Backward on given features (m = d): the gradients dfq, dfk, dv of L = sum(dO * O) for
+ * la_forward_causal_features / la_forward_noncausal_features (the same chain rule as
+ * la_backward_causal with phi the identity: G = dO / den, g = -G . O, dfq_i = S_i G_i +
+ * g_i z_i, dfk_j = R_j v_j + r_j, dv_j = R_j^T fk_j).  Layouts, workspaces
+ * (la_workspace_size of LA_OP_BWD_CAUSAL / LA_OP_BWD_NONCAUSAL) and errors as those
+ * calls; no saved state or start state.  Features must be positive (as in the forward). */
+la_status la_backward_causal_features(const void* fq, const void* fk, const void* v, const void* dout,
+                                      void* dfq, void* dfk, void* dv, int64_t B, int64_t H, int64_t N,
+                                      int64_t d, la_dtype dt, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+la_status la_backward_noncausal_features(const void* fq, const void* fk, const void* v, const void* dout,
+                                         void* dfq, void* dfk, void* dv, int64_t B, int64_t H, int64_t N,
+                                         int64_t d, la_dtype dt, void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
+/* The gradient through la_favor_features (m = d): F_i = exp(omega_i . x - |x|^2 / 2) has
+ * dF_i / dx = F_i (omega_i - x), so for features F [rows][d] of x [rows][d] (the forward's
+ * output, passed back in) and their upstream gradient dF [rows][d]:
+ *   dx = omega^T (dF * F) - x sum_i (dF * F)_i   per row.
+ * x, F, dF, dx in dtype dt; omega [d][d] fp32 as in the forward. */
+la_status la_favor_features_backward(const void* x, const float* omega, const void* F, const void* dF,
+                                     void* dx, int64_t rows, int64_t d, la_dtype dt, void* stream);
+
 /* ---- More random features than d: m = KF d, KF = m / d feature blocks --------------------
  * The Performer section of the same page draws m random directions, and m may exceed d
  * (the estimate's variance falls as 1/m).  Features come in blocks of d: block j holds

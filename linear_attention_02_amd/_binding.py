@@ -25,7 +25,8 @@ EXPORTS = ("la_workspace_size", "la_saved_state_size", "la_forward_noncausal", "
            "la_forward_causal_features", "la_forward_noncausal_features", "la_decode_steps_features",
            "la_backward_causal_state", "la_forward_causal_grouped", "la_features_workspace_size",
            "la_favor_features_blocks", "la_forward_causal_features_blocks", "la_forward_noncausal_features_blocks",
-           "la_decode_steps_features_blocks", "la_status_string", "la_last_error_message", "la_version",
+           "la_decode_steps_features_blocks", "la_backward_causal_features", "la_backward_noncausal_features",
+           "la_favor_features_backward", "la_status_string", "la_last_error_message", "la_version",
            "la_profile_enable", "la_profile_count", "la_profile_entry", "la_debug_set_wait_limit",
            "la_debug_wait_limit")
 
@@ -71,6 +72,12 @@ def load_library(path: str | None = None):
     lib.la_forward_noncausal_features_blocks.argtypes = [vp] * 5 + [i64, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_decode_steps_features_blocks.restype = i32
     lib.la_decode_steps_features_blocks.argtypes = [vp] * 6 + [i64, i64, i64, i64, i64, i64, i32, vp, sz, vp]
+    for name in ("la_backward_causal_features", "la_backward_noncausal_features"):
+        f = getattr(lib, name)
+        f.restype = i32
+        f.argtypes = [vp] * 7 + [i64, i64, i64, i64, i32, vp, sz, vp]
+    lib.la_favor_features_backward.restype = i32
+    lib.la_favor_features_backward.argtypes = [vp] * 5 + [i64, i64, i32, vp]
     lib.la_forward_causal_grouped.restype = i32
     lib.la_forward_causal_grouped.argtypes = [vp] * 9 + [i64, i64, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.la_backward_causal_state.restype = i32
@@ -506,6 +513,63 @@ def la_decode_steps_features_blocks(S, z, fq, fk, v, *, out=None, workspace=None
                                                           Hkv, T, d, m, _dtype_code(fq.dtype), _ptr(ws), nbytes,
                                                           _stream(fq.device)))
     return o
+
+
+def la_backward_causal_features(fq, fk, v, dout, *, out=None, workspace=None, causal=True):
+    """Gradients (dfq, dfk, dv) of sum(dout * O) for the forward on given features fq, fk [B, H, N, d]."""
+    B, H, N, d = _check_seq(fq, fk, v)
+    if dout.shape != v.shape or dout.dtype != v.dtype or not dout.is_contiguous():
+        raise ValueError("dout must match v")
+    g = tuple(torch.empty_like(t) for t in (fq, fk, v)) if out is None else out
+    op = LA_OP_BWD_CAUSAL if causal else LA_OP_BWD_NONCAUSAL
+    ws = _workspace(op, B, H, N, d, fq.dtype, fq.device, 0, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    fn = load_library().la_backward_causal_features if causal else load_library().la_backward_noncausal_features
+    _check(fn(_ptr(fq), _ptr(fk), _ptr(v), _ptr(dout), _ptr(g[0]), _ptr(g[1]), _ptr(g[2]), B, H, N, d,
+              _dtype_code(fq.dtype), _ptr(ws), nbytes, _stream(fq.device)))
+    return g
+
+
+def la_backward_noncausal_features(fq, fk, v, dout, *, out=None, workspace=None):
+    return la_backward_causal_features(fq, fk, v, dout, out=out, workspace=workspace, causal=False)
+
+
+def favor_features_backward(x, omega, F, dF, *, out=None):
+    """dx = omega^T (dF * F) - x sum(dF * F) per row: the gradient through favor_features(x, omega) = F."""
+    d = x.shape[-1]
+    if omega.shape != (d, d) or omega.dtype != torch.float32 or not omega.is_contiguous():
+        raise ValueError("omega must be a contiguous [d, d] fp32 tensor")
+    for t in (x, F, dF):
+        if t.shape != x.shape or t.dtype != x.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("x, F and dF must be contiguous HIP tensors of one shape and dtype")
+    dx = torch.empty_like(x) if out is None else out
+    rows = x.numel() // d if d else 0
+    _check(load_library().la_favor_features_backward(_ptr(x), _ptr(omega), _ptr(F), _ptr(dF), _ptr(dx), rows, d,
+                                                     _dtype_code(x.dtype), _stream(x.device)))
+    return dx
+
+
+class _FavorAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, omega, causal):
+        fq, fk = favor_features(q, omega), favor_features(k, omega)
+        o = la_forward_causal_features(fq, fk, v) if causal else la_forward_noncausal_features(fq, fk, v)
+        ctx.save_for_backward(q, k, v, omega, fq, fk)
+        ctx.causal = causal
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, omega, fq, fk = ctx.saved_tensors
+        dfq, dfk, dv = la_backward_causal_features(fq, fk, v, do.contiguous(), causal=ctx.causal)
+        return favor_features_backward(q, omega, fq, dfq), favor_features_backward(k, omega, fk, dfk), dv, None, None
+
+
+def favor_attention(q, k, v, omega, causal=True):
+    """Performer attention with FAVOR+ features (m = d) as an autograd op: O of linear attention on
+    favor_features(q, omega), favor_features(k, omega); q, k pre-normalized by the caller.
+    Gradients flow to q, k and v through the library's kernels."""
+    return _FavorAttention.apply(q, k, v, omega, causal)
 
 
 def la_forward_causal_features(fq, fk, v, *, return_den=False, return_state=False, out=None, workspace=None,

@@ -619,6 +619,28 @@ la_status la_features_workspace_size(int causal, int64_t B, int64_t H, int64_t N
     return LA_OK;
 }
 
+la_status la_favor_features_backward(const void* x, const float* omega, const void* F, const void* dF, void* dx,
+                                     int64_t rows, int64_t d, la_dtype dt, void* stream) {
+    if (dt != LA_F32 && dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "dtype %d is not LA_F32 or LA_BF16", (int)dt);
+    if (d != 32 && d != 64 && d != 128) return fail(LA_ERR_UNSUPPORTED, "d = %lld; built for 32, 64 and 128", (long long)d);
+    if (rows < 0) return fail(LA_ERR_INVALID_ARGUMENT, "negative row count %lld", (long long)rows);
+    if (rows > ((int64_t)1 << 40)) return fail(LA_ERR_UNSUPPORTED, "rows = %lld exceeds 2^40", (long long)rows);
+    if (!omega) return fail(LA_ERR_INVALID_ARGUMENT, "omega must be non-NULL");
+    if (rows > 0 && (!x || !F || !dF || !dx)) return fail(LA_ERR_INVALID_ARGUMENT, "x, F, dF and dx must be non-NULL");
+    const size_t xb = (size_t)rows * d * elem_size(dt);
+    const Range in[] = {{"x", x, xb}, {"omega", omega, (size_t)d * d * sizeof(float)}, {"F", F, xb}, {"dF", dF, xb}};
+    const Range out_r[] = {{"dx", dx, xb}};
+    la_status st = check_ptrs(in, 4, out_r, 1);
+    if (st != LA_OK) return st;
+    if (rows == 0) return LA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed("favor_features_bwd", s, [&] {
+        return la::launch_favor_features_bwd(dt == LA_BF16 ? la::kBF16 : la::kF32, (int)d, x, omega, F, dF, dx, rows, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "favor_features_bwd launch");
+    return LA_OK;
+}
+
 la_status la_favor_features_blocks(const void* x, const float* omega, void* out, int64_t heads, int64_t N, int64_t d,
                                    int64_t m, la_dtype dt, void* stream) {
     la_status st = check_blocks(d, m);
@@ -666,7 +688,7 @@ static la_status backward_causal(const void* q, const void* k, const void* v, co
                                  void* dv, const void* saved_state, size_t saved_state_bytes, const float* S0,
                                  const float* z0, const float* dSN, const float* dzN, float* dS0, float* dz0,
                                  int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+                                 size_t workspace_bytes, void* stream, int feat = la::kFeatElu) {
     bool empty = false;
     la_status st = check_shape(B, H, N, d, chunk, dt, &empty);
     if (st != LA_OK) return st;
@@ -722,7 +744,7 @@ static la_status backward_causal(const void* q, const void* k, const void* v, co
                        })) != hipSuccess)
         return hip_fail(e, "state_split launch");
     if (saved_state == nullptr) {
-        if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
+        if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s, feat); })) != hipSuccess)
             return hip_fail(e, "seg_state launch");
         if (L.plan.scan &&
             (e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, BH, L.plan.nseg, 1, s, init); })) != hipSuccess)
@@ -734,21 +756,21 @@ static la_status backward_causal(const void* q, const void* k, const void* v, co
         if ((e = timed("bwd_fused", s, [&] {
                  return la::launch_bwd_fused(idt, (int)d, q, k, v, dout, dq, dk, dv, rowstat, rrec, rec, flags, epoch,
                                              g_wait_limit.load(std::memory_order_relaxed), BH, N, L.plan, s, init,
-                                             init_n, rinit, dS0, dz0);
+                                             init_n, rinit, dS0, dz0, feat);
              })) != hipSuccess)
             return hip_fail(e, "bwd_fused launch");
         return LA_OK;
     }
-    if ((e = timed("bwd_prefix", s, [&] { return la::launch_bwd_prefix(idt, (int)d, q, k, v, dout, dq, rowstat, rrec, rec, BH, N, L.plan, s, init, init_n); })) !=
+    if ((e = timed("bwd_prefix", s, [&] { return la::launch_bwd_prefix(idt, (int)d, q, k, v, dout, dq, rowstat, rrec, rec, BH, N, L.plan, s, init, init_n, feat); })) !=
         hipSuccess)
         return hip_fail(e, "bwd_prefix launch");
     if (!la::prefix_forms_records((int)d) &&
-        (e = timed("rseg", s, [&] { return la::launch_rseg(idt, (int)d, q, dout, rowstat, rrec, BH, N, L.plan, s); })) !=
+        (e = timed("rseg", s, [&] { return la::launch_rseg(idt, (int)d, q, dout, rowstat, rrec, BH, N, L.plan, s, feat); })) !=
             hipSuccess)
         return hip_fail(e, "rseg launch");
     if (L.plan.scan && (e = timed("rscan", s, [&] { return la::launch_scan((int)d, rrec, BH, L.plan.nseg, -1, s, rinit); })) != hipSuccess)
         return hip_fail(e, "rscan launch");
-    if ((e = timed("bwd_suffix", s, [&] { return la::launch_bwd_suffix(idt, (int)d, q, k, v, dout, dk, dv, rowstat, rrec, BH, N, L.plan, s, rinit, dS0, dz0); })) !=
+    if ((e = timed("bwd_suffix", s, [&] { return la::launch_bwd_suffix(idt, (int)d, q, k, v, dout, dk, dv, rowstat, rrec, BH, N, L.plan, s, rinit, dS0, dz0, feat); })) !=
         hipSuccess)
         return hip_fail(e, "bwd_suffix launch");
     return LA_OK;
@@ -770,10 +792,10 @@ la_status la_backward_causal_state(const void* q, const void* k, const void* v, 
                            dt, workspace, workspace_bytes, stream);
 }
 
-la_status la_backward_noncausal(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
-                                void* dv, const void* saved_state, size_t saved_state_bytes, int64_t B, int64_t H,
-                                int64_t N, int64_t d, la_dtype dt, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+static la_status backward_noncausal(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+                                    void* dv, const void* saved_state, size_t saved_state_bytes, int64_t B, int64_t H,
+                                    int64_t N, int64_t d, la_dtype dt, void* workspace, size_t workspace_bytes,
+                                    void* stream, int feat) {
     bool empty = false;
     la_status st = check_shape(B, H, N, d, 0, dt, &empty);
     if (st != LA_OK) return st;
@@ -808,22 +830,44 @@ la_status la_backward_noncausal(const void* q, const void* k, const void* v, con
     const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
     hipError_t e;
     if (saved_state == nullptr) {
-        if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s); })) != hipSuccess)
+        if ((e = timed("seg_state", s, [&] { return la::launch_seg_state(idt, (int)d, k, v, rec, BH, N, L.plan, s, feat); })) != hipSuccess)
             return hip_fail(e, "seg_state launch");
         if ((e = timed("total", s, [&] { return la::launch_total((int)d, rec, total, BH, L.plan.nseg, s); })) != hipSuccess)
             return hip_fail(e, "total launch");
     }
     if ((e = timed("ncbwd_q", s, [&] {
-             return la::launch_ncbwd_q(idt, (int)d, q, dout, dq, total, 1, rrec, BH, N, L.plan, s);
+             return la::launch_ncbwd_q(idt, (int)d, q, dout, dq, total, 1, rrec, BH, N, L.plan, s, feat);
          })) != hipSuccess)
         return hip_fail(e, "ncbwd_q launch");
     if ((e = timed("total", s, [&] { return la::launch_total((int)d, rrec, rtotal, BH, L.plan.nseg, s); })) != hipSuccess)
         return hip_fail(e, "total launch");
     if ((e = timed("ncbwd_kv", s, [&] {
-             return la::launch_ncbwd_kv(idt, (int)d, k, v, dk, dv, rtotal, 1, BH, N, L.plan, s);
+             return la::launch_ncbwd_kv(idt, (int)d, k, v, dk, dv, rtotal, 1, BH, N, L.plan, s, feat);
          })) != hipSuccess)
         return hip_fail(e, "ncbwd_kv launch");
     return LA_OK;
+}
+
+la_status la_backward_noncausal(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+                                void* dv, const void* saved_state, size_t saved_state_bytes, int64_t B, int64_t H,
+                                int64_t N, int64_t d, la_dtype dt, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    return backward_noncausal(q, k, v, dout, dq, dk, dv, saved_state, saved_state_bytes, B, H, N, d, dt, workspace,
+                              workspace_bytes, stream, la::kFeatElu);
+}
+
+la_status la_backward_causal_features(const void* fq, const void* fk, const void* v, const void* dout, void* dfq,
+                                      void* dfk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, la_dtype dt,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+    return backward_causal(fq, fk, v, dout, dfq, dfk, dv, nullptr, 0, nullptr, nullptr, nullptr, nullptr, nullptr,
+                           nullptr, B, H, N, d, 0, dt, workspace, workspace_bytes, stream, la::kFeatGiven);
+}
+
+la_status la_backward_noncausal_features(const void* fq, const void* fk, const void* v, const void* dout, void* dfq,
+                                         void* dfk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, la_dtype dt,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+    return backward_noncausal(fq, fk, v, dout, dfq, dfk, dv, nullptr, 0, B, H, N, d, dt, workspace, workspace_bytes,
+                              stream, la::kFeatGiven);
 }
 
 la_status la_decode_step(float* S, float* z, const void* q, const void* k, const void* v, void* o, int64_t B,

@@ -71,7 +71,9 @@ struct BwdPrefixForms {
 // left to the sweep, and rseg forms the record from the saved den and g).
 // init / init_n (nullable): the forward's start state in split form and its token
 // count, one record and one count per head (the carried state starts from them).
-template <typename T, int D, bool kCoherentRecord, bool kRecord = true, bool kState = false>
+// FM: the feature map (FeatGiven: phi is the identity, E = phi and the rank-1 terms of the
+// split vanish: no q_sum, P or n anywhere, and dphi = 1).
+template <typename T, int D, bool kCoherentRecord, bool kRecord = true, bool kState = false, class FM = FeatElu>
 __device__ __forceinline__ void bwd_prefix_body(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dq, float2* __restrict__ rowstat, float* __restrict__ rrec, const float* __restrict__ rec, int N,
@@ -139,7 +141,7 @@ __device__ __forceinline__ void bwd_prefix_body(
         publish_state<T, D>(stS, tSt, lane, w);
         store_vec<D>(s_z, vz, lane, w);
         store_vec<D>(s_p, vp, lane, w);
-        stage_elu<T, D>(ck, tE, tid);
+        stage_elu<T, D, FM>(ck, tE, tid);
         stage_raw<T, D>(cv, tV, tid);
         // Loads past the segment are aimed at row N: out of the buffer's range,
         // they return zeros without touching memory, and the loop stays branch free.
@@ -152,7 +154,7 @@ __device__ __forceinline__ void bwd_prefix_body(
 
         // phi(Q) of this wave's rows: staged (for the R update) and read back in
         // accumulator order where it is used (short register lifetimes).
-        stage_phi<T, D, true>(cq, tQ, tid, 16 * tt);
+        stage_phi<T, D, true, FM>(cq, tQ, tid, 16 * tt);
         cq.load(bq, nxt < N ? nxt + 16 * tt_next : N, tid);
         wave_lds_sync();
         auto read_y = [&](float* y) {
@@ -183,12 +185,12 @@ __device__ __forceinline__ void bwd_prefix_body(
 #pragma unroll
             for (int k0 = 0; k0 < D; k0 += KS) {
                 const typename M::frag yq = M::vals_op(y, k0);
-                accq = M::mma(one, yq, accq);
+                if constexpr (FM::kSplit) accq = M::mma(one, yq, accq);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     if (j <= tt) accB[j] = M::mma(M::ld_acc(tE, 16 * j, k0, lane), yq, accB[j]);
             }
-            qs_t = accq[0];
+            qs_t = FM::kSplit ? accq[0] : 0.f;  // no rank-1 parts when unsplit
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 if (j < tt) {
@@ -218,9 +220,11 @@ __device__ __forceinline__ void bwd_prefix_body(
 #pragma unroll
             for (int m = 0; m < DT; ++m) {
                 store4(&tG.at(tl, 16 * m + 4 * g), f32x4{gy[4 * m], gy[4 * m + 1], gy[4 * m + 2], gy[4 * m + 3]});
-                const f32x4 pv = lds4(&s_p[16 * m + 4 * g]);
+                if constexpr (FM::kSplit) {
+                    const f32x4 pv = lds4(&s_p[16 * m + 4 * g]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) gp += gy[4 * m + e] * pv[e];
+                    for (int e = 0; e < 4; ++e) gp += gy[4 * m + e] * pv[e];
+                }
             }
             cdo.load(bdo, nxt < N ? nxt + 16 * tt_next : N, lane);
 #pragma unroll
@@ -296,14 +300,15 @@ __device__ __forceinline__ void bwd_prefix_body(
             }
         }
         {
-            const float bracket = rowdA + gp + gt * n;
+            const float bracket = FM::kSplit ? rowdA + gp + gt * n : 0.f;
 #pragma unroll
             for (int m = 0; m < DT; ++m) {
                 const int f0 = 16 * m + 4 * g;
                 const f32x4 zv = lds4(&s_z[f0]);
                 f32x4 x;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = (accQ[m][e] + zv[e] * gt + bracket) * fminf(y[4 * m + e], 1.f);
+                for (int e = 0; e < 4; ++e)
+                    x[e] = (accQ[m][e] + zv[e] * gt + bracket) * FM::dphi_at_phi(y[4 * m + e]);
                 gstore4<T>(bdq, (uint32_t)(tok * D + f0), x);
             }
         }
@@ -327,7 +332,7 @@ __device__ __forceinline__ void bwd_prefix_body(
     }
 }
 
-template <typename T, int D, bool kState = false>
+template <typename T, int D, bool kState = false, class FM = FeatElu>
 __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dq, float2* __restrict__ rowstat, float* __restrict__ rrec, const float* __restrict__ rec, int N,
@@ -336,8 +341,9 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
     // Later segments sum more records: they are dispatched first, since a CU's
     // older workgroup issues ahead of its younger one.
     const int seg = nseg - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
-    bwd_prefix_body<T, D, false, BwdPrefixForms<D>::kRecord, kState>(q, k, v, dout, dq, rowstat, rrec, rec, N, cps,
-                                                                     nseg, prefixed, seg, bh, lds, init, init_n);
+    bwd_prefix_body<T, D, false, BwdPrefixForms<D>::kRecord, kState, FM>(q, k, v, dout, dq, rowstat, rrec, rec, N,
+                                                                         cps, nseg, prefixed, seg, bh, lds, init,
+                                                                         init_n);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -346,7 +352,7 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
 // the per-row statistics the prefix sweep saved: the same operands, chunk order
 // and products as the prefix sweep's own update, so the record is bitwise the
 // same.  Used where the prefix sweep does not form the record (d = 128).
-template <typename T, int D>
+template <typename T, int D, class FM = FeatElu>
 __global__ __launch_bounds__(kBlock, 2) void rseg_kernel(const T* __restrict__ q, const T* __restrict__ dout,
                                                       const float2* __restrict__ rowstat, float* __restrict__ rrec,
                                                       int N, int cps, int nseg, int BH) {
@@ -380,7 +386,7 @@ __global__ __launch_bounds__(kBlock, 2) void rseg_kernel(const T* __restrict__ q
     int buf = 0;
     for (int c0 = tok_begin; c0 < tok_end; c0 += kC, buf ^= 1) {
         const Tile<T, kC, D> tQ{sm_q[buf]}, tG{sm_g[buf]};
-        stage_phi<T, D>(cq, tQ, tid);
+        stage_phi<T, D, false, FM>(cq, tQ, tid);
 #pragma unroll
         for (int i = 0; i < CR::NV; ++i) {
             const int t = CR::row(i, tid);
@@ -417,7 +423,7 @@ __global__ __launch_bounds__(kBlock, 2) void rseg_kernel(const T* __restrict__ q
 // the final state, which every suffix sum starts from.  dS0, dz0 (nullable): the
 // first segment writes the suffix state at the first token there, the gradient of
 // the start state (S [a][b], z [a] layouts).
-template <typename T, int D, bool kCoherentRecords, bool kState = false>
+template <typename T, int D, bool kCoherentRecords, bool kState = false, class FM = FeatElu>
 __device__ __forceinline__ void bwd_suffix_body(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dk, T* __restrict__ dv, const float2* __restrict__ rowstat, const float* __restrict__ rrec, int N,
@@ -498,7 +504,7 @@ __device__ __forceinline__ void bwd_suffix_body(
         const Tile<T, D, D> tRt{sm_rt[buf]};
         publish_state<T, D>(stR, tRt, lane, w);
         store_vec<D>(s_r[buf], vr, lane, w);
-        stage_phi<T, D>(cq, tQ, tid);
+        stage_phi<T, D, false, FM>(cq, tQ, tid);
         // G = round(dO / den) with the den saved by the prefix sweep (bitwise the same G).
 #pragma unroll
         for (int i = 0; i < CR::NV; ++i) {
@@ -516,9 +522,14 @@ __device__ __forceinline__ void bwd_suffix_body(
 #pragma unroll
         for (int i = 0; i < NY; ++i) {
             const float x = kr.get(i);
-            const float c = expc_f(x);
-            ke[i] = to_f32(from_f32<T>(fmaxf(x, c - 1.f)));
-            dphik[i] = c;
+            if constexpr (FM::kSplit) {
+                const float c = expc_f(x);
+                ke[i] = to_f32(from_f32<T>(fmaxf(x, c - 1.f)));
+                dphik[i] = c;
+            } else {
+                ke[i] = to_f32(from_f32<T>(FM::e(x)));
+                dphik[i] = 1.f;
+            }
         }
         const RowAcc<T, D> vcur = vrow;
         load_chunk(ci > 0 ? c0 - kC : N, (w + it + 1) & 3);  // past the head: zeros, no memory traffic
@@ -547,7 +558,7 @@ __device__ __forceinline__ void bwd_suffix_body(
                         const typename M::frag xq = M::ld_acc(tQ, 16 * i, k0, lane);
                         acc_d = M::mma(M::ld_acc(tG, 16 * i, k0, lane), yv[k0 / KS], acc_d);
                         acc_b = M::mma(xq, ye[k0 / KS], acc_b);
-                        acc_q = M::mma(xq, one, acc_q);
+                        if constexpr (FM::kSplit) acc_q = M::mma(xq, one, acc_q);
                     }
                     const f32x4 gt4 = lds4(&s_g[buf][16 * i + 4 * g]);
                     if (i > st) {
@@ -596,7 +607,7 @@ __device__ __forceinline__ void bwd_suffix_body(
                     const typename M::frag xr = M::ld_acc(tRt, 16 * m, k0, lane);
                     acck[m] = M::mma(M::ld_tr_acc(tRt, k0, 16 * m, lane), yv, acck[m]);
                     accv[m] = M::mma(xr, ye, accv[m]);
-                    accv[m] = M::mma(xr, one, accv[m]);
+                    if constexpr (FM::kSplit) accv[m] = M::mma(xr, one, accv[m]);  // w = sum_a R[a][.]
                 }
             }
         }
@@ -634,7 +645,7 @@ __device__ __forceinline__ void bwd_suffix_body(
     }
 }
 
-template <typename T, int D, bool kState = false>
+template <typename T, int D, bool kState = false, class FM = FeatElu>
 __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dk, T* __restrict__ dv, const float2* __restrict__ rowstat, const float* __restrict__ rrec, int N,
@@ -642,8 +653,8 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_ke
     float* __restrict__ dz0) {
     __shared__ __attribute__((aligned(16))) char lds[BwdSuffixLds<T, D>::kBytes];
     const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
-    bwd_suffix_body<T, D, false, kState>(q, k, v, dout, dk, dv, rowstat, rrec, N, cps, nseg, prefixed, seg, bh, false,
-                                         lds, rinit, dS0, dz0);
+    bwd_suffix_body<T, D, false, kState, FM>(q, k, v, dout, dk, dv, rowstat, rrec, N, cps, nseg, prefixed, seg, bh,
+                                             false, lds, rinit, dS0, dz0);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -655,7 +666,7 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_ke
 // starts from their records.  The suffix sweep's cold start (records, first
 // chunk) overlaps other workgroups' prefix sweeps instead of following a kernel
 // boundary.  den and g per row stay with the workgroup that wrote them.
-template <typename T, int D, bool kState = false>
+template <typename T, int D, bool kState = false, class FM = FeatElu>
 __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_fused_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv, float2* __restrict__ rowstat,
@@ -666,8 +677,8 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_fused_ker
     constexpr size_t kP = BwdPrefixLds<T, D>::kBytes, kS = BwdSuffixLds<T, D>::kBytes;
     __shared__ __attribute__((aligned(16))) char lds[kP > kS ? kP : kS];
     const int seg = nseg - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
-    bwd_prefix_body<T, D, true, true, kState>(q, k, v, dout, dq, rowstat, rrec, rec, N, cps, nseg, 0, seg, bh, lds,
-                                              init, init_n);
+    bwd_prefix_body<T, D, true, true, kState, FM>(q, k, v, dout, dq, rowstat, rrec, rec, N, cps, nseg, 0, seg, bh, lds,
+                                                  init, init_n);
     // Every wave's record stores (and den, g rows) are complete before the flag.
     wait_all_memory();
     __syncthreads();
@@ -677,17 +688,21 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_fused_ker
     if ((threadIdx.x & 63) == 0)
         for (int j = seg + 1; j < nseg; ++j) ok = ok && await_flag(&hf[j], epoch, wait_limit);
     ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
-    bwd_suffix_body<T, D, true, kState>(q, k, v, dout, dk, dv, rowstat, rrec, N, cps, nseg, 0, seg, bh, !ok, lds,
-                                        rinit, dS0, dz0);
+    bwd_suffix_body<T, D, true, kState, FM>(q, k, v, dout, dk, dv, rowstat, rrec, N, cps, nseg, 0, seg, bh, !ok, lds,
+                                            rinit, dS0, dz0);
 }
 
 // ---------------------------------------------------------------------------------------
 hipError_t launch_bwd_prefix(int dt, int d, const void* q, const void* k, const void* v, const void* dout, void* dq,
                              float* rowstat, float* rrec, const float* rec, int64_t BH, int64_t N, SegPlan p,
-                             hipStream_t s, const float* init, const float* init_n) {
+                             hipStream_t s, const float* init, const float* init_n, int feat) {
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_BWDP(TT, DD)                                                                                           \
-    if (init != nullptr || init_n != nullptr)                                                                     \
+    if (feat == kFeatGiven)                                                                                       \
+        hipLaunchKernelGGL((bwd_prefix_kernel<TT, DD, false, FeatGiven>), grid, dim3(kBlock), 0, s, (const TT*)q,  \
+                           (const TT*)k, (const TT*)v, (const TT*)dout, (TT*)dq, (float2*)rowstat, rrec, rec, (int)N,  \
+                           p.cps, p.nseg, (int)BH, (int)p.scan, nullptr, nullptr);                                   \
+    else if (init != nullptr || init_n != nullptr)                                                                \
         hipLaunchKernelGGL((bwd_prefix_kernel<TT, DD, true>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k, \
                            (const TT*)v, (const TT*)dout, (TT*)dq, (float2*)rowstat, rrec, rec, (int)N, p.cps, p.nseg, \
                            (int)BH, (int)p.scan, init, init_n);                                                      \
@@ -714,11 +729,15 @@ hipError_t launch_bwd_prefix(int dt, int d, const void* q, const void* k, const 
 }
 
 hipError_t launch_rseg(int dt, int d, const void* q, const void* dout, const float* rowstat, float* rrec, int64_t BH,
-                       int64_t N, SegPlan p, hipStream_t s) {
+                       int64_t N, SegPlan p, hipStream_t s, int feat) {
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_RSEG(TT, DD)                                                                                           \
-    hipLaunchKernelGGL((rseg_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)dout,           \
-                       (const float2*)rowstat, rrec, (int)N, p.cps, p.nseg, (int)BH)
+    if (feat == kFeatGiven)                                                                                       \
+        hipLaunchKernelGGL((rseg_kernel<TT, DD, FeatGiven>), grid, dim3(kBlock), 0, s, (const TT*)q,             \
+                           (const TT*)dout, (const float2*)rowstat, rrec, (int)N, p.cps, p.nseg, (int)BH);          \
+    else                                                                                                         \
+        hipLaunchKernelGGL((rseg_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)dout,       \
+                           (const float2*)rowstat, rrec, (int)N, p.cps, p.nseg, (int)BH)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_RSEG(bf16, 32); break;
@@ -740,11 +759,17 @@ hipError_t launch_rseg(int dt, int d, const void* q, const void* dout, const flo
 hipError_t launch_bwd_fused(int dt, int d, const void* q, const void* k, const void* v, const void* dout, void* dq,
                             void* dk, void* dv, float* rowstat, float* rrec, const float* rec, unsigned long long* flags,
                             unsigned long long epoch, int wait_limit, int64_t BH, int64_t N, SegPlan p, hipStream_t s,
-                            const float* init, const float* init_n, const float* rinit, float* dS0, float* dz0) {
+                            const float* init, const float* init_n, const float* rinit, float* dS0, float* dz0,
+                            int feat) {
     const dim3 grid((unsigned)(p.nseg * BH));
     const bool state = init != nullptr || init_n != nullptr || rinit != nullptr || dS0 != nullptr || dz0 != nullptr;
 #define LA_BWDF(TT, DD)                                                                                           \
-    if (state)                                                                                                   \
+    if (feat == kFeatGiven)                                                                                       \
+        hipLaunchKernelGGL((bwd_fused_kernel<TT, DD, false, FeatGiven>), grid, dim3(kBlock), 0, s, (const TT*)q,   \
+                           (const TT*)k, (const TT*)v, (const TT*)dout, (TT*)dq, (TT*)dk, (TT*)dv, (float2*)rowstat, \
+                           rrec, rec, flags, epoch, wait_limit, (int)N, p.cps, p.nseg, (int)BH, nullptr, nullptr,  \
+                           nullptr, nullptr, nullptr);                                                              \
+    else if (state)                                                                                              \
         hipLaunchKernelGGL((bwd_fused_kernel<TT, DD, true>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k, \
                            (const TT*)v, (const TT*)dout, (TT*)dq, (TT*)dk, (TT*)dv, (float2*)rowstat, rrec, rec,  \
                            flags, epoch, wait_limit, (int)N, p.cps, p.nseg, (int)BH, init, init_n, rinit, dS0, dz0); \
@@ -773,10 +798,14 @@ hipError_t launch_bwd_fused(int dt, int d, const void* q, const void* k, const v
 
 hipError_t launch_bwd_suffix(int dt, int d, const void* q, const void* k, const void* v, const void* dout, void* dk,
                              void* dv, const float* rowstat, const float* rrec, int64_t BH, int64_t N, SegPlan p,
-                             hipStream_t s, const float* rinit, float* dS0, float* dz0) {
+                             hipStream_t s, const float* rinit, float* dS0, float* dz0, int feat) {
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_BWDS(TT, DD)                                                                                           \
-    if (rinit != nullptr || dS0 != nullptr || dz0 != nullptr)                                                     \
+    if (feat == kFeatGiven)                                                                                       \
+        hipLaunchKernelGGL((bwd_suffix_kernel<TT, DD, false, FeatGiven>), grid, dim3(kBlock), 0, s, (const TT*)q,  \
+                           (const TT*)k, (const TT*)v, (const TT*)dout, (TT*)dk, (TT*)dv, (const float2*)rowstat,   \
+                           rrec, (int)N, p.cps, p.nseg, (int)BH, (int)p.scan, nullptr, nullptr, nullptr);           \
+    else if (rinit != nullptr || dS0 != nullptr || dz0 != nullptr)                                                \
         hipLaunchKernelGGL((bwd_suffix_kernel<TT, DD, true>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k, \
                            (const TT*)v, (const TT*)dout, (TT*)dk, (TT*)dv, (const float2*)rowstat, rrec, (int)N,  \
                            p.cps, p.nseg, (int)BH, (int)p.scan, rinit, dS0, dz0);                                    \

@@ -165,9 +165,9 @@ struct TileDma {
     }
 };
 
-// phi(Q) row-major into LDS.
+// phi(Q) row-major into LDS (phi of the feature map FM).
 // (kWaveRows: the wavefront's rows go to tile rows row0 ..)
-template <typename T, int D, bool kWaveRows = false>
+template <typename T, int D, bool kWaveRows = false, class FM = FeatElu>
 __device__ __forceinline__ void stage_phi(const ChunkRegs<T, D, kWaveRows>& cq, const Tile<T, kC, D>& tQ, int tid,
                                           int row0 = 0) {
     using CR = ChunkRegs<T, D, kWaveRows>;
@@ -176,7 +176,7 @@ __device__ __forceinline__ void stage_phi(const ChunkRegs<T, D, kWaveRows>& cq, 
         uint4 packed;
         T* pk = reinterpret_cast<T*>(&packed);
 #pragma unroll
-        for (int e = 0; e < CR::EV; ++e) pk[e] = from_f32<T>(phi_f(cq.get(i, e)));
+        for (int e = 0; e < CR::EV; ++e) pk[e] = from_f32<T>(FM::phi(cq.get(i, e)));
         *reinterpret_cast<uint4*>(tQ.granule(row0 + CR::row(i, tid), CR::gran(i, tid))) = packed;
     }
 }

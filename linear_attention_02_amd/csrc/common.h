@@ -67,15 +67,18 @@ __device__ __forceinline__ float dphi_f(float x) { return expc_f(x); }
 //     where a split around 1 would cancel catastrophically), so they are carried
 //     unsplit: E(x) = x and every rank-1 term is dropped.
 // Either way E(0) = 0: the zero rows read past a sequence's end add nothing.
+// dphi_at_phi(p): phi'(x) from p = phi(x) (the backward's chain factor).
 struct FeatElu {
     static constexpr bool kSplit = true;
     __device__ __forceinline__ static float phi(float x) { return phi_f(x); }
     __device__ __forceinline__ static float e(float x) { return elu_f(x); }
+    __device__ __forceinline__ static float dphi_at_phi(float p) { return fminf(p, 1.f); }
 };
 struct FeatGiven {
     static constexpr bool kSplit = false;
     __device__ __forceinline__ static float phi(float x) { return x; }
     __device__ __forceinline__ static float e(float x) { return x; }
+    __device__ __forceinline__ static float dphi_at_phi(float) { return 1.f; }
 };
 
 // 1/x to within an ulp: hardware reciprocal refined by one Newton step.

@@ -148,6 +148,144 @@ hipError_t launch_favor_features(int dt, int d, const void* x, const float* omeg
 }
 
 // ---------------------------------------------------------------------------------------
+// favor_features_bwd: the gradient through the features.  F_i = exp(w_i.x - |x|^2/2)
+// has dF_i/dx = F_i (w_i - x), so for an upstream gradient dF of a row
+//   dx = Omega^T u - x sum_i u_i,  u = dF * F   (elementwise, from the saved F).
+// Omega^T u for 16 rows per wavefront is one MFMA contraction over the features i
+// against Omega staged in LDS.  bf16 rows: u of two bf16 values has 16 significant
+// bits, so u = u_hi + u_lo exactly in bf16, Omega is split the same way, and three
+// bf16 MFMAs (hi hi, hi lo, lo hi) give the product to about 2^-16 relative; fp32 rows
+// use the fp32 MFMA.  One workgroup takes CPB chunks of 64 rows.
+template <typename T, int D>
+__global__ __launch_bounds__(kBlock) void favor_features_bwd_kernel(const T* __restrict__ x,
+                                                                    const float* __restrict__ omega,
+                                                                    const T* __restrict__ F, const T* __restrict__ dF,
+                                                                    T* __restrict__ dx, int64_t rows) {
+    constexpr bool kBF = sizeof(T) == 2;
+    using M = Mma<T>;
+    constexpr int DT = D / 16;
+    constexpr int CPB = 4;
+    constexpr int TPR = D / 4;
+    constexpr int NI = kC * TPR / kBlock;
+    static_assert(NI >= 1 && kC * TPR % kBlock == 0 && TPR <= kWave, "rows must tile the workgroup");
+    typedef typename std::conditional<kBF, uint2, uint4>::type word;
+    __shared__ __attribute__((aligned(16))) T s_om[kBF ? 2 : 1][D * D];  // bf16: hi, lo; fp32: omega
+    __shared__ __attribute__((aligned(16))) T s_u[kBF ? 2 : 1][kC * D];  // bf16: u hi, lo; fp32: u
+    __shared__ float s_s[kC];
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
+
+    for (int i = tid; i < D * D / 4; i += kBlock) {
+        const int r = (4 * i) / D, c = (4 * i) % D;
+        const f32x4 om = reinterpret_cast<const f32x4*>(omega)[i];
+        if constexpr (kBF) {
+            f32x4 hi;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hi[e] = (float)(bf16)om[e];
+            store4(&Tile<T, D, D>{s_om[0]}.at(r, c), hi);
+            store4(&Tile<T, D, D>{s_om[kBF ? 1 : 0]}.at(r, c), om - hi);
+        } else {
+            store4(&Tile<T, D, D>{s_om[0]}.at(r, c), om);
+        }
+    }
+    const int64_t base = (int64_t)blockIdx.x * CPB * kC;
+    for (int cb = 0; cb < CPB; ++cb) {
+        const int64_t r0 = base + (int64_t)cb * kC;
+        if (r0 >= rows) break;
+        if (cb > 0) __syncthreads();  // every wave has read the previous chunk's u
+        // u = dF * F of this thread's groups of 4, split hi + lo, and the row sums of u.
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int i = tid + kBlock * j;
+            const int rr = (4 * i) / D, c = (4 * i) % D;
+            const int64_t row = r0 + rr;
+            word fw{}, gw{};
+            if (row < rows) {
+                fw = *reinterpret_cast<const word*>(F + row * D + c);
+                gw = *reinterpret_cast<const word*>(dF + row * D + c);
+            }
+            const T* fh = reinterpret_cast<const T*>(&fw);
+            const T* gh = reinterpret_cast<const T*>(&gw);
+            f32x4 u;
+            float su = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                u[e] = to_f32(fh[e]) * to_f32(gh[e]);
+                su += u[e];
+            }
+            if constexpr (kBF) {
+                f32x4 hi;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hi[e] = (float)(bf16)u[e];
+                store4(&Tile<T, kC, D>{s_u[0]}.at(rr, c), hi);
+                store4(&Tile<T, kC, D>{s_u[kBF ? 1 : 0]}.at(rr, c), u - hi);
+            } else {
+                store4(&Tile<T, kC, D>{s_u[0]}.at(rr, c), u);
+            }
+            su = sum_lanes<TPR>(su);
+            if (c == 0) s_s[rr] = su;
+        }
+        __syncthreads();  // u and its row sums staged (and omega, for the first chunk)
+        // acc[m]: [feature 16 m + 4 g + e][row 16 w + (lane & 15)] of Omega^T u.
+        f32x4 acc[DT];
+#pragma unroll
+        for (int m = 0; m < DT; ++m) acc[m] = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < D; k0 += M::KSTEP) {
+            const typename M::frag uh = M::ld(Tile<T, kC, D>{s_u[0]}, 16 * w, k0, lane);
+#pragma unroll
+            for (int m = 0; m < DT; ++m) {
+                const typename M::frag oh = M::ld_tr(Tile<T, D, D>{s_om[0]}, k0, 16 * m, lane);
+                acc[m] = M::mma(oh, uh, acc[m]);
+                if constexpr (kBF) {
+                    const typename M::frag ul = M::ld(Tile<T, kC, D>{s_u[kBF ? 1 : 0]}, 16 * w, k0, lane);
+                    acc[m] = M::mma(oh, ul, acc[m]);
+                    acc[m] = M::mma(M::ld_tr(Tile<T, D, D>{s_om[kBF ? 1 : 0]}, k0, 16 * m, lane), uh, acc[m]);
+                }
+            }
+        }
+        const int t = 16 * w + (lane & 15);
+        const int64_t row = r0 + t;
+        if (row < rows) {
+            const float su = s_s[t];
+#pragma unroll
+            for (int m = 0; m < DT; ++m) {
+                const int c = 16 * m + 4 * g;
+                f32x4 y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = acc[m][e] - su * to_f32(x[row * D + c + e]);
+                store4(dx + row * D + c, y);
+            }
+        }
+    }
+}
+
+hipError_t launch_favor_features_bwd(int dt, int d, const void* x, const float* omega, const void* F, const void* dF,
+                                     void* dx, int64_t rows, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    const dim3 grid((unsigned)((rows + 4 * kC - 1) / (4 * kC)));
+#define LA_FAVB(TT, DD)                                                                                       \
+    hipLaunchKernelGGL((favor_features_bwd_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)x, omega,     \
+                       (const TT*)F, (const TT*)dF, (TT*)dx, rows)
+    if (dt == kBF16) {
+        switch (d) {
+            case 32: LA_FAVB(bf16, 32); break;
+            case 64: LA_FAVB(bf16, 64); break;
+            case 128: LA_FAVB(bf16, 128); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (d) {
+            case 32: LA_FAVB(float, 32); break;
+            case 64: LA_FAVB(float, 64); break;
+            case 128: LA_FAVB(float, 128); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+#undef LA_FAVB
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
 // combine_blocks: attention over KF feature blocks of one head, each computed as its own
 // head (o_j = num_j / den_j, den_j), put together: num = sum_j num_j and den = sum_j den_j,
 // so o = sum_j den_j o_j / sum_j den_j.  ob [BH][KF][N][D] in T, db [BH][KF][N] fp32;

@@ -84,11 +84,11 @@ hipError_t launch_noncausal_fwd(int dt, int d, const void* q, void* o, const flo
 hipError_t launch_bwd_prefix(int dt, int d, const void* q, const void* k, const void* v,
                              const void* dout, void* dq, float* rowstat, float* rrec,
                              const float* rec, int64_t BH, int64_t N, SegPlan p, hipStream_t s,
-                             const float* init = nullptr, const float* init_n = nullptr);
+                             const float* init = nullptr, const float* init_n = nullptr, int feat = kFeatElu);
 // The backward's per-segment (R, r) records from q, dout and the saved per-row
 // statistics, for head dimensions whose prefix sweep does not form them (d > 64).
 hipError_t launch_rseg(int dt, int d, const void* q, const void* dout, const float* rowstat, float* rrec, int64_t BH,
-                       int64_t N, SegPlan p, hipStream_t s);
+                       int64_t N, SegPlan p, hipStream_t s, int feat = kFeatElu);
 constexpr bool prefix_forms_records(int d) { return d <= 64; }
 // Default bound on the polls of one wait between workgroups (each poll sleeps
 // about 128 cycles after a coherent load: tens of milliseconds at most).
@@ -100,20 +100,21 @@ hipError_t launch_bwd_fused(int dt, int d, const void* q, const void* k, const v
                             void* dk, void* dv, float* rowstat, float* rrec, const float* rec, unsigned long long* flags,
                             unsigned long long epoch, int wait_limit, int64_t BH, int64_t N, SegPlan p, hipStream_t s,
                             const float* init = nullptr, const float* init_n = nullptr, const float* rinit = nullptr,
-                            float* dS0 = nullptr, float* dz0 = nullptr);
+                            float* dS0 = nullptr, float* dz0 = nullptr, int feat = kFeatElu);
 hipError_t launch_bwd_suffix(int dt, int d, const void* q, const void* k, const void* v,
                              const void* dout, void* dk, void* dv, const float* rowstat,
                              const float* rrec, int64_t BH, int64_t N, SegPlan p, hipStream_t s,
-                             const float* rinit = nullptr, float* dS0 = nullptr, float* dz0 = nullptr);
+                             const float* rinit = nullptr, float* dS0 = nullptr, float* dz0 = nullptr,
+                             int feat = kFeatElu);
 
 // Non-causal backward.  ncbwd_q: dQ of every row from the head's key state (the
 // in-order sum of `ntotal` records per head at `total`) and each segment's
 // (R, r) record; ncbwd_kv: dK, dV of every key row from the in-order sum of
 // `ntotal` (R, r) records per head at `rtotal`.
 hipError_t launch_ncbwd_q(int dt, int d, const void* q, const void* dout, void* dq, const float* total, int ntotal,
-                          float* rrec, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
+                          float* rrec, int64_t BH, int64_t N, SegPlan p, hipStream_t s, int feat = kFeatElu);
 hipError_t launch_ncbwd_kv(int dt, int d, const void* k, const void* v, void* dk, void* dv, const float* rtotal,
-                           int ntotal, int64_t BH, int64_t N, SegPlan p, hipStream_t s);
+                           int ntotal, int64_t BH, int64_t N, SegPlan p, hipStream_t s, int feat = kFeatElu);
 
 // Zero-fill n floats with a kernel (no memset node, so the call can sit in a captured graph).
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
@@ -134,6 +135,10 @@ hipError_t launch_decode_steps(int dt, int d, float* S, float* z, const void* q,
 // for the d rows of omega [d][d] fp32 (m = d features; the constant 1/sqrt(m) is left out).
 hipError_t launch_favor_features(int dt, int d, const void* x, const float* omega, void* out, int64_t rows,
                                  hipStream_t s, int64_t N = 0, int KF = 1);
+// dx = Omega^T (dF * F) - x sum(dF * F) per row (the gradient through the features F of x,
+// m = d, omega [d][d]).
+hipError_t launch_favor_features_bwd(int dt, int d, const void* x, const float* omega, const void* F, const void* dF,
+                                     void* dx, int64_t rows, hipStream_t s);
 // KF feature blocks of rows x [rows][d] (rows = heads x N; omega [KF d][d]) into
 // out [heads][KF][N][d]; N = 0: one head of all rows.
 // o = sum_j den_j o_j / sum_j den_j over the KF feature blocks of each head (ob

@@ -37,7 +37,8 @@ namespace la {
 // row reductions and the dQ epilogue.  phi(Q), G and g of the chunk are staged
 // in LDS (double-buffered, one barrier per chunk) for the update of (R, r),
 // which contracts over all 64 tokens.
-template <typename T, int D>
+// FM: the feature map (FeatGiven: phi is the identity and the rank-1 parts vanish).
+template <typename T, int D, class FM = FeatElu>
 __global__ __launch_bounds__(kBlock, 2) void ncbwd_q_kernel(const T* __restrict__ q, const T* __restrict__ dout,
                                                          T* __restrict__ dq, const float* __restrict__ total,
                                                          int ntotal, float* __restrict__ rrec, int N, int cps,
@@ -104,14 +105,14 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_q_kernel(const T* __restrict_
             const f32x4 zv = lds4(&s_z[16 * m + 4 * g]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float x = to_f32(from_f32<T>(phi_f(qrow.get(4 * m + e))));
+                const float x = to_f32(from_f32<T>(FM::phi(qrow.get(4 * m + e))));
                 y[4 * m + e] = x;
                 qs += x;
                 zd += x * zv[e];
             }
             store4(&tQ.at(tl, 16 * m + 4 * g), f32x4{y[4 * m], y[4 * m + 1], y[4 * m + 2], y[4 * m + 3]});
         }
-        qs = sum_over_groups(qs);
+        qs = FM::kSplit ? sum_over_groups(qs) : 0.f;  // no rank-1 parts when unsplit
         const float den = qs * n + sum_over_groups(zd);
         const float inv_den = rcp_f(den);
 
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_q_kernel(const T* __restrict_
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 gy[4 * m + e] = valid ? to_f32(from_f32<T>(cdo.get(4 * m + e) * inv_den)) : 0.f;
-                gp += gy[4 * m + e] * pv[e];
+                if constexpr (FM::kSplit) gp += gy[4 * m + e] * pv[e];
             }
             store4(&tG.at(tl, 16 * m + 4 * g), f32x4{gy[4 * m], gy[4 * m + 1], gy[4 * m + 2], gy[4 * m + 3]});
         }
@@ -154,14 +155,15 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_q_kernel(const T* __restrict_
         if (g == 0) s_g[buf][tl] = gt;
 
         // dQ = ((S_E G)_a + g z_E[a] + G.P + g N) phi'(Q_a), phi' = min(phi, 1).
-        const float bracket = gp + gt * n;
+        const float bracket = FM::kSplit ? gp + gt * n : 0.f;
 #pragma unroll
         for (int m = 0; m < DT; ++m) {
             const int f0 = 16 * m + 4 * g;
             const f32x4 zv = lds4(&s_z[f0]);
             f32x4 x;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = (accQ[m][e] + zv[e] * gt + bracket) * fminf(y[4 * m + e], 1.f);
+            for (int e = 0; e < 4; ++e)
+                x[e] = (accQ[m][e] + zv[e] * gt + bracket) * FM::dphi_at_phi(y[4 * m + e]);
             gstore4<T>(bdq, (uint32_t)(tok * D + f0), x);
         }
         __syncthreads();  // the chunk's phi(Q), G and g are staged
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_q_kernel(const T* __restrict_
 // into LDS once; wavefront w then walks key tile 16 w .. of every chunk on its
 // own (no barrier in the loop), with K and V of its rows in registers in
 // accumulator order (E(K) and phi'(K) from one exp).
-template <typename T, int D>
+template <typename T, int D, class FM = FeatElu>
 __global__ __launch_bounds__(kBlock, 2) void ncbwd_kv_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                           T* __restrict__ dk, T* __restrict__ dv,
                                                           const float* __restrict__ rtotal, int ntotal, int N,
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_kv_kernel(const T* __restrict
             if constexpr (D > 64) __atomic_signal_fence(__ATOMIC_SEQ_CST);  // one k-step's operands at a time
             float ke[NY];
 #pragma unroll
-            for (int i = 0; i < NY; ++i) ke[i] = to_f32(from_f32<T>(elu_f(kcur.get(i))));
+            for (int i = 0; i < NY; ++i) ke[i] = to_f32(from_f32<T>(FM::e(kcur.get(i))));
             const typename M::frag yv = M::raw_op(vcur.r, k0);
             const typename M::frag ye = M::vals_op(ke, k0);
 #pragma unroll
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_kv_kernel(const T* __restrict
                 const typename M::frag xr = M::ld_acc(tRt, 16 * m, k0, lane);
                 acck[m] = M::mma(M::ld_tr_acc(tRt, k0, 16 * m, lane), yv, acck[m]);
                 accv[m] = M::mma(xr, ye, accv[m]);
-                accv[m] = M::mma(xr, one, accv[m]);
+                if constexpr (FM::kSplit) accv[m] = M::mma(xr, one, accv[m]);  // w = sum_a R[a][.]
             }
         }
 #pragma unroll
@@ -276,7 +278,8 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_kv_kernel(const T* __restrict
             const f32x4 rv = lds4(&s_r[f0]);
             f32x4 xk;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) xk[e] = (acck[m][e] + rv[e]) * dphi_f(kcur.get(4 * m + e));
+            for (int e = 0; e < 4; ++e)
+                xk[e] = (acck[m][e] + rv[e]) * (FM::kSplit ? dphi_f(kcur.get(4 * m + e)) : 1.f);
             gstore4<T>(bdk, (uint32_t)(tok * D + f0), xk);
             gstore4<T>(bdv, (uint32_t)(tok * D + f0), accv[m]);
         }
@@ -293,11 +296,15 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_kv_kernel(const T* __restrict
 
 // ---------------------------------------------------------------------------------------
 hipError_t launch_ncbwd_q(int dt, int d, const void* q, const void* dout, void* dq, const float* total, int ntotal,
-                          float* rrec, int64_t BH, int64_t N, SegPlan p, hipStream_t s) {
+                          float* rrec, int64_t BH, int64_t N, SegPlan p, hipStream_t s, int feat) {
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_NCQ(TT, DD)                                                                                            \
-    hipLaunchKernelGGL((ncbwd_q_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)dout, (TT*)dq, \
-                       total, ntotal, rrec, (int)N, p.cps, p.nseg, (int)BH)
+    if (feat == kFeatGiven)                                                                                       \
+        hipLaunchKernelGGL((ncbwd_q_kernel<TT, DD, FeatGiven>), grid, dim3(kBlock), 0, s, (const TT*)q,          \
+                           (const TT*)dout, (TT*)dq, total, ntotal, rrec, (int)N, p.cps, p.nseg, (int)BH);          \
+    else                                                                                                         \
+        hipLaunchKernelGGL((ncbwd_q_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)dout,    \
+                           (TT*)dq, total, ntotal, rrec, (int)N, p.cps, p.nseg, (int)BH)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_NCQ(bf16, 32); break;
@@ -317,11 +324,15 @@ hipError_t launch_ncbwd_q(int dt, int d, const void* q, const void* dout, void* 
 }
 
 hipError_t launch_ncbwd_kv(int dt, int d, const void* k, const void* v, void* dk, void* dv, const float* rtotal,
-                           int ntotal, int64_t BH, int64_t N, SegPlan p, hipStream_t s) {
+                           int ntotal, int64_t BH, int64_t N, SegPlan p, hipStream_t s, int feat) {
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_NCKV(TT, DD)                                                                                           \
-    hipLaunchKernelGGL((ncbwd_kv_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)k, (const TT*)v, (TT*)dk,  \
-                       (TT*)dv, rtotal, ntotal, (int)N, p.cps, p.nseg, (int)BH)
+    if (feat == kFeatGiven)                                                                                       \
+        hipLaunchKernelGGL((ncbwd_kv_kernel<TT, DD, FeatGiven>), grid, dim3(kBlock), 0, s, (const TT*)k,         \
+                           (const TT*)v, (TT*)dk, (TT*)dv, rtotal, ntotal, (int)N, p.cps, p.nseg, (int)BH);          \
+    else                                                                                                         \
+        hipLaunchKernelGGL((ncbwd_kv_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)k, (const TT*)v,      \
+                           (TT*)dk, (TT*)dv, rtotal, ntotal, (int)N, p.cps, p.nseg, (int)BH)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_NCKV(bf16, 32); break;

@@ -271,3 +271,24 @@ def test_decode_blocks_validation(lib):
     # the states are m x d per key/value head: z right after S of 2 x 128 x 64 fp32
     assert f(S, S + 2 * 128 * 64 * 4 - 16, q, k, v, o, 1, 8, 2, 16, 64, 128, 1, wsp, 1 << 30, None) == 1
     assert f(S, z, q, k, v, o, 1, 8, 2, 0, 64, 128, 1, None, 0, None) == 0         # no tokens
+
+
+def test_features_backward_validation(lib):
+    b = lib.la_backward_causal_features
+    args = [A, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000, A + 0x5000000, A + 0x6000000]
+    wsp = A + 0x7000000
+    assert b(*args, 1, 1, 64, 64, 1, wsp, 8, None) == 3                   # workspace too small
+    assert b(*args, 1, 1, 64, 96, 1, wsp, 1 << 30, None) == 2             # d unsupported
+    bad = list(args)
+    bad[5] = args[4]                                                       # dfk aliases dfq
+    assert b(*bad, 1, 1, 64, 64, 1, wsp, 1 << 30, None) == 1
+    assert b(*args, 1, 1, 0, 64, 1, None, 0, None) == 0                   # no tokens
+    n = lib.la_backward_noncausal_features
+    assert n(*args, 1, 1, 64, 64, 1, wsp, 8, None) == 3
+    assert n(*args, 1, 1, 64, 128, 0, wsp, 1 << 30, None) == 2            # fp32 d = 128 not built
+    f = lib.la_favor_features_backward
+    x, om, F, dF, dx = A, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000
+    assert f(x, None, F, dF, dx, 64, 64, 1, None) == 1                    # no directions
+    assert f(x, om, F, dF, F, 64, 64, 1, None) == 1                       # dx aliases F
+    assert f(x, om, F, dF, dx, 64, 96, 1, None) == 2                      # d unsupported
+    assert f(x, om, F, dF, dx, 0, 64, 1, None) == 0                       # no rows

@@ -266,3 +266,90 @@ def test_favor_blocks_prefill_then_decode(la, oracle, d, KF, dtype):
     record(f"favor blocks prefill+decode d={d} m={m} {dtype}", **errs)
     assert errs["o"] < TOL[dtype], errs
     assert max(errs["S"], errs["z"]) < SUM_TOL[dtype], errs
+
+
+# ---- backward: on given features, through the feature map, and end to end ----------------------
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_favor_backward_given_features(la, oracle, shape, dtype, causal):
+    """dfq, dfk, dv on the library's FAVOR+ features against the oracle on the same features."""
+    B, H, N, d = shape
+    if dtype == torch.float32 and d == 128:
+        pytest.skip("fp32 backward is built for d <= 64")
+    q, k, v, do = (t.cuda() for t in inp.favor_qkv(B, H, N, d, dtype, seed=N + 90, with_dout=True))
+    om = inp.favor_omega(d, seed=N + 91).cuda()
+    fq, fk = la.favor_features(q, om), la.favor_features(k, om)
+    dfq, dfk, dv = la.la_backward_causal_features(fq, fk, v, do, causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle.backward_features(f64(fq), f64(fk), f64(v), f64(do), causal)
+    if N == 1:
+        # A single token: O_0 = V_0 whatever the features, so dfq and dfk vanish exactly and
+        # only rounding is left.  Causal: g is formed from the very products of dA, so dA_00 is
+        # a few fp32 roundings of M = sum_b |G_b V_b| (G = dO / den).  Non-causal: the state
+        # S = fk V^T and R = fq G^T enter their MFMAs rounded to bf16 against fp32 terms that
+        # cancel them, which leaves at most 2 u M fk_a in dfq_a and 2 u M fq_a in dfk_a (u = 2^-8).
+        ffq, ffk, vv = f64(fq), f64(fk), f64(v)
+        den = (ffq * ffk).sum(-1, keepdims=True)
+        M = (np.abs(f64(do) / den) * np.abs(vv)).sum(-1, keepdims=True)
+        c = 2.0 ** -7 if (dtype == torch.bfloat16 and not causal) else 1e-5
+        assert (np.abs(f64(dfq)) <= c * M * ffk + 1e-30).all()
+        assert (np.abs(f64(dfk)) <= c * M * ffq + 1e-30).all()
+        assert slice_err(dv, ref[2]) < TOL[dtype]
+        return
+    errs = {n: slice_err(g, r) for n, g, r in zip(("dfq", "dfk", "dv"), (dfq, dfk, dv), ref)}
+    record(f"favor_bwd {'causal' if causal else 'noncausal'} {B}x{H}x{N}x{d} {dtype}", **errs)
+    assert max(errs.values()) < TOL[dtype], errs
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_favor_features_backward(la, oracle, d, dtype):
+    """dx of the feature map, each element held to its first-order bound: the features the
+    kernel is handed carry their own error (feat_bound), the bf16 Omega split 2^-16, and the
+    fp32 sums (d + 2) 2^-24, each times sum_i |dF_i F_i| (|omega_ia| + |x_a|); then dx is
+    rounded to the output dtype (u |dx|)."""
+    rows = 777
+    x = inp.normal((rows, d), inp.generator(d + 7), dtype, d ** -0.25).cuda()
+    om = inp.favor_omega(d, seed=d + 8).cuda()
+    F = la.favor_features(x, om)
+    dF = inp.normal((rows, d), inp.generator(d + 9), dtype, 1.0).cuda()
+    dx = la.favor_features_backward(x, om, F, dF)
+    torch.cuda.synchronize()
+    ref = oracle.favor_features_backward(f64(x), f64(om), f64(dF)) * math.sqrt(d)
+    refF = oracle.favor_features(f64(x), f64(om)) * math.sqrt(d)
+    xx, oo, g = f64(x), f64(om), np.abs(f64(dF))
+    fb = feat_bound(refF, x, om, dtype)
+    c = (2.0 ** -16 if dtype == torch.bfloat16 else 0.0) + (d + 2) * 2.0 ** -24
+    bound = (g * fb) @ np.abs(oo) + np.abs(xx) * (g * fb).sum(-1, keepdims=True)
+    bound += c * ((g * refF) @ np.abs(oo) + np.abs(xx) * (g * refF).sum(-1, keepdims=True))
+    bound += (2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -24) * np.abs(ref)
+    ratio = float((np.abs(f64(dx) - ref) / bound).max())
+    record(f"favor_features_bwd d={d} {dtype}", ratio=ratio, dx=slice_err(dx[None], ref[None]))
+    assert ratio <= 1.0, ratio
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_favor_attention_autograd(la, oracle, dtype, causal):
+    """Performer attention trained end to end: O and dq, dk, dv of the autograd op against the
+    oracle's chain (features, attention on features, its backward, the feature map's backward);
+    the constant 1/sqrt(m) the library leaves out changes none of them."""
+    B, H, N, d = 2, 3, 333, 64
+    q, k, v, do = (t.cuda() for t in inp.favor_qkv(B, H, N, d, dtype, seed=100, with_dout=True))
+    om = inp.favor_omega(d, seed=101).cuda()
+    q.requires_grad_(True)
+    k.requires_grad_(True)
+    v.requires_grad_(True)
+    o = la.favor_attention(q, k, v, om, causal)
+    o.backward(do)
+    torch.cuda.synchronize()
+    rfq, rfk = oracle.favor_features(f64(q), f64(om)), oracle.favor_features(f64(k), f64(om))
+    ro = oracle.forward_features(rfq, rfk, f64(v), causal)
+    dfq, dfk, rdv = oracle.backward_features(rfq, rfk, f64(v), f64(do), causal)
+    rdq = oracle.favor_features_backward(f64(q), f64(om), dfq)
+    rdk = oracle.favor_features_backward(f64(k), f64(om), dfk)
+    errs = {"o": slice_err(o, ro), "dq": slice_err(q.grad, rdq), "dk": slice_err(k.grad, rdk),
+            "dv": slice_err(v.grad, rdv)}
+    record(f"favor_attention autograd {'causal' if causal else 'noncausal'} {dtype}", **errs)
+    assert max(errs.values()) < TOL[dtype], errs
