@@ -487,30 +487,56 @@ __global__ __launch_bounds__(kBlock) void noncausal_fwd_kernel(const T* __restri
 // record [S0_E^T | z0_E | P0] and n0 per head.  Either input may be null (zero).
 // split = 0 (features carried unsplit): P0 = 0, n0 = 0, the record is S0, z0 itself.
 // init_n may be null (no count wanted).
-// Thread b handles value column b (fixed-order sums: bitwise reproducible).
+// The state is staged through LDS (rows padded by one float) so that both its reads
+// and the transposed record's writes are coalesced; column b's mean is summed by
+// thread b in feature order (fixed order: bitwise reproducible).
 template <int D>
 __global__ __launch_bounds__(kBlock) void state_split_kernel(const float* __restrict__ S0, const float* __restrict__ z0,
                                                              float* __restrict__ init, float* __restrict__ init_n,
                                                              int split) {
-    const int bh = blockIdx.x, b = threadIdx.x;
+    __shared__ float s_S[D][D + 1];
+    __shared__ float s_p[D];
+    __shared__ float s_n;
+    const int bh = blockIdx.x, tid = threadIdx.x;
     float* r = init + (int64_t)bh * Rec<D>::kSize;
     const float* Sh = S0 != nullptr ? S0 + (int64_t)bh * D * D : nullptr;
     const float* zh = z0 != nullptr ? z0 + (int64_t)bh * D : nullptr;
-    float n0 = 0.f;
-    if (zh != nullptr && split) {
-        for (int a = 0; a < D; ++a) n0 += zh[a];
-        n0 *= 1.f / (float)D;
+    constexpr int D4 = D / 4;
+    for (int i = tid; i < D * D4; i += kBlock) {  // row i / D4, columns 4 (i % D4) ..
+        const int aa = i / D4, c = 4 * (i % D4);
+        const f32x4 x = Sh != nullptr ? *reinterpret_cast<const f32x4*>(Sh + aa * D + c) : zero4();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_S[aa][c + e] = x[e];
     }
-    if (b >= D) return;
-    float p = 0.f;
-    if (Sh != nullptr && split) {
-        for (int a = 0; a < D; ++a) p += Sh[a * D + b];
-        p *= 1.f / (float)D;
+    if (tid == kBlock - 1) {  // n0: the mean of z0 over the features
+        float n0 = 0.f;
+        if (zh != nullptr && split) {
+            for (int a = 0; a < D; ++a) n0 += zh[a];
+            n0 *= 1.f / (float)D;
+        }
+        s_n = n0;
+        if (init_n != nullptr) init_n[bh] = n0;
     }
-    for (int a = 0; a < D; ++a) r[Rec<D>::kSt + b * D + a] = Sh != nullptr ? Sh[a * D + b] - p : 0.f;
-    r[Rec<D>::kZ + b] = zh != nullptr ? zh[b] - n0 : 0.f;  // feature b of z0_E
-    r[Rec<D>::kP + b] = p;
-    if (b == 0 && init_n != nullptr) init_n[bh] = n0;
+    __syncthreads();
+    if (tid < D) {  // P0[b]: the mean of column b
+        float p = 0.f;
+        if (Sh != nullptr && split) {
+            for (int a = 0; a < D; ++a) p += s_S[a][tid];
+            p *= 1.f / (float)D;
+        }
+        s_p[tid] = p;
+        r[Rec<D>::kP + tid] = p;
+    }
+    __syncthreads();
+    // Record [S0_E^T | z0_E | P0]: element (b, a) of the transposed block is S0[a][b] - P0[b].
+    for (int i = tid; i < D * D4; i += kBlock) {  // row i / D4 of the block, columns 4 (i % D4) ..
+        const int bb = i / D4, a0 = 4 * (i % D4);
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = s_S[a0 + e][bb] - s_p[bb];
+        *reinterpret_cast<f32x4*>(r + Rec<D>::kSt + bb * D + a0) = y;
+    }
+    if (tid < D) r[Rec<D>::kZ + tid] = zh != nullptr ? zh[tid] - s_n : 0.f;  // feature tid of z0_E
 }
 
 // dst[i] = src[i], or 0 when src is null.
