@@ -83,7 +83,8 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(float* __restrict__ S, f
 // per query head).  Per token t: S += phi(k_t) v_t^T, z += phi(k_t) once, then
 // each of the G query heads reads o = phi(q)^T S / phi(q)^T z.  The d x d state is
 // held in registers across the call (thread (rg, cq) owns columns 4 cq .. 4 cq + 3
-// of rows rg + RPP p), so it moves through HBM once per call instead of once per
+// of rows NP rg .. NP rg + NP - 1: its feature values come in 16-byte LDS reads), so
+// it moves through HBM once per call instead of once per
 // token, and once per group instead of once per query head.
 // With KF feature blocks (features m = KF d, block layout), the state of block j of
 // key/value head kv is a state of its own (flat index kv KF + j) that reads the
@@ -102,8 +103,9 @@ __global__ __launch_bounds__(kBlock) void decode_steps_kernel(float* __restrict_
                                                               int G, int KFb, float* __restrict__ den_out) {
     const int KF = kBlocks ? KFb : 1;  // feature blocks (compiled out for one)
     constexpr int F4 = D / 4;         // float4 per state row
-    constexpr int RPP = kBlock / F4;  // rows per pass
-    constexpr int NP = D / RPP;       // passes
+    constexpr int RPP = kBlock / F4;  // row groups
+    constexpr int NP = D / RPP;       // rows per thread: rows NP rg .. NP rg + NP - 1
+    constexpr int VW = NP % 4 == 0 ? 4 : 1;  // feature values per LDS read
     constexpr int NW = kBlock / kWave;
     constexpr int RB = D <= 64 ? 16 : 8;  // (token, query head) rows per block
     static_assert(kBlock % F4 == 0 && D % RPP == 0 && F4 <= kWave, "state rows must tile the workgroup");
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(kBlock) void decode_steps_kernel(float* __restrict_
 
     f32x4 x[NP];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) x[p] = Sh[(rg + RPP * p) * F4 + cq];
+    for (int p = 0; p < NP; ++p) x[p] = Sh[(NP * rg + p) * F4 + cq];
     float zn = tid < D ? z[(int64_t)kvh * D + tid] : 0.f;
 
     for (int64_t r0 = 0; r0 < nrows; r0 += RB) {
@@ -166,11 +168,23 @@ __global__ __launch_bounds__(kBlock) void decode_steps_kernel(float* __restrict_
             if (opens) {
                 const f32x4 v4 = *reinterpret_cast<const f32x4*>(&s_v[i][4 * cq]);
 #pragma unroll
-                for (int p = 0; p < NP; ++p) x[p] += s_kf[i][rg + RPP * p] * v4;
+                for (int p4 = 0; p4 < NP; p4 += VW) {
+                    float kf4[VW];
+                    if constexpr (VW == 4) *reinterpret_cast<f32x4*>(kf4) = *reinterpret_cast<const f32x4*>(&s_kf[i][NP * rg + p4]);
+                    else kf4[0] = s_kf[i][NP * rg + p4];
+#pragma unroll
+                    for (int e = 0; e < VW; ++e) x[p4 + e] += kf4[e] * v4;
+                }
             }
             f32x4 acc = zero4();
 #pragma unroll
-            for (int p = 0; p < NP; ++p) acc += s_qf[i][rg + RPP * p] * x[p];
+            for (int p4 = 0; p4 < NP; p4 += VW) {
+                float qf4[VW];
+                if constexpr (VW == 4) *reinterpret_cast<f32x4*>(qf4) = *reinterpret_cast<const f32x4*>(&s_qf[i][NP * rg + p4]);
+                else qf4[0] = s_qf[i][NP * rg + p4];
+#pragma unroll
+                for (int e = 0; e < VW; ++e) acc += qf4[e] * x[p4 + e];
+            }
 #pragma unroll
             for (int off = F4; off < kWave; off <<= 1) {
 #pragma unroll
@@ -195,7 +209,7 @@ __global__ __launch_bounds__(kBlock) void decode_steps_kernel(float* __restrict_
         __syncthreads();  // the block's LDS is free for the next one
     }
 #pragma unroll
-    for (int p = 0; p < NP; ++p) Sh[(rg + RPP * p) * F4 + cq] = x[p];
+    for (int p = 0; p < NP; ++p) Sh[(NP * rg + p) * F4 + cq] = x[p];
     if (tid < D) z[(int64_t)kvh * D + tid] = zn;
 }
 
