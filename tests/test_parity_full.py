@@ -130,3 +130,46 @@ def test_decode_sampled_sequences(la, oracle):
     errs = {"o_worst_step": worst, "S_final": slice_err(rS_gpu, rS)}
     record("full decode 512 steps sampled", **errs)
     assert worst < TOL[w.dtype] and errs["S_final"] < 1e-3, errs
+
+
+# ---- the longest head the ABI takes ------------------------------------------------------------
+@pytest.mark.parametrize("d", [64, 128])
+def test_longest_head(la, oracle, d):
+    """One head of the longest sequence a call accepts (its bytes just under 2^31), causal.
+    Keys and values are drawn only for the first and last P tokens and are zero in between, so
+    the oracle can follow the whole sequence: a zero key adds phi(0) = 1 to every feature of z
+    and nothing to S.  The last P rows are the oracle's recurrence from the state
+    (S_1, z_1 + gap) the first block and the gap leave; a row i sampled in the gap reads
+    (S_1, z_1 + i - P + 1): the oracle's decode step from (S_1, z_1 + i - P) with the row's
+    own zero key and value."""
+    P = 1024
+    N = ((1 << 31) - 1) // (d * 2) - 64  # the largest N with N d 2 + 64 d 2 < 2^31 bytes per head
+    N -= N % 7                            # a ragged last chunk, N not a multiple of 64
+    gap = N - 2 * P
+    gen = inp.generator(d + 5, "cuda")
+    q = torch.zeros((1, 1, N, d), dtype=torch.bfloat16, device="cuda")
+    k, v = torch.zeros_like(q), torch.zeros_like(q)
+    s = 1.0 / d ** 0.5
+    for t in (q, k, v):
+        t[:, :, :P] = inp.normal((1, 1, P, d), gen, torch.bfloat16, s, "cuda")
+        t[:, :, N - P:] = inp.normal((1, 1, P, d), gen, torch.bfloat16, s, "cuda")
+    rows = np.array([P, P + 1, P + 63, N // 2, N // 2 + 1, N - P - 1])
+    q[0, 0, torch.from_numpy(rows).cuda()] = inp.normal((len(rows), d), gen, torch.bfloat16, s, "cuda")
+    o, S, z = la.la_forward_causal(q, k, v, return_state=True)
+    torch.cuda.synchronize()
+    hq, hk, hv = (f64(t[:, :, :P]) for t in (q, k, v))
+    ro1, S1, z1 = oracle.forward_causal(hq, hk, hv, return_state=True)
+    tq, tk, tv = (f64(t[:, :, N - P:]) for t in (q, k, v))
+    ro3, S3, z3 = oracle.forward_causal(tq, tk, tv, return_state=True, S0=S1, z0=z1 + gap)
+    errs = {"head": slice_err(o[:, :, :P], ro1), "tail": slice_err(o[:, :, N - P:], ro3),
+            "S": slice_err(S, S3), "z": slice_err(z[..., None], z3[..., None])}
+    zero = np.zeros((1, d))
+    worst = 0.0
+    for i in rows:
+        ro, _, _ = oracle.decode_step(S1[0], z1[0] + (i - P), f64(q[0, :, i]), zero, zero)
+        worst = max(worst, slice_err(o[0, :, i][None], ro[None]))
+    errs["gap rows"] = worst
+    record(f"longest head N={N} d={d}", **errs)
+    print(N, errs, flush=True)
+    assert max(errs["head"], errs["tail"], errs["gap rows"]) < TOL[torch.bfloat16], errs
+    assert max(errs["S"], errs["z"]) < 1e-3, errs
