@@ -13,7 +13,9 @@
  * memory-efficient Transformers at blopig.com, "Softmax approximators").  The
  * causal form updates S and z token by token ("Why It Matters"), so row i reads
  * keys 0..i inclusive.  The feature map is phi(x) = elu(x) + 1 elementwise, so
- * m = d.  No 1/sqrt(d) scale is applied inside: the formula has none, callers
+ * m = d; the *_features calls take features the caller applied instead (FAVOR+,
+ * below, with m = d or, in blocks of d, m > d).  No 1/sqrt(d) scale is applied
+ * inside: the formula has none, callers
  * scale Q or K themselves.  No epsilon is added to the denominator: phi > 0.
  *
  * Conventions for every call
@@ -221,7 +223,8 @@ la_status la_favor_features(const void* x, const float* omega, void* out, int64_
  * positive (denominators must not vanish; an exact 0 is read as the padding
  * past a sequence's end and adds nothing to the state).  Same layouts, workspaces
  * (la_workspace_size of the matching op), start states and errors as those
- * calls; no saved state (no backward on given features). */
+ * calls; no saved state (la_backward_causal_features / la_backward_noncausal_features
+ * rebuild the key aggregates themselves). */
 la_status la_forward_causal_features(const void* fq, const void* fk, const void* v, void* o,
                                      const float* S0, const float* z0, float* den_out, float* S_out,
                                      float* z_out, int64_t B, int64_t H, int64_t N, int64_t d,
