@@ -280,7 +280,8 @@ la_status la_favor_features_backward(const void* x, const float* omega, const vo
  * states (causal only, nullable, natural layout above) as la_forward_causal_features.
  * Workspace: la_features_workspace_size(causal != 0, B, H, N, d, m, dt, &bytes), which
  * for KF > 1 holds the blocks' outputs besides the plain call's workspace (causal = 2:
- * the workspace of la_decode_steps_features_blocks with N = T). */
+ * the workspace of la_decode_steps_features_blocks with N = T; causal = 3: that of
+ * la_backward_causal_features_blocks). */
 la_status la_features_workspace_size(int causal, int64_t B, int64_t H, int64_t N, int64_t d, int64_t m,
                                      la_dtype dt, size_t* bytes_out);
 la_status la_favor_features_blocks(const void* x, const float* omega, void* out, int64_t heads, int64_t N,
@@ -293,6 +294,18 @@ la_status la_forward_noncausal_features_blocks(const void* fq, const void* fk, c
                                                float* den_out, int64_t B, int64_t H, int64_t N, int64_t d,
                                                int64_t m, la_dtype dt, void* workspace, size_t workspace_bytes,
                                                void* stream);
+/* Causal backward on m = KF d features (block layout, as la_forward_causal_features_blocks
+ * from a zero state): dfq, dfk [B][H][KF][N][d] and dv [B][H][N][d] of L = sum(dO * O).  The
+ * blocks share one normalization, so every block uses the head's G = dO / den and
+ * g = -G . O: den [B][H][N] fp32 is the forward's den_out (the head's, over all m
+ * features).  A statistics sweep per block gives each row's G . num_j, their sum gives g,
+ * then the block's sweeps give dfq_j, dfk_j and its share of dv (summed over the blocks).
+ * Workspace: la_features_workspace_size(3, B, H, N, d, m, dt, &bytes); m = d is
+ * la_backward_causal_features (den unused). */
+la_status la_backward_causal_features_blocks(const void* fq, const void* fk, const void* v, const void* dout,
+                                             const float* den, void* dfq, void* dfk, void* dv, int64_t B,
+                                             int64_t H, int64_t N, int64_t d, int64_t m, la_dtype dt,
+                                             void* workspace, size_t workspace_bytes, void* stream);
 /* Multi-token decode (la_decode_steps_features) on m = KF d features: fq [B][H][KF][T][d]
  * and fk [B][Hkv][KF][T][d] in block layout, v, o as la_decode_steps; the state of key/value
  * head j is S [B][Hkv][m][d], z [B][Hkv][m] (what la_forward_causal_features_blocks leaves

@@ -30,6 +30,7 @@ from ._binding import (  # noqa: F401
     la_forward_noncausal_features_blocks,
     la_decode_steps_features_blocks,
     la_backward_causal_features,
+    la_backward_causal_features_blocks,
     la_backward_noncausal_features,
     favor_features_backward,
     favor_attention,

@@ -26,7 +26,7 @@ EXPORTS = ("la_workspace_size", "la_saved_state_size", "la_forward_noncausal", "
            "la_backward_causal_state", "la_forward_causal_grouped", "la_features_workspace_size",
            "la_favor_features_blocks", "la_forward_causal_features_blocks", "la_forward_noncausal_features_blocks",
            "la_decode_steps_features_blocks", "la_backward_causal_features", "la_backward_noncausal_features",
-           "la_favor_features_backward", "la_status_string", "la_last_error_message", "la_version",
+           "la_favor_features_backward", "la_backward_causal_features_blocks", "la_status_string", "la_last_error_message", "la_version",
            "la_profile_enable", "la_profile_count", "la_profile_entry", "la_debug_set_wait_limit",
            "la_debug_wait_limit")
 
@@ -76,6 +76,8 @@ def load_library(path: str | None = None):
         f = getattr(lib, name)
         f.restype = i32
         f.argtypes = [vp] * 7 + [i64, i64, i64, i64, i32, vp, sz, vp]
+    lib.la_backward_causal_features_blocks.restype = i32
+    lib.la_backward_causal_features_blocks.argtypes = [vp] * 8 + [i64, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_favor_features_backward.restype = i32
     lib.la_favor_features_backward.argtypes = [vp] * 5 + [i64, i64, i32, vp]
     lib.la_forward_causal_grouped.restype = i32
@@ -425,7 +427,7 @@ def favor_features_blocks(x, omega, *, out=None):
 
 def features_workspace_size(causal, B, H, N, d, m, dtype):
     out = ctypes.c_size_t(0)
-    kind = 2 if causal == 2 else (1 if causal else 0)
+    kind = causal if causal in (2, 3) else (1 if causal else 0)
     _check(load_library().la_features_workspace_size(kind, B, H, N, d, m, _dtype_code(dtype),
                                                      ctypes.byref(out)))
     return out.value
@@ -472,6 +474,26 @@ def la_forward_causal_features_blocks(fq, fk, v, *, return_den=False, return_sta
     if return_state:
         res += [S, z]
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def la_backward_causal_features_blocks(fq, fk, v, dout, den, *, out=None, workspace=None):
+    """Causal backward on m = KF d features in block layout fq, fk [B, H, KF, N, d]; den [B, H, N] is the
+    forward's den (return_den=True).  Returns (dfq, dfk) in block layout and dv [B, H, N, d]."""
+    B, H, N, d, m = _check_blocks(fq, fk, v)
+    if dout.shape != v.shape or dout.dtype != v.dtype or not dout.is_contiguous():
+        raise ValueError("dout must match v")
+    if den.shape != (B, H, N) or den.dtype != torch.float32 or not den.is_contiguous():
+        raise ValueError("den must be the forward's contiguous [B, H, N] fp32 denominators")
+    g = (torch.empty_like(fq), torch.empty_like(fk), torch.empty_like(v)) if out is None else out
+    need = features_workspace_size(3, B, H, N, d, m, fq.dtype)
+    ws = workspace if workspace is not None else (torch.empty(need, dtype=torch.uint8, device=fq.device)
+                                                  if need else None)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().la_backward_causal_features_blocks(_ptr(fq), _ptr(fk), _ptr(v), _ptr(dout), _ptr(den),
+                                                             _ptr(g[0]), _ptr(g[1]), _ptr(g[2]), B, H, N, d, m,
+                                                             _dtype_code(fq.dtype), _ptr(ws), nbytes,
+                                                             _stream(fq.device)))
+    return g
 
 
 def la_forward_noncausal_features_blocks(fq, fk, v, *, return_den=False, out=None, workspace=None):

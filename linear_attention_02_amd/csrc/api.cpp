@@ -608,6 +608,13 @@ la_status la_features_workspace_size(int causal, int64_t B, int64_t H, int64_t N
     if (st != LA_OK) return st;
     bool empty = false;
     if ((st = check_shape(B, H, N, d, 0, dt, &empty)) != LA_OK) return st;
+    if (causal == 3) {  // causal backward: the block heads' backward workspace, then their dv
+        const int64_t KF = m / d;
+        if (empty) { *bytes_out = 0; return LA_OK; }
+        const size_t wb = layout(LA_OP_BWD_CAUSAL, B, H * KF, N, d).bytes;
+        *bytes_out = KF == 1 ? wb : align_up(wb) + align_up((size_t)B * H * KF * N * d * elem_size(dt));
+        return LA_OK;
+    }
     if (causal == 2) {  // multi-token decode: N = T tokens per call, H query heads
         const int64_t KF = m / d;
         *bytes_out = (empty || KF == 1) ? 0
@@ -868,6 +875,95 @@ la_status la_backward_noncausal_features(const void* fq, const void* fk, const v
                                          void* workspace, size_t workspace_bytes, void* stream) {
     return backward_noncausal(fq, fk, v, dout, dfq, dfk, dv, nullptr, 0, B, H, N, d, dt, workspace, workspace_bytes,
                               stream, la::kFeatGiven);
+}
+
+la_status la_backward_causal_features_blocks(const void* fq, const void* fk, const void* v, const void* dout,
+                                             const float* den, void* dfq, void* dfk, void* dv, int64_t B, int64_t H,
+                                             int64_t N, int64_t d, int64_t m, la_dtype dt, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+    la_status st = check_blocks(d, m);
+    if (st != LA_OK) return st;
+    const int64_t KF = m / d;
+    if (KF == 1)
+        return backward_causal(fq, fk, v, dout, dfq, dfk, dv, nullptr, 0, nullptr, nullptr, nullptr, nullptr, nullptr,
+                               nullptr, B, H, N, d, 0, dt, workspace, workspace_bytes, stream, la::kFeatGiven);
+    bool empty = false;
+    if ((st = check_shape(B, H * KF, N, d, 0, dt, &empty)) != LA_OK) return st;
+    if (dt == LA_F32 && d == 128) return fail(LA_ERR_UNSUPPORTED, "fp32 causal backward is built for d = 32 and 64");
+    if (N > 0 && (!fq || !fk || !v || !dout || !den || !dfq || !dfk || !dv))
+        return fail(LA_ERR_INVALID_ARGUMENT, "fq, fk, v, dout, den, dfq, dfk and dv must be non-NULL");
+    const size_t tb = (size_t)B * H * N * d * elem_size(dt), fb = tb * KF;
+    const Range in[] = {{"fq", fq, fb}, {"fk", fk, fb}, {"v", v, tb}, {"dout", dout, tb},
+                        {"den", den, (size_t)B * H * N * sizeof(float)}};
+    const Range out[] = {{"dfq", dfq, fb}, {"dfk", dfk, fb}, {"dv", dv, tb}};
+    if ((st = check_ptrs(in, 5, out, 3)) != LA_OK) return st;
+    if (empty) return LA_OK;
+    const int64_t BHb = B * H * KF;  // block heads
+    const Layout L = layout(LA_OP_BWD_CAUSAL, B, H * KF, N, d);
+    const size_t dvb_off = align_up(L.bytes), need = dvb_off + align_up(fb);
+    if (workspace == nullptr) return fail(LA_ERR_WORKSPACE, "workspace is NULL; %zu bytes are needed", need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+        return fail(LA_ERR_INVALID_ARGUMENT, "workspace must be %zu-byte aligned", kAlign);
+    if (workspace_bytes < need)
+        return fail(LA_ERR_WORKSPACE, "workspace has %zu bytes; %zu are needed", workspace_bytes, need);
+    const Range wsr[] = {{"workspace", workspace, need}};
+    if ((st = check_ptrs(in, 5, wsr, 1)) != LA_OK) return st;
+    for (const Range& r : out)
+        if (overlap(wsr[0], r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+    if ((int64_t)L.plan.nseg * BHb > ((int64_t)1 << 24))
+        return fail(LA_ERR_UNSUPPORTED, "%lld workgroups exceed the 2^24 grid limit", (long long)L.plan.nseg * BHb);
+
+    char* ws = static_cast<char*>(workspace);
+    float* rec = reinterpret_cast<float*>(ws + L.rec);
+    float* rrec = reinterpret_cast<float*>(ws + L.rrec);
+    float* rowstat = reinterpret_cast<float*>(ws + L.rowstat);
+    void* dvb = ws + dvb_off;
+    const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
+    const int G = (int)KF;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    // Every block as a head of its own over its head's values and upstream gradient: the key
+    // aggregates, then the rows' G . num of each block with the head's den and G ...
+    if ((e = timed("seg_state", s, [&] {
+             return la::launch_seg_state(idt, (int)d, fk, v, rec, BHb, N, L.plan, s, la::kFeatGiven, G);
+         })) != hipSuccess)
+        return hip_fail(e, "seg_state launch");
+    if (L.plan.scan &&
+        (e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, BHb, L.plan.nseg, 1, s, nullptr); })) != hipSuccess)
+        return hip_fail(e, "scan launch");
+    if ((e = timed("bwd_prefix", s, [&] {
+             return la::launch_bwd_prefix(idt, (int)d, fq, fk, v, dout, dfq, rowstat, rrec, rec, BHb, N, L.plan, s,
+                                          nullptr, nullptr, la::kFeatGiven, 1, G, den);
+         })) != hipSuccess)
+        return hip_fail(e, "bwd_prefix launch");
+    // ... the head's g = -(sum_j G . num_j) / den for every block ...
+    if ((e = timed("combine_stats", s, [&] { return la::launch_combine_stats(rowstat, B * H * N, N, G, s); })) !=
+        hipSuccess)
+        return hip_fail(e, "combine_stats launch");
+    // ... then each block's sweeps with the head's (den, g): dfq, dfk and its share of dv.
+    if ((e = timed("bwd_prefix", s, [&] {
+             return la::launch_bwd_prefix(idt, (int)d, fq, fk, v, dout, dfq, rowstat, rrec, rec, BHb, N, L.plan, s,
+                                          nullptr, nullptr, la::kFeatGiven, 2, G, nullptr);
+         })) != hipSuccess)
+        return hip_fail(e, "bwd_prefix launch");
+    if (!la::prefix_forms_records((int)d) && (e = timed("rseg", s, [&] {
+                                                  return la::launch_rseg(idt, (int)d, fq, dout, rowstat, rrec, BHb, N,
+                                                                         L.plan, s, la::kFeatGiven, G);
+                                              })) != hipSuccess)
+        return hip_fail(e, "rseg launch");
+    if (L.plan.scan &&
+        (e = timed("rscan", s, [&] { return la::launch_scan((int)d, rrec, BHb, L.plan.nseg, -1, s, nullptr); })) != hipSuccess)
+        return hip_fail(e, "rscan launch");
+    if ((e = timed("bwd_suffix", s, [&] {
+             return la::launch_bwd_suffix(idt, (int)d, fq, fk, v, dout, dfk, dvb, rowstat, rrec, BHb, N, L.plan, s,
+                                          nullptr, nullptr, nullptr, la::kFeatGiven, G);
+         })) != hipSuccess)
+        return hip_fail(e, "bwd_suffix launch");
+    if ((e = timed("combine_blocks", s, [&] {
+             return la::launch_combine_blocks(idt, (int)d, dvb, nullptr, dv, nullptr, B * H * N, N, G, s);
+         })) != hipSuccess)
+        return hip_fail(e, "combine_blocks launch");
+    return LA_OK;
 }
 
 la_status la_decode_step(float* S, float* z, const void* q, const void* k, const void* v, void* o, int64_t B,

@@ -73,16 +73,24 @@ struct BwdPrefixForms {
 // count, one record and one count per head (the carried state starts from them).
 // FM: the feature map (FeatGiven: phi is the identity, E = phi and the rank-1 terms of the
 // split vanish: no q_sum, P or n anywhere, and dphi = 1).
-template <typename T, int D, bool kCoherentRecord, bool kRecord = true, bool kState = false, class FM = FeatElu>
+// Gv: heads per value head (v, dout, and den_in, of head bh / Gv: feature blocks of one head).
+// kMode, for attention split over feature blocks that share one normalization:
+//   0: the sweep as stated above;
+//   1: statistics: with the denominator den_in of the whole head given, G = round(dO / den),
+//      and each row's G . num of this block goes to rowstat (den, G . num); no dQ, no record;
+//   2: from given statistics: den and g are read from rowstat (den, g), the rest as in 0.
+template <typename T, int D, bool kCoherentRecord, bool kRecord = true, bool kState = false, class FM = FeatElu,
+          int kMode = 0>
 __device__ __forceinline__ void bwd_prefix_body(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dq, float2* __restrict__ rowstat, float* __restrict__ rrec, const float* __restrict__ rec, int N,
     int cps, int nseg, int prefixed, int seg, int bh, char* lds, const float* __restrict__ init,
-    const float* __restrict__ init_n) {
+    const float* __restrict__ init_n, int Gv = 1, const float* __restrict__ den_in = nullptr) {
     using M = Mma<T>;
     constexpr int KS = M::KSTEP;
     constexpr int DT = D / 16;
     constexpr int NY = D / 4;  // row values per lane in accumulator order
+    constexpr bool kFormsRecord = kRecord && kMode != 1;
     // E(K) and V are read after the mid-chunk barrier and are double-buffered;
     // phi(Q), G and g are written after the first barrier and read before the
     // next chunk's first barrier; S_E^T, z_E and P are read before the second.
@@ -99,9 +107,9 @@ __device__ __forceinline__ void bwd_prefix_body(
     const Tile<T, D, D> tSt{sm_st};
 
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
-    const int64_t hoff = (int64_t)bh * N * D;
+    const int64_t hoff = (int64_t)bh * N * D, voff = (int64_t)(bh / Gv) * N * D;
     const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
-    const GBuf bq(q + hoff, hbytes), bk(k + hoff, hbytes), bv(v + hoff, hbytes), bdo(dout + hoff, hbytes);
+    const GBuf bq(q + hoff, hbytes), bk(k + hoff, hbytes), bv(v + voff, hbytes), bdo(dout + voff, hbytes);
     const GBuf bdq(dq + hoff, hbytes), brs(rowstat + (int64_t)bh * N, (uint32_t)N * 8);
     const int tok_begin = seg * cps * kC;
     const int tok_end = min(N, tok_begin + cps * kC);
@@ -206,7 +214,9 @@ __device__ __forceinline__ void bwd_prefix_body(
                 }
             }
         }
-        const float den = qs_t * (n + (float)(tl + 1)) + sum_over_groups(rowB) + sum_over_groups(zd);
+        float den = qs_t * (n + (float)(tl + 1)) + sum_over_groups(rowB) + sum_over_groups(zd);
+        if constexpr (kMode == 1) den = valid ? den_in[(int64_t)(bh / Gv) * N + tok] : 1.f;
+        if constexpr (kMode == 2) den = valid ? brs.ld4f((uint32_t)tok * 8) : 1.f;
         const float inv_den = rcp_f(den);
 
         // (2)+(3) G_t = round(dO_t / den_t) of this wave's rows (staged for the R
@@ -262,11 +272,18 @@ __device__ __forceinline__ void bwd_prefix_body(
         for (int m = 0; m < DT; ++m)
 #pragma unroll
             for (int e = 0; e < 4; ++e) s3 += y[4 * m + e] * accQ[m][e];
-        const float gt = valid ? -(sum_over_groups(s1) + qs_t * gp + sum_over_groups(s3)) * inv_den : 0.f;
+        float gt;
+        if constexpr (kMode == 0)
+            gt = valid ? -(sum_over_groups(s1) + qs_t * gp + sum_over_groups(s3)) * inv_den : 0.f;
+        else if constexpr (kMode == 1)  // this block's G . num
+            gt = valid ? sum_over_groups(s1) + qs_t * gp + sum_over_groups(s3) : 0.f;
+        else
+            gt = valid ? brs.ld4f((uint32_t)tok * 8 + 4) : 0.f;
         if (g == 0) {
             s_g[tl] = gt;
-            brs.st8((uint32_t)tok * 8, make_uint2(__float_as_uint(den), __float_as_uint(gt)));
+            if constexpr (kMode != 2) brs.st8((uint32_t)tok * 8, make_uint2(__float_as_uint(den), __float_as_uint(gt)));
         }
+        if constexpr (kMode != 1) {
 
         // (5) dA_ts = G_t.V_s + g_t for s <= t, in place; its row sums.
         float rowdA = 0.f;
@@ -312,15 +329,16 @@ __device__ __forceinline__ void bwd_prefix_body(
                 gstore4<T>(bdq, (uint32_t)(tok * D + f0), x);
             }
         }
+        }  // kMode != 1
         __syncthreads();  // all rows of phi(Q), G and g are staged; S_E^T, z_E, P are no longer read
 
         // (7) State S_E += E^T V, z_E, P; segment aggregates R += phi(Q)^T G, r += phi(Q)^T g.
         state_update<T, D, true, true>(stS, vz, vp, tE, tV, nullptr, nullptr, lane, w);
-        if constexpr (kRecord) state_update<T, D, true, false>(stR, vr, vr, tQ, tG, s_g, nullptr, lane, w);
+        if constexpr (kFormsRecord) state_update<T, D, true, false>(stR, vr, vr, tQ, tG, s_g, nullptr, lane, w);
         n += (float)min(kC, N - c0);
     }
     // The record's last vector is unused (w = sum over a of R is formed from R where it is used).
-    if constexpr (!kRecord) {
+    if constexpr (!kFormsRecord) {
     } else if constexpr (kCoherentRecord) {
         const GBuf brr(rrec + (int64_t)bh * nseg * Rec<D>::kSize, (uint32_t)(nseg * Rec<D>::kSize * 4));
         store_record_coherent<D>(brr, (int64_t)seg * Rec<D>::kSize, stR, vr, nullptr, lane, w);
@@ -332,18 +350,18 @@ __device__ __forceinline__ void bwd_prefix_body(
     }
 }
 
-template <typename T, int D, bool kState = false, class FM = FeatElu>
+template <typename T, int D, bool kState = false, class FM = FeatElu, int kMode = 0>
 __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dq, float2* __restrict__ rowstat, float* __restrict__ rrec, const float* __restrict__ rec, int N,
-    int cps, int nseg, int BH, int prefixed, const float* __restrict__ init, const float* __restrict__ init_n) {
+    int cps, int nseg, int BH, int prefixed, const float* __restrict__ init, const float* __restrict__ init_n, int Gv,
+    const float* __restrict__ den_in) {
     __shared__ __attribute__((aligned(16))) char lds[BwdPrefixLds<T, D>::kBytes];
     // Later segments sum more records: they are dispatched first, since a CU's
     // older workgroup issues ahead of its younger one.
     const int seg = nseg - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
-    bwd_prefix_body<T, D, false, BwdPrefixForms<D>::kRecord, kState, FM>(q, k, v, dout, dq, rowstat, rrec, rec, N,
-                                                                         cps, nseg, prefixed, seg, bh, lds, init,
-                                                                         init_n);
+    bwd_prefix_body<T, D, false, BwdPrefixForms<D>::kRecord, kState, FM, kMode>(
+        q, k, v, dout, dq, rowstat, rrec, rec, N, cps, nseg, prefixed, seg, bh, lds, init, init_n, Gv, den_in);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -355,16 +373,16 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_prefix_ke
 template <typename T, int D, class FM = FeatElu>
 __global__ __launch_bounds__(kBlock, 2) void rseg_kernel(const T* __restrict__ q, const T* __restrict__ dout,
                                                       const float2* __restrict__ rowstat, float* __restrict__ rrec,
-                                                      int N, int cps, int nseg, int BH) {
+                                                      int N, int cps, int nseg, int BH, int Gv) {
     using CR = ChunkRegs<T, D>;
     __shared__ __attribute__((aligned(16))) T sm_q[2][kC * D];
     __shared__ __attribute__((aligned(16))) T sm_g[2][kC * D];
     __shared__ __attribute__((aligned(16))) float s_g[2][kC];
     const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
-    const int64_t hoff = (int64_t)bh * N * D;
+    const int64_t hoff = (int64_t)bh * N * D, voff = (int64_t)(bh / Gv) * N * D;
     const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
-    const GBuf bq(q + hoff, hbytes), bdo(dout + hoff, hbytes), brs(rowstat + (int64_t)bh * N, (uint32_t)N * 8);
+    const GBuf bq(q + hoff, hbytes), bdo(dout + voff, hbytes), brs(rowstat + (int64_t)bh * N, (uint32_t)N * 8);
     const int tok_begin = seg * cps * kC;
     const int tok_end = min(N, tok_begin + cps * kC);
 
@@ -428,7 +446,7 @@ __device__ __forceinline__ void bwd_suffix_body(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dk, T* __restrict__ dv, const float2* __restrict__ rowstat, const float* __restrict__ rrec, int N,
     int cps, int nseg, int prefixed, int seg, int bh, bool poison, char* lds, const float* __restrict__ rinit,
-    float* __restrict__ dS0, float* __restrict__ dz0) {
+    float* __restrict__ dS0, float* __restrict__ dz0, int Gv = 1) {
     using M = Mma<T>;
     using CR = ChunkRegs<T, D>;
     constexpr int KS = M::KSTEP;
@@ -442,9 +460,9 @@ __device__ __forceinline__ void bwd_suffix_body(
     float(*const s_r)[D] = reinterpret_cast<float(*)[D]>(lds + L::oR);
 
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
-    const int64_t hoff = (int64_t)bh * N * D;
+    const int64_t hoff = (int64_t)bh * N * D, voff = (int64_t)(bh / Gv) * N * D;
     const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
-    const GBuf bq(q + hoff, hbytes), bk(k + hoff, hbytes), bv(v + hoff, hbytes), bdo(dout + hoff, hbytes);
+    const GBuf bq(q + hoff, hbytes), bk(k + hoff, hbytes), bv(v + voff, hbytes), bdo(dout + voff, hbytes);
     const GBuf bdk(dk + hoff, hbytes), bdv(dv + hoff, hbytes), brs(rowstat + (int64_t)bh * N, (uint32_t)N * 8);
     const int tok_begin = seg * cps * kC;
     const int tok_end = min(N, tok_begin + cps * kC);
@@ -650,11 +668,11 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_ke
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dk, T* __restrict__ dv, const float2* __restrict__ rowstat, const float* __restrict__ rrec, int N,
     int cps, int nseg, int BH, int prefixed, const float* __restrict__ rinit, float* __restrict__ dS0,
-    float* __restrict__ dz0) {
+    float* __restrict__ dz0, int Gv) {
     __shared__ __attribute__((aligned(16))) char lds[BwdSuffixLds<T, D>::kBytes];
     const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
     bwd_suffix_body<T, D, false, kState, FM>(q, k, v, dout, dk, dv, rowstat, rrec, N, cps, nseg, prefixed, seg, bh,
-                                             false, lds, rinit, dS0, dz0);
+                                             false, lds, rinit, dS0, dz0, Gv);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -695,21 +713,28 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_fused_ker
 // ---------------------------------------------------------------------------------------
 hipError_t launch_bwd_prefix(int dt, int d, const void* q, const void* k, const void* v, const void* dout, void* dq,
                              float* rowstat, float* rrec, const float* rec, int64_t BH, int64_t N, SegPlan p,
-                             hipStream_t s, const float* init, const float* init_n, int feat) {
+                             hipStream_t s, const float* init, const float* init_n, int feat, int mode, int Gv,
+                             const float* den_in) {
     const dim3 grid((unsigned)(p.nseg * BH));
+#define LA_BWDP_GIVEN(TT, DD, MODE)                                                                               \
+    hipLaunchKernelGGL((bwd_prefix_kernel<TT, DD, false, FeatGiven, MODE>), grid, dim3(kBlock), 0, s, (const TT*)q, \
+                       (const TT*)k, (const TT*)v, (const TT*)dout, (TT*)dq, (float2*)rowstat, rrec, rec, (int)N,     \
+                       p.cps, p.nseg, (int)BH, (int)p.scan, nullptr, nullptr, Gv, den_in)
 #define LA_BWDP(TT, DD)                                                                                           \
-    if (feat == kFeatGiven)                                                                                       \
-        hipLaunchKernelGGL((bwd_prefix_kernel<TT, DD, false, FeatGiven>), grid, dim3(kBlock), 0, s, (const TT*)q,  \
-                           (const TT*)k, (const TT*)v, (const TT*)dout, (TT*)dq, (float2*)rowstat, rrec, rec, (int)N,  \
-                           p.cps, p.nseg, (int)BH, (int)p.scan, nullptr, nullptr);                                   \
+    if (feat == kFeatGiven && mode == 1)                                                                          \
+        LA_BWDP_GIVEN(TT, DD, 1);                                                                                 \
+    else if (feat == kFeatGiven && mode == 2)                                                                     \
+        LA_BWDP_GIVEN(TT, DD, 2);                                                                                 \
+    else if (feat == kFeatGiven)                                                                                  \
+        LA_BWDP_GIVEN(TT, DD, 0);                                                                                 \
     else if (init != nullptr || init_n != nullptr)                                                                \
         hipLaunchKernelGGL((bwd_prefix_kernel<TT, DD, true>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k, \
                            (const TT*)v, (const TT*)dout, (TT*)dq, (float2*)rowstat, rrec, rec, (int)N, p.cps, p.nseg, \
-                           (int)BH, (int)p.scan, init, init_n);                                                      \
+                           (int)BH, (int)p.scan, init, init_n, 1, nullptr);                                          \
     else                                                                                                         \
         hipLaunchKernelGGL((bwd_prefix_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k,    \
                            (const TT*)v, (const TT*)dout, (TT*)dq, (float2*)rowstat, rrec, rec, (int)N, p.cps, p.nseg, \
-                           (int)BH, (int)p.scan, nullptr, nullptr)
+                           (int)BH, (int)p.scan, nullptr, nullptr, 1, nullptr)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_BWDP(bf16, 32); break;
@@ -725,19 +750,20 @@ hipError_t launch_bwd_prefix(int dt, int d, const void* q, const void* k, const 
         }
     }
 #undef LA_BWDP
+#undef LA_BWDP_GIVEN
     return hipGetLastError();
 }
 
 hipError_t launch_rseg(int dt, int d, const void* q, const void* dout, const float* rowstat, float* rrec, int64_t BH,
-                       int64_t N, SegPlan p, hipStream_t s, int feat) {
+                       int64_t N, SegPlan p, hipStream_t s, int feat, int Gv) {
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_RSEG(TT, DD)                                                                                           \
     if (feat == kFeatGiven)                                                                                       \
         hipLaunchKernelGGL((rseg_kernel<TT, DD, FeatGiven>), grid, dim3(kBlock), 0, s, (const TT*)q,             \
-                           (const TT*)dout, (const float2*)rowstat, rrec, (int)N, p.cps, p.nseg, (int)BH);          \
+                           (const TT*)dout, (const float2*)rowstat, rrec, (int)N, p.cps, p.nseg, (int)BH, Gv);      \
     else                                                                                                         \
         hipLaunchKernelGGL((rseg_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)dout,       \
-                           (const float2*)rowstat, rrec, (int)N, p.cps, p.nseg, (int)BH)
+                           (const float2*)rowstat, rrec, (int)N, p.cps, p.nseg, (int)BH, Gv)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_RSEG(bf16, 32); break;
@@ -798,21 +824,21 @@ hipError_t launch_bwd_fused(int dt, int d, const void* q, const void* k, const v
 
 hipError_t launch_bwd_suffix(int dt, int d, const void* q, const void* k, const void* v, const void* dout, void* dk,
                              void* dv, const float* rowstat, const float* rrec, int64_t BH, int64_t N, SegPlan p,
-                             hipStream_t s, const float* rinit, float* dS0, float* dz0, int feat) {
+                             hipStream_t s, const float* rinit, float* dS0, float* dz0, int feat, int Gv) {
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_BWDS(TT, DD)                                                                                           \
     if (feat == kFeatGiven)                                                                                       \
         hipLaunchKernelGGL((bwd_suffix_kernel<TT, DD, false, FeatGiven>), grid, dim3(kBlock), 0, s, (const TT*)q,  \
                            (const TT*)k, (const TT*)v, (const TT*)dout, (TT*)dk, (TT*)dv, (const float2*)rowstat,   \
-                           rrec, (int)N, p.cps, p.nseg, (int)BH, (int)p.scan, nullptr, nullptr, nullptr);           \
+                           rrec, (int)N, p.cps, p.nseg, (int)BH, (int)p.scan, nullptr, nullptr, nullptr, Gv);       \
     else if (rinit != nullptr || dS0 != nullptr || dz0 != nullptr)                                                \
         hipLaunchKernelGGL((bwd_suffix_kernel<TT, DD, true>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k, \
                            (const TT*)v, (const TT*)dout, (TT*)dk, (TT*)dv, (const float2*)rowstat, rrec, (int)N,  \
-                           p.cps, p.nseg, (int)BH, (int)p.scan, rinit, dS0, dz0);                                    \
+                           p.cps, p.nseg, (int)BH, (int)p.scan, rinit, dS0, dz0, 1);                                 \
     else                                                                                                         \
         hipLaunchKernelGGL((bwd_suffix_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k,    \
                            (const TT*)v, (const TT*)dout, (TT*)dk, (TT*)dv, (const float2*)rowstat, rrec, (int)N,  \
-                           p.cps, p.nseg, (int)BH, (int)p.scan, nullptr, nullptr, nullptr)
+                           p.cps, p.nseg, (int)BH, (int)p.scan, nullptr, nullptr, nullptr, 1)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_BWDS(bf16, 32); break;

@@ -304,15 +304,43 @@ __global__ __launch_bounds__(kBlock) void combine_blocks_kernel(const T* __restr
     float den = 0.f;
     for (int j = 0; j < KF; ++j) {
         const int64_t br = (hh * KF + j) * N + t;
-        const float dj = db[br];
+        const float dj = db != nullptr ? db[br] : 1.f;
         const T* p = ob + br * D + c;
         den += dj;
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] += dj * to_f32(p[e]);
     }
+    if (db == nullptr) {  // a plain sum over the blocks (the value gradient)
+        store4(o + row * D + c, acc);
+        return;
+    }
     const float inv = rcp_f(den);
     store4(o + row * D + c, acc * inv);
     if (den_out != nullptr && c == 0) den_out[row] = den;
+}
+
+// ---------------------------------------------------------------------------------------
+// combine_stats: the backward's row statistics over KF feature blocks that share one
+// normalization.  rowstat [heads][KF][N] holds (den, G . num_j) per block from the
+// statistics sweep (den: the whole head's); every block's entry becomes (den, g) with
+// g = -(sum_j G . num_j) / den, the g of the whole head (same reciprocal as the sweeps).
+__global__ __launch_bounds__(kBlock) void combine_stats_kernel(float2* __restrict__ rowstat, int64_t rows, int64_t N,
+                                                               int KF) {
+    const int64_t row = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (row >= rows) return;
+    const int64_t hh = row / N, t = row - hh * N;
+    float h = 0.f;
+    for (int j = 0; j < KF; ++j) h += rowstat[(hh * KF + j) * N + t].y;
+    const float den = rowstat[hh * KF * N + t].x;
+    const float g = -h * rcp_f(den);
+    for (int j = 0; j < KF; ++j) rowstat[(hh * KF + j) * N + t] = make_float2(den, g);
+}
+
+hipError_t launch_combine_stats(float* rowstat, int64_t rows, int64_t N, int KF, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(combine_stats_kernel, dim3((unsigned)((rows + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
+                       reinterpret_cast<float2*>(rowstat), rows, N, KF);
+    return hipGetLastError();
 }
 
 hipError_t launch_combine_blocks(int dt, int d, const void* ob, const float* db, void* o, float* den_out,

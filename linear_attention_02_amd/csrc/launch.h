@@ -84,11 +84,15 @@ hipError_t launch_noncausal_fwd(int dt, int d, const void* q, void* o, const flo
 hipError_t launch_bwd_prefix(int dt, int d, const void* q, const void* k, const void* v,
                              const void* dout, void* dq, float* rowstat, float* rrec,
                              const float* rec, int64_t BH, int64_t N, SegPlan p, hipStream_t s,
-                             const float* init = nullptr, const float* init_n = nullptr, int feat = kFeatElu);
+                             const float* init = nullptr, const float* init_n = nullptr, int feat = kFeatElu,
+                             int mode = 0, int Gv = 1, const float* den_in = nullptr);
+// mode (given features only): 0 the sweep; 1 statistics (den_in [BH / Gv][N] given, each row's
+// (den, G . num of this head) to rowstat, no dq, no records); 2 from (den, g) in rowstat.
+// Gv: heads per value head (v and dout of head bh / Gv).
 // The backward's per-segment (R, r) records from q, dout and the saved per-row
 // statistics, for head dimensions whose prefix sweep does not form them (d > 64).
 hipError_t launch_rseg(int dt, int d, const void* q, const void* dout, const float* rowstat, float* rrec, int64_t BH,
-                       int64_t N, SegPlan p, hipStream_t s, int feat = kFeatElu);
+                       int64_t N, SegPlan p, hipStream_t s, int feat = kFeatElu, int Gv = 1);
 constexpr bool prefix_forms_records(int d) { return d <= 64; }
 // Default bound on the polls of one wait between workgroups (each poll sleeps
 // about 128 cycles after a coherent load: tens of milliseconds at most).
@@ -105,7 +109,7 @@ hipError_t launch_bwd_suffix(int dt, int d, const void* q, const void* k, const 
                              const void* dout, void* dk, void* dv, const float* rowstat,
                              const float* rrec, int64_t BH, int64_t N, SegPlan p, hipStream_t s,
                              const float* rinit = nullptr, float* dS0 = nullptr, float* dz0 = nullptr,
-                             int feat = kFeatElu);
+                             int feat = kFeatElu, int Gv = 1);
 
 // Non-causal backward.  ncbwd_q: dQ of every row from the head's key state (the
 // in-order sum of `ntotal` records per head at `total`) and each segment's
@@ -143,7 +147,11 @@ hipError_t launch_favor_features_bwd(int dt, int d, const void* x, const float* 
 // out [heads][KF][N][d]; N = 0: one head of all rows.
 // o = sum_j den_j o_j / sum_j den_j over the KF feature blocks of each head (ob
 // [heads][KF][N][d], db [heads][KF][N]); den_out (nullable) gets sum_j den_j.
+// (db null: o = sum_j o_j.)
 hipError_t launch_combine_blocks(int dt, int d, const void* ob, const float* db, void* o, float* den_out,
                                  int64_t rows, int64_t N, int KF, hipStream_t s);
+// Backward row statistics over KF feature blocks: rowstat [heads][KF][N] float2 (den, G . num_j)
+// becomes (den, g) in every block, g = -(sum_j G . num_j) / den.
+hipError_t launch_combine_stats(float* rowstat, int64_t rows, int64_t N, int KF, hipStream_t s);
 
 }  // namespace la
