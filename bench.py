@@ -335,7 +335,19 @@ def bench_calls(args, la, inp, torch, mid_sets):
 
     calls["mid_favor_m128_causal_fwd"] = bench_call("favor_m2", favor_fwd_m2, 100, 400, w.B * w.N,
                                                     4 * unit_bytes(w.B, w.H, w.N, w.d), la, torch, nsets=nsets)
-    del fq, fk, wsf
+    # Its backward on the features (m = 2d): statistics sweep, the head's g, the blocks' sweeps.
+    # Algorithmic bytes: q, k features (2 units each), v, dout read; their gradients written (8 units).
+    _, den2 = la.la_forward_causal_features_blocks(fq, fk, fsets[0][2], return_den=True)
+    g2 = (torch.empty_like(fq), torch.empty_like(fk), torch.empty_like(q0))
+    dos2 = [inp.normal((w.B, w.H, w.N, w.d), inp.generator(60 + s, "cuda"), w.dtype, 1.0, "cuda") for s in range(nsets)]
+    wsb2 = torch.empty(la.features_workspace_size(3, w.B, w.H, w.N, w.d, m, w.dtype), dtype=torch.uint8, device="cuda")
+
+    def favor_bwd_m2(i):
+        la.la_backward_causal_features_blocks(fq, fk, fsets[i][2], dos2[i], den2, out=g2, workspace=wsb2)
+
+    calls["mid_favor_m128_causal_bwd"] = bench_call("favor_m2_bwd", favor_bwd_m2, 100, 400, w.B * w.N,
+                                                    8 * unit_bytes(w.B, w.H, w.N, w.d), la, torch, nsets=nsets)
+    del fq, fk, wsf, den2, g2, dos2, wsb2
 
     # A FAVOR+ training step (m = d): features of q and k, the causal forward on them, its
     # backward on the features, and the gradient through the feature map for q and k.
@@ -540,6 +552,12 @@ def call_oracles(args, inp, torch):
     record("mid_favor_causal_fwd_bwd", favor_train, hs * w.N, w.H, hs,
            f"FAVOR+ features, causal forward and backward, feature-map backward of {hs} Mid heads")
     om2 = f64(inp.favor_omega(w.d, seed=0, m=2 * w.d))
+    def favor_m2_bwd():
+        rfq, rfk = oracle.favor_features(fq, om2), oracle.favor_features(fk, om2)
+        oracle.backward_features(rfq, rfk, fv, fdo, True)
+
+    record("mid_favor_m128_causal_bwd", favor_m2_bwd, hs * w.N, w.H, hs,
+           f"FAVOR+ features (m = 2d) and the causal backward on them, {hs} Mid heads")
     record("mid_favor_m128_causal_fwd",
            lambda: oracle.forward_features(oracle.favor_features(fq, om2), oracle.favor_features(fk, om2), fv, True),
            hs * w.N, w.H, hs, f"FAVOR+ features (m = 2d) + causal forward of {hs} Mid heads")

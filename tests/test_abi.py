@@ -292,3 +292,20 @@ def test_features_backward_validation(lib):
     assert f(x, om, F, dF, F, 64, 64, 1, None) == 1                       # dx aliases F
     assert f(x, om, F, dF, dx, 64, 96, 1, None) == 2                      # d unsupported
     assert f(x, om, F, dF, dx, 0, 64, 1, None) == 0                       # no rows
+
+
+def test_backward_blocks_validation(lib):
+    f = lib.la_backward_causal_features_blocks
+    fq, fk, v, do, den = A, A + 0x1000000, A + 0x2000000, A + 0x2100000, A + 0x2200000
+    dfq, dfk, dv, wsp = A + 0x3000000, A + 0x4000000, A + 0x5000000, A + 0x6000000
+    out = ctypes.c_size_t(0)
+    assert lib.la_features_workspace_size(3, 1, 2, 64, 64, 128, 1, ctypes.byref(out)) == 0
+    assert out.value >= ws(lib, la.LA_OP_BWD_CAUSAL, 1, 4, 64, 64)[1] + 4 * 64 * 64 * 2   # block heads + their dv
+    args = (fq, fk, v, do, den, dfq, dfk, dv)
+    assert f(*args, 1, 2, 64, 64, 96, 1, wsp, 1 << 30, None) == 1                  # m not a multiple of d
+    assert f(*args, 1, 2, 64, 64, 128, 1, wsp, 16, None) == 3                      # workspace too small
+    assert f(*args, 1, 2, 64, 64, 128, 1, None, 0, None) == 3                      # no workspace
+    assert f(fq, fk, v, do, None, dfq, dfk, dv, 1, 2, 64, 64, 128, 1, wsp, 1 << 30, None) == 1  # no den
+    assert f(fq, fk, v, do, den, dfq, dfq + 64, dv, 1, 2, 64, 64, 128, 1, wsp, 1 << 30, None) == 1  # dfk on dfq
+    assert f(*args, 1, 2, 64, 128, 256, 0, wsp, 1 << 30, None) == 2                # fp32 d = 128 not built
+    assert f(*args, 1, 2, 0, 64, 128, 1, None, 0, None) == 0                       # no tokens
