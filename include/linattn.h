@@ -281,11 +281,17 @@ la_status la_favor_features_backward(const void* x, const float* omega, const vo
  * Workspace: la_features_workspace_size(causal != 0, B, H, N, d, m, dt, &bytes), which
  * for KF > 1 holds the blocks' outputs besides the plain call's workspace (causal = 2:
  * the workspace of la_decode_steps_features_blocks with N = T; causal = 3: that of
- * la_backward_causal_features_blocks). */
+ * la_backward_causal_features_blocks; causal = 4: that of la_backward_noncausal_features_blocks). */
 la_status la_features_workspace_size(int causal, int64_t B, int64_t H, int64_t N, int64_t d, int64_t m,
                                      la_dtype dt, size_t* bytes_out);
 la_status la_favor_features_blocks(const void* x, const float* omega, void* out, int64_t heads, int64_t N,
                                    int64_t d, int64_t m, la_dtype dt, void* stream);
+/* The gradient through la_favor_features_blocks: x [heads][N][d], omega [m][d] fp32, F and dF
+ * [heads][KF][N][d] in block layout; dx [heads][N][d] = sum_j (omega_j^T (dF_j * F_j) - x sum(dF_j * F_j))
+ * over the blocks j (the formula of la_favor_features_backward, which is linear in dF_j * F_j). */
+la_status la_favor_features_blocks_backward(const void* x, const float* omega, const void* F, const void* dF,
+                                            void* dx, int64_t heads, int64_t N, int64_t d, int64_t m, la_dtype dt,
+                                            void* stream);
 la_status la_forward_causal_features_blocks(const void* fq, const void* fk, const void* v, void* o,
                                             const float* S0, const float* z0, float* den_out, float* S_out,
                                             float* z_out, int64_t B, int64_t H, int64_t N, int64_t d, int64_t m,
@@ -306,6 +312,17 @@ la_status la_backward_causal_features_blocks(const void* fq, const void* fk, con
                                              const float* den, void* dfq, void* dfk, void* dv, int64_t B,
                                              int64_t H, int64_t N, int64_t d, int64_t m, la_dtype dt,
                                              void* workspace, size_t workspace_bytes, void* stream);
+/* Non-causal backward on m = KF d features (block layout, as la_forward_noncausal_features_blocks):
+ * dfq, dfk [B][H][KF][N][d] and dv [B][H][N][d] of L = sum(dO * O), with den [B][H][N] fp32 the
+ * forward's den_out.  The same derivative of the non-causal form as la_backward_noncausal_features,
+ * with the head's G = dO / den and g = -G . O in every block: a statistics pass gives each row's
+ * G . num_j per block, their sum gives g, then each block's passes give dfq_j, dfk_j and its share
+ * of dv (summed over the blocks).  Workspace: la_features_workspace_size(4, B, H, N, d, m, dt,
+ * &bytes); m = d is la_backward_noncausal_features (den unused). */
+la_status la_backward_noncausal_features_blocks(const void* fq, const void* fk, const void* v, const void* dout,
+                                                const float* den, void* dfq, void* dfk, void* dv, int64_t B,
+                                                int64_t H, int64_t N, int64_t d, int64_t m, la_dtype dt,
+                                                void* workspace, size_t workspace_bytes, void* stream);
 /* Multi-token decode (la_decode_steps_features) on m = KF d features: fq [B][H][KF][T][d]
  * and fk [B][Hkv][KF][T][d] in block layout, v, o as la_decode_steps; the state of key/value
  * head j is S [B][Hkv][m][d], z [B][Hkv][m] (what la_forward_causal_features_blocks leaves

@@ -31,6 +31,8 @@ from ._binding import (  # noqa: F401
     la_decode_steps_features_blocks,
     la_backward_causal_features,
     la_backward_causal_features_blocks,
+    la_backward_noncausal_features_blocks,
+    favor_features_blocks_backward,
     la_backward_noncausal_features,
     favor_features_backward,
     favor_attention,

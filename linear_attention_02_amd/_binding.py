@@ -26,7 +26,8 @@ EXPORTS = ("la_workspace_size", "la_saved_state_size", "la_forward_noncausal", "
            "la_backward_causal_state", "la_forward_causal_grouped", "la_features_workspace_size",
            "la_favor_features_blocks", "la_forward_causal_features_blocks", "la_forward_noncausal_features_blocks",
            "la_decode_steps_features_blocks", "la_backward_causal_features", "la_backward_noncausal_features",
-           "la_favor_features_backward", "la_backward_causal_features_blocks", "la_status_string", "la_last_error_message", "la_version",
+           "la_favor_features_backward", "la_favor_features_blocks_backward", "la_backward_causal_features_blocks",
+           "la_backward_noncausal_features_blocks", "la_status_string", "la_last_error_message", "la_version",
            "la_profile_enable", "la_profile_count", "la_profile_entry", "la_debug_set_wait_limit",
            "la_debug_wait_limit")
 
@@ -76,10 +77,13 @@ def load_library(path: str | None = None):
         f = getattr(lib, name)
         f.restype = i32
         f.argtypes = [vp] * 7 + [i64, i64, i64, i64, i32, vp, sz, vp]
-    lib.la_backward_causal_features_blocks.restype = i32
-    lib.la_backward_causal_features_blocks.argtypes = [vp] * 8 + [i64, i64, i64, i64, i64, i32, vp, sz, vp]
+    for name in ("la_backward_causal_features_blocks", "la_backward_noncausal_features_blocks"):
+        getattr(lib, name).restype = i32
+        getattr(lib, name).argtypes = [vp] * 8 + [i64, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_favor_features_backward.restype = i32
     lib.la_favor_features_backward.argtypes = [vp] * 5 + [i64, i64, i32, vp]
+    lib.la_favor_features_blocks_backward.restype = i32
+    lib.la_favor_features_blocks_backward.argtypes = [vp] * 5 + [i64, i64, i64, i64, i32, vp]
     lib.la_forward_causal_grouped.restype = i32
     lib.la_forward_causal_grouped.argtypes = [vp] * 9 + [i64, i64, i64, i64, i64, i32, i32, vp, sz, vp]
     lib.la_backward_causal_state.restype = i32
@@ -427,7 +431,7 @@ def favor_features_blocks(x, omega, *, out=None):
 
 def features_workspace_size(causal, B, H, N, d, m, dtype):
     out = ctypes.c_size_t(0)
-    kind = causal if causal in (2, 3) else (1 if causal else 0)
+    kind = causal if causal in (2, 3, 4) else (1 if causal else 0)
     _check(load_library().la_features_workspace_size(kind, B, H, N, d, m, _dtype_code(dtype),
                                                      ctypes.byref(out)))
     return out.value
@@ -476,24 +480,35 @@ def la_forward_causal_features_blocks(fq, fk, v, *, return_den=False, return_sta
     return res[0] if len(res) == 1 else tuple(res)
 
 
-def la_backward_causal_features_blocks(fq, fk, v, dout, den, *, out=None, workspace=None):
-    """Causal backward on m = KF d features in block layout fq, fk [B, H, KF, N, d]; den [B, H, N] is the
-    forward's den (return_den=True).  Returns (dfq, dfk) in block layout and dv [B, H, N, d]."""
+def _backward_features_blocks(causal, fq, fk, v, dout, den, out, workspace):
     B, H, N, d, m = _check_blocks(fq, fk, v)
     if dout.shape != v.shape or dout.dtype != v.dtype or not dout.is_contiguous():
         raise ValueError("dout must match v")
     if den.shape != (B, H, N) or den.dtype != torch.float32 or not den.is_contiguous():
         raise ValueError("den must be the forward's contiguous [B, H, N] fp32 denominators")
     g = (torch.empty_like(fq), torch.empty_like(fk), torch.empty_like(v)) if out is None else out
-    need = features_workspace_size(3, B, H, N, d, m, fq.dtype)
+    need = features_workspace_size(3 if causal else 4, B, H, N, d, m, fq.dtype)
     ws = workspace if workspace is not None else (torch.empty(need, dtype=torch.uint8, device=fq.device)
                                                   if need else None)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(load_library().la_backward_causal_features_blocks(_ptr(fq), _ptr(fk), _ptr(v), _ptr(dout), _ptr(den),
-                                                             _ptr(g[0]), _ptr(g[1]), _ptr(g[2]), B, H, N, d, m,
-                                                             _dtype_code(fq.dtype), _ptr(ws), nbytes,
-                                                             _stream(fq.device)))
+    fn = (load_library().la_backward_causal_features_blocks if causal
+          else load_library().la_backward_noncausal_features_blocks)
+    _check(fn(_ptr(fq), _ptr(fk), _ptr(v), _ptr(dout), _ptr(den),
+              _ptr(g[0]), _ptr(g[1]), _ptr(g[2]), B, H, N, d, m, _dtype_code(fq.dtype), _ptr(ws), nbytes,
+              _stream(fq.device)))
     return g
+
+
+def la_backward_causal_features_blocks(fq, fk, v, dout, den, *, out=None, workspace=None):
+    """Causal backward on m = KF d features in block layout fq, fk [B, H, KF, N, d]; den [B, H, N] is the
+    forward's den (return_den=True).  Returns (dfq, dfk) in block layout and dv [B, H, N, d]."""
+    return _backward_features_blocks(True, fq, fk, v, dout, den, out, workspace)
+
+
+def la_backward_noncausal_features_blocks(fq, fk, v, dout, den, *, out=None, workspace=None):
+    """Non-causal backward on m = KF d features in block layout (la_forward_noncausal_features_blocks);
+    den [B, H, N] is that forward's den.  Returns (dfq, dfk) in block layout and dv [B, H, N, d]."""
+    return _backward_features_blocks(False, fq, fk, v, dout, den, out, workspace)
 
 
 def la_forward_noncausal_features_blocks(fq, fk, v, *, return_den=False, out=None, workspace=None):
@@ -571,26 +586,57 @@ def favor_features_backward(x, omega, F, dF, *, out=None):
     return dx
 
 
+def favor_features_blocks_backward(x, omega, F, dF, *, out=None):
+    """The gradient through favor_features_blocks(x, omega) = F [B, H, KF, N, d]: x [B, H, N, d], omega [m, d]."""
+    if x.dim() != 4 or F.dim() != 5:
+        raise ValueError("x must be [B, H, N, d] and F [B, H, KF, N, d]")
+    B, H, N, d = x.shape
+    m = omega.shape[0]
+    if omega.dim() != 2 or omega.shape[1] != d or omega.dtype != torch.float32 or not omega.is_contiguous():
+        raise ValueError("omega must be a contiguous [m, d] fp32 tensor")
+    if m < d or m % d or F.shape != (B, H, m // d, N, d) or dF.shape != F.shape:
+        raise ValueError("F and dF must be [B, H, m // d, N, d]")
+    for t in (x, F, dF):
+        if t.dtype != x.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("x, F and dF must be contiguous HIP tensors of one dtype")
+    dx = torch.empty_like(x) if out is None else out
+    _check(load_library().la_favor_features_blocks_backward(_ptr(x), _ptr(omega), _ptr(F), _ptr(dF), _ptr(dx),
+                                                            B * H, N, d, m, _dtype_code(x.dtype),
+                                                            _stream(x.device)))
+    return dx
+
+
 class _FavorAttention(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, omega, causal):
-        fq, fk = favor_features(q, omega), favor_features(k, omega)
-        o = la_forward_causal_features(fq, fk, v) if causal else la_forward_noncausal_features(fq, fk, v)
-        ctx.save_for_backward(q, k, v, omega, fq, fk)
+        if omega.shape[0] == q.shape[-1]:
+            fq, fk = favor_features(q, omega), favor_features(k, omega)
+            o = la_forward_causal_features(fq, fk, v) if causal else la_forward_noncausal_features(fq, fk, v)
+            den = None
+        else:  # m = KF d features in block layout
+            fq, fk = favor_features_blocks(q, omega), favor_features_blocks(k, omega)
+            fwd = la_forward_causal_features_blocks if causal else la_forward_noncausal_features_blocks
+            o, den = fwd(fq, fk, v, return_den=True)
+        ctx.save_for_backward(q, k, v, omega, fq, fk, den)
         ctx.causal = causal
         return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v, omega, fq, fk = ctx.saved_tensors
-        dfq, dfk, dv = la_backward_causal_features(fq, fk, v, do.contiguous(), causal=ctx.causal)
-        return favor_features_backward(q, omega, fq, dfq), favor_features_backward(k, omega, fk, dfk), dv, None, None
+        q, k, v, omega, fq, fk, den = ctx.saved_tensors
+        if den is None:
+            dfq, dfk, dv = la_backward_causal_features(fq, fk, v, do.contiguous(), causal=ctx.causal)
+            return favor_features_backward(q, omega, fq, dfq), favor_features_backward(k, omega, fk, dfk), dv, None, None
+        bwd = la_backward_causal_features_blocks if ctx.causal else la_backward_noncausal_features_blocks
+        dfq, dfk, dv = bwd(fq, fk, v, do.contiguous(), den)
+        return (favor_features_blocks_backward(q, omega, fq, dfq), favor_features_blocks_backward(k, omega, fk, dfk),
+                dv, None, None)
 
 
 def favor_attention(q, k, v, omega, causal=True):
-    """Performer attention with FAVOR+ features (m = d) as an autograd op: O of linear attention on
-    favor_features(q, omega), favor_features(k, omega); q, k pre-normalized by the caller.
-    Gradients flow to q, k and v through the library's kernels."""
+    """Performer attention with FAVOR+ features as an autograd op: O of linear attention on the
+    features of q and k for omega [m, d] (m a multiple of d; m > d runs in feature blocks);
+    q, k pre-normalized by the caller.  Gradients flow to q, k and v through the library's kernels."""
     return _FavorAttention.apply(q, k, v, omega, causal)
 
 

@@ -608,6 +608,15 @@ la_status la_features_workspace_size(int causal, int64_t B, int64_t H, int64_t N
     if (st != LA_OK) return st;
     bool empty = false;
     if ((st = check_shape(B, H, N, d, 0, dt, &empty)) != LA_OK) return st;
+    if (causal == 4) {  // non-causal backward: the block heads' workspace, their dv, the row statistics
+        const int64_t KF = m / d;
+        if (empty) { *bytes_out = 0; return LA_OK; }
+        const size_t wb = layout(LA_OP_BWD_NONCAUSAL, B, H * KF, N, d).bytes;
+        *bytes_out = KF == 1 ? wb
+                             : align_up(wb) + align_up((size_t)B * H * KF * N * d * elem_size(dt)) +
+                                   align_up((size_t)B * H * KF * N * 2 * sizeof(float));
+        return LA_OK;
+    }
     if (causal == 3) {  // causal backward: the block heads' backward workspace, then their dv
         const int64_t KF = m / d;
         if (empty) { *bytes_out = 0; return LA_OK; }
@@ -643,6 +652,33 @@ la_status la_favor_features_backward(const void* x, const float* omega, const vo
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = timed("favor_features_bwd", s, [&] {
         return la::launch_favor_features_bwd(dt == LA_BF16 ? la::kBF16 : la::kF32, (int)d, x, omega, F, dF, dx, rows, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "favor_features_bwd launch");
+    return LA_OK;
+}
+
+la_status la_favor_features_blocks_backward(const void* x, const float* omega, const void* F, const void* dF,
+                                            void* dx, int64_t heads, int64_t N, int64_t d, int64_t m, la_dtype dt,
+                                            void* stream) {
+    la_status st = check_blocks(d, m);
+    if (st != LA_OK) return st;
+    if (dt != LA_F32 && dt != LA_BF16) return fail(LA_ERR_UNSUPPORTED, "dtype %d is not LA_F32 or LA_BF16", (int)dt);
+    if (d != 32 && d != 64 && d != 128) return fail(LA_ERR_UNSUPPORTED, "d = %lld; built for 32, 64 and 128", (long long)d);
+    if (heads < 0 || N < 0) return fail(LA_ERR_INVALID_ARGUMENT, "negative heads %lld or N %lld", (long long)heads,
+                                        (long long)N);
+    const int64_t rows = heads * N;
+    if (rows > ((int64_t)1 << 40)) return fail(LA_ERR_UNSUPPORTED, "rows = %lld exceeds 2^40", (long long)rows);
+    if (!omega) return fail(LA_ERR_INVALID_ARGUMENT, "omega must be non-NULL");
+    if (rows > 0 && (!x || !F || !dF || !dx)) return fail(LA_ERR_INVALID_ARGUMENT, "x, F, dF and dx must be non-NULL");
+    const size_t xb = (size_t)rows * d * elem_size(dt), fb = xb * (size_t)(m / d);
+    const Range in[] = {{"x", x, xb}, {"omega", omega, (size_t)m * d * sizeof(float)}, {"F", F, fb}, {"dF", dF, fb}};
+    const Range out_r[] = {{"dx", dx, xb}};
+    if ((st = check_ptrs(in, 4, out_r, 1)) != LA_OK) return st;
+    if (rows == 0) return LA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = timed("favor_features_bwd", s, [&] {
+        return la::launch_favor_features_bwd(dt == LA_BF16 ? la::kBF16 : la::kF32, (int)d, x, omega, F, dF, dx, rows, s,
+                                             N, (int)(m / d));
     });
     if (e != hipSuccess) return hip_fail(e, "favor_features_bwd launch");
     return LA_OK;
@@ -959,6 +995,90 @@ la_status la_backward_causal_features_blocks(const void* fq, const void* fk, con
                                           nullptr, nullptr, nullptr, la::kFeatGiven, G);
          })) != hipSuccess)
         return hip_fail(e, "bwd_suffix launch");
+    if ((e = timed("combine_blocks", s, [&] {
+             return la::launch_combine_blocks(idt, (int)d, dvb, nullptr, dv, nullptr, B * H * N, N, G, s);
+         })) != hipSuccess)
+        return hip_fail(e, "combine_blocks launch");
+    return LA_OK;
+}
+
+la_status la_backward_noncausal_features_blocks(const void* fq, const void* fk, const void* v, const void* dout,
+                                                const float* den, void* dfq, void* dfk, void* dv, int64_t B,
+                                                int64_t H, int64_t N, int64_t d, int64_t m, la_dtype dt,
+                                                void* workspace, size_t workspace_bytes, void* stream) {
+    la_status st = check_blocks(d, m);
+    if (st != LA_OK) return st;
+    const int64_t KF = m / d;
+    if (KF == 1)
+        return backward_noncausal(fq, fk, v, dout, dfq, dfk, dv, nullptr, 0, B, H, N, d, dt, workspace,
+                                  workspace_bytes, stream, la::kFeatGiven);
+    bool empty = false;
+    if ((st = check_shape(B, H * KF, N, d, 0, dt, &empty)) != LA_OK) return st;
+    if (dt == LA_F32 && d == 128) return fail(LA_ERR_UNSUPPORTED, "fp32 non-causal backward is built for d = 32 and 64");
+    if (N > 0 && (!fq || !fk || !v || !dout || !den || !dfq || !dfk || !dv))
+        return fail(LA_ERR_INVALID_ARGUMENT, "fq, fk, v, dout, den, dfq, dfk and dv must be non-NULL");
+    const size_t tb = (size_t)B * H * N * d * elem_size(dt), fb = tb * KF;
+    const Range in[] = {{"fq", fq, fb}, {"fk", fk, fb}, {"v", v, tb}, {"dout", dout, tb},
+                        {"den", den, (size_t)B * H * N * sizeof(float)}};
+    const Range out[] = {{"dfq", dfq, fb}, {"dfk", dfk, fb}, {"dv", dv, tb}};
+    if ((st = check_ptrs(in, 5, out, 3)) != LA_OK) return st;
+    if (empty) return LA_OK;
+    const int64_t BHb = B * H * KF;  // block heads
+    const Layout L = layout(LA_OP_BWD_NONCAUSAL, B, H * KF, N, d);
+    const size_t dvb_off = align_up(L.bytes), rs_off = dvb_off + align_up(fb);
+    const size_t need = rs_off + align_up((size_t)BHb * N * 2 * sizeof(float));
+    if (workspace == nullptr) return fail(LA_ERR_WORKSPACE, "workspace is NULL; %zu bytes are needed", need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+        return fail(LA_ERR_INVALID_ARGUMENT, "workspace must be %zu-byte aligned", kAlign);
+    if (workspace_bytes < need)
+        return fail(LA_ERR_WORKSPACE, "workspace has %zu bytes; %zu are needed", workspace_bytes, need);
+    const Range wsr[] = {{"workspace", workspace, need}};
+    if ((st = check_ptrs(in, 5, wsr, 1)) != LA_OK) return st;
+    for (const Range& r : out)
+        if (overlap(wsr[0], r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+    if ((int64_t)L.plan.nseg * BHb > ((int64_t)1 << 24))
+        return fail(LA_ERR_UNSUPPORTED, "%lld workgroups exceed the 2^24 grid limit", (long long)L.plan.nseg * BHb);
+
+    char* ws = static_cast<char*>(workspace);
+    float* total = reinterpret_cast<float*>(ws + L.total);
+    float* rec = reinterpret_cast<float*>(ws + L.rec);
+    float* rrec = reinterpret_cast<float*>(ws + L.rrec);
+    float* rtotal = reinterpret_cast<float*>(ws + L.rtotal);
+    void* dvb = ws + dvb_off;
+    float* rowstat = reinterpret_cast<float*>(ws + rs_off);
+    const int idt = dt == LA_BF16 ? la::kBF16 : la::kF32;
+    const int G = (int)KF;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    // Every block as a head of its own over its head's values and upstream gradient: its key
+    // state, then the rows' G . num of each block with the head's den and G ...
+    if ((e = timed("seg_state", s, [&] {
+             return la::launch_seg_state(idt, (int)d, fk, v, rec, BHb, N, L.plan, s, la::kFeatGiven, G);
+         })) != hipSuccess)
+        return hip_fail(e, "seg_state launch");
+    if ((e = timed("total", s, [&] { return la::launch_total((int)d, rec, total, BHb, L.plan.nseg, s); })) != hipSuccess)
+        return hip_fail(e, "total launch");
+    if ((e = timed("ncbwd_q", s, [&] {
+             return la::launch_ncbwd_q(idt, (int)d, fq, dout, dfq, total, 1, rrec, BHb, N, L.plan, s, la::kFeatGiven,
+                                       1, G, den, rowstat);
+         })) != hipSuccess)
+        return hip_fail(e, "ncbwd_q launch");
+    // ... the head's g = -(sum_j G . num_j) / den for every block ...
+    if ((e = timed("combine_stats", s, [&] { return la::launch_combine_stats(rowstat, B * H * N, N, G, s); })) !=
+        hipSuccess)
+        return hip_fail(e, "combine_stats launch");
+    // ... then each block's passes with the head's (den, g): dfq_j and (R_j, r_j), dfk_j and its share of dv.
+    if ((e = timed("ncbwd_q", s, [&] {
+             return la::launch_ncbwd_q(idt, (int)d, fq, dout, dfq, total, 1, rrec, BHb, N, L.plan, s, la::kFeatGiven,
+                                       2, G, nullptr, rowstat);
+         })) != hipSuccess)
+        return hip_fail(e, "ncbwd_q launch");
+    if ((e = timed("total", s, [&] { return la::launch_total((int)d, rrec, rtotal, BHb, L.plan.nseg, s); })) != hipSuccess)
+        return hip_fail(e, "total launch");
+    if ((e = timed("ncbwd_kv", s, [&] {
+             return la::launch_ncbwd_kv(idt, (int)d, fk, v, dfk, dvb, rtotal, 1, BHb, N, L.plan, s, la::kFeatGiven, G);
+         })) != hipSuccess)
+        return hip_fail(e, "ncbwd_kv launch");
     if ((e = timed("combine_blocks", s, [&] {
              return la::launch_combine_blocks(idt, (int)d, dvb, nullptr, dv, nullptr, B * H * N, N, G, s);
          })) != hipSuccess)

@@ -116,9 +116,14 @@ hipError_t launch_bwd_suffix(int dt, int d, const void* q, const void* k, const 
 // (R, r) record; ncbwd_kv: dK, dV of every key row from the in-order sum of
 // `ntotal` (R, r) records per head at `rtotal`.
 hipError_t launch_ncbwd_q(int dt, int d, const void* q, const void* dout, void* dq, const float* total, int ntotal,
-                          float* rrec, int64_t BH, int64_t N, SegPlan p, hipStream_t s, int feat = kFeatElu);
+                          float* rrec, int64_t BH, int64_t N, SegPlan p, hipStream_t s, int feat = kFeatElu,
+                          int mode = 0, int Gv = 1, const float* den_in = nullptr, float* rowstat = nullptr);
+// mode (given features only): 0 the pass; 1 statistics (den_in [BH / Gv][N] given, each row's
+// (den, G . num of this head) to rowstat [BH][N] float2, no dq, no record); 2 the pass with (den, g)
+// read from rowstat.  Gv: heads per value head (dout of head bh / Gv).
 hipError_t launch_ncbwd_kv(int dt, int d, const void* k, const void* v, void* dk, void* dv, const float* rtotal,
-                           int ntotal, int64_t BH, int64_t N, SegPlan p, hipStream_t s, int feat = kFeatElu);
+                           int ntotal, int64_t BH, int64_t N, SegPlan p, hipStream_t s, int feat = kFeatElu,
+                           int Gv = 1);  // v of head bh / Gv
 
 // Zero-fill n floats with a kernel (no memset node, so the call can sit in a captured graph).
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
@@ -140,9 +145,10 @@ hipError_t launch_decode_steps(int dt, int d, float* S, float* z, const void* q,
 hipError_t launch_favor_features(int dt, int d, const void* x, const float* omega, void* out, int64_t rows,
                                  hipStream_t s, int64_t N = 0, int KF = 1);
 // dx = Omega^T (dF * F) - x sum(dF * F) per row (the gradient through the features F of x,
-// m = d, omega [d][d]).
+// m = d, omega [d][d]).  KF blocks: omega [KF d][d], F and dF [heads][KF][N][d] for x [heads][N][d]
+// (rows = heads x N), dx summed over the blocks.
 hipError_t launch_favor_features_bwd(int dt, int d, const void* x, const float* omega, const void* F, const void* dF,
-                                     void* dx, int64_t rows, hipStream_t s);
+                                     void* dx, int64_t rows, hipStream_t s, int64_t N = 0, int KF = 1);
 // KF feature blocks of rows x [rows][d] (rows = heads x N; omega [KF d][d]) into
 // out [heads][KF][N][d]; N = 0: one head of all rows.
 // o = sum_j den_j o_j / sum_j den_j over the KF feature blocks of each head (ob

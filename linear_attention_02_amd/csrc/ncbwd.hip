@@ -38,11 +38,17 @@ namespace la {
 // in LDS (double-buffered, one barrier per chunk) for the update of (R, r),
 // which contracts over all 64 tokens.
 // FM: the feature map (FeatGiven: phi is the identity and the rank-1 parts vanish).
-template <typename T, int D, class FM = FeatElu>
+// kMode (given features, for heads whose features come in several blocks): 0 the pass
+// above; 1 statistics only: den of every row from den_in (one per value head), and
+// (den, G . num of this block) to rowstat, no dQ and no record; 2 the pass with (den, g)
+// of every row read from rowstat.  dout is read at head bh / Gv.
+template <typename T, int D, class FM = FeatElu, int kMode = 0>
 __global__ __launch_bounds__(kBlock, 2) void ncbwd_q_kernel(const T* __restrict__ q, const T* __restrict__ dout,
                                                          T* __restrict__ dq, const float* __restrict__ total,
                                                          int ntotal, float* __restrict__ rrec, int N, int cps,
-                                                         int nseg, int BH) {
+                                                         int nseg, int BH, int Gv, const float* __restrict__ den_in,
+                                                         float2* __restrict__ rowstat) {
+    static_assert(kMode == 0 || !FM::kSplit, "the statistics modes are built for given features");
     using M = Mma<T>;
     constexpr int KS = M::KSTEP;
     constexpr int DT = D / 16;
@@ -57,7 +63,8 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_q_kernel(const T* __restrict_
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
     const int64_t hoff = (int64_t)bh * N * D;
     const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
-    const GBuf bq(q + hoff, hbytes), bdo(dout + hoff, hbytes), bdq(dq + hoff, hbytes);
+    const int64_t voff = (int64_t)(bh / Gv) * N * D;
+    const GBuf bq(q + hoff, hbytes), bdo(dout + voff, hbytes), bdq(dq + hoff, hbytes);
     const int tok_begin = seg * cps * kC;
     const int tok_end = min(N, tok_begin + cps * kC);
 
@@ -113,7 +120,16 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_q_kernel(const T* __restrict_
             store4(&tQ.at(tl, 16 * m + 4 * g), f32x4{y[4 * m], y[4 * m + 1], y[4 * m + 2], y[4 * m + 3]});
         }
         qs = FM::kSplit ? sum_over_groups(qs) : 0.f;  // no rank-1 parts when unsplit
-        const float den = qs * n + sum_over_groups(zd);
+        float den, gin = 0.f;
+        if constexpr (kMode == 0) {
+            den = qs * n + sum_over_groups(zd);
+        } else if constexpr (kMode == 1) {
+            den = valid ? den_in[(int64_t)(bh / Gv) * N + tok] : 1.f;
+        } else {
+            const float2 rs = valid ? rowstat[(int64_t)bh * N + tok] : float2{1.f, 0.f};
+            den = rs.x;
+            gin = rs.y;
+        }
         const float inv_den = rcp_f(den);
 
         // G = round(dO / den) (staged for the R update) and G.P.
@@ -147,11 +163,19 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_q_kernel(const T* __restrict_
         }
         // g = -(q_sum (G.P) + phi(Q).(S_E G)) / den.
         float s3 = 0.f;
+        if constexpr (kMode != 2) {
 #pragma unroll
-        for (int m = 0; m < DT; ++m)
+            for (int m = 0; m < DT; ++m)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s3 += y[4 * m + e] * accQ[m][e];
-        const float gt = valid ? -(qs * gp + sum_over_groups(s3)) * inv_den : 0.f;
+                for (int e = 0; e < 4; ++e) s3 += y[4 * m + e] * accQ[m][e];
+            s3 = sum_over_groups(s3);
+        }
+        if constexpr (kMode == 1) {
+            // This block's G . num of the row with the head's den.
+            if (g == 0 && valid) rowstat[(int64_t)bh * N + tok] = float2{den, s3};
+            return;
+        }
+        const float gt = kMode == 2 ? (valid ? gin : 0.f) : (valid ? -(qs * gp + s3) * inv_den : 0.f);
         if (g == 0) s_g[buf][tl] = gt;
 
         // dQ = ((S_E G)_a + g z_E[a] + G.P + g N) phi'(Q_a), phi' = min(phi, 1).
@@ -180,6 +204,7 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_q_kernel(const T* __restrict_
             chunk(qb[u], db[u], c0, ci & 1);
         }
     }
+    if constexpr (kMode == 1) return;
     // Record [R^T | r | 0].
     float* rr = rrec + ((int64_t)bh * nseg + seg) * Rec<D>::kSize;
     store_state<D>(rr, stR, lane, w);
@@ -196,7 +221,7 @@ template <typename T, int D, class FM = FeatElu>
 __global__ __launch_bounds__(kBlock, 2) void ncbwd_kv_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                           T* __restrict__ dk, T* __restrict__ dv,
                                                           const float* __restrict__ rtotal, int ntotal, int N,
-                                                          int cps, int nseg, int BH) {
+                                                          int cps, int nseg, int BH, int Gv) {
     using M = Mma<T>;
     constexpr int KS = M::KSTEP;
     constexpr int DT = D / 16;
@@ -209,7 +234,8 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_kv_kernel(const T* __restrict
     const int lane = threadIdx.x & 63, w = wave_id(), g = lane >> 4;
     const int64_t hoff = (int64_t)bh * N * D;
     const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
-    const GBuf bk(k + hoff, hbytes), bv(v + hoff, hbytes), bdk(dk + hoff, hbytes), bdv(dv + hoff, hbytes);
+    const GBuf bk(k + hoff, hbytes), bv(v + (int64_t)(bh / Gv) * N * D, hbytes), bdk(dk + hoff, hbytes),
+        bdv(dv + hoff, hbytes);
     const int tok_begin = seg * cps * kC;
     const int tok_end = min(N, tok_begin + cps * kC);
     {
@@ -296,15 +322,21 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_kv_kernel(const T* __restrict
 
 // ---------------------------------------------------------------------------------------
 hipError_t launch_ncbwd_q(int dt, int d, const void* q, const void* dout, void* dq, const float* total, int ntotal,
-                          float* rrec, int64_t BH, int64_t N, SegPlan p, hipStream_t s, int feat) {
+                          float* rrec, int64_t BH, int64_t N, SegPlan p, hipStream_t s, int feat, int mode, int Gv,
+                          const float* den_in, float* rowstat) {
     const dim3 grid((unsigned)(p.nseg * BH));
+    if (mode != 0 && feat != kFeatGiven) return hipErrorInvalidValue;
+#define LA_NCQ_ARGS(TT) (const TT*)q, (const TT*)dout, (TT*)dq, total, ntotal, rrec, (int)N, p.cps, p.nseg, (int)BH, \
+                        Gv, den_in, reinterpret_cast<float2*>(rowstat)
 #define LA_NCQ(TT, DD)                                                                                            \
-    if (feat == kFeatGiven)                                                                                       \
-        hipLaunchKernelGGL((ncbwd_q_kernel<TT, DD, FeatGiven>), grid, dim3(kBlock), 0, s, (const TT*)q,          \
-                           (const TT*)dout, (TT*)dq, total, ntotal, rrec, (int)N, p.cps, p.nseg, (int)BH);          \
-    else                                                                                                         \
-        hipLaunchKernelGGL((ncbwd_q_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)dout,    \
-                           (TT*)dq, total, ntotal, rrec, (int)N, p.cps, p.nseg, (int)BH)
+    if (feat != kFeatGiven)                                                                                       \
+        hipLaunchKernelGGL((ncbwd_q_kernel<TT, DD>), grid, dim3(kBlock), 0, s, LA_NCQ_ARGS(TT));                 \
+    else if (mode == 1)                                                                                           \
+        hipLaunchKernelGGL((ncbwd_q_kernel<TT, DD, FeatGiven, 1>), grid, dim3(kBlock), 0, s, LA_NCQ_ARGS(TT));   \
+    else if (mode == 2)                                                                                           \
+        hipLaunchKernelGGL((ncbwd_q_kernel<TT, DD, FeatGiven, 2>), grid, dim3(kBlock), 0, s, LA_NCQ_ARGS(TT));   \
+    else                                                                                                          \
+        hipLaunchKernelGGL((ncbwd_q_kernel<TT, DD, FeatGiven>), grid, dim3(kBlock), 0, s, LA_NCQ_ARGS(TT))
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_NCQ(bf16, 32); break;
@@ -320,19 +352,20 @@ hipError_t launch_ncbwd_q(int dt, int d, const void* q, const void* dout, void* 
         }
     }
 #undef LA_NCQ
+#undef LA_NCQ_ARGS
     return hipGetLastError();
 }
 
 hipError_t launch_ncbwd_kv(int dt, int d, const void* k, const void* v, void* dk, void* dv, const float* rtotal,
-                           int ntotal, int64_t BH, int64_t N, SegPlan p, hipStream_t s, int feat) {
+                           int ntotal, int64_t BH, int64_t N, SegPlan p, hipStream_t s, int feat, int Gv) {
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_NCKV(TT, DD)                                                                                           \
     if (feat == kFeatGiven)                                                                                       \
         hipLaunchKernelGGL((ncbwd_kv_kernel<TT, DD, FeatGiven>), grid, dim3(kBlock), 0, s, (const TT*)k,         \
-                           (const TT*)v, (TT*)dk, (TT*)dv, rtotal, ntotal, (int)N, p.cps, p.nseg, (int)BH);          \
+                           (const TT*)v, (TT*)dk, (TT*)dv, rtotal, ntotal, (int)N, p.cps, p.nseg, (int)BH, Gv);      \
     else                                                                                                         \
         hipLaunchKernelGGL((ncbwd_kv_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)k, (const TT*)v,      \
-                           (TT*)dk, (TT*)dv, rtotal, ntotal, (int)N, p.cps, p.nseg, (int)BH)
+                           (TT*)dk, (TT*)dv, rtotal, ntotal, (int)N, p.cps, p.nseg, (int)BH, Gv)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_NCKV(bf16, 32); break;

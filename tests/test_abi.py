@@ -309,3 +309,32 @@ def test_backward_blocks_validation(lib):
     assert f(fq, fk, v, do, den, dfq, dfq + 64, dv, 1, 2, 64, 64, 128, 1, wsp, 1 << 30, None) == 1  # dfk on dfq
     assert f(*args, 1, 2, 64, 128, 256, 0, wsp, 1 << 30, None) == 2                # fp32 d = 128 not built
     assert f(*args, 1, 2, 0, 64, 128, 1, None, 0, None) == 0                       # no tokens
+
+
+def test_backward_noncausal_blocks_validation(lib):
+    f = lib.la_backward_noncausal_features_blocks
+    fq, fk, v, do, den = A, A + 0x1000000, A + 0x2000000, A + 0x2100000, A + 0x2200000
+    dfq, dfk, dv, wsp = A + 0x3000000, A + 0x4000000, A + 0x5000000, A + 0x6000000
+    out = ctypes.c_size_t(0)
+    assert lib.la_features_workspace_size(4, 1, 2, 64, 64, 128, 1, ctypes.byref(out)) == 0
+    # block heads' workspace + their dv + a (den, g) pair per block row
+    assert out.value >= ws(lib, la.LA_OP_BWD_NONCAUSAL, 1, 4, 64, 64)[1] + 4 * 64 * 64 * 2 + 4 * 64 * 8
+    args = (fq, fk, v, do, den, dfq, dfk, dv)
+    assert f(*args, 1, 2, 64, 64, 96, 1, wsp, 1 << 30, None) == 1                  # m not a multiple of d
+    assert f(*args, 1, 2, 64, 64, 128, 1, wsp, out.value - 1, None) == 3           # workspace one byte short
+    assert f(*args, 1, 2, 64, 64, 128, 1, None, 0, None) == 3                      # no workspace
+    assert f(fq, fk, v, do, None, dfq, dfk, dv, 1, 2, 64, 64, 128, 1, wsp, 1 << 30, None) == 1  # no den
+    assert f(fq, fk, v, do, den, dfq, dfk, dfk + 64, 1, 2, 64, 64, 128, 1, wsp, 1 << 30, None) == 1  # dv on dfk
+    assert f(*args, 1, 2, 64, 128, 256, 0, wsp, 1 << 30, None) == 2                # fp32 d = 128 not built
+    assert f(*args, 1, 2, 0, 64, 128, 1, None, 0, None) == 0                       # no tokens
+
+
+def test_favor_features_blocks_backward_validation(lib):
+    f = lib.la_favor_features_blocks_backward
+    x, om, F, dF, dx = A, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x4000000
+    assert f(x, om, F, dF, dx, 2, 64, 64, 96, 1, None) == 1                         # m not a multiple of d
+    assert f(x, None, F, dF, dx, 2, 64, 64, 128, 1, None) == 1                      # no omega
+    assert f(x, om, F, dF, F + 64, 2, 64, 64, 128, 1, None) == 1                    # dx on F
+    assert f(x, om, F, dF, dx, -1, 64, 64, 128, 1, None) == 1                       # negative heads
+    assert f(x, om, F, dF, dx, 2, 64, 48, 96, 1, None) == 2                         # d = 48 not built
+    assert f(x, om, F, dF, dx, 2, 0, 64, 128, 1, None) == 0                         # no rows

@@ -329,15 +329,45 @@ def test_favor_features_backward(la, oracle, d, dtype):
     assert ratio <= 1.0, ratio
 
 
+@pytest.mark.parametrize("KF", [1, 2, 3])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_favor_features_blocks_backward(la, oracle, d, dtype, KF):
+    """dx through m = KF d features in block layout, against the oracle's feature-map gradient
+    over all m features, each element held to the bound of the m = d test with sums of m terms."""
+    B, H, N = 2, 3, 129
+    m = KF * d
+    x = inp.normal((B, H, N, d), inp.generator(d + 17), dtype, d ** -0.25).cuda()
+    om = inp.favor_omega(d, seed=d + 18, m=m).cuda()
+    F = la.favor_features_blocks(x, om)
+    dF = inp.normal((B, H, KF, N, d), inp.generator(d + 19), dtype, 1.0).cuda()
+    dx = la.favor_features_blocks_backward(x, om, F, dF)
+    torch.cuda.synchronize()
+    dFn = from_blocks(f64(dF))
+    ref = oracle.favor_features_backward(f64(x), f64(om), dFn) * math.sqrt(m)
+    refF = oracle.favor_features(f64(x), f64(om)) * math.sqrt(m)
+    xx, oo, g = f64(x), f64(om), np.abs(dFn)
+    fb = feat_bound(refF, x, om, dtype)
+    c = (2.0 ** -16 if dtype == torch.bfloat16 else 0.0) + (m + 2) * 2.0 ** -24
+    bound = (g * fb) @ np.abs(oo) + np.abs(xx) * (g * fb).sum(-1, keepdims=True)
+    bound += c * ((g * refF) @ np.abs(oo) + np.abs(xx) * (g * refF).sum(-1, keepdims=True))
+    bound += (2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -24) * np.abs(ref)
+    ratio = float((np.abs(f64(dx) - ref) / bound).max())
+    record(f"favor_features_blocks_bwd d={d} m={m} {dtype}", ratio=ratio)
+    assert ratio <= 1.0, ratio
+
+
+@pytest.mark.parametrize("KF", [1, 2])
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
-def test_favor_attention_autograd(la, oracle, dtype, causal):
+def test_favor_attention_autograd(la, oracle, dtype, causal, KF):
     """Performer attention trained end to end: O and dq, dk, dv of the autograd op against the
     oracle's chain (features, attention on features, its backward, the feature map's backward);
-    the constant 1/sqrt(m) the library leaves out changes none of them."""
+    the constant 1/sqrt(m) the library leaves out changes none of them.  KF = 2: m = 2d
+    features, run in feature blocks."""
     B, H, N, d = 2, 3, 333, 64
     q, k, v, do = (t.cuda() for t in inp.favor_qkv(B, H, N, d, dtype, seed=100, with_dout=True))
-    om = inp.favor_omega(d, seed=101).cuda()
+    om = inp.favor_omega(d, seed=101, m=KF * d).cuda()
     q.requires_grad_(True)
     k.requires_grad_(True)
     v.requires_grad_(True)
@@ -351,7 +381,7 @@ def test_favor_attention_autograd(la, oracle, dtype, causal):
     rdk = oracle.favor_features_backward(f64(k), f64(om), dfk)
     errs = {"o": slice_err(o, ro), "dq": slice_err(q.grad, rdq), "dk": slice_err(k.grad, rdk),
             "dv": slice_err(v.grad, rdv)}
-    record(f"favor_attention autograd {'causal' if causal else 'noncausal'} {dtype}", **errs)
+    record(f"favor_attention autograd {'causal' if causal else 'noncausal'} m={KF * d} {dtype}", **errs)
     assert max(errs.values()) < TOL[dtype], errs
 
 
@@ -361,25 +391,30 @@ def from_blocks(f):
     return np.moveaxis(f, -3, -2).reshape(*lead, N, KF * d)
 
 
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("shape", [(2, 3, 200, 64, 2), (1, 2, 300, 128, 2), (2, 2, 1000, 64, 4),
                                    (1, 2, 257, 32, 3), (1, 4, 64 * 130 + 17, 64, 2)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_favor_backward_blocks(la, oracle, shape, dtype):
-    """The causal backward on m = KF d features (every block with the head's G and g) against
+def test_favor_backward_blocks(la, oracle, shape, dtype, causal):
+    """The causal and non-causal backward on m = KF d features (every block with the head's G and g) against
     the oracle's backward on all m features at once, on the library's own features."""
     B, H, N, d, KF = shape
     m = KF * d
     if dtype == torch.float32 and d == 128:
-        pytest.skip("fp32 causal path is built for d <= 64")
+        pytest.skip("fp32 backward is built for d <= 64")
     q, k, v, do = (t.cuda() for t in inp.favor_qkv(B, H, N, d, dtype, seed=N + 110, with_dout=True))
     om = inp.favor_omega(d, seed=N + 111, m=m).cuda()
     fq, fk = la.favor_features_blocks(q, om), la.favor_features_blocks(k, om)
-    _, den = la.la_forward_causal_features_blocks(fq, fk, v, return_den=True)
-    dfq, dfk, dv = la.la_backward_causal_features_blocks(fq, fk, v, do, den)
+    if causal:
+        _, den = la.la_forward_causal_features_blocks(fq, fk, v, return_den=True)
+        dfq, dfk, dv = la.la_backward_causal_features_blocks(fq, fk, v, do, den)
+    else:
+        _, den = la.la_forward_noncausal_features_blocks(fq, fk, v, return_den=True)
+        dfq, dfk, dv = la.la_backward_noncausal_features_blocks(fq, fk, v, do, den)
     torch.cuda.synchronize()
-    rdfq, rdfk, rdv = oracle.backward_features(from_blocks(f64(fq)), from_blocks(f64(fk)), f64(v), f64(do), True)
+    rdfq, rdfk, rdv = oracle.backward_features(from_blocks(f64(fq)), from_blocks(f64(fk)), f64(v), f64(do), causal)
     errs = {"dfq": slice_err(dfq, to_blocks(rdfq, KF)), "dfk": slice_err(dfk, to_blocks(rdfk, KF)),
             "dv": slice_err(dv, rdv)}
-    record(f"favor_bwd_blocks {B}x{H}x{N}x{d} m={m} {dtype}", **errs)
+    record(f"favor_bwd_blocks {'causal' if causal else 'noncausal'} {B}x{H}x{N}x{d} m={m} {dtype}", **errs)
     assert max(errs.values()) < TOL[dtype], errs
