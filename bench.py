@@ -347,7 +347,28 @@ def bench_calls(args, la, inp, torch, mid_sets):
 
     calls["mid_favor_m128_causal_bwd"] = bench_call("favor_m2_bwd", favor_bwd_m2, 100, 400, w.B * w.N,
                                                     8 * unit_bytes(w.B, w.H, w.N, w.d), la, torch, nsets=nsets)
-    del fq, fk, wsf, den2, g2, dos2, wsb2
+    # A non-causal FAVOR+ training step with m = 2d: block features of q and k, the forward, its
+    # backward on the features, the feature map's backward.  Algorithmic bytes: the 8 units of the
+    # attention's own inputs and gradients (q, k, v, dout read; o, dq, dk, dv written).
+    wsn = torch.empty(la.features_workspace_size(False, w.B, w.H, w.N, w.d, m, w.dtype), dtype=torch.uint8,
+                      device="cuda")
+    wsn_b = torch.empty(la.features_workspace_size(4, w.B, w.H, w.N, w.d, m, w.dtype), dtype=torch.uint8,
+                        device="cuda")
+    dq2, dk2 = torch.empty_like(q0), torch.empty_like(q0)
+
+    def favor_train_nc_m2(i):
+        q, k, v = fsets[i]
+        la.favor_features_blocks(q, om2, out=fq)
+        la.favor_features_blocks(k, om2, out=fk)
+        la.la_forward_noncausal_features_blocks(fq, fk, v, out=o, workspace=wsn, den_out=den2)
+        la.la_backward_noncausal_features_blocks(fq, fk, v, dos2[i], den2, out=g2, workspace=wsn_b)
+        la.favor_features_blocks_backward(q, om2, fq, g2[0], out=dq2)
+        la.favor_features_blocks_backward(k, om2, fk, g2[1], out=dk2)
+
+    calls["mid_favor_m128_noncausal_fwd_bwd"] = bench_call("favor_m2_nc_train", favor_train_nc_m2, 50, 200, w.B * w.N,
+                                                           8 * unit_bytes(w.B, w.H, w.N, w.d), la, torch,
+                                                           nsets=nsets)
+    del fq, fk, wsf, den2, g2, dos2, wsb2, wsn, wsn_b, dq2, dk2
 
     # A FAVOR+ training step (m = d): features of q and k, the causal forward on them, its
     # backward on the features, and the gradient through the feature map for q and k.
@@ -558,6 +579,16 @@ def call_oracles(args, inp, torch):
 
     record("mid_favor_m128_causal_bwd", favor_m2_bwd, hs * w.N, w.H, hs,
            f"FAVOR+ features (m = 2d) and the causal backward on them, {hs} Mid heads")
+
+    def favor_m2_nc_train():
+        rfq, rfk = oracle.favor_features(fq, om2), oracle.favor_features(fk, om2)
+        oracle.forward_features(rfq, rfk, fv, False)
+        gq, gk, _ = oracle.backward_features(rfq, rfk, fv, fdo, False)
+        oracle.favor_features_backward(fq, om2, gq)
+        oracle.favor_features_backward(fk, om2, gk)
+
+    record("mid_favor_m128_noncausal_fwd_bwd", favor_m2_nc_train, hs * w.N, w.H, hs,
+           f"FAVOR+ features (m = 2d), non-causal forward and backward, feature-map backward of {hs} Mid heads")
     record("mid_favor_m128_causal_fwd",
            lambda: oracle.forward_features(oracle.favor_features(fq, om2), oracle.favor_features(fk, om2), fv, True),
            hs * w.N, w.H, hs, f"FAVOR+ features (m = 2d) + causal forward of {hs} Mid heads")

@@ -511,11 +511,16 @@ def la_backward_noncausal_features_blocks(fq, fk, v, dout, den, *, out=None, wor
     return _backward_features_blocks(False, fq, fk, v, dout, den, out, workspace)
 
 
-def la_forward_noncausal_features_blocks(fq, fk, v, *, return_den=False, out=None, workspace=None):
-    """Non-causal forward on m = KF d features in block layout fq, fk [B, H, KF, N, d]."""
+def la_forward_noncausal_features_blocks(fq, fk, v, *, return_den=False, out=None, workspace=None, den_out=None):
+    """Non-causal forward on m = KF d features in block layout fq, fk [B, H, KF, N, d]; den_out
+    (optional, [B, H, N] fp32) receives the denominators."""
     B, H, N, d, m = _check_blocks(fq, fk, v)
     o = torch.empty_like(v) if out is None else out
-    den = torch.empty((B, H, N), dtype=torch.float32, device=fq.device) if return_den else None
+    if den_out is not None and (den_out.shape != (B, H, N) or den_out.dtype != torch.float32
+                                or not den_out.is_contiguous()):
+        raise ValueError("den_out must be a contiguous [B, H, N] fp32 tensor")
+    den = den_out if den_out is not None else (
+        torch.empty((B, H, N), dtype=torch.float32, device=fq.device) if return_den else None)
     need = features_workspace_size(False, B, H, N, d, m, fq.dtype)
     ws = workspace if workspace is not None else (torch.empty(need, dtype=torch.uint8, device=fq.device)
                                                   if need else None)

@@ -156,15 +156,11 @@ hipError_t launch_favor_features(int dt, int d, const void* x, const float* omeg
 // bits, so u = u_hi + u_lo exactly in bf16, Omega is split the same way, and three
 // bf16 MFMAs (hi hi, hi lo, lo hi) give the product to about 2^-16 relative; fp32 rows
 // use the fp32 MFMA.  One workgroup takes CPB chunks of 64 rows.
-// KF feature blocks (m = KF d; omega [KF d][d], F and dF [heads][KF][N][d] for x [heads][N][d]):
-// the map is linear in u, so dx = sum_j (Omega_j^T u_j - x sum(u_j)); each chunk walks the
-// blocks with Omega_j restaged per block, and the MFMA accumulators and row sums carry over.
 template <typename T, int D>
 __global__ __launch_bounds__(kBlock) void favor_features_bwd_kernel(const T* __restrict__ x,
                                                                     const float* __restrict__ omega,
                                                                     const T* __restrict__ F, const T* __restrict__ dF,
-                                                                    T* __restrict__ dx, int64_t rows, int64_t N,
-                                                                    int KF) {
+                                                                    T* __restrict__ dx, int64_t rows) {
     constexpr bool kBF = sizeof(T) == 2;
     using M = Mma<T>;
     constexpr int DT = D / 16;
@@ -178,36 +174,24 @@ __global__ __launch_bounds__(kBlock) void favor_features_bwd_kernel(const T* __r
     __shared__ float s_s[kC];
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
 
-    auto stage_omega = [&](int jb) {
-        const f32x4* ob = reinterpret_cast<const f32x4*>(omega + (int64_t)jb * D * D);
-        for (int i = tid; i < D * D / 4; i += kBlock) {
-            const int r = (4 * i) / D, c = (4 * i) % D;
-            const f32x4 om = ob[i];
-            if constexpr (kBF) {
-                f32x4 hi;
+    for (int i = tid; i < D * D / 4; i += kBlock) {
+        const int r = (4 * i) / D, c = (4 * i) % D;
+        const f32x4 om = reinterpret_cast<const f32x4*>(omega)[i];
+        if constexpr (kBF) {
+            f32x4 hi;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) hi[e] = (float)(bf16)om[e];
-                store4(&Tile<T, D, D>{s_om[0]}.at(r, c), hi);
-                store4(&Tile<T, D, D>{s_om[kBF ? 1 : 0]}.at(r, c), om - hi);
-            } else {
-                store4(&Tile<T, D, D>{s_om[0]}.at(r, c), om);
-            }
+            for (int e = 0; e < 4; ++e) hi[e] = (float)(bf16)om[e];
+            store4(&Tile<T, D, D>{s_om[0]}.at(r, c), hi);
+            store4(&Tile<T, D, D>{s_om[kBF ? 1 : 0]}.at(r, c), om - hi);
+        } else {
+            store4(&Tile<T, D, D>{s_om[0]}.at(r, c), om);
         }
-    };
-    if (KF == 1) stage_omega(0);
+    }
     const int64_t base = (int64_t)blockIdx.x * CPB * kC;
-    bool first = true;
     for (int cb = 0; cb < CPB; ++cb) {
         const int64_t r0 = base + (int64_t)cb * kC;
         if (r0 >= rows) break;
-        // acc[m]: [feature 16 m + 4 g + e][row 16 w + (lane & 15)] of sum_j Omega_j^T u_j.
-        f32x4 acc[DT];
-#pragma unroll
-        for (int m = 0; m < DT; ++m) acc[m] = zero4();
-      for (int jb = 0; jb < KF; ++jb) {
-        if (!first) __syncthreads();  // every wave has read the previous u (and Omega block)
-        first = false;
-        if (KF > 1) stage_omega(jb);
+        if (cb > 0) __syncthreads();  // every wave has read the previous chunk's u
         // u = dF * F of this thread's groups of 4, split hi + lo, and the row sums of u.
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
@@ -216,10 +200,8 @@ __global__ __launch_bounds__(kBlock) void favor_features_bwd_kernel(const T* __r
             const int64_t row = r0 + rr;
             word fw{}, gw{};
             if (row < rows) {
-                const int64_t hh = KF == 1 ? 0 : row / N;
-                const int64_t frow = KF == 1 ? row : (hh * KF + jb) * N + (row - hh * N);
-                fw = *reinterpret_cast<const word*>(F + frow * D + c);
-                gw = *reinterpret_cast<const word*>(dF + frow * D + c);
+                fw = *reinterpret_cast<const word*>(F + row * D + c);
+                gw = *reinterpret_cast<const word*>(dF + row * D + c);
             }
             const T* fh = reinterpret_cast<const T*>(&fw);
             const T* gh = reinterpret_cast<const T*>(&gw);
@@ -240,9 +222,13 @@ __global__ __launch_bounds__(kBlock) void favor_features_bwd_kernel(const T* __r
                 store4(&Tile<T, kC, D>{s_u[0]}.at(rr, c), u);
             }
             su = sum_lanes<TPR>(su);
-            if (c == 0) s_s[rr] = jb == 0 ? su : s_s[rr] + su;
+            if (c == 0) s_s[rr] = su;
         }
-        __syncthreads();  // u, the row sums and the Omega block staged
+        __syncthreads();  // u and its row sums staged (and omega, for the first chunk)
+        // acc[m]: [feature 16 m + 4 g + e][row 16 w + (lane & 15)] of Omega^T u.
+        f32x4 acc[DT];
+#pragma unroll
+        for (int m = 0; m < DT; ++m) acc[m] = zero4();
 #pragma unroll
         for (int k0 = 0; k0 < D; k0 += M::KSTEP) {
             const typename M::frag uh = M::ld(Tile<T, kC, D>{s_u[0]}, 16 * w, k0, lane);
@@ -257,7 +243,6 @@ __global__ __launch_bounds__(kBlock) void favor_features_bwd_kernel(const T* __r
                 }
             }
         }
-      }
         const int t = 16 * w + (lane & 15);
         const int64_t row = r0 + t;
         if (row < rows) {
@@ -274,14 +259,139 @@ __global__ __launch_bounds__(kBlock) void favor_features_bwd_kernel(const T* __r
     }
 }
 
+// KF feature blocks (m = KF d; omega [KF d][d], F and dF [heads][KF][N][d] for x [heads][N][d]):
+// the map is linear in u, so dx = sum_j (Omega_j^T u_j - x sum(u_j)).  Blocks are the outer
+// loop, so each Omega_j is staged once per workgroup; the MFMA accumulators and row sums of
+// the workgroup's BCPB chunks carry over the blocks.  Omega and u as in the kernel above.
+template <int D>
+constexpr int favor_bwd_blocks_cpb() { return D > 64 ? 1 : 4; }
+template <typename T, int D>
+__global__ __launch_bounds__(kBlock) void favor_features_bwd_blocks_kernel(
+    const T* __restrict__ x, const float* __restrict__ omega, const T* __restrict__ F, const T* __restrict__ dF,
+    T* __restrict__ dx, int64_t rows, int64_t N, int KF) {
+    constexpr bool kBF = sizeof(T) == 2;
+    using M = Mma<T>;
+    constexpr int DT = D / 16;
+    constexpr int CPB = favor_bwd_blocks_cpb<D>();
+    constexpr int TPR = D / 4;
+    constexpr int NI = kC * TPR / kBlock;
+    static_assert(NI >= 1 && kC * TPR % kBlock == 0 && TPR <= kWave, "rows must tile the workgroup");
+    typedef typename std::conditional<kBF, uint2, uint4>::type word;
+    __shared__ __attribute__((aligned(16))) T s_om[kBF ? 2 : 1][D * D];
+    __shared__ __attribute__((aligned(16))) T s_u[kBF ? 2 : 1][kC * D];
+    __shared__ float s_s[CPB][kC];
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
+    const int64_t base = (int64_t)blockIdx.x * CPB * kC;
+
+    f32x4 acc[CPB][DT];
+#pragma unroll
+    for (int cb = 0; cb < CPB; ++cb)
+#pragma unroll
+        for (int m = 0; m < DT; ++m) acc[cb][m] = zero4();
+    for (int jb = 0; jb < KF; ++jb) {
+        if (jb > 0) __syncthreads();  // every wave has read Omega_{j-1} and the last u
+        const f32x4* ob = reinterpret_cast<const f32x4*>(omega + (int64_t)jb * D * D);
+        for (int i = tid; i < D * D / 4; i += kBlock) {
+            const int r = (4 * i) / D, c = (4 * i) % D;
+            const f32x4 om = ob[i];
+            if constexpr (kBF) {
+                f32x4 hi;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hi[e] = (float)(bf16)om[e];
+                store4(&Tile<T, D, D>{s_om[0]}.at(r, c), hi);
+                store4(&Tile<T, D, D>{s_om[kBF ? 1 : 0]}.at(r, c), om - hi);
+            } else {
+                store4(&Tile<T, D, D>{s_om[0]}.at(r, c), om);
+            }
+        }
+#pragma unroll
+        for (int cb = 0; cb < CPB; ++cb) {
+            const int64_t r0 = base + (int64_t)cb * kC;
+            if (r0 >= rows) break;
+            if (cb > 0) __syncthreads();  // every wave has read the previous chunk's u
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                const int i = tid + kBlock * j;
+                const int rr = (4 * i) / D, c = (4 * i) % D;
+                const int64_t row = r0 + rr;
+                word fw{}, gw{};
+                if (row < rows) {
+                    const int64_t hh = row / N;
+                    const int64_t frow = (hh * KF + jb) * N + (row - hh * N);
+                    fw = *reinterpret_cast<const word*>(F + frow * D + c);
+                    gw = *reinterpret_cast<const word*>(dF + frow * D + c);
+                }
+                const T* fh = reinterpret_cast<const T*>(&fw);
+                const T* gh = reinterpret_cast<const T*>(&gw);
+                f32x4 u;
+                float su = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    u[e] = to_f32(fh[e]) * to_f32(gh[e]);
+                    su += u[e];
+                }
+                if constexpr (kBF) {
+                    f32x4 hi;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) hi[e] = (float)(bf16)u[e];
+                    store4(&Tile<T, kC, D>{s_u[0]}.at(rr, c), hi);
+                    store4(&Tile<T, kC, D>{s_u[kBF ? 1 : 0]}.at(rr, c), u - hi);
+                } else {
+                    store4(&Tile<T, kC, D>{s_u[0]}.at(rr, c), u);
+                }
+                su = sum_lanes<TPR>(su);
+                if (c == 0) s_s[cb][rr] = jb == 0 ? su : s_s[cb][rr] + su;
+            }
+            __syncthreads();  // u, its row sums and Omega_j staged
+#pragma unroll
+            for (int k0 = 0; k0 < D; k0 += M::KSTEP) {
+                const typename M::frag uh = M::ld(Tile<T, kC, D>{s_u[0]}, 16 * w, k0, lane);
+#pragma unroll
+                for (int m = 0; m < DT; ++m) {
+                    const typename M::frag oh = M::ld_tr(Tile<T, D, D>{s_om[0]}, k0, 16 * m, lane);
+                    acc[cb][m] = M::mma(oh, uh, acc[cb][m]);
+                    if constexpr (kBF) {
+                        const typename M::frag ul = M::ld(Tile<T, kC, D>{s_u[kBF ? 1 : 0]}, 16 * w, k0, lane);
+                        acc[cb][m] = M::mma(oh, ul, acc[cb][m]);
+                        acc[cb][m] =
+                            M::mma(M::ld_tr(Tile<T, D, D>{s_om[kBF ? 1 : 0]}, k0, 16 * m, lane), uh, acc[cb][m]);
+                    }
+                }
+            }
+        }
+    }
+    // s_s of the last block was written before the last barrier; each row's own lanes read it.
+#pragma unroll
+    for (int cb = 0; cb < CPB; ++cb) {
+        const int t = 16 * w + (lane & 15);
+        const int64_t row = base + (int64_t)cb * kC + t;
+        if (row < rows) {
+            const float su = s_s[cb][t];
+#pragma unroll
+            for (int m = 0; m < DT; ++m) {
+                const int c = 16 * m + 4 * g;
+                f32x4 y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = acc[cb][m][e] - su * to_f32(x[row * D + c + e]);
+                store4(dx + row * D + c, y);
+            }
+        }
+    }
+}
+
 hipError_t launch_favor_features_bwd(int dt, int d, const void* x, const float* omega, const void* F, const void* dF,
                                      void* dx, int64_t rows, hipStream_t s, int64_t N, int KF) {
     if (KF < 1 || (KF > 1 && N <= 0)) return hipErrorInvalidValue;
     if (rows == 0) return hipSuccess;
-    const dim3 grid((unsigned)((rows + 4 * kC - 1) / (4 * kC)));
-#define LA_FAVB(TT, DD)                                                                                       \
-    hipLaunchKernelGGL((favor_features_bwd_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)x, omega,     \
-                       (const TT*)F, (const TT*)dF, (TT*)dx, rows, N, KF)
+    const int cpb = KF == 1 ? 4 : (d > 64 ? favor_bwd_blocks_cpb<128>() : favor_bwd_blocks_cpb<64>());
+    const dim3 grid((unsigned)((rows + cpb * kC - 1) / (cpb * kC)));
+#define LA_FAVB(TT, DD)                                                                                         \
+    if (KF > 1)                                                                                                 \
+        hipLaunchKernelGGL((favor_features_bwd_blocks_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)x,  \
+                           omega, (const TT*)F, (const TT*)dF, (TT*)dx, rows, N, KF);                           \
+    else                                                                                                        \
+        hipLaunchKernelGGL((favor_features_bwd_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)x, omega,  \
+                           (const TT*)F, (const TT*)dF, (TT*)dx, rows)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_FAVB(bf16, 32); break;
