@@ -188,6 +188,25 @@ __global__ __launch_bounds__(kBlock) void favor_features_bwd_kernel(const T* __r
         }
     }
     const int64_t base = (int64_t)blockIdx.x * CPB * kC;
+    // F and dF words of chunk cb for this thread's groups of 4 (zeros past the rows); the next
+    // chunk's are loaded while the current chunk's MFMAs run.
+    word pf[NI], pg[NI];
+    auto load_chunk = [&](int cb) {
+        const int64_t r0 = base + (int64_t)cb * kC;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int i = tid + kBlock * j;
+            const int64_t row = r0 + (4 * i) / D;
+            pf[j] = word{};
+            pg[j] = word{};
+            if (row < rows) {
+                pf[j] = *reinterpret_cast<const word*>(F + row * D + (4 * i) % D);
+                pg[j] = *reinterpret_cast<const word*>(dF + row * D + (4 * i) % D);
+            }
+        }
+    };
+    load_chunk(0);
+#pragma unroll
     for (int cb = 0; cb < CPB; ++cb) {
         const int64_t r0 = base + (int64_t)cb * kC;
         if (r0 >= rows) break;
@@ -197,12 +216,7 @@ __global__ __launch_bounds__(kBlock) void favor_features_bwd_kernel(const T* __r
         for (int j = 0; j < NI; ++j) {
             const int i = tid + kBlock * j;
             const int rr = (4 * i) / D, c = (4 * i) % D;
-            const int64_t row = r0 + rr;
-            word fw{}, gw{};
-            if (row < rows) {
-                fw = *reinterpret_cast<const word*>(F + row * D + c);
-                gw = *reinterpret_cast<const word*>(dF + row * D + c);
-            }
+            const word fw = pf[j], gw = pg[j];
             const T* fh = reinterpret_cast<const T*>(&fw);
             const T* gh = reinterpret_cast<const T*>(&gw);
             f32x4 u;
@@ -224,7 +238,8 @@ __global__ __launch_bounds__(kBlock) void favor_features_bwd_kernel(const T* __r
             su = sum_lanes<TPR>(su);
             if (c == 0) s_s[rr] = su;
         }
-        __syncthreads();  // u and its row sums staged (and omega, for the first chunk)
+        if (cb + 1 < CPB && r0 + kC < rows) load_chunk(cb + 1);
+        raw_barrier();  // u and its row sums staged (and omega, for the first chunk); loads stay in flight
         // acc[m]: [feature 16 m + 4 g + e][row 16 w + (lane & 15)] of Omega^T u.
         f32x4 acc[DT];
 #pragma unroll
@@ -262,7 +277,9 @@ __global__ __launch_bounds__(kBlock) void favor_features_bwd_kernel(const T* __r
 // KF feature blocks (m = KF d; omega [KF d][d], F and dF [heads][KF][N][d] for x [heads][N][d]):
 // the map is linear in u, so dx = sum_j (Omega_j^T u_j - x sum(u_j)).  Blocks are the outer
 // loop, so each Omega_j is staged once per workgroup; the MFMA accumulators and row sums of
-// the workgroup's BCPB chunks carry over the blocks.  Omega and u as in the kernel above.
+// the workgroup's CPB chunks carry over the blocks.  The F and dF words of the next (block,
+// chunk) step are loaded into registers while the current step's MFMAs run.  Omega and u
+// as in the kernel above.
 template <int D>
 constexpr int favor_bwd_blocks_cpb() { return D > 64 ? 1 : 4; }
 template <typename T, int D>
@@ -282,6 +299,27 @@ __global__ __launch_bounds__(kBlock) void favor_features_bwd_blocks_kernel(
     __shared__ float s_s[CPB][kC];
     const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), g = lane >> 4;
     const int64_t base = (int64_t)blockIdx.x * CPB * kC;
+
+    // F and dF words of step (jb, cb) for this thread's groups of 4 (zeros past the rows).
+    word pf[NI], pg[NI];
+    auto load_step = [&](int jb, int cb) {
+        const int64_t r0 = base + (int64_t)cb * kC;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int i = tid + kBlock * j;
+            const int rr = (4 * i) / D, c = (4 * i) % D;
+            const int64_t row = r0 + rr;
+            pf[j] = word{};
+            pg[j] = word{};
+            if (row < rows) {
+                const int64_t hh = row / N;
+                const int64_t frow = (hh * KF + jb) * N + (row - hh * N);
+                pf[j] = *reinterpret_cast<const word*>(F + frow * D + c);
+                pg[j] = *reinterpret_cast<const word*>(dF + frow * D + c);
+            }
+        }
+    };
+    load_step(0, 0);
 
     f32x4 acc[CPB][DT];
 #pragma unroll
@@ -313,14 +351,7 @@ __global__ __launch_bounds__(kBlock) void favor_features_bwd_blocks_kernel(
             for (int j = 0; j < NI; ++j) {
                 const int i = tid + kBlock * j;
                 const int rr = (4 * i) / D, c = (4 * i) % D;
-                const int64_t row = r0 + rr;
-                word fw{}, gw{};
-                if (row < rows) {
-                    const int64_t hh = row / N;
-                    const int64_t frow = (hh * KF + jb) * N + (row - hh * N);
-                    fw = *reinterpret_cast<const word*>(F + frow * D + c);
-                    gw = *reinterpret_cast<const word*>(dF + frow * D + c);
-                }
+                const word fw = pf[j], gw = pg[j];
                 const T* fh = reinterpret_cast<const T*>(&fw);
                 const T* gh = reinterpret_cast<const T*>(&gw);
                 f32x4 u;
@@ -342,7 +373,12 @@ __global__ __launch_bounds__(kBlock) void favor_features_bwd_blocks_kernel(
                 su = sum_lanes<TPR>(su);
                 if (c == 0) s_s[cb][rr] = jb == 0 ? su : s_s[cb][rr] + su;
             }
-            __syncthreads();  // u, its row sums and Omega_j staged
+            // The next step's words: the next chunk of this block, else the first chunk of the next block.
+            if (cb + 1 < CPB && r0 + kC < rows)
+                load_step(jb, cb + 1);
+            else if (jb + 1 < KF)
+                load_step(jb + 1, 0);
+            raw_barrier();  // u, its row sums and Omega_j staged (the next step's loads stay in flight)
 #pragma unroll
             for (int k0 = 0; k0 < D; k0 += M::KSTEP) {
                 const typename M::frag uh = M::ld(Tile<T, kC, D>{s_u[0]}, 16 * w, k0, lane);
