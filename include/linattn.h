@@ -362,7 +362,7 @@ int la_debug_wait_limit(void);
  * synchronises on its stop event and returns the kernel's name ("seg_state",
  * "total", "scan", "causal_fwd", "noncausal_fwd", "bwd_prefix", "rseg", "rscan",
  * "bwd_suffix", "bwd_fused", "ncbwd_q", "ncbwd_kv", "decode", "decode_steps",
- * "state_split", "favor_features", "favor_features_bwd", "combine_blocks", "fill_zero") and
+ * "state_split", "favor_features", "favor_features_bwd", "combine_blocks", "combine_stats", "fill_zero") and
  * its duration in milliseconds. */
 la_status la_profile_enable(int on);
 int la_profile_count(void);
