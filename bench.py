@@ -335,15 +335,15 @@ def bench_calls(args, la, inp, torch, mid_sets):
 
     calls["mid_favor_m128_causal_fwd"] = bench_call("favor_m2", favor_fwd_m2, 100, 400, w.B * w.N,
                                                     4 * unit_bytes(w.B, w.H, w.N, w.d), la, torch, nsets=nsets)
-    # Its backward on the features (m = 2d): statistics sweep, the head's g, the blocks' sweeps.
+    # Its backward on the features (m = 2d): the head's g from the forward's output, the blocks' sweeps.
     # Algorithmic bytes: q, k features (2 units each), v, dout read; their gradients written (8 units).
-    _, den2 = la.la_forward_causal_features_blocks(fq, fk, fsets[0][2], return_den=True)
+    o2, den2 = la.la_forward_causal_features_blocks(fq, fk, fsets[0][2], return_den=True)
     g2 = (torch.empty_like(fq), torch.empty_like(fk), torch.empty_like(q0))
     dos2 = [inp.normal((w.B, w.H, w.N, w.d), inp.generator(60 + s, "cuda"), w.dtype, 1.0, "cuda") for s in range(nsets)]
     wsb2 = torch.empty(la.features_workspace_size(3, w.B, w.H, w.N, w.d, m, w.dtype), dtype=torch.uint8, device="cuda")
 
     def favor_bwd_m2(i):
-        la.la_backward_causal_features_blocks(fq, fk, fsets[i][2], dos2[i], den2, out=g2, workspace=wsb2)
+        la.la_backward_causal_features_blocks(fq, fk, fsets[i][2], dos2[i], den2, o=o2, out=g2, workspace=wsb2)
 
     calls["mid_favor_m128_causal_bwd"] = bench_call("favor_m2_bwd", favor_bwd_m2, 100, 400, w.B * w.N,
                                                     8 * unit_bytes(w.B, w.H, w.N, w.d), la, torch, nsets=nsets)
@@ -361,14 +361,14 @@ def bench_calls(args, la, inp, torch, mid_sets):
         la.favor_features_blocks(q, om2, out=fq)
         la.favor_features_blocks(k, om2, out=fk)
         la.la_forward_noncausal_features_blocks(fq, fk, v, out=o, workspace=wsn, den_out=den2)
-        la.la_backward_noncausal_features_blocks(fq, fk, v, dos2[i], den2, out=g2, workspace=wsn_b)
+        la.la_backward_noncausal_features_blocks(fq, fk, v, dos2[i], den2, o=o, out=g2, workspace=wsn_b)
         la.favor_features_blocks_backward(q, om2, fq, g2[0], out=dq2)
         la.favor_features_blocks_backward(k, om2, fk, g2[1], out=dk2)
 
     calls["mid_favor_m128_noncausal_fwd_bwd"] = bench_call("favor_m2_nc_train", favor_train_nc_m2, 50, 200, w.B * w.N,
                                                            8 * unit_bytes(w.B, w.H, w.N, w.d), la, torch,
                                                            nsets=nsets)
-    del fq, fk, wsf, den2, g2, dos2, wsb2, wsn, wsn_b, dq2, dk2
+    del fq, fk, wsf, o2, den2, g2, dos2, wsb2, wsn, wsn_b, dq2, dk2
 
     # A FAVOR+ training step (m = d): features of q and k, the causal forward on them, its
     # backward on the features, and the gradient through the feature map for q and k.

@@ -306,10 +306,13 @@ la_status la_forward_noncausal_features_blocks(const void* fq, const void* fk, c
  * g = -G . O: den [B][H][N] fp32 is the forward's den_out (the head's, over all m
  * features).  A statistics sweep per block gives each row's G . num_j, their sum gives g,
  * then the block's sweeps give dfq_j, dfk_j and its share of dv (summed over the blocks).
+ * o (nullable) [B][H][N][d]: the forward's output; when given, g = -G . O of every row comes
+ * from it in one elementwise pass and the statistics sweep is skipped (the same gradients
+ * to the rounding of O).
  * Workspace: la_features_workspace_size(3, B, H, N, d, m, dt, &bytes); m = d is
- * la_backward_causal_features (den unused). */
+ * la_backward_causal_features (den and o unused). */
 la_status la_backward_causal_features_blocks(const void* fq, const void* fk, const void* v, const void* dout,
-                                             const float* den, void* dfq, void* dfk, void* dv, int64_t B,
+                                             const float* den, const void* o, void* dfq, void* dfk, void* dv, int64_t B,
                                              int64_t H, int64_t N, int64_t d, int64_t m, la_dtype dt,
                                              void* workspace, size_t workspace_bytes, void* stream);
 /* Non-causal backward on m = KF d features (block layout, as la_forward_noncausal_features_blocks):
@@ -317,10 +320,11 @@ la_status la_backward_causal_features_blocks(const void* fq, const void* fk, con
  * forward's den_out.  The same derivative of the non-causal form as la_backward_noncausal_features,
  * with the head's G = dO / den and g = -G . O in every block: a statistics pass gives each row's
  * G . num_j per block, their sum gives g, then each block's passes give dfq_j, dfk_j and its share
- * of dv (summed over the blocks).  Workspace: la_features_workspace_size(4, B, H, N, d, m, dt,
- * &bytes); m = d is la_backward_noncausal_features (den unused). */
+ * of dv (summed over the blocks); o (nullable) as in la_backward_causal_features_blocks.
+ * Workspace: la_features_workspace_size(4, B, H, N, d, m, dt,
+ * &bytes); m = d is la_backward_noncausal_features (den and o unused). */
 la_status la_backward_noncausal_features_blocks(const void* fq, const void* fk, const void* v, const void* dout,
-                                                const float* den, void* dfq, void* dfk, void* dv, int64_t B,
+                                                const float* den, const void* o, void* dfq, void* dfk, void* dv, int64_t B,
                                                 int64_t H, int64_t N, int64_t d, int64_t m, la_dtype dt,
                                                 void* workspace, size_t workspace_bytes, void* stream);
 /* Multi-token decode (la_decode_steps_features) on m = KF d features: fq [B][H][KF][T][d]
@@ -362,7 +366,7 @@ int la_debug_wait_limit(void);
  * synchronises on its stop event and returns the kernel's name ("seg_state",
  * "total", "scan", "causal_fwd", "noncausal_fwd", "bwd_prefix", "rseg", "rscan",
  * "bwd_suffix", "bwd_fused", "ncbwd_q", "ncbwd_kv", "decode", "decode_steps",
- * "state_split", "favor_features", "favor_features_bwd", "combine_blocks", "combine_stats", "fill_zero") and
+ * "state_split", "favor_features", "favor_features_bwd", "combine_blocks", "combine_stats", "stats_from_output", "fill_zero") and
  * its duration in milliseconds. */
 la_status la_profile_enable(int on);
 int la_profile_count(void);

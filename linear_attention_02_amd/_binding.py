@@ -79,7 +79,7 @@ def load_library(path: str | None = None):
         f.argtypes = [vp] * 7 + [i64, i64, i64, i64, i32, vp, sz, vp]
     for name in ("la_backward_causal_features_blocks", "la_backward_noncausal_features_blocks"):
         getattr(lib, name).restype = i32
-        getattr(lib, name).argtypes = [vp] * 8 + [i64, i64, i64, i64, i64, i32, vp, sz, vp]
+        getattr(lib, name).argtypes = [vp] * 9 + [i64, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_favor_features_backward.restype = i32
     lib.la_favor_features_backward.argtypes = [vp] * 5 + [i64, i64, i32, vp]
     lib.la_favor_features_blocks_backward.restype = i32
@@ -480,12 +480,14 @@ def la_forward_causal_features_blocks(fq, fk, v, *, return_den=False, return_sta
     return res[0] if len(res) == 1 else tuple(res)
 
 
-def _backward_features_blocks(causal, fq, fk, v, dout, den, out, workspace):
+def _backward_features_blocks(causal, fq, fk, v, dout, den, out, workspace, o=None):
     B, H, N, d, m = _check_blocks(fq, fk, v)
     if dout.shape != v.shape or dout.dtype != v.dtype or not dout.is_contiguous():
         raise ValueError("dout must match v")
     if den.shape != (B, H, N) or den.dtype != torch.float32 or not den.is_contiguous():
         raise ValueError("den must be the forward's contiguous [B, H, N] fp32 denominators")
+    if o is not None and (o.shape != v.shape or o.dtype != v.dtype or not o.is_contiguous()):
+        raise ValueError("o must be the forward's output, shaped like v")
     g = (torch.empty_like(fq), torch.empty_like(fk), torch.empty_like(v)) if out is None else out
     need = features_workspace_size(3 if causal else 4, B, H, N, d, m, fq.dtype)
     ws = workspace if workspace is not None else (torch.empty(need, dtype=torch.uint8, device=fq.device)
@@ -493,22 +495,24 @@ def _backward_features_blocks(causal, fq, fk, v, dout, den, out, workspace):
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     fn = (load_library().la_backward_causal_features_blocks if causal
           else load_library().la_backward_noncausal_features_blocks)
-    _check(fn(_ptr(fq), _ptr(fk), _ptr(v), _ptr(dout), _ptr(den),
+    _check(fn(_ptr(fq), _ptr(fk), _ptr(v), _ptr(dout), _ptr(den), _ptr(o),
               _ptr(g[0]), _ptr(g[1]), _ptr(g[2]), B, H, N, d, m, _dtype_code(fq.dtype), _ptr(ws), nbytes,
               _stream(fq.device)))
     return g
 
 
-def la_backward_causal_features_blocks(fq, fk, v, dout, den, *, out=None, workspace=None):
+def la_backward_causal_features_blocks(fq, fk, v, dout, den, *, o=None, out=None, workspace=None):
     """Causal backward on m = KF d features in block layout fq, fk [B, H, KF, N, d]; den [B, H, N] is the
-    forward's den (return_den=True).  Returns (dfq, dfk) in block layout and dv [B, H, N, d]."""
-    return _backward_features_blocks(True, fq, fk, v, dout, den, out, workspace)
+    forward's den (return_den=True), o (optional) its output, which replaces the statistics sweep.
+    Returns (dfq, dfk) in block layout and dv [B, H, N, d]."""
+    return _backward_features_blocks(True, fq, fk, v, dout, den, out, workspace, o)
 
 
-def la_backward_noncausal_features_blocks(fq, fk, v, dout, den, *, out=None, workspace=None):
+def la_backward_noncausal_features_blocks(fq, fk, v, dout, den, *, o=None, out=None, workspace=None):
     """Non-causal backward on m = KF d features in block layout (la_forward_noncausal_features_blocks);
-    den [B, H, N] is that forward's den.  Returns (dfq, dfk) in block layout and dv [B, H, N, d]."""
-    return _backward_features_blocks(False, fq, fk, v, dout, den, out, workspace)
+    den [B, H, N] is that forward's den, o (optional) its output.  Returns (dfq, dfk) in block layout
+    and dv [B, H, N, d]."""
+    return _backward_features_blocks(False, fq, fk, v, dout, den, out, workspace, o)
 
 
 def la_forward_noncausal_features_blocks(fq, fk, v, *, return_den=False, out=None, workspace=None, den_out=None):
@@ -622,18 +626,18 @@ class _FavorAttention(torch.autograd.Function):
             fq, fk = favor_features_blocks(q, omega), favor_features_blocks(k, omega)
             fwd = la_forward_causal_features_blocks if causal else la_forward_noncausal_features_blocks
             o, den = fwd(fq, fk, v, return_den=True)
-        ctx.save_for_backward(q, k, v, omega, fq, fk, den)
+        ctx.save_for_backward(q, k, v, omega, fq, fk, den, o if den is not None else None)
         ctx.causal = causal
         return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v, omega, fq, fk, den = ctx.saved_tensors
+        q, k, v, omega, fq, fk, den, o = ctx.saved_tensors
         if den is None:
             dfq, dfk, dv = la_backward_causal_features(fq, fk, v, do.contiguous(), causal=ctx.causal)
             return favor_features_backward(q, omega, fq, dfq), favor_features_backward(k, omega, fk, dfk), dv, None, None
         bwd = la_backward_causal_features_blocks if ctx.causal else la_backward_noncausal_features_blocks
-        dfq, dfk, dv = bwd(fq, fk, v, do.contiguous(), den)
+        dfq, dfk, dv = bwd(fq, fk, v, do.contiguous(), den, o=o)
         return (favor_features_blocks_backward(q, omega, fq, dfq), favor_features_blocks_backward(k, omega, fk, dfk),
                 dv, None, None)
 

@@ -914,7 +914,7 @@ la_status la_backward_noncausal_features(const void* fq, const void* fk, const v
 }
 
 la_status la_backward_causal_features_blocks(const void* fq, const void* fk, const void* v, const void* dout,
-                                             const float* den, void* dfq, void* dfk, void* dv, int64_t B, int64_t H,
+                                             const float* den, const void* o, void* dfq, void* dfk, void* dv, int64_t B, int64_t H,
                                              int64_t N, int64_t d, int64_t m, la_dtype dt, void* workspace,
                                              size_t workspace_bytes, void* stream) {
     la_status st = check_blocks(d, m);
@@ -930,9 +930,9 @@ la_status la_backward_causal_features_blocks(const void* fq, const void* fk, con
         return fail(LA_ERR_INVALID_ARGUMENT, "fq, fk, v, dout, den, dfq, dfk and dv must be non-NULL");
     const size_t tb = (size_t)B * H * N * d * elem_size(dt), fb = tb * KF;
     const Range in[] = {{"fq", fq, fb}, {"fk", fk, fb}, {"v", v, tb}, {"dout", dout, tb},
-                        {"den", den, (size_t)B * H * N * sizeof(float)}};
+                        {"den", den, (size_t)B * H * N * sizeof(float)}, {"o", o, o ? tb : 0}};
     const Range out[] = {{"dfq", dfq, fb}, {"dfk", dfk, fb}, {"dv", dv, tb}};
-    if ((st = check_ptrs(in, 5, out, 3)) != LA_OK) return st;
+    if ((st = check_ptrs(in, 6, out, 3)) != LA_OK) return st;
     if (empty) return LA_OK;
     const int64_t BHb = B * H * KF;  // block heads
     const Layout L = layout(LA_OP_BWD_CAUSAL, B, H * KF, N, d);
@@ -943,7 +943,7 @@ la_status la_backward_causal_features_blocks(const void* fq, const void* fk, con
     if (workspace_bytes < need)
         return fail(LA_ERR_WORKSPACE, "workspace has %zu bytes; %zu are needed", workspace_bytes, need);
     const Range wsr[] = {{"workspace", workspace, need}};
-    if ((st = check_ptrs(in, 5, wsr, 1)) != LA_OK) return st;
+    if ((st = check_ptrs(in, 6, wsr, 1)) != LA_OK) return st;
     for (const Range& r : out)
         if (overlap(wsr[0], r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
     if ((int64_t)L.plan.nseg * BHb > ((int64_t)1 << 24))
@@ -967,15 +967,23 @@ la_status la_backward_causal_features_blocks(const void* fq, const void* fk, con
     if (L.plan.scan &&
         (e = timed("scan", s, [&] { return la::launch_scan((int)d, rec, BHb, L.plan.nseg, 1, s, nullptr); })) != hipSuccess)
         return hip_fail(e, "scan launch");
-    if ((e = timed("bwd_prefix", s, [&] {
-             return la::launch_bwd_prefix(idt, (int)d, fq, fk, v, dout, dfq, rowstat, rrec, rec, BHb, N, L.plan, s,
-                                          nullptr, nullptr, la::kFeatGiven, 1, G, den);
-         })) != hipSuccess)
-        return hip_fail(e, "bwd_prefix launch");
-    // ... the head's g = -(sum_j G . num_j) / den for every block ...
-    if ((e = timed("combine_stats", s, [&] { return la::launch_combine_stats(rowstat, B * H * N, N, G, s); })) !=
-        hipSuccess)
-        return hip_fail(e, "combine_stats launch");
+    // (With the forward's output, g = -G . O of every row comes from one elementwise pass instead.)
+    if (o != nullptr) {
+        if ((e = timed("stats_from_output", s, [&] {
+                 return la::launch_stats_from_output(idt, (int)d, dout, o, den, rowstat, B * H * N, N, G, s);
+             })) != hipSuccess)
+            return hip_fail(e, "stats_from_output launch");
+    } else {
+        if ((e = timed("bwd_prefix", s, [&] {
+                 return la::launch_bwd_prefix(idt, (int)d, fq, fk, v, dout, dfq, rowstat, rrec, rec, BHb, N, L.plan, s,
+                                              nullptr, nullptr, la::kFeatGiven, 1, G, den);
+             })) != hipSuccess)
+            return hip_fail(e, "bwd_prefix launch");
+        // ... the head's g = -(sum_j G . num_j) / den for every block ...
+        if ((e = timed("combine_stats", s, [&] { return la::launch_combine_stats(rowstat, B * H * N, N, G, s); })) !=
+            hipSuccess)
+            return hip_fail(e, "combine_stats launch");
+    }
     // ... then each block's sweeps with the head's (den, g): dfq, dfk and its share of dv.
     if ((e = timed("bwd_prefix", s, [&] {
              return la::launch_bwd_prefix(idt, (int)d, fq, fk, v, dout, dfq, rowstat, rrec, rec, BHb, N, L.plan, s,
@@ -1003,7 +1011,7 @@ la_status la_backward_causal_features_blocks(const void* fq, const void* fk, con
 }
 
 la_status la_backward_noncausal_features_blocks(const void* fq, const void* fk, const void* v, const void* dout,
-                                                const float* den, void* dfq, void* dfk, void* dv, int64_t B,
+                                                const float* den, const void* o, void* dfq, void* dfk, void* dv, int64_t B,
                                                 int64_t H, int64_t N, int64_t d, int64_t m, la_dtype dt,
                                                 void* workspace, size_t workspace_bytes, void* stream) {
     la_status st = check_blocks(d, m);
@@ -1019,9 +1027,9 @@ la_status la_backward_noncausal_features_blocks(const void* fq, const void* fk, 
         return fail(LA_ERR_INVALID_ARGUMENT, "fq, fk, v, dout, den, dfq, dfk and dv must be non-NULL");
     const size_t tb = (size_t)B * H * N * d * elem_size(dt), fb = tb * KF;
     const Range in[] = {{"fq", fq, fb}, {"fk", fk, fb}, {"v", v, tb}, {"dout", dout, tb},
-                        {"den", den, (size_t)B * H * N * sizeof(float)}};
+                        {"den", den, (size_t)B * H * N * sizeof(float)}, {"o", o, o ? tb : 0}};
     const Range out[] = {{"dfq", dfq, fb}, {"dfk", dfk, fb}, {"dv", dv, tb}};
-    if ((st = check_ptrs(in, 5, out, 3)) != LA_OK) return st;
+    if ((st = check_ptrs(in, 6, out, 3)) != LA_OK) return st;
     if (empty) return LA_OK;
     const int64_t BHb = B * H * KF;  // block heads
     const Layout L = layout(LA_OP_BWD_NONCAUSAL, B, H * KF, N, d);
@@ -1033,7 +1041,7 @@ la_status la_backward_noncausal_features_blocks(const void* fq, const void* fk, 
     if (workspace_bytes < need)
         return fail(LA_ERR_WORKSPACE, "workspace has %zu bytes; %zu are needed", workspace_bytes, need);
     const Range wsr[] = {{"workspace", workspace, need}};
-    if ((st = check_ptrs(in, 5, wsr, 1)) != LA_OK) return st;
+    if ((st = check_ptrs(in, 6, wsr, 1)) != LA_OK) return st;
     for (const Range& r : out)
         if (overlap(wsr[0], r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
     if ((int64_t)L.plan.nseg * BHb > ((int64_t)1 << 24))
@@ -1058,15 +1066,23 @@ la_status la_backward_noncausal_features_blocks(const void* fq, const void* fk, 
         return hip_fail(e, "seg_state launch");
     if ((e = timed("total", s, [&] { return la::launch_total((int)d, rec, total, BHb, L.plan.nseg, s); })) != hipSuccess)
         return hip_fail(e, "total launch");
-    if ((e = timed("ncbwd_q", s, [&] {
-             return la::launch_ncbwd_q(idt, (int)d, fq, dout, dfq, total, 1, rrec, BHb, N, L.plan, s, la::kFeatGiven,
-                                       1, G, den, rowstat);
-         })) != hipSuccess)
-        return hip_fail(e, "ncbwd_q launch");
-    // ... the head's g = -(sum_j G . num_j) / den for every block ...
-    if ((e = timed("combine_stats", s, [&] { return la::launch_combine_stats(rowstat, B * H * N, N, G, s); })) !=
-        hipSuccess)
-        return hip_fail(e, "combine_stats launch");
+    // (With the forward's output, g = -G . O of every row comes from one elementwise pass instead.)
+    if (o != nullptr) {
+        if ((e = timed("stats_from_output", s, [&] {
+                 return la::launch_stats_from_output(idt, (int)d, dout, o, den, rowstat, B * H * N, N, G, s);
+             })) != hipSuccess)
+            return hip_fail(e, "stats_from_output launch");
+    } else {
+        if ((e = timed("ncbwd_q", s, [&] {
+                 return la::launch_ncbwd_q(idt, (int)d, fq, dout, dfq, total, 1, rrec, BHb, N, L.plan, s,
+                                           la::kFeatGiven, 1, G, den, rowstat);
+             })) != hipSuccess)
+            return hip_fail(e, "ncbwd_q launch");
+        // ... the head's g = -(sum_j G . num_j) / den for every block ...
+        if ((e = timed("combine_stats", s, [&] { return la::launch_combine_stats(rowstat, B * H * N, N, G, s); })) !=
+            hipSuccess)
+            return hip_fail(e, "combine_stats launch");
+    }
     // ... then each block's passes with the head's (den, g): dfq_j and (R_j, r_j), dfk_j and its share of dv.
     if ((e = timed("ncbwd_q", s, [&] {
              return la::launch_ncbwd_q(idt, (int)d, fq, dout, dfq, total, 1, rrec, BHb, N, L.plan, s, la::kFeatGiven,

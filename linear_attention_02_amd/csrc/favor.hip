@@ -498,6 +498,62 @@ __global__ __launch_bounds__(kBlock) void combine_stats_kernel(float2* __restric
     for (int j = 0; j < KF; ++j) rowstat[(hh * KF + j) * N + t] = make_float2(den, g);
 }
 
+// stats_from_output: the same row statistics from the forward's output O of each head row
+// instead of a statistics sweep: G . num_j summed over the blocks is G . O den, so
+// g = -G . O with G = dO / den rounded to the operand type as the sweeps round it (same
+// reciprocal).  dout, o [heads][N][D]; den [heads][N]; every block's entry of rowstat
+// [heads][KF][N] gets (den, g).  D / 4 adjacent lanes per row, 4 elements each.
+template <typename T, int D>
+__global__ __launch_bounds__(kBlock) void stats_from_output_kernel(const T* __restrict__ dout, const T* __restrict__ o,
+                                                                   const float* __restrict__ den,
+                                                                   float2* __restrict__ rowstat, int64_t rows,
+                                                                   int64_t N, int KF) {
+    constexpr int TPR = D / 4;
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int64_t row = i / TPR;
+    const int c = 4 * (int)(i % TPR);
+    const bool valid = row < rows;
+    const float dn = valid ? den[row] : 1.f;
+    const float inv = rcp_f(dn);
+    float s = 0.f;
+    if (valid) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            s += to_f32(from_f32<T>(to_f32(dout[row * D + c + e]) * inv)) * to_f32(o[row * D + c + e]);
+    }
+    s = sum_lanes<TPR>(s);
+    if (valid && c == 0) {
+        const int64_t hh = row / N, t = row - hh * N;
+        for (int j = 0; j < KF; ++j) rowstat[(hh * KF + j) * N + t] = make_float2(dn, -s);
+    }
+}
+
+hipError_t launch_stats_from_output(int dt, int d, const void* dout, const void* o, const float* den, float* rowstat,
+                                    int64_t rows, int64_t N, int KF, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    const dim3 grid((unsigned)((rows * (d / 4) + kBlock - 1) / kBlock));
+#define LA_SFO(TT, DD)                                                                                          \
+    hipLaunchKernelGGL((stats_from_output_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)dout,          \
+                       (const TT*)o, den, reinterpret_cast<float2*>(rowstat), rows, N, KF)
+    if (dt == kBF16) {
+        switch (d) {
+            case 32: LA_SFO(bf16, 32); break;
+            case 64: LA_SFO(bf16, 64); break;
+            case 128: LA_SFO(bf16, 128); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (d) {
+            case 32: LA_SFO(float, 32); break;
+            case 64: LA_SFO(float, 64); break;
+            case 128: LA_SFO(float, 128); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+#undef LA_SFO
+    return hipGetLastError();
+}
+
 hipError_t launch_combine_stats(float* rowstat, int64_t rows, int64_t N, int KF, hipStream_t s) {
     if (rows == 0) return hipSuccess;
     hipLaunchKernelGGL(combine_stats_kernel, dim3((unsigned)((rows + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,

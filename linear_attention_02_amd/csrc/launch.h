@@ -159,5 +159,9 @@ hipError_t launch_combine_blocks(int dt, int d, const void* ob, const float* db,
 // Backward row statistics over KF feature blocks: rowstat [heads][KF][N] float2 (den, G . num_j)
 // becomes (den, g) in every block, g = -(sum_j G . num_j) / den.
 hipError_t launch_combine_stats(float* rowstat, int64_t rows, int64_t N, int KF, hipStream_t s);
+// The same (den, g) from the forward's output o and the upstream gradient dout ([heads][N][d],
+// rows = heads x N) and den [heads][N]: g = -G . O with G = dO / den rounded to dt.
+hipError_t launch_stats_from_output(int dt, int d, const void* dout, const void* o, const float* den, float* rowstat,
+                                    int64_t rows, int64_t N, int KF, hipStream_t s);
 
 }  // namespace la

@@ -301,14 +301,15 @@ def test_backward_blocks_validation(lib):
     out = ctypes.c_size_t(0)
     assert lib.la_features_workspace_size(3, 1, 2, 64, 64, 128, 1, ctypes.byref(out)) == 0
     assert out.value >= ws(lib, la.LA_OP_BWD_CAUSAL, 1, 4, 64, 64)[1] + 4 * 64 * 64 * 2   # block heads + their dv
-    args = (fq, fk, v, do, den, dfq, dfk, dv)
+    args = (fq, fk, v, do, den, None, dfq, dfk, dv)
     assert f(*args, 1, 2, 64, 64, 96, 1, wsp, 1 << 30, None) == 1                  # m not a multiple of d
     assert f(*args, 1, 2, 64, 64, 128, 1, wsp, 16, None) == 3                      # workspace too small
     assert f(*args, 1, 2, 64, 64, 128, 1, None, 0, None) == 3                      # no workspace
-    assert f(fq, fk, v, do, None, dfq, dfk, dv, 1, 2, 64, 64, 128, 1, wsp, 1 << 30, None) == 1  # no den
-    assert f(fq, fk, v, do, den, dfq, dfq + 64, dv, 1, 2, 64, 64, 128, 1, wsp, 1 << 30, None) == 1  # dfk on dfq
+    assert f(fq, fk, v, do, None, None, dfq, dfk, dv, 1, 2, 64, 64, 128, 1, wsp, 1 << 30, None) == 1  # no den
+    assert f(fq, fk, v, do, den, None, dfq, dfq + 64, dv, 1, 2, 64, 64, 128, 1, wsp, 1 << 30, None) == 1  # dfk on dfq
     assert f(*args, 1, 2, 64, 128, 256, 0, wsp, 1 << 30, None) == 2                # fp32 d = 128 not built
     assert f(*args, 1, 2, 0, 64, 128, 1, None, 0, None) == 0                       # no tokens
+    assert f(fq, fk, v, do, den, dfq + 64, dfq, dfk, dv, 1, 2, 64, 64, 128, 1, wsp, 1 << 30, None) == 1  # o on dfq
 
 
 def test_backward_noncausal_blocks_validation(lib):
@@ -319,14 +320,15 @@ def test_backward_noncausal_blocks_validation(lib):
     assert lib.la_features_workspace_size(4, 1, 2, 64, 64, 128, 1, ctypes.byref(out)) == 0
     # block heads' workspace + their dv + a (den, g) pair per block row
     assert out.value >= ws(lib, la.LA_OP_BWD_NONCAUSAL, 1, 4, 64, 64)[1] + 4 * 64 * 64 * 2 + 4 * 64 * 8
-    args = (fq, fk, v, do, den, dfq, dfk, dv)
+    args = (fq, fk, v, do, den, None, dfq, dfk, dv)
     assert f(*args, 1, 2, 64, 64, 96, 1, wsp, 1 << 30, None) == 1                  # m not a multiple of d
     assert f(*args, 1, 2, 64, 64, 128, 1, wsp, out.value - 1, None) == 3           # workspace one byte short
     assert f(*args, 1, 2, 64, 64, 128, 1, None, 0, None) == 3                      # no workspace
-    assert f(fq, fk, v, do, None, dfq, dfk, dv, 1, 2, 64, 64, 128, 1, wsp, 1 << 30, None) == 1  # no den
-    assert f(fq, fk, v, do, den, dfq, dfk, dfk + 64, 1, 2, 64, 64, 128, 1, wsp, 1 << 30, None) == 1  # dv on dfk
+    assert f(fq, fk, v, do, None, None, dfq, dfk, dv, 1, 2, 64, 64, 128, 1, wsp, 1 << 30, None) == 1  # no den
+    assert f(fq, fk, v, do, den, None, dfq, dfk, dfk + 64, 1, 2, 64, 64, 128, 1, wsp, 1 << 30, None) == 1  # dv on dfk
     assert f(*args, 1, 2, 64, 128, 256, 0, wsp, 1 << 30, None) == 2                # fp32 d = 128 not built
     assert f(*args, 1, 2, 0, 64, 128, 1, None, 0, None) == 0                       # no tokens
+    assert f(fq, fk, v, do, den, dfq + 64, dfq, dfk, dv, 1, 2, 64, 64, 128, 1, wsp, 1 << 30, None) == 1  # o on dfq
 
 
 def test_favor_features_blocks_backward_validation(lib):

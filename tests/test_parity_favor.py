@@ -391,12 +391,13 @@ def from_blocks(f):
     return np.moveaxis(f, -3, -2).reshape(*lead, N, KF * d)
 
 
+@pytest.mark.parametrize("with_o", [False, True], ids=["stats_sweep", "from_output"])
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("shape", [(2, 3, 200, 64, 2), (1, 2, 300, 128, 2), (2, 2, 1000, 64, 4),
                                    (1, 2, 257, 32, 3), (1, 4, 64 * 130 + 17, 64, 2)],
                          ids=lambda s: "x".join(map(str, s)))
-def test_favor_backward_blocks(la, oracle, shape, dtype, causal):
+def test_favor_backward_blocks(la, oracle, shape, dtype, causal, with_o):
     """The causal and non-causal backward on m = KF d features (every block with the head's G and g) against
     the oracle's backward on all m features at once, on the library's own features."""
     B, H, N, d, KF = shape
@@ -406,15 +407,17 @@ def test_favor_backward_blocks(la, oracle, shape, dtype, causal):
     q, k, v, do = (t.cuda() for t in inp.favor_qkv(B, H, N, d, dtype, seed=N + 110, with_dout=True))
     om = inp.favor_omega(d, seed=N + 111, m=m).cuda()
     fq, fk = la.favor_features_blocks(q, om), la.favor_features_blocks(k, om)
+    # with_o: the head's g from the forward's output instead of a statistics sweep per block.
     if causal:
-        _, den = la.la_forward_causal_features_blocks(fq, fk, v, return_den=True)
-        dfq, dfk, dv = la.la_backward_causal_features_blocks(fq, fk, v, do, den)
+        o, den = la.la_forward_causal_features_blocks(fq, fk, v, return_den=True)
+        dfq, dfk, dv = la.la_backward_causal_features_blocks(fq, fk, v, do, den, o=o if with_o else None)
     else:
-        _, den = la.la_forward_noncausal_features_blocks(fq, fk, v, return_den=True)
-        dfq, dfk, dv = la.la_backward_noncausal_features_blocks(fq, fk, v, do, den)
+        o, den = la.la_forward_noncausal_features_blocks(fq, fk, v, return_den=True)
+        dfq, dfk, dv = la.la_backward_noncausal_features_blocks(fq, fk, v, do, den, o=o if with_o else None)
     torch.cuda.synchronize()
     rdfq, rdfk, rdv = oracle.backward_features(from_blocks(f64(fq)), from_blocks(f64(fk)), f64(v), f64(do), causal)
     errs = {"dfq": slice_err(dfq, to_blocks(rdfq, KF)), "dfk": slice_err(dfk, to_blocks(rdfk, KF)),
             "dv": slice_err(dv, rdv)}
-    record(f"favor_bwd_blocks {'causal' if causal else 'noncausal'} {B}x{H}x{N}x{d} m={m} {dtype}", **errs)
+    record(f"favor_bwd_blocks {'causal' if causal else 'noncausal'}{' from o' if with_o else ''} {B}x{H}x{N}x{d} "
+           f"m={m} {dtype}", **errs)
     assert max(errs.values()) < TOL[dtype], errs
