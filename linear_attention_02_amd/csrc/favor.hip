@@ -515,12 +515,18 @@ __global__ __launch_bounds__(kBlock) void stats_from_output_kernel(const T* __re
     const bool valid = row < rows;
     const float dn = valid ? den[row] : 1.f;
     const float inv = rcp_f(dn);
-    float s = 0.f;
+    // One 4-element word of dO and of O per thread (8 bytes for bf16, 16 for fp32).
+    typedef typename std::conditional<sizeof(T) == 2, uint2, uint4>::type word;
+    word dw{}, ow{};
     if (valid) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            s += to_f32(from_f32<T>(to_f32(dout[row * D + c + e]) * inv)) * to_f32(o[row * D + c + e]);
+        dw = *reinterpret_cast<const word*>(dout + row * D + c);
+        ow = *reinterpret_cast<const word*>(o + row * D + c);
     }
+    const T* dh = reinterpret_cast<const T*>(&dw);
+    const T* oh = reinterpret_cast<const T*>(&ow);
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += to_f32(from_f32<T>(to_f32(dh[e]) * inv)) * to_f32(oh[e]);
     s = sum_lanes<TPR>(s);
     if (valid && c == 0) {
         const int64_t hh = row / N, t = row - hh * N;
