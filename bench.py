@@ -8,9 +8,10 @@ d=64, bf16 inputs ~ N(0,1)/sqrt(d), chunk 64.  W untimed warmup steps, then K
 steps timed back to back between two device synchronisations.  Inputs are
 resident in HBM before the timed region; the step rotates over several input
 sets whose total exceeds the 256 MB last-level cache, so each step starts with
-its inputs in HBM, not in cache.  The defaults (300 warmup steps, 1000 timed)
-measure the steady state: the first few milliseconds of work after start-up run
-while the GPU clock ramps up and read about 5% slow.  Launches are eager; with
+its inputs in HBM, not in cache.  Before the W warmup steps, untimed steps run
+for 0.5 s of GPU time: the first milliseconds of work after start-up run while
+the GPU clock ramps up and read about 5-10% slow, which a short run (K = 20)
+would otherwise time.  Launches are eager; with
 --graph each input set's step is captured once into a HIP graph and the timed
 region replays the graphs (every graph's replays are first checked bitwise
 against eager steps; on this stack replays measure a few microseconds slower
@@ -21,7 +22,8 @@ The JSON line also carries
   * roofline    : the dominant kernel's algorithmic bytes per launch over its
                   average duration (HIP events around every launch, recorded
                   on the library's stream over a second run of the timed steps) against the
-                  8 TB/s HBM peak;
+                  8 TB/s HBM peak; step_frac / step_achieved inside it: the whole
+                  step (22 d bytes per token-head) over the timed step time;
   * step_roofline: the same for the whole step (22 d bytes per token-head);
   * calls       : the other measured calls (non-causal forward, non-causal
                   forward + backward, and the causal forward on FAVOR+ random
@@ -159,12 +161,33 @@ def sequence_roofline(stats, B, H, N, d, steps):
                   "alg_bytes_per_launch": alg}
 
 
-def time_steps(fn, nsets, warmup, steps, la, torch, timed_fn=None):
+PREWARM_S = 0.5
+
+
+def prewarm(run, nsets, torch, seconds=PREWARM_S):
+    """Untimed steps for `seconds` of GPU time before the warmup steps: the first
+    milliseconds of work after start-up run while the GPU clock ramps up, and a run
+    of a few dozen steps would otherwise be timed on the ramp."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            run(i % nsets)
+            i += 1
+        torch.cuda.synchronize()
+    return i
+
+
+def time_steps(fn, nsets, warmup, steps, la, torch, timed_fn=None, warm_s=0.0):
     """Wall time of `steps` back-to-back steps, then per-kernel event times over a second run of them.
 
     timed_fn (default fn) is what the timed region runs per step, e.g. the replay of
-    a captured graph of fn; the per-kernel event run always calls fn itself."""
+    a captured graph of fn; the per-kernel event run always calls fn itself.
+    warm_s: seconds of untimed steps before the warmup steps."""
     run = timed_fn or fn
+    if warm_s > 0:
+        prewarm(run, nsets, torch, warm_s)
     for i in range(warmup):
         run(i % nsets)
     torch.cuda.synchronize()
@@ -235,12 +258,17 @@ def bench_mid(args, la, inp, torch):
 
     graphs = capture_graphs(step, nsets, (o,) + grads, torch) if args.graph else None
     replay = None if graphs is None else (lambda i: graphs[i].replay())
-    dt, stats = time_steps(step, nsets, args.warmup, args.steps, la, torch, timed_fn=replay)
+    dt, stats = time_steps(step, nsets, args.warmup, args.steps, la, torch, timed_fn=replay, warm_s=PREWARM_S)
     T = B * H * N
     step_s = dt / args.steps
     step_bytes = 11 * unit_bytes(B, H, N, d)
     flops = 14 * d * d * T
     kname, roof = sequence_roofline(stats, B, H, N, d, args.steps)
+    if roof is not None:
+        # the whole step beside the dominant kernel: 11 units (22 d bytes per token-head)
+        roof["step_achieved"] = round(step_bytes / step_s / 1e9, 1)
+        roof["step_frac"] = round(step_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4)
+        roof["step_alg_bytes"] = step_bytes
     return {
         "value": B * N * args.steps / dt,
         "ms_per_step": step_s * 1e3,
@@ -500,13 +528,35 @@ def bench_calls(args, la, inp, torch, mid_sets):
     return calls
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_share():
+    """Host threads the oracle may use: every core this process may run on, within the
+    thread count the host grants the job (OMP_NUM_THREADS, when set)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        omp = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        omp = 0
+    return min(n, omp) if omp > 0 else n
+
+
 def cpu_baseline(args, inp, torch, mid_set):
     import oracle
 
     w = inp.MID
     q, k, v, do = (inp.to_f64(t) for t in mid_set)
-    cores = len(os.sched_getaffinity(0))
-    cores = min(cores, 16)
+    # the host's share of cores, capped at the heads (the oracle's parallelism)
+    cores = min(cpu_share(), w.B * w.H)
     oracle.set_threads(cores)
     reps = 0
     t0 = time.perf_counter()
@@ -518,6 +568,7 @@ def cpu_baseline(args, inp, torch, mid_set):
             break
     dt = time.perf_counter() - t0
     return {"value": round(reps * w.B * w.N / dt, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0)),
             "sample": f"{reps} full causal fwd+bwd steps of B4 H16 N4096 d64 (all 64 heads), fp64, "
                       f"{dt:.1f} s wall"}
 
@@ -528,8 +579,7 @@ def call_oracles(args, inp, torch):
     second divided by the workload's heads per token."""
     import oracle
 
-    cores = min(len(os.sched_getaffinity(0)), 16)
-    oracle.set_threads(cores)
+    cores = cpu_share()
     f64 = inp.to_f64
 
     def rate(fn, token_heads, heads_per_token, budget=1.5):
@@ -545,9 +595,11 @@ def call_oracles(args, inp, torch):
     out = {}
 
     def record(name, fn, token_heads, heads_per_token, threads, what):
+        # all affinity cores, capped at the sample's heads (the oracle's parallelism)
+        oracle.set_threads(min(cores, threads))
         v, reps, dt = rate(fn, token_heads, heads_per_token)
         out[name] = {"value": v, "unit": "tokens/s", "cores": min(cores, threads), "kind": "oracle",
-                     "sample": f"{reps} x {what}, fp64, {dt:.1f} s wall"}
+                     "cpu": cpu_model(), "sample": f"{reps} x {what}, fp64, {dt:.1f} s wall"}
 
     w = inp.MID
     hs = 8

@@ -40,9 +40,13 @@
  *     faults surface at the caller's next synchronisation.
  *   - Results are deterministic: the same inputs give bitwise-identical
  *     outputs (fixed-order reductions, no floating-point atomics).
- *   - Non-finite inputs: rows never read keys from later chunks of 64 tokens,
- *     but a NaN/Inf value row can reach earlier rows of its own chunk through
- *     the masked in-chunk product.  Inputs are expected to be finite.
+ *   - Non-finite inputs: causality is strict.  An inf or NaN in q, k, v (or dout)
+ *     of token t never reaches an output row that does not read token t: causal
+ *     rows before t are bitwise as without it, and in the backward the key-side
+ *     gradients of later keys likewise.  Inside a chunk the masked products take
+ *     such operands replaced by 0 and the rows that do read token t get their
+ *     non-finite result back explicitly.  phi(NaN) = NaN (the feature map
+ *     propagates NaN); a result the exact form gives as +-inf may come out NaN.
  */
 #ifndef LINATTN_H
 #define LINATTN_H
@@ -356,6 +360,21 @@ const char* la_version(void);
  * LA_ERR_INVALID_ARGUMENT for polls < 0.  la_debug_wait_limit() returns the bound. */
 la_status la_debug_set_wait_limit(int polls);
 int la_debug_wait_limit(void);
+
+/* For callers that must tell a poisoned result from real NaN data: the number of
+ * workgroups whose wait gave up (see above) in the last fused causal backward that
+ * ran on `workspace` for this shape (la_backward_causal, la_backward_causal_state,
+ * la_backward_causal_features); each one left NaN in its segment's dk and dv rows.
+ * Every workgroup of that launch writes its own count into the workspace, so no
+ * clearing is needed between calls.  Synchronises `stream` (a hipStream_t, NULL =
+ * the default stream) and copies the counts to the host.  *failures_out = 0 for
+ * shapes that run the two sweeps as separate launches (more than 12 segments per
+ * head, or d = 128), which never wait.  Errors: LA_ERR_INVALID_ARGUMENT
+ * (failures_out NULL), shape errors as la_workspace_size, LA_ERR_WORKSPACE
+ * (workspace NULL or smaller than la_workspace_size(LA_OP_BWD_CAUSAL, ...)),
+ * LA_ERR_HIP (the synchronisation or the copy failed). */
+la_status la_backward_causal_wait_failures(const void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                                           int64_t N, int64_t d, la_dtype dt, void* stream, int64_t* failures_out);
 
 /* Per-kernel timing for benchmarks and profiling.  While enabled (on != 0) on
  * the calling thread, every kernel that a call on this thread launches is

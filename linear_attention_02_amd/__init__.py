@@ -45,6 +45,7 @@ from ._binding import (  # noqa: F401
     profile_enable,
     profile_entries,
     saved_state_size,
+    backward_wait_failures,
     set_wait_limit,
     wait_limit,
     workspace_size,

@@ -102,6 +102,8 @@ def load_library(path: str | None = None):
     lib.la_forward_causal_features.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_forward_noncausal_features.restype = i32
     lib.la_forward_noncausal_features.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]
+    lib.la_backward_causal_wait_failures.restype = i32
+    lib.la_backward_causal_wait_failures.argtypes = [vp, sz, i64, i64, i64, i64, i32, vp, ctypes.POINTER(i64)]
     lib.la_status_string.restype = ctypes.c_char_p
     lib.la_status_string.argtypes = [i32]
     lib.la_last_error_message.restype = ctypes.c_char_p
@@ -684,6 +686,17 @@ def la_forward_noncausal_features(fq, fk, v, *, out=None, workspace=None):
                                                         _dtype_code(fq.dtype), _ptr(ws), nbytes,
                                                         _stream(fq.device)))
     return o
+
+
+def backward_wait_failures(workspace, q) -> int:
+    """Workgroups whose wait gave up in the last fused causal backward run on `workspace` for
+    inputs shaped like q [B, H, N, d] (their dk, dv rows are NaN); synchronises q's stream."""
+    B, H, N, d = q.shape
+    out = ctypes.c_int64(0)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().la_backward_causal_wait_failures(_ptr(workspace), nbytes, B, H, N, d, _dtype_code(q.dtype),
+                                                           _stream(q.device), ctypes.byref(out)))
+    return int(out.value)
 
 
 def set_wait_limit(polls: int) -> None:

@@ -117,7 +117,8 @@ la_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_
 struct Layout {
     la::SegPlan plan;
     int64_t heads = 0;
-    size_t rec = 0, total = 0, rrec = 0, rtotal = 0, rowstat = 0, flags = 0, init = 0, init_n = 0, rinit = 0;  // byte offsets
+    size_t rec = 0, total = 0, rrec = 0, rtotal = 0, rowstat = 0, flags = 0, giveups = 0, init = 0, init_n = 0,
+           rinit = 0;  // byte offsets
     bool fused = false;  // backward: both sweeps in one launch
     size_t bytes = 0;
 };
@@ -153,9 +154,11 @@ Layout layout(la_op op, int64_t B, int64_t H, int64_t N, int64_t d) {
         L.rowstat = off;
         off += align_up((size_t)BH * N * 2 * sizeof(float));
         L.fused = !L.plan.scan && la::prefix_forms_records((int)d);
-        if (L.fused) {  // the fused backward's per-segment flags
+        if (L.fused) {  // the fused backward's per-segment flags, and each workgroup's count of waits given up
             L.flags = off;
             off += align_up((size_t)BH * L.plan.nseg * sizeof(unsigned long long));
+            L.giveups = off;
+            off += align_up((size_t)BH * L.plan.nseg * sizeof(unsigned));
         }
         // a start state in split form, its counts, and the record of final-state gradients
         L.init = off;
@@ -795,9 +798,11 @@ static la_status backward_causal(const void* q, const void* k, const void* v, co
     }
     if (L.fused) {
         unsigned long long* flags = reinterpret_cast<unsigned long long*>(ws + L.flags);
+        unsigned* giveups = reinterpret_cast<unsigned*>(ws + L.giveups);
         const unsigned long long epoch = next_epoch();
         if ((e = timed("bwd_fused", s, [&] {
-                 return la::launch_bwd_fused(idt, (int)d, q, k, v, dout, dq, dk, dv, rowstat, rrec, rec, flags, epoch,
+                 return la::launch_bwd_fused(idt, (int)d, q, k, v, dout, dq, dk, dv, rowstat, rrec, rec, flags, giveups,
+                                             epoch,
                                              g_wait_limit.load(std::memory_order_relaxed), BH, N, L.plan, s, init,
                                              init_n, rinit, dS0, dz0, feat);
              })) != hipSuccess)
@@ -833,6 +838,30 @@ la_status la_backward_causal_state(const void* q, const void* k, const void* v, 
                                    int chunk, la_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
     return backward_causal(q, k, v, dout, dq, dk, dv, nullptr, 0, S0, z0, dS_out, dz_out, dS0, dz0, B, H, N, d, chunk,
                            dt, workspace, workspace_bytes, stream);
+}
+
+la_status la_backward_causal_wait_failures(const void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                                           int64_t N, int64_t d, la_dtype dt, void* stream, int64_t* failures_out) {
+    if (failures_out == nullptr) return fail(LA_ERR_INVALID_ARGUMENT, "failures_out is NULL");
+    bool empty = false;
+    la_status st = check_shape(B, H, N, d, 0, dt, &empty);
+    if (st != LA_OK) return st;
+    *failures_out = 0;
+    if (empty) return LA_OK;
+    const Layout L = layout(LA_OP_BWD_CAUSAL, B, H, N, d);
+    if (!L.fused) return LA_OK;  // the separate sweeps wait for nothing
+    if ((st = check_workspace(L, workspace, workspace_bytes)) != LA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+    std::vector<unsigned> slots((size_t)L.heads * L.plan.nseg);
+    e = hipMemcpy(slots.data(), static_cast<const char*>(workspace) + L.giveups, slots.size() * sizeof(unsigned),
+                  hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "copy of the wait counts");
+    int64_t n = 0;
+    for (unsigned c : slots) n += c;
+    *failures_out = n;
+    return LA_OK;
 }
 
 static la_status backward_noncausal(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,

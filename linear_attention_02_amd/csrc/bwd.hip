@@ -129,6 +129,25 @@ __device__ __forceinline__ void bwd_prefix_body(
     }
     zero_state<D>(stR);
     zero_vec<D>(vr);
+    // Whether the segment's key features hold an inf or NaN: the dQ product over the
+    // k-step holding the diagonal tile then takes E(K) with non-finite entries replaced
+    // by 0 (a masked dA is an exact zero, but 0 * inf = NaN would reach earlier rows);
+    // rows t >= s still become NaN through their den, formed from the unreplaced tile.
+    // The segment's own forward record holds z_E = the sum of its E(K), non-finite
+    // exactly then (running-sum records: the next one stands in; the last segment of
+    // such a plan always takes the path).
+    bool ebad;
+    {
+        const int own = prefixed ? seg + 1 : seg;
+        bool bad = own >= nseg;
+        if (!bad) {
+            const float* p = rec + ((int64_t)bh * nseg + own) * Rec<D>::kSize + Rec<D>::kZ;
+#pragma unroll
+            for (int i = 0; i < (D + kWave - 1) / kWave; ++i)
+                if (i * kWave + lane < D) bad = bad || !finite_f(p[i * kWave + lane]);
+        }
+        ebad = __builtin_amdgcn_ballot_w64(bad) != 0;
+    }
 
     ChunkRegs<T, D> ck, cv;
     ChunkRegs<T, D, true> cq;
@@ -312,8 +331,18 @@ __device__ __forceinline__ void bwd_prefix_body(
         for (int k0 = 0; k0 < kC; k0 += KS) {
             if (k0 / 16 <= tt) {
                 const typename M::frag yd = M::acc_op(accGV, k0);
+                auto step = [&](auto san) {
 #pragma unroll
-                for (int m = 0; m < DT; ++m) accQ[m] = M::mma(M::ld_tr_acc(tE, k0, 16 * m, lane), yd, accQ[m]);
+                    for (int m = 0; m < DT; ++m) {
+                        typename M::frag ef = M::ld_tr_acc(tE, k0, 16 * m, lane);
+                        if constexpr (decltype(san)::value) ef = finite_or_zero(ef);
+                        accQ[m] = M::mma(ef, yd, accQ[m]);
+                    }
+                };
+                if (ebad && (k0 + KS - 1) / 16 >= tt)  // the k-step reaching the diagonal tile
+                    step(std::true_type{});
+                else
+                    step(std::false_type{});
             }
         }
         {
@@ -541,8 +570,8 @@ __device__ __forceinline__ void bwd_suffix_body(
         for (int i = 0; i < NY; ++i) {
             const float x = kr.get(i);
             if constexpr (FM::kSplit) {
-                const float c = expc_f(x);
-                ke[i] = to_f32(from_f32<T>(fmaxf(x, c - 1.f)));
+                const float c = expn_f(x);  // NaN for NaN, so phi'(K) carries it into dK
+                ke[i] = to_f32(from_f32<T>(__builtin_elementwise_maximum(x, c - 1.f)));
                 dphik[i] = c;
             } else {
                 ke[i] = to_f32(from_f32<T>(FM::e(x)));
@@ -553,6 +582,15 @@ __device__ __forceinline__ void bwd_suffix_body(
         load_chunk(ci > 0 ? c0 - kC : N, (w + it + 1) & 3);  // past the head: zeros, no memory traffic
         const int tok = c0 + sl;
         __syncthreads();
+        // Rows t of the k-steps that reach the diagonal key tile mix masked (t < s)
+        // and live weights in the dK and dV products.  If one of them holds an inf or
+        // NaN (phi(Q_t) or G_t, then g_t too: den_t or G_t . num_t is not finite), those
+        // products take phi(Q) and G with non-finite entries replaced by 0 (0 * inf =
+        // NaN would reach later keys), and the live weights of such rows carry the NaN
+        // back: dA through g_t, A as A_ts + 0 g_t.
+        constexpr int KSPAN = KS >= 16 ? 2 * 16 : 16;  // rows of the k-steps that reach tile st
+        const int r0 = KS >= 16 ? 32 * (st >> 1) : 16 * st;
+        const bool rbad = __builtin_amdgcn_ballot_w64(!finite_f(s_g[buf][r0 + (lane & (KSPAN - 1))])) != 0;
 
         // (1) dA_ts = G_t.V_s + g_t and A_ts = q_sum_t + phi(Q_t).E(K_s) for s <= t
         //     (accumulators [t][s], all four token tiles, branch free).
@@ -579,15 +617,17 @@ __device__ __forceinline__ void bwd_suffix_body(
                         if constexpr (FM::kSplit) acc_q = M::mma(xq, one, acc_q);
                     }
                     const f32x4 gt4 = lds4(&s_g[buf][16 * i + 4 * g]);
+                    // A_ts + 0 g_t: bitwise A_ts, or NaN where g_t is not finite.
                     if (i > st) {
                         dA[i] = acc_d + gt4;
-                        A[i] = acc_b + acc_q;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) A[i][e] = __builtin_fmaf(gt4[e], 0.f, acc_b[e]) + acc_q[e];
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const bool live = (lane & 15) <= 4 * g + e;
                             dA[i][e] = live ? acc_d[e] + gt4[e] : 0.f;
-                            A[i][e] = live ? acc_b[e] + acc_q[e] : 0.f;
+                            A[i][e] = live ? __builtin_fmaf(gt4[e], 0.f, acc_b[e]) + acc_q[e] : 0.f;
                         }
                     }
                 }
@@ -607,11 +647,23 @@ __device__ __forceinline__ void bwd_suffix_body(
             if ((k0 + KS - 1) / 16 >= st) {
                 const typename M::frag yd = M::acc_op(dA, k0);
                 const typename M::frag ya = M::acc_op(A, k0);
+                auto step = [&](auto san) {
 #pragma unroll
-                for (int m = 0; m < DT; ++m) {
-                    acck[m] = M::mma(M::ld_tr_acc(tQ, k0, 16 * m, lane), yd, acck[m]);
-                    accv[m] = M::mma(M::ld_tr_acc(tG, k0, 16 * m, lane), ya, accv[m]);
-                }
+                    for (int m = 0; m < DT; ++m) {
+                        typename M::frag qf = M::ld_tr_acc(tQ, k0, 16 * m, lane);
+                        typename M::frag gf = M::ld_tr_acc(tG, k0, 16 * m, lane);
+                        if constexpr (decltype(san)::value) {
+                            qf = finite_or_zero(qf);
+                            gf = finite_or_zero(gf);
+                        }
+                        acck[m] = M::mma(qf, yd, acck[m]);
+                        accv[m] = M::mma(gf, ya, accv[m]);
+                    }
+                };
+                if (rbad && k0 / 16 <= st)
+                    step(std::true_type{});
+                else
+                    step(std::false_type{});
             }
         }
         {
@@ -689,7 +741,8 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_fused_ker
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv, float2* __restrict__ rowstat,
     float* __restrict__ rrec, const float* __restrict__ rec, unsigned long long* __restrict__ flags,
-    unsigned long long epoch, int wait_limit, int N, int cps, int nseg, int BH, const float* __restrict__ init,
+    unsigned* __restrict__ giveups, unsigned long long epoch, int wait_limit, int N, int cps, int nseg, int BH,
+    const float* __restrict__ init,
     const float* __restrict__ init_n, const float* __restrict__ rinit, float* __restrict__ dS0,
     float* __restrict__ dz0) {
     constexpr size_t kP = BwdPrefixLds<T, D>::kBytes, kS = BwdSuffixLds<T, D>::kBytes;
@@ -706,6 +759,9 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_fused_ker
     if ((threadIdx.x & 63) == 0)
         for (int j = seg + 1; j < nseg; ++j) ok = ok && await_flag(&hf[j], epoch, wait_limit);
     ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
+    // The host reads these counts back (la_backward_causal_wait_failures): a give-up
+    // leaves NaN rows that must not pass for a result of the data.
+    if (threadIdx.x == 0) giveups[(int64_t)bh * nseg + seg] = ok ? 0u : 1u;
     bwd_suffix_body<T, D, true, kState, FM>(q, k, v, dout, dk, dv, rowstat, rrec, N, cps, nseg, 0, seg, bh, !ok, lds,
                                             rinit, dS0, dz0);
 }
@@ -784,7 +840,8 @@ hipError_t launch_rseg(int dt, int d, const void* q, const void* dout, const flo
 
 hipError_t launch_bwd_fused(int dt, int d, const void* q, const void* k, const void* v, const void* dout, void* dq,
                             void* dk, void* dv, float* rowstat, float* rrec, const float* rec, unsigned long long* flags,
-                            unsigned long long epoch, int wait_limit, int64_t BH, int64_t N, SegPlan p, hipStream_t s,
+                            unsigned* giveups, unsigned long long epoch, int wait_limit, int64_t BH, int64_t N,
+                            SegPlan p, hipStream_t s,
                             const float* init, const float* init_n, const float* rinit, float* dS0, float* dz0,
                             int feat) {
     const dim3 grid((unsigned)(p.nseg * BH));
@@ -793,16 +850,17 @@ hipError_t launch_bwd_fused(int dt, int d, const void* q, const void* k, const v
     if (feat == kFeatGiven)                                                                                       \
         hipLaunchKernelGGL((bwd_fused_kernel<TT, DD, false, FeatGiven>), grid, dim3(kBlock), 0, s, (const TT*)q,   \
                            (const TT*)k, (const TT*)v, (const TT*)dout, (TT*)dq, (TT*)dk, (TT*)dv, (float2*)rowstat, \
-                           rrec, rec, flags, epoch, wait_limit, (int)N, p.cps, p.nseg, (int)BH, nullptr, nullptr,  \
+                           rrec, rec, flags, giveups, epoch, wait_limit, (int)N, p.cps, p.nseg, (int)BH, nullptr, nullptr, \
                            nullptr, nullptr, nullptr);                                                              \
     else if (state)                                                                                              \
         hipLaunchKernelGGL((bwd_fused_kernel<TT, DD, true>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k, \
                            (const TT*)v, (const TT*)dout, (TT*)dq, (TT*)dk, (TT*)dv, (float2*)rowstat, rrec, rec,  \
-                           flags, epoch, wait_limit, (int)N, p.cps, p.nseg, (int)BH, init, init_n, rinit, dS0, dz0); \
+                           flags, giveups, epoch, wait_limit, (int)N, p.cps, p.nseg, (int)BH, init, init_n, rinit, dS0, \
+                           dz0);                                                                                     \
     else                                                                                                         \
         hipLaunchKernelGGL((bwd_fused_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)q, (const TT*)k,     \
                            (const TT*)v, (const TT*)dout, (TT*)dq, (TT*)dk, (TT*)dv, (float2*)rowstat, rrec, rec,  \
-                           flags, epoch, wait_limit, (int)N, p.cps, p.nseg, (int)BH, nullptr, nullptr, nullptr,    \
+                           flags, giveups, epoch, wait_limit, (int)N, p.cps, p.nseg, (int)BH, nullptr, nullptr, nullptr, \
                            nullptr, nullptr)
     if (dt == kBF16) {
         switch (d) {

@@ -49,12 +49,20 @@ __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // 
 // clamps to [0, 1]: phi'(x) = c(x), and since exp(x) >= 1 + x everywhere and
 // c(x) = 1 for x > 0, phi(x) = max(x + 1, c(x)) and E(x) = max(x, c(x) - 1).
 // Each costs four VALU operations (mul, exp, add, max) and no compare or select.
+// NaN propagates: the maxima are IEEE maximum (v_maximum3_f32, NaN if either
+// operand is NaN, same cost as v_max), so phi(NaN) = E(NaN) = NaN even though the
+// clamp turns exp(NaN) into 0.  phi(-inf) = 0, E(-inf) = -1, phi(+inf) = +inf.
 __device__ __forceinline__ float expc_f(float x) {
     return __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(x * 1.4426950408889634f), 0.f, 1.f);
 }
-__device__ __forceinline__ float phi_f(float x) { return fmaxf(x + 1.f, expc_f(x)); }
-__device__ __forceinline__ float elu_f(float x) { return fmaxf(x, expc_f(x) - 1.f); }
-__device__ __forceinline__ float dphi_f(float x) { return expc_f(x); }
+// c(x) as exp(min(x, 0)) without the clamp: NaN for NaN (one more VALU operation),
+// 0 for -inf, 1 for +inf.  For phi'(x) where nothing else carries a NaN of x.
+__device__ __forceinline__ float expn_f(float x) {
+    return __builtin_amdgcn_exp2f(__builtin_elementwise_minimum(x * 1.4426950408889634f, 0.f));
+}
+__device__ __forceinline__ float phi_f(float x) { return __builtin_elementwise_maximum(x + 1.f, expc_f(x)); }
+__device__ __forceinline__ float elu_f(float x) { return __builtin_elementwise_maximum(x, expc_f(x) - 1.f); }
+__device__ __forceinline__ float dphi_f(float x) { return expn_f(x); }
 
 // The feature maps kernels are instantiated for.
 //   FeatElu: phi = elu + 1 elementwise (the default everywhere).  The kernels
@@ -72,7 +80,7 @@ struct FeatElu {
     static constexpr bool kSplit = true;
     __device__ __forceinline__ static float phi(float x) { return phi_f(x); }
     __device__ __forceinline__ static float e(float x) { return elu_f(x); }
-    __device__ __forceinline__ static float dphi_at_phi(float p) { return fminf(p, 1.f); }
+    __device__ __forceinline__ static float dphi_at_phi(float p) { return __builtin_elementwise_minimum(p, 1.f); }
 };
 struct FeatGiven {
     static constexpr bool kSplit = false;
@@ -402,6 +410,36 @@ __device__ __forceinline__ f32x4 lds4(const bf16* p) {
     const uint2 u = *reinterpret_cast<const uint2*>(p);
     const bf16* h = reinterpret_cast<const bf16*>(&u);
     return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+}
+
+// ---- non-finite operands ----------------------------------------------------------------
+// A masked weight is an exact zero, but 0 * inf = NaN: an operand row of a later
+// token that holds inf or NaN would reach earlier rows through the masked part of
+// an in-chunk product.  Where a segment can hold such a row, the kernels replace
+// the non-finite operand values of the products that mix masked and unmasked
+// weights by 0 (finite values pass bitwise unchanged) and restore the non-finite
+// results of the unmasked rows explicitly.
+__device__ __forceinline__ bool finite_f(float x) { return __builtin_isfinite(x); }
+__device__ __forceinline__ float finite_or_zero(float x) {
+    const uint32_t w = __float_as_uint(x);
+    return (w & 0x7f800000u) == 0x7f800000u ? 0.f : x;
+}
+// Two bf16 in a dword: each half becomes +0 where its exponent is all ones.  With
+// h | 0x807f, adding 1 carries into bit 15 (clearing it) exactly when the exponent
+// bits are all ones; a packed 16-bit add keeps the halves apart, and an arithmetic
+// shift by 15 turns bit 15 into the keep-mask.  Four VALU operations per dword.
+__device__ __forceinline__ uint32_t finite_or_zero_bf16x2(uint32_t w) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    typedef short i16x2 __attribute__((ext_vector_type(2)));
+    const u16x2 t = __builtin_bit_cast(u16x2, w | 0x807f807fu) + (u16x2){1, 1};
+    const i16x2 keep = __builtin_bit_cast(i16x2, t) >> (i16x2){15, 15};
+    return w & __builtin_bit_cast(uint32_t, keep);
+}
+__device__ __forceinline__ bf16x8 finite_or_zero(bf16x8 f) {
+    u32x4 w = __builtin_bit_cast(u32x4, f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = finite_or_zero_bf16x2(w[i]);
+    return __builtin_bit_cast(bf16x8, w);
 }
 
 // ---- wave reductions -------------------------------------------------------------------

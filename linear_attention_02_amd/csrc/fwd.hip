@@ -306,6 +306,26 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
     }
 
     // ---- output waves ------------------------------------------------------------------
+    // Whether the segment's values hold an inf or NaN.  Masked in-chunk weights are
+    // exact zeros, but 0 * inf = NaN: the block of 32 keys holding the diagonal then
+    // takes its value operands with non-finite entries replaced by 0, and the rows
+    // t >= s that such a value V_s[b] reaches get O_t[b] = NaN back explicitly, so no
+    // row reads a later token (the recurrent form of "Why It Matters").  The segment's
+    // own record holds P = the sum of its values, non-finite exactly then; with
+    // running-sum records the next one (which includes this segment) stands in, and
+    // the last segment of such a plan always takes the path.
+    bool vbad;
+    {
+        const int own = prefixed ? seg + 1 : seg;
+        bool bad = own >= nseg;
+        if (!bad) {
+            const float* p = rec + ((int64_t)kv * nseg + own) * Rec<D>::kSize + Rec<D>::kP;
+#pragma unroll
+            for (int i = 0; i < (D + kWave - 1) / kWave; ++i)
+                if (i * kWave + lane < D) bad = bad || !finite_f(p[i * kWave + lane]);
+        }
+        vbad = __builtin_amdgcn_ballot_w64(bad) != 0;
+    }
     const GBuf bq(q + hoff, hbytes), bo(o + hoff, hbytes);
     const GBuf bden(den_out != nullptr ? den_out + (int64_t)bh * N : nullptr, den_out != nullptr ? (uint32_t)N * 4 : 0u);
     // Tokens before the chunk (the count of the rank-1 part of z), from the start state's count.
@@ -364,13 +384,23 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
 #pragma unroll
                     for (int e = 0; e < 4; ++e) a[h][e] = lane_bit(lt | (le & diag[e])) ? a[h][e] : zero;
                 }
+                auto av = [&](auto san) {
 #pragma unroll
-                for (int kk = 0; kk < 32; kk += KS) {
-                    const F yf = M::acc_op(a, kk);
+                    for (int kk = 0; kk < 32; kk += KS) {
+                        const F yf = M::acc_op(a, kk);
 #pragma unroll
-                    for (int m = 0; m < DT; ++m) acc[m] = M::mma(M::ld_tr_acc(tV, 32 * kb + kk, 16 * m, lane), yf, acc[m]);
-                    acc[DT] = M::mma(one, yf, acc[DT]);
-                }
+                        for (int m = 0; m < DT; ++m) {
+                            F vf = M::ld_tr_acc(tV, 32 * kb + kk, 16 * m, lane);
+                            if constexpr (decltype(san)::value) vf = finite_or_zero(vf);
+                            acc[m] = M::mma(vf, yf, acc[m]);
+                        }
+                        acc[DT] = M::mma(one, yf, acc[DT]);
+                    }
+                };
+                if (vbad && 2 * kb + 1 >= tt)  // the block holding the diagonal tile
+                    av(std::true_type{});
+                else
+                    av(std::false_type{});
             }
         }
         // State part: S_E^T phi(Q_t) and z_E . phi(Q_t).
@@ -391,6 +421,13 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
             f32x4 x;
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = (acc[m][e] + qs_t * p4[e]) * inv;
+            if (vbad) {  // the non-finite values of keys s <= t that the diagonal block dropped
+                for (int s = 32 * (tt >> 1); s <= tl; ++s) {
+                    const f32x4 vv = lds4(&tV.at(s, b0));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] += vv[e] - vv[e];  // 0, or NaN
+                }
+            }
             gstore4<T>(bo, (uint32_t)(tok * D + b0), x);
         }
         if (den_out != nullptr && g == 0) bden.st4f((uint32_t)tok * 4, den);

@@ -99,10 +99,12 @@ constexpr bool prefix_forms_records(int d) { return d <= 64; }
 constexpr int kDefaultWaitLimit = 1 << 16;
 // Both backward sweeps in one launch (plans without the record scan); flags holds
 // BH * nseg words, epoch is a value no earlier launch on this workspace used,
-// wait_limit bounds the polls of each wait for a later segment's record.
+// wait_limit bounds the polls of each wait for a later segment's record; every
+// workgroup writes the number of its waits that gave up to giveups[BH * nseg].
 hipError_t launch_bwd_fused(int dt, int d, const void* q, const void* k, const void* v, const void* dout, void* dq,
                             void* dk, void* dv, float* rowstat, float* rrec, const float* rec, unsigned long long* flags,
-                            unsigned long long epoch, int wait_limit, int64_t BH, int64_t N, SegPlan p, hipStream_t s,
+                            unsigned* giveups, unsigned long long epoch, int wait_limit, int64_t BH, int64_t N,
+                            SegPlan p, hipStream_t s,
                             const float* init = nullptr, const float* init_n = nullptr, const float* rinit = nullptr,
                             float* dS0 = nullptr, float* dz0 = nullptr, int feat = kFeatElu);
 hipError_t launch_bwd_suffix(int dt, int d, const void* q, const void* k, const void* v,

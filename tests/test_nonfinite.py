@@ -1,0 +1,158 @@
+"""Non-finite inputs on the GPU: causality is strict inside a chunk, and NaN propagates.
+
+Row i of the causal form reads only tokens <= i (page "Efficient Transformers
+Survey", Linear Attention proposition, Why It Matters: the recurrent update of
+(S, z) token by token).  So an inf or NaN in the keys or values of token t0 must
+leave every output row before t0 bitwise as it is without it, and likewise a
+non-finite query or output gradient of token t0 must leave the key-side gradients
+of later keys untouched.  The poisoned token sits inside a 64-token chunk (not at
+a chunk or segment boundary), where masked weights multiply later rows.  Where
+the exact result is not finite, the GPU's must not be finite either: the set of
+non-finite rows (or entries) is the oracle's.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import la_inputs as inp  # noqa: E402
+from test_parity import draw, f64  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def la():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_attention_02_amd as m
+    m.load_library()
+    return m
+
+
+# (B, H, N, d, t0): one segment; several segments of several chunks with t0 in a later one
+CASES = [(1, 2, 256, 64, 130), (1, 8, 64 * 130 + 17, 64, 64 * 70 + 37), (1, 2, 300, 128, 200), (2, 1, 200, 32, 77)]
+IDS = ["N256_t130", "N8337_t4517", "d128_t200", "d32_t77"]
+
+
+def skip_f32_128(dtype, d):
+    if dtype == torch.float32 and d == 128:
+        pytest.skip("fp32 causal path is built for d <= 64")
+
+
+def finite_rows(x):
+    return torch.isfinite(x).all(-1).cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_forward_strict_inside_chunk(la, oracle, case, dtype):
+    """NaN keys and inf values from t0 on: rows < t0 are bitwise unchanged, rows >= t0 are
+    not finite (every one of them, as in the oracle)."""
+    B, H, N, d, t0 = case
+    skip_f32_128(dtype, d)
+    q, k, v, _ = draw(B, H, N, d, dtype, seed=t0)
+    o = la.la_forward_causal(q, k, v)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, t0:] = float("nan")
+    v2[:, :, t0:] = float("inf")
+    o2 = la.la_forward_causal(q, k2, v2)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :, :t0], o2[:, :, :t0])
+    ro = oracle.forward_causal(f64(q), f64(k2), f64(v2))
+    assert (~np.isfinite(ro[:, :, t0:]).all(-1)).all()
+    assert (~finite_rows(o2[:, :, t0:])).all()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_forward_one_infinite_value(la, oracle, case, dtype):
+    """V[t0][5] = inf alone: rows < t0 bitwise unchanged; from t0 on exactly column 5 is not
+    finite, as in the oracle (the other columns never see the value)."""
+    B, H, N, d, t0 = case
+    skip_f32_128(dtype, d)
+    q, k, v, _ = draw(B, H, N, d, dtype, seed=t0 + 1)
+    o = la.la_forward_causal(q, k, v)
+    v2 = v.clone()
+    v2[:, :, t0, 5] = float("inf")
+    o2 = la.la_forward_causal(q, k, v2)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :, :t0], o2[:, :, :t0])
+    ro = oracle.forward_causal(f64(q), f64(k), f64(v2))
+    assert np.array_equal(np.isfinite(ro), torch.isfinite(o2).cpu().numpy())
+
+
+@pytest.mark.parametrize("what", ["q", "k"])
+@pytest.mark.parametrize("case", CASES[:2], ids=IDS[:2])
+def test_forward_nan_propagates(la, oracle, case, what):
+    """One NaN element in a query or a key, values finite: the feature map carries it
+    (phi(NaN) = NaN), so the rows that read it are not finite, as in the oracle."""
+    B, H, N, d, t0 = case
+    q, k, v, _ = draw(B, H, N, d, torch.bfloat16, seed=t0 + 2)
+    x = q if what == "q" else k
+    x[:, :, t0, 3] = float("nan")
+    o = la.la_forward_causal(q, k, v)
+    torch.cuda.synchronize()
+    ro = oracle.forward_causal(f64(q), f64(k), f64(v))
+    assert np.array_equal(np.isfinite(ro).all(-1), finite_rows(o))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_backward_strict_inside_chunk(la, oracle, case, dtype):
+    """NaN keys and inf values from t0 on: dQ rows < t0 are bitwise unchanged (dQ_i reads
+    keys and values <= i only); every gradient row the oracle finds non-finite is non-finite."""
+    B, H, N, d, t0 = case
+    skip_f32_128(dtype, d)
+    q, k, v, do = draw(B, H, N, d, dtype, seed=t0 + 3)
+    g = la.la_backward_causal(q, k, v, do)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, t0:] = float("nan")
+    v2[:, :, t0:] = float("inf")
+    g2 = la.la_backward_causal(q, k2, v2, do)
+    torch.cuda.synchronize()
+    assert torch.equal(g[0][:, :, :t0], g2[0][:, :, :t0])
+    ref = oracle.backward_causal(f64(q), f64(k2), f64(v2), f64(do))
+    for x, r in zip(g2, ref):
+        bad = ~np.isfinite(r).all(-1)
+        assert (~finite_rows(x)[bad]).all()
+
+
+@pytest.mark.parametrize("what", ["q", "dout"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_backward_strict_for_later_keys(la, oracle, case, dtype, what):
+    """A NaN query or output gradient at token t0: dK and dV of keys s > t0 are bitwise
+    unchanged (they read tokens >= s only), as are dQ rows other than t0; dK and dV rows
+    <= t0 and dQ row t0 are not finite, as in the oracle."""
+    B, H, N, d, t0 = case
+    skip_f32_128(dtype, d)
+    q, k, v, do = draw(B, H, N, d, dtype, seed=t0 + 4)
+    g = la.la_backward_causal(q, k, v, do)
+    q2, do2 = q.clone(), do.clone()
+    (q2 if what == "q" else do2)[:, :, t0, 7] = float("nan")
+    g2 = la.la_backward_causal(q2, k, v, do2)
+    torch.cuda.synchronize()
+    for x, y in zip(g[1:], g2[1:]):
+        assert torch.equal(x[:, :, t0 + 1:], y[:, :, t0 + 1:])
+    keep = torch.ones(N, dtype=torch.bool)
+    keep[t0] = False
+    assert torch.equal(g[0][:, :, keep], g2[0][:, :, keep])
+    ref = oracle.backward_causal(f64(q2), f64(k), f64(v), f64(do2))
+    for x, r in zip(g2, ref):
+        assert np.array_equal(np.isfinite(r).all(-1), finite_rows(x))
+
+
+def test_features_forward_strict_inside_chunk(la):
+    """The same on given features (FAVOR+ path): rows < t0 bitwise unchanged."""
+    B, H, N, d, t0 = 1, 2, 256, 64, 150
+    q, k, v = (t.cuda() for t in inp.favor_qkv(B, H, N, d, torch.bfloat16, seed=9))
+    om = inp.favor_omega(d, seed=10).cuda()
+    fq, fk = la.favor_features(q, om), la.favor_features(k, om)
+    o = la.la_forward_causal_features(fq, fk, v)
+    fk2, v2 = fk.clone(), v.clone()
+    fk2[:, :, t0:] = float("nan")
+    v2[:, :, t0:] = float("inf")
+    o2 = la.la_forward_causal_features(fq, fk2, v2)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :, :t0], o2[:, :, :t0])
+    assert (~finite_rows(o2[:, :, t0:])).all()

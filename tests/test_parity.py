@@ -145,6 +145,12 @@ def den_check(den, rden, q, k, dtype, z0=None):
 DEN_BAR = {torch.float32: DEN_TOL[torch.float32], torch.bfloat16: 1.0}
 
 
+def workspace(la, op, q):
+    B, H, N, d = q.shape
+    n = la.workspace_size(op, B, H, N, d, q.dtype)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+
+
 def draw(B, H, N, d, dtype, seed=0, scale=None):
     sc = (dtype == torch.bfloat16) if scale is None else scale
     q, k, v, do = inp.qkv(B, H, N, d, dtype, seed=seed, scale=sc, with_dout=True)
@@ -180,7 +186,9 @@ def run_fwd_noncausal(la, oracle, B, H, N, d, dtype, seed=0, scale=None):
 def run_bwd_causal(la, oracle, B, H, N, d, dtype, seed=0, scale=None, causal=True):
     q, k, v, do = draw(B, H, N, d, dtype, seed, scale)
     if causal:
-        dq, dk, dv = la.la_backward_causal(q, k, v, do)
+        ws = workspace(la, la.LA_OP_BWD_CAUSAL, q)
+        dq, dk, dv = la.la_backward_causal(q, k, v, do, workspace=ws)
+        assert la.backward_wait_failures(ws, q) == 0
     else:
         dq, dk, dv = la.la_backward_noncausal(q, k, v, do)
     torch.cuda.synchronize()

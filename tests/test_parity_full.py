@@ -14,7 +14,8 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 import la_inputs as inp  # noqa: E402
-from test_parity import DEN_BAR, TOL, bwd_rows, den_check, fwd_rows, f64, record, row_ratios, slice_err  # noqa: E402
+from test_parity import (DEN_BAR, TOL, bwd_rows, den_check, fwd_rows, f64, record, row_ratios, slice_err,  # noqa: E402
+                         workspace)
 
 
 @pytest.fixture(scope="module")
@@ -43,7 +44,9 @@ def check_workload(la, oracle, w, nheads, with_bwd, seed=0):
     o, den = la.la_forward_causal(q, k, v, return_den=True)
     dq = dk = dv = None
     if with_bwd:
-        dq, dk, dv = la.la_backward_causal(q, k, v, do)
+        ws = workspace(la, la.LA_OP_BWD_CAUSAL, q)
+        dq, dk, dv = la.la_backward_causal(q, k, v, do, workspace=ws)
+        assert la.backward_wait_failures(ws, q) == 0
     torch.cuda.synchronize()
     idx = pick(w.B * w.H, nheads, seed + 1)
     hq, hk, hv = heads(q, idx), heads(k, idx), heads(v, idx)

@@ -3,10 +3,11 @@
 Where a head has at most 12 segments (and d <= 64) both backward sweeps run in
 one launch: every workgroup publishes its segment's suffix aggregates and waits
 for the later segments' before its suffix sweep.  A wait gives up after a bound
-on its polls; the segment's dk, dv rows then become NaN.  The test forces every
+on its polls; the segment's dk, dv rows then become NaN, and the workgroup counts
+the give-up where la_backward_causal_wait_failures reads it.  The test forces every
 wait to give up at once from the host (bound 0): no kernel faults or hangs, the
-rows that needed a later segment's record are NaN, and everything else is
-bitwise the result of an ordinary call.
+rows that needed a later segment's record are NaN, the count names every such
+workgroup, and everything else is bitwise the result of an ordinary call.
 """
 import os
 import sys
@@ -38,22 +39,28 @@ def test_wait_bound_zero_poisons_only_waiting_segments(la):
     assert all(torch.isfinite(t).all() for t in ref)
     default = la.wait_limit()
     assert default > 0
+    ws = torch.empty(la.workspace_size(la.LA_OP_BWD_CAUSAL, B, H, N, d, q.dtype), dtype=torch.uint8, device="cuda")
+    la.la_backward_causal(q, k, v, do, workspace=ws)
+    assert la.backward_wait_failures(ws, q) == 0
     try:
         la.set_wait_limit(0)
-        dq, dk, dv = la.la_backward_causal(q, k, v, do)
+        dq, dk, dv = la.la_backward_causal(q, k, v, do, workspace=ws)
         torch.cuda.synchronize()
     finally:
         la.set_wait_limit(default)
+    # every segment but the last of each head waited for a later one and gave up
+    assert la.backward_wait_failures(ws, q) == B * H * 7
     # dq comes from the prefix sweep, before any wait
     assert torch.equal(dq, ref[0])
     # the first segment of every head waits for the records of the 7 after it
     assert torch.isnan(dk[:, :, :64].float()).all() and torch.isnan(dv[:, :, :64].float()).all()
     # the last segment waits for nothing: its rows are the ordinary result
     assert torch.equal(dk[:, :, -64:], ref[1][:, :, -64:]) and torch.equal(dv[:, :, -64:], ref[2][:, :, -64:])
-    # and with the bound restored the call is ordinary again
-    again = la.la_backward_causal(q, k, v, do)
+    # and with the bound restored the call is ordinary again, with no give-ups reported
+    again = la.la_backward_causal(q, k, v, do, workspace=ws)
     torch.cuda.synchronize()
     assert all(torch.equal(a, b) for a, b in zip(again, ref))
+    assert la.backward_wait_failures(ws, q) == 0
 
 
 def test_wait_bound_rejects_negative(la):
