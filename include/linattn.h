@@ -341,6 +341,23 @@ la_status la_decode_steps_features_blocks(float* S, float* z, const void* fq, co
                                           int64_t m, la_dtype dt, void* workspace, size_t workspace_bytes,
                                           void* stream);
 
+/* For callers that cannot allocate device memory (code being captured into a HIP
+ * graph, tight serving loops, harnesses that forbid hipMalloc): la_forward_causal
+ * without the workspace argument.  Its workspace is a 64 MiB array that the library
+ * holds as a static device object, one per GPU it runs on, for the life of the
+ * process; the call allocates nothing (with per-kernel timing off, the default) and
+ * takes the array's device address, looked up once per device on its first call
+ * there.  Shapes whose workspace (la_workspace_size(LA_OP_FWD_CAUSAL, ...)) exceeds
+ * 64 MiB are rejected with LA_ERR_WORKSPACE before anything is launched (B H = 64
+ * heads of N = 4096 at d = 64 take 9.7 MiB).  The array is shared by every call on
+ * that GPU and keeps the last call's contents, all of which a call writes before it
+ * reads: calls that overlap on one GPU (other streams, other host threads) race and
+ * must be serialised by the caller.  No saved state.  Everything else (operation,
+ * layouts, start and final states, den_out, chunk, errors) as la_forward_causal. */
+la_status la_forward_causal_noalloc(const void* q, const void* k, const void* v, void* o, const float* S0,
+                                    const float* z0, float* den_out, float* S_out, float* z_out, int64_t B, int64_t H,
+                                    int64_t N, int64_t d, int chunk, la_dtype dt, void* stream);
+
 /* Static description of a status code. */
 const char* la_status_string(la_status s);
 

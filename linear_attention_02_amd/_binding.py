@@ -29,7 +29,7 @@ EXPORTS = ("la_workspace_size", "la_saved_state_size", "la_forward_noncausal", "
            "la_favor_features_backward", "la_favor_features_blocks_backward", "la_backward_causal_features_blocks",
            "la_backward_noncausal_features_blocks", "la_status_string", "la_last_error_message", "la_version",
            "la_profile_enable", "la_profile_count", "la_profile_entry", "la_debug_set_wait_limit",
-           "la_debug_wait_limit")
+           "la_debug_wait_limit", "la_backward_causal_wait_failures", "la_forward_causal_noalloc")
 
 _lib = None
 
@@ -102,6 +102,8 @@ def load_library(path: str | None = None):
     lib.la_forward_causal_features.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_forward_noncausal_features.restype = i32
     lib.la_forward_noncausal_features.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]
+    lib.la_forward_causal_noalloc.restype = i32
+    lib.la_forward_causal_noalloc.argtypes = [vp] * 9 + [i64, i64, i64, i64, i32, i32, vp]
     lib.la_backward_causal_wait_failures.restype = i32
     lib.la_backward_causal_wait_failures.argtypes = [vp, sz, i64, i64, i64, i64, i32, vp, ctypes.POINTER(i64)]
     lib.la_status_string.restype = ctypes.c_char_p
@@ -246,6 +248,18 @@ def la_forward_causal(q, k, v, *, chunk=0, return_den=False, return_state=False,
     if return_state:
         res += [S, z]
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def la_forward_causal_noalloc(q, k, v, o, *, den_out=None, S0=None, z0=None, S_out=None, z_out=None, chunk=0):
+    """la_forward_causal into caller-allocated outputs (o; den_out, S_out, z_out optional), with
+    the library's static device workspace: nothing is allocated, here or in the library."""
+    B, H, N, d = _check_seq(q, k, v, o)
+    _check_state(S0, z0, B, H, d, q.device)
+    _check_state(S_out, z_out, B, H, d, q.device)
+    _check(load_library().la_forward_causal_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(S0), _ptr(z0),
+                                                    _ptr(den_out), _ptr(S_out), _ptr(z_out), B, H, N, d, chunk,
+                                                    _dtype_code(q.dtype), _stream(q.device)))
+    return o
 
 
 def la_backward_causal(q, k, v, dout, *, chunk=0, out=None, workspace=None, saved_state=None):

@@ -447,6 +447,21 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* o, c
 
 }  // namespace
 
+namespace la {
+
+// The causal forward on a workspace the caller supplies (for the entry point whose
+// workspace is a static device array); the same checks and launches as la_forward_causal.
+la_status forward_causal_on(const void* q, const void* k, const void* v, void* o, const float* S0, const float* z0,
+                            float* den_out, float* S_out, float* z_out, int64_t B, int64_t H, int64_t N, int64_t d,
+                            int chunk, la_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+    return forward_causal(q, k, v, o, S0, z0, den_out, S_out, z_out, nullptr, 0, B, H, N, d, chunk, dt, workspace,
+                          workspace_bytes, stream, la::kFeatElu, H);
+}
+
+la_status fail_status(la_status s, const char* msg) { return fail(s, "%s", msg); }
+
+}  // namespace la
+
 extern "C" {
 
 la_status la_forward_noncausal(const void* q, const void* k, const void* v, void* o, void* saved_state,
