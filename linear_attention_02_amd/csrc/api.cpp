@@ -17,6 +17,26 @@
 
 #include "launch.h"
 
+namespace la {
+
+SegPlan plan_segments(int64_t BH, int64_t N) {
+    const int64_t nchunk = (N + kChunk - 1) / kChunk;
+    // Aim for about 512 workgroups (2 per CU): the heavy kernels keep 2-3
+    // workgroups resident per CU, and starting a segment costs one record read
+    // per segment before it, so fewer, longer segments are cheaper.
+    int64_t cps = (BH * nchunk + 511) / 512;
+    if (cps < 1) cps = 1;
+    if (cps > 16) cps = 16;
+    SegPlan p;
+    p.cps = (int)cps;
+    p.nseg = (int)((nchunk + cps - 1) / cps);
+    if (p.nseg < 1) p.nseg = 1;
+    p.scan = p.nseg > kDirectRecordMaxSegments;
+    return p;
+}
+
+}  // namespace la
+
 namespace {
 
 thread_local std::string g_last_error;

@@ -585,22 +585,6 @@ __global__ __launch_bounds__(kBlock) void fill_zero_kernel(float* __restrict__ p
 
 // ---------------------------------------------------------------------------------------
 // Host launchers.
-SegPlan plan_segments(int64_t BH, int64_t N) {
-    const int64_t nchunk = (N + kC - 1) / kC;
-    // Aim for about 512 workgroups (2 per CU): the heavy kernels keep 2-3
-    // workgroups resident per CU, and starting a segment costs one record read
-    // per segment before it, so fewer, longer segments are cheaper.
-    int64_t cps = (BH * nchunk + 511) / 512;
-    if (cps < 1) cps = 1;
-    if (cps > 16) cps = 16;
-    SegPlan p;
-    p.cps = (int)cps;
-    p.nseg = (int)((nchunk + cps - 1) / cps);
-    if (p.nseg < 1) p.nseg = 1;
-    p.scan = p.nseg > kDirectRecordMaxSegments;
-    return p;
-}
-
 #define LA_DISPATCH_D(d, ...)                 \
     switch (d) {                              \
         case 32: {                            \
