@@ -10,7 +10,8 @@ Recipe (the shapes are the workloads the library is measured on):
     fp32 and rounded to the target dtype (round-to-nearest-even for bf16);
   * the output gradient dO ~ N(0, 1) in the target dtype;
   * FAVOR+ random directions (``favor_omega``): a [d, d] fp32 matrix with rows
-    ~ N(0, I_d), from its own seeded generator; FAVOR+ queries and keys
+    ~ N(0, I_d), from its own seeded generator (i.i.d., or orthogonal within each
+    block of d rows); FAVOR+ queries and keys
     (``favor_qkv``) ~ N(0, 1) d^(-1/4), the page's pre-normalization;
   * draws come from one torch.Generator seeded with ``seed``, in the order
     q, k, v, dout.  ``device="cuda"`` draws with the device generator (fast for
@@ -117,10 +118,26 @@ def favor_qkv(B, H, N, d, dtype=torch.bfloat16, seed=0, device="cpu", with_dout=
     return q, k, v, normal((B, H, N, d), gen, dtype, 1.0, device)
 
 
-def favor_omega(d, seed=0, device="cpu", m=None):
-    """FAVOR+ random directions: an [m, d] fp32 matrix (m = d by default) whose rows are drawn from N(0, I_d)."""
-    return torch.randn((d if m is None else m, d), generator=generator(seed, device), dtype=torch.float32,
-                       device=device)
+def favor_omega(d, seed=0, device="cpu", m=None, orthogonal=False):
+    """FAVOR+ random directions: an [m, d] fp32 matrix (m = d by default) whose rows are drawn from N(0, I_d).
+
+    orthogonal: within every block of d rows the directions are exactly orthogonal (the Performer
+    section's orthogonal random features, which lower the estimate's variance below i.i.d. draws):
+    each block is the orthogonal factor of a QR decomposition of a d x d Gaussian matrix (column
+    signs fixed by R's diagonal, so the factor is Haar distributed), its rows scaled by the norms
+    of independent N(0, I_d) vectors, so that every row on its own is still distributed N(0, I_d)."""
+    m = d if m is None else m
+    gen = generator(seed, device)
+    if not orthogonal:
+        return torch.randn((m, d), generator=gen, dtype=torch.float32, device=device)
+    blocks = []
+    for _ in range((m + d - 1) // d):
+        g = torch.randn((d, d), generator=gen, dtype=torch.float64, device=device)
+        qf, r = torch.linalg.qr(g)
+        qf = qf * torch.sign(torch.diagonal(r))[None, :]
+        norms = torch.randn((d, d), generator=gen, dtype=torch.float64, device=device).norm(dim=1)
+        blocks.append(qf.T * norms[:, None])
+    return torch.cat(blocks)[:m].to(torch.float32)
 
 
 def to_f64(x: torch.Tensor):
