@@ -258,6 +258,18 @@ def test_forward_causal(la, oracle, shape, dtype):
     run_fwd_causal(la, oracle, B, H, N, d, dtype, seed=N)
 
 
+# Many heads whose segments hold several chunks each and number at most 12, so
+# that each segment sums the earlier segments' records directly (ragged last
+# segments and token tails included).
+DIRECT_SHAPES = [(3, 16, 4096 + 17, 64), (4, 16, 64 * 40, 64), (2, 32, 64 * 50 + 3, 32)]
+
+
+@pytest.mark.parametrize("shape", DIRECT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_forward_causal_direct_records(la, oracle, shape):
+    B, H, N, d = shape
+    run_fwd_causal(la, oracle, B, H, N, d, torch.bfloat16, seed=N + 9)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_forward_noncausal(la, oracle, shape, dtype):
@@ -445,7 +457,7 @@ def test_saved_state_roundtrip_noncausal(la, shape, dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
-@pytest.mark.parametrize("shape", [(2, 3, 1000, 64), (1, 2, 4096 + 17, 32), (1, 1, 300, 128)],
+@pytest.mark.parametrize("shape", [(2, 3, 1000, 64), (1, 2, 4096 + 17, 32), (1, 1, 300, 128), (3, 16, 4096 + 17, 64)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_saved_state_roundtrip(la, shape, dtype):
     """The backward fed the forward's saved state gives bitwise the results of the one that rebuilds it."""
