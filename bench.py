@@ -142,7 +142,7 @@ def unit_bytes(B, H, N, d, esize=2):
 # written through the ABI (workspace traffic is not algorithmic).
 # The fused backward reads q, k, v, dO and writes dq, dk, dv: 7 units (its second
 # sweep's re-reads of the segment are not algorithmic traffic).
-KERNEL_UNITS = {"seg_state": 2, "causal_fwd": 4, "noncausal_fwd": 2, "bwd_prefix": 5, "bwd_suffix": 6, "bwd_fused": 7,
+KERNEL_UNITS = {"seg_state": 2, "causal_fwd": 4, "causal_fwd_fused": 4, "noncausal_fwd": 2, "bwd_prefix": 5, "bwd_suffix": 6, "bwd_fused": 7,
                 "ncbwd_q": 3, "ncbwd_kv": 4}
 
 

@@ -367,31 +367,40 @@ const char* la_last_error_message(void);
 /* Library version string. */
 const char* la_version(void);
 
-/* Test hook for the fused causal backward (used where a head has at most 12
- * segments and d <= 64).  There each workgroup publishes its segment's suffix
- * aggregates and waits for those of the later segments of its head; a wait that
- * sees no data after `polls` polls (default 65536, tens of milliseconds) gives
- * up, and the dk and dv rows of that segment become NaN instead of using data
- * that never arrived.  polls = 0 makes every such wait give up at once (the last
- * segment of each head, which waits for nothing, is unaffected).  Process-wide;
- * LA_ERR_INVALID_ARGUMENT for polls < 0.  la_debug_wait_limit() returns the bound. */
+/* Test hook for the launches that wait for other workgroups: the fused causal
+ * backward (where a head has at most 12 segments and d <= 64) and the fused causal
+ * forward (where a head has at most 12 segments and every query head has its own
+ * key/value head).  There each workgroup publishes its segment's aggregates and
+ * waits for those of the other segments of its head that it needs (the later ones
+ * in the backward, the earlier ones in the forward); a wait that sees no data after
+ * `polls` polls (default 65536, tens of milliseconds) gives up, and that segment's
+ * rows (dk and dv in the backward, o in the forward) become NaN instead of using
+ * data that never arrived.  polls = 0 makes every such wait give up at once (the
+ * segments that wait for nothing, the last of each head in the backward and the
+ * first in the forward, are unaffected).  Process-wide; LA_ERR_INVALID_ARGUMENT for
+ * polls < 0.  la_debug_wait_limit() returns the bound. */
 la_status la_debug_set_wait_limit(int polls);
 int la_debug_wait_limit(void);
 
 /* For callers that must tell a poisoned result from real NaN data: the number of
- * workgroups whose wait gave up (see above) in the last fused causal backward that
- * ran on `workspace` for this shape (la_backward_causal, la_backward_causal_state,
- * la_backward_causal_features); each one left NaN in its segment's dk and dv rows.
- * Every workgroup of that launch writes its own count into the workspace, so no
- * clearing is needed between calls.  Synchronises `stream` (a hipStream_t, NULL =
- * the default stream) and copies the counts to the host.  *failures_out = 0 for
- * shapes that run the two sweeps as separate launches (more than 12 segments per
- * head, or d = 128), which never wait.  Errors: LA_ERR_INVALID_ARGUMENT
- * (failures_out NULL), shape errors as la_workspace_size, LA_ERR_WORKSPACE
- * (workspace NULL or smaller than la_workspace_size(LA_OP_BWD_CAUSAL, ...)),
- * LA_ERR_HIP (the synchronisation or the copy failed). */
-la_status la_backward_causal_wait_failures(const void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
-                                           int64_t N, int64_t d, la_dtype dt, void* stream, int64_t* failures_out);
+ * workgroups whose wait gave up (see above) in the last launch of `op` that ran on
+ * `workspace` for this shape.  op = LA_OP_BWD_CAUSAL: the fused causal backward
+ * (la_backward_causal, la_backward_causal_state, la_backward_causal_features), each
+ * give-up leaving NaN in its segment's dk and dv rows; op = LA_OP_FWD_CAUSAL: the
+ * fused causal forward (la_forward_causal, la_forward_causal_features,
+ * la_forward_causal_noalloc), each give-up leaving NaN in its segment's o rows (a
+ * causal forward whose key/value heads are shared, la_forward_causal_grouped with
+ * fewer key/value heads or la_forward_causal_features_blocks, runs as two launches,
+ * waits for nothing and sets the counts to zero).  Every workgroup of such
+ * a launch writes its own count into the workspace, so no clearing is needed between
+ * calls.  Synchronises `stream` (a hipStream_t, NULL = the default stream) and copies
+ * the counts to the host.  *failures_out = 0 for shapes whose launches never wait
+ * (more than 12 segments per head; for the backward also d = 128).  Errors:
+ * LA_ERR_INVALID_ARGUMENT (failures_out NULL, or another op), shape errors as
+ * la_workspace_size, LA_ERR_WORKSPACE (workspace NULL or smaller than
+ * la_workspace_size(op, ...)), LA_ERR_HIP (the synchronisation or the copy failed). */
+la_status la_wait_failures(la_op op, const void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t N,
+                           int64_t d, la_dtype dt, void* stream, int64_t* failures_out);
 
 /* Per-kernel timing for benchmarks and profiling.  While enabled (on != 0) on
  * the calling thread, every kernel that a call on this thread launches is
@@ -400,10 +409,11 @@ la_status la_backward_causal_wait_failures(const void* workspace, size_t workspa
  * library creates once with hipEventCreate and reuses (no device memory).
  * la_profile_count() is the number of launches recorded since; entry i
  * synchronises on its stop event and returns the kernel's name ("seg_state",
- * "total", "scan", "causal_fwd", "noncausal_fwd", "bwd_prefix", "rseg", "rscan",
- * "bwd_suffix", "bwd_fused", "ncbwd_q", "ncbwd_kv", "decode", "decode_steps",
- * "state_split", "favor_features", "favor_features_bwd", "combine_blocks", "combine_stats", "stats_from_output", "fill_zero") and
- * its duration in milliseconds. */
+ * "total", "scan", "causal_fwd", "causal_fwd_fused", "noncausal_fwd", "bwd_prefix",
+ * "rseg", "rscan", "bwd_suffix", "bwd_fused", "ncbwd_q", "ncbwd_kv", "decode",
+ * "decode_steps", "state_split", "favor_features", "favor_features_bwd",
+ * "combine_blocks", "combine_stats", "stats_from_output", "fill_zero") and its
+ * duration in milliseconds. */
 la_status la_profile_enable(int on);
 int la_profile_count(void);
 la_status la_profile_entry(int i, const char** name, float* ms);

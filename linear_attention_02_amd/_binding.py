@@ -29,7 +29,7 @@ EXPORTS = ("la_workspace_size", "la_saved_state_size", "la_forward_noncausal", "
            "la_favor_features_backward", "la_favor_features_blocks_backward", "la_backward_causal_features_blocks",
            "la_backward_noncausal_features_blocks", "la_status_string", "la_last_error_message", "la_version",
            "la_profile_enable", "la_profile_count", "la_profile_entry", "la_debug_set_wait_limit",
-           "la_debug_wait_limit", "la_backward_causal_wait_failures", "la_forward_causal_noalloc")
+           "la_debug_wait_limit", "la_wait_failures", "la_forward_causal_noalloc")
 
 _lib = None
 
@@ -104,8 +104,8 @@ def load_library(path: str | None = None):
     lib.la_forward_noncausal_features.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp]
     lib.la_forward_causal_noalloc.restype = i32
     lib.la_forward_causal_noalloc.argtypes = [vp] * 9 + [i64, i64, i64, i64, i32, i32, vp]
-    lib.la_backward_causal_wait_failures.restype = i32
-    lib.la_backward_causal_wait_failures.argtypes = [vp, sz, i64, i64, i64, i64, i32, vp, ctypes.POINTER(i64)]
+    lib.la_wait_failures.restype = i32
+    lib.la_wait_failures.argtypes = [i32, vp, sz, i64, i64, i64, i64, i32, vp, ctypes.POINTER(i64)]
     lib.la_status_string.restype = ctypes.c_char_p
     lib.la_status_string.argtypes = [i32]
     lib.la_last_error_message.restype = ctypes.c_char_p
@@ -702,15 +702,20 @@ def la_forward_noncausal_features(fq, fk, v, *, out=None, workspace=None):
     return o
 
 
-def backward_wait_failures(workspace, q) -> int:
-    """Workgroups whose wait gave up in the last fused causal backward run on `workspace` for
-    inputs shaped like q [B, H, N, d] (their dk, dv rows are NaN); synchronises q's stream."""
+def wait_failures(op, workspace, q) -> int:
+    """Workgroups whose wait gave up in the last launch of op (LA_OP_FWD_CAUSAL or LA_OP_BWD_CAUSAL) run
+    on `workspace` for inputs shaped like q [B, H, N, d] (their rows are NaN); synchronises q's stream."""
     B, H, N, d = q.shape
     out = ctypes.c_int64(0)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load_library().la_backward_causal_wait_failures(_ptr(workspace), nbytes, B, H, N, d, _dtype_code(q.dtype),
-                                                           _stream(q.device), ctypes.byref(out)))
+    _check(load_library().la_wait_failures(op, _ptr(workspace), nbytes, B, H, N, d, _dtype_code(q.dtype),
+                                           _stream(q.device), ctypes.byref(out)))
     return int(out.value)
+
+
+def backward_wait_failures(workspace, q) -> int:
+    """wait_failures of the causal backward."""
+    return wait_failures(LA_OP_BWD_CAUSAL, workspace, q)
 
 
 def set_wait_limit(polls: int) -> None:

@@ -168,6 +168,12 @@ Layout layout(la_op op, int64_t B, int64_t H, int64_t N, int64_t d) {
         off += align_up(totb);
         L.init_n = off;
         off += align_up((size_t)BH * sizeof(float));
+        if (!L.plan.scan) {  // the fused forward's per-segment flags and wait counts
+            L.flags = off;
+            off += align_up((size_t)BH * L.plan.nseg * sizeof(unsigned long long));
+            L.giveups = off;
+            off += align_up((size_t)BH * L.plan.nseg * sizeof(unsigned));
+        }
     } else if (op == LA_OP_BWD_CAUSAL) {
         L.rrec = off;
         off += align_up(recb);
@@ -450,6 +456,19 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* o, c
         (e = timed("state_split", s, [&] { return la::launch_state_split((int)d, S0, z0, init, init_n, BHkv, s, feat); })) !=
             hipSuccess)
         return hip_fail(e, "state_split launch");
+    unsigned* giveups = L.plan.scan ? nullptr : reinterpret_cast<unsigned*>(ws + L.giveups);
+    if (!L.plan.scan && Hkv == H && Gv == 1) {
+        // one launch: every workgroup forms its own segment's record, then waits for the earlier ones
+        unsigned long long* flags = reinterpret_cast<unsigned long long*>(ws + L.flags);
+        const unsigned long long epoch = next_epoch();
+        if ((e = timed("causal_fwd_fused", s, [&] {
+                 return la::launch_causal_fwd_fused(idt, (int)d, q, k, v, o, den_out, rec, S_out, z_out, BH, N,
+                                                    L.plan, s, init, init_n, feat, flags, giveups, epoch,
+                                                    g_wait_limit.load(std::memory_order_relaxed));
+             })) != hipSuccess)
+            return hip_fail(e, "causal_fwd_fused launch");
+        return LA_OK;
+    }
     if ((e = timed("seg_state", s, [&] {
              return la::launch_seg_state(idt, (int)d, k, v, rec, BHkv, N, L.plan, s, feat, (int)Gv);
          })) != hipSuccess)
@@ -459,7 +478,7 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* o, c
         return hip_fail(e, "scan launch");
     if ((e = timed("causal_fwd", s, [&] {
              return la::launch_causal_fwd(idt, (int)d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, L.plan, s, init,
-                                          init_n, feat, (int)(H / Hkv), (int)Gv);
+                                          init_n, feat, (int)(H / Hkv), (int)Gv, giveups);
          })) != hipSuccess)
         return hip_fail(e, "causal_fwd launch");
     return LA_OK;
@@ -875,16 +894,18 @@ la_status la_backward_causal_state(const void* q, const void* k, const void* v, 
                            dt, workspace, workspace_bytes, stream);
 }
 
-la_status la_backward_causal_wait_failures(const void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
-                                           int64_t N, int64_t d, la_dtype dt, void* stream, int64_t* failures_out) {
+la_status la_wait_failures(la_op op, const void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t N,
+                           int64_t d, la_dtype dt, void* stream, int64_t* failures_out) {
     if (failures_out == nullptr) return fail(LA_ERR_INVALID_ARGUMENT, "failures_out is NULL");
+    if (op != LA_OP_FWD_CAUSAL && op != LA_OP_BWD_CAUSAL)
+        return fail(LA_ERR_INVALID_ARGUMENT, "op %d has no waits between workgroups", (int)op);
     bool empty = false;
     la_status st = check_shape(B, H, N, d, 0, dt, &empty);
     if (st != LA_OK) return st;
     *failures_out = 0;
     if (empty) return LA_OK;
-    const Layout L = layout(LA_OP_BWD_CAUSAL, B, H, N, d);
-    if (!L.fused) return LA_OK;  // the separate sweeps wait for nothing
+    const Layout L = layout(op, B, H, N, d);
+    if (op == LA_OP_BWD_CAUSAL ? !L.fused : L.plan.scan) return LA_OK;  // launches that wait for nothing
     if ((st = check_workspace(L, workspace, workspace_bytes)) != LA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipStreamSynchronize(s);

@@ -116,16 +116,25 @@ __device__ __forceinline__ void bwd_prefix_body(
 
     // Prefix state (S_E, z_E, P) at the start of the segment: the records of the
     // segments before it, summed in order; segment aggregates from zero.
+    // The first chunk's loads are in flight while the records arrive.
+    ChunkRegs<T, D> ck, cv;
+    ChunkRegs<T, D, true> cq;
+    RowAcc<T, D> cdo;
+    ck.load(bk, tok_begin, tid);
+    cv.load(bv, tok_begin, tid);
+    cq.load(bq, tok_begin + 16 * w, tid);
+    cdo.load(bdo, tok_begin + 16 * w, lane);
     StateAcc<D> stS, stR;
     VecAcc<D> vz, vp, vr;
     float n = (float)tok_begin;
+    constexpr int kRecRegs = 192 - 4 * (int)(sizeof(ChunkRegs<T, D>) / 4);
     if constexpr (kState) {
-        carried_state<D>(rec + (int64_t)bh * nseg * Rec<D>::kSize, Rec<D>::kSize, seg, prefixed != 0, stS, vz, vp,
-                         lane, w, init != nullptr ? init + (int64_t)bh * Rec<D>::kSize : nullptr);
+        carried_state<D, kRecRegs>(rec + (int64_t)bh * nseg * Rec<D>::kSize, Rec<D>::kSize, seg, prefixed != 0, stS,
+                                   vz, vp, lane, w, init != nullptr ? init + (int64_t)bh * Rec<D>::kSize : nullptr);
         if (init_n != nullptr) n += init_n[bh];
     } else {
-        carried_state<D>(rec + (int64_t)bh * nseg * Rec<D>::kSize, Rec<D>::kSize, seg, prefixed != 0, stS, vz, vp,
-                         lane, w);
+        carried_state<D, kRecRegs>(rec + (int64_t)bh * nseg * Rec<D>::kSize, Rec<D>::kSize, seg, prefixed != 0, stS,
+                                   vz, vp, lane, w);
     }
     zero_state<D>(stR);
     zero_vec<D>(vr);
@@ -149,16 +158,9 @@ __device__ __forceinline__ void bwd_prefix_body(
         ebad = __builtin_amdgcn_ballot_w64(bad) != 0;
     }
 
-    ChunkRegs<T, D> ck, cv;
-    ChunkRegs<T, D, true> cq;
-    RowAcc<T, D> cdo;
     // Wavefront w takes token tile tt = (w + ci) mod 4 of chunk ci: the causal
     // mask leaves tt + 1 key tiles, and the rotation spreads that work evenly
     // over the SIMDs.
-    ck.load(bk, tok_begin, tid);
-    cv.load(bv, tok_begin, tid);
-    cq.load(bq, tok_begin + 16 * w, tid);
-    cdo.load(bdo, tok_begin + 16 * w, lane);
 
     int buf = 0, ci = 0;
     for (int c0 = tok_begin; c0 < tok_end; c0 += kC, buf ^= 1, ++ci) {
@@ -470,11 +472,11 @@ __global__ __launch_bounds__(kBlock, 2) void rseg_kernel(const T* __restrict__ q
 // the final state, which every suffix sum starts from.  dS0, dz0 (nullable): the
 // first segment writes the suffix state at the first token there, the gradient of
 // the start state (S [a][b], z [a] layouts).
-template <typename T, int D, bool kCoherentRecords, bool kState = false, class FM = FeatElu>
+template <typename T, int D, bool kCoherentRecords, bool kState = false, class FM = FeatElu, class Wait>
 __device__ __forceinline__ void bwd_suffix_body(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     T* __restrict__ dk, T* __restrict__ dv, const float2* __restrict__ rowstat, const float* __restrict__ rrec, int N,
-    int cps, int nseg, int prefixed, int seg, int bh, bool poison, char* lds, const float* __restrict__ rinit,
+    int cps, int nseg, int prefixed, int seg, int bh, Wait&& records_ready, char* lds, const float* __restrict__ rinit,
     float* __restrict__ dS0, float* __restrict__ dz0, int Gv = 1) {
     using M = Mma<T>;
     using CR = ChunkRegs<T, D>;
@@ -497,35 +499,6 @@ __device__ __forceinline__ void bwd_suffix_body(
     const int tok_end = min(N, tok_begin + cps * kC);
     const int nch = (tok_end - tok_begin + kC - 1) / kC;
 
-    // Suffix state (R, r): the records of the segments after this one, last segment first.
-    StateAcc<D> stR;
-    VecAcc<D> vr, vunused;
-    const float* ri = kState && rinit != nullptr ? rinit + (int64_t)bh * Rec<D>::kSize : nullptr;
-    if constexpr (kCoherentRecords) {
-        const GBuf brr(rrec + (int64_t)bh * nseg * Rec<D>::kSize, (uint32_t)(nseg * Rec<D>::kSize * 4));
-        if (ri != nullptr) {
-            load_state<D>(ri, stR, lane, w);
-            load_vec<D>(ri + Rec<D>::kZ, vr, lane, w);
-        } else {
-            zero_state<D>(stR);
-            zero_vec<D>(vr);
-        }
-        zero_vec<D>(vunused);
-        add_records_from<D, 192>(RecCoherent{brr}, (int64_t)(nseg - 1) * Rec<D>::kSize, -(int64_t)Rec<D>::kSize,
-                                 nseg - 1 - seg, stR, vr, vunused, lane, w);
-        if (poison) {
-            using ST = StateTiles<D>;
-            const float nan = __builtin_nanf("");
-#pragma unroll
-            for (int ia = 0; ia < ST::NAT; ++ia)
-#pragma unroll
-                for (int ib = 0; ib < ST::NBT; ++ib) stR[ia][ib] = splat4(nan);
-        }
-    } else {
-        carried_state<D>(rrec + ((int64_t)bh * nseg + nseg - 1) * Rec<D>::kSize, -(int64_t)Rec<D>::kSize,
-                         nseg - 1 - seg, prefixed != 0, stR, vr, vunused, lane, w, ri);
-    }
-
     CR cq, cdo;
     RowAcc<T, D> kr, vrow;
     float dn[CR::NV];
@@ -540,7 +513,41 @@ __device__ __forceinline__ void bwd_suffix_body(
         for (int i = 0; i < CR::NV; ++i) dn[i] = brs.ld4f((uint32_t)(c + CR::row(i, tid)) * 8);
         gv = brs.ld4f((uint32_t)(c + (tid & (kC - 1))) * 8 + 4);
     };
+    // The first chunk's loads are in flight while the later segments' records are
+    // awaited (records_ready() false: they could not be confirmed, and the results
+    // are made NaN) and read.
     load_chunk(tok_begin + (nch - 1) * kC, w);
+    const bool poison = !records_ready();
+    constexpr int kRecRegs = 192 - (int)((2 * sizeof(CR) + 2 * sizeof(RowAcc<T, D>)) / 4) - 8;
+
+    // Suffix state (R, r): the records of the segments after this one, last segment first.
+    StateAcc<D> stR;
+    VecAcc<D> vr, vunused;
+    const float* ri = kState && rinit != nullptr ? rinit + (int64_t)bh * Rec<D>::kSize : nullptr;
+    if constexpr (kCoherentRecords) {
+        const GBuf brr(rrec + (int64_t)bh * nseg * Rec<D>::kSize, (uint32_t)(nseg * Rec<D>::kSize * 4));
+        if (ri != nullptr) {
+            load_state<D>(ri, stR, lane, w);
+            load_vec<D>(ri + Rec<D>::kZ, vr, lane, w);
+        } else {
+            zero_state<D>(stR);
+            zero_vec<D>(vr);
+        }
+        zero_vec<D>(vunused);
+        add_records_from<D, kRecRegs>(RecCoherent{brr}, (int64_t)(nseg - 1) * Rec<D>::kSize,
+                                      -(int64_t)Rec<D>::kSize, nseg - 1 - seg, stR, vr, vunused, lane, w);
+        if (poison) {
+            using ST = StateTiles<D>;
+            const float nan = __builtin_nanf("");
+#pragma unroll
+            for (int ia = 0; ia < ST::NAT; ++ia)
+#pragma unroll
+                for (int ib = 0; ib < ST::NBT; ++ib) stR[ia][ib] = splat4(nan);
+        }
+    } else {
+        carried_state<D, kRecRegs>(rrec + ((int64_t)bh * nseg + nseg - 1) * Rec<D>::kSize, -(int64_t)Rec<D>::kSize,
+                                   nseg - 1 - seg, prefixed != 0, stR, vr, vunused, lane, w, ri);
+    }
 
     int buf = 0;
     for (int ci = nch - 1, it = 0; ci >= 0; --ci, ++it, buf ^= 1) {
@@ -724,7 +731,7 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_suffix_ke
     __shared__ __attribute__((aligned(16))) char lds[BwdSuffixLds<T, D>::kBytes];
     const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
     bwd_suffix_body<T, D, false, kState, FM>(q, k, v, dout, dk, dv, rowstat, rrec, N, cps, nseg, prefixed, seg, bh,
-                                             false, lds, rinit, dS0, dz0, Gv);
+                                             [] { return true; }, lds, rinit, dS0, dz0, Gv);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -755,15 +762,18 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_fused_ker
     __syncthreads();
     unsigned long long* hf = flags + (int64_t)bh * nseg;
     if (threadIdx.x == 0) post_flag(&hf[seg], epoch);
-    bool ok = true;
-    if ((threadIdx.x & 63) == 0)
-        for (int j = seg + 1; j < nseg; ++j) ok = ok && await_flag(&hf[j], epoch, wait_limit);
-    ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
-    // The host reads these counts back (la_backward_causal_wait_failures): a give-up
-    // leaves NaN rows that must not pass for a result of the data.
-    if (threadIdx.x == 0) giveups[(int64_t)bh * nseg + seg] = ok ? 0u : 1u;
-    bwd_suffix_body<T, D, true, kState, FM>(q, k, v, dout, dk, dv, rowstat, rrec, N, cps, nseg, 0, seg, bh, !ok, lds,
-                                            rinit, dS0, dz0);
+    auto records_ready = [&] {
+        bool ok = true;
+        if ((threadIdx.x & 63) == 0)
+            for (int j = seg + 1; j < nseg; ++j) ok = ok && await_flag(&hf[j], epoch, wait_limit);
+        ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
+        // The host reads these counts back (la_wait_failures): a give-up
+        // leaves NaN rows that must not pass for a result of the data.
+        if (threadIdx.x == 0) giveups[(int64_t)bh * nseg + seg] = ok ? 0u : 1u;
+        return ok;
+    };
+    bwd_suffix_body<T, D, true, kState, FM>(q, k, v, dout, dk, dv, rowstat, rrec, N, cps, nseg, 0, seg, bh,
+                                            records_ready, lds, rinit, dS0, dz0);
 }
 
 // ---------------------------------------------------------------------------------------

@@ -188,6 +188,15 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(float* __restrict__ rec, i
 //                      all-ones value column in the first product, z_E rows in the second)
 // Chunk loops are unrolled by two so that each chunk's LDS buffer is a
 // compile-time choice (its offsets fold into the instructions).
+//
+// kFused: the segment records are formed in the same launch.  Workgroups are then
+// numbered segment-major, first segments first, and each one first forms its own
+// segment's record (S_E, z_E, P) exactly as seg_state does (same tiles, same chunk
+// order, so bitwise the same record), publishes it with agent-coherent stores and
+// a per-launch flag, and waits (bounded) for the flags of the earlier segments of
+// its head, whose workgroups were dispatched before it.  The carried state then
+// sums their records as in the two-launch form.  A wait that gives up (a missing
+// producer) makes the segment's outputs NaN and is counted in `giveups`.
 template <typename T, int D>
 struct CausalFwdCfg {
     // resident waves per SIMD the register allocation must allow (two workgroups per CU where d <= 64)
@@ -196,12 +205,13 @@ struct CausalFwdCfg {
     static constexpr int kRecordRegs = D <= 64 ? 48 : 128;
 };
 
-template <typename T, int D, class FM = FeatElu>
+template <typename T, int D, class FM = FeatElu, bool kFused = false>
 __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) void causal_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ o,
-    float* __restrict__ den_out, const float* __restrict__ rec, float* __restrict__ S_out, float* __restrict__ z_out,
+    float* __restrict__ den_out, float* __restrict__ rec, float* __restrict__ S_out, float* __restrict__ z_out,
     const float* __restrict__ init, const float* __restrict__ init_n, int N, int cps, int nseg, int BH,
-    int prefixed, int G, int Gv) {
+    int prefixed, int G, int Gv, unsigned long long* __restrict__ flags, unsigned* __restrict__ giveups,
+    unsigned long long epoch, int wait_limit) {
     using M = Mma<T>;
     using F = typename M::frag;
     constexpr int KS = M::KSTEP;
@@ -213,8 +223,9 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
     __shared__ __attribute__((aligned(16))) float s_p[2][D];
 
     // Later segments sum more records: they are dispatched first, since a CU's
-    // older workgroup issues ahead of its younger one.
-    const int seg = nseg - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
+    // older workgroup issues ahead of its younger one (fused: first segments
+    // first, so that every record waited on has a producer dispatched earlier).
+    const int seg = kFused ? (int)(blockIdx.x / BH) : nseg - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
     // Query head bh reads the keys, values, records and start state of key/value
     // head kv (G query heads share one: grouped heads; G = 1: one each), and the
     // values of head kv / Gv (feature blocks of one head share its values).
@@ -226,6 +237,54 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
     const uint32_t hbytes = (uint32_t)N * D * sizeof(T);
     const int tok_begin = seg * cps * kC;
     const int tok_end = min(N, tok_begin + cps * kC);
+    // fused: the head's records (this launch writes them; read agent-coherent)
+    const GBuf brec(rec + (int64_t)kv * nseg * Rec<D>::kSize, (uint32_t)(nseg * Rec<D>::kSize * 4));
+    bool ok = true;  // fused: every earlier segment's record arrived
+
+    if constexpr (!kFused) {
+        // This form waits for nothing: its wait counts (when the workspace keeps them) are zero.
+        if (giveups != nullptr && threadIdx.x == 0) giveups[(int64_t)bh * nseg + seg] = 0u;
+    } else {
+        // ---- the segment's own record, as seg_state forms it ------------------------------
+        if (wv >= 4) {
+            const GBuf bk(k + kvoff, hbytes), bv(v + voff, hbytes);
+            ChunkRegs<T, D> ck, cv;
+            ck.load(bk, tok_begin, rtid);
+            cv.load(bv, tok_begin, rtid);
+            StateAcc<D> st;
+            VecAcc<D> vz, vp;
+            zero_state<D>(st);
+            zero_vec<D>(vz);
+            zero_vec<D>(vp);
+            for (int c0 = tok_begin, b = 0; c0 < tok_end; c0 += kC, b ^= 1) {
+                stage_elu<T, D, FM>(ck, Tile<T, kC, D>{sm_e[b]}, rtid);
+                stage_raw<T, D>(cv, Tile<T, kC, D>{sm_v[b]}, rtid);
+                ck.load(bk, c0 + kC < tok_end ? c0 + kC : N, rtid);
+                cv.load(bv, c0 + kC < tok_end ? c0 + kC : N, rtid);
+                __syncthreads();
+                state_update<T, D, true, true>(st, vz, vp, Tile<T, kC, D>{sm_e[b]}, Tile<T, kC, D>{sm_v[b]}, nullptr,
+                                               nullptr, lane, w);
+            }
+            store_record_coherent<D>(brec, (int64_t)seg * Rec<D>::kSize, st, vz, &vp, lane, w);
+            wait_all_memory();
+        } else {
+            for (int c0 = tok_begin; c0 < tok_end; c0 += kC) __syncthreads();
+        }
+        __syncthreads();  // every state wave's record stores are complete
+        // ---- the earlier segments' records ------------------------------------------------
+        __shared__ int s_ok;
+        unsigned long long* hf = flags + (int64_t)bh * nseg;
+        if (threadIdx.x == 0) {
+            post_flag(&hf[seg], epoch);
+            for (int j = 0; j < seg; ++j) ok = ok && await_flag(&hf[j], epoch, wait_limit);
+            s_ok = ok ? 1 : 0;
+            // The host reads these counts back (la_wait_failures): a give-up leaves NaN
+            // rows that must not pass for a result of the data.
+            giveups[(int64_t)bh * nseg + seg] = ok ? 0u : 1u;
+        }
+        __syncthreads();
+        ok = s_ok != 0;
+    }
 
     if (wv >= 4) {
         // ---- state waves -------------------------------------------------------------
@@ -237,9 +296,35 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
         cv.load(bv, tok_begin, rtid);
         StateAcc<D> st;
         VecAcc<D> vz, vp;
-        carried_state<D, CausalFwdCfg<T, D>::kRecordRegs>(rec + (int64_t)kv * nseg * Rec<D>::kSize, Rec<D>::kSize,
-                                                         seg, prefixed != 0, st, vz, vp, lane, w,
-                                                         init != nullptr ? init + (int64_t)kv * Rec<D>::kSize : nullptr);
+        if constexpr (kFused) {
+            if (init != nullptr) {
+                const float* r = init + (int64_t)kv * Rec<D>::kSize;
+                load_state<D>(r, st, lane, w);
+                load_vec<D>(r + Rec<D>::kZ, vz, lane, w);
+                load_vec<D>(r + Rec<D>::kP, vp, lane, w);
+            } else {
+                zero_state<D>(st);
+                zero_vec<D>(vz);
+                zero_vec<D>(vp);
+            }
+            add_records_from<D, CausalFwdCfg<T, D>::kRecordRegs>(RecCoherent{brec}, 0, Rec<D>::kSize, seg, st, vz, vp,
+                                                                 lane, w);
+            if (!ok) {  // a record never arrived: the segment's outputs become NaN
+                using ST = StateTiles<D>;
+                const float nan = __builtin_nanf("");
+#pragma unroll
+                for (int ia = 0; ia < ST::NAT; ++ia)
+#pragma unroll
+                    for (int ib = 0; ib < ST::NBT; ++ib) st[ia][ib] = splat4(nan);
+#pragma unroll
+                for (int x = 0; x < ST::NVT; ++x) vz[x] = splat4(nan);
+            }
+        } else {
+            carried_state<D, CausalFwdCfg<T, D>::kRecordRegs>(rec + (int64_t)kv * nseg * Rec<D>::kSize, Rec<D>::kSize,
+                                                             seg, prefixed != 0, st, vz, vp, lane, w,
+                                                             init != nullptr ? init + (int64_t)kv * Rec<D>::kSize
+                                                                             : nullptr);
+        }
         publish_state<T, D>(st, Tile<T, D, D>{sm_st[0]}, lane, w);
         store_vec_as<T, D>(s_zb[0], vz, lane, w);
         store_vec<D>(s_p[0], vp, lane, w);
@@ -319,10 +404,14 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
         const int own = prefixed ? seg + 1 : seg;
         bool bad = own >= nseg;
         if (!bad) {
-            const float* p = rec + ((int64_t)kv * nseg + own) * Rec<D>::kSize + Rec<D>::kP;
+            const int64_t p = (int64_t)own * Rec<D>::kSize + Rec<D>::kP;
 #pragma unroll
             for (int i = 0; i < (D + kWave - 1) / kWave; ++i)
-                if (i * kWave + lane < D) bad = bad || !finite_f(p[i * kWave + lane]);
+                if (i * kWave + lane < D)
+                    bad = bad || !finite_f(kFused ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                                        brec.r, (uint32_t)((p + i * kWave + lane) * 4), 0,
+                                                        GBuf::kCoherent))
+                                                  : rec[(int64_t)kv * nseg * Rec<D>::kSize + p + i * kWave + lane]);
         }
         vbad = __builtin_amdgcn_ballot_w64(bad) != 0;
     }
@@ -653,16 +742,17 @@ hipError_t launch_scan(int d, float* rec, int64_t BH, int nseg, int dir, hipStre
     return hipGetLastError();
 }
 
-template <class FM>
+template <class FM, bool kFused>
 static hipError_t launch_causal_fwd_fm(int dt, int d, const void* q, const void* k, const void* v, void* o,
-                                       float* den_out, const float* rec, float* S_out, float* z_out, int64_t BH,
+                                       float* den_out, float* rec, float* S_out, float* z_out, int64_t BH,
                                        int64_t N, SegPlan p, hipStream_t s, const float* init, const float* init_n,
-                                       int G, int Gv) {
+                                       int G, int Gv, unsigned long long* flags, unsigned* giveups,
+                                       unsigned long long epoch, int wait_limit) {
     const dim3 grid((unsigned)(p.nseg * BH));
 #define LA_CFWD(TT, DD)                                                                                          \
-    hipLaunchKernelGGL((causal_fwd_kernel<TT, DD, FM>), grid, dim3(2 * kBlock), 0, s, (const TT*)q, (const TT*)k,   \
-                       (const TT*)v, (TT*)o, den_out, rec, S_out, z_out, init, init_n, (int)N, p.cps, p.nseg,     \
-                       (int)BH, (int)p.scan, G, Gv)
+    hipLaunchKernelGGL((causal_fwd_kernel<TT, DD, FM, kFused>), grid, dim3(2 * kBlock), 0, s, (const TT*)q,       \
+                       (const TT*)k, (const TT*)v, (TT*)o, den_out, rec, S_out, z_out, init, init_n, (int)N, p.cps, \
+                       p.nseg, (int)BH, (int)p.scan, G, Gv, flags, giveups, epoch, wait_limit)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_CFWD(bf16, 32); break;
@@ -683,12 +773,27 @@ static hipError_t launch_causal_fwd_fm(int dt, int d, const void* q, const void*
 
 hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const void* v, void* o, float* den_out,
                              const float* rec, float* S_out, float* z_out, int64_t BH, int64_t N, SegPlan p,
-                             hipStream_t s, const float* init, const float* init_n, int feat, int G, int Gv) {
+                             hipStream_t s, const float* init, const float* init_n, int feat, int G, int Gv,
+                             unsigned* giveups) {
+    float* r = const_cast<float*>(rec);  // only read by this form
     return feat == kFeatGiven
-               ? launch_causal_fwd_fm<FeatGiven>(dt, d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, p, s, init, init_n,
-                                                 G, Gv)
-               : launch_causal_fwd_fm<FeatElu>(dt, d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, p, s, init, init_n,
-                                               G, Gv);
+               ? launch_causal_fwd_fm<FeatGiven, false>(dt, d, q, k, v, o, den_out, r, S_out, z_out, BH, N, p, s, init,
+                                                        init_n, G, Gv, nullptr, giveups, 0, 0)
+               : launch_causal_fwd_fm<FeatElu, false>(dt, d, q, k, v, o, den_out, r, S_out, z_out, BH, N, p, s, init,
+                                                      init_n, G, Gv, nullptr, giveups, 0, 0);
+}
+
+hipError_t launch_causal_fwd_fused(int dt, int d, const void* q, const void* k, const void* v, void* o,
+                                   float* den_out, float* rec, float* S_out, float* z_out, int64_t BH, int64_t N,
+                                   SegPlan p, hipStream_t s, const float* init, const float* init_n, int feat,
+                                   unsigned long long* flags, unsigned* giveups, unsigned long long epoch,
+                                   int wait_limit) {
+    if (p.scan) return hipErrorInvalidValue;  // the records are summed directly
+    return feat == kFeatGiven
+               ? launch_causal_fwd_fm<FeatGiven, true>(dt, d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, p, s, init,
+                                                       init_n, 1, 1, flags, giveups, epoch, wait_limit)
+               : launch_causal_fwd_fm<FeatElu, true>(dt, d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, p, s, init,
+                                                     init_n, 1, 1, flags, giveups, epoch, wait_limit);
 }
 
 template <class FM>

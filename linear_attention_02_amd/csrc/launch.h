@@ -59,11 +59,23 @@ hipError_t launch_scan(int d, float* rec, int64_t BH, int nseg, int dir, hipStre
 // (from launch_state_split); the carried state of every segment starts from them.
 // G: query heads per key/value head (BH counts query heads; k, v, rec, init, S_out
 // and z_out are indexed by key/value head bh / G).  Gv: key/value heads per value head
-// (v is indexed by (bh / G) / Gv).
+// (v is indexed by (bh / G) / Gv).  giveups (nullable, BH * nseg counts): set to zero,
+// so that a wait-count query after this launch reports none.
 hipError_t launch_causal_fwd(int dt, int d, const void* q, const void* k, const void* v, void* o,
                              float* den_out, const float* rec, float* S_out, float* z_out, int64_t BH,
                              int64_t N, SegPlan p, hipStream_t s, const float* init = nullptr,
-                             const float* init_n = nullptr, int feat = kFeatElu, int G = 1, int Gv = 1);
+                             const float* init_n = nullptr, int feat = kFeatElu, int G = 1, int Gv = 1,
+                             unsigned* giveups = nullptr);
+// The same outputs in one launch (plans with !p.scan, one query head per key/value
+// head): each workgroup forms its segment's record into rec itself (bitwise what
+// launch_seg_state writes), publishes it with a flag, and waits for the earlier
+// segments' (flags BH * nseg words, epoch and wait_limit as for the fused backward;
+// giveups BH * nseg counts, 1 where a wait gave up and the segment's rows are NaN).
+hipError_t launch_causal_fwd_fused(int dt, int d, const void* q, const void* k, const void* v, void* o,
+                                   float* den_out, float* rec, float* S_out, float* z_out, int64_t BH, int64_t N,
+                                   SegPlan p, hipStream_t s, const float* init, const float* init_n, int feat,
+                                   unsigned long long* flags, unsigned* giveups, unsigned long long epoch,
+                                   int wait_limit);
 // A start state (S0 [BH][d][d], z0 [BH][d], either nullable = zero) in the carried split
 // form: one record [S0_E^T | z0_E | P0] per head in init, and n0 per head in init_n.
 hipError_t launch_state_split(int d, const float* S0, const float* z0, float* init, float* init_n, int64_t BH,

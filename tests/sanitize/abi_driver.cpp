@@ -131,9 +131,11 @@ int main() {
     });
     int64_t fails = -1;
     check("wait failures: NULL out", LA_ERR_INVALID_ARGUMENT, false,
-          [&] { return la_backward_causal_wait_failures(P(s.w), GB, 4, 16, 4096, 64, LA_BF16, nullptr, nullptr); });
+          [&] { return la_wait_failures(LA_OP_BWD_CAUSAL, P(s.w), GB, 4, 16, 4096, 64, LA_BF16, nullptr, nullptr); });
+    check("wait failures: an op without waits", LA_ERR_INVALID_ARGUMENT, false,
+          [&] { return la_wait_failures(LA_OP_FWD_NONCAUSAL, P(s.w), GB, 4, 16, 4096, 64, LA_BF16, nullptr, &fails); });
     check("wait failures: separate sweeps (d = 128)", LA_OK, false, [&] {
-        return la_backward_causal_wait_failures(P(s.w), GB, 8, 16, 16384, 128, LA_BF16, nullptr, &fails);
+        return la_wait_failures(LA_OP_BWD_CAUSAL, P(s.w), GB, 8, 16, 16384, 128, LA_BF16, nullptr, &fails);
     });
     if (fails != 0) { std::fprintf(stderr, "FAIL wait failures of a non-fused plan: %lld\n", (long long)fails); g_bad = 1; }
 

@@ -159,7 +159,9 @@ def draw(B, H, N, d, dtype, seed=0, scale=None):
 
 def run_fwd_causal(la, oracle, B, H, N, d, dtype, seed=0, scale=None):
     q, k, v, _ = draw(B, H, N, d, dtype, seed, scale)
-    o, den, S, z = la.la_forward_causal(q, k, v, return_den=True, return_state=True)
+    ws = workspace(la, la.LA_OP_FWD_CAUSAL, q)
+    o, den, S, z = la.la_forward_causal(q, k, v, return_den=True, return_state=True, workspace=ws)
+    assert la.wait_failures(la.LA_OP_FWD_CAUSAL, ws, q) == 0
     torch.cuda.synchronize()
     ro, rden, rS, rz = oracle.forward_causal(f64(q), f64(k), f64(v), return_den=True, return_state=True)
     tol = TOL[dtype]

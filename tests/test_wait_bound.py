@@ -1,13 +1,15 @@
-"""The fused causal backward's bounded waits between workgroups (GPU).
+"""Bounded waits between workgroups (GPU): the fused causal backward and forward.
 
 Where a head has at most 12 segments (and d <= 64) both backward sweeps run in
 one launch: every workgroup publishes its segment's suffix aggregates and waits
-for the later segments' before its suffix sweep.  A wait gives up after a bound
-on its polls; the segment's dk, dv rows then become NaN, and the workgroup counts
-the give-up where la_backward_causal_wait_failures reads it.  The test forces every
-wait to give up at once from the host (bound 0): no kernel faults or hangs, the
-rows that needed a later segment's record are NaN, the count names every such
-workgroup, and everything else is bitwise the result of an ordinary call.
+for the later segments' before its suffix sweep.  The fused causal forward
+likewise publishes each segment's record and waits for the earlier segments'.
+A wait gives up after a bound on its polls; the rows of that segment then become
+NaN, and the workgroup counts the give-up where la_wait_failures reads it.  The
+tests force every wait to give up at once from the host (bound 0): no kernel
+faults or hangs, the rows that needed another segment's record are NaN, the
+count names every such workgroup, and everything else is bitwise the result of
+an ordinary call.
 """
 import os
 import sys
@@ -61,6 +63,39 @@ def test_wait_bound_zero_poisons_only_waiting_segments(la):
     torch.cuda.synchronize()
     assert all(torch.equal(a, b) for a, b in zip(again, ref))
     assert la.backward_wait_failures(ws, q) == 0
+
+
+def test_wait_bound_zero_forward(la):
+    # 64 heads x 16 chunks: 8 segments of 2 chunks per head (fused forward)
+    B, H, N, d = 4, 16, 1024, 64
+    q, k, v = [t.cuda() for t in inp.qkv(B, H, N, d, torch.bfloat16, seed=12, scale=True)]
+    ref = la.la_forward_causal(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.isfinite(ref).all()
+    default = la.wait_limit()
+    ws = torch.empty(la.workspace_size(la.LA_OP_FWD_CAUSAL, B, H, N, d, q.dtype), dtype=torch.uint8, device="cuda")
+    la.la_forward_causal(q, k, v, workspace=ws)
+    assert la.wait_failures(la.LA_OP_FWD_CAUSAL, ws, q) == 0
+    try:
+        la.set_wait_limit(0)
+        o = la.la_forward_causal(q, k, v, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        la.set_wait_limit(default)
+    # every segment but the first of each head waited for an earlier one and gave up
+    assert la.wait_failures(la.LA_OP_FWD_CAUSAL, ws, q) == B * H * 7
+    assert torch.equal(o[:, :, :128], ref[:, :, :128])
+    assert torch.isnan(o[:, :, 128:].float()).all()
+    again = la.la_forward_causal(q, k, v, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(again, ref)
+    assert la.wait_failures(la.LA_OP_FWD_CAUSAL, ws, q) == 0
+
+
+def test_wait_failures_rejects_ops_without_waits(la):
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(la.LinAttnError):
+        la.wait_failures(la.LA_OP_FWD_NONCAUSAL, None, q)
 
 
 def test_wait_bound_rejects_negative(la):
