@@ -358,6 +358,48 @@ __device__ __forceinline__ void add_records(const float* rec, int64_t stride, in
     add_records_from<D, kRegs>(RecPtr{rec}, 0, stride, count, st, va, vb, lane, w);
 }
 
+// init + the records at base + j * stride of src for j = 0 .. count-1, element by
+// element in that order (bitwise what add_records_from forms), by all kThreads
+// threads of the workgroup at once, into out (kSize floats, record layout; LDS).
+// Every thread keeps a few 16-byte granules of every record of a batch in flight,
+// so a batch costs one round trip whatever the number of waves that will use it.
+// init (nullable): a record the sum starts from.
+template <int D, int kThreads, typename Src>
+__device__ __forceinline__ void sum_records_to(const Src& src, int64_t base, int64_t stride, int count,
+                                               const float* init, float* out, int tid) {
+    constexpr int G4 = Rec<D>::kSize / 4;  // 16-byte granules of a record
+    static_assert(Rec<D>::kSize % 4 == 0, "records are whole granules");
+    constexpr int PER = (G4 + kThreads - 1) / kThreads;
+    constexpr int RB = PER <= 2 ? 8 : PER <= 4 ? 4 : 2;  // records per batch
+    f32x4 acc[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        const int g = tid + p * kThreads;
+        acc[p] = init != nullptr && g < G4 ? *reinterpret_cast<const f32x4*>(init + 4 * g) : zero4();
+    }
+    for (int j0 = 0; j0 < count; j0 += RB) {
+        f32x4 x[RB][PER];
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+#pragma unroll
+            for (int p = 0; p < PER; ++p) {
+                const int g = tid + p * kThreads;
+                x[b][p] = j0 + b < count && g < G4 ? src.ld4(base + (int64_t)(j0 + b) * stride + 4 * g) : zero4();
+            }
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+            if (j0 + b < count) {
+#pragma unroll
+                for (int p = 0; p < PER; ++p) acc[p] += x[b][p];
+            }
+    }
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        const int g = tid + p * kThreads;
+        if (g < G4) *reinterpret_cast<f32x4*>(out + 4 * g) = acc[p];
+    }
+}
+
 // One record [X^T | a | b] written with agent-coherent stores through b at float
 // index base (b = zeros when vb is null).
 template <int D>

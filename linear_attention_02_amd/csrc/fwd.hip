@@ -216,11 +216,20 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
     using F = typename M::frag;
     constexpr int KS = M::KSTEP;
     constexpr int DT = D / 16;
-    __shared__ __attribute__((aligned(16))) T sm_e[2][kC * D];
-    __shared__ __attribute__((aligned(16))) T sm_v[2][kC * D];
-    __shared__ __attribute__((aligned(16))) T sm_st[2][D * D];
-    __shared__ __attribute__((aligned(16))) T s_zb[2][D];
-    __shared__ __attribute__((aligned(16))) float s_p[2][D];
+    // One block of LDS, so that the fused form can lay a whole fp32 record over
+    // the tiles before the sweep starts.
+    struct Lds {
+        T e[2][kC * D], v[2][kC * D], st[2][D * D], zb[2][D];
+        float p[2][D];
+    };
+    static_assert(sizeof(T) * (4 * kC * D + 2 * D * D) >= sizeof(float) * Rec<D>::kSize,
+                  "a record fits over the tiles");
+    __shared__ __attribute__((aligned(16))) Lds sm;
+    T(&sm_e)[2][kC * D] = sm.e;
+    T(&sm_v)[2][kC * D] = sm.v;
+    T(&sm_st)[2][D * D] = sm.st;
+    T(&s_zb)[2][D] = sm.zb;
+    float(&s_p)[2][D] = sm.p;
 
     // Later segments sum more records: they are dispatched first, since a CU's
     // older workgroup issues ahead of its younger one (fused: first segments
@@ -271,20 +280,33 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
             for (int c0 = tok_begin; c0 < tok_end; c0 += kC) __syncthreads();
         }
         __syncthreads();  // every state wave's record stores are complete
-        // ---- the earlier segments' records ------------------------------------------------
-        __shared__ int s_ok;
-        unsigned long long* hf = flags + (int64_t)bh * nseg;
+    }
+
+    // fused: post this segment's flag, wait for the earlier segments' (bounded), and
+    // sum init + their records (every thread of the workgroup at once) into LDS over
+    // the idle tiles, bitwise what carried_state forms.  Called by both roles, so that
+    // each keeps its own first-chunk loads in flight meanwhile; true if every record
+    // arrived.
+    __shared__ int s_ok;
+    float* const xs = reinterpret_cast<float*>(&sm);
+    auto fused_records = [&]() -> bool {
         if (threadIdx.x == 0) {
+            unsigned long long* hf = flags + (int64_t)bh * nseg;
             post_flag(&hf[seg], epoch);
-            for (int j = 0; j < seg; ++j) ok = ok && await_flag(&hf[j], epoch, wait_limit);
-            s_ok = ok ? 1 : 0;
+            bool all = true;
+            for (int j = 0; j < seg; ++j) all = all && await_flag(&hf[j], epoch, wait_limit);
+            s_ok = all ? 1 : 0;
             // The host reads these counts back (la_wait_failures): a give-up leaves NaN
             // rows that must not pass for a result of the data.
-            giveups[(int64_t)bh * nseg + seg] = ok ? 0u : 1u;
+            giveups[(int64_t)bh * nseg + seg] = all ? 0u : 1u;
         }
         __syncthreads();
-        ok = s_ok != 0;
-    }
+        sum_records_to<D, 2 * kBlock>(RecCoherent{brec}, 0, Rec<D>::kSize, seg,
+                                      init != nullptr ? init + (int64_t)kv * Rec<D>::kSize : nullptr, xs,
+                                      (int)threadIdx.x);
+        __syncthreads();
+        return s_ok != 0;
+    };
 
     if (wv >= 4) {
         // ---- state waves -------------------------------------------------------------
@@ -297,18 +319,11 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
         StateAcc<D> st;
         VecAcc<D> vz, vp;
         if constexpr (kFused) {
-            if (init != nullptr) {
-                const float* r = init + (int64_t)kv * Rec<D>::kSize;
-                load_state<D>(r, st, lane, w);
-                load_vec<D>(r + Rec<D>::kZ, vz, lane, w);
-                load_vec<D>(r + Rec<D>::kP, vp, lane, w);
-            } else {
-                zero_state<D>(st);
-                zero_vec<D>(vz);
-                zero_vec<D>(vp);
-            }
-            add_records_from<D, CausalFwdCfg<T, D>::kRecordRegs>(RecCoherent{brec}, 0, Rec<D>::kSize, seg, st, vz, vp,
-                                                                 lane, w);
+            ok = fused_records();
+            load_state<D>(xs, st, lane, w);
+            load_vec<D>(xs + Rec<D>::kZ, vz, lane, w);
+            load_vec<D>(xs + Rec<D>::kP, vp, lane, w);
+            __syncthreads();  // the sum is read before any wave stages tiles over it
             if (!ok) {  // a record never arrived: the segment's outputs become NaN
                 using ST = StateTiles<D>;
                 const float nan = __builtin_nanf("");
@@ -424,6 +439,10 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
     // over the SIMDs.
     RowFrag<T, D> qr;
     qr.load(bq, tok_begin + 16 * w, lane);
+    if constexpr (kFused) {
+        fused_records();
+        __syncthreads();  // (the state waves read the sum)
+    }
     // Key s = 16 j + 4 g + e of tile j is visible to token t = 16 tt + (lane & 15)
     // iff j < tt, or j == tt and bit lane of diag[e] is set.
     uint64_t diag[4];
