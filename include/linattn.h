@@ -27,7 +27,17 @@
  *     LA_F32 (fp32 everywhere).  Outputs take the input dtype, rounded to
  *     nearest-even from fp32.
  *   - d must be 32, 64 or 128; B, H, N >= 1 (N = 0 is accepted and does
- *     nothing).  chunk is 0 (default) or 64.
+ *     nothing).
+ *   - chunk is 0 (default) or 64, the one chunk length built; 16, 32, 128 and
+ *     every other value return LA_ERR_UNSUPPORTED.  The chunk length changes no
+ *     result beyond rounding (the reassociation of "Intuition"): it is a tiling
+ *     choice, and the kernels map a 64-token chunk onto four 16-row MFMA tiles,
+ *     one per wavefront of a role.
+ *   - LA_F32 at d = 128 is built for the non-causal forward and for decode only:
+ *     the causal forward, the causal backward and the non-causal backward return
+ *     LA_ERR_UNSUPPORTED there (their fp32 tiles and states at d = 128 need more
+ *     LDS and registers per workgroup than a CU has).  bf16 covers d = 128 on
+ *     every call.
  *   - The caller owns every buffer, including the workspace, whose size comes
  *     from la_workspace_size().  The library never allocates or frees device
  *     memory and keeps no device state between calls.
