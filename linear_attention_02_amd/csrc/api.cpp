@@ -23,10 +23,17 @@ SegPlan plan_segments(int64_t BH, int64_t N) {
     const int64_t nchunk = (N + kChunk - 1) / kChunk;
     // Aim for about 512 workgroups (2 per CU): the heavy kernels keep 2-3
     // workgroups resident per CU, and starting a segment costs one record read
-    // per segment before it, so fewer, longer segments are cheaper.
+    // per segment before it, so fewer, longer segments are cheaper.  Segments
+    // grow to 64 chunks where that keeps a head within the segment count whose
+    // records are summed directly (one launch each way, no running-sum pass);
+    // otherwise to 32, past which shorter segments balance the rounds better
+    // (measured at B8 H16 N16384 and B1 H32 N131072, d = 128).
     int64_t cps = (BH * nchunk + 511) / 512;
     if (cps < 1) cps = 1;
-    if (cps > 16) cps = 16;
+    if (cps > 32) {
+        const int64_t longest = cps < 64 ? cps : 64;
+        cps = (nchunk + longest - 1) / longest <= kDirectRecordMaxSegments ? longest : 32;
+    }
     SegPlan p;
     p.cps = (int)cps;
     p.nseg = (int)((nchunk + cps - 1) / cps);

@@ -263,13 +263,21 @@ def test_forward_causal(la, oracle, shape, dtype):
 # Many heads whose segments hold several chunks each and number at most 12, so
 # that each segment sums the earlier segments' records directly (ragged last
 # segments and token tails included).
-DIRECT_SHAPES = [(3, 16, 4096 + 17, 64), (4, 16, 64 * 40, 64), (2, 32, 64 * 50 + 3, 32)]
+# (the last: 256 heads of 41 chunks, two segments of 21 and 20 chunks)
+DIRECT_SHAPES = [(3, 16, 4096 + 17, 64), (4, 16, 64 * 40, 64), (2, 32, 64 * 50 + 3, 32), (4, 64, 64 * 40 + 7, 32)]
 
 
 @pytest.mark.parametrize("shape", DIRECT_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_forward_causal_direct_records(la, oracle, shape):
     B, H, N, d = shape
     run_fwd_causal(la, oracle, B, H, N, d, torch.bfloat16, seed=N + 9)
+
+
+@pytest.mark.parametrize("shape", [(4, 64, 64 * 40 + 7, 32)], ids=lambda s: "x".join(map(str, s)))
+def test_backward_causal_long_segments(la, oracle, shape):
+    """Segments of more than 16 chunks in the fused backward."""
+    B, H, N, d = shape
+    run_bwd_causal(la, oracle, B, H, N, d, torch.bfloat16, seed=N + 10)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
