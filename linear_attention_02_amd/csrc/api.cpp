@@ -89,12 +89,12 @@ struct Timed {
         }
         if (T.names.size() < T.used + 1) T.names.resize(T.used + 1);
         T.names[T.used] = name;
-        hipEventRecord(T.pool[2 * T.used], s);
+        (void)hipEventRecord(T.pool[2 * T.used], s);  // timing only: a failed record leaves no entry time
         stop = T.pool[2 * T.used + 1];
         ++T.used;
     }
     ~Timed() {
-        if (stop != nullptr) hipEventRecord(stop, s);
+        if (stop != nullptr) (void)hipEventRecord(stop, s);
     }
 };
 
@@ -571,6 +571,8 @@ la_status la_favor_features(const void* x, const float* omega, void* out, int64_
 }
 
 // ---- more random features than d: KF = m / d feature blocks -----------------------------
+}  // extern "C"
+
 namespace {
 
 la_status check_blocks(int64_t d, int64_t m) {
@@ -789,7 +791,7 @@ la_status la_forward_noncausal_features_blocks(const void* fq, const void* fk, c
                           workspace, workspace_bytes, stream);
 }
 
-}  // extern "C"
+
 
 static la_status backward_causal(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
                                  void* dv, const void* saved_state, size_t saved_state_bytes, const float* S0,
