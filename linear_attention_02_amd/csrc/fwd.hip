@@ -199,8 +199,9 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(float* __restrict__ rec, i
 // producer) makes the segment's outputs NaN and is counted in `giveups`.
 template <typename T, int D>
 struct CausalFwdCfg {
-    // resident waves per SIMD the register allocation must allow (two workgroups per CU where d <= 64)
-    static constexpr int kWavesPerSimd = D <= 64 ? 4 : 2;
+    // resident waves per SIMD the register allocation must allow (two workgroups per CU where
+    // d <= 64 in bf16 and at d = 32 in fp32; fp32 tiles at d = 64 leave room for one)
+    static constexpr int kWavesPerSimd = (D <= 64 && sizeof(T) == 2) || D <= 32 ? 4 : 2;
     // registers the state waves give to segment records in flight
     static constexpr int kRecordRegs = D <= 64 ? 48 : 128;
 };

@@ -221,7 +221,7 @@ template <typename T, int D, class FM = FeatElu>
 __global__ __launch_bounds__(kBlock, 2) void ncbwd_kv_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                           T* __restrict__ dk, T* __restrict__ dv,
                                                           const float* __restrict__ rtotal, int ntotal, int N,
-                                                          int cps, int nseg, int BH, int Gv) {
+                                                          int cps, int BH, int Gv) {
     using M = Mma<T>;
     constexpr int KS = M::KSTEP;
     constexpr int DT = D / 16;
@@ -362,10 +362,10 @@ hipError_t launch_ncbwd_kv(int dt, int d, const void* k, const void* v, void* dk
 #define LA_NCKV(TT, DD)                                                                                           \
     if (feat == kFeatGiven)                                                                                       \
         hipLaunchKernelGGL((ncbwd_kv_kernel<TT, DD, FeatGiven>), grid, dim3(kBlock), 0, s, (const TT*)k,         \
-                           (const TT*)v, (TT*)dk, (TT*)dv, rtotal, ntotal, (int)N, p.cps, p.nseg, (int)BH, Gv);      \
+                           (const TT*)v, (TT*)dk, (TT*)dv, rtotal, ntotal, (int)N, p.cps, (int)BH, Gv);              \
     else                                                                                                         \
         hipLaunchKernelGGL((ncbwd_kv_kernel<TT, DD>), grid, dim3(kBlock), 0, s, (const TT*)k, (const TT*)v,      \
-                           (TT*)dk, (TT*)dv, rtotal, ntotal, (int)N, p.cps, p.nseg, (int)BH, Gv)
+                           (TT*)dk, (TT*)dv, rtotal, ntotal, (int)N, p.cps, (int)BH, Gv)
     if (dt == kBF16) {
         switch (d) {
             case 32: LA_NCKV(bf16, 32); break;
