@@ -90,6 +90,16 @@ def test_wait_bound_zero_forward(la):
     torch.cuda.synchronize()
     assert torch.equal(again, ref)
     assert la.wait_failures(la.LA_OP_FWD_CAUSAL, ws, q) == 0
+    # a forward with shared key/value heads runs as two launches that wait for nothing:
+    # after the give-ups of a forced bound it leaves the counts at zero
+    try:
+        la.set_wait_limit(0)
+        la.la_forward_causal(q, k, v, workspace=ws)
+    finally:
+        la.set_wait_limit(default)
+    assert la.wait_failures(la.LA_OP_FWD_CAUSAL, ws, q) == B * H * 7
+    la.la_forward_causal_grouped(q, k[:, :4].contiguous(), v[:, :4].contiguous(), workspace=ws)
+    assert la.wait_failures(la.LA_OP_FWD_CAUSAL, ws, q) == 0
 
 
 def test_wait_failures_rejects_ops_without_waits(la):
