@@ -41,7 +41,9 @@ def pick(BH, n, seed):
 
 def check_workload(la, oracle, w, nheads, with_bwd, seed=0):
     q, k, v, do = inp.workload_inputs(w, seed=seed, device="cuda", with_dout=True)
-    o, den = la.la_forward_causal(q, k, v, return_den=True)
+    wsf = workspace(la, la.LA_OP_FWD_CAUSAL, q)
+    o, den = la.la_forward_causal(q, k, v, return_den=True, workspace=wsf)
+    assert la.wait_failures(la.LA_OP_FWD_CAUSAL, wsf, q) == 0
     dq = dk = dv = None
     if with_bwd:
         ws = workspace(la, la.LA_OP_BWD_CAUSAL, q)
@@ -66,6 +68,22 @@ def check_workload(la, oracle, w, nheads, with_bwd, seed=0):
 
 def test_mid_all_heads(la, oracle):
     check_workload(la, oracle, inp.MID, nheads=10**9, with_bwd=True)
+
+
+def test_grid_beyond_residency(la, oracle):
+    """B4 H512 N8192 d32 bf16: 2048 heads of two segments each, 4096 workgroups per fused
+    launch, more than the chip holds at once.  A workgroup that waits on another segment's
+    record only waits on workgroups dispatched before it (first segments first in the forward,
+    last segments first in the backward), so both launches finish with no wait given up and
+    sampled heads match the oracle."""
+    w = inp.Workload("wide grid", 4, 512, 8192, 32, torch.bfloat16, True)
+    la.profile_enable(True)
+    try:
+        check_workload(la, oracle, w, nheads=8, with_bwd=True, seed=3)
+        names = {n for n, _ in la.profile_entries()}
+    finally:
+        la.profile_enable(False)
+    assert {"causal_fwd_fused", "bwd_fused"} <= names, names
 
 
 def test_mid_noncausal_all_heads(la, oracle):
