@@ -46,8 +46,12 @@ struct BwdPrefixLds {
 };
 template <typename T, int D>
 struct BwdSuffixLds {
+    // The G tiles sit 256 bytes past a multiple of 512 from the phi(Q) tiles (the bank
+    // mapping repeats every 256 bytes): no paired LDS read can then fetch a phi(Q) half
+    // and a G half together, which would cost register moves to assemble the operands.
     static constexpr size_t kTile = (size_t)kC * D * sizeof(T), kSt = (size_t)D * D * sizeof(T);
-    static constexpr size_t oQ = 0, oG = 2 * kTile, oRt = 4 * kTile, oGv = oRt + 2 * kSt, oR = oGv + 2 * kC * 4;
+    static constexpr size_t oQ = 0, oG = 2 * kTile + 256, oRt = oG + 2 * kTile + 256, oGv = oRt + 2 * kSt,
+                            oR = oGv + 2 * kC * 4;
     static constexpr size_t kBytes = oR + 2 * D * 4;
 };
 
@@ -555,7 +559,9 @@ __device__ __forceinline__ void bwd_suffix_body(
         const int st = (w + it) & 3;
         const int sl = 16 * st + (lane & 15);  // this lane's key
         const Tile<T, kC, D> tQ{sm_q[buf]}, tG{sm_g[buf]};
-        const Tile<T, D, D> tRt{sm_rt[buf]};
+        // R^T is read as accumulator-order operands (ld_acc) and transposed: bf16 tiles
+        // keep those operands' columns together.
+        const Tile<T, D, D, std::is_same<T, bf16>::value> tRt{sm_rt[buf]};
         publish_state<T, D>(stR, tRt, lane, w);
         store_vec<D>(s_r[buf], vr, lane, w);
         stage_phi<T, D, false, FM>(cq, tQ, tid);

@@ -308,12 +308,13 @@ struct RecCoherent {
 // Add the segment records at base + j * stride of src for j = 0 .. count-1, in
 // that order, to the wave's state tiles and vector tiles (fixed order: bitwise
 // reproducible).  kRegs: registers the records in flight may take (at most 8
-// records per batch).
-template <int D, int kRegs, typename Src>
+// records per batch).  kVecB false: the records' second vector is not read (vb is
+// left as it is), so that more records fit a batch.
+template <int D, int kRegs, bool kVecB = true, typename Src>
 __device__ __forceinline__ void add_records_from(const Src& src, int64_t base, int64_t stride, int count,
                                                  StateAcc<D>& st, VecAcc<D>& va, VecAcc<D>& vb, int lane, int w) {
     using ST = StateTiles<D>;
-    constexpr int PER_REC = 4 * (ST::NAT * ST::NBT + 2 * ST::NVT);
+    constexpr int PER_REC = 4 * (ST::NAT * ST::NBT + (kVecB ? 2 : 1) * ST::NVT);
     constexpr int B = kRegs / PER_REC >= 8 ? 8 : kRegs / PER_REC >= 1 ? kRegs / PER_REC : 1;
     for (int j0 = 0; j0 < count; j0 += B) {
         f32x4 xs[B][ST::NAT][ST::NBT], xa[B][ST::NVT], xb[B][ST::NVT];
@@ -330,7 +331,7 @@ __device__ __forceinline__ void add_records_from(const Src& src, int64_t base, i
                 for (int x = 0; x < ST::NVT; ++x) {
                     const int o = (ST::vt0(w) + x) * 16 + 4 * (lane >> 4);
                     xa[b][x] = src.ld4(r + Rec<D>::kZ + o);
-                    xb[b][x] = src.ld4(r + Rec<D>::kP + o);
+                    if constexpr (kVecB) xb[b][x] = src.ld4(r + Rec<D>::kP + o);
                 }
             }
         }
@@ -344,7 +345,7 @@ __device__ __forceinline__ void add_records_from(const Src& src, int64_t base, i
 #pragma unroll
                 for (int x = 0; x < ST::NVT; ++x) {
                     va[x] += xa[b][x];
-                    vb[x] += xb[b][x];
+                    if constexpr (kVecB) vb[x] += xb[b][x];
                 }
             }
         }
@@ -352,10 +353,10 @@ __device__ __forceinline__ void add_records_from(const Src& src, int64_t base, i
 }
 
 // The same for records read through a plain pointer: rec[j * stride], j = 0 .. count-1.
-template <int D, int kRegs = 192>
+template <int D, int kRegs = 192, bool kVecB = true>
 __device__ __forceinline__ void add_records(const float* rec, int64_t stride, int count, StateAcc<D>& st,
                                             VecAcc<D>& va, VecAcc<D>& vb, int lane, int w) {
-    add_records_from<D, kRegs>(RecPtr{rec}, 0, stride, count, st, va, vb, lane, w);
+    add_records_from<D, kRegs, kVecB>(RecPtr{rec}, 0, stride, count, st, va, vb, lane, w);
 }
 
 // init + the records at base + j * stride of src for j = 0 .. count-1, element by
@@ -427,7 +428,7 @@ __device__ __forceinline__ void store_record_coherent(const GBuf& buf, int64_t b
 // sum; otherwise the records are added here.  Either way the result is bitwise
 // the same.  init (nullable): a record the sum starts from (a scan starts from
 // it too, so a prefixed record already holds it).
-template <int D, int kRegs = 192>
+template <int D, int kRegs = 192, bool kVecB = true>
 __device__ __forceinline__ void carried_state(const float* first, int64_t stride, int count, bool prefixed,
                                               StateAcc<D>& st, VecAcc<D>& va, VecAcc<D>& vb, int lane, int w,
                                               const float* init = nullptr) {
@@ -446,12 +447,12 @@ __device__ __forceinline__ void carried_state(const float* first, int64_t stride
             zero_vec<D>(va);
             zero_vec<D>(vb);
         }
-        add_records<D, kRegs>(first, stride, count, st, va, vb, lane, w);
+        add_records<D, kRegs, kVecB>(first, stride, count, st, va, vb, lane, w);
     }
 }
 
-template <typename T, int D>
-__device__ __forceinline__ void publish_state(const StateAcc<D>& st, const Tile<T, D, D>& tXt, int lane, int w) {
+template <typename T, int D, bool A>
+__device__ __forceinline__ void publish_state(const StateAcc<D>& st, const Tile<T, D, D, A>& tXt, int lane, int w) {
     using ST = StateTiles<D>;
 #pragma unroll
     for (int ia = 0; ia < ST::NAT; ++ia)

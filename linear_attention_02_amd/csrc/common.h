@@ -191,7 +191,12 @@ __device__ __forceinline__ void raw_barrier() {
 // ROWS x COLS elements of OT, row-major, with the 16-byte granule index of each
 // row XOR-ed by a row-dependent value so that 16-row operand reads, 8-row
 // granule writes and 4-row transposing reads all spread over the banks.
-template <typename OT, int ROWS, int COLS>
+// kAccCols: within each 32-column block the 4-column groups are stored in the order
+// 0 4 1 5 2 6 3 7, so that the k values an accumulator-order operand takes in one lane
+// (columns k0 + 4 j .. + 3 and k0 + 16 + 4 j .. + 3) are one 16-byte granule.  Such a
+// tile is written 4 columns at a time (store4, store_T) and read by ld_acc and the
+// transposing loads; whole-granule writes and Mma::ld do not apply to it.
+template <typename OT, int ROWS, int COLS, bool kAccCols = false>
 struct Tile {
     static constexpr int EV = 16 / (int)sizeof(OT);
     static constexpr int G = COLS / EV;
@@ -208,10 +213,23 @@ struct Tile {
     __device__ __forceinline__ static int swz(int r) {
         return G >= 8 ? 2 * (r & 3) + ((r >> 2) & 1) : 2 * ((r >> 1) & 1) + ((r >> 2) & 1);
     }
-    __device__ __forceinline__ int off(int r, int c) const {
-        return r * COLS + (((c / EV) ^ swz(r)) * EV) + (c % EV);
+    __device__ __forceinline__ static int col(int c) {
+        if constexpr (kAccCols) {
+            static_assert(sizeof(OT) == 2 && COLS % 32 == 0, "acc-order columns are for bf16 tiles of 32-column blocks");
+            const int q = (c >> 2) & 7;
+            return (c & ~31) | ((2 * (q & 3) + (q >> 2)) << 2) | (c & 3);
+        } else {
+            return c;
+        }
     }
-    __device__ __forceinline__ OT* granule(int r, int gi) const { return p + r * COLS + ((gi ^ swz(r)) * EV); }
+    __device__ __forceinline__ int off(int r, int c) const {
+        const int cc = col(c);
+        return r * COLS + (((cc / EV) ^ swz(r)) * EV) + (cc % EV);
+    }
+    __device__ __forceinline__ OT* granule(int r, int gi) const {
+        static_assert(!kAccCols, "whole granules of an acc-order tile are not consecutive columns");
+        return p + r * COLS + ((gi ^ swz(r)) * EV);
+    }
     __device__ __forceinline__ OT& at(int r, int c) const { return p[off(r, c)]; }
 };
 
@@ -250,8 +268,8 @@ struct Mma<bf16> {
     // As ld_tr, but lane l takes the k values k0 + 4 (l >> 4) + 0..3 and
     // k0 + 16 + 4 (l >> 4) + 0..3: the rows that accumulator tiles k0/16 and
     // k0/16 + 1 hold in lane l, so that such a pair can be the other operand (acc_op).
-    template <int R, int K>
-    __device__ __forceinline__ static frag ld_tr_acc(const Tile<bf16, R, K>& t, int k0, int col0, int lane) {
+    template <int R, int K, bool A>
+    __device__ __forceinline__ static frag ld_tr_acc(const Tile<bf16, R, K, A>& t, int k0, int col0, int lane) {
         typedef __attribute__((address_space(3))) bf16x4 lds4;
         const int j = lane & 15;
         const int r = k0 + 4 * (lane >> 4) + (j >> 2);
@@ -262,12 +280,16 @@ struct Mma<bf16> {
     }
     // As ld, in the k order of ld_tr_acc: lane l takes columns k0 + 4 (l >> 4) + 0..3
     // and k0 + 16 + 4 (l >> 4) + 0..3 of its row.
-    template <int R, int K>
-    __device__ __forceinline__ static frag ld_acc(const Tile<bf16, R, K>& t, int row0, int k0, int lane) {
+    template <int R, int K, bool A>
+    __device__ __forceinline__ static frag ld_acc(const Tile<bf16, R, K, A>& t, int row0, int k0, int lane) {
         const int r = row0 + (lane & 15), c = k0 + 4 * (lane >> 4);
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&t.at(r, c));
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(&t.at(r, c + 16));
-        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        if constexpr (A) {
+            return *reinterpret_cast<const frag*>(&t.at(r, c));  // one granule
+        } else {
+            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&t.at(r, c));
+            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(&t.at(r, c + 16));
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
     }
     // Operand for k-step k0 from per-lane values in accumulator order: y[4 m + e]
     // is the value at k = 16 m + 4 (l >> 4) + e (the layout of an accumulator
@@ -399,8 +421,8 @@ __device__ __forceinline__ void store4(bf16* p, f32x4 a) {
 }
 __device__ __forceinline__ void store4(float* p, f32x4 a) { *reinterpret_cast<f32x4*>(p) = a; }
 
-template <typename OT, int ROWS, int COLS>
-__device__ __forceinline__ void store_T(const Tile<OT, ROWS, COLS>& dst, int row0, int col0, f32x4 acc, int lane) {
+template <typename OT, int ROWS, int COLS, bool A>
+__device__ __forceinline__ void store_T(const Tile<OT, ROWS, COLS, A>& dst, int row0, int col0, f32x4 acc, int lane) {
     store4(&dst.at(col0 + (lane & 15), row0 + 4 * (lane >> 4)), acc);
 }
 

@@ -228,7 +228,9 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_kv_kernel(const T* __restrict
     constexpr int NY = D / 4;
     __shared__ __attribute__((aligned(16))) T sm_rt[D * D];
     __shared__ __attribute__((aligned(16))) float s_r[D];
-    const Tile<T, D, D> tRt{sm_rt};
+    // R^T is read as accumulator-order operands (ld_acc) and transposed: bf16 tiles keep
+    // those operands' columns together.
+    const Tile<T, D, D, std::is_same<T, bf16>::value> tRt{sm_rt};
 
     const int seg = blockIdx.x / BH, bh = blockIdx.x % BH;
     const int lane = threadIdx.x & 63, w = wave_id(), g = lane >> 4;
@@ -244,8 +246,8 @@ __global__ __launch_bounds__(kBlock, 2) void ncbwd_kv_kernel(const T* __restrict
         zero_state<D>(stR);
         zero_vec<D>(vr);
         zero_vec<D>(vunused);
-        add_records<D, 64>(rtotal + (int64_t)bh * ntotal * Rec<D>::kSize, Rec<D>::kSize, ntotal, stR, vr, vunused, lane,
-                       w);
+        add_records<D, 64, false>(rtotal + (int64_t)bh * ntotal * Rec<D>::kSize, Rec<D>::kSize, ntotal, stR, vr,
+                                  vunused, lane, w);
         publish_state<T, D>(stR, tRt, lane, w);
         store_vec<D>(s_r, vr, lane, w);
     }
