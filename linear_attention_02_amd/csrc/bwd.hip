@@ -778,6 +778,10 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_fused_ker
         if (threadIdx.x == 0) giveups[(int64_t)bh * nseg + seg] = ok ? 0u : 1u;
         return ok;
     };
+    // The first half of the segments (dispatched last, so usually the younger of the
+    // two workgroups on a CU, the one the SIMDs serve second) sum the most records
+    // and start their suffix sweeps last: they take the higher wave priority for it.
+    if (2 * seg < nseg) __builtin_amdgcn_s_setprio(1);
     bwd_suffix_body<T, D, true, kState, FM>(q, k, v, dout, dk, dv, rowstat, rrec, N, cps, nseg, 0, seg, bh,
                                             records_ready, lds, rinit, dS0, dz0);
 }

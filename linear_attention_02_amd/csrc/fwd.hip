@@ -321,6 +321,7 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
         VecAcc<D> vz, vp;
         if constexpr (kFused) {
             ok = fused_records();
+            if (2 * seg >= nseg) __builtin_amdgcn_s_setprio(1);  // as the output waves below
             load_state<D>(xs, st, lane, w);
             load_vec<D>(xs + Rec<D>::kZ, vz, lane, w);
             load_vec<D>(xs + Rec<D>::kP, vp, lane, w);
@@ -443,6 +444,10 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
     if constexpr (kFused) {
         fused_records();
         __syncthreads();  // (the state waves read the sum)
+        // The second half of the segments (dispatched last, so usually the younger of
+        // the two workgroups on a CU, the one the SIMDs serve second) wait for the most
+        // records and start their sweeps last: they take the higher wave priority for it.
+        if (2 * seg >= nseg) __builtin_amdgcn_s_setprio(1);
     }
     // Key s = 16 j + 4 g + e of tile j is visible to token t = 16 tt + (lane & 15)
     // iff j < tt, or j == tt and bit lane of diag[e] is set.
