@@ -19,20 +19,30 @@
 
 namespace la {
 
-SegPlan plan_segments(int64_t BH, int64_t N) {
+SegPlan plan_segments(int64_t BH, int64_t N, int64_t d) {
     const int64_t nchunk = (N + kChunk - 1) / kChunk;
     // Aim for about 512 workgroups (2 per CU): the heavy kernels keep 2-3
     // workgroups resident per CU, and starting a segment costs one record read
     // per segment before it, so fewer, longer segments are cheaper.  Segments
     // grow to 64 chunks where that keeps a head within the segment count whose
-    // records are summed directly (one launch each way, no running-sum pass);
-    // otherwise to 32, past which shorter segments balance the rounds better
-    // (measured at B8 H16 N16384 and B1 H32 N131072, d = 128).
-    int64_t cps = (BH * nchunk + 511) / 512;
+    // records are summed directly (one launch each way, no running-sum pass).
+    // Past that, at d = 128 (whose sweeps hold one workgroup per CU), one round
+    // of workgroups that keeps at least 3/4 of the 256 CUs busy with at most that
+    // many segments per head is taken (the fused forward at B1 H32 N131072: 1.34
+    // against 1.52 ms for a running-sum plan); otherwise segments of 32 chunks,
+    // past which shorter segments balance the rounds better.
+    constexpr int64_t kCUs = 256;
+    int64_t cps = (BH * nchunk + 2 * kCUs - 1) / (2 * kCUs);
     if (cps < 1) cps = 1;
     if (cps > 32) {
         const int64_t longest = cps < 64 ? cps : 64;
-        cps = (nchunk + longest - 1) / longest <= kDirectRecordMaxSegments ? longest : 32;
+        const int64_t one_round = d >= 128 ? kCUs / BH : 0;  // segments per head
+        if ((nchunk + longest - 1) / longest <= kDirectRecordMaxSegments)
+            cps = longest;
+        else if (one_round >= 1 && one_round <= kDirectRecordMaxSegments && 4 * BH * one_round >= 3 * kCUs)
+            cps = (nchunk + one_round - 1) / one_round;
+        else
+            cps = 32;
     }
     SegPlan p;
     p.cps = (int)cps;
@@ -153,7 +163,7 @@ struct Layout {
 Layout layout(la_op op, int64_t B, int64_t H, int64_t N, int64_t d) {
     Layout L;
     const int64_t BH = B * H;
-    L.plan = la::plan_segments(BH, N);
+    L.plan = la::plan_segments(BH, N, d);
     L.heads = BH;
     const size_t recb = (size_t)BH * L.plan.nseg * la::rec_floats(d) * sizeof(float);
     size_t off = 0;
@@ -228,7 +238,7 @@ unsigned long long next_epoch() {
 // The saved forward state: every segment record, then (filled by the non-causal
 // forward only) one total per head.
 size_t saved_records_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
-    const la::SegPlan p = la::plan_segments(B * H, N);
+    const la::SegPlan p = la::plan_segments(B * H, N, d);
     return align_up((size_t)(B * H) * p.nseg * la::rec_floats(d) * sizeof(float));
 }
 

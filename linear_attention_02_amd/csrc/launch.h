@@ -37,7 +37,7 @@ struct SegPlan {
 // (each workgroup re-reads its predecessors' records: quadratic in the segment
 // count, cheaper than a scan pass only while that count is small).
 constexpr int kDirectRecordMaxSegments = 12;
-SegPlan plan_segments(int64_t BH, int64_t N);
+SegPlan plan_segments(int64_t BH, int64_t N, int64_t d);
 
 // Number of floats in one segment-state record for head dimension d:
 // S_E^T [d][d], z_E [d], P [d].
