@@ -103,7 +103,11 @@ int main() {
     check("fwd: no tokens", LA_OK, false, [&] { return fwd(4, 16, 0, 64, 0, 0, 0, 0); });
     check("fwd: fp32 d=128", LA_ERR_UNSUPPORTED, false, [&] { return fwd(1, 1, 64, 128, s.q, s.o, s.w, GB, LA_F32); });
     const size_t wv = ws(LA_OP_FWD_CAUSAL, 1, 32, 131072, 128);
-    check("fwd: valid Very long (scan plan)", LA_OK, true, [&] { return fwd(1, 32, 131072, 128, s.q, s.o, s.w, wv); });
+    check("fwd: valid Very long (one round of 8 segments per head)", LA_OK, true,
+          [&] { return fwd(1, 32, 131072, 128, s.q, s.o, s.w, wv); });
+    const size_t wsc = ws(LA_OP_FWD_CAUSAL, 1, 4, 1 << 20, 128);
+    check("fwd: valid B1 H4 N2^20 d128 (scan plan)", LA_OK, true,
+          [&] { return fwd(1, 4, 1 << 20, 128, s.q, s.o, s.w, wsc); });
     const int64_t nmax = ((int64_t)1 << 31) / (128 * 2) - 64 - 1;
     check("fwd: longest head d=128", LA_OK, true,
           [&] { return fwd(1, 1, nmax, 128, s.q, s.o, s.w, ws(LA_OP_FWD_CAUSAL, 1, 1, nmax, 128)); });

@@ -119,6 +119,28 @@ def test_backward_strict_inside_chunk(la, oracle, case, dtype):
         assert (~finite_rows(x)[bad]).all()
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_backward_from_saved_state_nonfinite(la, case, dtype):
+    """NaN keys and inf values from t0 on, the backward fed the forward's saved state (the
+    state each segment starts from, summed once by the forward): the same results as the
+    backward that forms the segment records itself, NaN for NaN, bit for bit elsewhere."""
+    B, H, N, d, t0 = case
+    skip_f32_128(dtype, d)
+    q, k, v, do = draw(B, H, N, d, dtype, seed=t0 + 5)
+    k[:, :, t0:] = float("nan")
+    v[:, :, t0:] = float("inf")
+    st = la.new_saved_state(q)
+    la.la_forward_causal(q, k, v, saved_state=st)
+    g1 = la.la_backward_causal(q, k, v, do, saved_state=st)
+    g2 = la.la_backward_causal(q, k, v, do)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        na, nb = torch.isnan(a), torch.isnan(b)
+        assert torch.equal(na, nb)
+        assert torch.equal(a[~na], b[~nb])
+
+
 @pytest.mark.parametrize("what", ["q", "dout"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("case", CASES, ids=IDS)

@@ -68,12 +68,13 @@ def test_noalloc_matches_workspace_call_twice(la, oracle):
 
 
 def test_noalloc_rejects_shapes_beyond_the_array(la):
-    """B1 H32 N131072 d128 needs about 272 MB of workspace: LA_ERR_WORKSPACE, nothing launched
-    (the small tensors' addresses are never read)."""
+    """B1 H4 N1048576 d128 needs about 130 MiB of workspace (a running-sum plan of 512
+    segments per head): LA_ERR_WORKSPACE, nothing launched (the small tensors' addresses
+    are never read)."""
     q = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16, device="cuda")
     o = torch.empty_like(q)
     lib = la.load_library()
-    st = lib.la_forward_causal_noalloc(_p(q), _p(q), _p(q), _p(o), None, None, None, None, None, 1, 32, 131072, 128, 0,
+    st = lib.la_forward_causal_noalloc(_p(q), _p(q), _p(q), _p(o), None, None, None, None, None, 1, 4, 1 << 20, 128, 0,
                                        la.LA_BF16, None)
     assert st == 3
     assert b"64 MiB" in lib.la_last_error_message()
