@@ -364,10 +364,12 @@ __device__ __forceinline__ void add_records(const float* rec, int64_t stride, in
 // threads of the workgroup at once, into out (kSize floats, record layout; LDS).
 // Every thread keeps a few 16-byte granules of every record of a batch in flight,
 // so a batch costs one round trip whatever the number of waves that will use it.
-// init (nullable): a record the sum starts from.
-template <int D, int kThreads, typename Src>
+// init (nullable): a record the sum starts from.  ready(j0, j1), called by every
+// thread before records j0 .. j1-1 are read (it may wait for them and hold a barrier),
+// lets the first batches be summed while later records are still being produced.
+template <int D, int kThreads, typename Src, typename Ready>
 __device__ __forceinline__ void sum_records_to(const Src& src, int64_t base, int64_t stride, int count,
-                                               const float* init, float* out, int tid) {
+                                               const float* init, float* out, int tid, Ready&& ready) {
     constexpr int G4 = Rec<D>::kSize / 4;  // 16-byte granules of a record
     static_assert(Rec<D>::kSize % 4 == 0, "records are whole granules");
     constexpr int PER = (G4 + kThreads - 1) / kThreads;
@@ -379,6 +381,7 @@ __device__ __forceinline__ void sum_records_to(const Src& src, int64_t base, int
         acc[p] = init != nullptr && g < G4 ? *reinterpret_cast<const f32x4*>(init + 4 * g) : zero4();
     }
     for (int j0 = 0; j0 < count; j0 += RB) {
+        ready(j0, j0 + RB < count ? j0 + RB : count);
         f32x4 x[RB][PER];
 #pragma unroll
         for (int b = 0; b < RB; ++b)
@@ -399,6 +402,12 @@ __device__ __forceinline__ void sum_records_to(const Src& src, int64_t base, int
         const int g = tid + p * kThreads;
         if (g < G4) *reinterpret_cast<f32x4*>(out + 4 * g) = acc[p];
     }
+}
+
+template <int D, int kThreads, typename Src>
+__device__ __forceinline__ void sum_records_to(const Src& src, int64_t base, int64_t stride, int count,
+                                               const float* init, float* out, int tid) {
+    sum_records_to<D, kThreads>(src, base, stride, count, init, out, tid, [](int, int) {});
 }
 
 // One record [X^T | a | b] written with agent-coherent stores through b at float

@@ -256,7 +256,12 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
         if (giveups != nullptr && threadIdx.x == 0) giveups[(int64_t)bh * nseg + seg] = 0u;
     } else {
         // ---- the segment's own record, as seg_state forms it ------------------------------
-        if (wv >= 4) {
+        // The state waves stage E(K) and form the record; the output waves, idle until the
+        // sweep, stage V.  Each role keeps the next two chunks of its tensor in flight (two
+        // register sets, chunk c in set c mod 2): the phase streams from HBM.  (At d = 128
+        // the registers are the sweep's: there the state waves stream both, one chunk ahead.)
+        auto next2 = [&](int c0) { return c0 + 2 * kC < tok_end ? c0 + 2 * kC : N; };  // past the segment: zeros
+        if (D > 64 && wv >= 4) {
             const GBuf bk(k + kvoff, hbytes), bv(v + voff, hbytes);
             ChunkRegs<T, D> ck, cv;
             ck.load(bk, tok_begin, rtid);
@@ -277,34 +282,82 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
             }
             store_record_coherent<D>(brec, (int64_t)seg * Rec<D>::kSize, st, vz, &vp, lane, w);
             wait_all_memory();
-        } else {
+        } else if (D > 64) {
             for (int c0 = tok_begin; c0 < tok_end; c0 += kC) __syncthreads();
+        } else if (wv >= 4) {
+            const GBuf bk(k + kvoff, hbytes);
+            ChunkRegs<T, D> ck0, ck1;
+            ck0.load(bk, tok_begin, rtid);
+            ck1.load(bk, tok_begin + kC < tok_end ? tok_begin + kC : N, rtid);
+            StateAcc<D> st;
+            VecAcc<D> vz, vp;
+            zero_state<D>(st);
+            zero_vec<D>(vz);
+            zero_vec<D>(vp);
+            auto chunk = [&](auto bsel, ChunkRegs<T, D>& ck, int c0) {
+                constexpr int B = decltype(bsel)::value;
+                stage_elu<T, D, FM>(ck, Tile<T, kC, D>{sm_e[B]}, rtid);
+                ck.load(bk, next2(c0), rtid);
+                __syncthreads();
+                state_update<T, D, true, true>(st, vz, vp, Tile<T, kC, D>{sm_e[B]}, Tile<T, kC, D>{sm_v[B]}, nullptr,
+                                               nullptr, lane, w);
+            };
+            for (int c0 = tok_begin; c0 < tok_end; c0 += 2 * kC) {
+                chunk(std::integral_constant<int, 0>{}, ck0, c0);
+                if (c0 + kC >= tok_end) break;
+                chunk(std::integral_constant<int, 1>{}, ck1, c0 + kC);
+            }
+            store_record_coherent<D>(brec, (int64_t)seg * Rec<D>::kSize, st, vz, &vp, lane, w);
+            wait_all_memory();
+        } else {
+            const GBuf bv(v + voff, hbytes);
+            ChunkRegs<T, D> cv0, cv1;
+            cv0.load(bv, tok_begin, rtid);
+            cv1.load(bv, tok_begin + kC < tok_end ? tok_begin + kC : N, rtid);
+            auto chunk = [&](auto bsel, ChunkRegs<T, D>& cv, int c0) {
+                constexpr int B = decltype(bsel)::value;
+                stage_raw<T, D>(cv, Tile<T, kC, D>{sm_v[B]}, rtid);
+                cv.load(bv, next2(c0), rtid);
+                __syncthreads();
+            };
+            for (int c0 = tok_begin; c0 < tok_end; c0 += 2 * kC) {
+                chunk(std::integral_constant<int, 0>{}, cv0, c0);
+                if (c0 + kC >= tok_end) break;
+                chunk(std::integral_constant<int, 1>{}, cv1, c0 + kC);
+            }
         }
         __syncthreads();  // every state wave's record stores are complete
     }
 
     // fused: post this segment's flag, wait for the earlier segments' (bounded), and
     // sum init + their records (every thread of the workgroup at once) into LDS over
-    // the idle tiles, bitwise what carried_state forms.  Called by both roles, so that
-    // each keeps its own first-chunk loads in flight meanwhile; true if every record
-    // arrived.
+    // the idle tiles, bitwise what carried_state forms.  The records are awaited batch
+    // by batch, so that the first batches are read and summed while the last segments'
+    // records (their producers finish last) are still on their way.  Called by both
+    // roles, so that each keeps its own first-chunk loads in flight meanwhile; true if
+    // every record arrived.
     __shared__ int s_ok;
     float* const xs = reinterpret_cast<float*>(&sm);
     auto fused_records = [&]() -> bool {
+        unsigned long long* hf = flags + (int64_t)bh * nseg;
         if (threadIdx.x == 0) {
-            unsigned long long* hf = flags + (int64_t)bh * nseg;
             post_flag(&hf[seg], epoch);
-            bool all = true;
-            for (int j = 0; j < seg; ++j) all = all && await_flag(&hf[j], epoch, wait_limit);
-            s_ok = all ? 1 : 0;
-            // The host reads these counts back (la_wait_failures): a give-up leaves NaN
-            // rows that must not pass for a result of the data.
-            giveups[(int64_t)bh * nseg + seg] = all ? 0u : 1u;
+            s_ok = 1;
         }
-        __syncthreads();
+        auto ready = [&](int j0, int j1) {
+            if (threadIdx.x == 0) {
+                bool all = s_ok != 0;
+                for (int j = j0; j < j1; ++j) all = all && await_flag(&hf[j], epoch, wait_limit);
+                s_ok = all ? 1 : 0;
+            }
+            __syncthreads();
+        };
         sum_records_to<D, 2 * kBlock>(RecCoherent{brec}, 0, Rec<D>::kSize, seg,
                                       init != nullptr ? init + (int64_t)kv * Rec<D>::kSize : nullptr, xs,
-                                      (int)threadIdx.x);
+                                      (int)threadIdx.x, ready);
+        // The host reads these counts back (la_wait_failures): a give-up leaves NaN rows
+        // that must not pass for a result of the data.
+        if (threadIdx.x == 0) giveups[(int64_t)bh * nseg + seg] = s_ok != 0 ? 0u : 1u;
         __syncthreads();
         return s_ok != 0;
     };
