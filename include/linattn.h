@@ -33,11 +33,14 @@
  *     result beyond rounding (the reassociation of "Intuition"): it is a tiling
  *     choice, and the kernels map a 64-token chunk onto four 16-row MFMA tiles,
  *     one per wavefront of a role.
- *   - LA_F32 at d = 128 is built for the non-causal forward and for decode only:
- *     the causal forward, the causal backward and the non-causal backward return
- *     LA_ERR_UNSUPPORTED there (their fp32 tiles and states at d = 128 need more
- *     LDS and registers per workgroup than a CU has).  bf16 covers d = 128 on
- *     every call.
+ *   - LA_F32 at d = 128 is built for the non-causal forward, decode and the causal
+ *     forward; the causal forward runs there on two blocks of 64 features of
+ *     phi(Q), phi(K) (formed in the workspace), one half of the value columns at a
+ *     time (its one-kernel fp32 tiles at d = 128 need more LDS than a CU has), with
+ *     no saved state and no grouped heads.  The causal backward and the non-causal
+ *     backward return LA_ERR_UNSUPPORTED for fp32 at d = 128 (their fp32 tiles and
+ *     states need more LDS and registers per workgroup than a CU has).  bf16 covers
+ *     d = 128 on every call.
  *   - The caller owns every buffer, including the workspace, whose size comes
  *     from la_workspace_size().  The library never allocates or frees device
  *     memory and keeps no device state between calls.
@@ -122,7 +125,9 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
  * state); saved_state (device, saved_state_bytes >= la_saved_state_size())
  * receives the per-segment carried state so that la_backward_causal on the same
  * q, k, v need not rebuild it.  The backward starts from a zero state, so a
- * saved_state together with S0 / z0 is LA_ERR_INVALID_ARGUMENT. */
+ * saved_state together with S0 / z0 is LA_ERR_INVALID_ARGUMENT; fp32 at d = 128
+ * (no causal backward there) takes no saved_state (LA_ERR_UNSUPPORTED) and a
+ * larger workspace (the feature blocks: la_workspace_size gives it). */
 la_status la_forward_causal(const void* q, const void* k, const void* v, void* o, const float* S0,
                             const float* z0, float* den_out, float* S_out, float* z_out,
                             void* saved_state, size_t saved_state_bytes, int64_t B, int64_t H,

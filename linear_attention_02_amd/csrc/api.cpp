@@ -246,6 +246,52 @@ size_t saved_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
     return saved_records_bytes(B, H, N, d) + (size_t)(B * H) * la::rec_floats(d) * sizeof(float);
 }
 
+struct BlockLayout {
+    size_t inner = 0, ob = 0, db = 0, bytes = 0;
+};
+BlockLayout block_layout(bool causal, int64_t B, int64_t H, int64_t N, int64_t d, int64_t KF, la_dtype dt) {
+    BlockLayout L;
+    if (B == 0 || H == 0 || N == 0) return L;
+    L.inner = layout(causal ? LA_OP_FWD_CAUSAL : LA_OP_FWD_NONCAUSAL, B, H * KF, N, d).bytes;
+    if (KF == 1) {
+        L.bytes = L.inner;
+        return L;
+    }
+    L.ob = align_up(L.inner);
+    L.db = L.ob + align_up((size_t)B * H * KF * N * d * elem_size(dt));
+    L.bytes = L.db + align_up((size_t)B * H * KF * N * sizeof(float));
+    return L;
+}
+
+
+// fp32 at d = 128, the causal forward: its fp32 tiles at d = 128 do not fit a CU's
+// LDS, so it runs on feature blocks.  phi(q), phi(k) go to two blocks of 64 features
+// each ([BH][2][N][64]), and each half of the value columns runs as the causal forward
+// on those blocks (la_forward_causal_features_blocks with m = 128, d = 64: the blocks
+// share one normalization); outputs and states are put back together.  Workspace:
+// the features, one value half and its output, the start and final state's halves,
+// and one block workspace per value half (so that the wait counts of both remain).
+struct F128Layout {
+    size_t fq = 0, fk = 0, vh = 0, oh = 0, s0h = 0, sh = 0, blk[2] = {0, 0}, blk_bytes = 0, bytes = 0;
+};
+F128Layout f128_layout(int64_t B, int64_t H, int64_t N) {
+    F128Layout L;
+    if (B == 0 || H == 0 || N == 0) return L;
+    const int64_t BH = B * H;
+    const size_t feat = align_up((size_t)BH * N * 128 * sizeof(float)), half = align_up((size_t)BH * N * 64 * sizeof(float));
+    const size_t st = align_up((size_t)BH * 128 * 64 * sizeof(float));
+    L.fk = feat;
+    L.vh = 2 * feat;
+    L.oh = L.vh + half;
+    L.s0h = L.oh + half;
+    L.sh = L.s0h + st;
+    L.blk_bytes = align_up(block_layout(true, B, H, N, 64, 2, LA_F32).bytes);
+    L.blk[0] = L.sh + st;
+    L.blk[1] = L.blk[0] + L.blk_bytes;
+    L.bytes = L.blk[1] + L.blk_bytes;
+    return L;
+}
+
 la_status check_workspace(const Layout& L, const void* ws, size_t ws_bytes) {
     if (L.bytes == 0) return LA_OK;
     if ((int64_t)L.plan.nseg * L.heads > ((int64_t)1 << 24))
@@ -328,7 +374,10 @@ la_status la_workspace_size(la_op op, int64_t B, int64_t H, int64_t N, int64_t d
     bool empty = false;
     la_status st = check_shape(B, H, N, d, chunk, dt, &empty);
     if (st != LA_OK) return st;
-    *bytes_out = empty ? 0 : layout(op, B, H, N, d).bytes;
+    if (op == LA_OP_FWD_CAUSAL && dt == LA_F32 && d == 128)
+        *bytes_out = empty ? 0 : f128_layout(B, H, N).bytes;
+    else
+        *bytes_out = empty ? 0 : layout(op, B, H, N, d).bytes;
     return LA_OK;
 }
 
@@ -399,6 +448,10 @@ la_status forward_noncausal(const void* q, const void* k, const void* v, void* o
 // Hkv: key/value heads (H a multiple of it); k, v, the start state and the final state
 // are per key/value head, q, o and den per query head.  Gv: key/value heads per value
 // head (v has B Hkv / Gv heads).
+la_status forward_causal_f128(const void* q, const void* k, const void* v, void* o, const float* S0, const float* z0,
+                              float* den_out, float* S_out, float* z_out, int64_t B, int64_t H, int64_t N,
+                              void* workspace, size_t workspace_bytes, hipStream_t s);
+
 la_status forward_causal(const void* q, const void* k, const void* v, void* o, const float* S0, const float* z0,
                          float* den_out, float* S_out, float* z_out, void* saved_state, size_t saved_state_bytes,
                          int64_t B, int64_t H, int64_t N, int64_t d, int chunk, la_dtype dt, void* workspace,
@@ -411,7 +464,12 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* o, c
                     (long long)Hkv);
     if (Hkv != H && saved_state)
         return fail(LA_ERR_INVALID_ARGUMENT, "saved_state is for la_backward_causal, which has no grouped heads");
-    if (dt == LA_F32 && d == 128) return fail(LA_ERR_UNSUPPORTED, "fp32 causal forward is built for d = 32 and 64");
+    // fp32 at d = 128 runs on feature blocks (forward_causal_f128): the default map on plain heads.
+    const bool f128 = dt == LA_F32 && d == 128;
+    if (f128 && (Hkv != H || Gv != 1 || feat != la::kFeatElu))
+        return fail(LA_ERR_UNSUPPORTED, "fp32 at d = 128: only the causal forward of phi = elu + 1 on plain heads is built");
+    if (f128 && saved_state)
+        return fail(LA_ERR_UNSUPPORTED, "fp32 at d = 128 has no causal backward, so no saved state");
     // Empty tensors (no tokens) may come as NULL pointers.
     if (N > 0 && (!q || !k || !v || !o)) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-NULL");
     const bool from_state = S0 != nullptr || z0 != nullptr;
@@ -455,6 +513,7 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* o, c
         }
         return LA_OK;
     }
+    if (f128) return forward_causal_f128(q, k, v, o, S0, z0, den_out, S_out, z_out, B, H, N, workspace, workspace_bytes, s);
     const Layout L = layout(LA_OP_FWD_CAUSAL, B, H, N, d);
     if ((st = check_workspace(L, workspace, workspace_bytes)) != LA_OK) return st;
     const Range wsr[] = {{"workspace", workspace, L.bytes}};
@@ -595,23 +654,6 @@ la_status check_blocks(int64_t d, int64_t m) {
 
 // Workspace of a call on KF feature blocks: the m = d call's workspace for B x (H KF)
 // heads, then every block's outputs o_j [B][H][KF][N][d] and den_j [B][H][KF][N].
-struct BlockLayout {
-    size_t inner = 0, ob = 0, db = 0, bytes = 0;
-};
-BlockLayout block_layout(bool causal, int64_t B, int64_t H, int64_t N, int64_t d, int64_t KF, la_dtype dt) {
-    BlockLayout L;
-    if (B == 0 || H == 0 || N == 0) return L;
-    L.inner = layout(causal ? LA_OP_FWD_CAUSAL : LA_OP_FWD_NONCAUSAL, B, H * KF, N, d).bytes;
-    if (KF == 1) {
-        L.bytes = L.inner;
-        return L;
-    }
-    L.ob = align_up(L.inner);
-    L.db = L.ob + align_up((size_t)B * H * KF * N * d * elem_size(dt));
-    L.bytes = L.db + align_up((size_t)B * H * KF * N * sizeof(float));
-    return L;
-}
-
 la_status forward_blocks(bool causal, const void* fq, const void* fk, const void* v, void* o, const float* S0,
                          const float* z0, float* den_out, float* S_out, float* z_out, int64_t B, int64_t H, int64_t N,
                          int64_t d, int64_t m, la_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
@@ -670,6 +712,66 @@ la_status forward_blocks(bool causal, const void* fq, const void* fk, const void
                                          N, (int)KF, s);
     });
     if (e != hipSuccess) return hip_fail(e, "combine_blocks launch");
+    return LA_OK;
+}
+
+la_status forward_causal_f128(const void* q, const void* k, const void* v, void* o, const float* S0, const float* z0,
+                              float* den_out, float* S_out, float* z_out, int64_t B, int64_t H, int64_t N,
+                              void* workspace, size_t workspace_bytes, hipStream_t s) {
+    const F128Layout L = f128_layout(B, H, N);
+    char* ws = static_cast<char*>(workspace);
+    if (ws == nullptr) return fail(LA_ERR_WORKSPACE, "workspace is NULL; %zu bytes are needed", L.bytes);
+    if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+        return fail(LA_ERR_INVALID_ARGUMENT, "workspace must be %zu-byte aligned", kAlign);
+    if (workspace_bytes < L.bytes)
+        return fail(LA_ERR_WORKSPACE, "workspace has %zu bytes; %zu are needed", workspace_bytes, L.bytes);
+    const int64_t BH = B * H;
+    const size_t tb = (size_t)BH * N * 128 * sizeof(float), Sb = (size_t)BH * 128 * 128 * sizeof(float);
+    const size_t zb = (size_t)BH * 128 * sizeof(float);
+    const Range wsr = {"workspace", ws, L.bytes};
+    const Range others[] = {{"q", q, tb},          {"k", k, tb},   {"v", v, tb},   {"o", o, tb},
+                            {"den_out", den_out, (size_t)BH * N * sizeof(float)}, {"S0", S0, Sb}, {"z0", z0, zb},
+                            {"S_out", S_out, Sb}, {"z_out", z_out, zb}};
+    for (const Range& r : others)
+        if (overlap(wsr, r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+    float* fq = reinterpret_cast<float*>(ws + L.fq);
+    float* fk = reinterpret_cast<float*>(ws + L.fk);
+    float* vh = reinterpret_cast<float*>(ws + L.vh);
+    float* oh = reinterpret_cast<float*>(ws + L.oh);
+    float* s0h = reinterpret_cast<float*>(ws + L.s0h);
+    float* sh = reinterpret_cast<float*>(ws + L.sh);
+    hipError_t e;
+    if ((e = timed("phi_blocks", s, [&] { return la::launch_phi_blocks(static_cast<const float*>(q), fq, BH, N, 2, 64, s); })) !=
+            hipSuccess ||
+        (e = timed("phi_blocks", s, [&] { return la::launch_phi_blocks(static_cast<const float*>(k), fk, BH, N, 2, 64, s); })) !=
+            hipSuccess)
+        return hip_fail(e, "phi_blocks launch");
+    for (int h = 0; h < 2; ++h) {
+        // The start state is read and the final state written half by half: in place (S_out = S0,
+        // z_out = z0) each half is copied out before its columns are overwritten, and z is written last.
+        const float* vsrc = static_cast<const float*>(v) + 64 * h;
+        if ((e = timed("copy_cols", s, [&] { return la::launch_copy_cols(vh, 64, vsrc, 128, BH * N, 64, s); })) !=
+            hipSuccess)
+            return hip_fail(e, "copy_cols launch");
+        if (S0 != nullptr &&
+            (e = timed("copy_cols", s, [&] { return la::launch_copy_cols(s0h, 64, S0 + 64 * h, 128, BH * 128, 64, s); })) !=
+                hipSuccess)
+            return hip_fail(e, "copy_cols launch");
+        const bool last = h == 1;
+        const la_status st = forward_blocks(true, fq, fk, vh, oh, S0 != nullptr ? s0h : nullptr, z0,
+                                            last ? den_out : nullptr, S_out != nullptr ? sh : nullptr,
+                                            last ? z_out : nullptr, B, H, N, 64, 128, LA_F32, ws + L.blk[h],
+                                            L.blk_bytes, s);
+        if (st != LA_OK) return st;
+        float* odst = static_cast<float*>(o) + 64 * h;
+        if ((e = timed("copy_cols", s, [&] { return la::launch_copy_cols(odst, 128, oh, 64, BH * N, 64, s); })) !=
+            hipSuccess)
+            return hip_fail(e, "copy_cols launch");
+        if (S_out != nullptr &&
+            (e = timed("copy_cols", s, [&] { return la::launch_copy_cols(S_out + 64 * h, 128, sh, 64, BH * 128, 64, s); })) !=
+                hipSuccess)
+            return hip_fail(e, "copy_cols launch");
+    }
     return LA_OK;
 }
 
@@ -923,6 +1025,25 @@ la_status la_wait_failures(la_op op, const void* workspace, size_t workspace_byt
     if (st != LA_OK) return st;
     *failures_out = 0;
     if (empty) return LA_OK;
+    if (op == LA_OP_FWD_CAUSAL && dt == LA_F32 && d == 128) {  // the two value halves' launches on feature blocks
+        const F128Layout F = f128_layout(B, H, N);
+        const Layout Li = layout(LA_OP_FWD_CAUSAL, B, 2 * H, N, 64);
+        if (Li.plan.scan) return LA_OK;
+        if (workspace == nullptr || workspace_bytes < F.bytes)
+            return fail(LA_ERR_WORKSPACE, "workspace has %zu bytes; %zu are needed", workspace_bytes, F.bytes);
+        hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+        std::vector<unsigned> slots((size_t)Li.heads * Li.plan.nseg);
+        int64_t n = 0;
+        for (int h = 0; h < 2; ++h) {
+            e = hipMemcpy(slots.data(), static_cast<const char*>(workspace) + F.blk[h] + Li.giveups,
+                          slots.size() * sizeof(unsigned), hipMemcpyDeviceToHost);
+            if (e != hipSuccess) return hip_fail(e, "copy of the wait counts");
+            for (unsigned c : slots) n += c;
+        }
+        *failures_out = n;
+        return LA_OK;
+    }
     const Layout L = layout(op, B, H, N, d);
     if (op == LA_OP_BWD_CAUSAL ? !L.fused : L.plan.scan) return LA_OK;  // launches that wait for nothing
     if ((st = check_workspace(L, workspace, workspace_bytes)) != LA_OK) return st;

@@ -786,6 +786,56 @@ hipError_t launch_copy_or_zero(float* p, const float* src, size_t n, hipStream_t
 
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s) { return launch_copy_or_zero(p, nullptr, n, s); }
 
+// ---------------------------------------------------------------------------------------
+// Pieces of the fp32 causal forward at d = 128, which runs on feature blocks (its fp32
+// tiles at d = 128 do not fit a CU's LDS): phi_blocks writes phi(x) = elu(x) + 1 of
+// x [heads][N][KF db] in block layout [heads][KF][N][db]; copy_cols moves a block of
+// `cols` columns between row-major fp32 matrices of different widths.
+__global__ __launch_bounds__(kBlock) void phi_blocks_kernel(const float* __restrict__ x, float* __restrict__ out,
+                                                            int64_t heads, int64_t N, int KF, int db) {
+    const int64_t q4 = db / 4;                          // 16-byte groups per block row
+    const int64_t total = heads * N * KF * q4;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < total; i += (int64_t)gridDim.x * kBlock) {
+        const int64_t c4 = i % q4, r = i / q4;           // r = (head, row, block): input order
+        const int64_t j = r % KF, hn = r / KF, n = hn % N, h = hn / N;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(x + (hn * KF + j) * db + 4 * c4);
+        f32x4 b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[e] = phi_f(a[e]);
+        *reinterpret_cast<f32x4*>(out + ((h * KF + j) * N + n) * db + 4 * c4) = b;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void copy_cols_kernel(float* __restrict__ dst, int64_t dst_ld,
+                                                           const float* __restrict__ src, int64_t src_ld,
+                                                           int64_t rows, int cols) {
+    const int64_t q4 = cols / 4, total = rows * q4;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < total; i += (int64_t)gridDim.x * kBlock) {
+        const int64_t r = i / q4, c4 = i % q4;
+        *reinterpret_cast<f32x4*>(dst + r * dst_ld + 4 * c4) = *reinterpret_cast<const f32x4*>(src + r * src_ld + 4 * c4);
+    }
+}
+
+hipError_t launch_phi_blocks(const float* x, float* out, int64_t heads, int64_t N, int KF, int db, hipStream_t s) {
+    if (db % 4 != 0) return hipErrorInvalidValue;
+    const int64_t total = heads * N * KF * (db / 4);
+    if (total == 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((total + kBlock - 1) / kBlock, 8192);
+    hipLaunchKernelGGL(phi_blocks_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, s, x, out, heads, N, KF, db);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_cols(float* dst, int64_t dst_ld, const float* src, int64_t src_ld, int64_t rows, int cols,
+                            hipStream_t s) {
+    if (cols % 4 != 0) return hipErrorInvalidValue;
+    const int64_t total = rows * (cols / 4);
+    if (total == 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((total + kBlock - 1) / kBlock, 8192);
+    hipLaunchKernelGGL(copy_cols_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, s, dst, dst_ld, src, src_ld, rows,
+                       cols);
+    return hipGetLastError();
+}
+
 template <class FM>
 static hipError_t launch_seg_state_fm(int dt, int d, const void* k, const void* v, float* rec, int64_t BH, int64_t N,
                                       SegPlan p, hipStream_t s, int Gv) {

@@ -143,6 +143,14 @@ hipError_t launch_ncbwd_kv(int dt, int d, const void* k, const void* v, void* dk
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t s);
 // Copy n floats from src (zero-fill when src is null) with the same kernel.
 hipError_t launch_copy_or_zero(float* p, const float* src, size_t n, hipStream_t s);
+// fp32 pieces of the causal forward at d = 128 on feature blocks: phi(x) = elu(x) + 1 of
+// x [heads][N][KF db] into block layout [heads][KF][N][db] (db a multiple of 4); and a
+// block of `cols` columns (a multiple of 4; 16-byte aligned rows) copied between
+// row-major matrices: dst[r][c] = src[r][c], r < rows, c < cols, rows dst_ld and src_ld
+// floats apart.
+hipError_t launch_phi_blocks(const float* x, float* out, int64_t heads, int64_t N, int KF, int db, hipStream_t s);
+hipError_t launch_copy_cols(float* dst, int64_t dst_ld, const float* src, int64_t src_ld, int64_t rows, int cols,
+                            hipStream_t s);
 
 // Decode.
 hipError_t launch_decode(int dt, int d, float* S, float* z, const void* q, const void* k,

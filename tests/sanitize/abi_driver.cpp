@@ -101,7 +101,9 @@ int main() {
     check("fwd: workspace overlaps v", LA_ERR_INVALID_ARGUMENT, false,
           [&] { return fwd(4, 16, 4096, 64, s.q, s.o, s.v + 256, wf); });
     check("fwd: no tokens", LA_OK, false, [&] { return fwd(4, 16, 0, 64, 0, 0, 0, 0); });
-    check("fwd: fp32 d=128", LA_ERR_UNSUPPORTED, false, [&] { return fwd(1, 1, 64, 128, s.q, s.o, s.w, GB, LA_F32); });
+    check("fwd: fp32 d=128 (feature blocks)", LA_OK, true, [&] { return fwd(1, 1, 64, 128, s.q, s.o, s.w, GB, LA_F32); });
+    check("fwd: fp32 d=128 workspace short", LA_ERR_WORKSPACE, false,
+          [&] { return fwd(1, 1, 64, 128, s.q, s.o, s.w, ws(LA_OP_FWD_CAUSAL, 1, 1, 64, 128, LA_F32) - 256, LA_F32); });
     const size_t wv = ws(LA_OP_FWD_CAUSAL, 1, 32, 131072, 128);
     check("fwd: valid Very long (one round of 8 segments per head)", LA_OK, true,
           [&] { return fwd(1, 32, 131072, 128, s.q, s.o, s.w, wv); });

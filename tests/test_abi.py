@@ -101,7 +101,8 @@ def test_forward_causal_validation(lib):
     assert fwd_causal(lib, o=A) == 1                         # o overlaps q
     assert fwd_causal(lib, d=96) == 2
     assert fwd_causal(lib, chunk=16) == 2
-    assert fwd_causal(lib, dt=la.LA_F32, d=128) == 2         # fp32 d=128 not built
+    assert fwd_causal(lib, dt=la.LA_F32, d=128) == 3         # fp32 d=128 (on feature blocks): workspace too small
+    assert fwd_causal(lib, dt=la.LA_F32, d=128, saved=A + 0x5000000, saved_bytes=1 << 30) == 2  # no fp32 d=128 backward
     assert fwd_causal(lib, wsb=16) == 3                      # workspace too small
     assert fwd_causal(lib, wsp=None, wsb=1 << 30) == 3       # NULL workspace
     assert fwd_causal(lib, wsp=A + 0x4000010, wsb=1 << 30) == 1   # workspace misaligned
