@@ -33,12 +33,14 @@
  *     result beyond rounding (the reassociation of "Intuition"): it is a tiling
  *     choice, and the kernels map a 64-token chunk onto four 16-row MFMA tiles,
  *     one per wavefront of a role.
- *   - LA_F32 at d = 128 is built for the non-causal forward, decode and the causal
- *     forward; the causal forward runs there on two blocks of 64 features of
- *     phi(Q), phi(K) (formed in the workspace), one half of the value columns at a
- *     time (its one-kernel fp32 tiles at d = 128 need more LDS than a CU has), with
- *     no saved state and no grouped heads.  The causal backward and the non-causal
- *     backward return LA_ERR_UNSUPPORTED for fp32 at d = 128 (their fp32 tiles and
+ *   - LA_F32 at d = 128 is built for the non-causal forward, decode, the causal
+ *     forward and the causal backward; the causal pair runs there on two blocks of
+ *     64 features of phi(Q), phi(K) (formed in the workspace), one half of the
+ *     value columns at a time (the one-kernel fp32 tiles at d = 128 need more LDS
+ *     than a CU has): phi = elu + 1 from a zero state (no S0 / z0 in the backward,
+ *     no state gradients), no grouped heads, and a saved state is taken but left
+ *     unused (the backward recomputes the forward on the blocks).  The non-causal
+ *     backward returns LA_ERR_UNSUPPORTED for fp32 at d = 128 (its fp32 tiles and
  *     states need more LDS and registers per workgroup than a CU has).  bf16 covers
  *     d = 128 on every call.
  *   - The caller owns every buffer, including the workspace, whose size comes
@@ -126,8 +128,8 @@ la_status la_forward_noncausal(const void* q, const void* k, const void* v, void
  * receives the per-segment carried state so that la_backward_causal on the same
  * q, k, v need not rebuild it.  The backward starts from a zero state, so a
  * saved_state together with S0 / z0 is LA_ERR_INVALID_ARGUMENT; fp32 at d = 128
- * (no causal backward there) takes no saved_state (LA_ERR_UNSUPPORTED) and a
- * larger workspace (the feature blocks: la_workspace_size gives it). */
+ * leaves saved_state unwritten (its backward recomputes) and needs a larger
+ * workspace (the feature blocks: la_workspace_size gives it). */
 la_status la_forward_causal(const void* q, const void* k, const void* v, void* o, const float* S0,
                             const float* z0, float* den_out, float* S_out, float* z_out,
                             void* saved_state, size_t saved_state_bytes, int64_t B, int64_t H,
@@ -159,7 +161,13 @@ la_status la_forward_causal_grouped(const void* q, const void* k, const void* v,
  * recomputed in fp32 from q, k, v; the forward's outputs are not inputs here.
  * saved_state (nullable) is the buffer a la_forward_causal call on the same
  * q, k, v and shape filled; when NULL the carried state is rebuilt from k, v.
- * Either way the results are bitwise the same.
+ * Either way the results are bitwise the same.  fp32 at d = 128 runs per half of
+ * the value columns on two 64-feature blocks: the forward on the blocks gives that
+ * half's O and den, the blocks' backward takes g_i from that half alone (the
+ * halves' g_i add up to the row's, and dphi(Q), dphi(K) are linear in G and g,
+ * so the halves' feature gradients add up), and dQ, dK = their sum * phi'; the
+ * saved state is not read there.  la_backward_causal_state at fp32 d = 128 with
+ * any state pointer set returns LA_ERR_UNSUPPORTED.
  * In: q, k, v, dout [B][H][N][d].  Out: dq, dk, dv [B][H][N][d]. */
 la_status la_backward_causal(const void* q, const void* k, const void* v, const void* dout,
                              void* dq, void* dk, void* dv, const void* saved_state,

@@ -292,6 +292,40 @@ F128Layout f128_layout(int64_t B, int64_t H, int64_t N) {
     return L;
 }
 
+// fp32 at d = 128, the causal backward, on the same feature blocks: per value half, the
+// forward on the blocks (its output half and the head's den) and the blocks' backward
+// with g from that output half (the halves' g add up to the row's g, and dphi(Q),
+// dphi(K) are linear in dA, so the halves' feature gradients add up); dq, dk = the
+// sum over the halves times phi'.  Workspace: features and their two gradients each,
+// one value half with its output, upstream gradient and dv, den, and the blocks'
+// forward and backward workspaces.
+struct B128Layout {
+    size_t fq = 0, fk = 0, dfq[2] = {0, 0}, dfk[2] = {0, 0}, vh = 0, oh = 0, doh = 0, dvh = 0, den = 0;
+    size_t fwd = 0, fwd_bytes = 0, bwd = 0, bwd_bytes = 0, bytes = 0;
+};
+B128Layout b128_layout(int64_t B, int64_t H, int64_t N) {
+    B128Layout L;
+    if (B == 0 || H == 0 || N == 0) return L;
+    const int64_t BH = B * H;
+    const size_t feat = align_up((size_t)BH * N * 128 * sizeof(float)), half = align_up((size_t)BH * N * 64 * sizeof(float));
+    L.fk = feat;
+    L.dfq[0] = 2 * feat;
+    L.dfq[1] = 3 * feat;
+    L.dfk[0] = 4 * feat;
+    L.dfk[1] = 5 * feat;
+    L.vh = 6 * feat;
+    L.oh = L.vh + half;
+    L.doh = L.oh + half;
+    L.dvh = L.doh + half;
+    L.den = L.dvh + half;
+    L.fwd = L.den + align_up((size_t)BH * N * sizeof(float));
+    L.fwd_bytes = align_up(block_layout(true, B, H, N, 64, 2, LA_F32).bytes);
+    L.bwd = L.fwd + L.fwd_bytes;
+    L.bwd_bytes = align_up(layout(LA_OP_BWD_CAUSAL, B, 2 * H, N, 64).bytes) + align_up((size_t)BH * N * 128 * sizeof(float));
+    L.bytes = L.bwd + L.bwd_bytes;
+    return L;
+}
+
 la_status check_workspace(const Layout& L, const void* ws, size_t ws_bytes) {
     if (L.bytes == 0) return LA_OK;
     if ((int64_t)L.plan.nseg * L.heads > ((int64_t)1 << 24))
@@ -376,6 +410,8 @@ la_status la_workspace_size(la_op op, int64_t B, int64_t H, int64_t N, int64_t d
     if (st != LA_OK) return st;
     if (op == LA_OP_FWD_CAUSAL && dt == LA_F32 && d == 128)
         *bytes_out = empty ? 0 : f128_layout(B, H, N).bytes;
+    else if (op == LA_OP_BWD_CAUSAL && dt == LA_F32 && d == 128)
+        *bytes_out = empty ? 0 : b128_layout(B, H, N).bytes;
     else
         *bytes_out = empty ? 0 : layout(op, B, H, N, d).bytes;
     return LA_OK;
@@ -468,8 +504,6 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* o, c
     const bool f128 = dt == LA_F32 && d == 128;
     if (f128 && (Hkv != H || Gv != 1 || feat != la::kFeatElu))
         return fail(LA_ERR_UNSUPPORTED, "fp32 at d = 128: only the causal forward of phi = elu + 1 on plain heads is built");
-    if (f128 && saved_state)
-        return fail(LA_ERR_UNSUPPORTED, "fp32 at d = 128 has no causal backward, so no saved state");
     // Empty tensors (no tokens) may come as NULL pointers.
     if (N > 0 && (!q || !k || !v || !o)) return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-NULL");
     const bool from_state = S0 != nullptr || z0 != nullptr;
@@ -513,6 +547,7 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* o, c
         }
         return LA_OK;
     }
+    // (fp32 at d = 128 leaves a saved state unused: its backward recomputes the forward on the feature blocks.)
     if (f128) return forward_causal_f128(q, k, v, o, S0, z0, den_out, S_out, z_out, B, H, N, workspace, workspace_bytes, s);
     const Layout L = layout(LA_OP_FWD_CAUSAL, B, H, N, d);
     if ((st = check_workspace(L, workspace, workspace_bytes)) != LA_OK) return st;
@@ -905,6 +940,10 @@ la_status la_forward_noncausal_features_blocks(const void* fq, const void* fk, c
 
 
 
+static la_status backward_causal_f128(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                                      void* dk, void* dv, int64_t B, int64_t H, int64_t N, void* workspace,
+                                      size_t workspace_bytes, hipStream_t s);
+
 static la_status backward_causal(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
                                  void* dv, const void* saved_state, size_t saved_state_bytes, const float* S0,
                                  const float* z0, const float* dSN, const float* dzN, float* dS0, float* dz0,
@@ -913,7 +952,10 @@ static la_status backward_causal(const void* q, const void* k, const void* v, co
     bool empty = false;
     la_status st = check_shape(B, H, N, d, chunk, dt, &empty);
     if (st != LA_OK) return st;
-    if (dt == LA_F32 && d == 128) return fail(LA_ERR_UNSUPPORTED, "fp32 causal backward is built for d = 32 and 64");
+    // fp32 at d = 128 runs on feature blocks (backward_causal_f128): the default map from a zero state.
+    const bool f128 = dt == LA_F32 && d == 128;
+    if (f128 && (feat != la::kFeatElu || S0 || z0 || dSN || dzN || dS0 || dz0))
+        return fail(LA_ERR_UNSUPPORTED, "fp32 at d = 128: only the causal backward of phi = elu + 1 from a zero state is built");
     if (N > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv))
         return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v, dout, dq, dk and dv must be non-NULL");
     const size_t tb = (size_t)B * H * N * d * elem_size(dt);
@@ -937,6 +979,8 @@ static la_status backward_causal(const void* q, const void* k, const void* v, co
             return hip_fail(e, "dz0");
         return LA_OK;
     }
+    // (fp32 at d = 128 does not read a saved state: it recomputes the forward on the feature blocks.)
+    if (f128) return backward_causal_f128(q, k, v, dout, dq, dk, dv, B, H, N, workspace, workspace_bytes, s);
     const Layout L = layout(LA_OP_BWD_CAUSAL, B, H, N, d);
     if ((st = check_workspace(L, workspace, workspace_bytes)) != LA_OK) return st;
     const Range wsr[] = {{"workspace", workspace, L.bytes}};
@@ -1025,6 +1069,7 @@ la_status la_wait_failures(la_op op, const void* workspace, size_t workspace_byt
     if (st != LA_OK) return st;
     *failures_out = 0;
     if (empty) return LA_OK;
+    if (op == LA_OP_BWD_CAUSAL && dt == LA_F32 && d == 128) return LA_OK;  // feature-block passes: no waits
     if (op == LA_OP_FWD_CAUSAL && dt == LA_F32 && d == 128) {  // the two value halves' launches on feature blocks
         const F128Layout F = f128_layout(B, H, N);
         const Layout Li = layout(LA_OP_FWD_CAUSAL, B, 2 * H, N, 64);
@@ -1432,3 +1477,66 @@ la_status la_decode_steps_features_blocks(float* S, float* z, const void* fq, co
 }
 
 }  // extern "C"
+
+static la_status backward_causal_f128(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                                      void* dk, void* dv, int64_t B, int64_t H, int64_t N, void* workspace,
+                                      size_t workspace_bytes, hipStream_t s) {
+    const B128Layout L = b128_layout(B, H, N);
+    char* ws = static_cast<char*>(workspace);
+    if (ws == nullptr) return fail(LA_ERR_WORKSPACE, "workspace is NULL; %zu bytes are needed", L.bytes);
+    if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+        return fail(LA_ERR_INVALID_ARGUMENT, "workspace must be %zu-byte aligned", kAlign);
+    if (workspace_bytes < L.bytes)
+        return fail(LA_ERR_WORKSPACE, "workspace has %zu bytes; %zu are needed", workspace_bytes, L.bytes);
+    const int64_t BH = B * H;
+    const size_t tb = (size_t)BH * N * 128 * sizeof(float);
+    const Range wsr = {"workspace", ws, L.bytes};
+    const Range others[] = {{"q", q, tb},   {"k", k, tb},   {"v", v, tb},  {"dout", dout, tb},
+                            {"dq", dq, tb}, {"dk", dk, tb}, {"dv", dv, tb}};
+    for (const Range& r : others)
+        if (overlap(wsr, r)) return fail(LA_ERR_INVALID_ARGUMENT, "workspace overlaps %s", r.name);
+    float* fq = reinterpret_cast<float*>(ws + L.fq);
+    float* fk = reinterpret_cast<float*>(ws + L.fk);
+    float* vh = reinterpret_cast<float*>(ws + L.vh);
+    float* oh = reinterpret_cast<float*>(ws + L.oh);
+    float* doh = reinterpret_cast<float*>(ws + L.doh);
+    float* dvh = reinterpret_cast<float*>(ws + L.dvh);
+    float* den = reinterpret_cast<float*>(ws + L.den);
+    const float* fq_in = static_cast<const float*>(q);
+    const float* fk_in = static_cast<const float*>(k);
+    hipError_t e;
+    if ((e = timed("phi_blocks", s, [&] { return la::launch_phi_blocks(fq_in, fq, BH, N, 2, 64, s); })) != hipSuccess ||
+        (e = timed("phi_blocks", s, [&] { return la::launch_phi_blocks(fk_in, fk, BH, N, 2, 64, s); })) != hipSuccess)
+        return hip_fail(e, "phi_blocks launch");
+    for (int h = 0; h < 2; ++h) {
+        const float* vsrc = static_cast<const float*>(v) + 64 * h;
+        const float* dosrc = static_cast<const float*>(dout) + 64 * h;
+        if ((e = timed("copy_cols", s, [&] { return la::launch_copy_cols(vh, 64, vsrc, 128, BH * N, 64, s); })) !=
+                hipSuccess ||
+            (e = timed("copy_cols", s, [&] { return la::launch_copy_cols(doh, 64, dosrc, 128, BH * N, 64, s); })) !=
+                hipSuccess)
+            return hip_fail(e, "copy_cols launch");
+        la_status st = forward_blocks(true, fq, fk, vh, oh, nullptr, nullptr, den, nullptr, nullptr, B, H, N, 64, 128,
+                                      LA_F32, ws + L.fwd, L.fwd_bytes, s);
+        if (st != LA_OK) return st;
+        st = la_backward_causal_features_blocks(fq, fk, vh, doh, den, oh, ws + L.dfq[h], ws + L.dfk[h], dvh, B, H, N,
+                                                64, 128, LA_F32, ws + L.bwd, L.bwd_bytes, s);
+        if (st != LA_OK) return st;
+        float* dvdst = static_cast<float*>(dv) + 64 * h;
+        if ((e = timed("copy_cols", s, [&] { return la::launch_copy_cols(dvdst, 128, dvh, 64, BH * N, 64, s); })) !=
+            hipSuccess)
+            return hip_fail(e, "copy_cols launch");
+    }
+    const float* dfq0 = reinterpret_cast<const float*>(ws + L.dfq[0]);
+    const float* dfq1 = reinterpret_cast<const float*>(ws + L.dfq[1]);
+    const float* dfk0 = reinterpret_cast<const float*>(ws + L.dfk[0]);
+    const float* dfk1 = reinterpret_cast<const float*>(ws + L.dfk[1]);
+    if ((e = timed("phi_blocks_grad", s, [&] {
+             return la::launch_phi_blocks_grad(fq_in, dfq0, dfq1, static_cast<float*>(dq), BH, N, 2, 64, s);
+         })) != hipSuccess ||
+        (e = timed("phi_blocks_grad", s, [&] {
+             return la::launch_phi_blocks_grad(fk_in, dfk0, dfk1, static_cast<float*>(dk), BH, N, 2, 64, s);
+         })) != hipSuccess)
+        return hip_fail(e, "phi_blocks_grad launch");
+    return LA_OK;
+}

@@ -816,6 +816,38 @@ __global__ __launch_bounds__(kBlock) void copy_cols_kernel(float* __restrict__ d
     }
 }
 
+// The gradient back through phi_blocks for two sets of feature gradients (the value halves'):
+// dx [heads][N][KF db] = (dF0 + dF1 in block layout) * phi'(x), phi'(x) = exp(min(x, 0)).
+__global__ __launch_bounds__(kBlock) void phi_blocks_grad_kernel(const float* __restrict__ x,
+                                                                 const float* __restrict__ dF0,
+                                                                 const float* __restrict__ dF1, float* __restrict__ dx,
+                                                                 int64_t heads, int64_t N, int KF, int db) {
+    const int64_t q4 = db / 4;
+    const int64_t total = heads * N * KF * q4;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < total; i += (int64_t)gridDim.x * kBlock) {
+        const int64_t c4 = i % q4, r = i / q4;
+        const int64_t j = r % KF, hn = r / KF, n = hn % N, h = hn / N;
+        const int64_t bo = ((h * KF + j) * N + n) * db + 4 * c4, xo = (hn * KF + j) * db + 4 * c4;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(x + xo);
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(dF0 + bo), g1 = *reinterpret_cast<const f32x4*>(dF1 + bo);
+        f32x4 r4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r4[e] = (g0[e] + g1[e]) * dphi_f(a[e]);
+        *reinterpret_cast<f32x4*>(dx + xo) = r4;
+    }
+}
+
+hipError_t launch_phi_blocks_grad(const float* x, const float* dF0, const float* dF1, float* dx, int64_t heads,
+                                  int64_t N, int KF, int db, hipStream_t s) {
+    if (db % 4 != 0) return hipErrorInvalidValue;
+    const int64_t total = heads * N * KF * (db / 4);
+    if (total == 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((total + kBlock - 1) / kBlock, 8192);
+    hipLaunchKernelGGL(phi_blocks_grad_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, s, x, dF0, dF1, dx, heads, N,
+                       KF, db);
+    return hipGetLastError();
+}
+
 hipError_t launch_phi_blocks(const float* x, float* out, int64_t heads, int64_t N, int KF, int db, hipStream_t s) {
     if (db % 4 != 0) return hipErrorInvalidValue;
     const int64_t total = heads * N * KF * (db / 4);

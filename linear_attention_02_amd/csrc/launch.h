@@ -151,6 +151,9 @@ hipError_t launch_copy_or_zero(float* p, const float* src, size_t n, hipStream_t
 hipError_t launch_phi_blocks(const float* x, float* out, int64_t heads, int64_t N, int KF, int db, hipStream_t s);
 hipError_t launch_copy_cols(float* dst, int64_t dst_ld, const float* src, int64_t src_ld, int64_t rows, int cols,
                             hipStream_t s);
+// And back: dx [heads][N][KF db] = (dF0 + dF1) * phi'(x) with dF0, dF1 in block layout.
+hipError_t launch_phi_blocks_grad(const float* x, const float* dF0, const float* dF1, float* dx, int64_t heads,
+                                  int64_t N, int KF, int db, hipStream_t s);
 
 // Decode.
 hipError_t launch_decode(int dt, int d, float* S, float* z, const void* q, const void* k,

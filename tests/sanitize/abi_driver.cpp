@@ -130,6 +130,14 @@ int main() {
     check("bwd: dq overlaps dk", LA_ERR_INVALID_ARGUMENT, false,
           [&] { return bwd(4, 16, 4096, 64, s.dk, ws(LA_OP_BWD_CAUSAL, 4, 16, 4096, 64)); });
     check("bwd: workspace short", LA_ERR_WORKSPACE, false, [&] { return bwd(4, 16, 4096, 64, s.dq, 1024); });
+    auto bwd32 = [&](int64_t N, size_t wb) {
+        return la_backward_causal(P(s.q), P(s.k), P(s.v), P(s.dout), P(s.dq), P(s.dk), P(s.dv), nullptr, 0, 2, 3, N,
+                                  128, 0, LA_F32, P(s.w), wb, nullptr);
+    };
+    check("bwd: fp32 d=128 (feature blocks)", LA_OK, true,
+          [&] { return bwd32(1000, ws(LA_OP_BWD_CAUSAL, 2, 3, 1000, 128, LA_F32)); });
+    check("bwd: fp32 d=128 workspace short", LA_ERR_WORKSPACE, false,
+          [&] { return bwd32(1000, ws(LA_OP_BWD_CAUSAL, 2, 3, 1000, 128, LA_F32) - 256); });
     check("bwd state: valid", LA_OK, true, [&] {
         return la_backward_causal_state(P(s.q), P(s.k), P(s.v), P(s.dout), F(s.st), F(s.st + GB / 4),
                                         F(s.st + GB / 2), F(s.st + 3 * GB / 4), P(s.dq), P(s.dk), P(s.dv), F(s.aux),

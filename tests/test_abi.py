@@ -102,7 +102,9 @@ def test_forward_causal_validation(lib):
     assert fwd_causal(lib, d=96) == 2
     assert fwd_causal(lib, chunk=16) == 2
     assert fwd_causal(lib, dt=la.LA_F32, d=128) == 3         # fp32 d=128 (on feature blocks): workspace too small
-    assert fwd_causal(lib, dt=la.LA_F32, d=128, saved=A + 0x5000000, saved_bytes=1 << 30) == 2  # no fp32 d=128 backward
+    # fp32 d=128 takes a saved state (and leaves it unused: its backward recomputes), checked for size like any other
+    assert fwd_causal(lib, dt=la.LA_F32, d=128, saved=A + 0x5000000, saved_bytes=1 << 30) == 3
+    assert fwd_causal(lib, dt=la.LA_F32, d=128, saved=A + 0x5000000, saved_bytes=4, wsb=1 << 30) == 1
     assert fwd_causal(lib, wsb=16) == 3                      # workspace too small
     assert fwd_causal(lib, wsp=None, wsb=1 << 30) == 3       # NULL workspace
     assert fwd_causal(lib, wsp=A + 0x4000010, wsb=1 << 30) == 1   # workspace misaligned
@@ -143,6 +145,11 @@ def test_forward_noncausal_and_backward_validation(lib):
     assert b(*bad, None, 0, 1, 1, 64, 64, 0, 1, A + 0x7000000, 1 << 30, None) == 1
     assert b(*args, A + 0x8000000, 4, 1, 1, 64, 64, 0, 1, A + 0x7000000, 1 << 30, None) == 1  # saved state short
     assert b(*args, A + 0x4000000, 1 << 20, 1, 1, 64, 64, 0, 1, A + 0x7000000, 1 << 30, None) == 1  # overlaps dq
+    assert b(*args, None, 0, 1, 1, 64, 128, 0, 0, A + 0x7000000, 8, None) == 3     # fp32 d=128: workspace too small
+    st = lib.la_backward_causal_state
+    sargs = [A, A + 0x1000000, A + 0x2000000, A + 0x3000000, A + 0x8000000, None, None, None,
+             A + 0x4000000, A + 0x5000000, A + 0x6000000, None, None]
+    assert st(*sargs, 1, 1, 64, 128, 0, 0, A + 0x7000000, 1 << 30, None) == 2  # fp32 d=128 from a start state
 
 
 def test_decode_steps_validation(lib):

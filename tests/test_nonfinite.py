@@ -36,11 +36,6 @@ CASES = [(1, 2, 256, 64, 130), (1, 8, 64 * 130 + 17, 64, 64 * 70 + 37), (1, 2, 3
 IDS = ["N256_t130", "N8337_t4517", "d128_t200", "d32_t77", "seg5_t1381"]
 
 
-def skip_f32_128(dtype, d):
-    if dtype == torch.float32 and d == 128:
-        pytest.skip("fp32 causal backward is built for d <= 64")
-
-
 def finite_rows(x):
     return torch.isfinite(x).all(-1).cpu().numpy()
 
@@ -102,7 +97,6 @@ def test_backward_strict_inside_chunk(la, oracle, case, dtype):
     """NaN keys and inf values from t0 on: dQ rows < t0 are bitwise unchanged (dQ_i reads
     keys and values <= i only); every gradient row the oracle finds non-finite is non-finite."""
     B, H, N, d, t0 = case
-    skip_f32_128(dtype, d)
     q, k, v, do = draw(B, H, N, d, dtype, seed=t0 + 3)
     g = la.la_backward_causal(q, k, v, do)
     k2, v2 = k.clone(), v.clone()
@@ -124,7 +118,6 @@ def test_backward_from_saved_state_nonfinite(la, case, dtype):
     state each segment starts from, summed once by the forward): the same results as the
     backward that forms the segment records itself, NaN for NaN, bit for bit elsewhere."""
     B, H, N, d, t0 = case
-    skip_f32_128(dtype, d)
     q, k, v, do = draw(B, H, N, d, dtype, seed=t0 + 5)
     k[:, :, t0:] = float("nan")
     v[:, :, t0:] = float("inf")
@@ -147,7 +140,6 @@ def test_backward_strict_for_later_keys(la, oracle, case, dtype, what):
     unchanged (they read tokens >= s only), as are dQ rows other than t0; dK and dV rows
     <= t0 and dQ row t0 are not finite, as in the oracle."""
     B, H, N, d, t0 = case
-    skip_f32_128(dtype, d)
     q, k, v, do = draw(B, H, N, d, dtype, seed=t0 + 4)
     g = la.la_backward_causal(q, k, v, do)
     q2, do2 = q.clone(), do.clone()

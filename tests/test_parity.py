@@ -290,8 +290,6 @@ def test_forward_noncausal(la, oracle, shape, dtype):
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_backward_causal(la, oracle, shape, dtype):
     B, H, N, d = shape
-    if dtype == torch.float32 and d == 128:
-        pytest.skip("fp32 causal path is built for d <= 64")
     run_bwd_causal(la, oracle, B, H, N, d, dtype, seed=N + 2)
 
 
@@ -471,8 +469,6 @@ def test_saved_state_roundtrip_noncausal(la, shape, dtype):
 def test_saved_state_roundtrip(la, shape, dtype):
     """The backward fed the forward's saved state gives bitwise the results of the one that rebuilds it."""
     B, H, N, d = shape
-    if dtype == torch.float32 and d == 128:
-        pytest.skip("fp32 causal path is built for d <= 64")
     q, k, v, do = draw(B, H, N, d, dtype, seed=N + 3)
     st = la.new_saved_state(q)
     o1 = la.la_forward_causal(q, k, v, saved_state=st)
