@@ -33,15 +33,15 @@
  *     result beyond rounding (the reassociation of "Intuition"): it is a tiling
  *     choice, and the kernels map a 64-token chunk onto four 16-row MFMA tiles,
  *     one per wavefront of a role.
- *   - LA_F32 at d = 128 is built for the non-causal forward, decode, the causal
- *     forward and the causal backward; the causal pair runs there on two blocks of
- *     64 features of phi(Q), phi(K) (formed in the workspace), one half of the
- *     value columns at a time (the one-kernel fp32 tiles at d = 128 need more LDS
- *     than a CU has): phi = elu + 1 from a zero state (no S0 / z0 in the backward,
- *     no state gradients), no grouped heads, and a saved state is taken but left
- *     unused (the backward recomputes the forward on the blocks).  The non-causal
- *     backward returns LA_ERR_UNSUPPORTED for fp32 at d = 128 (its fp32 tiles and
- *     states need more LDS and registers per workgroup than a CU has).  bf16 covers
+ *   - LA_F32 at d = 128: the non-causal forward and decode run native kernels;
+ *     the causal forward and both backwards run on two blocks of 64 features of
+ *     phi(Q), phi(K) (formed in the workspace), one half of the value columns at a
+ *     time (the one-kernel fp32 tiles and states at d = 128 need more LDS and
+ *     registers than a CU has): phi = elu + 1 from a zero state in the backward
+ *     (no S0 / z0, no state gradients), no grouped heads, and a saved state is
+ *     taken but left unused by the causal forward and both backwards (they
+ *     recompute on the blocks).  The *_features calls on given features keep
+ *     fp32 at d = 32 and 64 for their backward and causal forward.  bf16 covers
  *     d = 128 on every call.
  *   - The caller owns every buffer, including the workspace, whose size comes
  *     from la_workspace_size().  The library never allocates or frees device
@@ -184,7 +184,9 @@ la_status la_backward_causal(const void* q, const void* k, const void* v, const 
  * then dQ = dphi(Q) * phi'(Q), dK = dphi(K) * phi'(K).  den and O are
  * recomputed in fp32 from q, k, v.  saved_state (nullable) is the buffer a
  * la_forward_noncausal call on the same k, v and shape filled; when NULL the
- * key aggregates are rebuilt from k, v, with bitwise the same results.  d = 32, 64, 128 in bf16; 32, 64 in fp32.
+ * key aggregates are rebuilt from k, v, with bitwise the same results.  fp32 at
+ * d = 128 runs per value half on two 64-feature blocks as la_backward_causal does
+ * there (the saved state is not read).
  * In: q, k, v, dout [B][H][N][d].  Out: dq, dk, dv [B][H][N][d]. */
 la_status la_backward_noncausal(const void* q, const void* k, const void* v, const void* dout,
                                 void* dq, void* dk, void* dv, const void* saved_state,

@@ -292,18 +292,18 @@ F128Layout f128_layout(int64_t B, int64_t H, int64_t N) {
     return L;
 }
 
-// fp32 at d = 128, the causal backward, on the same feature blocks: per value half, the
-// forward on the blocks (its output half and the head's den) and the blocks' backward
-// with g from that output half (the halves' g add up to the row's g, and dphi(Q),
-// dphi(K) are linear in dA, so the halves' feature gradients add up); dq, dk = the
-// sum over the halves times phi'.  Workspace: features and their two gradients each,
-// one value half with its output, upstream gradient and dv, den, and the blocks'
-// forward and backward workspaces.
+// fp32 at d = 128, the causal and non-causal backward, on the same feature blocks: per
+// value half, the forward on the blocks (its output half and the head's den) and the
+// blocks' backward with g from that output half (the halves' g add up to the row's g,
+// and dphi(Q), dphi(K) are linear in G and g, so the halves' feature gradients add up);
+// dq, dk = the sum over the halves times phi'.  Workspace: features and their two
+// gradients each, one value half with its output, upstream gradient and dv, den, and
+// the blocks' forward and backward workspaces.
 struct B128Layout {
     size_t fq = 0, fk = 0, dfq[2] = {0, 0}, dfk[2] = {0, 0}, vh = 0, oh = 0, doh = 0, dvh = 0, den = 0;
     size_t fwd = 0, fwd_bytes = 0, bwd = 0, bwd_bytes = 0, bytes = 0;
 };
-B128Layout b128_layout(int64_t B, int64_t H, int64_t N) {
+B128Layout b128_layout(bool causal, int64_t B, int64_t H, int64_t N) {
     B128Layout L;
     if (B == 0 || H == 0 || N == 0) return L;
     const int64_t BH = B * H;
@@ -319,9 +319,12 @@ B128Layout b128_layout(int64_t B, int64_t H, int64_t N) {
     L.dvh = L.doh + half;
     L.den = L.dvh + half;
     L.fwd = L.den + align_up((size_t)BH * N * sizeof(float));
-    L.fwd_bytes = align_up(block_layout(true, B, H, N, 64, 2, LA_F32).bytes);
+    L.fwd_bytes = align_up(block_layout(causal, B, H, N, 64, 2, LA_F32).bytes);
     L.bwd = L.fwd + L.fwd_bytes;
-    L.bwd_bytes = align_up(layout(LA_OP_BWD_CAUSAL, B, 2 * H, N, 64).bytes) + align_up((size_t)BH * N * 128 * sizeof(float));
+    // the blocks' backward: its block heads' workspace and dv, and (non-causal) two row statistics per block row
+    L.bwd_bytes = align_up(layout(causal ? LA_OP_BWD_CAUSAL : LA_OP_BWD_NONCAUSAL, B, 2 * H, N, 64).bytes) +
+                  align_up((size_t)BH * N * 128 * sizeof(float)) +
+                  (causal ? 0 : align_up((size_t)BH * 2 * N * 2 * sizeof(float)));
     L.bytes = L.bwd + L.bwd_bytes;
     return L;
 }
@@ -410,8 +413,8 @@ la_status la_workspace_size(la_op op, int64_t B, int64_t H, int64_t N, int64_t d
     if (st != LA_OK) return st;
     if (op == LA_OP_FWD_CAUSAL && dt == LA_F32 && d == 128)
         *bytes_out = empty ? 0 : f128_layout(B, H, N).bytes;
-    else if (op == LA_OP_BWD_CAUSAL && dt == LA_F32 && d == 128)
-        *bytes_out = empty ? 0 : b128_layout(B, H, N).bytes;
+    else if ((op == LA_OP_BWD_CAUSAL || op == LA_OP_BWD_NONCAUSAL) && dt == LA_F32 && d == 128)
+        *bytes_out = empty ? 0 : b128_layout(op == LA_OP_BWD_CAUSAL, B, H, N).bytes;
     else
         *bytes_out = empty ? 0 : layout(op, B, H, N, d).bytes;
     return LA_OK;
@@ -940,9 +943,9 @@ la_status la_forward_noncausal_features_blocks(const void* fq, const void* fk, c
 
 
 
-static la_status backward_causal_f128(const void* q, const void* k, const void* v, const void* dout, void* dq,
-                                      void* dk, void* dv, int64_t B, int64_t H, int64_t N, void* workspace,
-                                      size_t workspace_bytes, hipStream_t s);
+static la_status backward_f128(bool causal, const void* q, const void* k, const void* v, const void* dout, void* dq,
+                               void* dk, void* dv, int64_t B, int64_t H, int64_t N, void* workspace,
+                               size_t workspace_bytes, hipStream_t s);
 
 static la_status backward_causal(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
                                  void* dv, const void* saved_state, size_t saved_state_bytes, const float* S0,
@@ -980,7 +983,7 @@ static la_status backward_causal(const void* q, const void* k, const void* v, co
         return LA_OK;
     }
     // (fp32 at d = 128 does not read a saved state: it recomputes the forward on the feature blocks.)
-    if (f128) return backward_causal_f128(q, k, v, dout, dq, dk, dv, B, H, N, workspace, workspace_bytes, s);
+    if (f128) return backward_f128(true, q, k, v, dout, dq, dk, dv, B, H, N, workspace, workspace_bytes, s);
     const Layout L = layout(LA_OP_BWD_CAUSAL, B, H, N, d);
     if ((st = check_workspace(L, workspace, workspace_bytes)) != LA_OK) return st;
     const Range wsr[] = {{"workspace", workspace, L.bytes}};
@@ -1112,7 +1115,10 @@ static la_status backward_noncausal(const void* q, const void* k, const void* v,
     bool empty = false;
     la_status st = check_shape(B, H, N, d, 0, dt, &empty);
     if (st != LA_OK) return st;
-    if (dt == LA_F32 && d == 128) return fail(LA_ERR_UNSUPPORTED, "fp32 non-causal backward is built for d = 32 and 64");
+    // fp32 at d = 128 runs on feature blocks (backward_f128), for phi = elu + 1.
+    const bool f128 = dt == LA_F32 && d == 128;
+    if (f128 && feat != la::kFeatElu)
+        return fail(LA_ERR_UNSUPPORTED, "fp32 at d = 128: only the non-causal backward of phi = elu + 1 is built");
     if (N > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv))
         return fail(LA_ERR_INVALID_ARGUMENT, "q, k, v, dout, dq, dk and dv must be non-NULL");
     const size_t tb = (size_t)B * H * N * d * elem_size(dt);
@@ -1123,6 +1129,10 @@ static la_status backward_noncausal(const void* q, const void* k, const void* v,
     const Range out[] = {{"dq", dq, tb}, {"dk", dk, tb}, {"dv", dv, tb}};
     if ((st = check_ptrs(in, 5, out, 3)) != LA_OK) return st;
     if (empty) return LA_OK;
+    // (fp32 at d = 128 does not read a saved state: it recomputes the forward on the feature blocks.)
+    if (f128)
+        return backward_f128(false, q, k, v, dout, dq, dk, dv, B, H, N, workspace, workspace_bytes,
+                             static_cast<hipStream_t>(stream));
     const Layout L = layout(LA_OP_BWD_NONCAUSAL, B, H, N, d);
     if ((st = check_workspace(L, workspace, workspace_bytes)) != LA_OK) return st;
     const Range wsr[] = {{"workspace", workspace, L.bytes}};
@@ -1478,10 +1488,10 @@ la_status la_decode_steps_features_blocks(float* S, float* z, const void* fq, co
 
 }  // extern "C"
 
-static la_status backward_causal_f128(const void* q, const void* k, const void* v, const void* dout, void* dq,
-                                      void* dk, void* dv, int64_t B, int64_t H, int64_t N, void* workspace,
-                                      size_t workspace_bytes, hipStream_t s) {
-    const B128Layout L = b128_layout(B, H, N);
+static la_status backward_f128(bool causal, const void* q, const void* k, const void* v, const void* dout, void* dq,
+                               void* dk, void* dv, int64_t B, int64_t H, int64_t N, void* workspace,
+                               size_t workspace_bytes, hipStream_t s) {
+    const B128Layout L = b128_layout(causal, B, H, N);
     char* ws = static_cast<char*>(workspace);
     if (ws == nullptr) return fail(LA_ERR_WORKSPACE, "workspace is NULL; %zu bytes are needed", L.bytes);
     if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
@@ -1516,11 +1526,13 @@ static la_status backward_causal_f128(const void* q, const void* k, const void* 
             (e = timed("copy_cols", s, [&] { return la::launch_copy_cols(doh, 64, dosrc, 128, BH * N, 64, s); })) !=
                 hipSuccess)
             return hip_fail(e, "copy_cols launch");
-        la_status st = forward_blocks(true, fq, fk, vh, oh, nullptr, nullptr, den, nullptr, nullptr, B, H, N, 64, 128,
-                                      LA_F32, ws + L.fwd, L.fwd_bytes, s);
+        la_status st = forward_blocks(causal, fq, fk, vh, oh, nullptr, nullptr, den, nullptr, nullptr, B, H, N, 64,
+                                      128, LA_F32, ws + L.fwd, L.fwd_bytes, s);
         if (st != LA_OK) return st;
-        st = la_backward_causal_features_blocks(fq, fk, vh, doh, den, oh, ws + L.dfq[h], ws + L.dfk[h], dvh, B, H, N,
-                                                64, 128, LA_F32, ws + L.bwd, L.bwd_bytes, s);
+        st = causal ? la_backward_causal_features_blocks(fq, fk, vh, doh, den, oh, ws + L.dfq[h], ws + L.dfk[h], dvh,
+                                                         B, H, N, 64, 128, LA_F32, ws + L.bwd, L.bwd_bytes, s)
+                    : la_backward_noncausal_features_blocks(fq, fk, vh, doh, den, oh, ws + L.dfq[h], ws + L.dfk[h],
+                                                            dvh, B, H, N, 64, 128, LA_F32, ws + L.bwd, L.bwd_bytes, s);
         if (st != LA_OK) return st;
         float* dvdst = static_cast<float*>(dv) + 64 * h;
         if ((e = timed("copy_cols", s, [&] { return la::launch_copy_cols(dvdst, 128, dvh, 64, BH * N, 64, s); })) !=

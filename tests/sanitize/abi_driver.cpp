@@ -162,6 +162,16 @@ int main() {
         return la_backward_noncausal(P(s.q), P(s.k), P(s.v), P(s.dout), P(s.dq), P(s.dk), P(s.dv), nullptr, 0, 4, 16,
                                      4096, 64, LA_BF16, P(s.w), ws(LA_OP_BWD_NONCAUSAL, 4, 16, 4096, 64), nullptr);
     });
+    check("noncausal bwd: fp32 d=128 (feature blocks)", LA_OK, true, [&] {
+        return la_backward_noncausal(P(s.q), P(s.k), P(s.v), P(s.dout), P(s.dq), P(s.dk), P(s.dv), nullptr, 0, 2, 3,
+                                     1000, 128, LA_F32, P(s.w), ws(LA_OP_BWD_NONCAUSAL, 2, 3, 1000, 128, LA_F32),
+                                     nullptr);
+    });
+    check("noncausal bwd: fp32 d=128 workspace short", LA_ERR_WORKSPACE, false, [&] {
+        return la_backward_noncausal(P(s.q), P(s.k), P(s.v), P(s.dout), P(s.dq), P(s.dk), P(s.dv), nullptr, 0, 2, 3,
+                                     1000, 128, LA_F32, P(s.w), ws(LA_OP_BWD_NONCAUSAL, 2, 3, 1000, 128, LA_F32) - 256,
+                                     nullptr);
+    });
     check("noncausal bwd: dtype unknown", LA_ERR_UNSUPPORTED, false, [&] {
         return la_backward_noncausal(P(s.q), P(s.k), P(s.v), P(s.dout), P(s.dq), P(s.dk), P(s.dv), nullptr, 0, 4, 16,
                                      4096, 64, (la_dtype)7, P(s.w), GB, nullptr);

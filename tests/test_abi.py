@@ -188,7 +188,7 @@ def test_backward_noncausal_validation(lib):
     wsp = A + 0x7000000
     assert b(*args, None, 0, 1, 1, 64, 64, 1, wsp, 8, None) == 3                   # workspace too small
     assert b(*args, None, 0, 1, 1, 64, 96, 1, wsp, 1 << 30, None) == 2             # d unsupported
-    assert b(*args, None, 0, 1, 1, 64, 128, 0, wsp, 1 << 30, None) == 2            # fp32 d=128 not built
+    assert b(*args, None, 0, 1, 1, 64, 128, 0, wsp, 8, None) == 3                  # fp32 d=128: workspace too small
     assert b(*args, None, 0, 1, 1, 0, 64, 1, None, 0, None) == 0                   # empty
     bad = list(args)
     bad[6] = args[0]                                                                # dv aliases q
