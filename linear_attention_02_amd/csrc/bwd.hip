@@ -470,8 +470,9 @@ __global__ __launch_bounds__(kBlock, 2) void rseg_kernel(const T* __restrict__ q
 // in the accumulators that form them and feed the dV and dK products directly;
 // w = sum_a R[a][b] comes from the same R^T operands against a ones operand.
 // kCoherentRecords: the (R, r) records of the later segments are read with
-// agent-coherent loads (written by other workgroups of the same launch).
-// poison: the records could not be confirmed; the results are made NaN.
+// agent-coherent loads (written by other workgroups of the same launch), each batch
+// of them once records_ready(s0, s1) has confirmed segments s0 .. s1-1 (false: they
+// could not be confirmed, and the results are made NaN).
 // rinit (nullable): per head, a record [dS_N^T | dz_N | 0] of upstream gradients of
 // the final state, which every suffix sum starts from.  dS0, dz0 (nullable): the
 // first segment writes the suffix state at the first token there, the gradient of
@@ -518,10 +519,8 @@ __device__ __forceinline__ void bwd_suffix_body(
         gv = brs.ld4f((uint32_t)(c + (tid & (kC - 1))) * 8 + 4);
     };
     // The first chunk's loads are in flight while the later segments' records are
-    // awaited (records_ready() false: they could not be confirmed, and the results
-    // are made NaN) and read.
+    // awaited and read.
     load_chunk(tok_begin + (nch - 1) * kC, w);
-    const bool poison = !records_ready();
     constexpr int kRecRegs = 192 - (int)((2 * sizeof(CR) + 2 * sizeof(RowAcc<T, D>)) / 4) - 8;
 
     // Suffix state (R, r): the records of the segments after this one, last segment first.
@@ -538,8 +537,12 @@ __device__ __forceinline__ void bwd_suffix_body(
             zero_vec<D>(vr);
         }
         zero_vec<D>(vunused);
+        // Record j is segment nseg-1-j: the last segments' records (their workgroups
+        // were dispatched first) are summed while the nearer ones are still on their way.
+        bool poison = false;
         add_records_from<D, kRecRegs>(RecCoherent{brr}, (int64_t)(nseg - 1) * Rec<D>::kSize,
-                                      -(int64_t)Rec<D>::kSize, nseg - 1 - seg, stR, vr, vunused, lane, w);
+                                      -(int64_t)Rec<D>::kSize, nseg - 1 - seg, stR, vr, vunused, lane, w,
+                                      [&](int j0, int j1) { poison = !records_ready(nseg - j1, nseg - j0) || poison; });
         if (poison) {
             using ST = StateTiles<D>;
             const float nan = __builtin_nanf("");
@@ -761,6 +764,7 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_fused_ker
     constexpr size_t kP = BwdPrefixLds<T, D>::kBytes, kS = BwdSuffixLds<T, D>::kBytes;
     __shared__ __attribute__((aligned(16))) char lds[kP > kS ? kP : kS];
     const int seg = nseg - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
+    if (threadIdx.x == 0) giveups[(int64_t)bh * nseg + seg] = 0u;  // ordered before any wave's give-up by the barriers below
     bwd_prefix_body<T, D, true, true, kState, FM>(q, k, v, dout, dq, rowstat, rrec, rec, N, cps, nseg, 0, seg, bh, lds,
                                                   init, init_n);
     // Every wave's record stores (and den, g rows) are complete before the flag.
@@ -768,14 +772,14 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_fused_ker
     __syncthreads();
     unsigned long long* hf = flags + (int64_t)bh * nseg;
     if (threadIdx.x == 0) post_flag(&hf[seg], epoch);
-    auto records_ready = [&] {
+    // Each wave confirms the flags of the records it is about to read (segments s0 .. s1-1).
+    bool all_ok = true;
+    auto records_ready = [&](int s0, int s1) {
         bool ok = true;
         if ((threadIdx.x & 63) == 0)
-            for (int j = seg + 1; j < nseg; ++j) ok = ok && await_flag(&hf[j], epoch, wait_limit);
+            for (int j = s0; j < s1; ++j) ok = ok && await_flag(&hf[j], epoch, wait_limit);
         ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
-        // The host reads these counts back (la_wait_failures): a give-up
-        // leaves NaN rows that must not pass for a result of the data.
-        if (threadIdx.x == 0) giveups[(int64_t)bh * nseg + seg] = ok ? 0u : 1u;
+        all_ok = all_ok && ok;
         return ok;
     };
     // The first half of the segments (dispatched last, so usually the younger of the
@@ -784,6 +788,10 @@ __global__ __launch_bounds__(kBlock, LA_HEAVY_WAVES_PER_SIMD) void bwd_fused_ker
     if (2 * seg < nseg) __builtin_amdgcn_s_setprio(1);
     bwd_suffix_body<T, D, true, kState, FM>(q, k, v, dout, dk, dv, rowstat, rrec, N, cps, nseg, 0, seg, bh,
                                             records_ready, lds, rinit, dS0, dz0);
+    // The host reads these counts back (la_wait_failures): a give-up leaves NaN rows
+    // that must not pass for a result of the data.  Thread 0 cleared the count before
+    // the prefix sweep; any wave that gave up sets it.
+    if ((threadIdx.x & 63) == 0 && !all_ok) atomicOr(&giveups[(int64_t)bh * nseg + seg], 1u);
 }
 
 // ---------------------------------------------------------------------------------------

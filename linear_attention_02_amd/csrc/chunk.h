@@ -309,14 +309,18 @@ struct RecCoherent {
 // that order, to the wave's state tiles and vector tiles (fixed order: bitwise
 // reproducible).  kRegs: registers the records in flight may take (at most 8
 // records per batch).  kVecB false: the records' second vector is not read (vb is
-// left as it is), so that more records fit a batch.
-template <int D, int kRegs, bool kVecB = true, typename Src>
+// left as it is), so that more records fit a batch.  ready(j0, j1), called by the
+// wave before records j0 .. j1-1 are read (it may wait for them), lets the first
+// batches be summed while later records are still being produced.
+template <int D, int kRegs, bool kVecB = true, typename Src, typename Ready>
 __device__ __forceinline__ void add_records_from(const Src& src, int64_t base, int64_t stride, int count,
-                                                 StateAcc<D>& st, VecAcc<D>& va, VecAcc<D>& vb, int lane, int w) {
+                                                 StateAcc<D>& st, VecAcc<D>& va, VecAcc<D>& vb, int lane, int w,
+                                                 Ready&& ready) {
     using ST = StateTiles<D>;
     constexpr int PER_REC = 4 * (ST::NAT * ST::NBT + (kVecB ? 2 : 1) * ST::NVT);
     constexpr int B = kRegs / PER_REC >= 8 ? 8 : kRegs / PER_REC >= 1 ? kRegs / PER_REC : 1;
     for (int j0 = 0; j0 < count; j0 += B) {
+        ready(j0, j0 + B < count ? j0 + B : count);
         f32x4 xs[B][ST::NAT][ST::NBT], xa[B][ST::NVT], xb[B][ST::NVT];
 #pragma unroll
         for (int b = 0; b < B; ++b) {
@@ -350,6 +354,12 @@ __device__ __forceinline__ void add_records_from(const Src& src, int64_t base, i
             }
         }
     }
+}
+
+template <int D, int kRegs, bool kVecB = true, typename Src>
+__device__ __forceinline__ void add_records_from(const Src& src, int64_t base, int64_t stride, int count,
+                                                 StateAcc<D>& st, VecAcc<D>& va, VecAcc<D>& vb, int lane, int w) {
+    add_records_from<D, kRegs, kVecB>(src, base, stride, count, st, va, vb, lane, w, [](int, int) {});
 }
 
 // The same for records read through a plain pointer: rec[j * stride], j = 0 .. count-1.
