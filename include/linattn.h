@@ -226,7 +226,12 @@ la_status la_decode_step(float* S, float* z, const void* q, const void* k, const
  * is read and written once per call (not once per token) and once per group
  * (not once per query head).  S [B][Hkv][d][d] and z [B][Hkv][d] are fp32 and
  * updated in place; q, o are [B][H][T][d] and k, v [B][Hkv][T][d] in dtype dt
- * (token t at row t).  T = 0 does nothing.  Needs no workspace. */
+ * (token t at row t).  T = 0 does nothing.  Needs no workspace.  With several
+ * query heads per state (H > Hkv) at d = 64 or 128 the rows (t, h) are formed in
+ * blocks of tokens by the chunked form of the same recurrence (fp32 MFMA
+ * products, the state updated after each block's whole tokens): the same values
+ * up to fp32 rounding, and an inf or NaN of token t reaches no row of an earlier
+ * token. */
 la_status la_decode_steps(float* S, float* z, const void* q, const void* k, const void* v, void* o,
                           int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t d, la_dtype dt,
                           void* stream);

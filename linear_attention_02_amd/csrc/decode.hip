@@ -213,11 +213,345 @@ __global__ __launch_bounds__(kBlock) void decode_steps_kernel(float* __restrict_
     if (tid < D) z[(int64_t)kvh * D + tid] = zn;
 }
 
+// ---------------------------------------------------------------------------------------
+// decode_steps_grouped: the same T steps for G >= 2 query heads per key/value state, with
+// every product on MFMA.  The G query heads of a token all read one state, so a block of
+// rows (t, h) (token-major, up to 64 rows) is the causal form of the proposition over the
+// block's tokens tau0 .. tau1, chunked:
+//   num_r = phi(q_r)^T S_<tau0 + sum_{tau0 <= tau <= t(r)} (phi(q_r).phi(k_tau)) v_tau,
+//   den_r = phi(q_r)^T z_<tau0 + sum_{tau0 <= tau <= t(r)} phi(q_r).phi(k_tau),
+// and S, z then take the updates of the block's tokens whose rows are all done (a token
+// whose rows continue into the next block is that block's first key).  The state term is
+// a [rows x d] x [d x d] product, the in-block terms [rows x keys] products, the update a
+// rank-(keys) product; all run as fp32 MFMA (v_mfma_f32_16x16x4_f32), so the state keeps
+// fp32 arithmetic throughout, as in the one-row kernels.
+// Wave w holds state columns w d/4 .. (w + 1) d/4 - 1 of every feature row in accumulator
+// tiles: element i of lane (g, c) of tile (at, bt) is S[16 at + 4 g + i][w d/4 + 16 bt + c].
+// Read as the B operand of a product that contracts over features in the order
+// 16 at + 4 g + i (the A operand, phi(q), is read from LDS in that order), the tiles need
+// no movement; the update accumulates into them.  The state moves through LDS once in
+// each direction (16-byte global accesses).  A later token's inf or NaN in v would reach
+// earlier rows through the masked zeros of the in-block product (0 * inf = NaN): blocks
+// holding one take v with non-finite entries replaced by 0 there, and the rows that do
+// read such a token get it back explicitly (num += v - v).
+template <typename T>
+__device__ __forceinline__ f32x4 gload4(const T* p);
+template <>
+__device__ __forceinline__ f32x4 gload4<float>(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+template <>
+__device__ __forceinline__ f32x4 gload4<bf16>(const bf16* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    const bf16* h = reinterpret_cast<const bf16*>(&u);
+    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+}
+
+template <int D>
+struct GroupedDecodeCfg {
+    static constexpr int RBM = 64;           // rows (token, query head) per block at most
+    static constexpr int KM = 16;            // key slots per block: blocks start at multiples of the row count,
+                                             // so 64 rows of G >= 4 heads (32 of G = 2, 3) span at most 16 tokens
+    static constexpr int DP = D + 4;         // LDS row stride in floats: 16 rows read 16 bytes each without conflicts
+    static constexpr int AP = KM + 4;
+    static constexpr int NAT = D / 16;       // feature tiles of the state
+    static constexpr int CPW = D / 4;        // state columns per wave
+    static constexpr int NBT = CPW / 16;     // column tiles per wave
+};
+
+template <typename T, int D, class FM>
+__global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* __restrict__ S, float* __restrict__ z,
+                                                                      const T* __restrict__ q, const T* __restrict__ k,
+                                                                      const T* __restrict__ v, T* __restrict__ o,
+                                                                      int ntok, int G) {
+    using C = GroupedDecodeCfg<D>;
+    constexpr int RBM = C::RBM, KM = C::KM, DP = C::DP, AP = C::AP, NAT = C::NAT, CPW = C::CPW, NBT = C::NBT;
+    constexpr int F4 = D / 4;
+    static_assert(NBT >= 1 && kBlock == 4 * kWave && RBM % 16 == 0 && D % RBM == 0,
+                  "four waves, whole column tiles per wave, the state in whole row buffers");
+    __shared__ __attribute__((aligned(16))) float sQ[RBM * DP];  // phi(q) of the block's rows; the state; outputs
+    __shared__ __attribute__((aligned(16))) float sK[KM * DP];   // phi(k) of the block's keys
+    __shared__ __attribute__((aligned(16))) float sV[KM * DP];   // v of the block's keys
+    __shared__ __attribute__((aligned(16))) float sA[RBM * AP];  // masked phi(q_r).phi(k_tau)
+    __shared__ __attribute__((aligned(16))) float sZ[D];
+    __shared__ float sDen[RBM];  // 1 / den of each row
+
+    const int64_t bkv = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave, g = lane >> 4, c16 = lane & 15;
+    const int cb0 = w * CPW;
+    float* const Sh = S + bkv * D * D;
+    const int64_t krow0 = bkv * ntok;
+    const int nrows = G * ntok;  // the launcher keeps it below 2^31
+    const int rb = G >= 4 ? RBM : RBM / 2;  // at most KM keys per block either way
+    const int nrt = rb / 16;
+    auto qoff = [&](int ra) {  // element offset of row ra = t G + h
+        const int t = ra / G, h = ra - t * G;
+        return ((bkv * G + h) * ntok + t) * D;
+    };
+
+    f32x4 st[NAT][NBT];
+    constexpr int NS = D * F4 / kBlock;  // 16-byte state loads per thread, all issued at once
+    f32x4 sld[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const int i4 = tid + j * kBlock;
+        sld[j] = *reinterpret_cast<const f32x4*>(&Sh[(int64_t)(i4 / F4) * D + 4 * (i4 % F4)]);
+    }
+#pragma unroll
+    for (int a0 = 0; a0 < D; a0 += RBM) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const int i4 = tid + j * kBlock, a = i4 / F4;
+            if (a >= a0 && a < a0 + RBM) *reinterpret_cast<f32x4*>(&sQ[(a - a0) * DP + 4 * (i4 % F4)]) = sld[j];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int at = 0; at < NAT; ++at)
+            if (16 * at >= a0 && 16 * at < a0 + RBM)
+#pragma unroll
+                for (int bt = 0; bt < NBT; ++bt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) st[at][bt][i] = sQ[(16 * at - a0 + 4 * g + i) * DP + cb0 + 16 * bt + c16];
+        __syncthreads();
+    }
+    float zn = 0.f;
+    if (tid < D) {
+        zn = z[bkv * D + tid];
+        sZ[tid] = zn;
+    }
+
+    int tau0 = 0;
+    for (int r0 = 0; r0 < nrows;) {
+        const int nb = min(rb, nrows - r0), rend = r0 + nb;
+        const int tbk = (rend - 1) / G - tau0 + 1;       // keys tau0 .. t(rend - 1)
+        const int tba = rend % G == 0 ? tbk : tbk - 1;  // keys whose rows are all done
+        const int nkt = (tbk + 15) / 16, nka = (tba + 15) / 16;
+
+        // Stage phi(q) of the rows (zero past the block), phi(k) and v of the keys (zero past them).
+        // Rows and keys past the block load a valid row (every load of the loop is issued
+        // before the first use) and stage zeros.
+        constexpr int NQ = RBM * F4 / kBlock, NK = KM * F4 / kBlock;
+        static_assert(NQ * kBlock == RBM * F4 && NK * kBlock == KM * F4, "whole staging passes");
+        f32x4 xq[NQ], xk[NK], xv[NK];
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const int i4 = tid + j * kBlock, r = i4 / F4, c = 4 * (i4 % F4);
+            xq[j] = gload4<T>(q + qoff(r0 + min(r, nb - 1)) + c);
+        }
+#pragma unroll
+        for (int j = 0; j < NK; ++j) {
+            const int i4 = tid + j * kBlock, s = i4 / F4, c = 4 * (i4 % F4);
+            const int64_t off = (krow0 + tau0 + min(s, tbk - 1)) * D + c;
+            xk[j] = gload4<T>(k + off);
+            xv[j] = gload4<T>(v + off);
+        }
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const int i4 = tid + j * kBlock, r = i4 / F4, c = 4 * (i4 % F4);
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = r < nb ? FM::phi(xq[j][e]) : 0.f;
+            *reinterpret_cast<f32x4*>(&sQ[r * DP + c]) = x;
+        }
+        int bad = 0;
+#pragma unroll
+        for (int j = 0; j < NK; ++j) {
+            const int i4 = tid + j * kBlock, s = i4 / F4, c = 4 * (i4 % F4);
+            f32x4 a, b;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[e] = s < tbk ? FM::phi(xk[j][e]) : 0.f;
+                b[e] = s < tbk ? xv[j][e] : 0.f;
+                bad |= !finite_f(b[e]);
+            }
+            *reinterpret_cast<f32x4*>(&sK[s * DP + c]) = a;
+            *reinterpret_cast<f32x4*>(&sV[s * DP + c]) = b;
+        }
+        const bool vbad = __syncthreads_or(bad) != 0;
+
+        // A[r][s] = phi(q_r).phi(k_{tau0+s}) for tau0 + s <= t(r), else 0: wave w, row tile w.
+        if (w < nrt) {
+#pragma unroll
+            for (int kt = 0; kt < KM / 16; ++kt) {
+                f32x4 acc = zero4();
+                if (kt < nkt) {
+#pragma unroll
+                    for (int at = 0; at < NAT; ++at) {
+                        const f32x4 xq = lds4(&sQ[(16 * w + c16) * DP + 16 * at + 4 * g]);
+                        const f32x4 xk = lds4(&sK[(16 * kt + c16) * DP + 16 * at + 4 * g]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[i], xk[i], acc, 0, 0, 0);
+                    }
+                }
+                const int s = 16 * kt + c16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * w + 4 * g + e;
+                    const bool live = r < nb && s < tbk && tau0 + s <= (r0 + r) / G;
+                    sA[r * AP + s] = live ? acc[e] : 0.f;
+                }
+            }
+        }
+        __syncthreads();
+
+        // den_r = phi(q_r).z + sum_s A[r][s]: four threads per row.
+        {
+            const int r = tid >> 2, p = tid & 3;
+            float dp = 0.f;
+            if (r < nb) {
+#pragma unroll
+                for (int a = p * F4; a < (p + 1) * F4; a += 4) {
+                    const f32x4 x = lds4(&sQ[r * DP + a]), zz = lds4(&sZ[a]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dp += x[e] * zz[e];
+                }
+#pragma unroll
+                for (int s = p * (KM / 4); s < (p + 1) * (KM / 4); s += 4) {
+                    const f32x4 x = lds4(&sA[r * AP + s]);
+                    dp += (x[0] + x[1]) + (x[2] + x[3]);
+                }
+            }
+            dp += __shfl_xor(dp, 1, kWave);
+            dp += __shfl_xor(dp, 2, kWave);
+            if (p == 0 && r < nb) sDen[r] = rcp_f(dp);  // 1 / den
+        }
+
+        // num = phi(Q) S + A V for this wave's columns.
+        f32x4 num[RBM / 16][NBT];
+#pragma unroll
+        for (int rt = 0; rt < RBM / 16; ++rt) {
+#pragma unroll
+            for (int bt = 0; bt < NBT; ++bt) num[rt][bt] = zero4();
+            if (rt < nrt) {
+#pragma unroll
+                for (int at = 0; at < NAT; ++at) {
+                    const f32x4 xq = lds4(&sQ[(16 * rt + c16) * DP + 16 * at + 4 * g]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int bt = 0; bt < NBT; ++bt)
+                            num[rt][bt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[i], st[at][bt][i], num[rt][bt], 0, 0, 0);
+                }
+#pragma unroll
+                for (int kt = 0; kt < KM / 16; ++kt) {
+                    if (kt < nkt) {
+                        const f32x4 xa = lds4(&sA[(16 * rt + c16) * AP + 16 * kt + 4 * g]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int bt = 0; bt < NBT; ++bt) {
+                                float yv = sV[(16 * kt + 4 * g + i) * DP + cb0 + 16 * bt + c16];
+                                if (vbad) yv = finite_or_zero(yv);
+                                num[rt][bt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[i], yv, num[rt][bt], 0, 0, 0);
+                            }
+                    }
+                }
+            }
+        }
+        __syncthreads();  // den is ready; phi(q) is no longer read
+
+        // o = num / den into the row buffer; the rows that read a non-finite v get it back.
+#pragma unroll
+        for (int rt = 0; rt < RBM / 16; ++rt) {
+            if (rt < nrt) {
+#pragma unroll
+                for (int bt = 0; bt < NBT; ++bt) {
+                    const int b = cb0 + 16 * bt + c16;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 16 * rt + 4 * g + e;
+                        if (r < nb) {
+                            float x = num[rt][bt][e];
+                            if (vbad) {
+                                const int last = (r0 + r) / G - tau0;  // keys tau0 .. tau0 + last
+                                for (int s = 0; s <= last; ++s) {
+                                    const float y = sV[s * DP + b];
+                                    if (!finite_f(y)) x += y - y;
+                                }
+                            }
+                            sQ[r * DP + b] = x * sDen[r];
+                        }
+                    }
+                }
+            }
+        }
+        // S += sum over the finished keys of phi(k) v^T (fp32 MFMA into the state tiles).
+#pragma unroll
+        for (int kt = 0; kt < KM / 16; ++kt) {
+            if (kt < nka) {
+                float yv[NBT][4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int s = 16 * kt + 4 * g + i;
+#pragma unroll
+                    for (int bt = 0; bt < NBT; ++bt) yv[bt][i] = s < tba ? sV[s * DP + cb0 + 16 * bt + c16] : 0.f;
+                }
+#pragma unroll
+                for (int at = 0; at < NAT; ++at) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int s = 16 * kt + 4 * g + i;
+                        const float xk = s < tba ? sK[s * DP + 16 * at + c16] : 0.f;
+#pragma unroll
+                        for (int bt = 0; bt < NBT; ++bt)
+                            st[at][bt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xk, yv[bt][i], st[at][bt], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        __syncthreads();  // the outputs are in the row buffer
+
+        for (int i4 = tid; i4 < nb * F4; i4 += kBlock) {
+            const int r = i4 / F4, c = 4 * (i4 % F4);
+            store4(o + qoff(r0 + r) + c, lds4(&sQ[r * DP + c]));
+        }
+        if (tid < D) {  // z over the finished keys, token by token
+            for (int s = 0; s < tba; ++s) zn += sK[s * DP + tid];
+            sZ[tid] = zn;
+        }
+        __syncthreads();  // the block's buffers are free for the next one
+        r0 = rend;
+        tau0 += tba;
+    }
+
+    // Write the state back through the row buffer (16-byte global stores).
+#pragma unroll
+    for (int a0 = 0; a0 < D; a0 += RBM) {
+#pragma unroll
+        for (int at = 0; at < NAT; ++at)
+            if (16 * at >= a0 && 16 * at < a0 + RBM)
+#pragma unroll
+                for (int bt = 0; bt < NBT; ++bt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sQ[(16 * at - a0 + 4 * g + i) * DP + cb0 + 16 * bt + c16] = st[at][bt][i];
+        __syncthreads();
+        for (int i4 = tid; i4 < RBM * F4; i4 += kBlock) {
+            const int r = i4 / F4, c = 4 * (i4 % F4);
+            *reinterpret_cast<f32x4*>(&Sh[(int64_t)(a0 + r) * D + c]) = lds4(&sQ[r * DP + c]);
+        }
+        __syncthreads();
+    }
+    if (tid < D) z[bkv * D + tid] = zn;
+}
+
 template <class FM>
 static hipError_t launch_decode_steps_fm(int dt, int d, float* S, float* z, const void* q, const void* k,
                                          const void* v, void* o, int64_t BHkv, int64_t T, int64_t G, hipStream_t s,
                                          int KF, float* den_out) {
     const dim3 grid((unsigned)(BHkv * KF));
+    // Several query heads per state: the MFMA kernel (d = 64 and 128, one feature block).
+    if (KF == 1 && G >= 2 && (d == 64 || d == 128) && G * T <= INT32_MAX) {
+#define LA_DECG(TT, DD)                                                                                     \
+    hipLaunchKernelGGL((decode_steps_grouped_kernel<TT, DD, FM>), grid, dim3(kBlock), 0, s, S, z, (const TT*)q, \
+                       (const TT*)k, (const TT*)v, (TT*)o, (int)T, (int)G)
+        if (dt == kBF16) {
+            if (d == 64) LA_DECG(bf16, 64);
+            else LA_DECG(bf16, 128);
+        } else {
+            if (d == 64) LA_DECG(float, 64);
+            else LA_DECG(float, 128);
+        }
+#undef LA_DECG
+        return hipGetLastError();
+    }
 #define LA_DECS(TT, DD)                                                                                    \
     do {                                                                                                   \
         if (KF > 1)                                                                                        \

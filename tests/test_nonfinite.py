@@ -170,3 +170,39 @@ def test_features_forward_strict_inside_chunk(la):
     torch.cuda.synchronize()
     assert torch.equal(o[:, :, :t0], o2[:, :, :t0])
     assert (~finite_rows(o2[:, :, t0:])).all()
+
+
+@pytest.mark.parametrize("poison", ["v_inf", "k_nan"])
+@pytest.mark.parametrize("heads,T,t0", [((8, 1), 16, 5), ((4, 2), 37, 20), ((32, 4), 16, 9)],
+                         ids=["G8_T16_t5", "G2_T37_t20", "G8kv4_T16_t9"])
+def test_grouped_decode_strict(la, oracle, heads, T, t0, poison):
+    """Multi-token decode with several query heads per state: the rows are formed in blocks
+    of tokens, and a poisoned key or value of token t0 must not reach the rows of earlier
+    tokens through the block's masked products; rows of tokens >= t0 that read it are not
+    finite, as in the oracle's recurrence, and the other states are untouched."""
+    H, Hkv = heads
+    B, d, G = 2, 128, H // Hkv
+    gen = inp.generator(T + t0)
+    S0 = (torch.randn(B, Hkv, d, d, generator=gen) * 0.05 + 1.0).float()
+    z0 = torch.full((B, Hkv, d), 40.0) + torch.rand(B, Hkv, d, generator=gen)
+    q = inp.qkv(B, H, T, d, torch.bfloat16, seed=t0, scale=True)[0]
+    _, k, v = inp.qkv(B, Hkv, T, d, torch.bfloat16, seed=t0 + 1, scale=True)
+    k2, v2 = k.clone(), v.clone()
+    if poison == "v_inf":
+        v2[0, 0, t0, 3] = float("inf")
+    else:
+        k2[0, 0, t0, 7] = float("nan")
+    S1, z1, S2, z2 = S0.cuda(), z0.cuda(), S0.cuda(), z0.cuda()
+    o1 = la.la_decode_steps(S1, z1, q.cuda(), k.cuda(), v.cuda())
+    o2 = la.la_decode_steps(S2, z2, q.cuda(), k2.cuda(), v2.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:, :, :t0], o2[:, :, :t0])
+    assert torch.equal(o1[1], o2[1]) and torch.equal(S1[1], S2[1]) and torch.equal(z1[1], z2[1])
+    if Hkv > 1:
+        assert torch.equal(o1[0, G:], o2[0, G:]) and torch.equal(S1[0, 1:], S2[0, 1:])
+    for h in range(G):
+        ro = oracle.forward_causal(f64(q[:1, h:h + 1]), f64(k2[:1, :1]), f64(v2[:1, :1]), S0=f64(S0[:1, :1]),
+                                   z0=f64(z0[:1, :1]))
+        assert (finite_rows(o2[:1, h:h + 1]) == np.isfinite(ro).all(-1)).all()
+        assert not np.isfinite(ro[0, 0, t0:]).all(-1).any()
+    assert not torch.isfinite(S2[0, 0]).all()
