@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kBlock) void decode_steps_kernel(float* __restrict_
 // ---------------------------------------------------------------------------------------
 // decode_steps_grouped: the same T steps for G >= 2 query heads per key/value state, with
 // every product on MFMA.  The G query heads of a token all read one state, so a block of
-// rows (t, h) (token-major, up to 64 rows) is the causal form of the proposition over the
+// rows (t, h) (token-major, up to 32 rows) is the causal form of the proposition over the
 // block's tokens tau0 .. tau1, chunked:
 //   num_r = phi(q_r)^T S_<tau0 + sum_{tau0 <= tau <= t(r)} (phi(q_r).phi(k_tau)) v_tau,
 //   den_r = phi(q_r)^T z_<tau0 + sum_{tau0 <= tau <= t(r)} phi(q_r).phi(k_tau),
@@ -248,7 +248,7 @@ __device__ __forceinline__ f32x4 gload4<bf16>(const bf16* p) {
 template <int D>
 struct GroupedDecodeCfg {
     static constexpr int RBM = 64;           // rows (token, query head) per block at most
-    static constexpr int KM = 16;            // key slots per block: blocks start at multiples of the row count,
+    static constexpr int KM = 16;            // key slots per block: blocks start at multiples of their row count,
                                              // so 64 rows of G >= 4 heads (32 of G = 2, 3) span at most 16 tokens
     static constexpr int DP = D + 4;         // LDS row stride in floats: 16 rows read 16 bytes each without conflicts
     static constexpr int AP = KM + 4;
@@ -288,19 +288,28 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
     };
 
     f32x4 st[NAT][NBT];
-    constexpr int NS = D * F4 / kBlock;  // 16-byte state loads per thread, all issued at once
-    f32x4 sld[NS];
+    // 16-byte state loads, RBM rows per pass, the next pass's loads in flight during this one's
+    constexpr int NSP = RBM * F4 / kBlock;
+    static_assert(NSP * kBlock == RBM * F4, "whole passes");
+    f32x4 sld[NSP], snx[NSP];
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
+    for (int j = 0; j < NSP; ++j) {
         const int i4 = tid + j * kBlock;
         sld[j] = *reinterpret_cast<const f32x4*>(&Sh[(int64_t)(i4 / F4) * D + 4 * (i4 % F4)]);
     }
 #pragma unroll
     for (int a0 = 0; a0 < D; a0 += RBM) {
+        if (a0 + RBM < D) {
 #pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            const int i4 = tid + j * kBlock, a = i4 / F4;
-            if (a >= a0 && a < a0 + RBM) *reinterpret_cast<f32x4*>(&sQ[(a - a0) * DP + 4 * (i4 % F4)]) = sld[j];
+            for (int j = 0; j < NSP; ++j) {
+                const int i4 = tid + j * kBlock;
+                snx[j] = *reinterpret_cast<const f32x4*>(&Sh[(int64_t)(a0 + RBM + i4 / F4) * D + 4 * (i4 % F4)]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NSP; ++j) {
+            const int i4 = tid + j * kBlock;
+            *reinterpret_cast<f32x4*>(&sQ[(i4 / F4) * DP + 4 * (i4 % F4)]) = sld[j];
         }
         __syncthreads();
 #pragma unroll
@@ -311,6 +320,8 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
 #pragma unroll
                     for (int i = 0; i < 4; ++i) st[at][bt][i] = sQ[(16 * at - a0 + 4 * g + i) * DP + cb0 + 16 * bt + c16];
         __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NSP; ++j) sld[j] = snx[j];
     }
     float zn = 0.f;
     if (tid < D) {
@@ -323,7 +334,9 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
         const int nb = min(rb, nrows - r0), rend = r0 + nb;
         const int tbk = (rend - 1) / G - tau0 + 1;       // keys tau0 .. t(rend - 1)
         const int tba = rend % G == 0 ? tbk : tbk - 1;  // keys whose rows are all done
-        const int nkt = (tbk + 15) / 16, nka = (tba + 15) / 16;
+        // Key slot s sits at k index 4 (s % 4) + s / 4 of the in-block products, so the
+        // products over the first n keys take ceil(n / 4) of the four MFMA k-steps.
+        const int nik = (tbk + 3) / 4, nia = (tba + 3) / 4;
 
         // Stage phi(q) of the rows (zero past the block), phi(k) and v of the keys (zero past them).
         // Rows and keys past the block load a valid row (every load of the loop is issued
@@ -368,46 +381,40 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
         const bool vbad = __syncthreads_or(bad) != 0;
 
         // A[r][s] = phi(q_r).phi(k_{tau0+s}) for tau0 + s <= t(r), else 0: wave w, row tile w.
+        static_assert(KM == 16, "one tile of key slots");
         if (w < nrt) {
+            f32x4 acc = zero4();
 #pragma unroll
-            for (int kt = 0; kt < KM / 16; ++kt) {
-                f32x4 acc = zero4();
-                if (kt < nkt) {
+            for (int at = 0; at < NAT; ++at) {
+                const f32x4 xq = lds4(&sQ[(16 * w + c16) * DP + 16 * at + 4 * g]);
+                const f32x4 xk = lds4(&sK[c16 * DP + 16 * at + 4 * g]);
 #pragma unroll
-                    for (int at = 0; at < NAT; ++at) {
-                        const f32x4 xq = lds4(&sQ[(16 * w + c16) * DP + 16 * at + 4 * g]);
-                        const f32x4 xk = lds4(&sK[(16 * kt + c16) * DP + 16 * at + 4 * g]);
+                for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[i], xk[i], acc, 0, 0, 0);
+            }
+            const int s = c16, sp = 4 * (s & 3) + (s >> 2);  // slot s at k index sp
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[i], xk[i], acc, 0, 0, 0);
-                    }
-                }
-                const int s = 16 * kt + c16;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * w + 4 * g + e;
-                    const bool live = r < nb && s < tbk && tau0 + s <= (r0 + r) / G;
-                    sA[r * AP + s] = live ? acc[e] : 0.f;
-                }
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * w + 4 * g + e;
+                const bool live = r < nb && s < tbk && tau0 + s <= (r0 + r) / G;
+                sA[r * AP + sp] = live ? acc[e] : 0.f;
             }
         }
         __syncthreads();
 
         // den_r = phi(q_r).z + sum_s A[r][s]: four threads per row.
         {
+            static_assert(RBM * 4 == kBlock && KM == 16, "four threads per row, four key slots each");
             const int r = tid >> 2, p = tid & 3;
             float dp = 0.f;
             if (r < nb) {
 #pragma unroll
-                for (int a = p * F4; a < (p + 1) * F4; a += 4) {
+                for (int a = p * (D / 4); a < (p + 1) * (D / 4); a += 4) {
                     const f32x4 x = lds4(&sQ[r * DP + a]), zz = lds4(&sZ[a]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) dp += x[e] * zz[e];
                 }
-#pragma unroll
-                for (int s = p * (KM / 4); s < (p + 1) * (KM / 4); s += 4) {
-                    const f32x4 x = lds4(&sA[r * AP + s]);
-                    dp += (x[0] + x[1]) + (x[2] + x[3]);
-                }
+                const f32x4 x = lds4(&sA[r * AP + 4 * p]);
+                dp += (x[0] + x[1]) + (x[2] + x[3]);
             }
             dp += __shfl_xor(dp, 1, kWave);
             dp += __shfl_xor(dp, 2, kWave);
@@ -430,20 +437,16 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
                         for (int bt = 0; bt < NBT; ++bt)
                             num[rt][bt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[i], st[at][bt][i], num[rt][bt], 0, 0, 0);
                 }
+                const f32x4 xa = lds4(&sA[(16 * rt + c16) * AP + 4 * g]);  // slots g, 4 + g, 8 + g, 12 + g
 #pragma unroll
-                for (int kt = 0; kt < KM / 16; ++kt) {
-                    if (kt < nkt) {
-                        const f32x4 xa = lds4(&sA[(16 * rt + c16) * AP + 16 * kt + 4 * g]);
+                for (int i = 0; i < 4; ++i)
+                    if (i < nik)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-#pragma unroll
-                            for (int bt = 0; bt < NBT; ++bt) {
-                                float yv = sV[(16 * kt + 4 * g + i) * DP + cb0 + 16 * bt + c16];
-                                if (vbad) yv = finite_or_zero(yv);
-                                num[rt][bt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[i], yv, num[rt][bt], 0, 0, 0);
-                            }
-                    }
-                }
+                        for (int bt = 0; bt < NBT; ++bt) {
+                            float yv = sV[(4 * i + g) * DP + cb0 + 16 * bt + c16];
+                            if (vbad) yv = finite_or_zero(yv);
+                            num[rt][bt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[i], yv, num[rt][bt], 0, 0, 0);
+                        }
             }
         }
         __syncthreads();  // den is ready; phi(q) is no longer read
@@ -475,25 +478,18 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
         }
         // S += sum over the finished keys of phi(k) v^T (fp32 MFMA into the state tiles).
 #pragma unroll
-        for (int kt = 0; kt < KM / 16; ++kt) {
-            if (kt < nka) {
-                float yv[NBT][4];
+        for (int i = 0; i < 4; ++i) {
+            if (i < nia) {
+                const int s = 4 * i + g;
+                float yv[NBT];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int s = 16 * kt + 4 * g + i;
-#pragma unroll
-                    for (int bt = 0; bt < NBT; ++bt) yv[bt][i] = s < tba ? sV[s * DP + cb0 + 16 * bt + c16] : 0.f;
-                }
+                for (int bt = 0; bt < NBT; ++bt) yv[bt] = s < tba ? sV[s * DP + cb0 + 16 * bt + c16] : 0.f;
 #pragma unroll
                 for (int at = 0; at < NAT; ++at) {
+                    const float xk = s < tba ? sK[s * DP + 16 * at + c16] : 0.f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int s = 16 * kt + 4 * g + i;
-                        const float xk = s < tba ? sK[s * DP + 16 * at + c16] : 0.f;
-#pragma unroll
-                        for (int bt = 0; bt < NBT; ++bt)
-                            st[at][bt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xk, yv[bt][i], st[at][bt], 0, 0, 0);
-                    }
+                    for (int bt = 0; bt < NBT; ++bt)
+                        st[at][bt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xk, yv[bt], st[at][bt], 0, 0, 0);
                 }
             }
         }
