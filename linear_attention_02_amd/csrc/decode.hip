@@ -287,6 +287,33 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
         return ((bkv * G + h) * ntok + t) * D;
     };
 
+    // The loads of a block's rows and keys go to registers one block ahead: the first
+    // block's are in flight during the state passes, each later block's during the
+    // products of the block before it.  Rows and keys past a block load a valid row
+    // (every load is issued before the first use) and are staged as zeros.
+    constexpr int NQ = RBM * F4 / kBlock, NK = KM * F4 / kBlock;
+    static_assert(NQ * kBlock == RBM * F4 && NK * kBlock == KM * F4, "whole staging passes");
+    f32x4 xq[NQ], xk[NK], xv[NK];
+    auto load_block = [&](int rs, int ts, int nbs, int tbks) {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const int i4 = tid + j * kBlock, r = i4 / F4, c = 4 * (i4 % F4);
+            xq[j] = gload4<T>(q + qoff(rs + min(r, nbs - 1)) + c);
+        }
+#pragma unroll
+        for (int j = 0; j < NK; ++j) {
+            const int i4 = tid + j * kBlock, sl = i4 / F4, c = 4 * (i4 % F4);
+            const int64_t off = (krow0 + ts + min(sl, tbks - 1)) * D + c;
+            xk[j] = gload4<T>(k + off);
+            xv[j] = gload4<T>(v + off);
+        }
+    };
+    // Block extent from its first row r0 and first key tau0 = t(r0): nb rows, keys
+    // tau0 .. t(r0 + nb - 1) (tbk of them), of which the first tba have all their rows here.
+    auto block_nb = [&](int rs) { return min(rb, nrows - rs); };
+    auto block_tbk = [&](int rs, int ts) { return (rs + block_nb(rs) - 1) / G - ts + 1; };
+    load_block(0, 0, block_nb(0), block_tbk(0, 0));
+
     f32x4 st[NAT][NBT];
     // 16-byte state loads, RBM rows per pass, the next pass's loads in flight during this one's
     constexpr int NSP = RBM * F4 / kBlock;
@@ -331,31 +358,14 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
 
     int tau0 = 0;
     for (int r0 = 0; r0 < nrows;) {
-        const int nb = min(rb, nrows - r0), rend = r0 + nb;
-        const int tbk = (rend - 1) / G - tau0 + 1;       // keys tau0 .. t(rend - 1)
+        const int nb = block_nb(r0), rend = r0 + nb;
+        const int tbk = block_tbk(r0, tau0);            // keys tau0 .. t(rend - 1)
         const int tba = rend % G == 0 ? tbk : tbk - 1;  // keys whose rows are all done
         // Key slot s sits at k index 4 (s % 4) + s / 4 of the in-block products, so the
         // products over the first n keys take ceil(n / 4) of the four MFMA k-steps.
         const int nik = (tbk + 3) / 4, nia = (tba + 3) / 4;
 
         // Stage phi(q) of the rows (zero past the block), phi(k) and v of the keys (zero past them).
-        // Rows and keys past the block load a valid row (every load of the loop is issued
-        // before the first use) and stage zeros.
-        constexpr int NQ = RBM * F4 / kBlock, NK = KM * F4 / kBlock;
-        static_assert(NQ * kBlock == RBM * F4 && NK * kBlock == KM * F4, "whole staging passes");
-        f32x4 xq[NQ], xk[NK], xv[NK];
-#pragma unroll
-        for (int j = 0; j < NQ; ++j) {
-            const int i4 = tid + j * kBlock, r = i4 / F4, c = 4 * (i4 % F4);
-            xq[j] = gload4<T>(q + qoff(r0 + min(r, nb - 1)) + c);
-        }
-#pragma unroll
-        for (int j = 0; j < NK; ++j) {
-            const int i4 = tid + j * kBlock, s = i4 / F4, c = 4 * (i4 % F4);
-            const int64_t off = (krow0 + tau0 + min(s, tbk - 1)) * D + c;
-            xk[j] = gload4<T>(k + off);
-            xv[j] = gload4<T>(v + off);
-        }
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
             const int i4 = tid + j * kBlock, r = i4 / F4, c = 4 * (i4 % F4);
@@ -379,6 +389,7 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
             *reinterpret_cast<f32x4*>(&sV[s * DP + c]) = b;
         }
         const bool vbad = __syncthreads_or(bad) != 0;
+        if (rend < nrows) load_block(rend, tau0 + tba, block_nb(rend), block_tbk(rend, tau0 + tba));
 
         // A[r][s] = phi(q_r).phi(k_{tau0+s}) for tau0 + s <= t(r), else 0: wave w, row tile w.
         static_assert(KM == 16, "one tile of key slots");
@@ -421,32 +432,47 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
             if (p == 0 && r < nb) sDen[r] = rcp_f(dp);  // 1 / den
         }
 
-        // num = phi(Q) S + A V for this wave's columns.
-        f32x4 num[RBM / 16][NBT];
+        // num = phi(Q) S + A V for this wave's columns, every row tile of the buffer (rows past
+        // the block are zeros): the row tiles' accumulators are independent chains, so the
+        // products of one feature step go to the MFMA unit back to back.
+        constexpr int NRT = RBM / 16;
+        f32x4 num[NRT][NBT];
 #pragma unroll
-        for (int rt = 0; rt < RBM / 16; ++rt) {
+        for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
             for (int bt = 0; bt < NBT; ++bt) num[rt][bt] = zero4();
-            if (rt < nrt) {
 #pragma unroll
-                for (int at = 0; at < NAT; ++at) {
-                    const f32x4 xq = lds4(&sQ[(16 * rt + c16) * DP + 16 * at + 4 * g]);
+        for (int at = 0; at < NAT; ++at) {
+            f32x4 xq[NRT];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
+            for (int rt = 0; rt < NRT; ++rt) xq[rt] = lds4(&sQ[(16 * rt + c16) * DP + 16 * at + 4 * g]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+                    for (int bt = 0; bt < NBT; ++bt)
+                        num[rt][bt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[rt][i], st[at][bt][i], num[rt][bt], 0, 0, 0);
+        }
+        {
+            f32x4 xa[NRT];
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) xa[rt] = lds4(&sA[(16 * rt + c16) * AP + 4 * g]);  // slots g, 4 + g, ..
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (i < nik) {
+                    float yv[NBT];
+#pragma unroll
+                    for (int bt = 0; bt < NBT; ++bt) {
+                        yv[bt] = sV[(4 * i + g) * DP + cb0 + 16 * bt + c16];
+                        if (vbad) yv[bt] = finite_or_zero(yv[bt]);
+                    }
+#pragma unroll
+                    for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
                         for (int bt = 0; bt < NBT; ++bt)
-                            num[rt][bt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[i], st[at][bt][i], num[rt][bt], 0, 0, 0);
+                            num[rt][bt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[rt][i], yv[bt], num[rt][bt], 0, 0, 0);
                 }
-                const f32x4 xa = lds4(&sA[(16 * rt + c16) * AP + 4 * g]);  // slots g, 4 + g, 8 + g, 12 + g
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (i < nik)
-#pragma unroll
-                        for (int bt = 0; bt < NBT; ++bt) {
-                            float yv = sV[(4 * i + g) * DP + cb0 + 16 * bt + c16];
-                            if (vbad) yv = finite_or_zero(yv);
-                            num[rt][bt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[i], yv, num[rt][bt], 0, 0, 0);
-                        }
             }
         }
         __syncthreads();  // den is ready; phi(q) is no longer read
