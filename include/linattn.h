@@ -228,10 +228,11 @@ la_status la_decode_step(float* S, float* z, const void* q, const void* k, const
  * updated in place; q, o are [B][H][T][d] and k, v [B][Hkv][T][d] in dtype dt
  * (token t at row t).  T = 0 does nothing.  Needs no workspace.  With several
  * query heads per state (H > Hkv) at d = 64 or 128 the rows (t, h) are formed in
- * blocks of tokens by the chunked form of the same recurrence (fp32 MFMA
- * products, the state updated after each block's whole tokens): the same values
- * up to fp32 rounding, and an inf or NaN of token t reaches no row of an earlier
- * token. */
+ * blocks of tokens by the chunked form of the same recurrence (MFMA products,
+ * the state updated in fp32 after each block's whole tokens; for bf16 inputs the
+ * products with phi(q) take hi + lo bf16 splits of both operands, about 2^-16
+ * relative per product): the same values up to that rounding, and an inf or NaN
+ * of token t reaches no row of an earlier token. */
 la_status la_decode_steps(float* S, float* z, const void* q, const void* k, const void* v, void* o,
                           int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t d, la_dtype dt,
                           void* stream);

@@ -223,8 +223,9 @@ __global__ __launch_bounds__(kBlock) void decode_steps_kernel(float* __restrict_
 // and S, z then take the updates of the block's tokens whose rows are all done (a token
 // whose rows continue into the next block is that block's first key).  The state term is
 // a [rows x d] x [d x d] product, the in-block terms [rows x keys] products, the update a
-// rank-(keys) product; all run as fp32 MFMA (v_mfma_f32_16x16x4_f32), so the state keeps
-// fp32 arithmetic throughout, as in the one-row kernels.
+// rank-(keys) product.  Sums into the state run as fp32 MFMA (v_mfma_f32_16x16x4_f32), so
+// the state keeps fp32 arithmetic throughout, as in the one-row kernels; the products with
+// phi(q) do too for fp32 inputs, and take bf16 hi + lo splits for bf16 inputs.
 // Wave w holds state columns w d/4 .. (w + 1) d/4 - 1 of every feature row in accumulator
 // tiles: element i of lane (g, c) of tile (at, bt) is S[16 at + 4 g + i][w d/4 + 16 bt + c].
 // Read as the B operand of a product that contracts over features in the order
@@ -252,10 +253,21 @@ struct GroupedDecodeCfg {
                                              // so 64 rows of G >= 4 heads (32 of G = 2, 3) span at most 16 tokens
     static constexpr int DP = D + 4;         // LDS row stride in floats: 16 rows read 16 bytes each without conflicts
     static constexpr int AP = KM + 4;
+    static constexpr int DQ = D + 8;         // bf16 row stride of the split phi tiles (16 rows of 8 bytes: no conflicts)
     static constexpr int NAT = D / 16;       // feature tiles of the state
     static constexpr int CPW = D / 4;        // state columns per wave
     static constexpr int NBT = CPW / 16;     // column tiles per wave
 };
+
+// Operand of a 16x16x32 bf16 MFMA from row `row` of a bf16 tile (stride ld): columns
+// k0 + 4 g .. + 3 and k0 + 16 + 4 g .. + 3, the k order of accumulator-tile pairs.
+__device__ __forceinline__ Mma<bf16>::frag ld_pair(const bf16* t, int ld, int row, int k0, int g) {
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(t + row * ld + k0 + 4 * g);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(t + row * ld + k0 + 16 + 4 * g);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi): 16 significant bits.
+__device__ __forceinline__ bf16 split_lo(float x, bf16 hi) { return (bf16)(x - (float)hi); }
 
 template <typename T, int D, class FM>
 __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* __restrict__ S, float* __restrict__ z,
@@ -264,10 +276,19 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
                                                                       int ntok, int G) {
     using C = GroupedDecodeCfg<D>;
     constexpr int RBM = C::RBM, KM = C::KM, DP = C::DP, AP = C::AP, NAT = C::NAT, CPW = C::CPW, NBT = C::NBT;
+    constexpr int DQ = C::DQ;
+    // bf16 inputs: the products with phi(q) (the state term and A) run as three bf16 MFMAs
+    // on hi + lo splits of both operands (hi hi + hi lo + lo hi: about 2^-16 relative per
+    // product, far below the bf16 rounding of the outputs) at a fifth of the fp32 MFMA's
+    // cycles; fp32 inputs keep the fp32 MFMA.  Sums into the state stay fp32 MFMA either way.
+    constexpr bool kSplit = sizeof(T) == 2;
+    typedef Mma<bf16>::frag BF;
     constexpr int F4 = D / 4;
     static_assert(NBT >= 1 && kBlock == 4 * kWave && RBM % 16 == 0 && D % RBM == 0,
                   "four waves, whole column tiles per wave, the state in whole row buffers");
-    __shared__ __attribute__((aligned(16))) float sQ[RBM * DP];  // phi(q) of the block's rows; the state; outputs
+    // phi(q) of the block's rows (fp32, or bf16 hi and lo tiles); the state; the outputs
+    __shared__ __attribute__((aligned(16))) float sQ[RBM * (DP > DQ ? DP : DQ)];
+    __shared__ __attribute__((aligned(16))) bf16 sKs[kSplit ? 2 * KM * DQ : 8];  // phi(k) hi, lo tiles
     __shared__ __attribute__((aligned(16))) float sK[KM * DP];   // phi(k) of the block's keys
     __shared__ __attribute__((aligned(16))) float sV[KM * DP];   // v of the block's keys
     __shared__ __attribute__((aligned(16))) float sA[RBM * AP];  // masked phi(q_r).phi(k_tau)
@@ -372,7 +393,19 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
             f32x4 x;
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = r < nb ? FM::phi(xq[j][e]) : 0.f;
-            *reinterpret_cast<f32x4*>(&sQ[r * DP + c]) = x;
+            if constexpr (kSplit) {
+                bf16x4 h, l;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[e] = (bf16)x[e];
+                    l[e] = split_lo(x[e], h[e]);
+                }
+                bf16* const qh = reinterpret_cast<bf16*>(sQ);
+                *reinterpret_cast<bf16x4*>(qh + r * DQ + c) = h;
+                *reinterpret_cast<bf16x4*>(qh + RBM * DQ + r * DQ + c) = l;
+            } else {
+                *reinterpret_cast<f32x4*>(&sQ[r * DP + c]) = x;
+            }
         }
         int bad = 0;
 #pragma unroll
@@ -387,6 +420,16 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
             }
             *reinterpret_cast<f32x4*>(&sK[s * DP + c]) = a;
             *reinterpret_cast<f32x4*>(&sV[s * DP + c]) = b;
+            if constexpr (kSplit) {
+                bf16x4 h, l;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[e] = (bf16)a[e];
+                    l[e] = split_lo(a[e], h[e]);
+                }
+                *reinterpret_cast<bf16x4*>(sKs + s * DQ + c) = h;
+                *reinterpret_cast<bf16x4*>(sKs + KM * DQ + s * DQ + c) = l;
+            }
         }
         const bool vbad = __syncthreads_or(bad) != 0;
         if (rend < nrows) load_block(rend, tau0 + tba, block_nb(rend), block_tbk(rend, tau0 + tba));
@@ -395,12 +438,24 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
         static_assert(KM == 16, "one tile of key slots");
         if (w < nrt) {
             f32x4 acc = zero4();
+            if constexpr (kSplit) {
+                const bf16* const qh = reinterpret_cast<const bf16*>(sQ);
 #pragma unroll
-            for (int at = 0; at < NAT; ++at) {
-                const f32x4 xq = lds4(&sQ[(16 * w + c16) * DP + 16 * at + 4 * g]);
-                const f32x4 xk = lds4(&sK[c16 * DP + 16 * at + 4 * g]);
+                for (int k0 = 0; k0 < D; k0 += 32) {
+                    const BF ah = ld_pair(qh, DQ, 16 * w + c16, k0, g), al = ld_pair(qh + RBM * DQ, DQ, 16 * w + c16, k0, g);
+                    const BF bh = ld_pair(sKs, DQ, c16, k0, g), bl = ld_pair(sKs + KM * DQ, DQ, c16, k0, g);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+                }
+            } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[i], xk[i], acc, 0, 0, 0);
+                for (int at = 0; at < NAT; ++at) {
+                    const f32x4 xq = lds4(&sQ[(16 * w + c16) * DP + 16 * at + 4 * g]);
+                    const f32x4 xk = lds4(&sK[c16 * DP + 16 * at + 4 * g]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[i], xk[i], acc, 0, 0, 0);
+                }
             }
             const int s = c16, sp = 4 * (s & 3) + (s >> 2);  // slot s at k index sp
 #pragma unroll
@@ -420,7 +475,17 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
             if (r < nb) {
 #pragma unroll
                 for (int a = p * (D / 4); a < (p + 1) * (D / 4); a += 4) {
-                    const f32x4 x = lds4(&sQ[r * DP + a]), zz = lds4(&sZ[a]);
+                    f32x4 x;
+                    if constexpr (kSplit) {
+                        const bf16* const qh = reinterpret_cast<const bf16*>(sQ);
+                        const bf16x4 h = *reinterpret_cast<const bf16x4*>(qh + r * DQ + a);
+                        const bf16x4 l = *reinterpret_cast<const bf16x4*>(qh + RBM * DQ + r * DQ + a);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] = (float)h[e] + (float)l[e];
+                    } else {
+                        x = lds4(&sQ[r * DP + a]);
+                    }
+                    const f32x4 zz = lds4(&sZ[a]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) dp += x[e] * zz[e];
                 }
@@ -441,18 +506,46 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
         for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
             for (int bt = 0; bt < NBT; ++bt) num[rt][bt] = zero4();
+        if constexpr (kSplit) {
+            const bf16* const qh = reinterpret_cast<const bf16*>(sQ);
 #pragma unroll
-        for (int at = 0; at < NAT; ++at) {
-            f32x4 xq[NRT];
+            for (int at = 0; at < NAT; at += 2) {  // k-step over features 16 at .. 16 at + 31
+                BF sh[NBT], sl[NBT];
 #pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) xq[rt] = lds4(&sQ[(16 * rt + c16) * DP + 16 * at + 4 * g]);
+                for (int bt = 0; bt < NBT; ++bt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                    for (int e = 0; e < 4; ++e) {
+                        sh[bt][e] = (bf16)st[at][bt][e];
+                        sl[bt][e] = split_lo(st[at][bt][e], sh[bt][e]);
+                        sh[bt][4 + e] = (bf16)st[at + 1][bt][e];
+                        sl[bt][4 + e] = split_lo(st[at + 1][bt][e], sh[bt][4 + e]);
+                    }
 #pragma unroll
-                for (int rt = 0; rt < NRT; ++rt)
+                for (int rt = 0; rt < NRT; ++rt) {
+                    const BF ah = ld_pair(qh, DQ, 16 * rt + c16, 16 * at, g);
+                    const BF al = ld_pair(qh + RBM * DQ, DQ, 16 * rt + c16, 16 * at, g);
 #pragma unroll
-                    for (int bt = 0; bt < NBT; ++bt)
-                        num[rt][bt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[rt][i], st[at][bt][i], num[rt][bt], 0, 0, 0);
+                    for (int bt = 0; bt < NBT; ++bt) {
+                        num[rt][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sh[bt], num[rt][bt], 0, 0, 0);
+                        num[rt][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sl[bt], num[rt][bt], 0, 0, 0);
+                        num[rt][bt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, sh[bt], num[rt][bt], 0, 0, 0);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int at = 0; at < NAT; ++at) {
+                f32x4 xq[NRT];
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt) xq[rt] = lds4(&sQ[(16 * rt + c16) * DP + 16 * at + 4 * g]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+                        for (int bt = 0; bt < NBT; ++bt)
+                            num[rt][bt] = __builtin_amdgcn_mfma_f32_16x16x4f32(xq[rt][i], st[at][bt][i], num[rt][bt], 0, 0, 0);
+            }
         }
         {
             f32x4 xa[NRT];
