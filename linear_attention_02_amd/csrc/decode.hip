@@ -294,6 +294,7 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
     __shared__ __attribute__((aligned(16))) float sA[RBM * AP];  // masked phi(q_r).phi(k_tau)
     __shared__ __attribute__((aligned(16))) float sZ[D];
     __shared__ float sDen[RBM];  // 1 / den of each row
+    __shared__ int sTok[RBM];    // token of each row of the block
 
     const int64_t bkv = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave, g = lane >> 4, c16 = lane & 15;
@@ -303,9 +304,18 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
     const int nrows = G * ntok;  // the launcher keeps it below 2^31
     const int rb = G >= 4 ? RBM : RBM / 2;  // at most KM keys per block either way
     const int nrt = rb / 16;
-    auto qoff = [&](int ra) {  // element offset of row ra = t G + h
-        const int t = ra / G, h = ra - t * G;
-        return ((bkv * G + h) * ntok + t) * D;
+    auto qoff = [&](int t, int h) { return ((bkv * G + h) * ntok + t) * D; };  // row t G + h
+    // A thread handles rows tid / F4 + RSTEP j of a block (j = 0, 1, ..): their (token, head)
+    // pairs follow from the first by steps of RSTEP rows, one division per block.
+    constexpr int RSTEP = kBlock / F4;
+    const int tstep = RSTEP / G, hstep = RSTEP - tstep * G;
+    auto step_row = [&](int& t, int& h) {
+        t += tstep;
+        h += hstep;
+        if (h >= G) {
+            h -= G;
+            ++t;
+        }
     };
 
     // The loads of a block's rows and keys go to registers one block ahead: the first
@@ -316,10 +326,14 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
     static_assert(NQ * kBlock == RBM * F4 && NK * kBlock == KM * F4, "whole staging passes");
     f32x4 xq[NQ], xk[NK], xv[NK];
     auto load_block = [&](int rs, int ts, int nbs, int tbks) {
+        const int ra = rs + tid / F4, rl = rs + nbs - 1;  // first row, last row of the block
+        int t = ra / G, h = ra - t * G;
+        const int tl = rl / G, hl = rl - tl * G;
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
             const int i4 = tid + j * kBlock, r = i4 / F4, c = 4 * (i4 % F4);
-            xq[j] = gload4<T>(q + qoff(rs + min(r, nbs - 1)) + c);
+            xq[j] = gload4<T>(q + (r < nbs ? qoff(t, h) : qoff(tl, hl)) + c);
+            step_row(t, h);
         }
 #pragma unroll
         for (int j = 0; j < NK; ++j) {
@@ -387,6 +401,7 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
         const int nik = (tbk + 3) / 4, nia = (tba + 3) / 4;
 
         // Stage phi(q) of the rows (zero past the block), phi(k) and v of the keys (zero past them).
+        if (tid < RBM) sTok[tid] = (r0 + tid) / G;
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
             const int i4 = tid + j * kBlock, r = i4 / F4, c = 4 * (i4 % F4);
@@ -461,7 +476,7 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * w + 4 * g + e;
-                const bool live = r < nb && s < tbk && tau0 + s <= (r0 + r) / G;
+                const bool live = r < nb && s < tbk && tau0 + s <= sTok[r];
                 sA[r * AP + sp] = live ? acc[e] : 0.f;
             }
         }
@@ -583,7 +598,7 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
                         if (r < nb) {
                             float x = num[rt][bt][e];
                             if (vbad) {
-                                const int last = (r0 + r) / G - tau0;  // keys tau0 .. tau0 + last
+                                const int last = sTok[r] - tau0;  // keys tau0 .. tau0 + last
                                 for (int s = 0; s <= last; ++s) {
                                     const float y = sV[s * DP + b];
                                     if (!finite_f(y)) x += y - y;
@@ -614,9 +629,15 @@ __global__ __launch_bounds__(kBlock, 2) void decode_steps_grouped_kernel(float* 
         }
         __syncthreads();  // the outputs are in the row buffer
 
-        for (int i4 = tid; i4 < nb * F4; i4 += kBlock) {
-            const int r = i4 / F4, c = 4 * (i4 % F4);
-            store4(o + qoff(r0 + r) + c, lds4(&sQ[r * DP + c]));
+        {
+            const int ra = r0 + tid / F4;
+            int t = ra / G, h = ra - t * G;
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                const int i4 = tid + j * kBlock, r = i4 / F4, c = 4 * (i4 % F4);
+                if (r < nb) store4(o + qoff(t, h) + c, lds4(&sQ[r * DP + c]));
+                step_row(t, h);
+            }
         }
         if (tid < D) {  // z over the finished keys, token by token
             for (int s = 0; s < tba; ++s) zn += sK[s * DP + tid];
