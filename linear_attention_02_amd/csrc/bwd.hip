@@ -250,11 +250,23 @@ __device__ __forceinline__ void bwd_prefix_body(
         float gp = 0.f;
         {
             float gy[NY];
+            // bf16: G rounded once and kept packed for the staged tile and the MFMA operands.
+            // Rows past the head read dO = 0; with the elu map their den is positive, so G = 0
+            // there without a select (a given map can leave den = 0 there).
+            T gb[NY];
 #pragma unroll
-            for (int i = 0; i < NY; ++i) gy[i] = valid ? to_f32(from_f32<T>(cdo.get(i) * inv_den)) : 0.f;
+            for (int i = 0; i < NY; ++i) {
+                float x = cdo.get(i) * inv_den;
+                if (!FM::kSplit || sizeof(T) != 2) x = valid ? x : 0.f;
+                gb[i] = from_f32<T>(x);
+                gy[i] = to_f32(gb[i]);
+            }
 #pragma unroll
             for (int m = 0; m < DT; ++m) {
-                store4(&tG.at(tl, 16 * m + 4 * g), f32x4{gy[4 * m], gy[4 * m + 1], gy[4 * m + 2], gy[4 * m + 3]});
+                if constexpr (sizeof(T) == 2)
+                    *reinterpret_cast<uint2*>(&tG.at(tl, 16 * m + 4 * g)) = *reinterpret_cast<const uint2*>(&gb[4 * m]);
+                else
+                    store4(&tG.at(tl, 16 * m + 4 * g), f32x4{gy[4 * m], gy[4 * m + 1], gy[4 * m + 2], gy[4 * m + 3]});
                 if constexpr (FM::kSplit) {
                     const f32x4 pv = lds4(&s_p[16 * m + 4 * g]);
 #pragma unroll
@@ -268,7 +280,11 @@ __device__ __forceinline__ void bwd_prefix_body(
             for (int m = 0; m < DT; ++m) accQ[m] = zero4();
 #pragma unroll
             for (int k0 = 0; k0 < D; k0 += KS) {
-                const typename M::frag yg = M::vals_op(gy, k0);
+                typename M::frag yg;
+                if constexpr (sizeof(T) == 2)
+                    yg = *reinterpret_cast<const typename M::frag*>(&gb[k0 / 4]);
+                else
+                    yg = M::vals_op(gy, k0);
 #pragma unroll
                 for (int m = 0; m < DT; ++m) accQ[m] = M::mma(M::ld_tr_acc(tSt, k0, 16 * m, lane), yg, accQ[m]);
 #pragma unroll
