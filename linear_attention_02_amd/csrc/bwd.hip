@@ -597,19 +597,29 @@ __device__ __forceinline__ void bwd_suffix_body(
         }
         if (tid < kC) s_g[buf][tid] = gv;
         // This wave's keys: E(K) and phi'(K) from one exp; V stays raw.
-        float ke[NY], dphik[NY];
+        // E(K) rounded once to the operand type (bf16: kept packed as the MFMA operands).
+        T ke[NY];
+        float dphik[NY];
 #pragma unroll
         for (int i = 0; i < NY; ++i) {
             const float x = kr.get(i);
             if constexpr (FM::kSplit) {
                 const float c = expn_f(x);  // NaN for NaN, so phi'(K) carries it into dK
-                ke[i] = to_f32(from_f32<T>(__builtin_elementwise_maximum(x, c - 1.f)));
+                ke[i] = from_f32<T>(__builtin_elementwise_maximum(x, c - 1.f));
                 dphik[i] = c;
             } else {
-                ke[i] = to_f32(from_f32<T>(FM::e(x)));
+                ke[i] = from_f32<T>(FM::e(x));
                 dphik[i] = 1.f;
             }
         }
+        // Operand of k-step k0 from ke (value k0 / 4 + e at position e, the order of vals_op).
+        auto ke_op = [&](int k0) {
+            if constexpr (sizeof(T) == 2) {
+                return *reinterpret_cast<const typename M::frag*>(&ke[k0 / 4]);
+            } else {
+                return M::vals_op(reinterpret_cast<const float*>(ke), k0);
+            }
+        };
         const RowAcc<T, D> vcur = vrow;
         load_chunk(ci > 0 ? c0 - kC : N, (w + it + 1) & 3);  // past the head: zeros, no memory traffic
         const int tok = c0 + sl;
@@ -633,7 +643,7 @@ __device__ __forceinline__ void bwd_suffix_body(
 #pragma unroll
             for (int k0 = 0; k0 < D; k0 += KS) {
                 yv[k0 / KS] = M::raw_op(vcur.r, k0);
-                ye[k0 / KS] = M::vals_op(ke, k0);
+                ye[k0 / KS] = ke_op(k0);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -703,7 +713,7 @@ __device__ __forceinline__ void bwd_suffix_body(
 #pragma unroll
             for (int k0 = 0; k0 < D; k0 += KS) {
                 const typename M::frag yv = M::raw_op(vcur.r, k0);
-                const typename M::frag ye = M::vals_op(ke, k0);
+                const typename M::frag ye = ke_op(k0);
 #pragma unroll
                 for (int m = 0; m < DT; ++m) {
                     const typename M::frag xr = M::ld_acc(tRt, 16 * m, k0, lane);
