@@ -149,12 +149,14 @@ def test_decode_steps_match_single_steps(la, oracle, d):
 
 # ---- shared key/value heads (GQA / MQA) ------------------------------------------------------
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
-@pytest.mark.parametrize("heads", [(8, 2), (6, 1), (3, 3), (32, 1)], ids=lambda h: f"H{h[0]}kv{h[1]}")
-@pytest.mark.parametrize("T", [1, 5, 19])
+@pytest.mark.parametrize("heads", [(8, 2), (6, 1), (3, 3), (32, 1), (4, 2), (9, 3)], ids=lambda h: f"H{h[0]}kv{h[1]}")
+@pytest.mark.parametrize("T", [1, 5, 19, 40])
 @pytest.mark.parametrize("d", [64, 128])
 def test_decode_steps_shared_state(la, oracle, d, T, heads, dtype):
     """Each query head continues the causal recurrence of its key/value head from the
-    shared start state: the oracle runs that recurrence per query head."""
+    shared start state: the oracle runs that recurrence per query head.  With several
+    query heads per state the rows (t, h) go in blocks of 64 (32 for 2 or 3 heads per
+    state) whose last token may continue into the next block: T = 19 and 40 cover that."""
     H, Hkv = heads
     B, G = 2, H // Hkv
     S0, z0 = start_state(oracle, B, Hkv, d, dtype, seed=7 * d + T)
