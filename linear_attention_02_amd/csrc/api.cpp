@@ -571,14 +571,14 @@ la_status forward_causal(const void* q, const void* k, const void* v, void* o, c
             hipSuccess)
         return hip_fail(e, "state_split launch");
     unsigned* giveups = L.plan.scan ? nullptr : reinterpret_cast<unsigned*>(ws + L.giveups);
-    if (!L.plan.scan && Hkv == H && Gv == 1) {
+    if (!L.plan.scan && Hkv == H) {
         // one launch: every workgroup forms its own segment's record, then waits for the earlier ones
         unsigned long long* flags = reinterpret_cast<unsigned long long*>(ws + L.flags);
         const unsigned long long epoch = next_epoch();
         if ((e = timed("causal_fwd_fused", s, [&] {
                  return la::launch_causal_fwd_fused(idt, (int)d, q, k, v, o, den_out, rec, S_out, z_out, BH, N,
                                                     L.plan, s, init, init_n, feat, flags, giveups, epoch,
-                                                    g_wait_limit.load(std::memory_order_relaxed));
+                                                    g_wait_limit.load(std::memory_order_relaxed), (int)Gv);
              })) != hipSuccess)
             return hip_fail(e, "causal_fwd_fused launch");
         return LA_OK;

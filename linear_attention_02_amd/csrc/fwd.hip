@@ -947,13 +947,13 @@ hipError_t launch_causal_fwd_fused(int dt, int d, const void* q, const void* k, 
                                    float* den_out, float* rec, float* S_out, float* z_out, int64_t BH, int64_t N,
                                    SegPlan p, hipStream_t s, const float* init, const float* init_n, int feat,
                                    unsigned long long* flags, unsigned* giveups, unsigned long long epoch,
-                                   int wait_limit) {
+                                   int wait_limit, int Gv) {
     if (p.scan) return hipErrorInvalidValue;  // the records are summed directly
     return feat == kFeatGiven
                ? launch_causal_fwd_fm<FeatGiven, true>(dt, d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, p, s, init,
-                                                       init_n, 1, 1, flags, giveups, epoch, wait_limit)
+                                                       init_n, 1, Gv, flags, giveups, epoch, wait_limit)
                : launch_causal_fwd_fm<FeatElu, true>(dt, d, q, k, v, o, den_out, rec, S_out, z_out, BH, N, p, s, init,
-                                                     init_n, 1, 1, flags, giveups, epoch, wait_limit);
+                                                     init_n, 1, Gv, flags, giveups, epoch, wait_limit);
 }
 
 template <class FM>

@@ -75,7 +75,7 @@ hipError_t launch_causal_fwd_fused(int dt, int d, const void* q, const void* k, 
                                    float* den_out, float* rec, float* S_out, float* z_out, int64_t BH, int64_t N,
                                    SegPlan p, hipStream_t s, const float* init, const float* init_n, int feat,
                                    unsigned long long* flags, unsigned* giveups, unsigned long long epoch,
-                                   int wait_limit);
+                                   int wait_limit, int Gv = 1);
 // A start state (S0 [BH][d][d], z0 [BH][d], either nullable = zero) in the carried split
 // form: one record [S0_E^T | z0_E | P0] per head in init, and n0 per head in init_n.
 hipError_t launch_state_split(int d, const float* S0, const float* z0, float* init, float* init_n, int64_t BH,
