@@ -30,19 +30,30 @@ SegPlan plan_segments(int64_t BH, int64_t N, int64_t d) {
     // of workgroups that keeps at least 3/4 of the 256 CUs busy with at most that
     // many segments per head is taken (the fused forward at B1 H32 N131072: 1.34
     // against 1.52 ms for a running-sum plan); otherwise segments of 32 chunks,
-    // past which shorter segments balance the rounds better.
+    // past which shorter segments balance the rounds better.  Shorter d = 128 heads
+    // whose plan would need the running-sum pass take that one round too.
     constexpr int64_t kCUs = 256;
     int64_t cps = (BH * nchunk + 2 * kCUs - 1) / (2 * kCUs);
     if (cps < 1) cps = 1;
+    // At d = 128: one round of workgroups, at most kDirectRecordMaxSegments segments per head,
+    // when that keeps at least 3/4 of the CUs busy (segments per head; 0 when it does not).
+    int64_t one_round = 0;
+    if (d >= 128 && BH <= kCUs) {
+        one_round = kCUs / BH < kDirectRecordMaxSegments ? kCUs / BH : kDirectRecordMaxSegments;
+        if (4 * BH * one_round < 3 * kCUs) one_round = 0;
+    }
     if (cps > 32) {
         const int64_t longest = cps < 64 ? cps : 64;
-        const int64_t one_round = d >= 128 ? kCUs / BH : 0;  // segments per head
         if ((nchunk + longest - 1) / longest <= kDirectRecordMaxSegments)
             cps = longest;
-        else if (one_round >= 1 && one_round <= kDirectRecordMaxSegments && 4 * BH * one_round >= 3 * kCUs)
+        else if (one_round >= 1)
             cps = (nchunk + one_round - 1) / one_round;
         else
             cps = 32;
+    } else if (one_round >= 1 && (nchunk + cps - 1) / cps > kDirectRecordMaxSegments) {
+        // A d = 128 plan that would need the running-sum pass (B1 H32 N8192: 16 segments of 8
+        // chunks in two rounds, 224 us) takes the one round instead (8 segments of 16 chunks).
+        cps = (nchunk + one_round - 1) / one_round;
     }
     SegPlan p;
     p.cps = (int)cps;

@@ -272,6 +272,19 @@ def test_forward_causal_direct_records(la, oracle, shape):
     run_fwd_causal(la, oracle, B, H, N, d, torch.bfloat16, seed=N + 9)
 
 
+# d = 128 heads whose default plan (about 512 workgroups) would need more than 12 segments
+# take one round of at most 12 segments per head (16 heads of 65 chunks: ten segments of 6
+# chunks, one of 5 with a ragged tail): the forward in one launch, the backward's direct record sums.
+ONE_ROUND_SHAPES = [(1, 16, 64 * 64 + 17, 128)]
+
+
+@pytest.mark.parametrize("shape", ONE_ROUND_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_causal_d128_one_round(la, oracle, shape):
+    B, H, N, d = shape
+    run_fwd_causal(la, oracle, B, H, N, d, torch.bfloat16, seed=N + 11)
+    run_bwd_causal(la, oracle, B, H, N, d, torch.bfloat16, seed=N + 12)
+
+
 @pytest.mark.parametrize("shape", [(4, 64, 64 * 40 + 7, 32)], ids=lambda s: "x".join(map(str, s)))
 def test_backward_causal_long_segments(la, oracle, shape):
     """Segments of more than 16 chunks in the fused backward."""
