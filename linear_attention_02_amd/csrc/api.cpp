@@ -35,18 +35,20 @@ SegPlan plan_segments(int64_t BH, int64_t N, int64_t d) {
     constexpr int64_t kCUs = 256;
     int64_t cps = (BH * nchunk + 2 * kCUs - 1) / (2 * kCUs);
     if (cps < 1) cps = 1;
-    // At d = 128: one round of workgroups, at most kDirectRecordMaxSegments segments per head,
-    // when that keeps at least 3/4 of the CUs busy (segments per head; 0 when it does not).
+    // One round of workgroups (the heavy kernels hold one per CU at d = 128, two below), at most
+    // kDirectRecordMaxSegments segments per head, when that fills at least 3/4 of the
+    // workgroup slots (segments per head; 0 when it does not).
+    const int64_t slots = d >= 128 ? kCUs : 2 * kCUs;
     int64_t one_round = 0;
-    if (d >= 128 && BH <= kCUs) {
-        one_round = kCUs / BH < kDirectRecordMaxSegments ? kCUs / BH : kDirectRecordMaxSegments;
-        if (4 * BH * one_round < 3 * kCUs) one_round = 0;
+    if (BH <= slots) {
+        one_round = slots / BH < kDirectRecordMaxSegments ? slots / BH : kDirectRecordMaxSegments;
+        if (4 * BH * one_round < 3 * slots) one_round = 0;
     }
     if (cps > 32) {
         const int64_t longest = cps < 64 ? cps : 64;
         if ((nchunk + longest - 1) / longest <= kDirectRecordMaxSegments)
             cps = longest;
-        else if (one_round >= 1)
+        else if (d >= 128 && one_round >= 1)
             cps = (nchunk + one_round - 1) / one_round;
         else
             cps = 32;

@@ -197,6 +197,24 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(float* __restrict__ rec, i
 // its head, whose workgroups were dispatched before it.  The carried state then
 // sums their records as in the two-launch form.  A wait that gives up (a missing
 // producer) makes the segment's outputs NaN and is counted in `giveups`.
+// Whether a chunk held in registers has an inf or NaN element (exponent bits all ones).
+template <typename T, int D>
+__device__ __forceinline__ bool chunk_nonfinite(const ChunkRegs<T, D>& c) {
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < ChunkRegs<T, D>::NV; ++i) {
+        const uint32_t w[4] = {c.r[i].x, c.r[i].y, c.r[i].z, c.r[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (sizeof(T) == 2)
+                bad = bad || (w[j] & 0x7f80u) == 0x7f80u || (w[j] & 0x7f800000u) == 0x7f800000u;
+            else
+                bad = bad || (w[j] & 0x7f800000u) == 0x7f800000u;
+        }
+    }
+    return bad;
+}
+
 template <typename T, int D>
 struct CausalFwdCfg {
     // resident waves per SIMD the register allocation must allow (two workgroups per CU where
@@ -337,6 +355,12 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
     // roles, so that each keeps its own first-chunk loads in flight meanwhile; true if
     // every record arrived.
     __shared__ int s_ok;
+    // The last segment of a running-sum plan has no record after it to tell whether its
+    // values hold an inf or NaN; there the state waves flag each staged chunk of V (one
+    // flag per state wave) and the output waves take the non-finite path only for chunks
+    // that have one.
+    __shared__ int s_vf[2][4];
+    const bool vchk = prefixed != 0 && seg + 1 >= nseg;
     float* const xs = reinterpret_cast<float*>(&sm);
     auto fused_records = [&]() -> bool {
         unsigned long long* hf = flags + (int64_t)bh * nseg;
@@ -400,6 +424,10 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
         store_vec<D>(s_p[0], vp, lane, w);
         stage_elu<T, D, FM>(ck, Tile<T, kC, D>{sm_e[0]}, rtid);
         stage_raw<T, D>(cv, Tile<T, kC, D>{sm_v[0]}, rtid);
+        if (vchk) {
+            const bool nf = __builtin_amdgcn_ballot_w64(chunk_nonfinite(cv)) != 0;
+            if (lane == 0) s_vf[0][w] = nf ? 1 : 0;
+        }
         // Loads past the segment are aimed at row N: out of the buffer's range, they
         // return zeros without touching memory, and the loop stays branch free.
         ck.load(bk, tok_begin + kC < tok_end ? tok_begin + kC : N, rtid);
@@ -413,6 +441,10 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
             // for the next chunk.
             stage_elu<T, D, FM>(ck, Tile<T, kC, D>{sm_e[B ^ 1]}, rtid);
             stage_raw<T, D>(cv, Tile<T, kC, D>{sm_v[B ^ 1]}, rtid);
+            if (vchk) {
+                const bool nf = __builtin_amdgcn_ballot_w64(chunk_nonfinite(cv)) != 0;
+                if (lane == 0) s_vf[B ^ 1][w] = nf ? 1 : 0;
+            }
             ck.load(bk, c0 + 2 * kC < tok_end ? c0 + 2 * kC : N, rtid);
             cv.load(bv, c0 + 2 * kC < tok_end ? c0 + 2 * kC : N, rtid);
             state_update<T, D, true, true>(st, vz, vp, Tile<T, kC, D>{sm_e[B]}, Tile<T, kC, D>{sm_v[B]}, nullptr,
@@ -517,6 +549,7 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
         const Tile<T, D, D> tSt{sm_st[B]};
         const bool more = c0 + kC < tok_end;
         const int tt = (w + ci) & 3;
+        const bool cbad = vbad && (!vchk || (s_vf[B][0] | s_vf[B][1] | s_vf[B][2] | s_vf[B][3]) != 0);
         const int tl = 16 * tt + (lane & 15);  // this lane's token (accumulator column)
 
         F qf[D / KS];
@@ -564,7 +597,7 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
                         acc[DT] = M::mma(one, yf, acc[DT]);
                     }
                 };
-                if (vbad && 2 * kb + 1 >= tt)  // the block holding the diagonal tile
+                if (cbad && 2 * kb + 1 >= tt)  // the block holding the diagonal tile
                     av(std::true_type{});
                 else
                     av(std::false_type{});
@@ -588,7 +621,7 @@ __global__ __launch_bounds__(2 * kBlock, (CausalFwdCfg<T, D>::kWavesPerSimd)) vo
             f32x4 x;
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = (acc[m][e] + qs_t * p4[e]) * inv;
-            if (vbad) {  // the non-finite values of keys s <= t that the diagonal block dropped
+            if (cbad) {  // the non-finite values of keys s <= t that the diagonal block dropped
                 for (int s = 32 * (tt >> 1); s <= tl; ++s) {
                     const f32x4 vv = lds4(&tV.at(s, b0));
 #pragma unroll

@@ -30,10 +30,11 @@ def la():
 
 
 # (B, H, N, d, t0): one segment; several segments of several chunks with t0 in a later one;
-# d = 128; d = 32; 8 segments of 5 chunks per head with t0 inside a segment's second chunk
+# d = 128; d = 32; 8 segments of 5 chunks per head with t0 inside a segment's second chunk;
+# t0 inside the last segment of a running-sum plan (44 segments of 3 chunks per head)
 CASES = [(1, 2, 256, 64, 130), (1, 8, 64 * 130 + 17, 64, 64 * 70 + 37), (1, 2, 300, 128, 200), (2, 1, 200, 32, 77),
-         (4, 16, 64 * 40, 64, 64 * 21 + 37)]
-IDS = ["N256_t130", "N8337_t4517", "d128_t200", "d32_t77", "seg5_t1381"]
+         (4, 16, 64 * 40, 64, 64 * 21 + 37), (1, 8, 64 * 130 + 17, 64, 8300)]
+IDS = ["N256_t130", "N8337_t4517", "d128_t200", "d32_t77", "seg5_t1381", "scan_last_t8300"]
 
 
 def finite_rows(x):
