@@ -19,7 +19,7 @@
 
 namespace la {
 
-SegPlan plan_segments(int64_t BH, int64_t N, int64_t d) {
+SegPlan plan_segments(int64_t BH, int64_t N, int64_t d, bool causal) {
     const int64_t nchunk = (N + kChunk - 1) / kChunk;
     // Aim for about 512 workgroups (2 per CU): the heavy kernels keep 2-3
     // workgroups resident per CU, and starting a segment costs one record read
@@ -30,8 +30,10 @@ SegPlan plan_segments(int64_t BH, int64_t N, int64_t d) {
     // of workgroups that keeps at least 3/4 of the 256 CUs busy with at most that
     // many segments per head is taken (the fused forward at B1 H32 N131072: 1.34
     // against 1.52 ms for a running-sum plan); otherwise segments of 32 chunks,
-    // past which shorter segments balance the rounds better.  Shorter d = 128 heads
-    // whose plan would need the running-sum pass take that one round too.
+    // past which shorter segments balance the rounds better.  Shorter causal heads
+    // whose plan would need the running-sum pass take that one round too (the
+    // non-causal passes sum their records in a pass of their own and keep the
+    // larger count of workgroups).
     constexpr int64_t kCUs = 256;
     int64_t cps = (BH * nchunk + 2 * kCUs - 1) / (2 * kCUs);
     if (cps < 1) cps = 1;
@@ -52,7 +54,7 @@ SegPlan plan_segments(int64_t BH, int64_t N, int64_t d) {
             cps = (nchunk + one_round - 1) / one_round;
         else
             cps = 32;
-    } else if (one_round >= 1 && (nchunk + cps - 1) / cps > kDirectRecordMaxSegments) {
+    } else if (causal && one_round >= 1 && (nchunk + cps - 1) / cps > kDirectRecordMaxSegments) {
         // A d = 128 plan that would need the running-sum pass (B1 H32 N8192: 16 segments of 8
         // chunks in two rounds, 224 us) takes the one round instead (8 segments of 16 chunks).
         cps = (nchunk + one_round - 1) / one_round;
@@ -176,7 +178,7 @@ struct Layout {
 Layout layout(la_op op, int64_t B, int64_t H, int64_t N, int64_t d) {
     Layout L;
     const int64_t BH = B * H;
-    L.plan = la::plan_segments(BH, N, d);
+    L.plan = la::plan_segments(BH, N, d, op == LA_OP_FWD_CAUSAL || op == LA_OP_BWD_CAUSAL);
     L.heads = BH;
     const size_t recb = (size_t)BH * L.plan.nseg * la::rec_floats(d) * sizeof(float);
     size_t off = 0;
@@ -249,9 +251,10 @@ unsigned long long next_epoch() {
 }
 
 // The saved forward state: every segment record, then (filled by the non-causal
-// forward only) one total per head.
+// forward only) one total per head.  The records of the non-causal plan: the causal
+// plan never has more segments, so its records fit in front of the totals too.
 size_t saved_records_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
-    const la::SegPlan p = la::plan_segments(B * H, N, d);
+    const la::SegPlan p = la::plan_segments(B * H, N, d, false);
     return align_up((size_t)(B * H) * p.nseg * la::rec_floats(d) * sizeof(float));
 }
 

@@ -37,7 +37,9 @@ struct SegPlan {
 // (each workgroup re-reads its predecessors' records: quadratic in the segment
 // count, cheaper than a scan pass only while that count is small).
 constexpr int kDirectRecordMaxSegments = 12;
-SegPlan plan_segments(int64_t BH, int64_t N, int64_t d);
+// causal: the plan of the causal calls (d = 128 heads and a few more at d = 64 may take one
+// round of fewer segments where the default would need the running-sum pass).
+SegPlan plan_segments(int64_t BH, int64_t N, int64_t d, bool causal = true);
 
 // Number of floats in one segment-state record for head dimension d:
 // S_E^T [d][d], z_E [d], P [d].
