@@ -275,14 +275,35 @@ def test_forward_causal_direct_records(la, oracle, shape):
 # d = 128 heads whose default plan (about 512 workgroups) would need more than 12 segments
 # take one round of at most 12 segments per head (16 heads of 65 chunks: ten segments of 6
 # chunks, one of 5 with a ragged tail): the forward in one launch, the backward's direct record sums.
-ONE_ROUND_SHAPES = [(1, 16, 64 * 64 + 17, 128)]
+# At d = 64 the same holds with two workgroups per CU (32 heads of 65 chunks: 11 segments).
+ONE_ROUND_SHAPES = [(1, 16, 64 * 64 + 17, 128), (1, 32, 64 * 64 + 17, 64)]
 
 
 @pytest.mark.parametrize("shape", ONE_ROUND_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_causal_d128_one_round(la, oracle, shape):
+def test_causal_one_round(la, oracle, shape):
     B, H, N, d = shape
     run_fwd_causal(la, oracle, B, H, N, d, torch.bfloat16, seed=N + 11)
     run_bwd_causal(la, oracle, B, H, N, d, torch.bfloat16, seed=N + 12)
+
+
+@pytest.mark.parametrize("shape", ONE_ROUND_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_saved_state_one_round(la, shape):
+    """Where the causal plan takes fewer segments than the non-causal one, one saved-state
+    buffer serves both: each backward reading its forward's saved state is bitwise the
+    backward that rebuilds the state itself."""
+    B, H, N, d = shape
+    q, k, v, do = draw(B, H, N, d, torch.bfloat16, seed=N + 13)
+    saved = la.new_saved_state(q)
+    la.la_forward_causal(q, k, v, saved_state=saved)
+    g1 = la.la_backward_causal(q, k, v, do, saved_state=saved)
+    g2 = la.la_backward_causal(q, k, v, do)
+    saved2 = la.new_saved_state(q)
+    la.la_forward_noncausal(q, k, v, saved_state=saved2)
+    h1 = la.la_backward_noncausal(q, k, v, do, saved_state=saved2)
+    h2 = la.la_backward_noncausal(q, k, v, do)
+    torch.cuda.synchronize()
+    for a, b in zip(g1 + h1, g2 + h2):
+        assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("shape", [(4, 64, 64 * 40 + 7, 32)], ids=lambda s: "x".join(map(str, s)))
