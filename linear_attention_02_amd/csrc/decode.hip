@@ -216,8 +216,8 @@ __global__ __launch_bounds__(kBlock) void decode_steps_kernel(float* __restrict_
 // ---------------------------------------------------------------------------------------
 // decode_steps_grouped: the same T steps for G >= 2 query heads per key/value state, with
 // every product on MFMA.  The G query heads of a token all read one state, so a block of
-// rows (t, h) (token-major, up to 32 rows) is the causal form of the proposition over the
-// block's tokens tau0 .. tau1, chunked:
+// rows (t, h) (token-major, up to 64 rows; 32 for fewer than 4 heads per state) is the causal
+// form of the proposition over the block's tokens tau0 .. tau1, chunked:
 //   num_r = phi(q_r)^T S_<tau0 + sum_{tau0 <= tau <= t(r)} (phi(q_r).phi(k_tau)) v_tau,
 //   den_r = phi(q_r)^T z_<tau0 + sum_{tau0 <= tau <= t(r)} phi(q_r).phi(k_tau),
 // and S, z then take the updates of the block's tokens whose rows are all done (a token
